@@ -1,0 +1,123 @@
+// Device entry points of lowbit.h: host-side argument validation, then the
+// kernel launchers.  Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime_api.h>
+
+#include "internal.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ll_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return LL_OK;
+    return ll::failf(LL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape and pointer checks common to every product entry point.
+ll_status check_weights(const ll_weights* w, const char* fn) {
+    if (!w) return ll::failf(LL_EINVAL, "%s: weights descriptor is NULL", fn);
+    if (w->N <= 0 || w->K <= 0) return ll::failf(LL_EINVAL, "%s: N and K must be positive", fn);
+    if (w->N > (int64_t(1) << 31) - 1 || w->K > (int64_t(1) << 24))
+        return ll::failf(LL_ERANGE, "%s: N must be < 2^31 and K <= 2^24", fn);
+    if (!w->codes) return ll::failf(LL_EINVAL, "%s: codes pointer is NULL", fn);
+    if (!aligned(w->codes, 16)) return ll::failf(LL_EALIGN, "%s: codes must be 16-byte aligned", fn);
+    switch (w->fmt) {
+    case LL_FMT_I2S:
+        if (w->K % 128) return ll::failf(LL_ESHAPE, "%s: i2_s needs K %% 128 == 0", fn);
+        return LL_OK;
+    case LL_FMT_TQ2_0:
+        if (w->K % 256) return ll::failf(LL_ESHAPE, "%s: TQ2_0 needs K %% 256 == 0", fn);
+        if (!w->scales) return ll::failf(LL_EINVAL, "%s: TQ2_0 scales pointer is NULL", fn);
+        if (!aligned(w->scales, 2)) return ll::failf(LL_EALIGN, "%s: scales must be 2-byte aligned", fn);
+        return LL_OK;
+    case LL_FMT_W1:
+        if (w->group <= 0 || w->group % 32 || w->K % w->group)
+            return ll::failf(LL_ESHAPE, "%s: W1 needs group a positive multiple of 32 dividing K", fn);
+        if (!w->scales) return ll::failf(LL_EINVAL, "%s: W1 scales pointer is NULL", fn);
+        if (!aligned(w->scales, 2)) return ll::failf(LL_EALIGN, "%s: scales must be 2-byte aligned", fn);
+        return LL_OK;
+    default:
+        return ll::failf(LL_EINVAL, "%s: unknown format %d", fn, int(w->fmt));
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* xq, float* xs, void* stream) {
+    if (!x || !xq || !xs) return ll::fail(LL_EINVAL, "ll_quantize_act: NULL pointer");
+    if (x_dtype != LL_DT_F32 && x_dtype != LL_DT_BF16) return ll::fail(LL_EINVAL, "ll_quantize_act: unknown dtype");
+    if (M <= 0 || K <= 0) return ll::fail(LL_EINVAL, "ll_quantize_act: M and K must be positive");
+    if (M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 20)) return ll::fail(LL_ERANGE, "ll_quantize_act: M < 2^31, K <= 2^20");
+    if (!aligned(x, x_dtype == LL_DT_F32 ? 4 : 2) || !aligned(xs, 4))
+        return ll::fail(LL_EALIGN, "ll_quantize_act: x / xs not aligned to their element size");
+    return hip_status(llk::launch_quantize(x, x_dtype == LL_DT_BF16, M, K, xq, xs, static_cast<hipStream_t>(stream)),
+                      "ll_quantize_act");
+}
+
+size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M) {
+    if (!w || M < 1 || M > 16 || w->K <= 0) return size_t(-1);
+    if (act == LL_ACT_F32) return llk::gemv_f32_workspace(M, w->K);
+    if (act == LL_ACT_I8) return 0;
+    return size_t(-1);
+}
+
+ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs, int64_t M,
+                            const float* bias, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ll_bitlinear_gemv";
+    ll_status st = check_weights(w, fn);
+    if (st) return st;
+    if (M < 1 || M > 16) return ll::fail(LL_ESHAPE, "ll_bitlinear_gemv: M must be in [1, 16] (use ll_bitlinear_gemm above)");
+    if (!x || !y) return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: x or y is NULL");
+    if (!aligned(x, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: x must be 16-byte aligned");
+    if (!aligned(y, 4) || (bias && !aligned(bias, 4))) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: y / bias must be 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (act == LL_ACT_F32) {
+        if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0)
+            return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: fp32 activations need format i2_s or TQ2_0");
+        const size_t need = llk::gemv_f32_workspace(M, w->K);
+        if (!workspace || workspace_bytes < need)
+            return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
+        if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
+        return hip_status(llk::launch_gemv_f32(w->fmt, w->codes, w->scales, w->N, w->K, static_cast<const float*>(x), M,
+                                               bias, y, workspace, s),
+                          fn);
+    }
+    if (act == LL_ACT_I8) {
+        if (!xs) return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: int8 activations need their scales xs");
+        if (!aligned(xs, 4)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: xs must be 4-byte aligned");
+        if (w->fmt == LL_FMT_I2S)
+            return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K,
+                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, s),
+                              fn);
+        return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: int8 activations with this format are not supported");
+    }
+    return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: unknown activation type");
+}
+
+size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
+    if (!w || M < 1) return size_t(-1);
+    return 0;
+}
+
+ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
+                            float* y, int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    const char* fn = "ll_bitlinear_gemm";
+    ll_status st = check_weights(w, fn);
+    if (st) return st;
+    if (M < 1 || M > 65535 * 128) return ll::fail(LL_ESHAPE, "ll_bitlinear_gemm: M must be in [1, 65535*128]");
+    if (!xq || !xs || !y) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: xq, xs or y is NULL");
+    if (!aligned(xq, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xq must be 16-byte aligned");
+    if (!aligned(xs, 4) || !aligned(y, 4) || (bias && !aligned(bias, 4)) || (acc_out && !aligned(acc_out, 4)))
+        return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xs / y / bias / acc_out must be 4-byte aligned");
+    if (w->fmt != LL_FMT_I2S) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: only format i2_s is supported");
+    return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y,
+                                              acc_out, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+}  // extern "C"

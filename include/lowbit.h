@@ -1,0 +1,204 @@
+/*
+ * lowbit.h -- C ABI of the packed low-bit BitLinear library for AMD MI355X
+ * (gfx950).  The library computes
+ *
+ *     y[m, n] = scale * sum_k w[n, k] * x[m, k]
+ *
+ * reading ternary or binary weights directly in their packed layouts.
+ *
+ * Sources of the operations declared here:
+ *   [BL] Hesper API doc "Hesper/Layers/BitLinear": "i2_s Packing Format"
+ *        (code table, 128-element / 32-byte groups at shifts 6/4/2/0, one
+ *        fp32 scale at the end of the tensor data), "BitLinear Mathematics"
+ *        (the product), "High-Level API" (4-byte little-endian scale,
+ *        forward(in, out)).
+ *   [TQ] Hesper API doc "Hesper/Quantization/TQ2_0": "TQ2_0 Format"
+ *        (256-element blocks, 64 packed bytes + fp16 scale = 66 bytes,
+ *        codes 0b11/0b00/0b01), "GPU Unpacking Kernel" (packed codes and
+ *        fp16 scales as two separate device buffers).
+ *   [BG] binary-gemm kernel card: "API" (pack_weights, unpack_weights,
+ *        quantize_activation, binary_gemm), "Method" (stored bit
+ *        b = (w+1)/2, per-group fp16 scales, dot identity), "Usage"
+ *        (from_dense), "Requirements and limits" (K a multiple of 32 and of
+ *        the group size).
+ *
+ * Conventions for every function:
+ *   - Matrices are row-major: x is [M, K], y is [M, N], weights are [N, K]
+ *     (y = x * W^T).
+ *   - Host functions take host pointers; device functions take device
+ *     pointers allocated by the caller (for example torch tensors).  The
+ *     library never frees, and no device function allocates or
+ *     synchronizes: kernels are enqueued on `stream` (a hipStream_t; NULL
+ *     means the default stream) and the call returns.
+ *   - Every argument is validated on the host before anything is written or
+ *     launched.  On error the function returns a negative ll_status, leaves
+ *     every output untouched, and ll_last_error() describes the problem.
+ *   - Device pointers must be 16-byte aligned (LL_EALIGN otherwise).
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LL_ABI_VERSION 1
+
+typedef enum {
+    LL_OK = 0,
+    LL_EINVAL = -1,      /* null pointer, unknown enum, non-positive size */
+    LL_ESHAPE = -2,      /* K not a multiple of the format's group/block, M outside the entry point's range */
+    LL_EALIGN = -3,      /* a device pointer is not 16-byte aligned */
+    LL_ECODE = -4,       /* weight value outside the format's alphabet, or an invalid packed code */
+    LL_EWORKSPACE = -5,  /* workspace missing or smaller than ll_*_workspace_size() */
+    LL_EHIP = -6,        /* HIP runtime error (no device, launch failure); detail in ll_last_error() */
+    LL_ERANGE = -7       /* a size does not fit the kernel's index arithmetic */
+} ll_status;
+
+typedef enum {
+    LL_FMT_I2S = 1,      /* [BL] ternary, 2-bit codes, one fp32 scale per tensor */
+    LL_FMT_TQ2_0 = 2,    /* [TQ] ternary, 256-element blocks, fp16 scale per block */
+    LL_FMT_W1 = 3        /* [BG] binary sign bits, fp16 scale per G weights */
+} ll_format;
+
+typedef enum {
+    LL_ACT_F32 = 1,      /* activations fp32 [M, K] */
+    LL_ACT_I8 = 2        /* activations int8 [M, K] with one fp32 scale per token (ll_quantize_act) */
+} ll_act;
+
+typedef enum {
+    LL_DT_F32 = 1,
+    LL_DT_BF16 = 2
+} ll_dtype;
+
+/*
+ * A packed weight matrix resident in device memory.
+ *   LL_FMT_I2S : codes  = N*K/4 packed bytes followed by the 4-byte
+ *                         little-endian fp32 scale (exactly the output of
+ *                         ll_pack_i2s); scales = NULL.  K % 128 == 0.
+ *   LL_FMT_TQ2_0: codes = the 64 code bytes of every block, blocks in
+ *                         order (N*K/4 bytes); scales = fp16 [N*K/256], one
+ *                         per block in the same order (ll_tq2_split turns
+ *                         66-byte blocks into these two arrays).  K % 256 == 0.
+ *   LL_FMT_W1  : codes  = uint32 [N, K/32] sign bits (ll_pack_w1);
+ *                scales = fp16 [N, K/group].  K % 32 == 0, K % group == 0.
+ * group: W1 scale group size G (> 0, multiple of 32); ignored otherwise.
+ */
+typedef struct {
+    int32_t fmt;         /* ll_format */
+    int32_t group;
+    int64_t N, K;
+    const void* codes;
+    const void* scales;
+} ll_weights;
+
+/* ------------------------------------------------------------------ */
+/* Library information                                                  */
+/* ------------------------------------------------------------------ */
+
+int ll_abi_version(void);
+const char* ll_strerror(int status);
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* ll_last_error(void);
+
+/* ------------------------------------------------------------------ */
+/* Host-side formats (CPU, host pointers, caller-owned buffers)          */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of the packed codes of an N x K matrix in format fmt (the i2_s
+   count includes its 4-byte tail scale; TQ2_0 counts the 66-byte blocks).
+   *scales_bytes (if not NULL) receives the size of the separate scale array
+   (0 for i2_s; 2*N*K/256 for the split TQ2_0 device layout; 2*N*K/group for
+   W1).  Returns 0 for an invalid shape. */
+size_t ll_packed_size(int32_t fmt, int64_t N, int64_t K, int32_t group, size_t* scales_bytes);
+
+/* [BL "i2_s Packing Format"] w: int8 [N,K] in {-1,0,+1}; out: N*K/4 + 4
+   bytes.  Code of w is w+1 (-1 -> 0b00, 0 -> 0b01, +1 -> 0b10); element r of
+   each 128-element group goes to byte r%32 of the group's 32 bytes at shift
+   6 - 2*(r/32); the scale is appended as 4 little-endian bytes.
+   LL_ESHAPE if K % 128, LL_ECODE for a value outside {-1,0,1}. */
+ll_status ll_pack_i2s(const int8_t* w, int64_t N, int64_t K, float scale, uint8_t* out);
+/* Inverse of ll_pack_i2s.  LL_ECODE if a code 0b11 occurs (w is then
+   filled anyway, that element as +2). scale may be NULL. */
+ll_status ll_unpack_i2s(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, float* scale);
+
+/* [TQ "TQ2_0 Format"] w: int8 [N,K] in {-1,0,+1}; scales: fp16 bits
+   [N*K/256] (block order); out: 66*N*K/256 bytes of blocks (64 code bytes,
+   then scale_low, scale_high).  Codes 0 -> 0b00, +1 -> 0b01, -1 -> 0b11;
+   element e of a block sits in byte e/4 at bits 2*(e%4).
+   LL_ESHAPE if K % 256, LL_ECODE for a value outside {-1,0,1}. */
+ll_status ll_pack_tq2(const int8_t* w, const uint16_t* scales, int64_t N, int64_t K, uint8_t* out);
+/* Inverse of ll_pack_tq2; LL_ECODE if a code 0b10 occurs (decoded as -2). */
+ll_status ll_unpack_tq2(const uint8_t* blocks, int64_t N, int64_t K, int8_t* w, uint16_t* scales);
+/* [TQ "GPU Unpacking Kernel": separate packed and scale buffers] 66-byte
+   blocks -> codes (N*K/4 bytes) + scales (fp16 [N*K/256]). */
+ll_status ll_tq2_split(const uint8_t* blocks, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+
+/* [BG "API": pack_weights] w: int8 [N,K]; bit k%32 of word n*(K/32)+k/32
+   is 1 where w > 0 (stored bit (w+1)/2; zeros store 0, i.e. -1).
+   LL_ESHAPE if K % 32. */
+ll_status ll_pack_w1(const int8_t* w, int64_t N, int64_t K, uint32_t* out);
+/* [BG "API": unpack_weights] bits -> int8 {-1,+1} [N,K]. */
+ll_status ll_unpack_w1(const uint32_t* bits, int64_t N, int64_t K, int8_t* w);
+/* [BG "Usage": from_dense, sign + group mean-abs scale] W: fp32 [N,K].
+   bits as ll_pack_w1 of sign(W) (W > 0 -> +1); scales[n, g] = fp16 (round
+   to nearest even) of mean_{k in g} |W[n,k]| accumulated in fp64.
+   LL_ESHAPE unless K % 32 == 0, group > 0 and K % group == 0. */
+ll_status ll_w1_from_dense(const float* W, int64_t N, int64_t K, int32_t group, uint32_t* bits, uint16_t* scales);
+
+/* Checks a host copy of packed codes: LL_ECODE for an invalid code (i2_s
+   0b11, TQ2_0 0b10; W1 has none), *bad_index (may be NULL) = element index
+   n*K+k of the first one, else -1.  For TQ2_0, codes is the split layout. */
+ll_status ll_validate(int32_t fmt, const void* codes, int64_t N, int64_t K, int64_t* bad_index);
+
+/* ------------------------------------------------------------------ */
+/* Device entry points (gfx950)                                          */
+/* ------------------------------------------------------------------ */
+
+/* [BG "API": quantize_activation] Per-token absmax quantization.
+   x: device [M,K] fp32 or bf16 (x_dtype); xq: device int8 [M,K];
+   xs: device fp32 [M].  For each token: a = max|x|; a == 0 gives s = 0 and
+   q = 0; else inv = 127/a (IEEE fp32 division), q = round-half-even(x*inv)
+   clamped to [-127,127], s = a/127.  1 <= M, 1 <= K <= 2^20. */
+ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                          int8_t* xq, float* xs, void* stream);
+
+/* Bytes of device workspace ll_bitlinear_gemv needs for these arguments
+   (0 when none is needed).  Returns (size_t)-1 for invalid arguments. */
+size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
+
+/* [BL "Fused BitLinear Kernel", "M=1 Warp-Cooperative" ; BG "API":
+   binary_gemm] Decode-size product, 1 <= M <= 16, reading the packed codes
+   in the kernel.  act == LL_ACT_F32: x fp32 [M,K], xs unused (NULL); formats
+   i2_s and TQ2_0; y = scale * sum_k w*x (i2_s) or sum over blocks of
+   s_block * sum w*x (TQ2_0), fp32 accumulation.
+   act == LL_ACT_I8: x int8 [M,K], xs fp32 [M] from ll_quantize_act; formats
+   i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32) and W1
+   (y = (float)((double)xs[m] * sum_g s_g * d_g), d_g the exact per-group
+   integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
+   [M,N].  workspace: device buffer of at least
+   ll_gemv_workspace_size(w, act, M) bytes (may be NULL when that is 0);
+   it is overwritten. */
+ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs,
+                            int64_t M, const float* bias, float* y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* [BL "Subgroup-Matrix Multi-row BitLinear Kernel"; BG "Requirements and
+   limits": route prefill elsewhere] Prefill-size product, M >= 1 (meant for
+   M > 16), int8 activations with int8 MFMA and exact int32 accumulation.
+   Format i2_s: y = ((float)acc * xs[m]) * scale.  xq: device int8 [M,K];
+   xs: device fp32 [M]; bias: device fp32 [N] or NULL; y: device fp32 [M,N];
+   acc_out: device int32 [M,N] receiving the raw integer dot (or NULL).
+   workspace as for ll_bitlinear_gemv with ll_gemm_workspace_size. */
+size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M);
+ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,
+                            const float* bias, float* y, int32_t* acc_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWBIT_H */

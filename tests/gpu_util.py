@@ -1,0 +1,45 @@
+"""Helpers for the GPU parity tests: seeded inputs (binary_bit_weight_amd.synth),
+library calls through the C ABI (binary_bit_weight_amd.lowbit) and the CPU
+oracle on the same inputs."""
+import sys
+
+import numpy as np
+
+import oracle
+from binary_bit_weight_amd import lowbit as L
+from binary_bit_weight_amd import synth
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def announce(*parts):
+    """Names the case about to touch the GPU (flushed before the launch)."""
+    print("[gpu case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def f32_tol_ok(y_gpu, y_ref, tsum):
+    """The fp32 bound |y_gpu - y_ref| <= 1e-5 * T + 1e-6 (T = scale * sum|x|
+    for i2_s, sum_b |s_b| * sum_{k in b} |x| for TQ2_0)."""
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = 1e-5 * tsum + 1e-6
+    bad = err > bound
+    return (not bad.any()), float((err / bound).max())
+
+
+def make_i2s(seed, N, K, scale=None, p0=0.4):
+    w = synth.ternary(seed, N, K, p0)
+    if scale is None:
+        scale = float(synth.uniform_f32(seed + 1, 1, 0.01, 0.1)[0])
+    packed = L.ll_pack_i2s(w, scale)
+    return w, np.float32(scale), packed
+
+
+def make_tq2(seed, N, K):
+    w = synth.ternary(seed, N, K)
+    sc = synth.uniform_f16_bits(seed + 1, N * K // 256, 0.005, 0.05)
+    blocks = L.ll_pack_tq2(w, sc)
+    return w, sc, blocks

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Integer-activation paths must be bit-exact; fp32
+activation paths must satisfy |y_gpu - y_ref| <= 1e-5 * T + 1e-6.
+
+Small shapes are compared element by element (they still span several
+tiles and a ragged tail); the full configuration sizes are compared on
+sampled output rows (always including the first and the last row), in the
+launch configuration the benchmark times."""
+import numpy as np
+import pytest
+
+import oracle
+from binary_bit_weight_amd import lowbit as L
+from binary_bit_weight_amd import synth
+from gpu_util import announce, f32_tol_ok, make_i2s, make_tq2, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(seed, M, K):
+    return synth.normal_f32(seed, M, K)
+
+
+# ------------------------------------------------------------------ quantize
+@pytest.mark.parametrize("M,K,dtype", [(1, 512, "f32"), (7, 2560, "f32"), (512, 2560, "bf16"), (512, 6912, "bf16"),
+                                       (3, 1000, "f32"), (5, 1001, "bf16"), (16, 5120, "f32")])
+def test_quantize_bitexact(M, K, dtype):
+    t = torch()
+    announce("quantize", M, K, dtype)
+    if dtype == "bf16":
+        xb = synth.normal_bf16_bits(11 + M, M, K)
+        xb[0, :] = 0                                   # zero token
+        x = t.from_numpy(xb.view(np.int16)).cuda().view(t.bfloat16)
+        q_ref, s_ref = oracle.quantize_bf16(xb)
+    else:
+        xf = _x(12 + M, M, K)
+        xf[-1, :] = 0.0
+        if K >= 8:
+            xf[0, :4] = [127.0, 2.5, -3.5, 0.5]        # exact ties when absmax is 127
+            xf[0, 4:] = np.clip(xf[0, 4:], -100, 100)
+        x = t.from_numpy(xf).cuda()
+        q_ref, s_ref = oracle.quantize_f32(xf)
+    xq, xs = L.quantize(x)
+    t.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ i2_s, fp32 activations
+I2S_F32_SMALL = [(256, 512, 1), (37, 384, 1), (16, 128, 1), (1, 128, 1), (100, 640, 2), (77, 512, 5),
+                 (64, 256, 6), (50, 384, 11), (33, 512, 16), (129, 1024, 3)]
+
+
+@pytest.mark.parametrize("N,K,M", I2S_F32_SMALL)
+def test_i2s_gemv_f32_small(N, K, M):
+    t = torch()
+    w, scale, packed = make_i2s(100 + N + K + M, N, K, scale=0.0625 if (N, K) == (256, 512) else None)
+    x = _x(200 + N + M, M, K)
+    bias = synth.uniform_f32(300 + N, N, -1, 1) if M == 2 else None
+    announce("i2s gemv f32", N, K, M)
+    W = L.upload_i2s(packed, N, K)
+    y = L.gemv(W, t.from_numpy(x).cuda(), bias=None if bias is None else t.from_numpy(bias).cuda())
+    y = y.cpu().numpy()
+    y_ref, tsum = oracle.i2s_gemv_f32(packed, N, K, x)
+    if bias is not None:
+        y_ref = y_ref + bias.astype(np.float64)[None, :]
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
+    assert ok, "worst error / bound = %.3f" % worst
+
+
+I2S_DECODE = [(2560, 2560, 201), (6912, 2560, 205), (2560, 6912, 207)]
+
+
+@pytest.mark.parametrize("N,K,seed", I2S_DECODE)
+def test_i2s_gemv_f32_decode_full(N, K, seed):
+    t = torch()
+    w, scale, packed = make_i2s(seed, N, K)
+    x = _x(seed + 50, 1, K)
+    announce("i2s gemv f32 full", N, K)
+    W = L.upload_i2s(packed, N, K)
+    y = L.gemv(W, t.from_numpy(x).cuda()).cpu().numpy()
+    rows = synth.sample_rows(seed, N, 96)
+    y_ref, tsum = oracle.i2s_gemv_f32(packed, N, K, x, rows)
+    ok, worst = f32_tol_ok(y[:, rows], y_ref, tsum)
+    assert ok, "worst error / bound = %.3f" % worst
+
+
+def test_i2s_gemv_f32_closed_forms():
+    """One-hot rows locate every k end to end; all-zero rows give exactly 0."""
+    t = torch()
+    K = 512
+    N = 128
+    w = np.zeros((N, K), np.int8)
+    ks = np.arange(N) * 4 + 1
+    w[np.arange(N), ks] = np.where(np.arange(N) % 2 == 0, 1, -1)
+    w[-1] = 0
+    packed = L.ll_pack_i2s(w, 1.0)
+    x = _x(77, 1, K)
+    announce("i2s gemv onehot")
+    y = L.gemv(L.upload_i2s(packed, N, K), t.from_numpy(x).cuda()).cpu().numpy()[0]
+    expect = np.where(np.arange(N) % 2 == 0, 1.0, -1.0) * x[0, ks]
+    expect[-1] = 0.0
+    assert np.array_equal(y, expect.astype(np.float32))
+
+
+def test_i2s_gemv_f32_deterministic():
+    t = torch()
+    N, K = 1000, 2560
+    _, _, packed = make_i2s(5, N, K)
+    x = t.from_numpy(_x(6, 1, K)).cuda()
+    W = L.upload_i2s(packed, N, K)
+    announce("i2s gemv determinism")
+    a = L.gemv(W, x).cpu().numpy()
+    b = L.gemv(W, x).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ TQ2_0, fp32 activations
+@pytest.mark.parametrize("N,K,M", [(17, 256, 1), (100, 512, 8), (40, 768, 16), (6, 1024, 3), (256, 2560, 1)])
+def test_tq2_gemv_f32_small(N, K, M):
+    t = torch()
+    w, sc, blocks = make_tq2(400 + N + M, N, K)
+    x = _x(500 + N + M, M, K)
+    announce("tq2 gemv f32", N, K, M)
+    W = L.upload_tq2(blocks, N, K)
+    y = L.gemv(W, t.from_numpy(x).cuda()).cpu().numpy()
+    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x)
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
+    assert ok, "worst error / bound = %.3f" % worst
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_tq2_gemv_f32_full(M):
+    t = torch()
+    N, K = 6912, 2560
+    w, sc, blocks = make_tq2(301, N, K)
+    x = _x(302 + M, M, K)
+    announce("tq2 gemv f32 full", M)
+    W = L.upload_tq2(blocks, N, K)
+    y = L.gemv(W, t.from_numpy(x).cuda()).cpu().numpy()
+    rows = synth.sample_rows(301, N, 64)
+    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x, rows)
+    ok, worst = f32_tol_ok(y[:, rows], y_ref, tsum)
+    assert ok, "worst error / bound = %.3f" % worst
+
+
+# ------------------------------------------------------------------ i2_s, int8 activations (GEMM)
+def _i2s_i8_case(N, K, M, seed, rows=None, bias=False):
+    t = torch()
+    w, scale, packed = make_i2s(seed, N, K)
+    xb = synth.normal_bf16_bits(seed + 3, M, K)
+    q, s = oracle.quantize_bf16(xb)
+    W = L.upload_i2s(packed, N, K)
+    b = synth.uniform_f32(seed + 4, N, -1, 1) if bias else None
+    y, acc = L.gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(),
+                    bias=None if b is None else t.from_numpy(b).cuda(), want_acc=True)
+    y = y.cpu().numpy()
+    acc = acc.cpu().numpy()
+    y_ref, acc_ref = oracle.i2s_gemm_i8(packed, N, K, q, s, rows)
+    if rows is not None:
+        y, acc = y[:, rows], acc[:, rows]
+    if b is not None:
+        bb = b if rows is None else b[rows]
+        y_ref = (y_ref + bb[None, :]).astype(np.float32)
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,M", [(77, 384, 65), (128, 256, 128), (200, 512, 17), (33, 128, 1), (130, 640, 129),
+                                   (5, 2560, 300)])
+def test_i2s_gemm_i8_small(N, K, M):
+    announce("i2s gemm i8", N, K, M)
+    _i2s_i8_case(N, K, M, 600 + N + M, bias=(M == 65))
+
+
+@pytest.mark.parametrize("N,K", [(6912, 2560), (2560, 6912)])
+def test_i2s_gemm_i8_prefill_full(N, K):
+    announce("i2s gemm i8 full", N, K)
+    _i2s_i8_case(N, K, 512, 401 if N == 6912 else 402, rows=synth.sample_rows(7, N, 48))
+
+
+def test_i2s_gemv_i8_matches_gemm():
+    """The int8 decode entry point (M <= 16) gives the same bits as the oracle."""
+    t = torch()
+    N, K, M = 300, 1024, 4
+    w, scale, packed = make_i2s(9, N, K)
+    q, s = oracle.quantize_f32(_x(10, M, K))
+    W = L.upload_i2s(packed, N, K)
+    announce("i2s gemv i8")
+    y = L.gemv(W, t.from_numpy(q).cuda(), xs=t.from_numpy(s).cuda()).cpu().numpy()
+    y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
