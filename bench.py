@@ -1,0 +1,236 @@
+"""Benchmark of the packed low-bit BitLinear hot path on one MI355X.
+
+Headline workload (one "step"): an i2_s BitLinear decode step of a
+30-layer, hidden-2560 BitNet-2B-like stack at M = 1 with fp32 activations --
+per layer Q, K, V, O (2560 x 2560), up and gate (6912 x 2560) and down
+(2560 x 6912), each with its own synthetic activation (Q/K/V share one,
+up/gate share one).  The 210 products of a step run as one prepared batch
+(two launches: activation layout + product).  The metric is effective
+weight bandwidth: packed bytes read per step (codes plus the 4-byte tail
+scale of each matrix, 594.7 MB, more than twice the 256 MiB Infinity Cache)
+divided by the step time.
+
+The JSON line also carries the roofline of the dominant kernel (the batched
+product, timed live with HIP events on its stream), the CPU oracle timed on a
+bounded sample (one layer's seven products, repeated), and extras: single-call
+per-matrix GEMV times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM
+(TOPS against the int8 matrix-core peak).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores, published (POP/s x 1000)
+LAYERS = 30
+HIDDEN, FFN = 2560, 6912
+ROLES = [("q", HIDDEN, HIDDEN, 0), ("k", HIDDEN, HIDDEN, 0), ("v", HIDDEN, HIDDEN, 0), ("o", HIDDEN, HIDDEN, 1),
+         ("up", FFN, HIDDEN, 2), ("gate", FFN, HIDDEN, 2), ("down", HIDDEN, FFN, 3)]   # (name, N, K, x slot)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def build_decode_step(L, synth, torch, dev):
+    """Seven distinct packed matrices (one per role, seeds 201..207), each
+    copied to LAYERS distinct device buffers; activations N(0,1) per layer
+    and slot."""
+    packed = {}
+    for i, (name, N, K, _) in enumerate(ROLES):
+        w = synth.ternary(201 + i, N, K)
+        scale = float(synth.uniform_f32(211 + i, 1, 0.01, 0.1)[0])
+        packed[name] = (L.ll_pack_i2s(w, scale), N, K)
+    items, weight_bytes, keep = [], 0, []
+    for layer in range(LAYERS):
+        xs = [torch.from_numpy(synth.normal_f32(1000 + 4 * layer + s, 1, HIDDEN if s != 3 else FFN)).to(dev)
+              for s in range(4)]
+        keep.append(xs)
+        for name, N, K, slot in ROLES:
+            p, _, _ = packed[name]
+            W = L.upload_i2s(p, N, K, dev)
+            y = torch.empty((1, N), dtype=torch.float32, device=dev)
+            items.append((W, xs[slot], None, y))
+            weight_bytes += p.size
+    return packed, items, weight_bytes
+
+
+def time_events(torch, fn, reps, stream):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(oracle, synth, packed, budget_s=12.0):
+    """The oracle (single thread, fp64, decoding every weight from the packed
+    bytes) on one layer's seven products, repeated until budget_s elapses."""
+    xs = [synth.normal_f32(9000 + s, 1, HIDDEN if s != 3 else FFN) for s in range(4)]
+    done_bytes, t0, layers = 0, time.perf_counter(), 0
+    while True:
+        for name, N, K, slot in ROLES:
+            p, _, _ = packed[name]
+            oracle.i2s_gemv_f32(p, N, K, xs[slot])
+            done_bytes += p.size
+        layers += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full layer(s) of the decode step (7 i2_s GEMVs, %.1f MB) on one host core, %.1f s"
+                      % (layers, done_bytes / 1e6, dt)}
+
+
+def extras_single(L, synth, torch, dev, stream):
+    out = {}
+    for name, N, K in [("2560x2560", 2560, 2560), ("6912x2560", 6912, 2560), ("2560x6912", 2560, 6912)]:
+        w = synth.ternary(5, N, K)
+        p = L.ll_pack_i2s(w, 0.05)
+        # rotate over enough copies to exceed 2 x 256 MiB
+        reps = max(1, int(np.ceil(2 ** 29 / p.size)))
+        Ws = [L.upload_i2s(p, N, K, dev) for _ in range(reps)]
+        x = torch.from_numpy(synth.normal_f32(6, 1, K)).to(dev)
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, 1),), dtype=torch.uint8, device=dev)
+        it = iter(range(10 ** 9))
+
+        def one():
+            W = Ws[next(it) % reps]
+            L.ll_bitlinear_gemv(W, L.LL_ACT_F32, x, None, 1, None, y, ws, stream)
+        for _ in range(reps):
+            one()
+        ms = time_events(torch, one, 2 * reps, stream)
+        out["i2s_gemv_f32_single_call_" + name] = {"us": round(ms * 1e3, 2),
+                                                   "GB_s": round(p.size / (ms * 1e-3) / 1e9, 1)}
+    # TQ2_0 small batch, N=6912, K=2560
+    N, K = 6912, 2560
+    w = synth.ternary(301, N, K)
+    sc = synth.uniform_f16_bits(302, N * K // 256, 0.005, 0.05)
+    blocks = L.ll_pack_tq2(w, sc)
+    reps = max(1, int(np.ceil(2 ** 29 / blocks.size)))
+    Ws = [L.upload_tq2(blocks, N, K, dev) for _ in range(reps)]
+    for M in (1, 8, 16):
+        x = torch.from_numpy(synth.normal_f32(303, M, K)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, M),), dtype=torch.uint8, device=dev)
+        it = iter(range(10 ** 9))
+
+        def one():
+            L.ll_bitlinear_gemv(Ws[next(it) % reps], L.LL_ACT_F32, x, None, M, None, y, ws, stream)
+        for _ in range(reps):
+            one()
+        ms = time_events(torch, one, 2 * reps, stream)
+        out["tq2_gemv_f32_single_call_6912x2560_M%d" % M] = {
+            "us": round(ms * 1e3, 2), "GB_s": round(blocks.size / (ms * 1e-3) / 1e9, 1),
+            "GFLOP_s": round(2 * M * N * K / (ms * 1e-3) / 1e9, 1)}
+    # int8 prefill GEMM, M=512 (bf16 activations quantized per token)
+    for N, K in [(6912, 2560), (2560, 6912)]:
+        w = synth.ternary(401, N, K)
+        p = L.ll_pack_i2s(w, 0.05)
+        W = L.upload_i2s(p, N, K, dev)
+        xb = torch.from_numpy(synth.normal_bf16_bits(402, 512, K).view(np.int16)).to(dev).view(torch.bfloat16)
+        xq, xsc = L.quantize(xb, stream)
+        y = torch.empty((512, N), dtype=torch.float32, device=dev)
+
+        def g():
+            L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, None, stream)
+
+        def q():
+            L.ll_quantize_act(xb, xq, xsc, stream)
+        for _ in range(3):
+            g()
+        ms = time_events(torch, g, 20, stream)
+        msq = time_events(torch, q, 20, stream)
+        tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
+        out["i2s_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
+                                                   "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                                                   "quantize_us": round(msq * 1e3, 2)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the product shards by output "
+              "rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from binary_bit_weight_amd import lowbit as L
+    from binary_bit_weight_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log("building the decode step")
+    packed, items, weight_bytes = build_decode_step(L, synth, torch, dev)
+    plan = L.GemvPlan(items, 1)
+    log("plan: %d products, %d tiles, %.1f MB of packed weights" % (plan.plan.count, plan.plan.tiles, weight_bytes / 1e6))
+
+    def step():
+        plan.prepare(stream)
+        plan.product(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.prepare(stream)
+        ev[i][0].record(stream)
+        plan.product(stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    prod_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = weight_bytes / (prod_ms * 1e-3) / 1e9
+    log("step %.3f ms (%.1f GB/s); product kernel %.3f ms (%.1f GB/s)" % (ms_per_step, value, prod_ms, achieved))
+
+    res = {
+        "metric": "M=1 effective weight GB/s (% HBM peak); M=512 int8 TOPS (% MFMA peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "i2_s BitLinear decode step, M=1, fp32 x ~ N(0,1): 30 layers x (Q,K,V,O 2560x2560; "
+                               "up,gate 6912x2560; down 2560x6912), ternary P(0)=0.4, per-tensor fp32 scale "
+                               "~U(0.01,0.1); 210 products as one prepared batch (2 launches)",
+                   "M": 1, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN,
+                   "weight_bytes_per_step": int(weight_bytes)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_f32_batch_kernel<i2_s,1>", "kernel_ms": round(prod_ms, 4)},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(oracle, synth, packed)
+    if not args.no_extras:
+        log("extras")
+        res["extras"] = extras_single(L, synth, torch, dev, stream)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+// Prepared batches of decode products (ll_gemv_plan_* in lowbit.h): the
+// host validates every item once and lays out device tables inside the
+// plan memory; every later run costs two launches: one preparing the
+// operands of every distinct activation (into the plan memory), one walking
+// the table of products.  M <= 3 uses the int8-plane kernels, larger M the
+// bf16-plane kernels.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+    bool planes = false;
+    size_t prob_off = 0, prep_off = 0, frag_off = 0, total = 0;
+    std::vector<int> prep_of;          // item -> distinct activation index
+    std::vector<const void*> xs;       // distinct activations
+    std::vector<int64_t> xk;           // their K
+    std::vector<size_t> frag_at;       // byte offset of each activation's operands
+    std::vector<int64_t> ent0;         // bf16 path: first fragment entry of each activation
+    int64_t entries = 0, tiles = 0, kmax = 0;
+};
+
+ll_status check_item(const ll_gemv_item& it, int i, int32_t act, int64_t M, int32_t fmt0) {
+    const ll_weights& w = it.w;
+    if (w.fmt != fmt0) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d has a different format", i);
+    if (w.N <= 0 || w.K <= 0) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: N and K must be positive", i);
+    if (w.N > (int64_t(1) << 31) - 1 || w.K > (int64_t(1) << 24))
+        return ll::failf(LL_ERANGE, "ll_gemv_plan: item %d: N must be < 2^31 and K <= 2^24", i);
+    if (!w.codes || !it.x || !it.y) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: NULL codes, x or y", i);
+    if (!aligned(w.codes, 16) || !aligned(it.x, 16))
+        return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: codes and x must be 16-byte aligned", i);
+    if (!aligned(it.y, 4) || (it.bias && !aligned(it.bias, 4)))
+        return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: y / bias must be 4-byte aligned", i);
+    if (act != LL_ACT_F32) return ll::fail(LL_EINVAL, "ll_gemv_plan: only fp32 activations are supported");
+    if (M < 1 || M > 16) return ll::fail(LL_ESHAPE, "ll_gemv_plan: M must be in [1, 16]");
+    if (w.fmt == LL_FMT_I2S) {
+        if (w.K % 128) return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: i2_s needs K %% 128 == 0", i);
+    } else if (w.fmt == LL_FMT_TQ2_0) {
+        if (w.K % 256) return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: TQ2_0 needs K %% 256 == 0", i);
+        if (!w.scales) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: TQ2_0 scales pointer is NULL", i);
+        if (!aligned(w.scales, 2)) return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: scales must be 2-byte aligned", i);
+    } else {
+        return ll::fail(LL_EINVAL, "ll_gemv_plan: fp32 activations need format i2_s or TQ2_0");
+    }
+    return LL_OK;
+}
+
+ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M, Layout& L) {
+    if (!items || count <= 0) return ll::fail(LL_EINVAL, "ll_gemv_plan: no items");
+    for (int i = 0; i < count; ++i) {
+        ll_status st = check_item(items[i], i, act, M, items[0].w.fmt);
+        if (st) return st;
+    }
+    L.planes = M <= llk::kPlanesMaxM;
+    L.prep_of.assign(size_t(count), -1);
+    for (int i = 0; i < count; ++i) {
+        L.kmax = std::max(L.kmax, items[i].w.K);
+        int found = -1;
+        for (size_t j = 0; j < L.xs.size(); ++j)
+            if (L.xs[j] == items[i].x && L.xk[j] == items[i].w.K) { found = int(j); break; }
+        if (found < 0) {
+            found = int(L.xs.size());
+            L.xs.push_back(items[i].x);
+            L.xk.push_back(items[i].w.K);
+        }
+        L.prep_of[size_t(i)] = found;
+        if (L.planes) {
+            const int64_t rows = llk::planes_batch_rows();
+            L.tiles += (items[i].w.N + rows - 1) / rows;          // workgroups
+        } else {
+            L.tiles += (items[i].w.N + 15) / 16;                  // 16-row tiles
+        }
+    }
+    const size_t prob_sz = L.planes ? llk::planes_prob_bytes() : llk::batch_prob_bytes();
+    const size_t prep_sz = L.planes ? llk::planes_prep_bytes() : llk::batch_prep_bytes();
+    L.prob_off = 0;
+    L.prep_off = round_up(size_t(count) * prob_sz, 256);
+    L.frag_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
+    size_t at = L.frag_off;
+    for (size_t j = 0; j < L.xs.size(); ++j) {
+        L.frag_at.push_back(at);
+        L.ent0.push_back(L.entries);
+        const size_t bytes = L.planes ? llk::planes_workspace(M, L.xk[j]) : llk::gemv_f32_workspace(M, L.xk[j]);
+        if (!L.planes) L.entries += int64_t(bytes / 16);
+        at = round_up(at + bytes, 256);
+    }
+    L.total = at;
+    if (L.tiles > (int64_t(1) << 31) - 1 || L.entries > (int64_t(1) << 40) || L.xs.size() > 65535)
+        return ll::fail(LL_ERANGE, "ll_gemv_plan: batch too large");
+    return LL_OK;
+}
+
+ll_status check_plan(const ll_gemv_plan* p) {
+    if (!p || !p->mem || !p->prob_table || !p->prep_table || p->count <= 0 || p->nprep <= 0)
+        return ll::fail(LL_EINVAL, "ll_gemv_plan: plan not initialised");
+    return LL_OK;
+}
+
+ll_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return LL_OK;
+    return ll::failf(LL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ll_gemv_plan_bytes(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M) {
+    Layout L;
+    if (plan_layout(items, count, act, M, L)) return size_t(-1);
+    return L.total;
+}
+
+ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M, void* mem, size_t bytes,
+                            ll_gemv_plan* plan) {
+    if (!plan) return ll::fail(LL_EINVAL, "ll_gemv_plan_init: plan is NULL");
+    Layout L;
+    ll_status st = plan_layout(items, count, act, M, L);
+    if (st) return st;
+    if (!mem || bytes < L.total) return ll::failf(LL_EWORKSPACE, "ll_gemv_plan_init: %zu device bytes required", L.total);
+    if (!aligned(mem, 16)) return ll::fail(LL_EALIGN, "ll_gemv_plan_init: mem must be 16-byte aligned");
+    char* base = static_cast<char*>(mem);
+    std::vector<char> host(L.frag_off, 0);
+    int64_t first = 0;
+    for (int i = 0; i < count; ++i) {
+        const ll_gemv_item& it = items[i];
+        char* ops = base + L.frag_at[size_t(L.prep_of[size_t(i)])];
+        if (L.planes) {
+            llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
+                                  it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
+            first += (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
+        } else {
+            llk::fill_batch_prob(host.data() + L.prob_off + size_t(i) * llk::batch_prob_bytes(), it.w.codes,
+                                 it.w.scales, it.bias, it.y, ops, it.w.N, it.w.K, first);
+            first += (it.w.N + 15) / 16;
+        }
+    }
+    int64_t prep_wg = 0;
+    for (size_t j = 0; j < L.xs.size(); ++j) {
+        const float* x = static_cast<const float*>(L.xs[j]);
+        if (L.planes) {
+            llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
+                                  L.xk[j], prep_wg);
+            prep_wg += llk::planes_prep_wgs(M, L.xk[j]);
+        } else
+            llk::fill_batch_prep(host.data() + L.prep_off + j * llk::batch_prep_bytes(), x, base + L.frag_at[j],
+                                 L.xk[j], L.ent0[j]);
+    }
+    if (L.planes) L.entries = prep_wg;          // preparation workgroups of the plane path
+    st = hip_status(hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice), "ll_gemv_plan_init");
+    if (st) return st;
+    ll_gemv_plan p;
+    std::memset(&p, 0, sizeof p);
+    p.mem = mem;
+    p.bytes = L.total;
+    p.count = count;
+    p.nprep = int32_t(L.xs.size());
+    p.act = act;
+    p.fmt = items[0].w.fmt;
+    p.M = M;
+    p.tiles = L.tiles;
+    p.prep_entries = L.entries;
+    p.kmax = L.kmax;
+    p.prob_table = base + L.prob_off;
+    p.prep_table = base + L.prep_off;
+    *plan = p;
+    return LL_OK;
+}
+
+ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
+    ll_status st = check_plan(plan);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->M <= llk::kPlanesMaxM)
+        return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M,
+                                                        plan->prep_entries, s),
+                          "ll_gemv_plan_prepare");
+    return hip_status(llk::launch_gemv_f32_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M,
+                                                      plan->prep_entries, s),
+                      "ll_gemv_plan_prepare");
+}
+
+ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
+    ll_status st = check_plan(plan);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->M <= llk::kPlanesMaxM)
+        return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->count, plan->fmt, plan->M,
+                                                           plan->tiles, s),
+                          "ll_gemv_plan_product");
+    return hip_status(llk::launch_gemv_f32_batch_product(plan->prob_table, plan->count, plan->fmt, plan->M,
+                                                         plan->tiles, s),
+                      "ll_gemv_plan_product");
+}
+
+ll_status ll_gemv_plan_run(const ll_gemv_plan* plan, void* stream) {
+    ll_status st = ll_gemv_plan_prepare(plan, stream);
+    if (st) return st;
+    return ll_gemv_plan_product(plan, stream);
+}
+
+}  // extern "C"

@@ -14,13 +14,22 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 constexpr int kWave = 64;
 
+// Global-memory views.  Pointers that a kernel reads from a table in memory
+// are generic to the compiler, which then emits FLAT instructions; a FLAT
+// load also counts against the LDS wait counter, so every LDS wait would
+// stall on outstanding weight prefetches.  Loads go through explicitly
+// global (address space 1) pointers instead.
+typedef __attribute__((address_space(1))) const i32x4 gi32x4;
+typedef __attribute__((address_space(1))) const int32_t gint32;
+
 // 16-byte global load / store through the vector memory path.
-__device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
-__device__ __forceinline__ void st16(void* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+// (C-style casts: they are address-space conversions, which reinterpret_cast
+// does not perform.)
+__device__ __forceinline__ i32x4 ld16(const void* p) { return *(gi32x4*)p; }
+__device__ __forceinline__ void st16(void* p, i32x4 v) { *(__attribute__((address_space(1))) i32x4*)p = v; }
 // Streaming (non-temporal) 16-byte load for weights that are read once.
-__device__ __forceinline__ i32x4 ld16_stream(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
-}
+__device__ __forceinline__ i32x4 ld16_stream(const void* p) { return __builtin_nontemporal_load((gi32x4*)p); }
+__device__ __forceinline__ int32_t ld32(const void* p) { return *(gint32*)p; }
 
 // Butterfly sum / max over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {

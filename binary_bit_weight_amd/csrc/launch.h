@@ -25,3 +25,35 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
                               int32_t* acc_out, hipStream_t stream);
 
 }  // namespace llk
+
+namespace llk {
+// Prepared batch of fp32-activation decode products (device tables built by
+// the C-ABI layer; see ll_gemv_plan_init).
+size_t batch_prob_bytes();
+size_t batch_prep_bytes();
+void fill_batch_prob(void* dst, const void* codes, const void* scales, const float* bias, float* y, const void* afrag,
+                     int64_t N, int64_t K, int64_t tile0);
+void fill_batch_prep(void* dst, const float* x, void* afrag, int64_t K, int64_t ent0);
+hipError_t launch_gemv_f32_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, int64_t entries,
+                                      hipStream_t stream);
+hipError_t launch_gemv_f32_batch_product(const void* prob_table, int count, int fmt, int64_t M, int64_t tiles,
+                                         hipStream_t stream);
+
+// 1 <= M <= 3: activations split into int8 planes (one preparation launch),
+// int8 matrix cores with exact int32 accumulation (gemv_planes.hip).
+constexpr int64_t kPlanesMaxM = 3;
+size_t planes_workspace(int64_t M, int64_t K);
+int64_t planes_batch_rows();
+size_t planes_prob_bytes();
+size_t planes_prep_bytes();
+void fill_planes_prob(void* dst, const void* codes, const void* scales, const void* ws, const float* bias, float* y,
+                      int64_t N, int64_t K, int64_t wg0);
+void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K, int64_t wg0);
+int64_t planes_prep_wgs(int64_t M, int64_t K);
+hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K, const float* x,
+                              int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
+hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, int64_t wgs,
+                                    hipStream_t stream);
+hipError_t launch_planes_batch_product(const void* prob_table, int count, int fmt, int64_t M, int64_t wgs,
+                                       hipStream_t stream);
+}  // namespace llk

@@ -302,3 +302,55 @@ def gemm(w: Weights, xq, xs, bias=None, want_acc=False, stream=None):
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=xq.device) if nws else None
     ll_bitlinear_gemm(w, xq, xs, M, bias, y, acc, ws, stream)
     return y, acc
+
+
+# ------------------------------------------------------------------ prepared batches
+class ll_gemv_item(C.Structure):
+    _fields_ = [("w", ll_weights), ("x", C.c_void_p), ("bias", C.c_void_p), ("y", C.c_void_p)]
+
+
+class ll_gemv_plan(C.Structure):
+    _fields_ = [("mem", C.c_void_p), ("bytes", C.c_size_t), ("count", C.c_int32), ("nprep", C.c_int32),
+                ("act", C.c_int32), ("fmt", C.c_int32), ("M", C.c_int64), ("tiles", C.c_int64),
+                ("prep_entries", C.c_int64), ("kmax", C.c_int64), ("prob_table", C.c_void_p),
+                ("prep_table", C.c_void_p)]
+
+
+SIGNATURES.update({
+    "ll_gemv_plan_bytes": (_SZ, [_P, _I32, _I32, _I64]),
+    "ll_gemv_plan_init": (C.c_int, [_P, _I32, _I32, _I64, _P, _SZ, _P]),
+    "ll_gemv_plan_run": (C.c_int, [_P, _P]),
+    "ll_gemv_plan_prepare": (C.c_int, [_P, _P]),
+    "ll_gemv_plan_product": (C.c_int, [_P, _P]),
+})
+
+
+class GemvPlan:
+    """A prepared batch of fp32-activation decode products (ll_gemv_plan_*).
+
+    items: list of (Weights, x, bias_or_None, y) with GPU tensors; the plan
+    keeps them alive.  run() = prepare() + product()."""
+
+    def __init__(self, items, M):
+        import torch
+        self.items = list(items)
+        arr = (ll_gemv_item * len(self.items))()
+        for i, (w, x, b, y) in enumerate(self.items):
+            arr[i] = ll_gemv_item(w.desc, _dev(x), _dev(b), _dev(y))
+        self._arr = arr
+        self.plan = ll_gemv_plan()
+        n = lib().ll_gemv_plan_bytes(arr, len(self.items), LL_ACT_F32, M)
+        if n == 2 ** 64 - 1:   # invalid items: let init report which one
+            _check(lib().ll_gemv_plan_init(arr, len(self.items), LL_ACT_F32, M, None, 0, C.byref(self.plan)))
+        self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=self.items[0][1].device)
+        _check(lib().ll_gemv_plan_init(arr, len(self.items), LL_ACT_F32, M, _dev(self.mem), int(n),
+                                       C.byref(self.plan)))
+
+    def prepare(self, stream=None):
+        _check(lib().ll_gemv_plan_prepare(C.byref(self.plan), _stream(stream)))
+
+    def product(self, stream=None):
+        _check(lib().ll_gemv_plan_product(C.byref(self.plan), _stream(stream)))
+
+    def run(self, stream=None):
+        _check(lib().ll_gemv_plan_run(C.byref(self.plan), _stream(stream)))

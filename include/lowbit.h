@@ -186,6 +186,53 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
                             int64_t M, const float* bias, float* y,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ */
+/* Prepared batch of decode products                                     */
+/* ------------------------------------------------------------------ */
+
+/* [BL "High-Level API" / layer header: PreparedDispatch fast path replayed
+   per forward call; "Execute forward pass" for each layer] Many independent
+   decode products y_i = W_i x_i (for example every BitLinear of a decode
+   step) prepared once and then run with two launches per call: one that
+   lays every distinct activation out as matrix-core operands, one that
+   walks a device-resident table of all products.  All items share act,
+   format and M (1 <= M <= 16); N and K may differ.  Only act == LL_ACT_F32
+   with i2_s or TQ2_0 is supported.  Items with the same x pointer and K
+   share one activation layout. */
+typedef struct {
+    ll_weights w;        /* packed weights (device pointers, as for ll_bitlinear_gemv) */
+    const void* x;       /* device fp32 [M, K] */
+    const float* bias;   /* device fp32 [N] or NULL */
+    float* y;            /* device fp32 [M, N] */
+} ll_gemv_item;
+
+typedef struct {
+    void* mem;           /* device memory given to ll_gemv_plan_init (caller-owned) */
+    size_t bytes;
+    int32_t count, nprep, act, fmt;
+    int64_t M, tiles, prep_entries, kmax;
+    void* prob_table;    /* inside mem */
+    void* prep_table;    /* inside mem; NULL when no preparation launch is needed (M <= 5) */
+} ll_gemv_plan;
+
+/* Device bytes ll_gemv_plan_init needs for these items ((size_t)-1 for
+   invalid arguments). */
+size_t ll_gemv_plan_bytes(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M);
+/* Validates every item (same rules and status codes as ll_bitlinear_gemv),
+   writes the product and activation tables into mem with a synchronous
+   host-to-device copy and fills *plan.  mem (16-byte aligned, at least
+   ll_gemv_plan_bytes) must stay allocated, and every pointer in the items
+   valid, for as long as the plan is run.  This is the only call here that
+   synchronizes. */
+ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M,
+                            void* mem, size_t bytes, ll_gemv_plan* plan);
+/* Both launches: ll_gemv_plan_prepare, then ll_gemv_plan_product. */
+ll_status ll_gemv_plan_run(const ll_gemv_plan* plan, void* stream);
+/* Lays out the current contents of every x as operands (inside mem). */
+ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream);
+/* The products from the last prepared activations; writes every y. */
+ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
+
 /* [BL "Subgroup-Matrix Multi-row BitLinear Kernel"; BG "Requirements and
    limits": route prefill elsewhere] Prefill-size product, M >= 1 (meant for
    M > 16), int8 activations with int8 MFMA and exact int32 accumulation.

@@ -190,3 +190,46 @@ def test_i2s_gemv_i8_matches_gemm():
     y = L.gemv(W, t.from_numpy(q).cuda(), xs=t.from_numpy(s).cuda()).cpu().numpy()
     y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s)
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ prepared batch
+@pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 4), ("tq2", 1), ("tq2", 16)])
+def test_gemv_plan_matches_oracle(fmt, M):
+    """A prepared batch of products with mixed N and K (some sharing x) against
+    the oracle, row by row, run twice (second run with new x contents)."""
+    t = torch()
+    shapes = [(2560, 2560, 0), (6912, 2560, 0), (2560, 6912, 1), (37, 384 if fmt == "i2s" else 512, 2),
+              (16, 256, 3)]
+    xs_np = {}
+    items, refs = [], []
+    for i, (N, K, slot) in enumerate(shapes):
+        if fmt == "i2s":
+            w, scale, packed = make_i2s(700 + i, N, K)
+            W = L.upload_i2s(packed, N, K)
+        else:
+            w, sc, packed = make_tq2(700 + i, N, K)
+            W = L.upload_tq2(packed, N, K)
+        if slot not in xs_np:
+            xs_np[slot] = (_x(800 + slot, M, K), None)
+        x = xs_np[slot][0]
+        if xs_np[slot][1] is None:
+            xs_np[slot] = (x, t.from_numpy(x).cuda())
+        y = t.empty((M, N), dtype=t.float32, device="cuda")
+        items.append((W, xs_np[slot][1], None, y))
+        refs.append((packed, N, K, slot))
+    announce("gemv plan", fmt, M)
+    plan = L.GemvPlan(items, M)
+    for rnd in range(2):
+        if rnd == 1:
+            for slot, (x, xd) in xs_np.items():
+                x2 = _x(900 + slot, M, x.shape[1])
+                xd.copy_(t.from_numpy(x2))
+                xs_np[slot] = (x2, xd)
+        plan.run()
+        t.cuda.synchronize()
+        for (W, xd, _, y), (packed, N, K, slot) in zip(items, refs):
+            rows = synth.sample_rows(N + rnd, N, 40)
+            fn = oracle.i2s_gemv_f32 if fmt == "i2s" else oracle.tq2_gemv_f32
+            y_ref, tsum = fn(packed, N, K, xs_np[slot][0], rows)
+            ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
+            assert ok, "N=%d K=%d round %d: worst error / bound %.3f" % (N, K, rnd, worst)

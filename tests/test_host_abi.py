@@ -136,8 +136,8 @@ def test_gemv_argument_errors():
     assert _gemv(_w(codes=FAKE + 4)) == -3
     assert _gemv(_w(), x=FAKE + 8) == -3
     assert _gemv(_w(), y=0) == -1
-    assert _gemv(_w(), ws=0) == -5
-    assert _gemv(_w(), wsb=16) == -5
+    assert _gemv(_w(), ws=0) == -5               # fp32 activations need the operand workspace
+    assert _gemv(_w(), M=6, wsb=16) == -5
     assert _gemv(_w(fmt=L.LL_FMT_TQ2_0, scales=0)) == -1
     assert _gemv(_w(fmt=L.LL_FMT_W1, K=256, group=96)) == -2
     assert _gemv(_w(), act=9) == -1
@@ -159,5 +159,8 @@ def test_gemm_and_quantize_argument_errors():
 
 def test_workspace_sizes():
     w = _w(N=6912, K=2560)
-    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) > 0
+    # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + per-block plane sums + exponents
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == (5 * 2560 + 5 * 10 * 4 + 4 + 15) // 16 * 16
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 8) > 0
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 17) == 2 ** 64 - 1
