@@ -20,7 +20,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
     bool planes = false;
-    size_t prob_off = 0, prep_off = 0, frag_off = 0, total = 0;
+    size_t prob_off = 0, prep_off = 0, map_off = 0, frag_off = 0, total = 0;
     std::vector<int> prep_of;          // item -> distinct activation index
     std::vector<const void*> xs;       // distinct activations
     std::vector<int64_t> xk;           // their K
@@ -84,7 +84,8 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     const size_t prep_sz = L.planes ? llk::planes_prep_bytes() : llk::batch_prep_bytes();
     L.prob_off = 0;
     L.prep_off = round_up(size_t(count) * prob_sz, 256);
-    L.frag_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
+    L.map_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
+    L.frag_off = round_up(L.map_off + (L.planes ? size_t(L.tiles) * 4 : 0), 256);
     size_t at = L.frag_off;
     for (size_t j = 0; j < L.xs.size(); ++j) {
         L.frag_at.push_back(at);
@@ -100,7 +101,8 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
 }
 
 ll_status check_plan(const ll_gemv_plan* p) {
-    if (!p || !p->mem || !p->prob_table || !p->prep_table || p->count <= 0 || p->nprep <= 0)
+    if (!p || !p->mem || !p->prob_table || !p->prep_table || p->count <= 0 || p->nprep <= 0 ||
+        (p->M <= llk::kPlanesMaxM && !p->map_table))
         return ll::fail(LL_EINVAL, "ll_gemv_plan: plan not initialised");
     return LL_OK;
 }
@@ -130,6 +132,7 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     if (!aligned(mem, 16)) return ll::fail(LL_EALIGN, "ll_gemv_plan_init: mem must be 16-byte aligned");
     char* base = static_cast<char*>(mem);
     std::vector<char> host(L.frag_off, 0);
+    int32_t* map = reinterpret_cast<int32_t*>(host.data() + L.map_off);
     int64_t first = 0;
     for (int i = 0; i < count; ++i) {
         const ll_gemv_item& it = items[i];
@@ -137,25 +140,25 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
         if (L.planes) {
             llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
                                   it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
-            first += (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
+            const int64_t wgs = (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
+            for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
+            first += wgs;
         } else {
             llk::fill_batch_prob(host.data() + L.prob_off + size_t(i) * llk::batch_prob_bytes(), it.w.codes,
                                  it.w.scales, it.bias, it.y, ops, it.w.N, it.w.K, first);
             first += (it.w.N + 15) / 16;
         }
     }
-    int64_t prep_wg = 0;
     for (size_t j = 0; j < L.xs.size(); ++j) {
         const float* x = static_cast<const float*>(L.xs[j]);
-        if (L.planes) {
+        if (L.planes)
             llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
-                                  L.xk[j], prep_wg);
-            prep_wg += llk::planes_prep_wgs(M, L.xk[j]);
-        } else
+                                  L.xk[j]);
+        else
             llk::fill_batch_prep(host.data() + L.prep_off + j * llk::batch_prep_bytes(), x, base + L.frag_at[j],
                                  L.xk[j], L.ent0[j]);
     }
-    if (L.planes) L.entries = prep_wg;          // preparation workgroups of the plane path
+    if (L.planes) L.entries = int64_t(L.xs.size()) * M;   // preparation workgroups of the plane path
     st = hip_status(hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice), "ll_gemv_plan_init");
     if (st) return st;
     ll_gemv_plan p;
@@ -172,6 +175,7 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     p.kmax = L.kmax;
     p.prob_table = base + L.prob_off;
     p.prep_table = base + L.prep_off;
+    p.map_table = L.planes ? base + L.map_off : nullptr;
     *plan = p;
     return LL_OK;
 }
@@ -181,8 +185,7 @@ ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (plan->M <= llk::kPlanesMaxM)
-        return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M,
-                                                        plan->prep_entries, s),
+        return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M, s),
                           "ll_gemv_plan_prepare");
     return hip_status(llk::launch_gemv_f32_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M,
                                                       plan->prep_entries, s),
@@ -194,7 +197,7 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (plan->M <= llk::kPlanesMaxM)
-        return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->count, plan->fmt, plan->M,
+        return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
                                                            plan->tiles, s),
                           "ll_gemv_plan_product");
     return hip_status(llk::launch_gemv_f32_batch_product(plan->prob_table, plan->count, plan->fmt, plan->M,

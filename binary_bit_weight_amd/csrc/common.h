@@ -21,6 +21,7 @@ constexpr int kWave = 64;
 // global (address space 1) pointers instead.
 typedef __attribute__((address_space(1))) const i32x4 gi32x4;
 typedef __attribute__((address_space(1))) const int32_t gint32;
+typedef __attribute__((address_space(1))) const f32x4 gf32x4;
 
 // 16-byte global load / store through the vector memory path.
 // (C-style casts: they are address-space conversions, which reinterpret_cast
@@ -30,6 +31,7 @@ __device__ __forceinline__ void st16(void* p, i32x4 v) { *(__attribute__((addres
 // Streaming (non-temporal) 16-byte load for weights that are read once.
 __device__ __forceinline__ i32x4 ld16_stream(const void* p) { return __builtin_nontemporal_load((gi32x4*)p); }
 __device__ __forceinline__ int32_t ld32(const void* p) { return *(gint32*)p; }
+__device__ __forceinline__ f32x4 ld16f(const void* p) { return *(gf32x4*)p; }
 
 // Butterfly sum / max over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {

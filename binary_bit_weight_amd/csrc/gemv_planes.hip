@@ -6,11 +6,15 @@
 // where 2^(E-1) <= max|x| < 2^E, q_p are int8 (|q_p| <= 64) and
 // |r| <= 2^(E-41): r0 = x * 2^(6-E), q_p = rint(r_p), r_(p+1) = 128 (r_p - q_p),
 // every step exact in fp32.  The planes are rows of the MFMA operand A.
-// Weights.  Codes are fed as int8 c = w + 1 in {0, 1, 2} (i2_s codes as they
-// are; TQ2_0 codes c' = w mod 4 remapped by c = ((b0 ^ b1) << 1) | !b0 on the
+// Weights.  Codes are fed as c = w + 1 in {0, 1, 2} (i2_s codes as they are;
+// TQ2_0 codes c' = w mod 4 remapped by c = ((b0 ^ b1) << 1) | !b0 on the
 // packed word), so sum w*q = sum c*q - sum q, with the plane sums sum q
-// computed once per token.  Every product and sum is an exact integer in
-// int32; the epilogue forms
+// computed once per token.  A code is not shifted down to bit 0 of its
+// byte: masked in place it is the int8 value c * 4^j (j < 3), so three of
+// the four fields of a word cost one AND each; the MFMAs of each field
+// accumulate separately and are divided by their exact power of two at the
+// end.  Every product and sum is an exact integer in int32; the epilogue
+// forms
 //     y = scale * 2^(E-6) * sum_p 128^-p (acc_p - xsum_p)
 // in fp64 (exact up to the final roundings), so the only deviation from the
 // exact product is the plane truncation r: |y - y_exact| <=
@@ -24,10 +28,10 @@
 // order.  Weight rows are fetched per 1024-k window with loads of 4 rows x
 // 256 contiguous bytes (long runs the memory system serves at full speed,
 // unlike the 16-rows-by-64-bytes shape of the operand) and transposed
-// through padded LDS rows; the window's activation planes are staged in LDS
-// too.  Loads run two windows ahead of the multiply (registers hold the
-// next-but-one window, LDS the next one).  A prepared batch runs many
-// products per launch.
+// through a padded LDS tile private to the wave; the window's activation
+// planes are staged in a shared, double-buffered LDS window, the only thing
+// the workgroup synchronises on.  Loads run two windows ahead of the
+// multiply.  A prepared batch runs many products per launch.
 #include "common.h"
 #include "launch.h"
 
@@ -35,32 +39,43 @@ namespace {
 
 using namespace llk;
 
+#ifndef LL_PLANES_WAVES
+#define LL_PLANES_WAVES 4
+#endif
+#ifndef LL_PLANES_WINK
+#define LL_PLANES_WINK 1024
+#endif
+#ifndef LL_PLANES_NT
+#define LL_PLANES_NT 1
+#endif
+
 constexpr int kP = 5;                     // activation planes
-constexpr int kWaves = 4;                 // 16-row tiles per workgroup
+constexpr int kWaves = LL_PLANES_WAVES;   // 16-row tiles per workgroup
 constexpr int kRows = 16 * kWaves;
-constexpr int kWinK = 1024;               // k per window
+constexpr int kWinK = LL_PLANES_WINK;     // k per window
 constexpr int kWinB = kWinK / 4;          // code bytes per row per window
 constexpr int kWStride = kWinB + 16;      // padded LDS weight row
-constexpr int kWTile = 16 * kWStride;
+constexpr int kWTile = 16 * kWStride;     // one wave's weight tile
 constexpr int kAStride = kWinK + 16;      // padded LDS plane row
-constexpr int kAChunks = 4;               // 16-byte plane chunks per thread per window (<= 1024 / 256)
 
-__host__ __device__ inline int lds_bytes(int M) { return 2 * kWaves * kWTile + 2 * kP * M * kAStride + 64; }
+__host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * kP * M * kAStride; }
 
 // Position of element k inside its 256-element TQ2_0 block in the plane
 // layout: field f = k%4 of byte 16q + 4v + b (k = 64q + 16v + 4b + f) goes to
 // 64f + 16q + 4v + b, so one MFMA (one field) reads 16 consecutive bytes.
 __device__ __forceinline__ int tq2_pos(int e) { return 64 * (e & 3) + 16 * (e >> 6) + 4 * ((e >> 4) & 3) + ((e >> 2) & 3); }
 
-// Workspace layout of one activation: planes [5M][K] | xsum [5M][nblk] | E [M].
+// Workspace layout of one activation:
+//     planes [5M][K] | xsum [5M][nblk] (per 256-k block) | E [M] | xtot [5M] (per row).
 struct PlaneView {
     int8_t* planes;
     int32_t* xsum;
     int32_t* ex;
+    int32_t* xtot;
 };
 __host__ __device__ inline size_t planes_bytes(int64_t M, int64_t K) {
     const int64_t nblk = (K + 255) / 256;
-    return size_t((kP * M * K + 15) / 16 * 16 + kP * M * nblk * 4 + M * 4 + 15) / 16 * 16;
+    return size_t((kP * M * K + 15) / 16 * 16 + kP * M * nblk * 4 + M * 4 + kP * M * 4 + 15) / 16 * 16;
 }
 __host__ __device__ inline PlaneView plane_view(void* base, int64_t M, int64_t K) {
     const int64_t nblk = (K + 255) / 256;
@@ -69,80 +84,153 @@ __host__ __device__ inline PlaneView plane_view(void* base, int64_t M, int64_t K
     v.planes = reinterpret_cast<int8_t*>(p);
     v.xsum = reinterpret_cast<int32_t*>(p + (kP * M * K + 15) / 16 * 16);
     v.ex = v.xsum + kP * M * nblk;
+    v.xtot = v.ex + M;
     return v;
 }
 
 // ---------------------------------------------------------------- activation preparation
-// One workgroup of 256 threads per (256-k block, token): the row maximum
-// (every workgroup of the token reads the whole row, from L2), then the five
-// planes of its block and their sums.
+// One workgroup of 256 threads per token.  Thread t holds elements
+// 4t + 1024i + [0, 4) (float4 loads, all issued before any use), so the
+// 256-k block 4i + wave is held by exactly one wave and its plane sums are
+// wave reductions; the row maximum costs one barrier.  Rows are processed
+// in chunks of kPrepK elements (registers), the maximum over all chunks
+// first.
+constexpr int kPrepIt = 8;                           // float4 per thread per chunk
+constexpr int kPrepK = 1024 * kPrepIt;               // elements per chunk
+
 template <int FMT>
-__device__ __forceinline__ void prep_block(const float* __restrict__ xr, int64_t K, int M, int m, int64_t b,
+__device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t K, int M, int m,
                                            void* __restrict__ ws) {
     __shared__ float smax[4];
-    __shared__ int ssum[4][kP];
+    __shared__ int stot[4][kP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const PlaneView v = plane_view(ws, M, K);
+    int tot[kP] = {0, 0, 0, 0, 0};                   // this wave's share of the row's plane sums
     const int64_t nblk = (K + 255) / 256;
+    const bool vec = (K % 4) == 0;                   // always true for the formats here (K % 128 == 0)
+    auto load_chunk = [&](int64_t k0, f32x4 (&x4)[kPrepIt]) {
+#pragma unroll
+        for (int i = 0; i < kPrepIt; ++i) {
+            const int64_t k = k0 + 1024 * i + 4 * tid;
+            if (vec && k + 3 < K) {
+                x4[i] = ld16f(xr + k);
+            } else {
+                x4[i].x = k < K ? xr[k] : 0.f;
+                x4[i].y = k + 1 < K ? xr[k + 1] : 0.f;
+                x4[i].z = k + 2 < K ? xr[k + 2] : 0.f;
+                x4[i].w = k + 3 < K ? xr[k + 3] : 0.f;
+            }
+        }
+    };
     float a = 0.0f;
-    for (int64_t k = tid; k < K; k += 256) a = fmaxf(a, fabsf(xr[k]));
+    for (int64_t k0 = 0; k0 < K; k0 += kPrepK) {
+        f32x4 x4[kPrepIt];
+        load_chunk(k0, x4);
+#pragma unroll
+        for (int i = 0; i < kPrepIt; ++i)
+            a = fmaxf(fmaxf(a, fmaxf(fabsf(x4[i].x), fabsf(x4[i].y))), fmaxf(fabsf(x4[i].z), fabsf(x4[i].w)));
+    }
     a = wave_max(a);
     if (lane == 0) smax[wave] = a;
     __syncthreads();
     a = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
     int E = 0;
     if (a > 0.0f) (void)frexpf(a, &E);            // 2^(E-1) <= a < 2^E
-    if (b == 0 && tid == 0) v.ex[m] = E;
-    const int64_t k = 256 * b + tid;
-    float r = (k < K && a > 0.0f) ? ldexpf(xr[k], 6 - E) : 0.0f;
-    int q[kP];
+    if (tid == 0) v.ex[m] = E;
+    for (int64_t k0 = 0; k0 < K; k0 += kPrepK) {
+        f32x4 x4[kPrepIt];
+        load_chunk(k0, x4);                          // L2-resident re-read
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-        const float qp = __builtin_rintf(r);
-        q[p] = int(qp);
-        r = __fmul_rn(__fsub_rn(r, qp), 128.0f);
+        for (int i = 0; i < kPrepIt; ++i) {
+            const int64_t kb = k0 + 1024 * i;        // this wave's block: kb/256 + wave
+            if (kb >= K) break;
+            const int64_t k = kb + 4 * tid;
+            const float xv[4] = {x4[i].x, x4[i].y, x4[i].z, x4[i].w};
+            int q[4][kP];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float r = a > 0.0f ? ldexpf(xv[j], 6 - E) : 0.0f;
+#pragma unroll
+                for (int p = 0; p < kP; ++p) {
+                    const float qp = __builtin_rintf(r);
+                    q[j][p] = int(qp);
+                    r = __fmul_rn(__fsub_rn(r, qp), 128.0f);
+                }
+            }
+            if (k < K) {
+#pragma unroll
+                for (int p = 0; p < kP; ++p) {
+                    int8_t* row = v.planes + int64_t(m * kP + p) * K;
+                    if (FMT == 1) {
+                        const uint32_t packed = uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
+                                                uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
+                        *reinterpret_cast<uint32_t*>(row + k) = packed;
+                    } else {
+                        const int64_t base = k - (k & 255);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) row[base + tq2_pos(int((k + j) & 255))] = int8_t(q[j][p]);
+                    }
+                }
+            }
+            const int64_t b = kb / 256 + wave;
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                int s = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+                if (lane == 0 && b < nblk) v.xsum[int64_t(m * kP + p) * nblk + b] = s;
+                tot[p] += s;
+            }
+        }
     }
-    if (k < K) {
-        const int64_t pos = FMT == 2 ? 256 * b + tq2_pos(tid) : k;
+    if (lane == 0)
 #pragma unroll
-        for (int p = 0; p < kP; ++p) v.planes[int64_t(m * kP + p) * K + pos] = int8_t(q[p]);
-    }
-#pragma unroll
-    for (int p = 0; p < kP; ++p) {
-        int s = q[p];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) ssum[wave][p] = s;
-    }
+        for (int p = 0; p < kP; ++p) stot[wave][p] = tot[p];
     __syncthreads();
-    if (tid < kP) v.xsum[int64_t(m * kP + tid) * nblk + b] = ssum[0][tid] + ssum[1][tid] + ssum[2][tid] + ssum[3][tid];
+    if (tid < kP) v.xtot[m * kP + tid] = stot[0][tid] + stot[1][tid] + stot[2][tid] + stot[3][tid];
 }
 
 template <int FMT>
 __global__ void __launch_bounds__(256) prep_planes_kernel(const float* __restrict__ x, int64_t K, int M,
                                                           void* __restrict__ ws) {
-    const int64_t b = blockIdx.x;
-    const int m = blockIdx.y;
-    prep_block<FMT>(x + int64_t(m) * K, K, M, m, b, ws);
+    const int m = blockIdx.x;
+    prep_token<FMT>(x + int64_t(m) * K, K, M, m, ws);
 }
 
 // ---------------------------------------------------------------- product
+// Field j of a code byte, masked in place: its int8 value is c * kFieldMul[j].
+// i2_s MFMA t reads the field at bits 6-2t (elements 32t.. of each group);
+// TQ2_0 MFMA t reads field t (bits 2t).
 template <int FMT>
+__device__ __forceinline__ uint32_t field(uint32_t u, int t) {
+    const int bit = FMT == 1 ? 6 - 2 * t : 2 * t;
+    if (bit == 6) return (u >> 2) & 0x30303030u;   // c * 16
+    if (bit == 4) return u & 0x30303030u;          // c * 16
+    if (bit == 2) return u & 0x0C0C0C0Cu;          // c * 4
+    return u & 0x03030303u;                        // c
+}
+template <int FMT>
+__host__ __device__ constexpr int field_mul(int t) {
+    return (FMT == 1 ? 6 - 2 * t : 2 * t) >= 4 ? 16 : ((FMT == 1 ? 6 - 2 * t : 2 * t) == 2 ? 4 : 1);
+}
+
+template <int FMT, int M>
 __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                            int64_t N, int64_t K, const void* __restrict__ ws, int M,
+                                            int64_t N, int64_t K, const void* __restrict__ ws,
                                             const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
                                             char* __restrict__ lds) {
+    constexpr int RR = kP * M;                          // plane rows in use (<= 15)
+    constexpr int kAChunks = (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
-    const int RR = kP * M;                              // plane rows in use (<= 15)
+    const int arow = nl < RR ? nl : RR - 1;             // rows >= RR of the operand are never used
     const uint32_t rowbytes = uint32_t(K / 4);
     const int nwin = int((K + kWinK - 1) / kWinK);
     const int nblk = int((K + 255) / 256);
     const PlaneView pv = plane_view(const_cast<void*>(ws), M, K);
-    char* wbuf = lds;
-    int8_t* abuf = reinterpret_cast<int8_t*>(lds + 2 * kWaves * kWTile);
-    const int abytes = RR * kAStride;
-    int* xtot = reinterpret_cast<int*>(abuf + 2 * abytes);   // [RR] total plane sums (i2_s)
+    char* wtile = lds + wave * kWTile;                  // private to this wave
+    int8_t* abuf = reinterpret_cast<int8_t*>(lds + kWaves * kWTile);
+    constexpr int abytes = RR * kAStride;
 
     // loads of this lane: row 4i + q of the wave's tile, 16-byte chunk nl of each window
     const uint8_t* lrow[4];
@@ -156,47 +244,69 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     orow = orow < N ? orow : N - 1;
     const uint16_t* srow = FMT == 2 ? scales + orow * (K / 256) : nullptr;
 
+    // Per window a wave loads its 16 rows x kWinB bytes as kLPR loads of
+    // 4 rows x 256 bytes per row group; lane (q, nl) takes row 4i + q,
+    // bytes 256j + 16nl of the window.
+    constexpr int kLPR = kWinB / 256;
+    constexpr int kAPerRow = kWinK / 16;                   // 16-byte plane chunks per plane row
     struct Regs {
-        i32x4 w[4];
+        i32x4 w[4 * kLPR];
         i32x4 a[kAChunks];
     };
     auto load = [&](int w, Regs& r) {
-        const uint32_t off = uint32_t(w) * kWinB + 16 * nl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r.w[i] = (off < rowbytes) ? ld16_stream(lrow[i] + uint32_t(w) * kWinB) : i32x4{0, 0, 0, 0};
+        for (int j = 0; j < kLPR; ++j) {
+            const uint32_t off = uint32_t(w) * kWinB + 256 * j + 16 * nl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint8_t* p = lrow[i] + uint32_t(w) * kWinB + 256 * j;
+                r.w[4 * j + i] = (off < rowbytes) ? (LL_PLANES_NT ? ld16_stream(p) : ld16(p)) : i32x4{0, 0, 0, 0};
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 6, col = c & 63;
+            const int c = tid + 64 * kWaves * i;
+            const int row = c / kAPerRow, col = c % kAPerRow;
             const int64_t k = int64_t(w) * kWinK + 16 * col;
             r.a[i] = (row < RR && k < K) ? ld16(pv.planes + int64_t(row) * K + k) : i32x4{0, 0, 0, 0};
         }
     };
-    auto store = [&](int buf, const Regs& r) {
-        char* base = wbuf + (buf * kWaves + wave) * kWTile;
+    auto store_w = [&](const Regs& r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(base + (4 * i + q) * kWStride + 16 * nl) = r.w[i];
+        for (int j = 0; j < kLPR; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<i32x4*>(wtile + (4 * i + q) * kWStride + 256 * j + 16 * nl) = r.w[4 * j + i];
+    };
+    auto store_a = [&](int buf, const Regs& r) {
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 6, col = c & 63;
+            const int c = tid + 64 * kWaves * i;
+            const int row = c / kAPerRow, col = c % kAPerRow;
             if (row < RR) *reinterpret_cast<i32x4*>(abuf + buf * abytes + row * kAStride + 16 * col) = r.a[i];
         }
     };
 
-    i32x4 acc = {0, 0, 0, 0};
+    i32x4 acc[4];                                        // i2_s: one accumulator per field
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = i32x4{0, 0, 0, 0};
     double dacc[4] = {0.0, 0.0, 0.0, 0.0};               // TQ2_0: block-scaled sums per plane row
 
     auto compute = [&](int w) {
-        const int cur = w & 1;
-        const char* wb = wbuf + (cur * kWaves + wave) * kWTile + nl * kWStride + 16 * q;
-        const int8_t* ab = abuf + cur * abytes + nl * kAStride;
+        const char* wb = wtile + nl * kWStride + 16 * q;
+        const int8_t* ab = abuf + (w & 1) * abytes + arow * kAStride;
 #pragma unroll
-        for (int seg = 0; seg < 4; ++seg) {
-            const int s = 4 * w + seg;                     // 256-k segment (= TQ2_0 block)
+        for (int seg = 0; seg < kWinK / 256; ++seg) {
+            const int s = (kWinK / 256) * w + seg;         // 256-k segment (= TQ2_0 block)
             if (uint32_t(64 * s) >= rowbytes) break;
             i32x4 u = *reinterpret_cast<const i32x4*>(wb + 64 * seg);
+            i32x4 a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int aoff = FMT == 1 ? 256 * seg + 128 * (q >> 1) + 32 * t + 16 * (q & 1)
+                                          : 256 * seg + 64 * t + 16 * q;
+                a[t] = *reinterpret_cast<const i32x4*>(ab + aoff);
+            }
             if (FMT == 2) {
                 // c = ((b0 ^ b1) << 1) | !b0 turns the two's-complement field w into w + 1
 #pragma unroll
@@ -205,20 +315,13 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                     u[j] = int((v ^ ((v & 0x55555555u) << 1)) ^ 0x55555555u);
                 }
             }
-            i32x4 bacc = (FMT == 2) ? i32x4{0, 0, 0, 0} : acc;
+            i32x4 bacc[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                // i2_s: MFMA t takes shift 6-2t (elements 32t..32t+31 of each group);
-                // TQ2_0: field t; the operand offsets follow the plane layout.
-                const int sh = FMT == 1 ? 6 - 2 * t : 2 * t;
                 i32x4 b;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = int((uint32_t(u[j]) >> sh) & 0x03030303u);
-                i32x4 a = {0, 0, 0, 0};
-                const int aoff = FMT == 1 ? 256 * seg + 128 * (q >> 1) + 32 * t + 16 * (q & 1)
-                                          : 256 * seg + 64 * t + 16 * q;
-                if (nl < RR) a = *reinterpret_cast<const i32x4*>(ab + aoff);
-                bacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, bacc, 0, 0, 0);
+                for (int j = 0; j < 4; ++j) b[j] = int(field<FMT>(uint32_t(u[j]), t));
+                bacc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, FMT == 2 ? i32x4{0, 0, 0, 0} : acc[t], 0, 0, 0);
             }
             if (FMT == 2) {
                 // C lane (column nl, quarter q) holds plane rows 4q..4q+3
@@ -227,56 +330,69 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q + r;
                     const int xs = row < RR ? ld32(pv.xsum + row * nblk + s) : 0;
-                    dacc[r] = __builtin_fma(sc, double(bacc[r] - xs), dacc[r]);
+                    int dot = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) dot += bacc[t][r] / field_mul<FMT>(t);
+                    dacc[r] = __builtin_fma(sc, double(dot - xs), dacc[r]);
                 }
             } else {
-                acc = bacc;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[t] = bacc[t];
             }
         }
     };
 
-    // total plane sums for i2_s, once per workgroup
-    if (FMT == 1 && tid < RR) {
-        int s = 0;
-        for (int b = 0; b < nblk; ++b) s += ld32(pv.xsum + tid * nblk + b);
-        xtot[tid] = s;
-    }
-
     Regs r0, r1;
     load(0, r0);
     if (nwin > 1) load(1, r1);
-    store(0, r0);
+    store_w(r0);
+    store_a(0, r0);
     __syncthreads();
-    // window w is multiplied from LDS buffer w%2 while window w+1 waits in
-    // registers and window w+2 is being fetched
+    // Window w is multiplied from LDS while window w+1 waits in registers and
+    // window w+2 is being fetched.  The weight tile is private to the wave:
+    // its LDS accesses execute in program order, so rewriting it after the
+    // multiply needs no workgroup barrier; the barrier orders the shared
+    // activation window.
     for (int w = 0; w < nwin; w += 2) {
         if (w + 2 < nwin) load(w + 2, r0);
         compute(w);
-        if (w + 1 < nwin) store((w + 1) & 1, r1);
+        if (w + 1 < nwin) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            store_w(r1);
+            store_a((w + 1) & 1, r1);
+        }
         __syncthreads();
         if (w + 1 >= nwin) break;
         if (w + 3 < nwin) load(w + 3, r1);
         compute(w + 1);
-        if (w + 2 < nwin) store((w + 2) & 1, r0);
+        if (w + 2 < nwin) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            store_w(r0);
+            store_a((w + 2) & 1, r0);
+        }
         __syncthreads();
     }
 
-    // per plane row: D_row = (i2_s) acc - total plane sum, or (TQ2_0) the
-    // block-scaled sum; then y = f * 2^(E-6) * sum_p 128^-p D_(5m+p)
+    // per plane row: D_row = (i2_s) sum_t acc_t / mul_t - total plane sum, or
+    // (TQ2_0) the block-scaled sum; then y = f * 2^(E-6) * sum_p 128^-p D_(5m+p)
     double d[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = 4 * q + r;
-        if (FMT == 1) d[r] = double(acc[r] - (row < RR ? xtot[row] : 0));
-        else d[r] = dacc[r];
+        if (FMT == 1) {
+            int dot = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dot += acc[t][r] / field_mul<FMT>(t);
+            d[r] = double(dot - (row < RR ? ld32(pv.xtot + row) : 0));
+        } else {
+            d[r] = dacc[r];
+        }
     }
-    const double f = FMT == 1 ? double(*(const __attribute__((address_space(1))) float*)(
-                                    codes + N * int64_t(rowbytes)))
+    const double f = FMT == 1 ? double(*(const __attribute__((address_space(1))) float*)(codes + N * int64_t(rowbytes)))
                               : 1.0;
     const int64_t n = n0 + 16 * wave + nl;
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-        if (m >= M) break;
+    for (int m = 0; m < M; ++m) {
         double v = 0.0;
 #pragma unroll
         for (int p = kP - 1; p >= 0; --p) {
@@ -293,14 +409,14 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     }
 }
 
-template <int FMT>
+template <int FMT, int M>
 __global__ void __launch_bounds__(64 * kWaves) gemv_planes_kernel(const uint8_t* __restrict__ codes,
                                                                    const uint16_t* __restrict__ scales, int64_t N,
-                                                                   int64_t K, const void* __restrict__ ws, int M,
+                                                                   int64_t K, const void* __restrict__ ws,
                                                                    const float* __restrict__ bias,
                                                                    float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT>(codes, scales, N, K, ws, M, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    planes_rows<FMT, M>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 struct PlanesProb {          // product of a prepared batch
@@ -316,36 +432,26 @@ struct PlanesPrep {          // distinct activation of a prepared batch
     const float* x;
     void* ws;
     int64_t K;
-    int64_t wg0;             // first preparation workgroup (one per 256-k block and token)
 };
 
-template <typename T>
-__device__ __forceinline__ int find_wg(const T* __restrict__ tab, int count, int64_t wg) {
-    int lo = 0, hi = count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tab[mid].wg0 <= wg) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
 
-template <int FMT>
-__global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const PlanesProb* __restrict__ tab, int count,
-                                                                         int M) {
+// Workgroup wg of a batch runs product map[wg] (one table load instead of a
+// search: a workgroup's first weight fetch waits on this lookup).
+template <int FMT, int M>
+__global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const PlanesProb* __restrict__ tab,
+                                                                         const int32_t* __restrict__ map) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t wg = blockIdx.x;
-    const PlanesProb& P = tab[find_wg(tab, count, wg)];
-    planes_rows<FMT>(P.codes, P.scales, P.N, P.K, P.ws, M, P.bias, P.y, (wg - P.wg0) * kRows, lds);
+    const PlanesProb& P = tab[ld32(map + wg)];
+    planes_rows<FMT, M>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(256) prep_planes_batch_kernel(const PlanesPrep* __restrict__ tab, int count, int M) {
-    const int64_t wg = blockIdx.x;
-    const PlanesPrep& P = tab[find_wg(tab, count, wg)];
-    const int64_t nblk = (P.K + 255) / 256;
-    const int64_t local = wg - P.wg0;
-    const int m = int(local / nblk);
-    prep_block<FMT>(P.x + int64_t(m) * P.K, P.K, M, m, local % nblk, P.ws);
+__global__ void __launch_bounds__(256) prep_planes_batch_kernel(const PlanesPrep* __restrict__ tab, int M) {
+    const int wg = int(blockIdx.x);                  // activation wg / M, token wg % M
+    const PlanesPrep& P = tab[wg / M];
+    const int m = wg % M;
+    prep_token<FMT>(P.x + int64_t(m) * P.K, P.K, M, m, P.ws);
 }
 
 template <typename F>
@@ -353,6 +459,27 @@ hipError_t allow_lds(F* kernel, size_t bytes) {
     if (bytes <= 65536) return hipSuccess;
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                                int(bytes));
+}
+
+template <int FMT, int M>
+hipError_t launch_single(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, void* ws, const float* bias,
+                         float* y, hipStream_t stream) {
+    const dim3 grid{unsigned((N + kRows - 1) / kRows)}, block{64 * kWaves};
+    const size_t lds = size_t(lds_bytes(M));
+    hipError_t e = allow_lds(gemv_planes_kernel<FMT, M>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_kernel<FMT, M>), grid, block, lds, stream, c, s, N, K, ws, bias, y);
+    return hipGetLastError();
+}
+
+template <int FMT, int M>
+hipError_t launch_batch(const PlanesProb* tab, const int32_t* map, int64_t wgs, hipStream_t stream) {
+    const dim3 grid{unsigned(wgs)}, block{64 * kWaves};
+    const size_t lds = size_t(lds_bytes(M));
+    hipError_t e = allow_lds(gemv_planes_batch_kernel<FMT, M>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_batch_kernel<FMT, M>), grid, block, lds, stream, tab, map);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -363,7 +490,6 @@ size_t planes_workspace(int64_t M, int64_t K) { return planes_bytes(M, K); }
 int64_t planes_batch_rows() { return kRows; }
 size_t planes_prob_bytes() { return sizeof(PlanesProb); }
 size_t planes_prep_bytes() { return sizeof(PlanesPrep); }
-int64_t planes_prep_wgs(int64_t M, int64_t K) { return M * ((K + 255) / 256); }
 
 void fill_planes_prob(void* dst, const void* codes, const void* scales, const void* ws, const float* bias, float* y,
                       int64_t N, int64_t K, int64_t wg0) {
@@ -379,58 +505,51 @@ void fill_planes_prob(void* dst, const void* codes, const void* scales, const vo
     *static_cast<PlanesProb*>(dst) = p;
 }
 
-void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K, int64_t wg0) {
+void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K) {
     PlanesPrep p;
     p.x = x;
     p.ws = ws;
     p.K = K;
-    p.wg0 = wg0;
     *static_cast<PlanesPrep*>(dst) = p;
 }
 
 hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K, const float* x,
                               int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
-    const dim3 pgrid{unsigned((K + 255) / 256), unsigned(M)}, pblock{256};
-    const dim3 grid{unsigned((N + kRows - 1) / kRows)}, block{64 * kWaves};
+    const dim3 pgrid{unsigned(M)}, pblock{256};
     const uint8_t* c = static_cast<const uint8_t*>(codes);
     const uint16_t* s = static_cast<const uint16_t*>(scales);
-    const size_t lds = size_t(lds_bytes(int(M)));
-    hipError_t e;
-    if (fmt == 1) {
-        hipLaunchKernelGGL(prep_planes_kernel<1>, pgrid, pblock, 0, stream, x, K, int(M), ws);
-        if ((e = allow_lds(gemv_planes_kernel<1>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(gemv_planes_kernel<1>, grid, block, lds, stream, c, s, N, K, ws, int(M), bias, y);
-    } else {
-        hipLaunchKernelGGL(prep_planes_kernel<2>, pgrid, pblock, 0, stream, x, K, int(M), ws);
-        if ((e = allow_lds(gemv_planes_kernel<2>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(gemv_planes_kernel<2>, grid, block, lds, stream, c, s, N, K, ws, int(M), bias, y);
+    if (fmt == 1) hipLaunchKernelGGL(prep_planes_kernel<1>, pgrid, pblock, 0, stream, x, K, int(M), ws);
+    else hipLaunchKernelGGL(prep_planes_kernel<2>, pgrid, pblock, 0, stream, x, K, int(M), ws);
+    switch (fmt * 4 + int(M)) {
+    case 5: return launch_single<1, 1>(c, s, N, K, ws, bias, y, stream);
+    case 6: return launch_single<1, 2>(c, s, N, K, ws, bias, y, stream);
+    case 7: return launch_single<1, 3>(c, s, N, K, ws, bias, y, stream);
+    case 9: return launch_single<2, 1>(c, s, N, K, ws, bias, y, stream);
+    case 10: return launch_single<2, 2>(c, s, N, K, ws, bias, y, stream);
+    default: return launch_single<2, 3>(c, s, N, K, ws, bias, y, stream);
     }
-    return hipGetLastError();
 }
 
-hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, int64_t wgs,
-                                    hipStream_t stream) {
-    const dim3 grid{unsigned(wgs)}, block{256};
+hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, hipStream_t stream) {
+    const dim3 grid{unsigned(int64_t(nprep) * M)}, block{256};
     const PlanesPrep* tab = static_cast<const PlanesPrep*>(prep_table);
-    if (fmt == 1) hipLaunchKernelGGL(prep_planes_batch_kernel<1>, grid, block, 0, stream, tab, nprep, int(M));
-    else hipLaunchKernelGGL(prep_planes_batch_kernel<2>, grid, block, 0, stream, tab, nprep, int(M));
+    if (fmt == 1) hipLaunchKernelGGL(prep_planes_batch_kernel<1>, grid, block, 0, stream, tab, int(M));
+    else hipLaunchKernelGGL(prep_planes_batch_kernel<2>, grid, block, 0, stream, tab, int(M));
     return hipGetLastError();
 }
 
-hipError_t launch_planes_batch_product(const void* prob_table, int count, int fmt, int64_t M, int64_t wgs,
+hipError_t launch_planes_batch_product(const void* prob_table, const void* map, int fmt, int64_t M, int64_t wgs,
                                        hipStream_t stream) {
-    const dim3 grid{unsigned(wgs)}, block{64 * kWaves};
     const PlanesProb* tab = static_cast<const PlanesProb*>(prob_table);
-    const size_t lds = size_t(lds_bytes(int(M)));
-    hipError_t e;
-    if (fmt == 1) {
-        if ((e = allow_lds(gemv_planes_batch_kernel<1>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(gemv_planes_batch_kernel<1>, grid, block, lds, stream, tab, count, int(M));
-    } else {
-        if ((e = allow_lds(gemv_planes_batch_kernel<2>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(gemv_planes_batch_kernel<2>, grid, block, lds, stream, tab, count, int(M));
+    const int32_t* mp = static_cast<const int32_t*>(map);
+    switch (fmt * 4 + int(M)) {
+    case 5: return launch_batch<1, 1>(tab, mp, wgs, stream);
+    case 6: return launch_batch<1, 2>(tab, mp, wgs, stream);
+    case 7: return launch_batch<1, 3>(tab, mp, wgs, stream);
+    case 9: return launch_batch<2, 1>(tab, mp, wgs, stream);
+    case 10: return launch_batch<2, 2>(tab, mp, wgs, stream);
+    default: return launch_batch<2, 3>(tab, mp, wgs, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace llk

@@ -48,12 +48,11 @@ size_t planes_prob_bytes();
 size_t planes_prep_bytes();
 void fill_planes_prob(void* dst, const void* codes, const void* scales, const void* ws, const float* bias, float* y,
                       int64_t N, int64_t K, int64_t wg0);
-void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K, int64_t wg0);
-int64_t planes_prep_wgs(int64_t M, int64_t K);
+void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K);
 hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K, const float* x,
                               int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
-hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, int64_t wgs,
-                                    hipStream_t stream);
-hipError_t launch_planes_batch_product(const void* prob_table, int count, int fmt, int64_t M, int64_t wgs,
+hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, hipStream_t stream);
+// map: int32 [wgs], the product each workgroup runs
+hipError_t launch_planes_batch_product(const void* prob_table, const void* map, int fmt, int64_t M, int64_t wgs,
                                        hipStream_t stream);
 }  // namespace llk

@@ -313,7 +313,7 @@ class ll_gemv_plan(C.Structure):
     _fields_ = [("mem", C.c_void_p), ("bytes", C.c_size_t), ("count", C.c_int32), ("nprep", C.c_int32),
                 ("act", C.c_int32), ("fmt", C.c_int32), ("M", C.c_int64), ("tiles", C.c_int64),
                 ("prep_entries", C.c_int64), ("kmax", C.c_int64), ("prob_table", C.c_void_p),
-                ("prep_table", C.c_void_p)]
+                ("prep_table", C.c_void_p), ("map_table", C.c_void_p)]
 
 
 SIGNATURES.update({

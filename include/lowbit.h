@@ -212,7 +212,8 @@ typedef struct {
     int32_t count, nprep, act, fmt;
     int64_t M, tiles, prep_entries, kmax;
     void* prob_table;    /* inside mem */
-    void* prep_table;    /* inside mem; NULL when no preparation launch is needed (M <= 5) */
+    void* prep_table;    /* inside mem */
+    void* map_table;     /* inside mem: product index of every workgroup (M <= 3), else NULL */
 } ll_gemv_plan;
 
 /* Device bytes ll_gemv_plan_init needs for these items ((size_t)-1 for

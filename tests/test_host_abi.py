@@ -159,8 +159,8 @@ def test_gemm_and_quantize_argument_errors():
 
 def test_workspace_sizes():
     w = _w(N=6912, K=2560)
-    # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + per-block plane sums + exponents
-    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == (5 * 2560 + 5 * 10 * 4 + 4 + 15) // 16 * 16
+    # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + per-block plane sums + exponents + row sums
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == (5 * 2560 + 5 * 10 * 4 + 4 + 5 * 4 + 15) // 16 * 16
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 8) > 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 17) == 2 ** 64 - 1
