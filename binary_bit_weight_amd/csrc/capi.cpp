@@ -80,9 +80,10 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
             return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: fp32 activations need format i2_s or TQ2_0");
         const bool planes = M <= llk::kPlanesMaxM;
         const size_t need = planes ? llk::planes_workspace(M, w->K) : llk::gemv_f32_workspace(M, w->K);
-        if (!workspace || workspace_bytes < need)
+        if (need > 0 && (!workspace || workspace_bytes < need))
             return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
-        if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
+        if (need > 0 && !aligned(workspace, 16))
+            return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
         if (planes)
             return hip_status(llk::launch_gemv_planes(w->fmt, w->codes, w->scales, w->N, w->K,
                                                       static_cast<const float*>(x), M, bias, y, workspace, s),

@@ -62,8 +62,8 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     }
     L.planes = M <= llk::kPlanesMaxM;
     L.prep_of.assign(size_t(count), -1);
+    for (int i = 0; i < count; ++i) L.kmax = std::max(L.kmax, items[i].w.K);
     for (int i = 0; i < count; ++i) {
-        L.kmax = std::max(L.kmax, items[i].w.K);
         int found = -1;
         for (size_t j = 0; j < L.xs.size(); ++j)
             if (L.xs[j] == items[i].x && L.xk[j] == items[i].w.K) { found = int(j); break; }
@@ -90,7 +90,7 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     for (size_t j = 0; j < L.xs.size(); ++j) {
         L.frag_at.push_back(at);
         L.ent0.push_back(L.entries);
-        const size_t bytes = L.planes ? llk::planes_workspace(M, L.xk[j]) : llk::gemv_f32_workspace(M, L.xk[j]);
+        const size_t bytes = L.planes ? llk::planes_operand_bytes(M, L.xk[j]) : llk::gemv_f32_workspace(M, L.xk[j]);
         if (!L.planes) L.entries += int64_t(bytes / 16);
         at = round_up(at + bytes, 256);
     }

@@ -60,6 +60,26 @@ constexpr int kAStride = kWinK + 16;      // padded LDS plane row
 
 __host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * kP * M * kAStride; }
 
+// Fused form of a single product (M = 1, K <= kFusedMaxK): every workgroup
+// builds the planes of the whole row in its LDS (no preparation launch), then
+// multiplies with no workgroup barrier.  It halves the latency of one call;
+// in a prepared batch the repeated preparation and the larger LDS cost more
+// than the launch it saves, so batches keep the preparation kernel.
+// LDS: weight tiles | planes [5][astride] | sums | max.
+#ifndef LL_PLANES_FUSED
+#define LL_PLANES_FUSED 1
+#endif
+constexpr int kThreads = 64 * kWaves;
+constexpr int64_t kFusedMaxK = LL_PLANES_FUSED ? 8192 : 0;
+constexpr int kXIt = 8192 / (4 * kThreads);          // float4 of x per thread
+__host__ __device__ inline int fused_astride(int64_t K) { return int((K + 255) / 256 * 256 + 16); }
+__host__ __device__ inline int fused_sums(int64_t K) {
+    return kP * int((K + 255) / 256) > kWaves * kP ? kP * int((K + 255) / 256) : kWaves * kP;
+}
+__host__ __device__ inline int fused_lds_bytes(int64_t K) {
+    return kWaves * kWTile + kP * fused_astride(K) + 4 * fused_sums(K) + 4 * kWaves;
+}
+
 // Position of element k inside its 256-element TQ2_0 block in the plane
 // layout: field f = k%4 of byte 16q + 4v + b (k = 64q + 16v + 4b + f) goes to
 // 64f + 16q + 4v + b, so one MFMA (one field) reads 16 consecutive bytes.
@@ -197,6 +217,94 @@ __global__ void __launch_bounds__(256) prep_planes_kernel(const float* __restric
     prep_token<FMT>(x + int64_t(m) * K, K, M, m, ws);
 }
 
+// Fused preparation of one token row inside the product workgroup (same
+// split as above).  With T threads, thread t holds x[4t + 4Ti + (0..3)], so
+// 256-k block (T/64)i + wave belongs to one wave.  Writes planes [5][astride]
+// into A and the plane sums into sums: TQ2_0 per block [5][nblk], i2_s per
+// wave [waves][5].
+// Returns E; contains one workgroup barrier (the row maximum); the caller's
+// next barrier publishes A and sums.
+template <int FMT>
+__device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K, int8_t* __restrict__ A, int astride,
+                                          int* __restrict__ sums, float* __restrict__ smax) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nblk = int((K + 255) / 256);
+    f32x4 xv[kXIt];
+#pragma unroll
+    for (int i = 0; i < kXIt; ++i) {
+        const int64_t k = 4 * kThreads * i + 4 * tid;  // K % 128 == 0: k < K implies k + 3 < K
+        xv[i] = k < K ? ld16f(x + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kXIt; ++i)
+        a = fmaxf(fmaxf(a, fmaxf(fabsf(xv[i].x), fabsf(xv[i].y))), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w)));
+    a = wave_max(a);
+    if (lane == 0) smax[wave] = a;
+    __syncthreads();
+    a = smax[0];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) a = fmaxf(a, smax[v]);
+    int E = 0;
+    if (a > 0.0f) (void)frexpf(a, &E);                // 2^(E-1) <= a < 2^E
+    int tot[kP] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kXIt; ++i) {
+        const int64_t kb = 4 * kThreads * i;
+        if (kb >= K) break;
+        const int k = int(kb) + 4 * tid;
+        const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        int q[4][kP];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r = a > 0.0f ? ldexpf(xe[j], 6 - E) : 0.0f;
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                const float qp = __builtin_rintf(r);
+                q[j][p] = int(qp);
+                r = __fmul_rn(__fsub_rn(r, qp), 128.0f);
+            }
+        }
+        if (k < K) {
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                int8_t* row = A + p * astride;
+                if (FMT == 1) {
+                    *reinterpret_cast<uint32_t*>(row + k) =
+                        uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
+                        uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) row[(k & ~255) + tq2_pos((k + j) & 255)] = int8_t(q[j][p]);
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+            const int s4 = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
+            if (FMT == 1) {
+                tot[p] += s4;
+            } else {
+                int sw = s4;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) sw += __shfl_xor(sw, o, 64);
+                const int b = kWaves * i + wave;
+                if (lane == 0 && b < nblk) sums[p * nblk + b] = sw;
+            }
+        }
+    }
+    if (FMT == 1) {
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+            int sw = tot[p];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) sw += __shfl_xor(sw, o, 64);
+            if (lane == 0) sums[wave * kP + p] = sw;
+        }
+    }
+    return E;
+}
+
 // ---------------------------------------------------------------- product
 // Field j of a code byte, masked in place: its int8 value is c * kFieldMul[j].
 // i2_s MFMA t reads the field at bits 6-2t (elements 32t.. of each group);
@@ -214,13 +322,15 @@ __host__ __device__ constexpr int field_mul(int t) {
     return (FMT == 1 ? 6 - 2 * t : 2 * t) >= 4 ? 16 : ((FMT == 1 ? 6 - 2 * t : 2 * t) == 2 ? 4 : 1);
 }
 
-template <int FMT, int M>
+// FUSED: src is the fp32 token row (M == 1); otherwise the prepared workspace.
+template <int FMT, int M, bool FUSED>
 __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int64_t N, int64_t K, const void* __restrict__ ws,
                                             const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
                                             char* __restrict__ lds) {
+    static_assert(!FUSED || M == 1, "the fused form handles one token");
     constexpr int RR = kP * M;                          // plane rows in use (<= 15)
-    constexpr int kAChunks = (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
+    constexpr int kAChunks = FUSED ? 1 : (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
     const int arow = nl < RR ? nl : RR - 1;             // rows >= RR of the operand are never used
@@ -231,6 +341,9 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     char* wtile = lds + wave * kWTile;                  // private to this wave
     int8_t* abuf = reinterpret_cast<int8_t*>(lds + kWaves * kWTile);
     constexpr int abytes = RR * kAStride;
+    const int astride = FUSED ? fused_astride(K) : kAStride;
+    int* fsums = reinterpret_cast<int*>(abuf + kP * fused_astride(K));           // fused only
+    float* fsmax = reinterpret_cast<float*>(fsums + fused_sums(K));
 
     // loads of this lane: row 4i + q of the wave's tile, 16-byte chunk nl of each window
     const uint8_t* lrow[4];
@@ -263,12 +376,14 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 r.w[4 * j + i] = (off < rowbytes) ? (LL_PLANES_NT ? ld16_stream(p) : ld16(p)) : i32x4{0, 0, 0, 0};
             }
         }
+        if constexpr (!FUSED) {
 #pragma unroll
-        for (int i = 0; i < kAChunks; ++i) {
-            const int c = tid + 64 * kWaves * i;
-            const int row = c / kAPerRow, col = c % kAPerRow;
-            const int64_t k = int64_t(w) * kWinK + 16 * col;
-            r.a[i] = (row < RR && k < K) ? ld16(pv.planes + int64_t(row) * K + k) : i32x4{0, 0, 0, 0};
+            for (int i = 0; i < kAChunks; ++i) {
+                const int c = tid + 64 * kWaves * i;
+                const int row = c / kAPerRow, col = c % kAPerRow;
+                const int64_t k = int64_t(w) * kWinK + 16 * col;
+                r.a[i] = (row < RR && k < K) ? ld16(pv.planes + int64_t(row) * K + k) : i32x4{0, 0, 0, 0};
+            }
         }
     };
     auto store_w = [&](const Regs& r) {
@@ -294,7 +409,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
 
     auto compute = [&](int w) {
         const char* wb = wtile + nl * kWStride + 16 * q;
-        const int8_t* ab = abuf + (w & 1) * abytes + arow * kAStride;
+        const int8_t* ab = FUSED ? abuf + arow * astride + w * kWinK : abuf + (w & 1) * abytes + arow * kAStride;
 #pragma unroll
         for (int seg = 0; seg < kWinK / 256; ++seg) {
             const int s = (kWinK / 256) * w + seg;         // 256-k segment (= TQ2_0 block)
@@ -329,7 +444,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q + r;
-                    const int xs = row < RR ? ld32(pv.xsum + row * nblk + s) : 0;
+                    const int xs = row >= RR ? 0 : FUSED ? fsums[row * nblk + s] : ld32(pv.xsum + row * nblk + s);
                     int dot = 0;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) dot += bacc[t][r] / field_mul<FMT>(t);
@@ -345,32 +460,34 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     Regs r0, r1;
     load(0, r0);
     if (nwin > 1) load(1, r1);
+    int Ef = 0;
+    if constexpr (FUSED) Ef = fused_prep<FMT>(static_cast<const float*>(ws), K, abuf, astride, fsums, fsmax);
     store_w(r0);
-    store_a(0, r0);
+    if constexpr (!FUSED) store_a(0, r0);
     __syncthreads();
     // Window w is multiplied from LDS while window w+1 waits in registers and
     // window w+2 is being fetched.  The weight tile is private to the wave:
     // its LDS accesses execute in program order, so rewriting it after the
     // multiply needs no workgroup barrier; the barrier orders the shared
-    // activation window.
+    // activation window (the fused form holds the whole row: no barrier).
     for (int w = 0; w < nwin; w += 2) {
         if (w + 2 < nwin) load(w + 2, r0);
         compute(w);
         if (w + 1 < nwin) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             store_w(r1);
-            store_a((w + 1) & 1, r1);
+            if constexpr (!FUSED) store_a((w + 1) & 1, r1);
         }
-        __syncthreads();
+        if constexpr (!FUSED) __syncthreads();
         if (w + 1 >= nwin) break;
         if (w + 3 < nwin) load(w + 3, r1);
         compute(w + 1);
         if (w + 2 < nwin) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             store_w(r0);
-            store_a((w + 2) & 1, r0);
+            if constexpr (!FUSED) store_a((w + 2) & 1, r0);
         }
-        __syncthreads();
+        if constexpr (!FUSED) __syncthreads();
     }
 
     // per plane row: D_row = (i2_s) sum_t acc_t / mul_t - total plane sum, or
@@ -383,7 +500,16 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
             int dot = 0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) dot += acc[t][r] / field_mul<FMT>(t);
-            d[r] = double(dot - (row < RR ? ld32(pv.xtot + row) : 0));
+            int xt = 0;
+            if (row < RR) {
+                if constexpr (FUSED) {
+#pragma unroll
+                    for (int v = 0; v < kWaves; ++v) xt += fsums[v * kP + row];
+                } else {
+                    xt = ld32(pv.xtot + row);
+                }
+            }
+            d[r] = double(dot - xt);
         } else {
             d[r] = dacc[r];
         }
@@ -401,7 +527,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
             v = __builtin_fma(v, 1.0 / 128.0, part);     // Horner in 1/128: exact for these integers
         }
         if (q == 0 && n < N) {
-            const int E = ld32(pv.ex + m);
+            const int E = FUSED ? Ef : ld32(pv.ex + m);
             float out = float(f * ldexp(v, E - 6));
             if (bias) out = __fadd_rn(out, bias[n]);
             y[int64_t(m) * N + n] = out;
@@ -416,7 +542,17 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_kernel(const uint8_t*
                                                                    const float* __restrict__ bias,
                                                                    float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT, M>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    planes_rows<FMT, M, false>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kWaves) gemv_planes_fused_kernel(const uint8_t* __restrict__ codes,
+                                                                         const uint16_t* __restrict__ scales, int64_t N,
+                                                                         int64_t K, const float* __restrict__ x,
+                                                                         const float* __restrict__ bias,
+                                                                         float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    planes_rows<FMT, 1, true>(codes, scales, N, K, x, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 struct PlanesProb {          // product of a prepared batch
@@ -443,7 +579,7 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const Pl
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t wg = blockIdx.x;
     const PlanesProb& P = tab[ld32(map + wg)];
-    planes_rows<FMT, M>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
+    planes_rows<FMT, M, false>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
 }
 
 template <int FMT>
@@ -472,6 +608,17 @@ hipError_t launch_single(const uint8_t* c, const uint16_t* s, int64_t N, int64_t
     return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_fused_single(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, const float* x,
+                               const float* bias, float* y, hipStream_t stream) {
+    const dim3 grid{unsigned((N + kRows - 1) / kRows)}, block{64 * kWaves};
+    const size_t lds = size_t(fused_lds_bytes(K));
+    hipError_t e = allow_lds(gemv_planes_fused_kernel<FMT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_fused_kernel<FMT>), grid, block, lds, stream, c, s, N, K, x, bias, y);
+    return hipGetLastError();
+}
+
 template <int FMT, int M>
 hipError_t launch_batch(const PlanesProb* tab, const int32_t* map, int64_t wgs, hipStream_t stream) {
     const dim3 grid{unsigned(wgs)}, block{64 * kWaves};
@@ -486,7 +633,9 @@ hipError_t launch_batch(const PlanesProb* tab, const int32_t* map, int64_t wgs, 
 
 namespace llk {
 
-size_t planes_workspace(int64_t M, int64_t K) { return planes_bytes(M, K); }
+bool planes_fused(int64_t M, int64_t K) { return M == 1 && K <= kFusedMaxK; }
+size_t planes_workspace(int64_t M, int64_t K) { return planes_fused(M, K) ? 0 : planes_bytes(M, K); }
+size_t planes_operand_bytes(int64_t M, int64_t K) { return planes_bytes(M, K); }
 int64_t planes_batch_rows() { return kRows; }
 size_t planes_prob_bytes() { return sizeof(PlanesProb); }
 size_t planes_prep_bytes() { return sizeof(PlanesPrep); }
@@ -518,6 +667,9 @@ hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, in
     const dim3 pgrid{unsigned(M)}, pblock{256};
     const uint8_t* c = static_cast<const uint8_t*>(codes);
     const uint16_t* s = static_cast<const uint16_t*>(scales);
+    if (planes_fused(M, K))
+        return fmt == 1 ? launch_fused_single<1>(c, s, N, K, x, bias, y, stream)
+                        : launch_fused_single<2>(c, s, N, K, x, bias, y, stream);
     if (fmt == 1) hipLaunchKernelGGL(prep_planes_kernel<1>, pgrid, pblock, 0, stream, x, K, int(M), ws);
     else hipLaunchKernelGGL(prep_planes_kernel<2>, pgrid, pblock, 0, stream, x, K, int(M), ws);
     switch (fmt * 4 + int(M)) {

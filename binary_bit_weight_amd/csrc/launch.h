@@ -41,8 +41,12 @@ hipError_t launch_gemv_f32_batch_product(const void* prob_table, int count, int 
 
 // 1 <= M <= 3: activations split into int8 planes (one preparation launch),
 // int8 matrix cores with exact int32 accumulation (gemv_planes.hip).
+// A single call with M == 1 and K <= 8192 runs fused: each product workgroup
+// builds the planes itself from x, so no workspace and no preparation launch.
 constexpr int64_t kPlanesMaxM = 3;
-size_t planes_workspace(int64_t M, int64_t K);
+bool planes_fused(int64_t M, int64_t K);
+size_t planes_workspace(int64_t M, int64_t K);       // single call: 0 when fused
+size_t planes_operand_bytes(int64_t M, int64_t K);   // prepared operands of one activation
 int64_t planes_batch_rows();
 size_t planes_prob_bytes();
 size_t planes_prep_bytes();

@@ -174,7 +174,9 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    binary_gemm] Decode-size product, 1 <= M <= 16, reading the packed codes
    in the kernel.  act == LL_ACT_F32: x fp32 [M,K], xs unused (NULL); formats
    i2_s and TQ2_0; y = scale * sum_k w*x (i2_s) or sum over blocks of
-   s_block * sum w*x (TQ2_0), fp32 accumulation.
+   s_block * sum w*x (TQ2_0), within 1e-5 * scale * sum|x| (+1e-6) of the
+   exact value (M <= 3: x split into five int8 planes, exact integer sums,
+   fp64 epilogue; M > 3: bf16 planes, fp32 accumulation).
    act == LL_ACT_I8: x int8 [M,K], xs fp32 [M] from ll_quantize_act; formats
    i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32) and W1
    (y = (float)((double)xs[m] * sum_g s_g * d_g), d_g the exact per-group

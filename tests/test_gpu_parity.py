@@ -47,8 +47,12 @@ def test_quantize_bitexact(M, K, dtype):
 
 
 # ------------------------------------------------------------------ i2_s, fp32 activations
+# A single call with M = 1 up to K = 8192 runs the fused kernel (planes built
+# per workgroup); K = 8320 and M = 2, 3 the preparation + product pair;
+# M > 3 the bf16 path.
 I2S_F32_SMALL = [(256, 512, 1), (37, 384, 1), (16, 128, 1), (1, 128, 1), (100, 640, 2), (77, 512, 5),
-                 (64, 256, 6), (50, 384, 11), (33, 512, 16), (129, 1024, 3)]
+                 (64, 256, 6), (50, 384, 11), (33, 512, 16), (129, 1024, 3), (40, 8192, 1), (70, 8320, 1),
+                 (65, 1152, 2), (3, 3200, 1)]
 
 
 @pytest.mark.parametrize("N,K,M", I2S_F32_SMALL)
@@ -116,7 +120,8 @@ def test_i2s_gemv_f32_deterministic():
 
 
 # ------------------------------------------------------------------ TQ2_0, fp32 activations
-@pytest.mark.parametrize("N,K,M", [(17, 256, 1), (100, 512, 8), (40, 768, 16), (6, 1024, 3), (256, 2560, 1)])
+@pytest.mark.parametrize("N,K,M", [(17, 256, 1), (100, 512, 8), (40, 768, 16), (6, 1024, 3), (256, 2560, 1),
+                                   (9, 8192, 1), (5, 8448, 1), (70, 1280, 2)])
 def test_tq2_gemv_f32_small(N, K, M):
     t = torch()
     w, sc, blocks = make_tq2(400 + N + M, N, K)
@@ -193,13 +198,15 @@ def test_i2s_gemv_i8_matches_gemm():
 
 
 # ------------------------------------------------------------------ prepared batch
-@pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 4), ("tq2", 1), ("tq2", 16)])
-def test_gemv_plan_matches_oracle(fmt, M):
+@pytest.mark.parametrize("fmt,M,big", [("i2s", 1, False), ("i2s", 1, True), ("i2s", 2, False), ("i2s", 4, False),
+                                      ("tq2", 1, False), ("tq2", 1, True), ("tq2", 3, False), ("tq2", 16, False)])
+def test_gemv_plan_matches_oracle(fmt, M, big):
     """A prepared batch of products with mixed N and K (some sharing x) against
-    the oracle, row by row, run twice (second run with new x contents)."""
+    the oracle, row by row, run twice (second run with new x contents).  With
+    big, one product has K = 8448 (33 plane blocks, a ragged last window)."""
     t = torch()
     shapes = [(2560, 2560, 0), (6912, 2560, 0), (2560, 6912, 1), (37, 384 if fmt == "i2s" else 512, 2),
-              (16, 256, 3)]
+              (16, 256, 3)] + ([(100, 8448, 4)] if big else [])
     xs_np = {}
     items, refs = [], []
     for i, (N, K, slot) in enumerate(shapes):
@@ -233,3 +240,28 @@ def test_gemv_plan_matches_oracle(fmt, M):
             y_ref, tsum = fn(packed, N, K, xs_np[slot][0], rows)
             ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
             assert ok, "N=%d K=%d round %d: worst error / bound %.3f" % (N, K, rnd, worst)
+
+
+@pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 2), ("tq2", 1), ("tq2", 3), ("i2s", 6)])
+def test_gemv_f32_zero_token(fmt, M):
+    """An all-zero token gives exactly the bias (no exponent, no planes); the
+    other tokens still match the oracle."""
+    t = torch()
+    N, K = 90, 1024
+    if fmt == "i2s":
+        _, _, packed = make_i2s(41 + M, N, K)
+        W = L.upload_i2s(packed, N, K)
+        fn = oracle.i2s_gemv_f32
+    else:
+        _, _, packed = make_tq2(42 + M, N, K)
+        W = L.upload_tq2(packed, N, K)
+        fn = oracle.tq2_gemv_f32
+    x = _x(43 + M, M, K)
+    x[0, :] = 0.0
+    bias = synth.uniform_f32(44, N, -1, 1)
+    announce("zero token", fmt, M)
+    y = L.gemv(W, t.from_numpy(x).cuda(), bias=t.from_numpy(bias).cuda()).cpu().numpy()
+    assert np.array_equal(y[0], bias)
+    y_ref, tsum = fn(packed, N, K, x)
+    ok, worst = f32_tol_ok(y, y_ref + bias.astype(np.float64)[None, :], tsum)
+    assert ok, "worst error / bound = %.3f" % worst

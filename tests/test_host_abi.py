@@ -136,7 +136,7 @@ def test_gemv_argument_errors():
     assert _gemv(_w(codes=FAKE + 4)) == -3
     assert _gemv(_w(), x=FAKE + 8) == -3
     assert _gemv(_w(), y=0) == -1
-    assert _gemv(_w(), ws=0) == -5               # fp32 activations need the operand workspace
+    assert _gemv(_w(), M=2, ws=0) == -5          # fp32 activations, M > 1: operand workspace needed
     assert _gemv(_w(), M=6, wsb=16) == -5
     assert _gemv(_w(fmt=L.LL_FMT_TQ2_0, scales=0)) == -1
     assert _gemv(_w(fmt=L.LL_FMT_W1, K=256, group=96)) == -2
@@ -160,7 +160,32 @@ def test_gemm_and_quantize_argument_errors():
 def test_workspace_sizes():
     w = _w(N=6912, K=2560)
     # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + per-block plane sums + exponents + row sums
-    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == (5 * 2560 + 5 * 10 * 4 + 4 + 5 * 4 + 15) // 16 * 16
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 2) == (10 * 2560 + 10 * 10 * 4 + 8 + 10 * 4 + 15) // 16 * 16
+    # M = 1 with K <= 8192 builds the planes inside the product kernel
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == 0
+    w2 = _w(N=64, K=8320)
+    assert L.lib().ll_gemv_workspace_size(C.byref(w2), L.LL_ACT_F32, 1) == (5 * 8320 + 5 * 33 * 4 + 4 + 5 * 4 + 15) // 16 * 16
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 8) > 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 17) == 2 ** 64 - 1
+
+
+def _item(N, K, x, y):
+    return L.ll_gemv_item(_w(N=N, K=K), C.c_void_p(x), None, C.c_void_p(y))
+
+
+def test_plan_bytes_hold_every_activation_layout():
+    """Host-only: a plan prepares every distinct activation into plan memory
+    (also where a single call of that shape needs no workspace), so its size
+    covers each one's operands (5K int8 plane bytes per token)."""
+    lib = L.lib()
+    two = (L.ll_gemv_item * 2)(_item(2560, 2560, FAKE, FAKE), _item(2560, 6912, FAKE + 0x10000, FAKE))
+    split = (L.ll_gemv_item * 2)(_item(2560, 2560, FAKE, FAKE), _item(100, 8448, FAKE + 0x10000, FAKE))
+    assert lib.ll_gemv_plan_bytes(two, 2, L.LL_ACT_F32, 1) >= 5 * (2560 + 6912)
+    assert lib.ll_gemv_plan_bytes(split, 2, L.LL_ACT_F32, 1) >= 5 * (2560 + 8448)
+    fused = two
+    # two products sharing x (same pointer and K) share one layout
+    shared = (L.ll_gemv_item * 3)(_item(64, 2560, FAKE, FAKE), _item(64, 2560, FAKE, FAKE), _item(64, 8448, FAKE * 3, FAKE))
+    b_shared = lib.ll_gemv_plan_bytes(shared, 3, L.LL_ACT_F32, 1)
+    assert 5 * (2560 + 8448) <= b_shared < 5 * (2 * 2560 + 8448)
+    assert lib.ll_gemv_plan_bytes(fused, 2, L.LL_ACT_I8, 1) == 2 ** 64 - 1
