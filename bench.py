@@ -11,13 +11,18 @@ scale of each matrix, 594.7 MB, more than twice the 256 MiB Infinity Cache)
 divided by the step time.
 
 The JSON line also carries the roofline of the dominant kernel (the batched
-product, timed live with HIP events on its stream), the CPU oracle timed on a
-bounded sample (one layer's seven products, repeated), and extras: single-call
-per-matrix GEMV times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM
-(TOPS against the int8 matrix-core peak).
+product, timed live with HIP events on its stream; its HBM traffic is taken
+from the committed rocprofv3 counter summary when that summary was made from
+the current kernel source), the CPU oracle timed on a bounded sample (one
+layer's seven products, repeated), and extras: single-call per-matrix GEMV
+times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM (TOPS against the
+int8 matrix-core peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+       python bench.py --copy-probe     (a plain 256 MiB device copy, to
+                                         calibrate rocprofv3 byte counters)
 """
+import hashlib
 import argparse
 import json
 import os
@@ -33,12 +38,56 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores, published (POP/s x 1000)
 LAYERS = 30
 HIDDEN, FFN = 2560, 6912
+# dominant kernel of a step: i2_s, M = 1, activation windows staged through LDS
+KERNEL = "gemv_planes_batch_kernel<1, 1, 0>"
+KERNEL_SOURCES = ["binary_bit_weight_amd/csrc/gemv_planes.hip", "binary_bit_weight_amd/csrc/common.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_planes_batch_i2s_m1_decode30_counters.md")
+COPY_PROBE_BYTES = 256 << 20
 ROLES = [("q", HIDDEN, HIDDEN, 0), ("k", HIDDEN, HIDDEN, 0), ("v", HIDDEN, HIDDEN, 0), ("o", HIDDEN, HIDDEN, 1),
          ("up", FFN, HIDDEN, 2), ("gate", FFN, HIDDEN, 2), ("down", HIDDEN, FFN, 3)]   # (name, N, K, x slot)
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per launch of KERNEL from the committed counter summary
+    (lines 'key: value'), or None when it is missing or was taken from
+    another version of the kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    kv[k.strip()] = v.strip().strip("`")
+        if kv.get("kernel_source_sha256_16") != kernel_source_sha():
+            return None
+        return int(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """A plain device-to-device copy of COPY_PROBE_BYTES, five times: run under
+    rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) to learn how many counter KiB
+    one byte of known traffic reads as."""
+    import torch
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 5}), flush=True)
 
 
 def build_decode_step(L, synth, torch, dev):
@@ -167,7 +216,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the product shards by output "
               "rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -220,8 +273,11 @@ def main():
                    "M": 1, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN,
                    "weight_bytes_per_step": int(weight_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_f32_batch_kernel<i2_s,1>", "kernel_ms": round(prod_ms, 4)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": int(weight_bytes),
+                     "kernel": KERNEL, "kernel_ms": round(prod_ms, 4),
+                     "kernel_source_sha256_16": kernel_source_sha()},
     }
     if not args.no_cpu:
         log("timing the CPU oracle")

@@ -32,6 +32,7 @@ __device__ __forceinline__ void st16(void* p, i32x4 v) { *(__attribute__((addres
 __device__ __forceinline__ i32x4 ld16_stream(const void* p) { return __builtin_nontemporal_load((gi32x4*)p); }
 __device__ __forceinline__ int32_t ld32(const void* p) { return *(gint32*)p; }
 __device__ __forceinline__ f32x4 ld16f(const void* p) { return *(gf32x4*)p; }
+__device__ __forceinline__ uint16_t ld2(const void* p) { return *(__attribute__((address_space(1))) const uint16_t*)p; }
 
 // Butterfly sum / max over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -43,6 +44,21 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     return v;
+}
+
+// Butterfly sums of N independent values over the 64 lanes of a wave, the N
+// shuffles of each step issued together (one LDS-permute wait per step
+// instead of one per shuffle).
+template <int N>
+__device__ __forceinline__ void wave_sum_n(int (&v)[N]) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        int t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = __shfl_xor(v[i], o, kWave);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += t[i];
+    }
 }
 
 // fp16 bits -> fp32 (exact).

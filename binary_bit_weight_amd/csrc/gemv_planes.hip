@@ -48,6 +48,9 @@ using namespace llk;
 #ifndef LL_PLANES_NT
 #define LL_PLANES_NT 1
 #endif
+#ifndef LL_PLANES_DUMMY
+#define LL_PLANES_DUMMY 0
+#endif
 
 constexpr int kP = 5;                     // activation planes
 constexpr int kWaves = LL_PLANES_WAVES;   // 16-row tiles per workgroup
@@ -58,7 +61,7 @@ constexpr int kWStride = kWinB + 16;      // padded LDS weight row
 constexpr int kWTile = 16 * kWStride;     // one wave's weight tile
 constexpr int kAStride = kWinK + 16;      // padded LDS plane row
 
-__host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * kP * M * kAStride; }
+__host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * (kP * M * kAStride + 256); }
 
 // Fused form of a single product (M = 1, K <= kFusedMaxK): every workgroup
 // builds the planes of the whole row in its LDS (no preparation launch), then
@@ -86,24 +89,25 @@ __host__ __device__ inline int fused_lds_bytes(int64_t K) {
 __device__ __forceinline__ int tq2_pos(int e) { return 64 * (e & 3) + 16 * (e >> 6) + 4 * ((e >> 4) & 3) + ((e >> 2) & 3); }
 
 // Workspace layout of one activation:
-//     planes [5M][K] | xsum [5M][nblk] (per 256-k block) | E [M] | xtot [5M] (per row).
+//     planes [5M][K] | xsum [nblk4][16] | E [M] | xtot [5M] (per row),
+// xsum[b][5m + p] the sum of plane row 5m + p over 256-k block b, blocks
+// padded to a multiple of 4 (one 1024-k window = one 256-byte piece).
 struct PlaneView {
     int8_t* planes;
     int32_t* xsum;
     int32_t* ex;
     int32_t* xtot;
 };
+__host__ __device__ inline int64_t nblk4(int64_t K) { return (K + 1023) / 1024 * 4; }
 __host__ __device__ inline size_t planes_bytes(int64_t M, int64_t K) {
-    const int64_t nblk = (K + 255) / 256;
-    return size_t((kP * M * K + 15) / 16 * 16 + kP * M * nblk * 4 + M * 4 + kP * M * 4 + 15) / 16 * 16;
+    return size_t((kP * M * K + 15) / 16 * 16 + nblk4(K) * 64 + M * 4 + kP * M * 4 + 15) / 16 * 16;
 }
 __host__ __device__ inline PlaneView plane_view(void* base, int64_t M, int64_t K) {
-    const int64_t nblk = (K + 255) / 256;
     char* p = static_cast<char*>(base);
     PlaneView v;
     v.planes = reinterpret_cast<int8_t*>(p);
     v.xsum = reinterpret_cast<int32_t*>(p + (kP * M * K + 15) / 16 * 16);
-    v.ex = v.xsum + kP * M * nblk;
+    v.ex = v.xsum + nblk4(K) * 16;
     v.xtot = v.ex + M;
     return v;
 }
@@ -127,28 +131,26 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
     const PlaneView v = plane_view(ws, M, K);
     int tot[kP] = {0, 0, 0, 0, 0};                   // this wave's share of the row's plane sums
     const int64_t nblk = (K + 255) / 256;
-    const bool vec = (K % 4) == 0;                   // always true for the formats here (K % 128 == 0)
+    // K % 128 == 0 (both formats), so k < K implies k + 3 < K.  (A scalar
+    // fallback here would turn these into FLAT loads, each waiting for the
+    // previous one.)
     auto load_chunk = [&](int64_t k0, f32x4 (&x4)[kPrepIt]) {
 #pragma unroll
         for (int i = 0; i < kPrepIt; ++i) {
             const int64_t k = k0 + 1024 * i + 4 * tid;
-            if (vec && k + 3 < K) {
-                x4[i] = ld16f(xr + k);
-            } else {
-                x4[i].x = k < K ? xr[k] : 0.f;
-                x4[i].y = k + 1 < K ? xr[k + 1] : 0.f;
-                x4[i].z = k + 2 < K ? xr[k + 2] : 0.f;
-                x4[i].w = k + 3 < K ? xr[k + 3] : 0.f;
-            }
+            x4[i] = k < K ? ld16f(xr + k) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
     float a = 0.0f;
+    f32x4 xfirst[kPrepIt];                           // the first chunk stays in registers
     for (int64_t k0 = 0; k0 < K; k0 += kPrepK) {
         f32x4 x4[kPrepIt];
         load_chunk(k0, x4);
 #pragma unroll
-        for (int i = 0; i < kPrepIt; ++i)
+        for (int i = 0; i < kPrepIt; ++i) {
             a = fmaxf(fmaxf(a, fmaxf(fabsf(x4[i].x), fabsf(x4[i].y))), fmaxf(fabsf(x4[i].z), fabsf(x4[i].w)));
+            if (k0 == 0) xfirst[i] = x4[i];
+        }
     }
     a = wave_max(a);
     if (lane == 0) smax[wave] = a;
@@ -159,7 +161,15 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
     if (tid == 0) v.ex[m] = E;
     for (int64_t k0 = 0; k0 < K; k0 += kPrepK) {
         f32x4 x4[kPrepIt];
-        load_chunk(k0, x4);                          // L2-resident re-read
+        if (k0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kPrepIt; ++i) x4[i] = xfirst[i];
+        } else {
+            load_chunk(k0, x4);                      // L2-resident re-read
+        }
+        int s[kPrepIt * kP];                         // per 1024-k slice: this thread's part of the block sums
+#pragma unroll
+        for (int e = 0; e < kPrepIt * kP; ++e) s[e] = 0;
 #pragma unroll
         for (int i = 0; i < kPrepIt; ++i) {
             const int64_t kb = k0 + 1024 * i;        // this wave's block: kb/256 + wave
@@ -192,14 +202,17 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
                     }
                 }
             }
-            const int64_t b = kb / 256 + wave;
+#pragma unroll
+            for (int p = 0; p < kP; ++p) s[i * kP + p] = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
+        }
+        wave_sum_n(s);                               // all slices at once: six permute waits
+#pragma unroll
+        for (int i = 0; i < kPrepIt; ++i) {
+            const int64_t b = (k0 + 1024 * i) / 256 + wave;
 #pragma unroll
             for (int p = 0; p < kP; ++p) {
-                int s = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-                if (lane == 0 && b < nblk) v.xsum[int64_t(m * kP + p) * nblk + b] = s;
-                tot[p] += s;
+                if (lane == 0 && b < nblk) v.xsum[b * 16 + m * kP + p] = s[i * kP + p];
+                tot[p] += s[i * kP + p];
             }
         }
     }
@@ -248,6 +261,9 @@ __device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K
     int E = 0;
     if (a > 0.0f) (void)frexpf(a, &E);                // 2^(E-1) <= a < 2^E
     int tot[kP] = {0, 0, 0, 0, 0};
+    int bs[kXIt * kP];                                // TQ2_0: this thread's part of each block sum
+#pragma unroll
+    for (int e = 0; e < kXIt * kP; ++e) bs[e] = 0;
 #pragma unroll
     for (int i = 0; i < kXIt; ++i) {
         const int64_t kb = 4 * kThreads * i;
@@ -279,28 +295,30 @@ __device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K
                 }
             }
         }
+        int s4[kP];
+#pragma unroll
+        for (int p = 0; p < kP; ++p) s4[p] = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
-            const int s4 = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
-            if (FMT == 1) {
-                tot[p] += s4;
-            } else {
-                int sw = s4;
+            if (FMT == 1) tot[p] += s4[p];
+            else bs[i * kP + p] = s4[p];
+        }
+    }
+    if (FMT == 2) {
+        wave_sum_n(bs);
 #pragma unroll
-                for (int o = 32; o > 0; o >>= 1) sw += __shfl_xor(sw, o, 64);
-                const int b = kWaves * i + wave;
-                if (lane == 0 && b < nblk) sums[p * nblk + b] = sw;
-            }
+        for (int i = 0; i < kXIt; ++i) {
+            const int b = kWaves * i + wave;
+#pragma unroll
+            for (int p = 0; p < kP; ++p)
+                if (lane == 0 && b < nblk) sums[p * nblk + b] = bs[i * kP + p];
         }
     }
     if (FMT == 1) {
+        wave_sum_n(tot);
 #pragma unroll
-        for (int p = 0; p < kP; ++p) {
-            int sw = tot[p];
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) sw += __shfl_xor(sw, o, 64);
-            if (lane == 0) sums[wave * kP + p] = sw;
-        }
+        for (int p = 0; p < kP; ++p)
+            if (lane == 0) sums[wave * kP + p] = tot[p];
     }
     return E;
 }
@@ -322,15 +340,26 @@ __host__ __device__ constexpr int field_mul(int t) {
     return (FMT == 1 ? 6 - 2 * t : 2 * t) >= 4 ? 16 : ((FMT == 1 ? 6 - 2 * t : 2 * t) == 2 ? 4 : 1);
 }
 
-// FUSED: src is the fp32 token row (M == 1); otherwise the prepared workspace.
-template <int FMT, int M, bool FUSED>
+// Where the activation operand comes from.
+//   kWindowed: prepared workspace, staged per window through a shared,
+//              double-buffered LDS window (one workgroup barrier per window);
+//   kFused:    the fp32 row x (M == 1), split into planes by the workgroup,
+//              whole row in LDS, no barrier in the main loop.
+// (Copying a prepared row whole into LDS instead of windowing it was
+// measured slower in batches: the larger LDS lowers occupancy more than
+// the barriers cost.)
+enum { kWindowed = 0, kFused = 1 };
+
+template <int FMT, int M, int MODE>
 __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int64_t N, int64_t K, const void* __restrict__ ws,
                                             const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
                                             char* __restrict__ lds) {
-    static_assert(!FUSED || M == 1, "the fused form handles one token");
+    constexpr bool FUSED = MODE == kFused;
+    constexpr bool WHOLE = FUSED;                      // whole plane row in LDS
+    static_assert(!WHOLE || M == 1, "whole-row forms handle one token");
     constexpr int RR = kP * M;                          // plane rows in use (<= 15)
-    constexpr int kAChunks = FUSED ? 1 : (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
+    constexpr int kAChunks = WHOLE ? 1 : (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
     const int arow = nl < RR ? nl : RR - 1;             // rows >= RR of the operand are never used
@@ -340,8 +369,8 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     const PlaneView pv = plane_view(const_cast<void*>(ws), M, K);
     char* wtile = lds + wave * kWTile;                  // private to this wave
     int8_t* abuf = reinterpret_cast<int8_t*>(lds + kWaves * kWTile);
-    constexpr int abytes = RR * kAStride;
-    const int astride = FUSED ? fused_astride(K) : kAStride;
+    constexpr int abytes = RR * kAStride + 256;          // planes, then the window's block sums
+    const int astride = WHOLE ? fused_astride(K) : kAStride;
     int* fsums = reinterpret_cast<int*>(abuf + kP * fused_astride(K));           // fused only
     float* fsmax = reinterpret_cast<float*>(fsums + fused_sums(K));
 
@@ -365,41 +394,73 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     struct Regs {
         i32x4 w[4 * kLPR];
         i32x4 a[kAChunks];
+        i32x4 xs;                                          // TQ2_0: block sums of the window (16 B per thread)
+        uint16_t sc[kWinK / 256];                          // TQ2_0: scales of this lane's row
     };
+    uint16_t csc[kWinK / 256];                             // scales of the window being multiplied
+    // Every load of a window is issued by every lane from an in-bounds
+    // (clamped) address; chunks past the end of a row are zeroed when stored
+    // to LDS.  (Lane-divergent branches around the loads made the compiler
+    // wait for all outstanding loads before each LDS store.)  The prefetch of
+    // a window past the last one is skipped with a uniform branch; issuing it
+    // anyway on a few hot bytes (LL_PLANES_DUMMY=1) gives the compiler exact
+    // wait counts, i.e. a full two-window prefetch, but measured slower on
+    // the decode step (more requests in flight, no gain in bandwidth).
+    const uint8_t* dummy = static_cast<const uint8_t*>(ws) + 16 * nl;
     auto load = [&](int w, Regs& r) {
+        const bool live = w < nwin;
 #pragma unroll
         for (int j = 0; j < kLPR; ++j) {
             const uint32_t off = uint32_t(w) * kWinB + 256 * j + 16 * nl;
+            const uint32_t offc = off < rowbytes ? off : rowbytes - 16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint8_t* p = lrow[i] + uint32_t(w) * kWinB + 256 * j;
-                r.w[4 * j + i] = (off < rowbytes) ? (LL_PLANES_NT ? ld16_stream(p) : ld16(p)) : i32x4{0, 0, 0, 0};
+                const uint8_t* p = live ? lrow[i] - 16 * nl + offc : dummy;
+                r.w[4 * j + i] = LL_PLANES_NT ? ld16_stream(p) : ld16(p);
             }
         }
-        if constexpr (!FUSED) {
+        if constexpr (!WHOLE) {
 #pragma unroll
             for (int i = 0; i < kAChunks; ++i) {
                 const int c = tid + 64 * kWaves * i;
                 const int row = c / kAPerRow, col = c % kAPerRow;
                 const int64_t k = int64_t(w) * kWinK + 16 * col;
-                r.a[i] = (row < RR && k < K) ? ld16(pv.planes + int64_t(row) * K + k) : i32x4{0, 0, 0, 0};
+                r.a[i] = ld16(pv.planes + int64_t(row < RR ? row : RR - 1) * K + (k < K ? k : K - 16));
+            }
+            if (FMT == 2) r.xs = ld16(pv.xsum + 64 * (live ? w : nwin - 1) + 4 * (tid & 15));
+        }
+        if (FMT == 2) {
+#pragma unroll
+            for (int t = 0; t < kWinK / 256; ++t) {
+                const int b = (kWinK / 256) * w + t;
+                r.sc[t] = ld2(srow + (b < nblk ? b : nblk - 1));
             }
         }
     };
-    auto store_w = [&](const Regs& r) {
+    auto store_w = [&](int w, const Regs& r) {
+        if (FMT == 2)
 #pragma unroll
-        for (int j = 0; j < kLPR; ++j)
+            for (int t = 0; t < kWinK / 256; ++t) csc[t] = r.sc[t];
+#pragma unroll
+        for (int j = 0; j < kLPR; ++j) {
+            const bool ok = uint32_t(w) * kWinB + 256 * j + 16 * nl < rowbytes;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<i32x4*>(wtile + (4 * i + q) * kWStride + 256 * j + 16 * nl) = r.w[4 * j + i];
+                *reinterpret_cast<i32x4*>(wtile + (4 * i + q) * kWStride + 256 * j + 16 * nl) =
+                    ok ? r.w[4 * j + i] : i32x4{0, 0, 0, 0};
+        }
     };
-    auto store_a = [&](int buf, const Regs& r) {
+    auto store_a = [&](int w, const Regs& r) {
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + 64 * kWaves * i;
             const int row = c / kAPerRow, col = c % kAPerRow;
-            if (row < RR) *reinterpret_cast<i32x4*>(abuf + buf * abytes + row * kAStride + 16 * col) = r.a[i];
+            const bool ok = int64_t(w) * kWinK + 16 * col < K;
+            if (row < RR)
+                *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + row * kAStride + 16 * col) =
+                    ok ? r.a[i] : i32x4{0, 0, 0, 0};
         }
+        if (FMT == 2 && tid < 16) *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + RR * kAStride + 16 * tid) = r.xs;
     };
 
     i32x4 acc[4];                                        // i2_s: one accumulator per field
@@ -409,7 +470,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
 
     auto compute = [&](int w) {
         const char* wb = wtile + nl * kWStride + 16 * q;
-        const int8_t* ab = FUSED ? abuf + arow * astride + w * kWinK : abuf + (w & 1) * abytes + arow * kAStride;
+        const int8_t* ab = WHOLE ? abuf + arow * astride + w * kWinK : abuf + (w & 1) * abytes + arow * kAStride;
 #pragma unroll
         for (int seg = 0; seg < kWinK / 256; ++seg) {
             const int s = (kWinK / 256) * w + seg;         // 256-k segment (= TQ2_0 block)
@@ -440,11 +501,14 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
             }
             if (FMT == 2) {
                 // C lane (column nl, quarter q) holds plane rows 4q..4q+3
-                const double sc = double(half_bits_to_float(srow[s]));
+                const double sc = double(half_bits_to_float(csc[seg]));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q + r;
-                    const int xs = row >= RR ? 0 : FUSED ? fsums[row * nblk + s] : ld32(pv.xsum + row * nblk + s);
+                    const int xs = row >= RR ? 0
+                                   : WHOLE ? fsums[row * nblk + s]
+                                           : *reinterpret_cast<const int*>(abuf + (w & 1) * abytes + RR * kAStride +
+                                                                           4 * (16 * seg + row));
                     int dot = 0;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) dot += bacc[t][r] / field_mul<FMT>(t);
@@ -459,11 +523,11 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
 
     Regs r0, r1;
     load(0, r0);
-    if (nwin > 1) load(1, r1);
+    load(1, r1);
     int Ef = 0;
     if constexpr (FUSED) Ef = fused_prep<FMT>(static_cast<const float*>(ws), K, abuf, astride, fsums, fsmax);
-    store_w(r0);
-    if constexpr (!FUSED) store_a(0, r0);
+    store_w(0, r0);
+    if constexpr (!WHOLE) store_a(0, r0);
     __syncthreads();
     // Window w is multiplied from LDS while window w+1 waits in registers and
     // window w+2 is being fetched.  The weight tile is private to the wave:
@@ -471,23 +535,23 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     // multiply needs no workgroup barrier; the barrier orders the shared
     // activation window (the fused form holds the whole row: no barrier).
     for (int w = 0; w < nwin; w += 2) {
-        if (w + 2 < nwin) load(w + 2, r0);
+        if (LL_PLANES_DUMMY || w + 2 < nwin) load(w + 2, r0);
         compute(w);
         if (w + 1 < nwin) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            store_w(r1);
-            if constexpr (!FUSED) store_a((w + 1) & 1, r1);
+            store_w(w + 1, r1);
+            if constexpr (!WHOLE) store_a(w + 1, r1);
         }
-        if constexpr (!FUSED) __syncthreads();
+        if constexpr (!WHOLE) __syncthreads();
         if (w + 1 >= nwin) break;
-        if (w + 3 < nwin) load(w + 3, r1);
+        if (LL_PLANES_DUMMY || w + 3 < nwin) load(w + 3, r1);
         compute(w + 1);
         if (w + 2 < nwin) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            store_w(r0);
-            if constexpr (!FUSED) store_a((w + 2) & 1, r0);
+            store_w(w + 2, r0);
+            if constexpr (!WHOLE) store_a(w + 2, r0);
         }
-        if constexpr (!FUSED) __syncthreads();
+        if constexpr (!WHOLE) __syncthreads();
     }
 
     // per plane row: D_row = (i2_s) sum_t acc_t / mul_t - total plane sum, or
@@ -542,7 +606,7 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_kernel(const uint8_t*
                                                                    const float* __restrict__ bias,
                                                                    float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT, M, false>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    planes_rows<FMT, M, kWindowed>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 template <int FMT>
@@ -552,7 +616,7 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_fused_kernel(const ui
                                                                          const float* __restrict__ bias,
                                                                          float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT, 1, true>(codes, scales, N, K, x, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    planes_rows<FMT, 1, kFused>(codes, scales, N, K, x, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 struct PlanesProb {          // product of a prepared batch
@@ -573,13 +637,13 @@ struct PlanesPrep {          // distinct activation of a prepared batch
 
 // Workgroup wg of a batch runs product map[wg] (one table load instead of a
 // search: a workgroup's first weight fetch waits on this lookup).
-template <int FMT, int M>
+template <int FMT, int M, int MODE>
 __global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const PlanesProb* __restrict__ tab,
                                                                          const int32_t* __restrict__ map) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t wg = blockIdx.x;
     const PlanesProb& P = tab[ld32(map + wg)];
-    planes_rows<FMT, M, false>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
+    planes_rows<FMT, M, MODE>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
 }
 
 template <int FMT>
@@ -623,9 +687,9 @@ template <int FMT, int M>
 hipError_t launch_batch(const PlanesProb* tab, const int32_t* map, int64_t wgs, hipStream_t stream) {
     const dim3 grid{unsigned(wgs)}, block{64 * kWaves};
     const size_t lds = size_t(lds_bytes(M));
-    hipError_t e = allow_lds(gemv_planes_batch_kernel<FMT, M>, lds);
+    hipError_t e = allow_lds(gemv_planes_batch_kernel<FMT, M, kWindowed>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemv_planes_batch_kernel<FMT, M>), grid, block, lds, stream, tab, map);
+    hipLaunchKernelGGL((gemv_planes_batch_kernel<FMT, M, kWindowed>), grid, block, lds, stream, tab, map);
     return hipGetLastError();
 }
 
