@@ -113,6 +113,18 @@ def build_decode_step(L, synth, torch, dev):
     return packed, items, weight_bytes
 
 
+def w1_weights(L, synth, seed, N, K, G):
+    """Sign bits and fp16 group mean-abs scales of dense N(0, 0.02) rows
+    (generated in 4096-row chunks, converted by ll_w1_from_dense)."""
+    bits = np.empty((N, K // 32), np.uint32)
+    scales = np.empty((N, K // G), np.uint16)
+    for c in range((N + synth.CHUNK_ROWS - 1) // synth.CHUNK_ROWS):
+        r0 = c * synth.CHUNK_ROWS
+        rows = min(synth.CHUNK_ROWS, N - r0)
+        bits[r0:r0 + rows], scales[r0:r0 + rows] = L.ll_w1_from_dense(synth.dense_chunk(seed, K, c, rows), G)
+    return bits, scales
+
+
 def time_events(torch, fn, reps, stream):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
@@ -184,6 +196,30 @@ def extras_single(L, synth, torch, dev, stream):
         out["tq2_gemv_f32_single_call_6912x2560_M%d" % M] = {
             "us": round(ms * 1e3, 2), "GB_s": round(blocks.size / (ms * 1e-3) / 1e9, 1),
             "GFLOP_s": round(2 * M * N * K / (ms * 1e-3) / 1e9, 1)}
+    # W1A8 decode, hidden 5120, G = 128: QKV, MLP gate, LM head at M = 1 and 8
+    K, G = 5120, 128
+    for name, N, seed in [("qkv", 7168, 501), ("gate", 17408, 502), ("lm_head", 248320, 503)]:
+        bits, sc = w1_weights(L, synth, seed, N, K, G)
+        wbytes = bits.nbytes + sc.nbytes
+        reps = max(1, int(np.ceil(2 ** 29 / wbytes)))
+        Ws = [L.upload_w1(bits, sc, K, G, dev) for _ in range(reps)]
+        for M in (1, 8):
+            x = torch.from_numpy(synth.normal_f32(510 + M, M, K)).to(dev)
+            xq, xsc = L.quantize(x, stream)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
+            it = iter(range(10 ** 9))
+
+            def one():
+                L.ll_bitlinear_gemv(Ws[next(it) % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream)
+            for _ in range(reps):
+                one()
+            ms = time_events(torch, one, max(2 * reps, 10), stream)
+            out["w1a8_gemv_%s_%dx%d_M%d" % (name, N, K, M)] = {
+                "us": round(ms * 1e3, 2), "GB_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}
+        del Ws
+        torch.cuda.empty_cache()
     # int8 prefill GEMM, M=512 (bf16 activations quantized per token)
     for N, K in [(6912, 2560), (2560, 6912)]:
         w = synth.ternary(401, N, K)

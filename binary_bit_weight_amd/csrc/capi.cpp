@@ -15,6 +15,14 @@ ll_status hip_status(hipError_t e, const char* what) {
 }
 
 // Shape and pointer checks common to every product entry point.
+// The W1 device kernels work on 128-k chunks: K % 128 == 0, G in {32, 64, 128, 256}.
+ll_status check_w1_device(const ll_weights* w, const char* fn) {
+    if (w->K % 128) return ll::failf(LL_ESHAPE, "%s: the W1 device path needs K %% 128 == 0", fn);
+    if (w->group != 32 && w->group != 64 && w->group != 128 && w->group != 256)
+        return ll::failf(LL_ESHAPE, "%s: the W1 device path needs group 32, 64, 128 or 256", fn);
+    return LL_OK;
+}
+
 ll_status check_weights(const ll_weights* w, const char* fn) {
     if (!w) return ll::failf(LL_EINVAL, "%s: weights descriptor is NULL", fn);
     if (w->N <= 0 || w->K <= 0) return ll::failf(LL_EINVAL, "%s: N and K must be positive", fn);
@@ -61,7 +69,7 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M) {
     if (!w || M < 1 || M > 16 || w->K <= 0) return size_t(-1);
     if (act == LL_ACT_F32)
         return M <= llk::kPlanesMaxM ? llk::planes_workspace(M, w->K) : llk::gemv_f32_workspace(M, w->K);
-    if (act == LL_ACT_I8) return 0;
+    if (act == LL_ACT_I8) return w->fmt == LL_FMT_W1 && w->group > 0 ? llk::w1_workspace(M, w->K, w->group) : 0;
     return size_t(-1);
 }
 
@@ -99,6 +107,18 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
             return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K,
                                                       static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, s),
                               fn);
+        if (w->fmt == LL_FMT_W1) {
+            st = check_w1_device(w, fn);
+            if (st) return st;
+            const size_t need = llk::w1_workspace(M, w->K, w->group);
+            if (!workspace || workspace_bytes < need)
+                return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
+            if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
+            return hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes),
+                                                  static_cast<const uint16_t*>(w->scales), w->N, w->K, w->group,
+                                                  static_cast<const int8_t*>(x), xs, M, bias, y, workspace, s),
+                              fn);
+        }
         return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: int8 activations with this format are not supported");
     }
     return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: unknown activation type");
@@ -106,13 +126,12 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
 
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     if (!w || M < 1) return size_t(-1);
+    if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->K, w->group);
     return 0;
 }
 
 ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
                             float* y, int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     const char* fn = "ll_bitlinear_gemm";
     ll_status st = check_weights(w, fn);
     if (st) return st;
@@ -121,7 +140,20 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
     if (!aligned(xq, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xq must be 16-byte aligned");
     if (!aligned(xs, 4) || !aligned(y, 4) || (bias && !aligned(bias, 4)) || (acc_out && !aligned(acc_out, 4)))
         return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xs / y / bias / acc_out must be 4-byte aligned");
-    if (w->fmt != LL_FMT_I2S) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: only format i2_s is supported");
+    if (w->fmt == LL_FMT_W1) {
+        st = check_w1_device(w, fn);
+        if (st) return st;
+        if (acc_out) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for W1 (per-group scales)");
+        const size_t need = llk::w1_workspace(M, w->K, w->group);
+        if (!workspace || workspace_bytes < need)
+            return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
+        if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
+        return hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes),
+                                              static_cast<const uint16_t*>(w->scales), w->N, w->K, w->group, xq, xs, M,
+                                              bias, y, workspace, static_cast<hipStream_t>(stream)),
+                          fn);
+    }
+    if (w->fmt != LL_FMT_I2S) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s and W1 only");
     return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y,
                                               acc_out, static_cast<hipStream_t>(stream)),
                       fn);

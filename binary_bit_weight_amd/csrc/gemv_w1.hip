@@ -1,0 +1,448 @@
+// W1A8 product: binary weights (one sign bit each, one fp16 scale per group of
+// G weights), int8 activations with a per-token scale, 1 <= M <= 16.
+//
+// [BG "Method"] With the stored bit b = (w + 1) / 2 the group dot product is
+//     d = sum w*q = 2 * sum_{b=1} q - sum q,
+// so only sum_{b=1} q has to be formed from the bits.  It runs on the fp8 x fp4
+// matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales):
+//   B (weights): a 32-bit word of bits masked in place, (word >> j) & 0x11111111,
+//       is eight fp4 (e2m1) values b * 0.5 -- no unpacking beyond one shift
+//       and one AND per 8 weights;
+//   A (activations): q = 16 * hi + lo with hi, lo in [-8, 8], both exact in
+//       fp8 e4m3, one MFMA row each; rows are (token, group slot, digit).
+// Every product is a multiple of 1/4 below 2^10 and every sum stays below
+// 2^22, so the fp32 accumulation is exact: sum_{b=1} q = 2 * (16 D_hi + D_lo).
+// The epilogue forms S = sum_g s_g * d_g with fp64 fmas of exact products in
+// group order and y = (float)((double)xs * S) (+ bias), bit for bit the
+// oracle's result.
+//
+// Operand layout.  For the 16x16x128 f8f6f4 MFMA with fp8 A and fp4 B the
+// hardware pairs A element (lane quarter q, byte e) with B element (lane
+// quarter q' = 2(e/16) + q/2, nibble e' = 16(q%2) + e%16) of the same
+// column/row lane index (measured on the device).  B lane quarter q' holds
+// word q' of the 128-k chunk of its row, its nibble e' = 8j + i being bit
+// 4i + j, i.e. chunk-local weight 32q' + 4(e'%8) + e'/8.  The preparation
+// kernel writes each A row in the matching order.
+//
+// Memory.  A workgroup is 4 waves x 32 rows (two 16-column MFMA blocks per
+// wave).  Per 1024-k window each wave loads its rows as 8 rows x 128
+// contiguous bytes per instruction into a padded LDS tile private to the
+// wave, together with the window's group scales; the prepared A rows and
+// group sums of the window are staged in a shared, double-buffered LDS
+// window.  Loads run two windows ahead of the multiply.
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+using namespace llk;
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+constexpr int kW1Waves = 4;
+constexpr int kW1RowsPerWave = 32;
+constexpr int kW1Rows = kW1Waves * kW1RowsPerWave;   // 128 rows per workgroup
+constexpr int kWinK1 = 1024;                          // k per window
+constexpr int kWinB1 = kWinK1 / 8;                    // 128 code bytes per row per window
+constexpr int kChunks = kWinK1 / 128;                 // 8 MFMA chunks per window
+
+// LDS row of a wave's tile: 128 code bytes | the window's scales (1024/G fp16) | pad to 16 mod 128.
+__host__ __device__ inline int w1_stride(int G) {
+    const int raw = kWinB1 + 2 * (kWinK1 / G);
+    return (raw + 127) / 128 * 128 + 16;
+}
+
+// Rows of the A operand: (token m, group slot j, digit h) -> 2 (m S + j) + h,
+// S = 128 / G slots per 128-k chunk (1 for G >= 128).
+__host__ __device__ inline int w1_slots(int G) { return G >= 128 ? 1 : 128 / G; }
+__host__ __device__ inline int w1_arows(int M, int G) { return 2 * M * w1_slots(G); }
+
+// Workspace of one activation: A [K/128 chunks][R rows][128 B] | qs [M][K/G] int32.
+__host__ __device__ inline size_t w1_a_bytes(int64_t M, int64_t K, int G) {
+    return size_t(K / 128) * size_t(w1_arows(int(M), G)) * 128;
+}
+__host__ __device__ inline size_t w1_ws_bytes(int64_t M, int64_t K, int G) {
+    return (w1_a_bytes(M, K, G) + 15) / 16 * 16 + size_t(M) * size_t(K / G) * 4;
+}
+
+// A window in LDS: [chunk 8][R rows][128 B] | zero row [128 B] | qs [M][1024/G] int32.
+__host__ __device__ inline int w1_abuf_bytes(int M, int G) {
+    return kChunks * w1_arows(M, G) * 128 + 128 + M * (kWinK1 / G) * 4;
+}
+__host__ __device__ inline int w1_lds_bytes(int M, int G) {
+    return kW1Waves * kW1RowsPerWave * w1_stride(G) + 2 * ((w1_abuf_bytes(M, G) + 15) / 16 * 16);
+}
+
+__device__ __forceinline__ uint8_t fp8_small_int(int v) {
+    // exact e4m3 encoding of an integer in [-8, 8]
+    const int a = v < 0 ? -v : v;
+    int code;
+    if (a == 0) code = 0;
+    else if (a == 1) code = 0x38;
+    else if (a < 4) code = 0x40 | ((a - 2) << 2);          // 2 -> 0x40, 3 -> 0x44
+    else if (a < 8) code = 0x48 | ((a - 4) << 1);          // 4..7 -> 0x48, 0x4A, 0x4C, 0x4E
+    else code = 0x50;                                      // 8
+    return uint8_t(code | (v < 0 ? 0x80 : 0));
+}
+
+// ---------------------------------------------------------------- preparation
+// One thread per 16-byte piece of an A row (chunk c, row r, piece u), plus the
+// group sums.  Grid: (ceil(chunks * R * 8 / 256), 1) and a second pass over
+// groups.  Reads xq [M][K] int8.
+__global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
+                                                      void* __restrict__ ws) {
+    const int S = w1_slots(G), R = w1_arows(int(M), G);
+    const int64_t pieces = (K / 128) * R * 8;
+    const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    int8_t* A = static_cast<int8_t*>(ws);
+    if (id < pieces) {
+        const int u = int(id % 8);
+        const int r = int((id / 8) % R);
+        const int64_t c = id / (8 * int64_t(R));
+        const int h = r & 1, pm = r >> 1;
+        const int m = pm / S, j = pm % S;
+        const int8_t* xr = xq + int64_t(m) * K + 128 * c;
+        uint32_t out[4];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int pos = 16 * u + 4 * w4 + bb;      // byte of the 128-byte row
+                const int q = pos >> 5, e = pos & 31;       // A lane quarter, byte in lane
+                const int qp = 2 * (e >> 4) + (q >> 1);     // paired B lane quarter
+                const int ep = 16 * (q & 1) + (e & 15);     // paired B nibble
+                const int kw = 32 * qp + 4 * (ep & 7) + (ep >> 3);
+                const bool in_slot = G >= 128 || kw / G == j;
+                int v = in_slot ? int(xr[kw]) : 0;
+                const int hi = (v + 8) >> 4;                // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
+                const int d = h == 0 ? hi : v - 16 * hi;
+                word |= uint32_t(fp8_small_int(d)) << (8 * bb);
+            }
+            out[w4] = word;
+        }
+        st16(A + (c * R + r) * 128 + 16 * u, i32x4{int(out[0]), int(out[1]), int(out[2]), int(out[3])});
+    }
+}
+
+// Group sums qs[m][g] = sum_{k in g} q: one wave per (token, group).
+__global__ void __launch_bounds__(256) w1_qsum_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
+                                                      void* __restrict__ ws) {
+    const int lane = threadIdx.x & 63;
+    const int64_t ng = K / G;
+    const int64_t item = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (item >= M * ng) return;
+    const int64_t m = item / ng, g = item % ng;
+    int s = 0;
+    for (int i = lane; i < G; i += 64) s += xq[m * K + g * G + i];
+    int v[1] = {s};
+    wave_sum_n(v);
+    int32_t* qs = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
+    if (lane == 0) qs[m * ng + g] = v[0];
+}
+
+// ---------------------------------------------------------------- product
+// G: group size; MT: A row blocks of 16 (R = 2 M S <= 16 MT rows); NP: pairs
+// (token, slot) per lane and row block that can be live (1 when R <= 2, else 2).
+template <int G, int MT, int NP>
+__global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* __restrict__ bits,
+                                                                 const uint16_t* __restrict__ scales, int64_t N,
+                                                                 int64_t K, int M, const void* __restrict__ ws,
+                                                                 const float* __restrict__ xs,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nl = lane & 15, q = lane >> 4;
+    constexpr int S = G >= 128 ? 1 : 128 / G;
+    const int R = w1_arows(M, G);
+    constexpr int stride = (kWinB1 + 2 * (kWinK1 / G) + 127) / 128 * 128 + 16;
+    constexpr int ngw = kWinK1 / G;                        // groups per window
+    const int64_t ng = K / G;
+    const uint32_t rowbytes = uint32_t(K / 8);
+    const int nwin = int((K + kWinK1 - 1) / kWinK1);
+    const int64_t n0 = int64_t(blockIdx.x) * kW1Rows + kW1RowsPerWave * wave;
+    char* wtile = lds + wave * kW1RowsPerWave * stride;
+    const int abytes = (w1_abuf_bytes(M, G) + 15) / 16 * 16;
+    char* abase = lds + kW1Waves * kW1RowsPerWave * stride;
+    const int8_t* Ag = static_cast<const int8_t*>(ws);
+    const int32_t* qsg = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
+
+    // weight loads: 8 rows x 128 B per instruction, lane -> row 8i + lane/8, bytes 16 (lane%8)
+    const int lr = lane >> 3, lc = lane & 7;
+    const uint8_t* wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t n = n0 + 8 * i + lr;
+        n = n < N ? n : N - 1;
+        wrow[i] = reinterpret_cast<const uint8_t*>(bits) + n * int64_t(rowbytes) + 16 * lc;
+    }
+    // scale loads: 32 rows x ngw scales per window, one fp16 per lane and load
+    constexpr int kScMax = (kW1RowsPerWave * ngw + 63) / 64;
+    constexpr int nsc = kScMax;
+    // A window loads: R rows x 8 chunks x 128 B = 64 R pieces of 16 B; qs: M x ngw ints
+    const int apieces = 64 * R;
+    constexpr int kAMax = NP == 1 ? 1 : (16 * MT * 64 + 255) / 256;
+    struct Regs {
+        i32x4 w[4];
+        uint16_t sc[kScMax];
+        i32x4 a[kAMax];
+        int32_t qs[2];
+    };
+    auto load = [&](int w, Regs& r) {
+        const uint32_t off = uint32_t(w) * kWinB1 + 16 * lc;
+        const uint32_t offc = off < rowbytes ? off : rowbytes - 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.w[i] = ld16_stream(wrow[i] - 16 * lc + offc);
+#pragma unroll
+        for (int u = 0; u < kScMax; ++u) {
+            if (u < nsc) {
+                const int e = lane + 64 * u;
+                const int row = e / ngw, gi = e % ngw;
+                int64_t n = n0 + (row < kW1RowsPerWave ? row : kW1RowsPerWave - 1);
+                n = n < N ? n : N - 1;
+                int64_t g = int64_t(w) * ngw + gi;
+                g = g < ng ? g : ng - 1;
+                r.sc[u] = ld2(scales + n * ng + g);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kAMax; ++i) {
+            if (i * 256 < apieces) {
+                const int p = tid + 256 * i;
+                const int pc = p < apieces ? p : apieces - 1;
+                const int c = pc / (8 * R), rem = pc % (8 * R);
+                int64_t cg = int64_t(w) * kChunks + c;
+                const int64_t nchunk = K / 128;
+                cg = cg < nchunk ? cg : nchunk - 1;
+                r.a[i] = ld16(Ag + (cg * R) * 128 + 16 * rem);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + 256 * i;
+            const int m = e / ngw, gi = e % ngw;
+            int64_t g = int64_t(w) * ngw + gi;
+            g = g < ng ? g : ng - 1;
+            r.qs[i] = ld32(qsg + int64_t(m < M ? m : M - 1) * ng + g);
+        }
+    };
+    auto store_w = [&](int w, const Regs& r) {
+        const bool ok = uint32_t(w) * kWinB1 + 16 * lc < rowbytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<i32x4*>(wtile + (8 * i + lr) * stride + 16 * lc) = ok ? r.w[i] : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kScMax; ++u) {
+            if (u < nsc) {
+                const int e = lane + 64 * u;
+                const int row = e / ngw, gi = e % ngw;
+                if (row < kW1RowsPerWave)
+                    *reinterpret_cast<uint16_t*>(wtile + row * stride + kWinB1 + 2 * gi) = r.sc[u];
+            }
+        }
+    };
+    auto store_a = [&](int w, const Regs& r) {
+        char* ab = abase + (w & 1) * abytes;
+#pragma unroll
+        for (int i = 0; i < kAMax; ++i) {
+            const int p = tid + 256 * i;
+            if (i * 256 < apieces && p < apieces) *reinterpret_cast<i32x4*>(ab + 16 * p) = r.a[i];
+        }
+        int32_t* qsl = reinterpret_cast<int32_t*>(ab + kChunks * R * 128 + 128);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + 256 * i;
+            if (e < M * ngw) qsl[e] = r.qs[i];
+        }
+    };
+
+    // zero rows (read by lanes whose A row is >= R) in both buffers
+    if (tid < 16) {
+        *reinterpret_cast<i32x4*>(abase + kChunks * R * 128 + 16 * (tid & 7) + 0 * abytes) = i32x4{0, 0, 0, 0};
+        *reinterpret_cast<i32x4*>(abase + kChunks * R * 128 + 16 * (tid & 7) + 1 * abytes) = i32x4{0, 0, 0, 0};
+    }
+
+    f32x4 acc[2][MT];
+    double sacc[2][MT][NP];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int b = 0; b < MT; ++b) {
+            acc[cb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < NP; ++t) sacc[cb][b][t] = 0.0;
+        }
+
+    constexpr int cpg = G >= 128 ? G / 128 : 1;            // chunks per group
+    auto compute = [&](int w) {
+        const char* ab = abase + (w & 1) * abytes;
+        const int32_t* qsl = reinterpret_cast<const int32_t*>(ab + kChunks * R * 128 + 128);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int64_t cg = int64_t(w) * kChunks + c;   // global chunk
+            if (cg >= K / 128) break;
+            // A operands (32 bytes per lane and row block)
+            i32x8 av[MT];
+#pragma unroll
+            for (int b = 0; b < MT; ++b) {
+                const int r = 16 * b + nl;
+                const char* ap = r < R ? ab + (c * R + r) * 128 + 32 * q : ab + kChunks * R * 128;   // zero row
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
+                av[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(wtile + (16 * cb + nl) * stride + 16 * c + 4 * q);
+                const i32x8 bv{int(word & 0x11111111u), int((word >> 1) & 0x11111111u), int((word >> 2) & 0x11111111u),
+                               int((word >> 3) & 0x11111111u), 0, 0, 0, 0};
+                const bool first = (cg % cpg) == 0;
+#pragma unroll
+                for (int b = 0; b < MT; ++b)
+                    acc[cb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av[b], bv, first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[cb][b], 0, 4, 0, 127, 0, 127);
+            }
+            if ((cg % cpg) == cpg - 1) {
+                // epilogue of the group(s) ending with this chunk
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const char* srow = wtile + (16 * cb + nl) * stride + kWinB1;
+#pragma unroll
+                    for (int b = 0; b < MT; ++b) {
+#pragma unroll
+                        for (int t = 0; t < NP; ++t) {
+                            const int p = 8 * b + 2 * q + t;          // (token, slot) pair
+                            const int m = p / S, j = p % S;
+                            const int64_t g = G >= 128 ? cg / cpg : cg * S + j;
+                            const int gi = int(g - int64_t(w) * ngw);  // group within the window
+                            const float v = __builtin_fmaf(16.0f, acc[cb][b][2 * t], acc[cb][b][2 * t + 1]);
+                            const int qsv = qsl[(m < M ? m : 0) * ngw + gi];
+                            const int d = int(4.0f * v) - qsv;
+                            const double s = double(half_bits_to_float(*reinterpret_cast<const uint16_t*>(srow + 2 * gi)));
+                            sacc[cb][b][t] = __builtin_fma(s, double(d), sacc[cb][b][t]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    Regs r0, r1;
+    load(0, r0);
+    if (nwin > 1) load(1, r1);
+    store_w(0, r0);
+    store_a(0, r0);
+    __syncthreads();
+    for (int w = 0; w < nwin; w += 2) {
+        if (w + 2 < nwin) load(w + 2, r0);
+        compute(w);
+        if (w + 1 < nwin) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            store_w(w + 1, r1);
+            store_a(w + 1, r1);
+        }
+        __syncthreads();
+        if (w + 1 >= nwin) break;
+        if (w + 3 < nwin) load(w + 3, r1);
+        compute(w + 1);
+        if (w + 2 < nwin) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            store_w(w + 2, r0);
+            store_a(w + 2, r0);
+        }
+        __syncthreads();
+    }
+
+    // y[m][n] = (float)((double)xs[m] * S[m][n]) (+ bias).  Pair p = m S + j
+    // of row block b lives in lane quarter (p % 8) / 2, slot t = p % 2; the S
+    // slots of one token (G < 128) are added through LDS (every partial sum
+    // is exact, so the order of groups does not matter).
+    __syncthreads();
+    double* red = reinterpret_cast<double*>(lds);      // [2 cb][16 col][pairs up to 8 MT]
+    const int npairs = 8 * MT;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int b = 0; b < MT; ++b)
+#pragma unroll
+            for (int t = 0; t < NP; ++t) {
+                const int p = 8 * b + 2 * q + t;
+                red[(wave * 2 * 16 + cb * 16 + nl) * npairs + p] = sacc[cb][b][t];
+            }
+    __syncthreads();
+    for (int e = tid; e < kW1Waves * 2 * 16 * M; e += 64 * kW1Waves) {
+        const int m = e % M;
+        const int col = e / M;                             // wave * 32 + cb * 16 + nl
+        const int64_t n = int64_t(blockIdx.x) * kW1Rows + col;
+        if (n >= N) continue;
+        double s = 0.0;
+        for (int j = 0; j < S; ++j) s += red[col * npairs + m * S + j];
+        float out = float(double(xs[m]) * s);
+        if (bias) out = __fadd_rn(out, bias[n]);
+        y[int64_t(m) * N + n] = out;
+    }
+}
+
+template <int G, int MT, int NP>
+hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                     const float* xs, const float* bias, float* y, hipStream_t stream) {
+    const dim3 grid{unsigned((N + kW1Rows - 1) / kW1Rows)}, block{64 * kW1Waves};
+    size_t lds = size_t(w1_lds_bytes(M, G));
+    const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
+    lds = lds > red ? lds : red;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                       const float* xs, const float* bias, float* y, hipStream_t stream) {
+    const int R = w1_arows(M, G);
+    if (R <= 2) return launch_w1<G, 1, 1>(bits, sc, N, K, M, ws, xs, bias, y, stream);
+    if (R <= 16) return launch_w1<G, 1, 2>(bits, sc, N, K, M, ws, xs, bias, y, stream);
+    return launch_w1<G, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, stream);
+}
+
+// Tokens per pass: the A rows of a pass (2 x tokens x slots) fit two row blocks.
+int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
+
+}  // namespace
+
+namespace llk {
+
+size_t w1_workspace(int64_t M, int64_t K, int G) {
+    const int64_t tb = w1_tokens_per_pass(G);
+    return w1_ws_bytes(M < tb ? M : tb, K, G);
+}
+
+hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
+                          const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
+    const int64_t tb = w1_tokens_per_pass(G);
+    for (int64_t m0 = 0; m0 < M; m0 += tb) {               // every pass reads the weights once
+        const int64_t Mb = M - m0 < tb ? M - m0 : tb;
+        const int8_t* xb = xq + m0 * K;
+        const int R = w1_arows(int(Mb), G);
+        const int64_t pieces = (K / 128) * R * 8;
+        hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned((pieces + 255) / 256)}, dim3{256}, 0, stream, xb, Mb, K, G,
+                           ws);
+        const int64_t items = Mb * (K / G);
+        hipLaunchKernelGGL(w1_qsum_kernel, dim3{unsigned((items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb, K, G, ws);
+        hipError_t e = hipSuccess;
+        switch (G) {
+        case 32: e = launch_w1_g<32>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
+        case 64: e = launch_w1_g<64>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
+        case 128: e = launch_w1_g<128>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
+        default: e = launch_w1_g<256>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace llk

@@ -19,6 +19,12 @@ hipError_t launch_gemv_f32(int fmt, const void* codes, const void* scales, int64
                            const float* x, int64_t M, const float* bias, float* y, void* ws,
                            hipStream_t stream);
 
+// W1A8 product (binary weights, int8 activations), any M (passes of up to 16
+// tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.
+size_t w1_workspace(int64_t M, int64_t K, int G);
+hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
+                          const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
+
 // int8-activation prefill product, format i2_s.
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,

@@ -69,6 +69,14 @@ def lib():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("liblowbit.so is not built; run `python -m binary_bit_weight_amd.build`")
+        # torch ships its own HIP runtime under the same soname.  Loading it
+        # first lets the library bind to that copy; loaded the other way round
+        # the process would hold two HIP/HSA runtimes, and the second one finds
+        # no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = C.CDLL(_LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)

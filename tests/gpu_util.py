@@ -43,3 +43,26 @@ def make_tq2(seed, N, K):
     sc = synth.uniform_f16_bits(seed + 1, N * K // 256, 0.005, 0.05)
     blocks = L.ll_pack_tq2(w, sc)
     return w, sc, blocks
+
+
+_W1_CACHE = {}
+
+
+def make_w1(seed, N, K, G):
+    """Binary weights of the W1A8 recipe: dense N(0, 0.02) rows (generated in
+    4096-row chunks) -> ll_w1_from_dense (sign bits, fp16 group mean-abs
+    scales).  Returns (bits uint32 [N, K/32], scales uint16 [N, K/G]); cached
+    per process for the large shapes."""
+    key = (seed, N, K, G)
+    if key in _W1_CACHE:
+        return _W1_CACHE[key]
+    bits = np.empty((N, K // 32), np.uint32)
+    scales = np.empty((N, K // G), np.uint16)
+    for c in range((N + synth.CHUNK_ROWS - 1) // synth.CHUNK_ROWS):
+        r0 = c * synth.CHUNK_ROWS
+        rows = min(synth.CHUNK_ROWS, N - r0)
+        b, s = L.ll_w1_from_dense(synth.dense_chunk(seed, K, c, rows), G)
+        bits[r0:r0 + rows], scales[r0:r0 + rows] = b, s
+    if N * K >= 1 << 26:
+        _W1_CACHE[key] = (bits, scales)
+    return bits, scales

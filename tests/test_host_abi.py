@@ -190,3 +190,21 @@ def test_plan_bytes_hold_every_activation_layout():
     b_shared = lib.ll_gemv_plan_bytes(shared, 3, L.LL_ACT_F32, 1)
     assert 5 * (2560 + 8448) <= b_shared < 5 * (2 * 2560 + 8448)
     assert lib.ll_gemv_plan_bytes(fused, 2, L.LL_ACT_I8, 1) == 2 ** 64 - 1
+
+
+def test_w1_device_argument_errors_and_workspace():
+    lib = L.lib()
+    w = _w(fmt=L.LL_FMT_W1, N=64, K=5120, group=128)
+    # A rows: 40 chunks x (2 digits x 8 tokens) x 128 B, then int32 group sums [8][40]
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 8) == 40 * 16 * 128 + 8 * 40 * 4
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 40 * 2 * 128 + 40 * 4
+    # G = 32: four group slots per 128-k chunk, passes of 4 tokens
+    w32 = _w(fmt=L.LL_FMT_W1, N=64, K=512, group=32)
+    assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == 4 * 32 * 128 + 4 * 16 * 4
+    assert _gemv(w, act=L.LL_ACT_I8, M=8, ws=0) == -5
+    assert _gemv(w, act=L.LL_ACT_I8, M=8, wsb=16) == -5
+    assert _gemv(_w(fmt=L.LL_FMT_W1, K=160, group=32), act=L.LL_ACT_I8) == -2      # K % 128 on the device
+    assert _gemv(_w(fmt=L.LL_FMT_W1, K=384, group=96), act=L.LL_ACT_I8) == -2      # group 96
+    assert _gemv(_w(fmt=L.LL_FMT_W1, K=512, group=128, scales=0), act=L.LL_ACT_I8) == -1
+    assert lib.ll_bitlinear_gemm(C.byref(w), C.c_void_p(FAKE), C.c_void_p(FAKE), 32, None, C.c_void_p(FAKE),
+                                 C.c_void_p(FAKE), C.c_void_p(FAKE), 1 << 30, None) == -1   # acc_out with W1
