@@ -228,9 +228,10 @@ def extras_single(L, synth, torch, dev, stream):
         xb = torch.from_numpy(synth.normal_bf16_bits(402, 512, K).view(np.int16)).to(dev).view(torch.bfloat16)
         xq, xsc = L.quantize(xb, stream)
         y = torch.empty((512, N), dtype=torch.float32, device=dev)
+        gws = torch.zeros((max(L.ll_gemm_workspace_size(W, 512), 16),), dtype=torch.uint8, device=dev)
 
         def g():
-            L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, None, stream)
+            L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, gws, stream)
 
         def q():
             L.ll_quantize_act(xb, xq, xsc, stream)

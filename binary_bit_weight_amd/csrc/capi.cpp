@@ -105,7 +105,8 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
         if (!aligned(xs, 4)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: xs must be 4-byte aligned");
         if (w->fmt == LL_FMT_I2S)
             return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K,
-                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, s),
+                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
+                                                      s),
                               fn);
         if (w->fmt == LL_FMT_W1) {
             st = check_w1_device(w, fn);
@@ -127,6 +128,7 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     if (!w || M < 1) return size_t(-1);
     if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->K, w->group);
+    if (w->fmt == LL_FMT_I2S && w->K > 0 && w->N > 0) return llk::gemm_i8_workspace(M, w->N, w->K);
     return 0;
 }
 
@@ -154,8 +156,14 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                           fn);
     }
     if (w->fmt != LL_FMT_I2S) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s and W1 only");
+    const size_t need = llk::gemm_i8_workspace(M, w->N, w->K);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
+    if (need > 0 && !aligned(workspace, 16))
+        return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
     return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y,
-                                              acc_out, static_cast<hipStream_t>(stream)),
+                                              acc_out, need > 0 ? workspace : nullptr,
+                                              static_cast<hipStream_t>(stream)),
                       fn);
 }
 

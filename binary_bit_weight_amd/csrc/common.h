@@ -61,6 +61,19 @@ __device__ __forceinline__ void wave_sum_n(int (&v)[N]) {
     }
 }
 
+// Device-coherent 32-bit store / load (agent scope): written through, and
+// read from, the point of coherence of all XCDs, so a value passed between
+// workgroups needs no cache-wide writeback or invalidate.
+__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory operation of this wave has completed
+// (gfx9 s_waitcnt: vmcnt = 0, expcnt and lgkmcnt not waited on).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // fp16 bits -> fp32 (exact).
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return float(__builtin_bit_cast(_Float16, h));

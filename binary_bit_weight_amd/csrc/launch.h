@@ -25,10 +25,13 @@ size_t w1_workspace(int64_t M, int64_t K, int G);
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
 
-// int8-activation prefill product, format i2_s.
+// int8-activation prefill product, format i2_s.  ws: gemm_i8_workspace bytes
+// (split-K partial tiles and per-tile counters; zero-filled before its first
+// use, the counters are left zero by every call), or NULL to forbid splits.
+size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,
-                              int32_t* acc_out, hipStream_t stream);
+                              int32_t* acc_out, void* ws, hipStream_t stream);
 
 }  // namespace llk
 

@@ -307,7 +307,8 @@ def gemm(w: Weights, xq, xs, bias=None, want_acc=False, stream=None):
     y = torch.empty((M, w.N), dtype=torch.float32, device=xq.device)
     acc = torch.empty((M, w.N), dtype=torch.int32, device=xq.device) if want_acc else None
     nws = ll_gemm_workspace_size(w, M)
-    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=xq.device) if nws else None
+    # zero-filled: the split-K tile counters must start at zero (each call leaves them zero)
+    ws = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=xq.device) if nws else None
     ll_bitlinear_gemm(w, xq, xs, M, bias, y, acc, ws, stream)
     return y, acc
 

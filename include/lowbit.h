@@ -241,8 +241,14 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
    M > 16), int8 activations with int8 MFMA and exact int32 accumulation.
    Format i2_s: y = ((float)acc * xs[m]) * scale.  xq: device int8 [M,K];
    xs: device fp32 [M]; bias: device fp32 [N] or NULL; y: device fp32 [M,N];
-   acc_out: device int32 [M,N] receiving the raw integer dot (or NULL).
-   workspace as for ll_bitlinear_gemv with ll_gemm_workspace_size. */
+   acc_out: device int32 [M,N] receiving the raw integer dot (or NULL; i2_s
+   only).  Format W1 [BG "Method"]: as ll_bitlinear_gemv, in passes of up to
+   16 tokens that each read the weights once.
+   workspace: device buffer of at least ll_gemm_workspace_size(w, M) bytes,
+   16-byte aligned (NULL allowed when that is 0).  For i2_s it holds the
+   split-K partial tiles and per-tile counters: it must be zero-filled
+   before its first use, every call leaves the counters zero again, and two
+   calls sharing one workspace must not run concurrently. */
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M);
 ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,
                             const float* bias, float* y, int32_t* acc_out,

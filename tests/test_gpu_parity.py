@@ -171,8 +171,9 @@ def _i2s_i8_case(N, K, M, seed, rows=None, bias=False):
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
 
 
+# split K: (5, 2560, 300) 5 ways, (300, 2048, 200) 4, (64, 4096, 40) 8, (257, 1664, 130) 3 uneven ways
 @pytest.mark.parametrize("N,K,M", [(77, 384, 65), (128, 256, 128), (200, 512, 17), (33, 128, 1), (130, 640, 129),
-                                   (5, 2560, 300)])
+                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1664, 130)])
 def test_i2s_gemm_i8_small(N, K, M):
     announce("i2s gemm i8", N, K, M)
     _i2s_i8_case(N, K, M, 600 + N + M, bias=(M == 65))
@@ -182,6 +183,25 @@ def test_i2s_gemm_i8_small(N, K, M):
 def test_i2s_gemm_i8_prefill_full(N, K):
     announce("i2s gemm i8 full", N, K)
     _i2s_i8_case(N, K, 512, 401 if N == 6912 else 402, rows=synth.sample_rows(7, N, 48))
+
+
+def test_i2s_gemm_i8_workspace_reuse():
+    """Two calls sharing one (zero-filled once) workspace: the split-K tile
+    counters are left zero by the first call, so the second is exact too."""
+    t = torch()
+    N, K, M = 2560, 6912, 256
+    w, scale, packed = make_i2s(650, N, K)
+    W = L.upload_i2s(packed, N, K)
+    ws = t.zeros((max(L.ll_gemm_workspace_size(W, M), 16),), dtype=t.uint8, device="cuda")
+    assert L.ll_gemm_workspace_size(W, M) > 0
+    rows = synth.sample_rows(651, N, 40)
+    for rnd in range(2):
+        q, s = oracle.quantize_bf16(synth.normal_bf16_bits(652 + rnd, M, K))
+        y = t.empty((M, N), dtype=t.float32, device="cuda")
+        announce("gemm workspace reuse", rnd)
+        L.ll_bitlinear_gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, None, ws)
+        y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s, rows)
+        assert np.array_equal(y.cpu().numpy()[:, rows].view(np.uint32), y_ref.view(np.uint32)), rnd
 
 
 def test_i2s_gemv_i8_matches_gemm():
