@@ -196,6 +196,22 @@ def extras_single(L, synth, torch, dev, stream):
         out["tq2_gemv_f32_single_call_6912x2560_M%d" % M] = {
             "us": round(ms * 1e3, 2), "GB_s": round(blocks.size / (ms * 1e-3) / 1e9, 1),
             "GFLOP_s": round(2 * M * N * K / (ms * 1e-3) / 1e9, 1)}
+    # TQ2_0 6912 x 2560 as a prepared batch of distinct copies past twice the
+    # Infinity Cache (one launch each for preparation and product), M = 1, 8,
+    # 16: the bandwidth view
+    ncopy = max(1, int(np.ceil(2 ** 29 / blocks.size)))
+    for M in (1, 8, 16):
+        copies = [L.upload_tq2(blocks, N, K, dev) for _ in range(ncopy)]
+        x = torch.from_numpy(synth.normal_f32(304 + M, M, K)).to(dev)
+        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in copies]
+        plan = L.GemvPlan([(Wc, x, None, yc) for Wc, yc in zip(copies, ys)], M)
+        for _ in range(3):
+            plan.run(stream)
+        ms = time_events(torch, lambda: plan.run(stream), 20, stream)
+        nbytes = ncopy * blocks.size
+        out["tq2_plan_%dx6912x2560_M%d" % (ncopy, M)] = {"us": round(ms * 1e3, 2), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                                 "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del copies, plan
     # W1A8 decode, hidden 5120, G = 128: QKV, MLP gate, LM head at M = 1 and 8
     K, G = 5120, 128
     for name, N, seed in [("qkv", 7168, 501), ("gate", 17408, 502), ("lm_head", 248320, 503)]:

@@ -68,7 +68,7 @@ ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
 size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M) {
     if (!w || M < 1 || M > 16 || w->K <= 0) return size_t(-1);
     if (act == LL_ACT_F32)
-        return M <= llk::kPlanesMaxM ? llk::planes_workspace(M, w->K) : llk::gemv_f32_workspace(M, w->K);
+        return llk::planes_workspace(M, w->K);
     if (act == LL_ACT_I8) return w->fmt == LL_FMT_W1 && w->group > 0 ? llk::w1_workspace(M, w->K, w->group) : 0;
     return size_t(-1);
 }
@@ -86,18 +86,13 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
     if (act == LL_ACT_F32) {
         if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0)
             return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: fp32 activations need format i2_s or TQ2_0");
-        const bool planes = M <= llk::kPlanesMaxM;
-        const size_t need = planes ? llk::planes_workspace(M, w->K) : llk::gemv_f32_workspace(M, w->K);
+        const size_t need = llk::planes_workspace(M, w->K);
         if (need > 0 && (!workspace || workspace_bytes < need))
             return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
         if (need > 0 && !aligned(workspace, 16))
             return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
-        if (planes)
-            return hip_status(llk::launch_gemv_planes(w->fmt, w->codes, w->scales, w->N, w->K,
-                                                      static_cast<const float*>(x), M, bias, y, workspace, s),
-                              fn);
-        return hip_status(llk::launch_gemv_f32(w->fmt, w->codes, w->scales, w->N, w->K, static_cast<const float*>(x), M,
-                                               bias, y, workspace, s),
+        return hip_status(llk::launch_gemv_planes(w->fmt, w->codes, w->scales, w->N, w->K, static_cast<const float*>(x),
+                                                  M, bias, y, workspace, s),
                           fn);
     }
     if (act == LL_ACT_I8) {

@@ -2,8 +2,7 @@
 // host validates every item once and lays out device tables inside the
 // plan memory; every later run costs two launches: one preparing the
 // operands of every distinct activation (into the plan memory), one walking
-// the table of products.  M <= 3 uses the int8-plane kernels, larger M the
-// bf16-plane kernels.
+// the table of products (int8-plane kernels, up to three tokens per pass).
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -19,14 +18,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-    bool planes = false;
     size_t prob_off = 0, prep_off = 0, map_off = 0, frag_off = 0, total = 0;
     std::vector<int> prep_of;          // item -> distinct activation index
     std::vector<const void*> xs;       // distinct activations
     std::vector<int64_t> xk;           // their K
     std::vector<size_t> frag_at;       // byte offset of each activation's operands
-    std::vector<int64_t> ent0;         // bf16 path: first fragment entry of each activation
-    int64_t entries = 0, tiles = 0, kmax = 0;
+    int64_t tiles = 0, kmax = 0;       // workgroups of the product launch
 };
 
 ll_status check_item(const ll_gemv_item& it, int i, int32_t act, int64_t M, int32_t fmt0) {
@@ -60,7 +57,6 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
         ll_status st = check_item(items[i], i, act, M, items[0].w.fmt);
         if (st) return st;
     }
-    L.planes = M <= llk::kPlanesMaxM;
     L.prep_of.assign(size_t(count), -1);
     for (int i = 0; i < count; ++i) L.kmax = std::max(L.kmax, items[i].w.K);
     for (int i = 0; i < count; ++i) {
@@ -73,36 +69,29 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
             L.xk.push_back(items[i].w.K);
         }
         L.prep_of[size_t(i)] = found;
-        if (L.planes) {
-            const int64_t rows = llk::planes_batch_rows();
-            L.tiles += (items[i].w.N + rows - 1) / rows;          // workgroups
-        } else {
-            L.tiles += (items[i].w.N + 15) / 16;                  // 16-row tiles
-        }
+        const int64_t rows = llk::planes_batch_rows();
+        L.tiles += (items[i].w.N + rows - 1) / rows;              // workgroups
     }
-    const size_t prob_sz = L.planes ? llk::planes_prob_bytes() : llk::batch_prob_bytes();
-    const size_t prep_sz = L.planes ? llk::planes_prep_bytes() : llk::batch_prep_bytes();
+    const size_t prob_sz = llk::planes_prob_bytes();
+    const size_t prep_sz = llk::planes_prep_bytes();
     L.prob_off = 0;
     L.prep_off = round_up(size_t(count) * prob_sz, 256);
     L.map_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
-    L.frag_off = round_up(L.map_off + (L.planes ? size_t(L.tiles) * 4 : 0), 256);
+    L.frag_off = round_up(L.map_off + size_t(L.tiles) * 4, 256);
     size_t at = L.frag_off;
     for (size_t j = 0; j < L.xs.size(); ++j) {
         L.frag_at.push_back(at);
-        L.ent0.push_back(L.entries);
-        const size_t bytes = L.planes ? llk::planes_operand_bytes(M, L.xk[j]) : llk::gemv_f32_workspace(M, L.xk[j]);
-        if (!L.planes) L.entries += int64_t(bytes / 16);
+        const size_t bytes = llk::planes_operand_bytes(M, L.xk[j]);
         at = round_up(at + bytes, 256);
     }
     L.total = at;
-    if (L.tiles > (int64_t(1) << 31) - 1 || L.entries > (int64_t(1) << 40) || L.xs.size() > 65535)
+    if (L.tiles > (int64_t(1) << 31) - 1 || L.xs.size() > 65535)
         return ll::fail(LL_ERANGE, "ll_gemv_plan: batch too large");
     return LL_OK;
 }
 
 ll_status check_plan(const ll_gemv_plan* p) {
-    if (!p || !p->mem || !p->prob_table || !p->prep_table || p->count <= 0 || p->nprep <= 0 ||
-        (p->M <= llk::kPlanesMaxM && !p->map_table))
+    if (!p || !p->mem || !p->prob_table || !p->prep_table || !p->map_table || p->count <= 0 || p->nprep <= 0)
         return ll::fail(LL_EINVAL, "ll_gemv_plan: plan not initialised");
     return LL_OK;
 }
@@ -137,28 +126,17 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     for (int i = 0; i < count; ++i) {
         const ll_gemv_item& it = items[i];
         char* ops = base + L.frag_at[size_t(L.prep_of[size_t(i)])];
-        if (L.planes) {
-            llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
-                                  it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
-            const int64_t wgs = (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
-            for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
-            first += wgs;
-        } else {
-            llk::fill_batch_prob(host.data() + L.prob_off + size_t(i) * llk::batch_prob_bytes(), it.w.codes,
-                                 it.w.scales, it.bias, it.y, ops, it.w.N, it.w.K, first);
-            first += (it.w.N + 15) / 16;
-        }
+        llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
+                              it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
+        const int64_t wgs = (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
+        for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
+        first += wgs;
     }
     for (size_t j = 0; j < L.xs.size(); ++j) {
         const float* x = static_cast<const float*>(L.xs[j]);
-        if (L.planes)
-            llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
-                                  L.xk[j]);
-        else
-            llk::fill_batch_prep(host.data() + L.prep_off + j * llk::batch_prep_bytes(), x, base + L.frag_at[j],
-                                 L.xk[j], L.ent0[j]);
+        llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
+                              L.xk[j]);
     }
-    if (L.planes) L.entries = int64_t(L.xs.size()) * M;   // preparation workgroups of the plane path
     st = hip_status(hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice), "ll_gemv_plan_init");
     if (st) return st;
     ll_gemv_plan p;
@@ -171,11 +149,11 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     p.fmt = items[0].w.fmt;
     p.M = M;
     p.tiles = L.tiles;
-    p.prep_entries = L.entries;
+    p.prep_entries = int64_t(L.xs.size()) * M;          // preparation workgroups (one per token)
     p.kmax = L.kmax;
     p.prob_table = base + L.prob_off;
     p.prep_table = base + L.prep_off;
-    p.map_table = L.planes ? base + L.map_off : nullptr;
+    p.map_table = base + L.map_off;
     *plan = p;
     return LL_OK;
 }
@@ -184,11 +162,7 @@ ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (plan->M <= llk::kPlanesMaxM)
-        return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M, s),
-                          "ll_gemv_plan_prepare");
-    return hip_status(llk::launch_gemv_f32_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M,
-                                                      plan->prep_entries, s),
+    return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M, s),
                       "ll_gemv_plan_prepare");
 }
 
@@ -196,12 +170,8 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (plan->M <= llk::kPlanesMaxM)
-        return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
-                                                           plan->tiles, s),
-                          "ll_gemv_plan_product");
-    return hip_status(llk::launch_gemv_f32_batch_product(plan->prob_table, plan->count, plan->fmt, plan->M,
-                                                         plan->tiles, s),
+    return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
+                                                       plan->tiles, s),
                       "ll_gemv_plan_product");
 }
 

@@ -88,10 +88,16 @@ __host__ __device__ inline int fused_lds_bytes(int64_t K) {
 // 64f + 16q + 4v + b, so one MFMA (one field) reads 16 consecutive bytes.
 __device__ __forceinline__ int tq2_pos(int e) { return 64 * (e & 3) + 16 * (e >> 6) + 4 * ((e >> 4) & 3) + ((e >> 2) & 3); }
 
+// The product multiplies up to kPassM tokens at a time (5 x 3 = 15 plane
+// rows fill one 16-row MFMA operand); larger M runs several passes.
+constexpr int kPassM = 3;
+__host__ __device__ inline int64_t npass(int64_t M) { return (M + kPassM - 1) / kPassM; }
+
 // Workspace layout of one activation:
-//     planes [5M][K] | xsum [nblk4][16] | E [M] | xtot [5M] (per row),
-// xsum[b][5m + p] the sum of plane row 5m + p over 256-k block b, blocks
-// padded to a multiple of 4 (one 1024-k window = one 256-byte piece).
+//     planes [5M][K] | xsum [npass][nblk4][16] | E [M] | xtot [5M] (per row),
+// xsum[pass][b][5j + p] the sum of plane row 5m + p (m = 3 pass + j) over
+// 256-k block b, blocks padded to a multiple of 4 (one 1024-k window = one
+// 256-byte piece per pass).
 struct PlaneView {
     int8_t* planes;
     int32_t* xsum;
@@ -100,16 +106,25 @@ struct PlaneView {
 };
 __host__ __device__ inline int64_t nblk4(int64_t K) { return (K + 1023) / 1024 * 4; }
 __host__ __device__ inline size_t planes_bytes(int64_t M, int64_t K) {
-    return size_t((kP * M * K + 15) / 16 * 16 + nblk4(K) * 64 + M * 4 + kP * M * 4 + 15) / 16 * 16;
+    return size_t((kP * M * K + 15) / 16 * 16 + npass(M) * nblk4(K) * 64 + M * 4 + kP * M * 4 + 15) / 16 * 16;
 }
-__host__ __device__ inline PlaneView plane_view(void* base, int64_t M, int64_t K) {
-    char* p = static_cast<char*>(base);
+__host__ __device__ inline PlaneView plane_view(const void* base, int64_t M, int64_t K) {
+    char* p = static_cast<char*>(const_cast<void*>(base));
     PlaneView v;
     v.planes = reinterpret_cast<int8_t*>(p);
     v.xsum = reinterpret_cast<int32_t*>(p + (kP * M * K + 15) / 16 * 16);
-    v.ex = v.xsum + nblk4(K) * 16;
+    v.ex = v.xsum + npass(M) * nblk4(K) * 16;
     v.xtot = v.ex + M;
     return v;
+}
+// The view of pass `pass` (tokens 3 pass .. 3 pass + 2) of a full view.
+__host__ __device__ inline PlaneView pass_view(const PlaneView& v, int pass, int64_t K) {
+    PlaneView u;
+    u.planes = v.planes + int64_t(kP * kPassM) * pass * K;
+    u.xsum = v.xsum + int64_t(pass) * nblk4(K) * 16;
+    u.ex = v.ex + kPassM * pass;
+    u.xtot = v.xtot + kP * kPassM * pass;
+    return u;
 }
 
 // ---------------------------------------------------------------- activation preparation
@@ -211,7 +226,8 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
             const int64_t b = (k0 + 1024 * i) / 256 + wave;
 #pragma unroll
             for (int p = 0; p < kP; ++p) {
-                if (lane == 0 && b < nblk) v.xsum[b * 16 + m * kP + p] = s[i * kP + p];
+                if (lane == 0 && b < nblk)
+                    v.xsum[(m / kPassM) * nblk4(K) * 16 + b * 16 + (m % kPassM) * kP + p] = s[i * kP + p];
                 tot[p] += s[i * kP + p];
             }
         }
@@ -350,9 +366,11 @@ __host__ __device__ constexpr int field_mul(int t) {
 // the barriers cost.)
 enum { kWindowed = 0, kFused = 1 };
 
+// ws: the fp32 token row (kFused); pvw: the prepared operands of these M <= 3
+// tokens (kWindowed).
 template <int FMT, int M, int MODE>
 __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                            int64_t N, int64_t K, const void* __restrict__ ws,
+                                            int64_t N, int64_t K, const void* __restrict__ ws, const PlaneView& pvw,
                                             const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
                                             char* __restrict__ lds) {
     constexpr bool FUSED = MODE == kFused;
@@ -366,7 +384,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     const uint32_t rowbytes = uint32_t(K / 4);
     const int nwin = int((K + kWinK - 1) / kWinK);
     const int nblk = int((K + 255) / 256);
-    const PlaneView pv = plane_view(const_cast<void*>(ws), M, K);
+    const PlaneView pv = pvw;
     char* wtile = lds + wave * kWTile;                  // private to this wave
     int8_t* abuf = reinterpret_cast<int8_t*>(lds + kWaves * kWTile);
     constexpr int abytes = RR * kAStride + 256;          // planes, then the window's block sums
@@ -406,7 +424,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     // anyway on a few hot bytes (LL_PLANES_DUMMY=1) gives the compiler exact
     // wait counts, i.e. a full two-window prefetch, but measured slower on
     // the decode step (more requests in flight, no gain in bandwidth).
-    const uint8_t* dummy = static_cast<const uint8_t*>(ws) + 16 * nl;
+    const uint8_t* dummy = (FUSED ? static_cast<const uint8_t*>(ws) : reinterpret_cast<const uint8_t*>(pv.planes)) + 16 * nl;
     auto load = [&](int w, Regs& r) {
         const bool live = w < nwin;
 #pragma unroll
@@ -606,7 +624,35 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_kernel(const uint8_t*
                                                                    const float* __restrict__ bias,
                                                                    float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT, M, kWindowed>(codes, scales, N, K, ws, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    const PlaneView pv = plane_view(ws, M, K);
+    planes_rows<FMT, M, kWindowed>(codes, scales, N, K, ws, pv, bias, y, int64_t(blockIdx.x) * kRows, lds);
+}
+
+// Mt > 3 tokens: passes of up to three tokens run as the second grid
+// dimension, side by side (each streams the weights; the passes of one row
+// tile read the same bytes at about the same time).
+template <int FMT>
+__device__ __forceinline__ void planes_pass(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                                            int64_t N, int64_t K, const void* __restrict__ ws, int Mt, int pass,
+                                            const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
+                                            char* __restrict__ lds) {
+    const PlaneView pv = pass_view(plane_view(ws, Mt, K), pass, K);
+    float* yp = y + int64_t(kPassM * pass) * N;
+    switch (Mt - kPassM * pass) {
+    case 1: planes_rows<FMT, 1, kWindowed>(codes, scales, N, K, ws, pv, bias, yp, n0, lds); break;
+    case 2: planes_rows<FMT, 2, kWindowed>(codes, scales, N, K, ws, pv, bias, yp, n0, lds); break;
+    default: planes_rows<FMT, 3, kWindowed>(codes, scales, N, K, ws, pv, bias, yp, n0, lds); break;
+    }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kWaves) gemv_planes_multi_kernel(const uint8_t* __restrict__ codes,
+                                                                         const uint16_t* __restrict__ scales, int64_t N,
+                                                                         int64_t K, const void* __restrict__ ws, int Mt,
+                                                                         const float* __restrict__ bias,
+                                                                         float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    planes_pass<FMT>(codes, scales, N, K, ws, Mt, int(blockIdx.y), bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 template <int FMT>
@@ -616,7 +662,7 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_fused_kernel(const ui
                                                                          const float* __restrict__ bias,
                                                                          float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_rows<FMT, 1, kFused>(codes, scales, N, K, x, bias, y, int64_t(blockIdx.x) * kRows, lds);
+    planes_rows<FMT, 1, kFused>(codes, scales, N, K, x, PlaneView{}, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
 struct PlanesProb {          // product of a prepared batch
@@ -643,7 +689,18 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const Pl
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t wg = blockIdx.x;
     const PlanesProb& P = tab[ld32(map + wg)];
-    planes_rows<FMT, M, MODE>(P.codes, P.scales, P.N, P.K, P.ws, P.bias, P.y, (wg - P.wg0) * kRows, lds);
+    const PlaneView pv = plane_view(P.ws, M, P.K);
+    planes_rows<FMT, M, MODE>(P.codes, P.scales, P.N, P.K, P.ws, pv, P.bias, P.y, (wg - P.wg0) * kRows, lds);
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_multi_kernel(const PlanesProb* __restrict__ tab,
+                                                                               const int32_t* __restrict__ map,
+                                                                               int Mt) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int64_t wg = blockIdx.x;
+    const PlanesProb& P = tab[ld32(map + wg)];
+    planes_pass<FMT>(P.codes, P.scales, P.N, P.K, P.ws, Mt, int(blockIdx.y), P.bias, P.y, (wg - P.wg0) * kRows, lds);
 }
 
 template <int FMT>
@@ -680,6 +737,27 @@ hipError_t launch_fused_single(const uint8_t* c, const uint16_t* s, int64_t N, i
     hipError_t e = allow_lds(gemv_planes_fused_kernel<FMT>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_planes_fused_kernel<FMT>), grid, block, lds, stream, c, s, N, K, x, bias, y);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_multi(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, void* ws, int Mt,
+                        const float* bias, float* y, hipStream_t stream) {
+    const dim3 grid{unsigned((N + kRows - 1) / kRows), unsigned(npass(Mt))}, block{64 * kWaves};
+    const size_t lds = size_t(lds_bytes(kPassM));
+    hipError_t e = allow_lds(gemv_planes_multi_kernel<FMT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_multi_kernel<FMT>), grid, block, lds, stream, c, s, N, K, ws, Mt, bias, y);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_batch_multi(const PlanesProb* tab, const int32_t* map, int64_t wgs, int Mt, hipStream_t stream) {
+    const dim3 grid{unsigned(wgs), unsigned(npass(Mt))}, block{64 * kWaves};
+    const size_t lds = size_t(lds_bytes(kPassM));
+    hipError_t e = allow_lds(gemv_planes_batch_multi_kernel<FMT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_batch_multi_kernel<FMT>), grid, block, lds, stream, tab, map, Mt);
     return hipGetLastError();
 }
 
@@ -736,6 +814,9 @@ hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, in
                         : launch_fused_single<2>(c, s, N, K, x, bias, y, stream);
     if (fmt == 1) hipLaunchKernelGGL(prep_planes_kernel<1>, pgrid, pblock, 0, stream, x, K, int(M), ws);
     else hipLaunchKernelGGL(prep_planes_kernel<2>, pgrid, pblock, 0, stream, x, K, int(M), ws);
+    if (M > kPassM)
+        return fmt == 1 ? launch_multi<1>(c, s, N, K, ws, int(M), bias, y, stream)
+                        : launch_multi<2>(c, s, N, K, ws, int(M), bias, y, stream);
     switch (fmt * 4 + int(M)) {
     case 5: return launch_single<1, 1>(c, s, N, K, ws, bias, y, stream);
     case 6: return launch_single<1, 2>(c, s, N, K, ws, bias, y, stream);
@@ -758,6 +839,9 @@ hipError_t launch_planes_batch_product(const void* prob_table, const void* map, 
                                        hipStream_t stream) {
     const PlanesProb* tab = static_cast<const PlanesProb*>(prob_table);
     const int32_t* mp = static_cast<const int32_t*>(map);
+    if (M > kPassM)
+        return fmt == 1 ? launch_batch_multi<1>(tab, mp, wgs, int(M), stream)
+                        : launch_batch_multi<2>(tab, mp, wgs, int(M), stream);
     switch (fmt * 4 + int(M)) {
     case 5: return launch_batch<1, 1>(tab, mp, wgs, stream);
     case 6: return launch_batch<1, 2>(tab, mp, wgs, stream);

@@ -11,14 +11,6 @@ namespace llk {
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs,
                            hipStream_t stream);
 
-// fp32-activation decode product, formats i2_s (fmt 1) and TQ2_0 (fmt 2),
-// 1 <= M <= 16.  Two kernels: the activation split into bf16 planes laid out
-// as MFMA operands (into `ws`), then the packed-weight product.
-size_t gemv_f32_workspace(int64_t M, int64_t K);
-hipError_t launch_gemv_f32(int fmt, const void* codes, const void* scales, int64_t N, int64_t K,
-                           const float* x, int64_t M, const float* bias, float* y, void* ws,
-                           hipStream_t stream);
-
 // W1A8 product (binary weights, int8 activations), any M (passes of up to 16
 // tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.
 size_t w1_workspace(int64_t M, int64_t K, int G);
@@ -36,23 +28,14 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
 }  // namespace llk
 
 namespace llk {
-// Prepared batch of fp32-activation decode products (device tables built by
-// the C-ABI layer; see ll_gemv_plan_init).
-size_t batch_prob_bytes();
-size_t batch_prep_bytes();
-void fill_batch_prob(void* dst, const void* codes, const void* scales, const float* bias, float* y, const void* afrag,
-                     int64_t N, int64_t K, int64_t tile0);
-void fill_batch_prep(void* dst, const float* x, void* afrag, int64_t K, int64_t ent0);
-hipError_t launch_gemv_f32_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, int64_t entries,
-                                      hipStream_t stream);
-hipError_t launch_gemv_f32_batch_product(const void* prob_table, int count, int fmt, int64_t M, int64_t tiles,
-                                         hipStream_t stream);
-
-// 1 <= M <= 3: activations split into int8 planes (one preparation launch),
-// int8 matrix cores with exact int32 accumulation (gemv_planes.hip).
+// fp32-activation decode product, formats i2_s (fmt 1) and TQ2_0 (fmt 2),
+// 1 <= M <= 16: activations split into int8 planes (one preparation launch),
+// int8 matrix cores with exact int32 accumulation, up to three tokens per
+// pass (gemv_planes.hip).  Prepared batches: device tables built by the C-ABI
+// layer (ll_gemv_plan_init).
 // A single call with M == 1 and K <= 8192 runs fused: each product workgroup
 // builds the planes itself from x, so no workspace and no preparation launch.
-constexpr int64_t kPlanesMaxM = 3;
+constexpr int64_t kPlanesMaxM = 16;
 bool planes_fused(int64_t M, int64_t K);
 size_t planes_workspace(int64_t M, int64_t K);       // single call: 0 when fused
 size_t planes_operand_bytes(int64_t M, int64_t K);   // prepared operands of one activation

@@ -175,8 +175,8 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    in the kernel.  act == LL_ACT_F32: x fp32 [M,K], xs unused (NULL); formats
    i2_s and TQ2_0; y = scale * sum_k w*x (i2_s) or sum over blocks of
    s_block * sum w*x (TQ2_0), within 1e-5 * scale * sum|x| (+1e-6) of the
-   exact value (M <= 3: x split into five int8 planes, exact integer sums,
-   fp64 epilogue; M > 3: bf16 planes, fp32 accumulation).
+   exact value (x split into five int8 planes per token, exact integer sums,
+   fp64 epilogue; up to three tokens per pass over the weights).
    act == LL_ACT_I8: x int8 [M,K], xs fp32 [M] from ll_quantize_act; formats
    i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32) and W1
    (y = (float)((double)xs[m] * sum_g s_g * d_g), d_g the exact per-group
@@ -215,7 +215,7 @@ typedef struct {
     int64_t M, tiles, prep_entries, kmax;
     void* prob_table;    /* inside mem */
     void* prep_table;    /* inside mem */
-    void* map_table;     /* inside mem: product index of every workgroup (M <= 3), else NULL */
+    void* map_table;     /* inside mem: product index of every workgroup */
 } ll_gemv_plan;
 
 /* Device bytes ll_gemv_plan_init needs for these items ((size_t)-1 for
