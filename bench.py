@@ -125,6 +125,23 @@ def w1_weights(L, synth, seed, N, K, G):
     return bits, scales
 
 
+def time_graph(torch, call, copies, calls, stream):
+    """GPU time of one call: `calls` calls (call(i, stream) with i cycling
+    over `copies` weight copies) captured in one HIP graph and replayed, so
+    the host's per-call cost stays out of the figure."""
+    for i in range(copies):
+        call(i, None)                               # warm-up; sets per-kernel launch attributes
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            call(i % copies, None)
+    g.replay()
+    ms = time_events(torch, g.replay, 3, stream)
+    del g
+    return ms / calls
+
+
 def time_events(torch, fn, reps, stream):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
@@ -165,14 +182,8 @@ def extras_single(L, synth, torch, dev, stream):
         x = torch.from_numpy(synth.normal_f32(6, 1, K)).to(dev)
         y = torch.empty((1, N), dtype=torch.float32, device=dev)
         ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, 1),), dtype=torch.uint8, device=dev)
-        it = iter(range(10 ** 9))
-
-        def one():
-            W = Ws[next(it) % reps]
-            L.ll_bitlinear_gemv(W, L.LL_ACT_F32, x, None, 1, None, y, ws, stream)
-        for _ in range(reps):
-            one()
-        ms = time_events(torch, one, 2 * reps, stream)
+        ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_F32, x, None, 1, None, y, ws, st),
+                        reps, 2 * reps, stream)
         out["i2s_gemv_f32_single_call_" + name] = {"us": round(ms * 1e3, 2),
                                                    "GB_s": round(p.size / (ms * 1e-3) / 1e9, 1)}
     # TQ2_0 small batch, N=6912, K=2560
@@ -185,14 +196,9 @@ def extras_single(L, synth, torch, dev, stream):
     for M in (1, 8, 16):
         x = torch.from_numpy(synth.normal_f32(303, M, K)).to(dev)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, M),), dtype=torch.uint8, device=dev)
-        it = iter(range(10 ** 9))
-
-        def one():
-            L.ll_bitlinear_gemv(Ws[next(it) % reps], L.LL_ACT_F32, x, None, M, None, y, ws, stream)
-        for _ in range(reps):
-            one()
-        ms = time_events(torch, one, 2 * reps, stream)
+        ws = torch.empty((max(L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, M), 16),), dtype=torch.uint8, device=dev)
+        ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_F32, x, None, M, None, y, ws, st),
+                        reps, 2 * reps, stream)
         out["tq2_gemv_f32_single_call_6912x2560_M%d" % M] = {
             "us": round(ms * 1e3, 2), "GB_s": round(blocks.size / (ms * 1e-3) / 1e9, 1),
             "GFLOP_s": round(2 * M * N * K / (ms * 1e-3) / 1e9, 1)}
@@ -224,13 +230,8 @@ def extras_single(L, synth, torch, dev, stream):
             xq, xsc = L.quantize(x, stream)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
-            it = iter(range(10 ** 9))
-
-            def one():
-                L.ll_bitlinear_gemv(Ws[next(it) % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream)
-            for _ in range(reps):
-                one()
-            ms = time_events(torch, one, max(2 * reps, 10), stream)
+            ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_I8, xq, xsc, M, None, y, ws, st),
+                            reps, max(2 * reps, 16), stream)
             out["w1a8_gemv_%s_%dx%d_M%d" % (name, N, K, M)] = {
                 "us": round(ms * 1e3, 2), "GB_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}
@@ -246,15 +247,8 @@ def extras_single(L, synth, torch, dev, stream):
         y = torch.empty((512, N), dtype=torch.float32, device=dev)
         gws = torch.zeros((max(L.ll_gemm_workspace_size(W, 512), 16),), dtype=torch.uint8, device=dev)
 
-        def g():
-            L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, gws, stream)
-
-        def q():
-            L.ll_quantize_act(xb, xq, xsc, stream)
-        for _ in range(3):
-            g()
-        ms = time_events(torch, g, 20, stream)
-        msq = time_events(torch, q, 20, stream)
+        ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, gws, st), 1, 20, stream)
+        msq = time_graph(torch, lambda i, st: L.ll_quantize_act(xb, xq, xsc, st), 1, 20, stream)
         tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
         out["i2s_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
                                                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),

@@ -2,6 +2,10 @@
 // kernel launchers.  Nothing here allocates, frees or synchronizes.
 #include <hip/hip_runtime_api.h>
 
+#include <mutex>
+#include <tuple>
+#include <vector>
+
 #include "internal.h"
 #include "launch.h"
 
@@ -51,6 +55,25 @@ ll_status check_weights(const ll_weights* w, const char* fn) {
 }
 
 }  // namespace
+
+namespace llk {
+
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::vector<std::tuple<const void*, int, size_t>> done;   // (kernel, device, bytes allowed)
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& d : done)
+        if (std::get<0>(d) == kernel && std::get<1>(d) == dev && std::get<2>(d) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e == hipSuccess) done.emplace_back(kernel, dev, bytes);
+    return e;
+}
+
+}  // namespace llk
 
 extern "C" {
 

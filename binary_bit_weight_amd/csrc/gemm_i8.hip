@@ -281,8 +281,7 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     int32_t* part = static_cast<int32_t*>(ws);
     int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
     const dim3 grid{unsigned(tiles * S)}, block{256};
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_i8_i2s_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kGemmLds));
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_i2s_kernel), kGemmLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_i8_i2s_kernel, grid, block, kGemmLds, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
                        part, counters);

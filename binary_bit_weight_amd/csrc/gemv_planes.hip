@@ -713,9 +713,7 @@ __global__ void __launch_bounds__(256) prep_planes_batch_kernel(const PlanesPrep
 
 template <typename F>
 hipError_t allow_lds(F* kernel, size_t bytes) {
-    if (bytes <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               int(bytes));
+    return allow_dynamic_lds(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 template <int FMT, int M>

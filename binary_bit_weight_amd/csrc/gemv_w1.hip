@@ -391,11 +391,8 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     size_t lds = size_t(w1_lds_bytes(M, G));
     const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
     lds = lds > red ? lds : red;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP>), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y);
     return hipGetLastError();
 }

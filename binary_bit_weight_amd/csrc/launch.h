@@ -8,6 +8,11 @@
 
 namespace llk {
 
+// Raises a kernel's dynamic LDS limit to at least `bytes` on the current
+// device.  hipFuncSetAttribute is a host-side call that costs microseconds,
+// so each (kernel, device) pair is set once and remembered.
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
+
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs,
                            hipStream_t stream);
 
