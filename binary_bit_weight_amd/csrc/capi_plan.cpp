@@ -2,7 +2,9 @@
 // host validates every item once and lays out device tables inside the
 // plan memory; every later run costs two launches: one preparing the
 // operands of every distinct activation (into the plan memory), one walking
-// the table of products (int8-plane kernels, up to three tokens per pass).
+// the table of products.  One token (M == 1): fp4 digit planes on the fp4
+// matrix cores (gemv_fp4.hip); 2 <= M <= 16: int8 planes on the int8 matrix
+// cores, up to three tokens per pass (gemv_planes.hip).
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -24,6 +26,7 @@ struct Layout {
     std::vector<int64_t> xk;           // their K
     std::vector<size_t> frag_at;       // byte offset of each activation's operands
     int64_t tiles = 0, kmax = 0;       // workgroups of the product launch
+    bool f4 = false;                   // fp4 engine (one token)
 };
 
 ll_status check_item(const ll_gemv_item& it, int i, int32_t act, int64_t M, int32_t fmt0) {
@@ -59,6 +62,8 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     }
     L.prep_of.assign(size_t(count), -1);
     for (int i = 0; i < count; ++i) L.kmax = std::max(L.kmax, items[i].w.K);
+    L.f4 = llk::f4_engine(M, L.kmax);
+    const int64_t rows = L.f4 ? llk::f4_batch_rows() : llk::planes_batch_rows();
     for (int i = 0; i < count; ++i) {
         int found = -1;
         for (size_t j = 0; j < L.xs.size(); ++j)
@@ -69,11 +74,10 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
             L.xk.push_back(items[i].w.K);
         }
         L.prep_of[size_t(i)] = found;
-        const int64_t rows = llk::planes_batch_rows();
-        L.tiles += (items[i].w.N + rows - 1) / rows;              // workgroups
+        L.tiles += (items[i].w.N + rows - 1) / rows;              // (logical) workgroups
     }
-    const size_t prob_sz = llk::planes_prob_bytes();
-    const size_t prep_sz = llk::planes_prep_bytes();
+    const size_t prob_sz = L.f4 ? llk::f4_prob_bytes() : llk::planes_prob_bytes();
+    const size_t prep_sz = L.f4 ? llk::f4_prep_bytes() : llk::planes_prep_bytes();
     L.prob_off = 0;
     L.prep_off = round_up(size_t(count) * prob_sz, 256);
     L.map_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
@@ -81,7 +85,7 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     size_t at = L.frag_off;
     for (size_t j = 0; j < L.xs.size(); ++j) {
         L.frag_at.push_back(at);
-        const size_t bytes = llk::planes_operand_bytes(M, L.xk[j]);
+        const size_t bytes = L.f4 ? llk::f4_operand_bytes(L.xk[j]) : llk::planes_operand_bytes(M, L.xk[j]);
         at = round_up(at + bytes, 256);
     }
     L.total = at;
@@ -123,19 +127,27 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     std::vector<char> host(L.frag_off, 0);
     int32_t* map = reinterpret_cast<int32_t*>(host.data() + L.map_off);
     int64_t first = 0;
+    const int64_t rows = L.f4 ? llk::f4_batch_rows() : llk::planes_batch_rows();
     for (int i = 0; i < count; ++i) {
         const ll_gemv_item& it = items[i];
         char* ops = base + L.frag_at[size_t(L.prep_of[size_t(i)])];
-        llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
-                              it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
-        const int64_t wgs = (it.w.N + llk::planes_batch_rows() - 1) / llk::planes_batch_rows();
+        if (L.f4)
+            llk::fill_f4_prob(host.data() + L.prob_off + size_t(i) * llk::f4_prob_bytes(), it.w.codes, it.w.scales,
+                              ops, it.bias, it.y, it.w.N, it.w.K, first);
+        else
+            llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
+                                  it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
+        const int64_t wgs = (it.w.N + rows - 1) / rows;
         for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
         first += wgs;
     }
     for (size_t j = 0; j < L.xs.size(); ++j) {
         const float* x = static_cast<const float*>(L.xs[j]);
-        llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
-                              L.xk[j]);
+        if (L.f4)
+            llk::fill_f4_prep(host.data() + L.prep_off + j * llk::f4_prep_bytes(), x, base + L.frag_at[j], L.xk[j]);
+        else
+            llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
+                                  L.xk[j]);
     }
     st = hip_status(hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice), "ll_gemv_plan_init");
     if (st) return st;
@@ -162,6 +174,9 @@ ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (llk::f4_engine(plan->M, plan->kmax))
+        return hip_status(llk::launch_f4_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->kmax, s),
+                          "ll_gemv_plan_prepare");
     return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M, s),
                       "ll_gemv_plan_prepare");
 }
@@ -170,6 +185,10 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (llk::f4_engine(plan->M, plan->kmax))
+        return hip_status(llk::launch_f4_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->tiles,
+                                                       plan->kmax, s),
+                          "ll_gemv_plan_product");
     return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
                                                        plan->tiles, s),
                       "ll_gemv_plan_product");

@@ -1,0 +1,485 @@
+// Single-token decode product with fp32 activations (M = 1), i2_s or TQ2_0,
+// on the fp4 x fp4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4 with both
+// operands e2m1 and unit block scales).
+//
+// The product is y[n] = scale * sum_k w[n,k] x[k] with ternary w (BitNet
+// b1.58 i2_s format: codes 00/01/10 for -1/0/+1, 128-element groups, one fp32
+// tensor scale after the codes; llama.cpp TQ2_0: 256-element blocks of 2-bit
+// two's-complement codes with an fp16 scale per block).
+//
+// Activation digits.  Let max|x| < 2^E.  Every element is rounded to the
+// integer X = rint(x * 2^(34-E)), |X| < 2^34, and X is written with twelve
+// balanced base-8 digits d_r in [-4, 3]:
+//     X = sum_{r=0..11} d_r * 8^(11-r)
+// (the digits of X + 4*(8^12-1)/7, each minus 4).  Every digit is an e2m1
+// value, so the twelve digit planes are the rows of the fp4 operand A.  The
+// rounding to X is the only approximation: |x - X 2^(E-34)| <= 2^(E-35) <=
+// 2^-34 max|x|, so |y - y_exact| <= scale * K * 2^-34 * max|x|, far inside
+// 1e-5 * scale * sum|x| for any K the engine accepts (K <= 2^20).
+//
+// Weights as fp4.  i2_s codes c = w + 1 in {0, 1, 2} are used as the e2m1
+// bit patterns 0000 / 0001 / 0010, i.e. the values c/2; masking a code word
+// with 0x33333333 (and the word shifted by 2) leaves two codes per byte in
+// the low bits of two nibbles, so eight weights cost one or two operations.
+// Then sum_k w x = 2 * sum_k (c/2) X - sum_k X, with sum_k X formed by the
+// preparation.  TQ2_0 codes are turned into signed e2m1 halves (+-0.5 as
+// 0001 / 1001) by moving the code's high bit to the nibble's sign bit, and
+// each 256-k block's MFMA sum is multiplied by the block's fp16 scale.
+// Every MFMA sum is exact in fp32 (multiples of 1/2 below 2^23); the
+// epilogue weights the planes by 8^(11-r) in fp64.
+//
+// Layout and parallelism.  MFMA lane l holds row (or column) l % 16 and the
+// 32 k values 32 (l/16) + e of a 128-k step.  The 16 bytes of a weight row at
+// byte 16 q of a 64-byte chunk (256 k: two i2_s groups, one TQ2_0 block)
+// give lane quarter q the B operands of the chunk's two steps; the
+// preparation writes the activation digits in exactly the k order this
+// implies.  A wave owns 32 weight rows (two 16-row column blocks sharing each
+// activation operand read) and fetches them per 1024 k with loads of 4 rows x
+// 256 contiguous bytes (the shape the memory system streams fastest; a load
+// in operand order touches 16 rows per 16 lanes), which go through a padded
+// LDS tile private to the wave.  The workgroup's four waves share a
+// double-buffered LDS window of activation digits, the only thing they
+// synchronise on.  Loads run two tiles ahead of the multiply.  Workgroup ids
+// are mapped so that the workgroups of one product run on one XCD and share
+// its L2 copy of the activation digits.
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+using namespace llk;
+
+constexpr int kPl = 12;                                // digit planes
+constexpr int kPlRowBytes = 16;                        // 32 nibbles: one plane, one step, one lane quarter
+constexpr int kQuarterBytes = kPl * kPlRowBytes;       // 192
+constexpr int kStepBytes = 4 * kQuarterBytes;          // 768: one 128-k step
+constexpr int kChunkBytes = 2 * kStepBytes;            // 1536: one 256-k chunk
+constexpr int kSliceChunks = 8;                        // chunks per preparation workgroup
+#ifndef LL_F4_CB
+#define LL_F4_CB 2                                     // 16-row column blocks per wave
+#endif
+#ifndef LL_F4_CUNROLL
+#define LL_F4_CUNROLL 1                                // chunk loop of the multiply not unrolled (register use)
+#endif
+#ifndef LL_F4_CHUNK_BARRIER
+#define LL_F4_CHUNK_BARRIER 1
+#endif
+#ifndef LL_F4_NT
+#define LL_F4_NT 0                                     // weights read with non-temporal loads
+#endif
+constexpr int kCB = LL_F4_CB;
+constexpr int kGroup = 4;                              // chunks per weight tile: 256 bytes of each row
+constexpr int kWStride = kGroup * 64 + 16;             // padded LDS tile row
+constexpr int kWTile = 16 * kCB * kWStride;            // one wave's tile
+constexpr int kWaveRows = 16 * kCB;
+#ifndef LL_F4_WAVES
+#define LL_F4_WAVES 4
+#endif
+constexpr int kWaves = LL_F4_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAWin = kGroup * kChunkBytes;            // activation digits of one tile's k range
+constexpr int kAPer = (kAWin / 16 + kThreads - 1) / kThreads;   // 16-byte window pieces per thread
+constexpr int kWgRows = kWaves * kWaveRows;
+constexpr int64_t kMaxK = int64_t(1) << 20;            // exact fp32 MFMA sums: 4 K < 2^23
+
+constexpr uint32_t kDigitNibbles = 0x5420ACDEu;        // nibble v: e2m1 code of the digit v - 4
+constexpr uint32_t kBiasLo = 0x24924u, kBiasHi = 0x24924u;   // 4*(8^12-1)/7 split at bit 18
+
+__host__ __device__ constexpr int64_t nchunks(int64_t K) { return (K + 255) / 256; }
+__host__ __device__ constexpr int64_t nslices(int64_t K) { return (nchunks(K) + kSliceChunks - 1) / kSliceChunks; }
+// After the digit planes: int32 E at meta + 0, the slices' int64 sums of X at meta + 8 + 8 s.
+__host__ __device__ constexpr int64_t meta_off(int64_t K) { return nchunks(K) * kChunkBytes; }
+__host__ __device__ constexpr int64_t op_bytes(int64_t K) { return meta_off(K) + 8 + 8 * nslices(K); }
+
+struct F4Prep {
+    const float* x;
+    void* ops;
+    int64_t K;
+};
+
+struct F4Prob {
+    const uint8_t* codes;
+    const uint16_t* scales;       // TQ2_0 block scales, [N][K/256]
+    const uint8_t* ops;           // prepared digits of its activation
+    const float* bias;
+    float* y;
+    int64_t N, K;
+    int64_t wg0;                  // first (logical) workgroup of this product
+};
+
+// ---------------------------------------------------------------- preparation
+// Workgroup (token, slice): digits of chunks [8 slice, 8 slice + 8).  Thread
+// t: chunk 8 slice + t/32, step s = (t/16) % 2, lane quarter q = (t/4) % 4,
+// dword j = t % 4 of the quarter's 16-byte plane rows: eight elements, whose
+// digits fill nibbles e = 2b + h (b = 0..3, h = 0..1) of twelve dwords.
+template <int FMT>
+__global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__ tab) {
+    const F4Prep& P = tab[blockIdx.x];
+    const int64_t K = P.K;
+    const int slice = int(blockIdx.y);
+    if (slice >= nslices(K)) return;                       // whole workgroup
+    const float* x = P.x;
+    uint8_t* ops = static_cast<uint8_t*>(P.ops);
+    __shared__ float smax[4];                              // four waves
+    __shared__ long long ssum[4];
+    const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+
+    const int lc = tid >> 5, s = (tid >> 4) & 1, q = (tid >> 2) & 3, j = tid & 3;
+    const int64_t c = int64_t(slice) * kSliceChunks + lc;
+    const bool live = c < nchunks(K);
+    float v[8];
+    if (FMT == 1) {
+        // i2_s: byte 16 (q%2) + 4 j + b of group 2c + q/2 holds the elements
+        // 128 g + 32 t + 16 (q%2) + 4 j + b at shifts 6 - 2t; nibble h of the
+        // masked word takes t = 3 - 2h (step 0) or t = 2 - 2h (step 1).
+        const int64_t g = 2 * c + (q >> 1);
+        const bool ok = live && g < K / 128;
+        const int64_t gc = ok ? g : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = (s == 0 ? 3 : 2) - 2 * h;
+            const f32x4 w4 = ld16f(x + 128 * gc + 32 * t + 16 * (q & 1) + 4 * j);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v[2 * b + h] = ok ? w4[b] : 0.0f;
+        }
+    } else {
+        // TQ2_0: byte 16 q + 4 j + b of block c holds elements 4 (16 q + 4 j + b) + i
+        // at bits 2 i; nibble h of step s takes i = 2h + s.
+        const int64_t cc = live ? c : 0;
+        const float* xb = x + 256 * cc + 64 * q + 16 * j;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x4 w4 = ld16f(xb + 4 * b);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) v[2 * b + h] = live ? w4[2 * h + s] : 0.0f;
+        }
+    }
+
+    // max |x| over the token (this thread's elements were requested above, so
+    // both loads are in flight together)
+    float mx = 0.0f;
+    for (int64_t i = tid; i < K / 4; i += 256) {
+        const f32x4 u = ld16f(x + 4 * i);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
+    }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    int E = 0;
+    (void)frexpf(mx, &E);                                  // mx < 2^E; E = 0 when mx == 0
+    const int sh = 34 - E;                                 // in [-94, 183]: two exact power-of-two factors
+    const int sa = sh < 120 ? sh : 120;
+    const float f1 = ldexpf(1.0f, sa), f2 = ldexpf(1.0f, sh - sa);
+
+    uint32_t out[kPl];
+#pragma unroll
+    for (int r = 0; r < kPl; ++r) out[r] = 0;
+    long long xsum = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float t = rintf((v[e] * f1) * f2);           // X, an integer-valued float, |X| < 2^34
+        const float th = floorf(t * 0x1p-18f);             // X = th 2^18 + tl, 0 <= tl < 2^18 (both exact)
+        const float tl = fmaf(th, -0x1p18f, t);
+        const int hi = int(th), lo = int(tl);
+        xsum += (long long)hi * (1 << 18) + lo;
+        const uint32_t l2 = uint32_t(lo) + kBiasLo;        // X + bias = H 2^18 + L
+        const uint32_t L = l2 & 0x3FFFFu;
+        const uint32_t H = uint32_t(hi + int(kBiasHi) + int(l2 >> 18));
+#pragma unroll
+        for (int r = 0; r < kPl; ++r) {
+            const uint32_t src = r < 6 ? H : L;
+            const int o = 3 * (5 - (r % 6));
+            const uint32_t d = (src >> o) & 7u;
+            out[r] |= ((kDigitNibbles >> (4 * d)) & 15u) << (4 * e);
+        }
+    }
+    if (live) {
+        uint8_t* dst = ops + c * kChunkBytes + s * kStepBytes + q * kQuarterBytes + 4 * j;
+#pragma unroll
+        for (int r = 0; r < kPl; ++r)
+            *(__attribute__((address_space(1))) uint32_t*)(dst + r * kPlRowBytes) = out[r];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) xsum += __shfl_xor(xsum, o, kWave);
+    if (lane == 0) ssum[wave] = xsum;
+    __syncthreads();
+    if (tid == 0) {
+        const long long tot = ssum[0] + ssum[1] + ssum[2] + ssum[3];
+        *(__attribute__((address_space(1))) long long*)(ops + meta_off(K) + 8 + 8 * slice) = tot;
+        if (slice == 0) *(__attribute__((address_space(1))) int32_t*)(ops + meta_off(K)) = E;
+    }
+}
+
+// ---------------------------------------------------------------- product
+__device__ __forceinline__ f32x4 mfma_f4(i32x4 a, i32x4 b, f32x4 c) {
+    const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, 127, 0, 127);
+}
+
+// LDS: two activation windows (digits of 1024 k), then one weight tile per wave.
+__host__ __device__ constexpr int64_t prod_lds_bytes() { return 2 * kAWin + kWaves * kWTile; }
+
+template <int FMT>
+struct Regs {
+    i32x4 w[4 * kCB];             // load i of column block cb: rows 16 cb + 4 i + q, 16 bytes at 16 nl
+    i32x4 a[kAPer];               // pieces tid + kThreads p of the activation window
+    uint16_t sc[kGroup * kCB];    // TQ2_0: scale of this lane's row per chunk and column block
+};
+
+template <int FMT>
+__device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, char* abuf, char* wtile) {
+    const int lane = tid & 63, nl = lane & 15, q = lane >> 4;
+    const int64_t N = P.N, K = P.K, nch = nchunks(K);
+    const uint32_t rowbytes = uint32_t(K / 4);
+    const int ngr = int((nch + kGroup - 1) / kGroup);
+    const int64_t abytes = nch * kChunkBytes;
+    // loads: lane (q, nl) takes row 16 cb + 4 i + q, bytes 256 g + 16 nl of group g
+    const uint8_t* lrow[4 * kCB];
+#pragma unroll
+    for (int j = 0; j < 4 * kCB; ++j) {
+        int64_t r = row0 + 4 * j + q;
+        r = r < N ? r : N - 1;                             // clamped rows are not stored
+        lrow[j] = P.codes + r * int64_t(rowbytes);
+    }
+    const uint16_t* srow[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+        int64_t r = row0 + 16 * cb + nl;
+        r = r < N ? r : N - 1;
+        srow[cb] = P.scales + r * nch;
+    }
+    // Every load is issued by every lane from an in-bounds (clamped) address;
+    // bytes past the end of a row are zeroed when stored to LDS.
+    auto load = [&](int g, Regs<FMT>& r) {
+        const int gc = g < ngr ? g : ngr - 1;
+        const uint32_t off = uint32_t(gc) * (kGroup * 64) + 16 * nl;
+        const uint32_t offc = off < rowbytes ? off : rowbytes - 16;
+#pragma unroll
+        for (int j = 0; j < 4 * kCB; ++j) r.w[j] = LL_F4_NT ? ld16_stream(lrow[j] + offc) : ld16(lrow[j] + offc);
+#pragma unroll
+        for (int p = 0; p < kAPer; ++p) {
+            int64_t o = int64_t(gc) * kAWin + 16 * (tid + kThreads * p);
+            o = o < abytes ? o : abytes - 16;
+            r.a[p] = ld16(P.ops + o);
+        }
+        if (FMT == 2) {
+#pragma unroll
+            for (int c = 0; c < kGroup; ++c) {
+                int64_t b = int64_t(gc) * kGroup + c;
+                b = b < nch ? b : nch - 1;
+#pragma unroll
+                for (int cb = 0; cb < kCB; ++cb) r.sc[c * kCB + cb] = ld2(srow[cb] + b);
+            }
+        }
+    };
+    uint16_t csc[kGroup * kCB];
+    auto store = [&](int g, const Regs<FMT>& r) {
+        const bool ok = uint32_t(g) * (kGroup * 64) + 16 * nl < rowbytes;
+#pragma unroll
+        for (int j = 0; j < 4 * kCB; ++j)
+            *reinterpret_cast<i32x4*>(wtile + (4 * j + q) * kWStride + 16 * nl) = ok ? r.w[j] : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < kAPer; ++p) {
+            const int o = 16 * (tid + kThreads * p);
+            const bool aok = int64_t(g) * kAWin + o < abytes;      // digits past the row end are zero
+            if (kAPer * kThreads * 16 == kAWin || o < kAWin)
+                *reinterpret_cast<i32x4*>(abuf + (g & 1) * kAWin + o) = aok ? r.a[p] : i32x4{0, 0, 0, 0};
+        }
+        if (FMT == 2)
+#pragma unroll
+            for (int i = 0; i < kGroup * kCB; ++i) csc[i] = r.sc[i];
+    };
+
+    f32x4 acc[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int arow = q * kQuarterBytes + (nl < kPl ? nl : kPl - 1) * kPlRowBytes;
+
+    auto compute = [&](int g) {
+        const int cn = nch - int64_t(g) * kGroup < kGroup ? int(nch - int64_t(g) * kGroup) : kGroup;
+#pragma unroll LL_F4_CUNROLL
+        for (int c = 0; c < cn; ++c) {                  // the last group may hold fewer chunks
+            const char* ap = abuf + (g & 1) * kAWin + arow + c * kChunkBytes;
+            const i32x4 a0 = *reinterpret_cast<const i32x4*>(ap);
+            const i32x4 a1 = *reinterpret_cast<const i32x4*>(ap + kStepBytes);
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) {
+                const i32x4 u4 = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * kWStride + 64 * c + 16 * q);
+                i32x4 b0, b1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t u = uint32_t(u4[i]);
+                    if (FMT == 1) {
+                        b0[i] = int(u & 0x33333333u);
+                        b1[i] = int((u >> 2) & 0x33333333u);
+                    } else {
+                        b0[i] = int((u & 0x11111111u) | ((u & 0x22222222u) << 2));
+                        b1[i] = int(((u >> 2) & 0x11111111u) | (u & 0x88888888u));
+                    }
+                }
+                if (FMT == 1) {
+                    acc[cb] = mfma_f4(a0, b0, acc[cb]);
+                    acc[cb] = mfma_f4(a1, b1, acc[cb]);
+                } else {
+                    f32x4 blk = mfma_f4(a0, b0, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                    blk = mfma_f4(a1, b1, blk);
+                    const float sb = half_bits_to_float(csc[c * kCB + cb]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[cb][i] = fmaf(sb, blk[i], acc[cb][i]);
+                }
+            }
+#if LL_F4_CHUNK_BARRIER
+            asm volatile("" ::: "memory");                 // keep one chunk's operands live at a time
+#endif
+        }
+    };
+
+    // Group g is multiplied from LDS (the wave's weight tile, the shared
+    // activation window g % 2) while group g + 1 waits in registers and group
+    // g + 2 is being fetched.  The weight tile is private to the wave and its
+    // LDS accesses execute in program order, so it is rewritten after the
+    // multiply without a barrier; the barrier orders the shared windows.
+    Regs<FMT> r0, r1;
+    load(0, r0);
+    load(1, r1);
+    store(0, r0);
+    __syncthreads();
+    int g = 0;
+    for (; g + 2 <= ngr; g += 2) {                     // no exit between a load and its use
+        load(g + 2, r0);
+        compute(g);
+        __builtin_amdgcn_sched_barrier(0);             // a group's multiplies stay before its successor's
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 1, r1);
+        __syncthreads();
+        load(g + 3, r1);
+        compute(g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 2, r0);
+        __syncthreads();
+    }
+    if (g < ngr) compute(g);                           // odd group count: the last one is in the tile
+
+    // Epilogue: plane 4q + i of this lane's column weighted by 2 * 8^(11 - r)
+    // (the 2 undoes the half-valued weights), summed over the quarters.
+    const uint8_t* meta = P.ops + meta_off(K);
+    const int E = ld32(meta);
+    double tot[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q + i;
+            const double wgt = r < kPl ? ldexp(1.0, 1 + 3 * (kPl - 1 - r)) : 0.0;
+            t = fma(double(acc[cb][i]), wgt, t);
+        }
+        t += __shfl_xor(t, 16, kWave);
+        t += __shfl_xor(t, 32, kWave);
+        tot[cb] = t;
+    }
+    // lane l stores row row0 + l of column block l / 16
+    double t = tot[0];
+#pragma unroll
+    for (int cb = 1; cb < kCB; ++cb)
+        if (q == cb) t = tot[cb];
+    const double unit = ldexp(1.0, E - 34);
+    double yv;
+    if (FMT == 1) {
+        long long xs = 0;
+        for (int64_t sl = 0; sl < nslices(K); ++sl)
+            xs += *(__attribute__((address_space(1))) const long long*)(meta + 8 + 8 * sl);
+        const float scale = *(const __attribute__((address_space(1))) float*)(P.codes + N * int64_t(rowbytes));
+        yv = double(scale) * ((t - double(xs)) * unit);
+    } else {
+        yv = t * unit;                                      // block scales are inside t
+    }
+    const int64_t row = row0 + lane;                       // = row0 + 16 cb + nl for cb = q
+    float out = float(yv);
+    if (P.bias) out = __fadd_rn(out, P.bias[row < N ? row : N - 1]);
+    if (q < kCB && row < N) P.y[row] = out;
+}
+
+// grid: 8 * ceil(T / 8) workgroups for T logical ones; hardware workgroup w
+// runs on XCD w % 8, and takes logical index (w % 8) * T8 + w / 8.
+#ifndef LL_F4_OCC
+#define LL_F4_OCC 3                                    // waves per SIMD the register allocation aims at
+#endif
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LL_F4_OCC))) f4_batch_kernel(const F4Prob* __restrict__ tab,
+                                                            const int32_t* __restrict__ map, int64_t T) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int64_t w = blockIdx.x, T8 = (T + 7) / 8;
+    const int64_t L = (w % 8) * T8 + w / 8;
+    if (L >= T) return;                                    // whole workgroup
+    const F4Prob& P = tab[ld32(map + L)];
+    const int tid = int(threadIdx.x), wave = tid >> 6;
+    // waves past the last row still take part (clamped rows, nothing stored): the loop has barriers
+    const int64_t row0 = (L - P.wg0) * kWgRows + wave * kWaveRows;
+    f4_rows<FMT>(P, row0, tid, lds, lds + 2 * kAWin + wave * kWTile);
+}
+
+}  // namespace
+
+namespace llk {
+
+bool f4_engine(int64_t M, int64_t kmax) { return M == 1 && kmax <= kMaxK; }
+size_t f4_operand_bytes(int64_t K) { return size_t(op_bytes(K)); }
+int64_t f4_batch_rows() { return kWgRows; }
+size_t f4_prob_bytes() { return sizeof(F4Prob); }
+size_t f4_prep_bytes() { return sizeof(F4Prep); }
+int64_t f4_grid(int64_t T) { return 8 * ((T + 7) / 8); }
+
+void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
+                  int64_t N, int64_t K, int64_t wg0) {
+    F4Prob p;
+    p.codes = static_cast<const uint8_t*>(codes);
+    p.scales = static_cast<const uint16_t*>(scales);
+    p.ops = static_cast<const uint8_t*>(ops);
+    p.bias = bias;
+    p.y = y;
+    p.N = N;
+    p.K = K;
+    p.wg0 = wg0;
+    *static_cast<F4Prob*>(dst) = p;
+}
+
+void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K) {
+    F4Prep p;
+    p.x = x;
+    p.ops = ops;
+    p.K = K;
+    *static_cast<F4Prep*>(dst) = p;
+}
+
+hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int64_t kmax, hipStream_t stream) {
+    const dim3 grid{unsigned(nprep), unsigned(nslices(kmax))}, block{256};
+    const F4Prep* t = static_cast<const F4Prep*>(prep_table);
+    if (fmt == 1)
+        hipLaunchKernelGGL(f4_prep_kernel<1>, grid, block, 0, stream, t);
+    else
+        hipLaunchKernelGGL(f4_prep_kernel<2>, grid, block, 0, stream, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
+                                   hipStream_t stream) {
+    (void)kmax;
+    const dim3 grid{unsigned(f4_grid(T))}, block{unsigned(kThreads)};
+    const size_t lds = size_t(prod_lds_bytes());
+    const F4Prob* t = static_cast<const F4Prob*>(prob_table);
+    const int32_t* m = static_cast<const int32_t*>(map);
+    hipError_t e = allow_dynamic_lds(fmt == 1 ? reinterpret_cast<const void*>(f4_batch_kernel<1>)
+                                              : reinterpret_cast<const void*>(f4_batch_kernel<2>), lds);
+    if (e != hipSuccess) return e;
+    if (fmt == 1)
+        hipLaunchKernelGGL(f4_batch_kernel<1>, grid, block, lds, stream, t, m, T);
+    else
+        hipLaunchKernelGGL(f4_batch_kernel<2>, grid, block, lds, stream, t, m, T);
+    return hipGetLastError();
+}
+
+}  // namespace llk

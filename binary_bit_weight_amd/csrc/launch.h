@@ -57,3 +57,23 @@ hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, 
 hipError_t launch_planes_batch_product(const void* prob_table, const void* map, int fmt, int64_t M, int64_t wgs,
                                        hipStream_t stream);
 }  // namespace llk
+
+namespace llk {
+// fp32-activation single-token product on the fp4 matrix cores (gemv_fp4.hip),
+// formats i2_s (fmt 1) and TQ2_0 (fmt 2): activations as twelve base-8 digit
+// planes (one preparation launch), weights fed to the MFMAs straight from
+// registers.  Used by prepared batches with M == 1 and every K <= 2^20.
+bool f4_engine(int64_t M, int64_t kmax);
+size_t f4_operand_bytes(int64_t K);                  // prepared digits of one activation
+int64_t f4_batch_rows();
+size_t f4_prob_bytes();
+size_t f4_prep_bytes();
+int64_t f4_grid(int64_t T);                         // workgroups launched for T logical ones
+void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
+                  int64_t N, int64_t K, int64_t wg0);
+void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K);
+hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int64_t kmax, hipStream_t stream);
+// map: int32 [T], the product of each logical workgroup
+hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
+                                   hipStream_t stream);
+}  // namespace llk

@@ -49,7 +49,7 @@ def test_quantize_bitexact(M, K, dtype):
 # ------------------------------------------------------------------ i2_s, fp32 activations
 # A single call with M = 1 up to K = 8192 runs the fused kernel (planes built
 # per workgroup); K = 8320 and M = 2, 3 the preparation + product pair;
-# M > 3 the bf16 path.
+# M > 3 the same kernels in passes of up to three tokens.
 I2S_F32_SMALL = [(256, 512, 1), (37, 384, 1), (16, 128, 1), (1, 128, 1), (100, 640, 2), (77, 512, 5),
                  (64, 256, 6), (50, 384, 11), (33, 512, 16), (129, 1024, 3), (40, 8192, 1), (70, 8320, 1),
                  (65, 1152, 2), (3, 3200, 1)]
@@ -260,6 +260,64 @@ def test_gemv_plan_matches_oracle(fmt, M, big):
             y_ref, tsum = fn(packed, N, K, xs_np[slot][0], rows)
             ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
             assert ok, "N=%d K=%d round %d: worst error / bound %.3f" % (N, K, rnd, worst)
+
+
+@pytest.mark.parametrize("fmt", ["i2s", "tq2"])
+def test_gemv_plan_one_token_edges(fmt):
+    """One-token prepared batch (the fp4 digit-plane engine) on the cases its
+    activation split has to survive: an all-zero token (y = bias exactly),
+    every element at +-max|x| (largest digit words), magnitudes near 1e30 and
+    1e-30 (exponent scaling in two steps), one large element among tiny ones
+    (sum|x| close to max|x|, so the bound is tight), the shortest rows (one
+    group / one block), row counts that end inside a column block, and
+    biases."""
+    t = torch()
+    base = 256 if fmt == "tq2" else 128
+    rng = synth.rng(4300)
+    cases = []
+    for i, (N, K) in enumerate([(90, 1024), (33, 2 * base), (1, base), (257, 2560), (70, 3 * base),
+                                (17, 1536), (300, 768)]):
+        x = synth.normal_f32(4310 + i, 1, K)
+        if i == 0:
+            x[:] = 0.0
+        elif i == 1:
+            x[:] = np.where(rng.random(K) < 0.5, -1.0, 1.0).astype(np.float32) * np.float32(3.0)
+        elif i == 3:
+            x *= np.float32(1e30)
+        elif i == 4:
+            x *= np.float32(1e-30)
+        elif i == 5:
+            x *= np.float32(1e-6)
+            x[0, 7] = np.float32(-40.0)
+        bias = synth.uniform_f32(4320 + i, N, -1, 1) if i % 2 == 0 else None
+        cases.append((N, K, x, bias))
+    items, refs = [], []
+    for i, (N, K, x, bias) in enumerate(cases):
+        if fmt == "i2s":
+            _, _, packed = make_i2s(4330 + i, N, K)
+            W = L.upload_i2s(packed, N, K)
+        else:
+            _, _, packed = make_tq2(4330 + i, N, K)
+            W = L.upload_tq2(packed, N, K)
+        y = t.empty((1, N), dtype=t.float32, device="cuda")
+        b = None if bias is None else t.from_numpy(bias).cuda()
+        items.append((W, t.from_numpy(x).cuda(), b, y))
+        refs.append((packed, N, K, x, bias))
+    announce("plan one-token edges", fmt)
+    plan = L.GemvPlan(items, 1)
+    plan.run()
+    t.cuda.synchronize()
+    fn = oracle.i2s_gemv_f32 if fmt == "i2s" else oracle.tq2_gemv_f32
+    for i, ((_, _, _, y), (packed, N, K, x, bias)) in enumerate(zip(items, refs)):
+        got = y.cpu().numpy()
+        if i == 0:
+            assert np.array_equal(got[0], bias)
+            continue
+        y_ref, tsum = fn(packed, N, K, x)
+        if bias is not None:
+            y_ref = y_ref + bias.astype(np.float64)[None, :]
+        ok, worst = f32_tol_ok(got, y_ref, tsum)
+        assert ok, "case %d (N=%d K=%d): worst error / bound %.3f" % (i, N, K, worst)
 
 
 @pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 2), ("tq2", 1), ("tq2", 3), ("i2s", 6)])
