@@ -61,9 +61,6 @@ constexpr int kSliceChunks = 8;                        // chunks per preparation
 #ifndef LL_F4_CUNROLL
 #define LL_F4_CUNROLL 1                                // chunk loop of the multiply not unrolled (register use)
 #endif
-#ifndef LL_F4_CHUNK_BARRIER
-#define LL_F4_CHUNK_BARRIER 1
-#endif
 #ifndef LL_F4_NT
 #define LL_F4_NT 0                                     // weights read with non-temporal loads
 #endif
@@ -330,9 +327,6 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, 
                     for (int i = 0; i < 4; ++i) acc[cb][i] = fmaf(sb, blk[i], acc[cb][i]);
                 }
             }
-#if LL_F4_CHUNK_BARRIER
-            asm volatile("" ::: "memory");                 // keep one chunk's operands live at a time
-#endif
         }
     };
 
