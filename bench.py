@@ -229,7 +229,7 @@ def extras_single(L, synth, torch, dev, stream):
             x = torch.from_numpy(synth.normal_f32(510 + M, M, K)).to(dev)
             xq, xsc = L.quantize(x, stream)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
+            ws = torch.zeros((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
             ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_I8, xq, xsc, M, None, y, ws, st),
                             reps, max(2 * reps, 16), stream)
             out["w1a8_gemv_%s_%dx%d_M%d" % (name, N, K, M)] = {

@@ -92,7 +92,7 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M) {
     if (!w || M < 1 || M > 16 || w->K <= 0) return size_t(-1);
     if (act == LL_ACT_F32)
         return llk::planes_workspace(M, w->K);
-    if (act == LL_ACT_I8) return w->fmt == LL_FMT_W1 && w->group > 0 ? llk::w1_workspace(M, w->K, w->group) : 0;
+    if (act == LL_ACT_I8) return w->fmt == LL_FMT_W1 && w->group > 0 ? llk::w1_workspace(M, w->N, w->K, w->group) : 0;
     return size_t(-1);
 }
 
@@ -129,7 +129,7 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
         if (w->fmt == LL_FMT_W1) {
             st = check_w1_device(w, fn);
             if (st) return st;
-            const size_t need = llk::w1_workspace(M, w->K, w->group);
+            const size_t need = llk::w1_workspace(M, w->N, w->K, w->group);
             if (!workspace || workspace_bytes < need)
                 return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
             if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
@@ -145,7 +145,7 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
 
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     if (!w || M < 1) return size_t(-1);
-    if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->K, w->group);
+    if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->N, w->K, w->group);
     if (w->fmt == LL_FMT_I2S && w->K > 0 && w->N > 0) return llk::gemm_i8_workspace(M, w->N, w->K);
     return 0;
 }
@@ -164,7 +164,7 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
         st = check_w1_device(w, fn);
         if (st) return st;
         if (acc_out) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for W1 (per-group scales)");
-        const size_t need = llk::w1_workspace(M, w->K, w->group);
+        const size_t need = llk::w1_workspace(M, w->N, w->K, w->group);
         if (!workspace || workspace_bytes < need)
             return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
         if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");

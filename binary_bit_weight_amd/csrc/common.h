@@ -70,6 +70,14 @@ __device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
 __device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
     return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_coherent64(double* p, double v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __double_as_longlong(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_coherent64(const double* p) {
+    return __longlong_as_double(__hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 // Wait until every vector memory operation of this wave has completed
 // (gfx9 s_waitcnt: vmcnt = 0, expcnt and lgkmcnt not waited on).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

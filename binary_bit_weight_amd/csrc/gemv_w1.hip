@@ -45,6 +45,7 @@ constexpr int kW1Rows = kW1Waves * kW1RowsPerWave;   // 128 rows per workgroup
 constexpr int kWinK1 = 1024;                          // k per window
 constexpr int kWinB1 = kWinK1 / 8;                    // 128 code bytes per row per window
 constexpr int kChunks = kWinK1 / 128;                 // 8 MFMA chunks per window
+constexpr int kW1MaxSplits = 8;                       // K splits of a narrow matrix
 
 // LDS row of a wave's tile: 128 code bytes | the window's scales (1024/G fp16) | pad to 16 mod 128.
 __host__ __device__ inline int w1_stride(int G) {
@@ -89,8 +90,15 @@ __device__ __forceinline__ uint8_t fp8_small_int(int v) {
 // One thread per 16-byte piece of an A row (chunk c, row r, piece u), plus the
 // group sums.  Grid: (ceil(chunks * R * 8 / 256), 1) and a second pass over
 // groups.  Reads xq [M][K] int8.
+__device__ void w1_qsum(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G, void* __restrict__ ws,
+                        int64_t block);
+
 __global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
-                                                      void* __restrict__ ws) {
+                                                      void* __restrict__ ws, int64_t prep_blocks) {
+    if (int64_t(blockIdx.x) >= prep_blocks) {              // the group sums, in the same launch
+        w1_qsum(xq, M, K, G, ws, int64_t(blockIdx.x) - prep_blocks);
+        return;
+    }
     const int S = w1_slots(G), R = w1_arows(int(M), G);
     const int64_t pieces = (K / 128) * R * 8;
     const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -102,19 +110,24 @@ __global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__
         const int h = r & 1, pm = r >> 1;
         const int m = pm / S, j = pm % S;
         const int8_t* xr = xq + int64_t(m) * K + 128 * c;
+        // Piece u holds A bytes 16u + i of lane quarter q = u / 2; byte i pairs
+        // with B quarter qp = 2 (u % 2) + u / 4, nibble 16 (q % 2) + i, i.e. the
+        // chunk-local weight 32 qp + 2 (q % 2) + i / 8 + 4 (i % 8): all sixteen
+        // lie in the 32 bytes at 32 qp, read with two vector loads.
+        const int q = u >> 1, qp = 2 * (u & 1) + (u >> 2);
+        const bool in_slot = G >= 128 || (32 * qp) / G == j;   // the whole piece is in slot j or not
+        const i32x4 lo4 = ld16(xr + 32 * qp), hi4 = ld16(xr + 32 * qp + 16);
+        const uint32_t dw[8] = {uint32_t(lo4[0]), uint32_t(lo4[1]), uint32_t(lo4[2]), uint32_t(lo4[3]),
+                                uint32_t(hi4[0]), uint32_t(hi4[1]), uint32_t(hi4[2]), uint32_t(hi4[3])};
+        const int b0 = 2 * (q & 1);
         uint32_t out[4];
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
             uint32_t word = 0;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
-                const int pos = 16 * u + 4 * w4 + bb;      // byte of the 128-byte row
-                const int q = pos >> 5, e = pos & 31;       // A lane quarter, byte in lane
-                const int qp = 2 * (e >> 4) + (q >> 1);     // paired B lane quarter
-                const int ep = 16 * (q & 1) + (e & 15);     // paired B nibble
-                const int kw = 32 * qp + 4 * (ep & 7) + (ep >> 3);
-                const bool in_slot = G >= 128 || kw / G == j;
-                int v = in_slot ? int(xr[kw]) : 0;
+                const int i = 4 * w4 + bb;
+                const int v = in_slot ? int(int8_t(dw[i & 7] >> (8 * (b0 + (i >> 3))))) : 0;
                 const int hi = (v + 8) >> 4;                // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
                 const int d = h == 0 ? hi : v - 16 * hi;
                 word |= uint32_t(fp8_small_int(d)) << (8 * bb);
@@ -126,11 +139,11 @@ __global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__
 }
 
 // Group sums qs[m][g] = sum_{k in g} q: one wave per (token, group).
-__global__ void __launch_bounds__(256) w1_qsum_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
-                                                      void* __restrict__ ws) {
+__device__ void w1_qsum(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G, void* __restrict__ ws,
+                        int64_t block) {
     const int lane = threadIdx.x & 63;
     const int64_t ng = K / G;
-    const int64_t item = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t item = block * 4 + (threadIdx.x >> 6);
     if (item >= M * ng) return;
     const int64_t m = item / ng, g = item % ng;
     int s = 0;
@@ -144,15 +157,25 @@ __global__ void __launch_bounds__(256) w1_qsum_kernel(const int8_t* __restrict__
 // ---------------------------------------------------------------- product
 // G: group size; MT: A row blocks of 16 (R = 2 M S <= 16 MT rows); NP: pairs
 // (token, slot) per lane and row block that can be live (1 when R <= 2, else 2).
+// Split K.  With few row blocks (a narrow matrix) the workgroups of a row
+// block split its windows nsplit ways; each writes its partial sums S (exact
+// in fp64, so their sum is too, in any order) to part and counts itself in;
+// the last to arrive adds the partials and writes y, then resets the counter
+// (counters start zero and every call leaves them zero).
 template <int G, int MT, int NP>
 __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
                                                                  const float* __restrict__ xs,
                                                                  const float* __restrict__ bias,
-                                                                 float* __restrict__ y) {
+                                                                 float* __restrict__ y, int nsplit,
+                                                                 double* __restrict__ part,
+                                                                 int32_t* __restrict__ counters) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ int last_flag;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t rb = int64_t(blockIdx.x) / nsplit;      // row block
+    const int split = int(blockIdx.x % nsplit);
     const int nl = lane & 15, q = lane >> 4;
     constexpr int S = G >= 128 ? 1 : 128 / G;
     const int R = w1_arows(M, G);
@@ -160,8 +183,10 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
     constexpr int ngw = kWinK1 / G;                        // groups per window
     const int64_t ng = K / G;
     const uint32_t rowbytes = uint32_t(K / 8);
-    const int nwin = int((K + kWinK1 - 1) / kWinK1);
-    const int64_t n0 = int64_t(blockIdx.x) * kW1Rows + kW1RowsPerWave * wave;
+    const int nwall = int((K + kWinK1 - 1) / kWinK1);
+    const int w0 = int(int64_t(nwall) * split / nsplit);  // windows [w0, nwin) of this split
+    const int nwin = int(int64_t(nwall) * (split + 1) / nsplit);
+    const int64_t n0 = rb * kW1Rows + kW1RowsPerWave * wave;
     char* wtile = lds + wave * kW1RowsPerWave * stride;
     const int abytes = (w1_abuf_bytes(M, G) + 15) / 16 * 16;
     char* abase = lds + kW1Waves * kW1RowsPerWave * stride;
@@ -328,31 +353,33 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
         }
     };
 
+    // Window w is multiplied from LDS while window w + 1 waits in registers
+    // and window w + 2 is being fetched.  Every load is issued (windows past
+    // the range reload in-bounds bytes that are never multiplied) and the
+    // loop has no exit between a load and its use, so the compiler's waits
+    // count exactly and the prefetch overlaps the multiply.
     Regs r0, r1;
-    load(0, r0);
-    if (nwin > 1) load(1, r1);
-    store_w(0, r0);
-    store_a(0, r0);
+    load(w0, r0);
+    load(w0 + 1, r1);
+    store_w(w0, r0);
+    store_a(w0, r0);
     __syncthreads();
-    for (int w = 0; w < nwin; w += 2) {
-        if (w + 2 < nwin) load(w + 2, r0);
+    int w = w0;
+    for (; w + 2 <= nwin; w += 2) {
+        load(w + 2, r0);
         compute(w);
-        if (w + 1 < nwin) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            store_w(w + 1, r1);
-            store_a(w + 1, r1);
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store_w(w + 1, r1);
+        store_a(w + 1, r1);
         __syncthreads();
-        if (w + 1 >= nwin) break;
-        if (w + 3 < nwin) load(w + 3, r1);
+        load(w + 3, r1);
         compute(w + 1);
-        if (w + 2 < nwin) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            store_w(w + 2, r0);
-            store_a(w + 2, r0);
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store_w(w + 2, r0);
+        store_a(w + 2, r0);
         __syncthreads();
     }
+    if (w < nwin) compute(w);                              // odd window count: the last one is in LDS
 
     // y[m][n] = (float)((double)xs[m] * S[m][n]) (+ bias).  Pair p = m S + j
     // of row block b lives in lane quarter (p % 8) / 2, slot t = p % 2; the S
@@ -374,68 +401,136 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
     for (int e = tid; e < kW1Waves * 2 * 16 * M; e += 64 * kW1Waves) {
         const int m = e % M;
         const int col = e / M;                             // wave * 32 + cb * 16 + nl
-        const int64_t n = int64_t(blockIdx.x) * kW1Rows + col;
-        if (n >= N) continue;
+        const int64_t n = rb * kW1Rows + col;
         double s = 0.0;
         for (int j = 0; j < S; ++j) s += red[col * npairs + m * S + j];
+        if (nsplit > 1) {
+            st_coherent64(part + (int64_t(blockIdx.x) * kW1Rows + col) * M + m, s);
+        } else if (n < N) {
+            float out = float(double(xs[m]) * s);
+            if (bias) out = __fadd_rn(out, bias[n]);
+            y[int64_t(m) * N + n] = out;
+        }
+    }
+    if (nsplit == 1) return;
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) last_flag = atomicAdd(counters + rb, 1) == nsplit - 1;
+    __syncthreads();
+    if (!last_flag) return;
+    for (int e = tid; e < kW1Waves * 2 * 16 * M; e += 64 * kW1Waves) {
+        const int m = e % M;
+        const int col = e / M;
+        const int64_t n = rb * kW1Rows + col;
+        if (n >= N) continue;
+        // every split's partial requested at once (nsplit <= kW1MaxSplits), added in split order
+        double pv[kW1MaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kW1MaxSplits; ++sp) {
+            const int spc = sp < nsplit ? sp : nsplit - 1;
+            pv[sp] = ld_coherent64(part + ((rb * nsplit + spc) * kW1Rows + col) * M + m);
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int sp = 0; sp < kW1MaxSplits; ++sp)
+            if (sp < nsplit) s += pv[sp];
         float out = float(double(xs[m]) * s);
         if (bias) out = __fadd_rn(out, bias[n]);
         y[int64_t(m) * N + n] = out;
     }
+    if (tid == 0) st_coherent(counters + rb, 0);          // ready for the next call
 }
 
 template <int G, int MT, int NP>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
-                     const float* xs, const float* bias, float* y, hipStream_t stream) {
-    const dim3 grid{unsigned((N + kW1Rows - 1) / kW1Rows)}, block{64 * kW1Waves};
+                     const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
+                     hipStream_t stream) {
+    const dim3 grid{unsigned((N + kW1Rows - 1) / kW1Rows * nsplit)}, block{64 * kW1Waves};
     size_t lds = size_t(w1_lds_bytes(M, G));
     const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
     lds = lds > red ? lds : red;
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y);
+    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y,
+                       nsplit, part, counters);
     return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
-                       const float* xs, const float* bias, float* y, hipStream_t stream) {
+                       const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
+                       hipStream_t stream) {
     const int R = w1_arows(M, G);
-    if (R <= 2) return launch_w1<G, 1, 1>(bits, sc, N, K, M, ws, xs, bias, y, stream);
-    if (R <= 16) return launch_w1<G, 1, 2>(bits, sc, N, K, M, ws, xs, bias, y, stream);
-    return launch_w1<G, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, stream);
+    if (R <= 2) return launch_w1<G, 1, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    if (R <= 16) return launch_w1<G, 1, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    return launch_w1<G, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
 }
 
 // Tokens per pass: the A rows of a pass (2 x tokens x slots) fit two row blocks.
 int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
 
+#ifndef LL_W1_TARGET_WGS
+#define LL_W1_TARGET_WGS 512
+#endif
+// K splits: enough workgroups to spread a narrow matrix over the chip, at
+// most one split per 1024-k window.
+int w1_splits(int64_t N, int64_t K) {
+    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
+    const int64_t nwin = (K + kWinK1 - 1) / kWinK1;
+    int64_t s = (LL_W1_TARGET_WGS + rbs - 1) / rbs;
+    s = s < nwin ? s : nwin;
+    s = s < kW1MaxSplits ? s : kW1MaxSplits;
+    return int(s < 1 ? 1 : s);
+}
+// Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64, counters [rbs].
+size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G) + 255) / 256 * 256; }
+
 }  // namespace
 
 namespace llk {
 
-size_t w1_workspace(int64_t M, int64_t K, int G) {
+size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G) {
     const int64_t tb = w1_tokens_per_pass(G);
-    return w1_ws_bytes(M < tb ? M : tb, K, G);
+    const int64_t Mp = M < tb ? M : tb;
+    const int ns = w1_splits(N, K);
+    if (ns == 1) return w1_ws_bytes(Mp, K, G);
+    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
+    return w1_split_off(Mp, K, G) + size_t(rbs) * ns * kW1Rows * Mp * 8 + size_t(rbs) * 4;
 }
 
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
     const int64_t tb = w1_tokens_per_pass(G);
+    const int ns = w1_splits(N, K);
+    const int64_t Mp = M < tb ? M : tb;
+    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
+    double* part = ns > 1 ? reinterpret_cast<double*>(static_cast<char*>(ws) + w1_split_off(Mp, K, G)) : nullptr;
+    int32_t* counters = ns > 1 ? reinterpret_cast<int32_t*>(part + rbs * ns * kW1Rows * Mp) : nullptr;
     for (int64_t m0 = 0; m0 < M; m0 += tb) {               // every pass reads the weights once
         const int64_t Mb = M - m0 < tb ? M - m0 : tb;
         const int8_t* xb = xq + m0 * K;
         const int R = w1_arows(int(Mb), G);
         const int64_t pieces = (K / 128) * R * 8;
-        hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned((pieces + 255) / 256)}, dim3{256}, 0, stream, xb, Mb, K, G,
-                           ws);
+        const int64_t pblocks = (pieces + 255) / 256;
         const int64_t items = Mb * (K / G);
-        hipLaunchKernelGGL(w1_qsum_kernel, dim3{unsigned((items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb, K, G, ws);
+        hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned(pblocks + (items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb, K,
+                           G, ws, pblocks);
         hipError_t e = hipSuccess;
         switch (G) {
-        case 32: e = launch_w1_g<32>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
-        case 64: e = launch_w1_g<64>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
-        case 128: e = launch_w1_g<128>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
-        default: e = launch_w1_g<256>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, stream); break;
+        case 32:
+            e = launch_w1_g<32>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters, stream);
+            break;
+        case 64:
+            e = launch_w1_g<64>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters, stream);
+            break;
+        case 128:
+            e = launch_w1_g<128>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters,
+                                 stream);
+            break;
+        default:
+            e = launch_w1_g<256>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters,
+                                 stream);
+            break;
         }
         if (e != hipSuccess) return e;
     }

@@ -18,7 +18,10 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_
 
 // W1A8 product (binary weights, int8 activations), any M (passes of up to 16
 // tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.
-size_t w1_workspace(int64_t M, int64_t K, int G);
+// Narrow matrices split K over workgroups: the workspace then also holds
+// partial sums and per-row-block counters (zero-filled before its first use;
+// every call leaves the counters zero).
+size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G);
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
 

@@ -295,7 +295,8 @@ def gemv(w: Weights, x, xs=None, bias=None, stream=None):
     act = LL_ACT_I8 if x.dtype == torch.int8 else LL_ACT_F32
     y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
     nws = ll_gemv_workspace_size(w, act, M)
-    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device) if nws else None
+    # zero-filled: split-K counters (W1) must start at zero (each call leaves them zero)
+    ws = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=x.device) if nws else None
     ll_bitlinear_gemv(w, act, x, xs, M, bias, y, ws, stream)
     return y
 

@@ -183,7 +183,11 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
    [M,N].  workspace: device buffer of at least
    ll_gemv_workspace_size(w, act, M) bytes (may be NULL when that is 0);
-   it is overwritten. */
+   it is overwritten.  With W1 weights a narrow matrix splits K over
+   workgroups and the workspace also holds their per-row-block counters: it
+   must be zero-filled before its first use (every call leaves the counters
+   zero again), and two calls sharing one workspace must not run
+   concurrently. */
 ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs,
                             int64_t M, const float* bias, float* y,
                             void* workspace, size_t workspace_bytes, void* stream);

@@ -122,3 +122,24 @@ def test_w1a8_unit_scales_integer_result():
     w = L.ll_unpack_w1(bits, K).astype(np.int64)
     exact = (q.astype(np.int64) @ w.T).astype(np.float32)
     assert np.array_equal(y, exact) and np.array_equal(y_ref, exact)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_w1a8_split_workspace_reuse(M):
+    """A narrow matrix splits K over workgroups (partial sums and per-row-block
+    counters in the workspace): three calls in a row on one zero-filled
+    workspace, with new activations each time, stay bit-exact (the counters
+    are left zero by every call)."""
+    t = torch()
+    N, K, G = 300, 5120, 128
+    bits, scales = make_w1(5800 + M, N, K, G)
+    W = L.upload_w1(bits, scales, K, G)
+    nws = L.ll_gemv_workspace_size(W, L.LL_ACT_I8, M)
+    ws = t.zeros((nws,), dtype=t.uint8, device="cuda")
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    for rnd in range(3):
+        q, s = _acts(5810 + 10 * M + rnd, M, K)
+        announce("w1a8 split reuse", M, rnd)
+        L.ll_bitlinear_gemv(W, L.LL_ACT_I8, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, ws)
+        y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rnd

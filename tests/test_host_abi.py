@@ -195,9 +195,15 @@ def test_plan_bytes_hold_every_activation_layout():
 def test_w1_device_argument_errors_and_workspace():
     lib = L.lib()
     w = _w(fmt=L.LL_FMT_W1, N=64, K=5120, group=128)
-    # A rows: 40 chunks x (2 digits x 8 tokens) x 128 B, then int32 group sums [8][40]
-    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 8) == 40 * 16 * 128 + 8 * 40 * 4
-    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 40 * 2 * 128 + 40 * 4
+    # A rows: 40 chunks x (2 digits x 8 tokens) x 128 B, then int32 group sums [8][40]; one row block
+    # of 128 splits K five ways (one per 1024-k window): fp64 partial sums [5][128][tokens] at the
+    # next 256-byte boundary, then one int32 counter
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 8) == 40 * 16 * 128 + 8 * 40 * 4 + 5 * 128 * 8 * 8 + 4
+    base1 = 40 * 2 * 128 + 40 * 4
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == (base1 + 255) // 256 * 256 + 5 * 128 * 8 + 4
+    # a wide matrix (1940 row blocks) is not split
+    wide = _w(fmt=L.LL_FMT_W1, N=248320, K=5120, group=128)
+    assert lib.ll_gemv_workspace_size(C.byref(wide), L.LL_ACT_I8, 1) == base1
     # G = 32: four group slots per 128-k chunk, passes of 4 tokens
     w32 = _w(fmt=L.LL_FMT_W1, N=64, K=512, group=32)
     assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == 4 * 32 * 128 + 4 * 16 * 4
