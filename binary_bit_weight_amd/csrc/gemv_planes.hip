@@ -1,5 +1,7 @@
-// Decode product with fp32 activations, 1 <= M <= 3, i2_s or TQ2_0, on the
-// int8 matrix cores with exact integer accumulation.
+// Decode product with fp32 activations, 1 <= M <= 16 (passes of up to three
+// tokens), i2_s or TQ2_0, on the int8 matrix cores with exact integer
+// accumulation.  Single calls and M >= 2; a prepared batch of one token runs
+// on the fp4 digit-plane engine instead.
 //
 // Activation split.  Each token row x is written as
 //     x = 2^(E-6) * sum_{p=0..4} q_p * 128^-p  +  r,

@@ -470,7 +470,7 @@ hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int6
 int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
 
 #ifndef LL_W1_TARGET_WGS
-#define LL_W1_TARGET_WGS 512
+#define LL_W1_TARGET_WGS 256
 #endif
 // K splits: enough workgroups to spread a narrow matrix over the chip, at
 // most one split per 1024-k window.
