@@ -5,23 +5,23 @@
 // decode GEMV).  acc[m,n] = sum_k w[n,k] q[m,k] exactly in int32, and
 // y = ((float)acc * s_tok[m]) * s_w.
 //
-// MI355X design: v_mfma_i32_32x32x32_i8.  Its B operand gives each lane 16
-// consecutive k of one column; one 16-byte load of i2_s codes at byte
-// 32g + 16h of a row holds, in its four shift planes, exactly the 16-k runs
-// 128g + 32t + 16h + [0,16) for t = 0..3.  So lane (column n = lane%32,
-// h = lane/32) feeds four MFMAs (t = 0..3) from one load, in natural k
-// order, and the activations need no reordering.  A plane is decoded to
-// int8 {-1,0,+1} in three ops per four weights: shift, mask to one code per
-// byte, and a byte permute through the table {0xFF, 0x00, 0x01}.
+// MI355X design: v_mfma_i32_32x32x32_i8; lane l holds 16 consecutive k of
+// row (or column) l % 32 at k offset 16 (l / 32) of a 32-k step.  The 32
+// bytes of one 128-k group of an i2_s row hold, in their four 2-bit fields,
+// the k runs 32t + [0, 32) for t = 0..3 (byte j of the group, field t:
+// element 32t + j), so the weights decode in natural k order and the
+// activations need no reordering.
 //
-// Workgroup tile 128 x 128 (four waves of 64 x 64), one 128-k group per
-// step.  The int8 activation tile of a step sits in one of four LDS
-// buffers (rows padded to 144 bytes so the 32 rows of an MFMA operand fall
-// on distinct banks); the activation and code loads of step g + 3 are
-// issued into one of four register stages before step g multiplies (a
-// scheduling barrier keeps them there), every load unconditionally from a
-// clamped address so the compiler can count its waits.  One workgroup
-// barrier per step.
+// Workgroup tile 128 x 128, eight waves of 32 x 64 (two waves per SIMD, so
+// one wave's operand reads and barrier waits overlap the other's
+// multiplies).  Per 128-k group the workgroup stores the int8 activation
+// tile and the weight tile, decoded once to int8 {-1, 0, +1} (shift, mask,
+// byte permute through {0xFF, 0x00, 0x01}), into one of two LDS buffers;
+// rows are padded to 144 bytes so an MFMA operand's 32 rows fall on distinct
+// banks.  Inside a group the operand reads of step t + 1 are issued before
+// the multiplies of step t.  Global loads run three groups ahead in four
+// register stages, every load from a clamped in-bounds address so the
+// compiler can count its waits; one barrier per group.
 //
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its exact
@@ -36,33 +36,24 @@ namespace {
 
 using namespace llk;
 
-constexpr int BM = 128, BN = 128, LDA = 144;
+constexpr int BM = 128, BN = 128, LDA = 144, LDB = 144;
+constexpr int kThreads = 512;                            // eight waves
 constexpr int kTileInts = BM * BN;                       // one partial tile
-constexpr int kStages = 4;                               // LDS buffers / register stages
-constexpr size_t kGemmLds = size_t(kStages) * BM * LDA;
+constexpr int kBuf = BM * LDA + BN * LDB;                // one LDS buffer: activation tile, then weight tile
+constexpr size_t kGemmLds = size_t(2) * kBuf;
 
-__device__ __forceinline__ i32x4 decode_plane_i8(i32x4 u, int t) {
-    const int sh = 6 - 2 * t;
-    i32x4 b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t c = (uint32_t(u[j]) >> sh) & 0x03030303u;
-        b[j] = int(__builtin_amdgcn_perm(0u, 0x000100FFu, c));
-    }
-    return b;
-}
 
-__global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K,
-                                                           const int8_t* __restrict__ xq,
-                                                           const float* __restrict__ xs, int64_t M,
-                                                           const float* __restrict__ bias, float* __restrict__ y,
-                                                           int32_t* __restrict__ acc_out, int S,
-                                                           int32_t* __restrict__ part, int32_t* __restrict__ counters) {
-    extern __shared__ __attribute__((aligned(16))) int8_t As_raw[];
-    int8_t (*As)[BM * LDA] = reinterpret_cast<int8_t (*)[BM * LDA]>(As_raw);   // [kStages][BM * LDA]
+__global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N,
+                                                                int64_t K, const int8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs, int64_t M,
+                                                                const float* __restrict__ bias, float* __restrict__ y,
+                                                                int32_t* __restrict__ acc_out, int S,
+                                                                int32_t* __restrict__ part,
+                                                                int32_t* __restrict__ counters) {
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;               // rows 32 wm, columns 64 wn of the tile
     const int li = lane & 31, h = lane >> 5;
     const int64_t TM = (M + BM - 1) / BM;
     const int64_t tile = int64_t(blockIdx.x) / S;
@@ -72,114 +63,132 @@ __global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restr
     const int64_t ng = K / 128;
     const int64_t g0 = ng * split / S, g1 = ng * (split + 1) / S;
 
-    // B rows of this lane (clamped to the last row; results of clamped rows are not stored)
-    const uint8_t* brow[2];
+    // Loads of one group: two 16-byte activation chunks (row idx / 8, chunk
+    // idx % 8 for idx = tid, tid + 512) and 8 code bytes (column tid / 4,
+    // quarter tid % 4 of the 32-byte group); rows and columns are clamped
+    // (results of clamped ones are not stored).
+    const int8_t* arow[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        int64_t n = n0 + wn * 64 + nb * 32 + li;
-        n = n < N ? n : N - 1;
-        brow[nb] = codes + n * rowbytes + 16 * h;
-    }
-    // A rows of this thread's four 16-byte chunks per step (clamped likewise)
-    const int8_t* arow[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int idx = tid + 256 * c;
+    for (int c = 0; c < 2; ++c) {
+        const int idx = tid + kThreads * c;
         int64_t m = m0 + (idx >> 3);
         m = m < M ? m : M - 1;
         arow[c] = xq + m * K + 16 * (idx & 7);
     }
+    const int bcol = tid >> 2, bq = tid & 3;
+    int64_t ncl = n0 + bcol;
+    ncl = ncl < N ? ncl : N - 1;
+    const uint8_t* bptr = codes + ncl * rowbytes + 8 * bq;
 
     struct Stage {
-        i32x4 a[4];
-        i32x4 b[2];
+        i32x4 a[2];
+        uint32_t b[2];
     };
     auto load = [&](int64_t g, Stage& s) {
-        const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (cached, unused)
+        const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s.b[nb] = ld16_stream(brow[nb] + 32 * gc);
+        for (int c = 0; c < 2; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+        const u32x2 b2 = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc));
+        s.b[0] = b2[0];
+        s.b[1] = b2[1];
     };
-    auto store_a = [&](int buf, const Stage& s) {
+    // Byte j of quarter bq is group byte 8 bq + j; its field t is element
+    // 32 t + 8 bq + j, so each field gives 8 consecutive k of step t.
+    auto store = [&](int buf, const Stage& s) {
+        int8_t* A = lds + buf * kBuf;
+        int8_t* B = A + BM * LDA;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int idx = tid + 256 * c;
-            *reinterpret_cast<i32x4*>(&As[buf][(idx >> 3) * LDA + 16 * (idx & 7)]) = s.a[c];
+        for (int c = 0; c < 2; ++c) {
+            const int idx = tid + kThreads * c;
+            *reinterpret_cast<i32x4*>(&A[(idx >> 3) * LDA + 16 * (idx & 7)]) = s.a[c];
         }
-    };
-
-    i32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
-
-    auto compute = [&](int buf, const Stage& s) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            i32x4 bop[2], aop[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) bop[nb] = decode_plane_i8(s.b[nb], t);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                aop[mb] = *reinterpret_cast<const i32x4*>(&As[buf][(wm * 64 + mb * 32 + li) * LDA + 32 * t + 16 * h]);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[mb], bop[nb], acc[mb][nb], 0, 0, 0);
+            const int sh = 6 - 2 * t;
+            uint2 v;
+            v.x = __builtin_amdgcn_perm(0u, 0x000100FFu, (s.b[0] >> sh) & 0x03030303u);
+            v.y = __builtin_amdgcn_perm(0u, 0x000100FFu, (s.b[1] >> sh) & 0x03030303u);
+            *reinterpret_cast<uint2*>(&B[bcol * LDB + 32 * t + 8 * bq]) = v;
         }
     };
 
-    // Step g multiplies from LDS buffer g%4 and register stage g%4; the loads
-    // of step g + 3 go to stage (g+3)%4 (free since step g - 1) before the
-    // multiply.  The main loop runs whole quadruples of steps with no early
-    // exit (an exit between a load and its use would let the compiler sink
-    // the load past the multiply); the last one to three steps follow it.
+    i32x16 acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][r] = 0;
+
+    auto compute = [&](int buf) {
+        const int8_t* A = lds + buf * kBuf + (wm * 32 + li) * LDA + 16 * h;
+        const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + 16 * h;
+        i32x4 ao[2], bo[2][2];
+        ao[0] = *reinterpret_cast<const i32x4*>(A);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bo[0][nb] = *reinterpret_cast<const i32x4*>(B + nb * 32 * LDB);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 3) {                                   // operands of step t + 1 first
+                ao[nxt] = *reinterpret_cast<const i32x4*>(A + 32 * (t + 1));
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    bo[nxt][nb] = *reinterpret_cast<const i32x4*>(B + nb * 32 * LDB + 32 * (t + 1));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[cur], bo[cur][nb], acc[nb], 0, 0, 0);
+        }
+    };
+
+    // Group g + i is multiplied from LDS buffer i % 2; register stage i % 4
+    // holds group g + i from its load (three groups earlier) to its store
+    // (one group earlier).  The main loop runs whole quadruples of groups with
+    // no early exit; the last one to three groups follow it.
     Stage st0, st1, st2, st3;
     load(g0, st0);
     load(g0 + 1, st1);
     load(g0 + 2, st2);
-    store_a(0, st0);
+    load(g0 + 3, st3);
+    store(0, st0);
     __syncthreads();
     const int64_t nsteps = g1 - g0;
     int64_t g = g0;
     for (; g + 4 <= g1; g += 4) {
-        load(g + 3, st3);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0, st0);
-        store_a(1, st1);
-        __syncthreads();
+        // loads first (kept there by the scheduling barrier); the store of the
+        // next group and the multiplies of this one may interleave
         load(g + 4, st0);
         __builtin_amdgcn_sched_barrier(0);
-        compute(1, st1);
-        store_a(2, st2);
+        store(1, st1);
+        compute(0);
         __syncthreads();
         load(g + 5, st1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(2, st2);
-        store_a(3, st3);
+        store(0, st2);
+        compute(1);
         __syncthreads();
         load(g + 6, st2);
         __builtin_amdgcn_sched_barrier(0);
-        compute(3, st3);
-        store_a(0, st0);
+        store(1, st3);
+        compute(0);
+        __syncthreads();
+        load(g + 7, st3);
+        __builtin_amdgcn_sched_barrier(0);
+        store(0, st0);
+        compute(1);
         __syncthreads();
     }
     const int64_t rem = nsteps % 4;
-    if (rem >= 1) compute(0, st0);
+    if (rem >= 1) compute(0);
     if (rem >= 2) {
-        store_a(1, st1);
+        store(1, st1);
         __syncthreads();
-        compute(1, st1);
+        compute(1);
     }
     if (rem >= 3) {
-        store_a(2, st2);
+        store(0, st2);
         __syncthreads();
-        compute(2, st2);
+        compute(0);
     }
 
     if (S > 1) {
@@ -188,11 +197,9 @@ __global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restr
         // reads the others' partials (device-coherent loads) and finishes the tile.
         int32_t* mine = part + (tile * S + split) * int64_t(kTileInts);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st_coherent(mine + ((mb * 2 + nb) * 16 + r) * 256 + tid, acc[mb][nb][r]);
+            for (int r = 0; r < 16; ++r) st_coherent(mine + (nb * 16 + r) * kThreads + tid, acc[nb][r]);
         wait_vmem();
         __syncthreads();
         if (tid == 0) last_flag = atomicAdd(counters + tile, 1) == S - 1;
@@ -202,11 +209,9 @@ __global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restr
             if (s == split) continue;
             const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mb][nb][r] += ld_coherent(other + ((mb * 2 + nb) * 16 + r) * 256 + tid);
+                for (int r = 0; r < 16; ++r) acc[nb][r] += ld_coherent(other + (nb * 16 + r) * kThreads + tid);
         }
         if (tid == 0) st_coherent(counters + tile, 0);    // ready for the next call
     }
@@ -215,14 +220,12 @@ __global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restr
     // loaded up front from clamped indices (a load under a per-element branch
     // would be waited on one at a time); only the stores are guarded.
     const float sw = *reinterpret_cast<const float*>(codes + N * rowbytes);
-    float xsv[2][16];
+    float xsv[16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            xsv[mb][r] = xs[m < M ? m : M - 1];
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        xsv[r] = xs[m < M ? m : M - 1];
+    }
     float bnv[2] = {0.0f, 0.0f};
     if (bias)
 #pragma unroll
@@ -231,22 +234,20 @@ __global__ void __launch_bounds__(256) gemm_i8_i2s_kernel(const uint8_t* __restr
             bnv[nb] = bias[n < N ? n : N - 1];
         }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t n = n0 + wn * 64 + nb * 32 + li;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int64_t n = n0 + wn * 64 + nb * 32 + li;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int32_t a = acc[mb][nb][r];
-                float v = __fmul_rn(__fmul_rn(float(a), xsv[mb][r]), sw);
-                if (bias) v = __fadd_rn(v, bnv[nb]);
-                if (m < M && n < N) {
-                    y[m * N + n] = v;
-                    if (acc_out) acc_out[m * N + n] = a;
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int32_t a = acc[nb][r];
+            float v = __fmul_rn(__fmul_rn(float(a), xsv[r]), sw);
+            if (bias) v = __fadd_rn(v, bnv[nb]);
+            if (m < M && n < N) {
+                y[m * N + n] = v;
+                if (acc_out) acc_out[m * N + n] = a;
             }
         }
+    }
 }
 
 #ifndef LL_GEMM_SLOTS
@@ -280,7 +281,7 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     int32_t* part = static_cast<int32_t*>(ws);
     int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
-    const dim3 grid{unsigned(tiles * S)}, block{256};
+    const dim3 grid{unsigned(tiles * S)}, block{unsigned(kThreads)};
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_i2s_kernel), kGemmLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_i8_i2s_kernel, grid, block, kGemmLds, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
