@@ -320,6 +320,47 @@ def test_gemv_plan_one_token_edges(fmt):
         assert ok, "case %d (N=%d K=%d): worst error / bound %.3f" % (i, N, K, worst)
 
 
+@pytest.mark.parametrize("fmt,M", [("i2s", 1), ("tq2", 1), ("i2s", 3)])
+def test_gemv_plan_graph_replay(fmt, M):
+    """A prepared batch captured in a HIP graph (its two launches): several
+    replays, with eager work (new activations, an eager run of the same plan)
+    between them, each equal bit for bit to the eager result on the same
+    inputs."""
+    t = torch()
+    shapes = [(2560, 2560, 0), (6912, 2560, 0), (2560, 6912, 1)]
+    items, xs_d = [], {}
+    for i, (N, K, slot) in enumerate(shapes):
+        if fmt == "i2s":
+            _, _, packed = make_i2s(7700 + i, N, K)
+            W = L.upload_i2s(packed, N, K)
+        else:
+            _, _, packed = make_tq2(7700 + i, N, K)
+            W = L.upload_tq2(packed, N, K)
+        if slot not in xs_d:
+            xs_d[slot] = t.from_numpy(_x(7800 + slot, M, K)).cuda()
+        items.append((W, xs_d[slot], None, t.empty((M, N), dtype=t.float32, device="cuda")))
+    plan = L.GemvPlan(items, M)
+    announce("plan graph replay", fmt, M)
+    plan.run()
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        plan.prepare(None)
+        plan.product(None)
+    for rnd in range(3):
+        for slot, xd in xs_d.items():
+            xd.copy_(t.from_numpy(_x(7900 + 10 * rnd + slot, M, xd.shape[1])))
+        plan.run()                                     # eager result on these inputs
+        t.cuda.synchronize()
+        eager = [y.clone() for (_, _, _, y) in items]
+        for (_, _, _, y) in items:
+            y.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        for (_, _, _, y), ye in zip(items, eager):
+            assert t.equal(y.view(t.int32), ye.view(t.int32)), rnd
+
+
 @pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 2), ("tq2", 1), ("tq2", 3), ("i2s", 6)])
 def test_gemv_f32_zero_token(fmt, M):
     """An all-zero token gives exactly the bias (no exponent, no planes); the
