@@ -104,6 +104,60 @@ struct F4Prob {
     int64_t wg0;                  // first (logical) workgroup of this product
 };
 
+// ---------------------------------------------------------------- digits
+struct TokScale {
+    int E;                        // max|x| < 2^E
+    float f1, f2;                 // x * f1 * f2 = x * 2^(34 - E), both factors exact powers of two
+};
+
+// max |x| over a token row, by the 256 threads of a workgroup (barrier inside).
+__device__ __forceinline__ TokScale token_scale(const float* x, int64_t K, int tid, float* smax) {
+    float mx = 0.0f;
+    for (int64_t i = tid; i < K / 4; i += 256) {
+        const f32x4 u = ld16f(x + 4 * i);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
+    }
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) smax[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    TokScale ts;
+    ts.E = 0;
+    (void)frexpf(mx, &ts.E);                               // E = 0 when mx == 0
+    const int sh = 34 - ts.E;                              // in [-94, 183]
+    const int sa = sh < 120 ? sh : 120;
+    ts.f1 = ldexpf(1.0f, sa);
+    ts.f2 = ldexpf(1.0f, sh - sa);
+    return ts;
+}
+
+// Digits of NE elements: nibble e of out[r] = e2m1 code of digit r of element
+// e (element e at bits 4e); xsum += their X.
+template <int NE>
+__device__ __forceinline__ void make_digits(const float (&v)[NE], const TokScale& ts, uint32_t (&out)[kPl],
+                                            long long& xsum) {
+#pragma unroll
+    for (int r = 0; r < kPl; ++r) out[r] = 0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const float t = rintf((v[e] * ts.f1) * ts.f2);     // X, an integer-valued float, |X| < 2^34
+        const float th = floorf(t * 0x1p-18f);             // X = th 2^18 + tl, 0 <= tl < 2^18 (both exact)
+        const float tl = fmaf(th, -0x1p18f, t);
+        const int hi = int(th), lo = int(tl);
+        xsum += (long long)hi * (1 << 18) + lo;
+        const uint32_t l2 = uint32_t(lo) + kBiasLo;        // X + bias = H 2^18 + L
+        const uint32_t L = l2 & 0x3FFFFu;
+        const uint32_t H = uint32_t(hi + int(kBiasHi) + int(l2 >> 18));
+#pragma unroll
+        for (int r = 0; r < kPl; ++r) {
+            const uint32_t src = r < 6 ? H : L;
+            const int o = 3 * (5 - (r % 6));
+            const uint32_t d = (src >> o) & 7u;
+            out[r] |= ((kDigitNibbles >> (4 * d)) & 15u) << (4 * e);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- preparation
 // Workgroup (token, slice): digits of chunks [8 slice, 8 slice + 8).  Thread
 // t: chunk 8 slice + t/32, step s = (t/16) % 2, lane quarter q = (t/4) % 4,
@@ -154,43 +208,11 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
 
     // max |x| over the token (this thread's elements were requested above, so
     // both loads are in flight together)
-    float mx = 0.0f;
-    for (int64_t i = tid; i < K / 4; i += 256) {
-        const f32x4 u = ld16f(x + 4 * i);
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
-    }
-    mx = wave_max(mx);
-    if (lane == 0) smax[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-    int E = 0;
-    (void)frexpf(mx, &E);                                  // mx < 2^E; E = 0 when mx == 0
-    const int sh = 34 - E;                                 // in [-94, 183]: two exact power-of-two factors
-    const int sa = sh < 120 ? sh : 120;
-    const float f1 = ldexpf(1.0f, sa), f2 = ldexpf(1.0f, sh - sa);
-
+    const TokScale ts = token_scale(x, K, tid, smax);
+    const int E = ts.E;
     uint32_t out[kPl];
-#pragma unroll
-    for (int r = 0; r < kPl; ++r) out[r] = 0;
     long long xsum = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float t = rintf((v[e] * f1) * f2);           // X, an integer-valued float, |X| < 2^34
-        const float th = floorf(t * 0x1p-18f);             // X = th 2^18 + tl, 0 <= tl < 2^18 (both exact)
-        const float tl = fmaf(th, -0x1p18f, t);
-        const int hi = int(th), lo = int(tl);
-        xsum += (long long)hi * (1 << 18) + lo;
-        const uint32_t l2 = uint32_t(lo) + kBiasLo;        // X + bias = H 2^18 + L
-        const uint32_t L = l2 & 0x3FFFFu;
-        const uint32_t H = uint32_t(hi + int(kBiasHi) + int(l2 >> 18));
-#pragma unroll
-        for (int r = 0; r < kPl; ++r) {
-            const uint32_t src = r < 6 ? H : L;
-            const int o = 3 * (5 - (r % 6));
-            const uint32_t d = (src >> o) & 7u;
-            out[r] |= ((kDigitNibbles >> (4 * d)) & 15u) << (4 * e);
-        }
-    }
+    make_digits<8>(v, ts, out, xsum);
     if (live) {
         uint8_t* dst = ops + c * kChunkBytes + s * kStepBytes + q * kQuarterBytes + 4 * j;
 #pragma unroll
