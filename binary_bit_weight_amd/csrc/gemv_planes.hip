@@ -630,9 +630,15 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_kernel(const uint8_t*
     planes_rows<FMT, M, kWindowed>(codes, scales, N, K, ws, pv, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
-// Mt > 3 tokens: passes of up to three tokens run as the second grid
-// dimension, side by side (each streams the weights; the passes of one row
-// tile read the same bytes at about the same time).
+// Mt > 3 tokens: passes of up to three tokens.  The passes of one row tile
+// are consecutive logical workgroups, and logical runs are mapped onto one
+// XCD (hardware workgroup w runs on XCD w % 8 and takes logical index
+// (w % 8) * ceil(T / 8) + w / 8), so the passes of a tile run together and
+// read its weights through one L2.
+__device__ __forceinline__ int64_t xcd_logical(int64_t w, int64_t T) {
+    const int64_t T8 = (T + 7) / 8;
+    return (w % 8) * T8 + w / 8;
+}
 template <int FMT>
 __device__ __forceinline__ void planes_pass(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int64_t N, int64_t K, const void* __restrict__ ws, int Mt, int pass,
@@ -654,7 +660,10 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_multi_kernel(const ui
                                                                          const float* __restrict__ bias,
                                                                          float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    planes_pass<FMT>(codes, scales, N, K, ws, Mt, int(blockIdx.y), bias, y, int64_t(blockIdx.x) * kRows, lds);
+    const int64_t np = npass(Mt), T = (N + kRows - 1) / kRows * np;
+    const int64_t L = xcd_logical(blockIdx.x, T);
+    if (L >= T) return;                                    // whole workgroup
+    planes_pass<FMT>(codes, scales, N, K, ws, Mt, int(L % np), bias, y, (L / np) * kRows, lds);
 }
 
 template <int FMT>
@@ -698,11 +707,14 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_kernel(const Pl
 template <int FMT>
 __global__ void __launch_bounds__(64 * kWaves) gemv_planes_batch_multi_kernel(const PlanesProb* __restrict__ tab,
                                                                                const int32_t* __restrict__ map,
-                                                                               int Mt) {
+                                                                               int Mt, int64_t wgs) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int64_t wg = blockIdx.x;
+    const int64_t np = npass(Mt), T = wgs * np;
+    const int64_t L = xcd_logical(blockIdx.x, T);
+    if (L >= T) return;                                    // whole workgroup
+    const int64_t wg = L / np;
     const PlanesProb& P = tab[ld32(map + wg)];
-    planes_pass<FMT>(P.codes, P.scales, P.N, P.K, P.ws, Mt, int(blockIdx.y), P.bias, P.y, (wg - P.wg0) * kRows, lds);
+    planes_pass<FMT>(P.codes, P.scales, P.N, P.K, P.ws, Mt, int(L % np), P.bias, P.y, (wg - P.wg0) * kRows, lds);
 }
 
 template <int FMT>
@@ -743,7 +755,8 @@ hipError_t launch_fused_single(const uint8_t* c, const uint16_t* s, int64_t N, i
 template <int FMT>
 hipError_t launch_multi(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, void* ws, int Mt,
                         const float* bias, float* y, hipStream_t stream) {
-    const dim3 grid{unsigned((N + kRows - 1) / kRows), unsigned(npass(Mt))}, block{64 * kWaves};
+    const int64_t T = (N + kRows - 1) / kRows * npass(Mt);
+    const dim3 grid{unsigned((T + 7) / 8 * 8)}, block{64 * kWaves};
     const size_t lds = size_t(lds_bytes(kPassM));
     hipError_t e = allow_lds(gemv_planes_multi_kernel<FMT>, lds);
     if (e != hipSuccess) return e;
@@ -753,11 +766,12 @@ hipError_t launch_multi(const uint8_t* c, const uint16_t* s, int64_t N, int64_t 
 
 template <int FMT>
 hipError_t launch_batch_multi(const PlanesProb* tab, const int32_t* map, int64_t wgs, int Mt, hipStream_t stream) {
-    const dim3 grid{unsigned(wgs), unsigned(npass(Mt))}, block{64 * kWaves};
+    const int64_t T = wgs * npass(Mt);
+    const dim3 grid{unsigned((T + 7) / 8 * 8)}, block{64 * kWaves};
     const size_t lds = size_t(lds_bytes(kPassM));
     hipError_t e = allow_lds(gemv_planes_batch_multi_kernel<FMT>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemv_planes_batch_multi_kernel<FMT>), grid, block, lds, stream, tab, map, Mt);
+    hipLaunchKernelGGL((gemv_planes_batch_multi_kernel<FMT>), grid, block, lds, stream, tab, map, Mt, wgs);
     return hipGetLastError();
 }
 
