@@ -55,8 +55,18 @@ __host__ __device__ inline int w1_stride(int G) {
 
 // Rows of the A operand: (token m, group slot j, digit h) -> 2 (m S + j) + h,
 // S = 128 / G slots per 128-k chunk (1 for G >= 128).
-__host__ __device__ inline int w1_slots(int G) { return G >= 128 ? 1 : 128 / G; }
+__host__ __device__ constexpr int w1_slots(int G) { return G >= 128 ? 1 : 128 / G; }
 __host__ __device__ inline int w1_arows(int M, int G) { return 2 * M * w1_slots(G); }
+// Units (a group of G >= 128, else a 128-k chunk) packed into one MFMA
+// accumulator: the largest power of two with PK R <= 16, at most the units of
+// a 1024-k window.
+inline int w1_pack(int M, int G) {
+    const int R = w1_arows(M, G);
+    const int units = G >= 128 ? 8 / (G / 128) : 8;
+    int pk = 1;
+    while (pk * 2 * R <= 16 && pk * 2 <= units) pk *= 2;
+    return pk;
+}
 
 // Workspace of one activation: A [K/128 chunks][R rows][128 B] | qs [M][K/G] int32.
 __host__ __device__ inline size_t w1_a_bytes(int64_t M, int64_t K, int G) {
@@ -156,14 +166,15 @@ __device__ void w1_qsum(const int8_t* __restrict__ xq, int64_t M, int64_t K, int
 
 // ---------------------------------------------------------------- product
 // G: group size; MT: A row blocks of 16 (R = 2 M S <= 16 MT rows); NP: pairs
-// (token, slot) per lane and row block that can be live (1 when R <= 2, else 2).
+// (token, slot) per lane and row block that can be live (1 when R <= 2, else
+// 2); PK: units packed into one accumulator (MT = 1, NP = 2 when PK > 1).
 // Split K.  With few row blocks (a narrow matrix) the workgroups of a row
 // block split its windows nsplit ways; each writes its partial sums S (exact
 // in fp64, so their sum is too, in any order) to part and counts itself in;
 // the last to arrive adds the partials and writes y, then resets the counter
 // (counters start zero and every call leaves them zero).
-template <int G, int MT, int NP>
-__global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* __restrict__ bits,
+template <int G, int MT, int NP, int PK>
+__global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per_eu(G >= 128 && PK * (G / 128) == 8 ? 3 : 1))) w1_gemv_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
                                                                  const float* __restrict__ xs,
@@ -207,7 +218,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
     constexpr int nsc = kScMax;
     // A window loads: R rows x 8 chunks x 128 B = 64 R pieces of 16 B; qs: M x ngw ints
     const int apieces = 64 * R;
-    constexpr int kAMax = NP == 1 ? 1 : (16 * MT * 64 + 255) / 256;
+    constexpr int kAMax = NP == 1 ? 1 : (16 * MT * 64 / PK + 255) / 256;   // R <= 16 MT / PK
     struct Regs {
         i32x4 w[4];
         uint16_t sc[kScMax];
@@ -299,37 +310,49 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
             for (int t = 0; t < NP; ++t) sacc[cb][b][t] = 0.0;
         }
 
-    constexpr int cpg = G >= 128 ? G / 128 : 1;            // chunks per group
+    constexpr int cpg = G >= 128 ? G / 128 : 1;            // chunks per unit (a group, or one chunk of S groups)
+    // Packing: the PK units of a set put their R rows at row offsets R s of
+    // one accumulator, so one epilogue serves PK units.  Lane row nl carries
+    // slot sl = nl / R, row rl = nl % R (no slot if nl >= PK R).
+    constexpr int kSet = cpg * PK;                          // chunks per set (divides the window's 8)
+    const int sl = PK == 1 ? 0 : (nl < PK * R ? nl / R : PK), rl = PK == 1 ? nl : nl % R;
+    const int64_t nchunk = K / 128;
     auto compute = [&](int w) {
         const char* ab = abase + (w & 1) * abytes;
         const int32_t* qsl = reinterpret_cast<const int32_t*>(ab + kChunks * R * 128 + 128);
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int64_t cg = int64_t(w) * kChunks + c;   // global chunk
-            if (cg >= K / 128) break;
+            if (cg >= nchunk) break;
             // A operands (32 bytes per lane and row block)
             i32x8 av[MT];
 #pragma unroll
             for (int b = 0; b < MT; ++b) {
-                const int r = 16 * b + nl;
-                const char* ap = r < R ? ab + (c * R + r) * 128 + 32 * q : ab + kChunks * R * 128;   // zero row
+                const char* ap;
+                if (PK == 1) {
+                    const int r = 16 * b + nl;
+                    ap = r < R ? ab + (c * R + r) * 128 + 32 * q : ab + kChunks * R * 128;   // zero row
+                } else {
+                    ap = sl == (c / cpg) % PK ? ab + (c * R + rl) * 128 + 32 * q : ab + kChunks * R * 128;
+                }
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
                 const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
                 av[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+            const bool first = (c % kSet) == 0;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const uint32_t word = *reinterpret_cast<const uint32_t*>(wtile + (16 * cb + nl) * stride + 16 * c + 4 * q);
                 const i32x8 bv{int(word & 0x11111111u), int((word >> 1) & 0x11111111u), int((word >> 2) & 0x11111111u),
                                int((word >> 3) & 0x11111111u), 0, 0, 0, 0};
-                const bool first = (cg % cpg) == 0;
 #pragma unroll
                 for (int b = 0; b < MT; ++b)
                     acc[cb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         av[b], bv, first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[cb][b], 0, 4, 0, 127, 0, 127);
             }
-            if ((cg % cpg) == cpg - 1) {
-                // epilogue of the group(s) ending with this chunk
+            if ((c % kSet) == kSet - 1 || cg + 1 == nchunk) {
+                // epilogue of the set ending with this chunk
+                const int u0 = (c / kSet) * PK;               // first unit of the set within the window
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
                     const char* srow = wtile + (16 * cb + nl) * stride + kWinB1;
@@ -337,15 +360,19 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
                     for (int b = 0; b < MT; ++b) {
 #pragma unroll
                         for (int t = 0; t < NP; ++t) {
-                            const int p = 8 * b + 2 * q + t;          // (token, slot) pair
+                            const int pp = 8 * b + 2 * q + t;         // pair of rows: slot s, (token, group slot) p
+                            const int s = PK == 1 ? 0 : pp / (M * S);
+                            const int p = PK == 1 ? pp : pp % (M * S);
                             const int m = p / S, j = p % S;
-                            const int64_t g = G >= 128 ? cg / cpg : cg * S + j;
-                            const int gi = int(g - int64_t(w) * ngw);  // group within the window
+                            const int gi = G >= 128 ? u0 + s : (u0 + s) * S + j;   // group within the window
+                            const bool ok = PK == 1 || (s < PK && int64_t(w) * ngw + gi < ng);
                             const float v = __builtin_fmaf(16.0f, acc[cb][b][2 * t], acc[cb][b][2 * t + 1]);
-                            const int qsv = qsl[(m < M ? m : 0) * ngw + gi];
+                            const int gic = ok ? gi : 0;
+                            const int qsv = qsl[(m < M ? m : 0) * ngw + gic];
                             const int d = int(4.0f * v) - qsv;
-                            const double s = double(half_bits_to_float(*reinterpret_cast<const uint16_t*>(srow + 2 * gi)));
-                            sacc[cb][b][t] = __builtin_fma(s, double(d), sacc[cb][b][t]);
+                            const double sc = double(half_bits_to_float(*reinterpret_cast<const uint16_t*>(srow + 2 * gic)));
+                            const double nv = __builtin_fma(sc, double(d), sacc[cb][b][t]);
+                            sacc[cb][b][t] = ok ? nv : sacc[cb][b][t];
                         }
                     }
                 }
@@ -381,10 +408,11 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
     }
     if (w < nwin) compute(w);                              // odd window count: the last one is in LDS
 
-    // y[m][n] = (float)((double)xs[m] * S[m][n]) (+ bias).  Pair p = m S + j
-    // of row block b lives in lane quarter (p % 8) / 2, slot t = p % 2; the S
-    // slots of one token (G < 128) are added through LDS (every partial sum
-    // is exact, so the order of groups does not matter).
+    // y[m][n] = (float)((double)xs[m] * S[m][n]) (+ bias).  Pair
+    // p = (k M + m) S + j (pack slot k) of row block b lives in lane quarter
+    // (p % 8) / 2, slot t = p % 2; the pack slots and group slots of one token
+    // are added through LDS (every partial sum is exact, so the order of
+    // groups does not matter).
     __syncthreads();
     double* red = reinterpret_cast<double*>(lds);      // [2 cb][16 col][pairs up to 8 MT]
     const int npairs = 8 * MT;
@@ -403,7 +431,8 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
         const int col = e / M;                             // wave * 32 + cb * 16 + nl
         const int64_t n = rb * kW1Rows + col;
         double s = 0.0;
-        for (int j = 0; j < S; ++j) s += red[col * npairs + m * S + j];
+        for (int k = 0; k < PK; ++k)
+            for (int j = 0; j < S; ++j) s += red[col * npairs + (k * M + m) * S + j];
         if (nsplit > 1) {
             st_coherent64(part + (int64_t(blockIdx.x) * kW1Rows + col) * M + m, s);
         } else if (n < N) {
@@ -441,7 +470,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) w1_gemv_kernel(const uint32_t* 
     if (tid == 0) st_coherent(counters + rb, 0);          // ready for the next call
 }
 
-template <int G, int MT, int NP>
+template <int G, int MT, int NP, int PK>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                      const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
                      hipStream_t stream) {
@@ -449,9 +478,9 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     size_t lds = size_t(w1_lds_bytes(M, G));
     const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
     lds = lds > red ? lds : red;
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP>), lds);
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP, PK>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y,
+    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP, PK>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y,
                        nsplit, part, counters);
     return hipGetLastError();
 }
@@ -460,10 +489,17 @@ template <int G>
 hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                        const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
                        hipStream_t stream) {
-    const int R = w1_arows(M, G);
-    if (R <= 2) return launch_w1<G, 1, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-    if (R <= 16) return launch_w1<G, 1, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-    return launch_w1<G, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    constexpr int kUnits = G >= 128 ? kChunks / (G / 128) : kChunks;   // units per window
+    constexpr int kMaxPk = G >= 128 ? kUnits : 8 / w1_slots(G);          // R >= 2 S
+    constexpr int P8 = kMaxPk < 8 ? kMaxPk : 8, P4 = kMaxPk < 4 ? kMaxPk : 4;
+    switch (w1_pack(M, G)) {
+    case 8: return launch_w1<G, 1, 2, P8>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    case 4: return launch_w1<G, 1, 2, P4>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    case 2: return launch_w1<G, 1, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    default: break;
+    }
+    if (w1_arows(M, G) <= 16) return launch_w1<G, 1, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    return launch_w1<G, 2, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
 }
 
 // Tokens per pass: the A rows of a pass (2 x tokens x slots) fit two row blocks.

@@ -36,10 +36,13 @@ def _run(bits, scales, K, G, q, s, bias=None, rows=None, use_gemm=False):
 
 
 # (N, K, G, M): ragged row counts (the workgroup covers 128 rows), every group
-# size, token counts that need one or two A row blocks and several passes
+# size, token counts that need one or two A row blocks and several passes, and
+# every number of units packed into one accumulator (8, 4, 2) with the last
+# packed set of the matrix cut short by the end of K
 W1_SMALL = [(37, 128, 128, 1), (64, 256, 32, 3), (100, 512, 64, 8), (130, 1024, 128, 16), (7, 384, 128, 2),
             (33, 2048, 256, 5), (250, 1152, 32, 4), (16, 5120, 128, 8), (129, 640, 64, 1), (40, 256, 256, 1),
-            (300, 1280, 64, 9), (90, 2304, 32, 11)]
+            (300, 1280, 64, 9), (90, 2304, 32, 11), (50, 1152, 128, 4), (77, 1536, 128, 3), (45, 640, 32, 1),
+            (61, 896, 64, 2), (23, 768, 256, 2), (140, 2944, 128, 1)]
 
 
 @pytest.mark.parametrize("N,K,G,M", W1_SMALL)
