@@ -12,18 +12,20 @@
 // element 32t + j), so the weights decode in natural k order and the
 // activations need no reordering.
 //
-// Workgroup tile 128 x 128, four waves of 64 x 64 (one per SIMD; each wave
-// keeps four 32 x 32 accumulators, so every operand read from LDS feeds two
-// multiplies).  Per 128-k group the workgroup stores the int8 activation
-// tile (rows padded to 144 bytes) and the weight codes still packed (32
-// bytes per column, padded to 48) into one of two LDS buffers.  A lane reads
-// its column's 16 code bytes once per group and decodes the four 32-k steps
-// in registers (shift, mask, byte permute through {0xFF, 0x00, 0x01}); the
-// activation operands of step t + 1 are read before the multiplies of step
-// t.  Both paddings put the 8 lanes of one LDS access on distinct banks.
-// Global loads run three groups ahead in four register stages, every load
-// from a clamped in-bounds address so the compiler can count its waits; one
-// barrier per group.
+// Workgroup tile 128 x 128 as four 64 x 64 wave tiles, each owned by two
+// waves (eight waves, two per SIMD): one multiplies the 32-k steps 0 and 1
+// of every 128-k group, the other steps 2 and 3, and the pair adds its
+// halves through LDS at the end.  A wave keeps four 32 x 32 accumulators,
+// so every operand read from LDS feeds two multiplies, and while one wave of
+// a SIMD waits (LDS, barrier) the other multiplies.  Per group the workgroup
+// stores the int8 activation tile (rows padded to 144 bytes) and the weight
+// codes still packed (32 bytes per column, padded to 48) into one of two LDS
+// buffers.  A lane reads its column's 16 code bytes once per group and
+// decodes its two steps in registers (shift, mask, byte permute through
+// {0xFF, 0x00, 0x01}).  Both paddings put the 8 lanes of one LDS access on
+// distinct banks.  Global loads run D - 1 groups ahead in D register
+// stages, every load from a clamped in-bounds address so the compiler can
+// count its waits; one barrier per group.
 //
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its exact
@@ -38,11 +40,14 @@ namespace {
 
 using namespace llk;
 
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
 constexpr int BM = 128, BN = 128, LDA = 144, LDB = 48;
-constexpr int kThreads = 256;                            // four waves
+constexpr int kThreads = 512;                            // eight waves
 constexpr int kTileInts = BM * BN;                       // one partial tile
 constexpr int kBuf = BM * LDA + BN * LDB;                // one LDS buffer: activation tile, then packed codes
-constexpr size_t kGemmLds = size_t(2) * kBuf;
+constexpr int kXchg = kTileInts * 4;                     // final exchange of half accumulators (bytes)
+constexpr size_t kGemmLds = size_t(2) * kBuf > size_t(kXchg) ? size_t(2) * kBuf : size_t(kXchg);
 #ifndef LL_GEMM_XCD
 #define LL_GEMM_XCD 1                                    // XCD-grouped workgroup order
 #endif
@@ -60,8 +65,10 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
                                                                 int32_t* __restrict__ counters) {
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;               // rows 64 wm, columns 64 wn of the tile
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int kh = __builtin_amdgcn_readfirstlane(tid >> 8);   // k half: steps 2 kh, 2 kh + 1
+    const int wq = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+    const int wm = wq >> 1, wn = wq & 1;                   // rows 64 wm, columns 64 wn of the tile
     const int li = lane & 31, h = lane >> 5;
     const int64_t TM = (M + BM - 1) / BM;
     // Hardware workgroup w runs on XCD w % 8; it takes logical index
@@ -78,53 +85,43 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     const int64_t ng = K / 128;
     const int64_t g0 = ng * split / S, g1 = ng * (split + 1) / S;
 
-    // Loads of one group: four 16-byte activation chunks (row idx / 8, chunk
-    // idx % 8 for idx = tid + 256 c) and 16 code bytes (column tid / 2, half
-    // tid % 2 of the 32-byte group); rows and columns are clamped (results of
-    // clamped ones are not stored).
-    const int8_t* arow[4];
+    // Loads of one group: two 16-byte activation chunks (row idx / 8, chunk
+    // idx % 8 for idx = tid + 512 c) and 8 code bytes (column tid / 4,
+    // quarter tid % 4 of the 32-byte group); rows and columns are clamped
+    // (results of clamped ones are not stored).
+    const int8_t* arow[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
         const int idx = tid + kThreads * c;
         int64_t m = m0 + (idx >> 3);
         m = m < M ? m : M - 1;
         arow[c] = xq + m * K + 16 * (idx & 7);
     }
-    const int bcol = tid >> 1, bh = tid & 1;
+    const int bcol = tid >> 2, bqt = tid & 3;
     int64_t ncl = n0 + bcol;
     ncl = ncl < N ? ncl : N - 1;
-    const uint8_t* bptr = codes + ncl * rowbytes + 16 * bh;
+    const uint8_t* bptr = codes + ncl * rowbytes + 8 * bqt;
 
     struct Stage {
-        i32x4 a[4];
-        i32x4 b;
+        i32x4 a[2];
+        u32x2 b;
     };
     auto load = [&](int64_t g, Stage& s) {
         const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
-        s.b = ld16(bptr + 32 * gc);
+        for (int c = 0; c < 2; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
+        s.b = *(const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc);
     };
     auto store = [&](int buf, const Stage& s) {
         int8_t* A = lds + buf * kBuf;
         int8_t* B = A + BM * LDA;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
             const int idx = tid + kThreads * c;
             *reinterpret_cast<i32x4*>(&A[(idx >> 3) * LDA + 16 * (idx & 7)]) = s.a[c];
         }
-        *reinterpret_cast<i32x4*>(&B[bcol * LDB + 16 * bh]) = s.b;
+        *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
     };
-
-    // token scales of this lane's rows, requested before the main loop
-    float xsv[2][16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            xsv[mb][r] = xs[m < M ? m : M - 1];
-        }
 
     i32x16 acc[2][2];
 #pragma unroll
@@ -135,7 +132,7 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
             for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0;
 
     auto compute = [&](int buf) {
-        const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 16 * h;
+        const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 16 * h + 64 * kh;
         const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + 16 * h;
         // code byte j of this lane's 16 holds, in field t (bits 6 - 2t), the
         // weight of k = 32 t + 16 h + j: the B operand of step t
@@ -143,15 +140,13 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) bq[nb] = *reinterpret_cast<const i32x4*>(B + nb * 32 * LDB);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) ao[0][mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA);
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int cur = t & 1, nxt = cur ^ 1;
-            if (t < 3)                                     // operands of step t + 1 first
+            for (int mb = 0; mb < 2; ++mb)
+                ao[tt][mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA + 32 * tt);
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    ao[nxt][mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA + 32 * (t + 1));
-            const int sh = 6 - 2 * t;
+        for (int tt = 0; tt < 2; ++tt) {
+            const int sh = 6 - 4 * kh - 2 * tt;
             i32x4 bo[2];
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
@@ -162,7 +157,7 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[cur][mb], bo[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[tt][mb], bo[nb], acc[mb][nb], 0, 0, 0);
         }
     };
 
@@ -203,18 +198,52 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
         }
     }
 
+    // The two k halves of each wave tile meet: the wave of half kh keeps row
+    // block mb = kh and hands the other to its partner through LDS.
+    // token scales of this lane's rows (row half kh after the exchange),
+    // requested before the exchange so their latency overlaps it
+    float xsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + kh * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        xsv[r] = xs[m < M ? m : M - 1];
+    }
+    __syncthreads();                                       // every wave is done with the operand buffers
+    int32_t* xb = reinterpret_cast<int32_t*>(lds);
+    i32x16 fin[2];
+    if (kh == 0) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            fin[nb] = acc[0][nb];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[1][nb][r];
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            fin[nb] = acc[1][nb];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[0][nb][r];
+        }
+    }
+    __syncthreads();
+    {
+        const int32_t* pb = xb + ((1 - kh) * 4 + wq) * 32 * 64;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) fin[nb][r] += pb[(nb * 16 + r) * 64 + lane];
+    }
+
     if (S > 1) {
         // Publish this split's partial tile with device-coherent stores, wait for
         // them to complete, then count the split in; the split that arrives last
         // reads the others' partials (device-coherent loads) and finishes the tile.
         int32_t* mine = part + (tile * S + split) * int64_t(kTileInts);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    st_coherent(mine + ((mb * 2 + nb) * 16 + r) * kThreads + tid, acc[mb][nb][r]);
+            for (int r = 0; r < 16; ++r) st_coherent(mine + (nb * 16 + r) * kThreads + tid, fin[nb][r]);
         wait_vmem();
         __syncthreads();
         if (tid == 0) last_flag = atomicAdd(counters + tile, 1) == S - 1;
@@ -224,21 +253,18 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
             if (s == split) continue;
             const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[mb][nb][r] += ld_coherent(other + ((mb * 2 + nb) * 16 + r) * kThreads + tid);
+                for (int r = 0; r < 16; ++r) fin[nb][r] += ld_coherent(other + (nb * 16 + r) * kThreads + tid);
         }
         if (tid == 0) st_coherent(counters + tile, 0);    // ready for the next call
     }
 
-    // Epilogue: y = ((float)acc * s_tok) * s_w (+ bias).  Lane (li, h) holds
-    // column wn 64 + nb 32 + li and rows wm 64 + mb 32 + 8 (r / 4) + 4 h + r % 4;
-    // its output pointer is formed once, each store adds a uniform row offset.
-    // The stores of a full tile run as one straight block (a branch between
-    // stores would make each wait for the one before).
+    // Epilogue: y = ((float)acc * s_tok) * s_w (+ bias).  Lane (li, h) of half
+    // kh holds column wn 64 + nb 32 + li and rows wm 64 + kh 32 + 8 (r / 4) +
+    // 4 h + r % 4; its output pointer is formed once, each store adds a
+    // uniform row offset.  The stores of a full tile run as one straight block
+    // (a branch between stores would make each wait for the one before).
     const float sw = *reinterpret_cast<const float*>(codes + N * rowbytes);
     const float* bsrc = bias ? bias : xs;                 // always a valid address
     float bnv[2];
@@ -247,48 +273,39 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
         const int64_t n = n0 + wn * 64 + nb * 32 + li;
         bnv[nb] = bsrc[bias ? (n < N ? n : N - 1) : 0];
     }
-    float out[2][2][16];
+    float out[2][16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float v = __fmul_rn(__fmul_rn(float(fin[nb][r]), xsv[r]), sw);
+            out[nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
+        }
+    const int64_t lrow = m0 + wm * 64 + kh * 32 + 4 * h, lcol = n0 + wn * 64 + li;
+    float* yl = y + lrow * N + lcol;
+    if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yl[int64_t(8 * (r >> 2) + (r & 3)) * N + nb * 32] = out[nb][r];
+    } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float v = __fmul_rn(__fmul_rn(float(acc[mb][nb][r]), xsv[mb][r]), sw);
-                out[mb][nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
+                const int ml = 8 * (r >> 2) + (r & 3);
+                if (lrow + ml < M && lcol + nb * 32 < N) yl[int64_t(ml) * N + nb * 32] = out[nb][r];
             }
-    const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * 64 + li;
-    float* yl = y + lrow * N + lcol;
-    if (m0 + BM <= M && n0 + BN <= N) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    yl[int64_t(mb * 32 + 8 * (r >> 2) + (r & 3)) * N + nb * 32] = out[mb][nb][r];
-    } else {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
-                    if (lrow + ml < M && lcol + nb * 32 < N) yl[int64_t(ml) * N + nb * 32] = out[mb][nb][r];
-                }
     }
     if (acc_out) {
         int32_t* al = acc_out + lrow * N + lcol;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
-                    if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = acc[mb][nb][r];
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int ml = 8 * (r >> 2) + (r & 3);
+                if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = fin[nb][r];
+            }
     }
 }
 
