@@ -18,7 +18,14 @@ layer's seven products, repeated), and extras: single-call per-matrix GEMV
 times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM (TOPS against the
 int8 matrix-core peak).
 
+The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
+reported as "roofline_gemm": the GEMM kernel timed the same way (back-to-back
+launches between HIP events), int8 TOPS against the dense int8 peak, with its
+HBM traffic and matrix-core busy fraction from its own committed counter
+summary when that matches the current source.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+       python bench.py --gemm-only      (the GEMM roofline alone)
        python bench.py --copy-probe     (a plain 256 MiB device copy, to
                                          calibrate rocprofv3 byte counters)
 """
@@ -42,6 +49,11 @@ HIDDEN, FFN = 2560, 6912
 KERNEL = "f4_batch_kernel<1>"
 KERNEL_SOURCES = ["binary_bit_weight_amd/csrc/gemv_fp4.hip", "binary_bit_weight_amd/csrc/common.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "f4_batch_i2s_m1_decode30_counters.md")
+# the other half of the metric: the i2_s int8 prefill GEMM at M = 512
+GEMM_KERNEL = "gemm_i8_i2s_kernel"
+GEMM_SOURCES = ["binary_bit_weight_amd/csrc/gemm_i8.hip", "binary_bit_weight_amd/csrc/common.h"]
+GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_i8_i2s_m512_counters.md")
+GEMM_SHAPES = [(6912, 2560), (2560, 6912)]    # (N, K) at M = 512; the first is the roofline line
 COPY_PROBE_BYTES = 256 << 20
 ROLES = [("q", HIDDEN, HIDDEN, 0), ("k", HIDDEN, HIDDEN, 0), ("v", HIDDEN, HIDDEN, 0), ("o", HIDDEN, HIDDEN, 1),
          ("up", FFN, HIDDEN, 2), ("gate", FFN, HIDDEN, 2), ("down", HIDDEN, FFN, 3)]   # (name, N, K, x slot)
@@ -51,29 +63,35 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic():
-    """HBM bytes per launch of KERNEL from the committed counter summary
-    (lines 'key: value'), or None when it is missing or was taken from
-    another version of the kernel source."""
+def summary_values(path, sources):
+    """The 'key: value' lines of a committed counter summary, or {} when it is
+    missing or was taken from another version of the kernel source."""
     try:
         kv = {}
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(path) as fh:
             for line in fh:
                 if ":" in line and line.startswith("- "):
                     k, v = line[2:].split(":", 1)
                     kv[k.strip()] = v.strip().strip("`")
-        if kv.get("kernel_source_sha256_16") != kernel_source_sha():
-            return None
-        return int(kv["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return kv if kv.get("kernel_source_sha256_16") == kernel_source_sha(sources) else {}
+    except OSError:
+        return {}
+
+
+def profiled_traffic():
+    """HBM bytes per launch of KERNEL from the committed counter summary, or
+    None when it is missing or stale."""
+    try:
+        return int(summary_values(TRAFFIC_SUMMARY, KERNEL_SOURCES)["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
 
 
@@ -171,6 +189,54 @@ def cpu_baseline(oracle, synth, packed, budget_s=12.0):
                       % (layers, done_bytes / 1e6, dt)}
 
 
+def gemm_operands(L, synth, torch, dev, stream, N, K, M=512):
+    """i2_s weights (seed 401) and bf16 activations N(0,1) (seed 402)
+    quantized per token; output and a zero-filled split-K workspace."""
+    w = synth.ternary(401, N, K)
+    p = L.ll_pack_i2s(w, 0.05)
+    W = L.upload_i2s(p, N, K, dev)
+    xb = torch.from_numpy(synth.normal_bf16_bits(402, M, K).view(np.int16)).to(dev).view(torch.bfloat16)
+    xq, xsc = L.quantize(xb, stream)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gws = torch.zeros((max(L.ll_gemm_workspace_size(W, M), 16),), dtype=torch.uint8, device=dev)
+    return W, xb, xq, xsc, y, gws
+
+
+def gemm_roofline(L, synth, torch, dev, stream, steps, M=512):
+    """The int8 GEMM kernel launched back to back `steps` times between two
+    HIP events on its stream, per shape; TOPS = 2 M N K per launch / kernel
+    time, against the dense int8 matrix-core peak."""
+    lines = []
+    for N, K in GEMM_SHAPES:
+        W, _, xq, xsc, y, gws = gemm_operands(L, synth, torch, dev, stream, N, K, M)
+        for _ in range(5):
+            L.ll_bitlinear_gemm(W, xq, xsc, M, None, y, None, gws, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            L.ll_bitlinear_gemm(W, xq, xsc, M, None, y, None, gws, stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        ops = 2 * M * N * K
+        tops = ops / (ms * 1e-3) / 1e12
+        lines.append({"workload": "i2_s int8 GEMM M=%d N=%d K=%d (bf16 x ~ N(0,1) quantized per token)" % (M, N, K),
+                      "achieved": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4),
+                      "kernel_ms": round(ms, 5), "algorithmic_ops_per_launch": ops})
+        del W, xq, xsc, y, gws
+    kv = summary_values(GEMM_SUMMARY, GEMM_SOURCES)
+    head = lines[0]
+    res = {"bound": "mfma", "achieved": head["achieved"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+           "frac": head["frac"], "workload": head["workload"], "kernel": GEMM_KERNEL, "kernel_ms": head["kernel_ms"],
+           "algorithmic_ops_per_launch": head["algorithmic_ops_per_launch"],
+           "traffic": int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None,
+           "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+           "mfma_busy_frac": float(kv["mfma_busy_frac"]) if "mfma_busy_frac" in kv else None,
+           "kernel_source_sha256_16": kernel_source_sha(GEMM_SOURCES),
+           "other_shapes": lines[1:]}
+    return res
+
+
 def extras_single(L, synth, torch, dev, stream):
     out = {}
     for name, N, K in [("2560x2560", 2560, 2560), ("6912x2560", 6912, 2560), ("2560x6912", 2560, 6912)]:
@@ -237,16 +303,9 @@ def extras_single(L, synth, torch, dev, stream):
                 "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}
         del Ws
         torch.cuda.empty_cache()
-    # int8 prefill GEMM, M=512 (bf16 activations quantized per token)
-    for N, K in [(6912, 2560), (2560, 6912)]:
-        w = synth.ternary(401, N, K)
-        p = L.ll_pack_i2s(w, 0.05)
-        W = L.upload_i2s(p, N, K, dev)
-        xb = torch.from_numpy(synth.normal_bf16_bits(402, 512, K).view(np.int16)).to(dev).view(torch.bfloat16)
-        xq, xsc = L.quantize(xb, stream)
-        y = torch.empty((512, N), dtype=torch.float32, device=dev)
-        gws = torch.zeros((max(L.ll_gemm_workspace_size(W, 512), 16),), dtype=torch.uint8, device=dev)
-
+    # int8 prefill GEMM, M=512 (bf16 activations quantized per token), as graph replays
+    for N, K in GEMM_SHAPES:
+        W, xb, xq, xsc, y, gws = gemm_operands(L, synth, torch, dev, stream, N, K)
         ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemm(W, xq, xsc, 512, None, y, None, gws, st), 1, 20, stream)
         msq = time_graph(torch, lambda i, st: L.ll_quantize_act(xb, xq, xsc, st), 1, 20, stream)
         tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
@@ -264,6 +323,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--gemm-only", action="store_true")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -282,6 +342,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.gemm_only:                                   # the GEMM roofline alone (for the profiler)
+        print(json.dumps({"roofline_gemm": gemm_roofline(L, synth, torch, dev, stream, args.steps)}), flush=True)
+        return
     log("building the decode step")
     packed, items, weight_bytes = build_decode_step(L, synth, torch, dev)
     plan = L.GemvPlan(items, 1)
@@ -357,6 +420,8 @@ def main():
                      "kernel": KERNEL, "kernel_ms": round(prod_ms, 4), "kernel_ms_in_step": round(launch_ms, 4),
                      "kernel_source_sha256_16": kernel_source_sha()},
     }
+    log("int8 GEMM roofline")
+    res["roofline_gemm"] = gemm_roofline(L, synth, torch, dev, stream, args.steps)
     if not args.no_cpu:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(oracle, synth, packed)
