@@ -4,7 +4,9 @@
 // operands of every distinct activation (into the plan memory), one walking
 // the table of products.  One token (M == 1): fp4 digit planes on the fp4
 // matrix cores (gemv_fp4.hip); 2 <= M <= 16: int8 planes on the int8 matrix
-// cores, up to three tokens per pass (gemv_planes.hip).
+// cores, up to three tokens per pass (gemv_planes.hip).  An item may carry a
+// fused epilogue: a gated pair (gate and up of one activation, y = relu(g)^2
+// * u, one token) runs as workgroups of 64 rows of both matrices.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -29,19 +31,13 @@ struct Layout {
     bool f4 = false;                   // fp4 engine (one token)
 };
 
-ll_status check_item(const ll_gemv_item& it, int i, int32_t act, int64_t M, int32_t fmt0) {
-    const ll_weights& w = it.w;
+ll_status check_weights(const ll_weights& w, int i, int32_t fmt0) {
     if (w.fmt != fmt0) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d has a different format", i);
     if (w.N <= 0 || w.K <= 0) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: N and K must be positive", i);
     if (w.N > (int64_t(1) << 31) - 1 || w.K > (int64_t(1) << 24))
         return ll::failf(LL_ERANGE, "ll_gemv_plan: item %d: N must be < 2^31 and K <= 2^24", i);
-    if (!w.codes || !it.x || !it.y) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: NULL codes, x or y", i);
-    if (!aligned(w.codes, 16) || !aligned(it.x, 16))
-        return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: codes and x must be 16-byte aligned", i);
-    if (!aligned(it.y, 4) || (it.bias && !aligned(it.bias, 4)))
-        return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: y / bias must be 4-byte aligned", i);
-    if (act != LL_ACT_F32) return ll::fail(LL_EINVAL, "ll_gemv_plan: only fp32 activations are supported");
-    if (M < 1 || M > 16) return ll::fail(LL_ESHAPE, "ll_gemv_plan: M must be in [1, 16]");
+    if (!w.codes) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: NULL codes", i);
+    if (!aligned(w.codes, 16)) return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: codes must be 16-byte aligned", i);
     if (w.fmt == LL_FMT_I2S) {
         if (w.K % 128) return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: i2_s needs K %% 128 == 0", i);
     } else if (w.fmt == LL_FMT_TQ2_0) {
@@ -54,7 +50,30 @@ ll_status check_item(const ll_gemv_item& it, int i, int32_t act, int64_t M, int3
     return LL_OK;
 }
 
-ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M, Layout& L) {
+ll_status check_item(const ll_gemv_item_ex& it, int i, int32_t act, int64_t M, int32_t fmt0) {
+    if (act != LL_ACT_F32) return ll::fail(LL_EINVAL, "ll_gemv_plan: only fp32 activations are supported");
+    if (M < 1 || M > 16) return ll::fail(LL_ESHAPE, "ll_gemv_plan: M must be in [1, 16]");
+    ll_status st = check_weights(it.w, i, fmt0);
+    if (st) return st;
+    if (!it.x || !it.y) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: NULL x or y", i);
+    if (!aligned(it.x, 16)) return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: x must be 16-byte aligned", i);
+    if (!aligned(it.y, 4) || (it.bias && !aligned(it.bias, 4)))
+        return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: y / bias must be 4-byte aligned", i);
+    if (it.epilogue == LL_EPI_NONE) return LL_OK;
+    if (it.epilogue != LL_EPI_RELU2_MUL)
+        return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: unknown epilogue %d", i, int(it.epilogue));
+    if (M != 1) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: the gated pair needs M == 1", i);
+    if (it.bias) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: the gated pair takes no bias", i);
+    st = check_weights(it.w2, i, fmt0);
+    if (st) return st;
+    if (it.w2.N != it.w.N || it.w2.K != it.w.K)
+        return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: gate and up matrices differ in N or K", i);
+    return LL_OK;
+}
+
+bool is_pair(const ll_gemv_item_ex& it) { return it.epilogue == LL_EPI_RELU2_MUL; }
+
+ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M, Layout& L) {
     if (!items || count <= 0) return ll::fail(LL_EINVAL, "ll_gemv_plan: no items");
     for (int i = 0; i < count; ++i) {
         ll_status st = check_item(items[i], i, act, M, items[0].w.fmt);
@@ -63,8 +82,11 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     L.prep_of.assign(size_t(count), -1);
     for (int i = 0; i < count; ++i) L.kmax = std::max(L.kmax, items[i].w.K);
     L.f4 = llk::f4_engine(M, L.kmax);
-    const int64_t rows = L.f4 ? llk::f4_batch_rows() : llk::planes_batch_rows();
+    for (int i = 0; i < count; ++i)
+        if (is_pair(items[i]) && !L.f4)
+            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: the gated pair needs every K <= 2^20", i);
     for (int i = 0; i < count; ++i) {
+        const int64_t rows = L.f4 ? llk::f4_batch_rows(is_pair(items[i])) : llk::planes_batch_rows();
         int found = -1;
         for (size_t j = 0; j < L.xs.size(); ++j)
             if (L.xs[j] == items[i].x && L.xk[j] == items[i].w.K) { found = int(j); break; }
@@ -94,6 +116,22 @@ ll_status plan_layout(const ll_gemv_item* items, int32_t count, int32_t act, int
     return LL_OK;
 }
 
+// plain items as items without a fused epilogue
+std::vector<ll_gemv_item_ex> widen(const ll_gemv_item* items, int32_t count) {
+    std::vector<ll_gemv_item_ex> ex(static_cast<size_t>(count));
+    for (int32_t i = 0; i < count; ++i) {
+        ll_gemv_item_ex e;
+        std::memset(&e, 0, sizeof e);
+        e.w = items[i].w;
+        e.x = items[i].x;
+        e.bias = items[i].bias;
+        e.y = items[i].y;
+        e.epilogue = LL_EPI_NONE;
+        ex[size_t(i)] = e;
+    }
+    return ex;
+}
+
 ll_status check_plan(const ll_gemv_plan* p) {
     if (!p || !p->mem || !p->prob_table || !p->prep_table || !p->map_table || p->count <= 0 || p->nprep <= 0)
         return ll::fail(LL_EINVAL, "ll_gemv_plan: plan not initialised");
@@ -109,14 +147,14 @@ ll_status hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-size_t ll_gemv_plan_bytes(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M) {
+size_t ll_gemv_plan_bytes_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M) {
     Layout L;
     if (plan_layout(items, count, act, M, L)) return size_t(-1);
     return L.total;
 }
 
-ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M, void* mem, size_t bytes,
-                            ll_gemv_plan* plan) {
+ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M, void* mem,
+                               size_t bytes, ll_gemv_plan* plan) {
     if (!plan) return ll::fail(LL_EINVAL, "ll_gemv_plan_init: plan is NULL");
     Layout L;
     ll_status st = plan_layout(items, count, act, M, L);
@@ -127,16 +165,18 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     std::vector<char> host(L.frag_off, 0);
     int32_t* map = reinterpret_cast<int32_t*>(host.data() + L.map_off);
     int64_t first = 0;
-    const int64_t rows = L.f4 ? llk::f4_batch_rows() : llk::planes_batch_rows();
     for (int i = 0; i < count; ++i) {
-        const ll_gemv_item& it = items[i];
+        const ll_gemv_item_ex& it = items[i];
+        const bool pair = is_pair(it);
         char* ops = base + L.frag_at[size_t(L.prep_of[size_t(i)])];
         if (L.f4)
             llk::fill_f4_prob(host.data() + L.prob_off + size_t(i) * llk::f4_prob_bytes(), it.w.codes, it.w.scales,
-                              ops, it.bias, it.y, it.w.N, it.w.K, first);
+                              ops, it.bias, it.y, it.w.N, it.w.K, first, pair ? it.w2.codes : nullptr,
+                              pair ? it.w2.scales : nullptr);
         else
             llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
                                   it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
+        const int64_t rows = L.f4 ? llk::f4_batch_rows(pair) : llk::planes_batch_rows();
         const int64_t wgs = (it.w.N + rows - 1) / rows;
         for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
         first += wgs;
@@ -166,8 +206,23 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     p.prob_table = base + L.prob_off;
     p.prep_table = base + L.prep_off;
     p.map_table = base + L.map_off;
+    p.epilogues = 0;
+    for (int i = 0; i < count; ++i) p.epilogues |= is_pair(items[i]) ? 1 : 0;
     *plan = p;
     return LL_OK;
+}
+
+size_t ll_gemv_plan_bytes(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M) {
+    if (!items || count <= 0) return size_t(-1);
+    const std::vector<ll_gemv_item_ex> ex = widen(items, count);
+    return ll_gemv_plan_bytes_ex(ex.data(), count, act, M);
+}
+
+ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M, void* mem, size_t bytes,
+                            ll_gemv_plan* plan) {
+    if (!items || count <= 0) return ll::fail(LL_EINVAL, "ll_gemv_plan: no items");
+    const std::vector<ll_gemv_item_ex> ex = widen(items, count);
+    return ll_gemv_plan_init_ex(ex.data(), count, act, M, mem, bytes, plan);
 }
 
 ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
@@ -187,7 +242,7 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (llk::f4_engine(plan->M, plan->kmax))
         return hip_status(llk::launch_f4_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->tiles,
-                                                       plan->kmax, s),
+                                                       plan->kmax, plan->epilogues != 0, s),
                           "ll_gemv_plan_product");
     return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
                                                        plan->tiles, s),

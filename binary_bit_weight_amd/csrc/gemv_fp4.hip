@@ -102,6 +102,12 @@ struct F4Prob {
     float* y;
     int64_t N, K;
     int64_t wg0;                  // first (logical) workgroup of this product
+    // Gated pair [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"]: codes/scales are
+    // the gate, codes2/scales2 the up weights (same N, K, x);
+    // y = (r * r) * u with r = max(0, gate), u = up.
+    const uint8_t* codes2;
+    const uint16_t* scales2;
+    int32_t pair;
 };
 
 // ---------------------------------------------------------------- digits
@@ -247,8 +253,12 @@ struct Regs {
     uint16_t sc[kGroup * kCB];    // TQ2_0: scale of this lane's row per chunk and column block
 };
 
+// Returns this lane's result: lane l holds row row0 + l (column block l / 16,
+// meaningful for l < 16 kCB and rows < N), bias not added.
 template <int FMT>
-__device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, char* abuf, char* wtile) {
+__device__ __forceinline__ float f4_rows(const F4Prob& P, const uint8_t* __restrict__ codes,
+                                         const uint16_t* __restrict__ scales, int64_t row0, int tid, char* abuf,
+                                         char* wtile) {
     const int lane = tid & 63, nl = lane & 15, q = lane >> 4;
     const int64_t N = P.N, K = P.K, nch = nchunks(K);
     const uint32_t rowbytes = uint32_t(K / 4);
@@ -260,14 +270,14 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, 
     for (int j = 0; j < 4 * kCB; ++j) {
         int64_t r = row0 + 4 * j + q;
         r = r < N ? r : N - 1;                             // clamped rows are not stored
-        lrow[j] = P.codes + r * int64_t(rowbytes);
+        lrow[j] = codes + r * int64_t(rowbytes);
     }
     const uint16_t* srow[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
         int64_t r = row0 + 16 * cb + nl;
         r = r < N ? r : N - 1;
-        srow[cb] = P.scales + r * nch;
+        srow[cb] = scales + r * nch;
     }
     // Every load is issued by every lane from an in-bounds (clamped) address;
     // bytes past the end of a row are zeroed when stored to LDS.
@@ -408,15 +418,12 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, 
         long long xs = 0;
         for (int64_t sl = 0; sl < nslices(K); ++sl)
             xs += *(__attribute__((address_space(1))) const long long*)(meta + 8 + 8 * sl);
-        const float scale = *(const __attribute__((address_space(1))) float*)(P.codes + N * int64_t(rowbytes));
+        const float scale = *(const __attribute__((address_space(1))) float*)(codes + N * int64_t(rowbytes));
         yv = double(scale) * ((t - double(xs)) * unit);
     } else {
         yv = t * unit;                                      // block scales are inside t
     }
-    const int64_t row = row0 + lane;                       // = row0 + 16 cb + nl for cb = q
-    float out = float(yv);
-    if (P.bias) out = __fadd_rn(out, P.bias[row < N ? row : N - 1]);
-    if (q < kCB && row < N) P.y[row] = out;
+    return float(yv);
 }
 
 // grid: 8 * ceil(T / 8) workgroups for T logical ones; hardware workgroup w
@@ -424,7 +431,7 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, int64_t row0, int tid, 
 #ifndef LL_F4_OCC
 #define LL_F4_OCC 3                                    // waves per SIMD the register allocation aims at
 #endif
-template <int FMT>
+template <int FMT, bool PAIRS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LL_F4_OCC))) f4_batch_kernel(const F4Prob* __restrict__ tab,
                                                             const int32_t* __restrict__ map, int64_t T) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -432,10 +439,36 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(L
     const int64_t L = (w % 8) * T8 + w / 8;
     if (L >= T) return;                                    // whole workgroup
     const F4Prob& P = tab[ld32(map + L)];
-    const int tid = int(threadIdx.x), wave = tid >> 6;
-    // waves past the last row still take part (clamped rows, nothing stored): the loop has barriers
-    const int64_t row0 = (L - P.wg0) * kWgRows + wave * kWaveRows;
-    f4_rows<FMT>(P, row0, tid, lds, lds + 2 * kAWin + wave * kWTile);
+    const int tid = int(threadIdx.x), lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: selects stay scalar
+    char* wtile = lds + 2 * kAWin + wave * kWTile;
+    // Gated pair (only in launches whose table holds one): waves 0, 1
+    // multiply 64 gate rows, waves 2, 3 the same rows of the up matrix, all
+    // from one activation window.  Waves past the last row still take part
+    // (clamped rows, nothing stored): the loop has barriers.
+    const bool pair = PAIRS && P.pair != 0;
+    const int half = pair ? wave >> 1 : 0;
+    const int64_t row0 = pair ? (L - P.wg0) * (kWgRows / 2) + (wave & 1) * kWaveRows
+                              : (L - P.wg0) * kWgRows + wave * kWaveRows;
+    const float v = f4_rows<FMT>(P, half ? P.codes2 : P.codes, half ? P.scales2 : P.scales, row0, tid, lds, wtile);
+    const int64_t row = row0 + lane;                       // = row0 + 16 cb + nl for cb = q
+    if (!pair) {
+        // [BL "Fused BitLinear + Residual Add Kernel"]: a residual passed as the bias is added last
+        float out = v;
+        if (P.bias) out = __fadd_rn(out, P.bias[row < P.N ? row : P.N - 1]);
+        if (lane < kWaveRows && row < P.N) P.y[row] = out;
+        return;
+    }
+    // the up results reach the gate waves through LDS
+    __syncthreads();                                       // every wave is done with the operand buffers
+    float* xch = reinterpret_cast<float*>(lds);
+    if (half == 1 && lane < kWaveRows) xch[(wave & 1) * kWaveRows + lane] = v;
+    __syncthreads();
+    if (half == 0 && lane < kWaveRows && row < P.N) {
+        const float u = xch[(wave & 1) * kWaveRows + lane];
+        const float r = v > 0.0f ? v : 0.0f;
+        P.y[row] = __fmul_rn(__fmul_rn(r, r), u);
+    }
 }
 
 }  // namespace
@@ -444,14 +477,17 @@ namespace llk {
 
 bool f4_engine(int64_t M, int64_t kmax) { return M == 1 && kmax <= kMaxK; }
 size_t f4_operand_bytes(int64_t K) { return size_t(op_bytes(K)); }
-int64_t f4_batch_rows() { return kWgRows; }
+int64_t f4_batch_rows(bool pair) { return pair ? kWgRows / 2 : kWgRows; }
 size_t f4_prob_bytes() { return sizeof(F4Prob); }
 size_t f4_prep_bytes() { return sizeof(F4Prep); }
 int64_t f4_grid(int64_t T) { return 8 * ((T + 7) / 8); }
 
 void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
-                  int64_t N, int64_t K, int64_t wg0) {
+                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2) {
     F4Prob p;
+    p.codes2 = static_cast<const uint8_t*>(codes2);
+    p.scales2 = static_cast<const uint16_t*>(scales2);
+    p.pair = codes2 != nullptr;
     p.codes = static_cast<const uint8_t*>(codes);
     p.scales = static_cast<const uint16_t*>(scales);
     p.ops = static_cast<const uint8_t*>(ops);
@@ -481,21 +517,23 @@ hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int6
     return hipGetLastError();
 }
 
-hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
-                                   hipStream_t stream) {
-    (void)kmax;
+template <int FMT, bool PAIRS>
+hipError_t launch_f4_product(const F4Prob* t, const int32_t* m, int64_t T, hipStream_t stream) {
     const dim3 grid{unsigned(f4_grid(T))}, block{unsigned(kThreads)};
     const size_t lds = size_t(prod_lds_bytes());
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(f4_batch_kernel<FMT, PAIRS>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((f4_batch_kernel<FMT, PAIRS>), grid, block, lds, stream, t, m, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
+                                   bool pairs, hipStream_t stream) {
+    (void)kmax;
     const F4Prob* t = static_cast<const F4Prob*>(prob_table);
     const int32_t* m = static_cast<const int32_t*>(map);
-    hipError_t e = allow_dynamic_lds(fmt == 1 ? reinterpret_cast<const void*>(f4_batch_kernel<1>)
-                                              : reinterpret_cast<const void*>(f4_batch_kernel<2>), lds);
-    if (e != hipSuccess) return e;
-    if (fmt == 1)
-        hipLaunchKernelGGL(f4_batch_kernel<1>, grid, block, lds, stream, t, m, T);
-    else
-        hipLaunchKernelGGL(f4_batch_kernel<2>, grid, block, lds, stream, t, m, T);
-    return hipGetLastError();
+    if (fmt == 1) return pairs ? launch_f4_product<1, true>(t, m, T, stream) : launch_f4_product<1, false>(t, m, T, stream);
+    return pairs ? launch_f4_product<2, true>(t, m, T, stream) : launch_f4_product<2, false>(t, m, T, stream);
 }
 
 }  // namespace llk

@@ -68,15 +68,17 @@ namespace llk {
 // registers.  Used by prepared batches with M == 1 and every K <= 2^20.
 bool f4_engine(int64_t M, int64_t kmax);
 size_t f4_operand_bytes(int64_t K);                  // prepared digits of one activation
-int64_t f4_batch_rows();
+int64_t f4_batch_rows(bool pair);                   // output rows per workgroup (a gated pair: rows of both)
 size_t f4_prob_bytes();
 size_t f4_prep_bytes();
 int64_t f4_grid(int64_t T);                         // workgroups launched for T logical ones
+// codes2 / scales2: the up weights of a gated pair (codes / scales the gate), or NULL
 void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
-                  int64_t N, int64_t K, int64_t wg0);
+                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2);
 void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K);
 hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int64_t kmax, hipStream_t stream);
 // map: int32 [T], the product of each logical workgroup
+// pairs: the table holds gated pairs (a kernel variant with their epilogue)
 hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
-                                   hipStream_t stream);
+                                   bool pairs, hipStream_t stream);
 }  // namespace llk

@@ -319,42 +319,66 @@ class ll_gemv_item(C.Structure):
     _fields_ = [("w", ll_weights), ("x", C.c_void_p), ("bias", C.c_void_p), ("y", C.c_void_p)]
 
 
+LL_EPI_NONE, LL_EPI_RELU2_MUL = 0, 1
+
+
+class ll_gemv_item_ex(C.Structure):
+    _fields_ = [("w", ll_weights), ("w2", ll_weights), ("x", C.c_void_p), ("bias", C.c_void_p), ("y", C.c_void_p),
+                ("epilogue", C.c_int32)]
+
+
 class ll_gemv_plan(C.Structure):
     _fields_ = [("mem", C.c_void_p), ("bytes", C.c_size_t), ("count", C.c_int32), ("nprep", C.c_int32),
                 ("act", C.c_int32), ("fmt", C.c_int32), ("M", C.c_int64), ("tiles", C.c_int64),
                 ("prep_entries", C.c_int64), ("kmax", C.c_int64), ("prob_table", C.c_void_p),
-                ("prep_table", C.c_void_p), ("map_table", C.c_void_p)]
+                ("prep_table", C.c_void_p), ("map_table", C.c_void_p), ("epilogues", C.c_int32)]
 
 
 SIGNATURES.update({
     "ll_gemv_plan_bytes": (_SZ, [_P, _I32, _I32, _I64]),
     "ll_gemv_plan_init": (C.c_int, [_P, _I32, _I32, _I64, _P, _SZ, _P]),
+    "ll_gemv_plan_bytes_ex": (_SZ, [_P, _I32, _I32, _I64]),
+    "ll_gemv_plan_init_ex": (C.c_int, [_P, _I32, _I32, _I64, _P, _SZ, _P]),
     "ll_gemv_plan_run": (C.c_int, [_P, _P]),
     "ll_gemv_plan_prepare": (C.c_int, [_P, _P]),
     "ll_gemv_plan_product": (C.c_int, [_P, _P]),
 })
 
 
+class Relu2Mul:
+    """A gated pair for GemvPlan (M = 1): y = relu(W_gate x)^2 * (W_up x)
+    [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"], both products from one x."""
+
+    def __init__(self, w_gate, w_up, x, y):
+        self.w_gate, self.w_up, self.x, self.y = w_gate, w_up, x, y
+
+
 class GemvPlan:
     """A prepared batch of fp32-activation decode products (ll_gemv_plan_*).
 
-    items: list of (Weights, x, bias_or_None, y) with GPU tensors; the plan
-    keeps them alive.  run() = prepare() + product()."""
+    items: list of (Weights, x, bias_or_None, y) with GPU tensors, or
+    Relu2Mul gated pairs (ll_gemv_plan_init_ex); the plan keeps them alive.
+    With M = 1 the bias is the residual add.  run() = prepare() + product()."""
 
     def __init__(self, items, M):
         import torch
         self.items = list(items)
-        arr = (ll_gemv_item * len(self.items))()
-        for i, (w, x, b, y) in enumerate(self.items):
-            arr[i] = ll_gemv_item(w.desc, _dev(x), _dev(b), _dev(y))
+        arr = (ll_gemv_item_ex * len(self.items))()
+        for i, it in enumerate(self.items):
+            if isinstance(it, Relu2Mul):
+                arr[i] = ll_gemv_item_ex(it.w_gate.desc, it.w_up.desc, _dev(it.x), None, _dev(it.y), LL_EPI_RELU2_MUL)
+            else:
+                w, x, b, y = it
+                arr[i] = ll_gemv_item_ex(w.desc, ll_weights(), _dev(x), _dev(b), _dev(y), LL_EPI_NONE)
         self._arr = arr
         self.plan = ll_gemv_plan()
-        n = lib().ll_gemv_plan_bytes(arr, len(self.items), LL_ACT_F32, M)
+        n = lib().ll_gemv_plan_bytes_ex(arr, len(self.items), LL_ACT_F32, M)
         if n == 2 ** 64 - 1:   # invalid items: let init report which one
-            _check(lib().ll_gemv_plan_init(arr, len(self.items), LL_ACT_F32, M, None, 0, C.byref(self.plan)))
-        self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=self.items[0][1].device)
-        _check(lib().ll_gemv_plan_init(arr, len(self.items), LL_ACT_F32, M, _dev(self.mem), int(n),
-                                       C.byref(self.plan)))
+            _check(lib().ll_gemv_plan_init_ex(arr, len(self.items), LL_ACT_F32, M, None, 0, C.byref(self.plan)))
+        dev = self.items[0].x.device if isinstance(self.items[0], Relu2Mul) else self.items[0][1].device
+        self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=dev)
+        _check(lib().ll_gemv_plan_init_ex(arr, len(self.items), LL_ACT_F32, M, _dev(self.mem), int(n),
+                                          C.byref(self.plan)))
 
     def prepare(self, stream=None):
         _check(lib().ll_gemv_plan_prepare(C.byref(self.plan), _stream(stream)))

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LL_ABI_VERSION 1
+#define LL_ABI_VERSION 2
 
 typedef enum {
     LL_OK = 0,
@@ -223,7 +223,30 @@ typedef struct {
     void* prob_table;    /* inside mem */
     void* prep_table;    /* inside mem */
     void* map_table;     /* inside mem: product index of every workgroup */
+    int32_t epilogues;   /* nonzero when some item has a fused epilogue */
 } ll_gemv_plan;
+
+/* Fused epilogues of a prepared product.
+   LL_EPI_NONE: y = W x (+ bias).  With M == 1 the bias operand is the
+     residual stream of [BL "Fused BitLinear + Residual Add Kernel"] and "M=1
+     warp-cooperative kernel with fused residual add": y = residual + W x,
+     the add done last in fp32.
+   LL_EPI_RELU2_MUL [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"]: two products
+     of one activation, gate = W x and up = W2 x (each rounded to fp32 as a
+     plain product would be), and y = (r * r) * up with r = max(0, gate), two
+     fp32 multiplies in that order.  W and W2 must have the same format, N
+     and K; M must be 1 (the fp4 engine); bias must be NULL.  The two
+     matrices are read in one pass over x's operands. */
+typedef enum { LL_EPI_NONE = 0, LL_EPI_RELU2_MUL = 1 } ll_epilogue;
+
+typedef struct {
+    ll_weights w;        /* packed weights; the gate for LL_EPI_RELU2_MUL */
+    ll_weights w2;       /* LL_EPI_RELU2_MUL: the up weights; ignored otherwise */
+    const void* x;       /* device fp32 [M, K] */
+    const float* bias;   /* device fp32 [N] or NULL (LL_EPI_NONE only) */
+    float* y;            /* device fp32 [M, N] */
+    int32_t epilogue;    /* ll_epilogue */
+} ll_gemv_item_ex;
 
 /* Device bytes ll_gemv_plan_init needs for these items ((size_t)-1 for
    invalid arguments). */
@@ -236,6 +259,13 @@ size_t ll_gemv_plan_bytes(const ll_gemv_item* items, int32_t count, int32_t act,
    synchronizes. */
 ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t act, int64_t M,
                             void* mem, size_t bytes, ll_gemv_plan* plan);
+/* The same for items with a fused epilogue (ll_gemv_item_ex); plain items
+   are LL_EPI_NONE with w2 unused.  An invalid epilogue code, a gated pair
+   whose matrices differ in format, N or K, a gated pair with M != 1 or a
+   bias is LL_EINVAL (LL_ESHAPE for the shape mismatch). */
+size_t ll_gemv_plan_bytes_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M);
+ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M,
+                               void* mem, size_t bytes, ll_gemv_plan* plan);
 /* Both launches: ll_gemv_plan_prepare, then ll_gemv_plan_product. */
 ll_status ll_gemv_plan_run(const ll_gemv_plan* plan, void* stream);
 /* Lays out the current contents of every x as operands (inside mem). */

@@ -246,3 +246,14 @@ def quantize_bf16(xb):
     s = np.empty(M, np.float32)
     lib().orc_quantize_bf16(_p(xb), M, K, _p(q), _p(s))
     return q, s
+
+
+# ---------------------------------------------------------------- fused epilogues
+def relu2_mul(gate, up):
+    """[BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"] out = (r * r) * up with
+    r = max(0, gate), elementwise in fp64; gate and up are the two products
+    of one activation (the exact values of the oracle's gemv functions)."""
+    g = np.asarray(gate, np.float64)
+    u = np.asarray(up, np.float64)
+    r = np.where(g > 0.0, g, 0.0)
+    return (r * r) * u

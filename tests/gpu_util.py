@@ -30,6 +30,21 @@ def f32_tol_ok(y_gpu, y_ref, tsum):
     return (not bad.any()), float((err / bound).max())
 
 
+def relu2_mul_tol_ok(out_gpu, g_ref, tg, u_ref, tu):
+    """Bound for out = (r * r) * u computed in fp32 from gate and up products
+    that each meet the fp32 bound (eg = 1e-5 tg + 1e-6, eu likewise): with
+    r = max(0, g) (1-Lipschitz), the product rule gives
+    |out - r^2 u| <= (2 r + eg) eg (|u| + eu) + r^2 eu, plus the two fp32
+    multiplies, each within 2^-24 relative: 2^-22 (r + eg)^2 (|u| + eu)."""
+    eg = 1e-5 * tg + 1e-6
+    eu = 1e-5 * tu + 1e-6
+    r = np.maximum(g_ref, 0.0)
+    ref = r * r * u_ref
+    bound = (2 * r + eg) * eg * (np.abs(u_ref) + eu) + r * r * eu + 2.0 ** -22 * (r + eg) ** 2 * (np.abs(u_ref) + eu)
+    err = np.abs(out_gpu.astype(np.float64) - ref)
+    return (not (err > bound).any()), float((err / bound).max())
+
+
 def make_i2s(seed, N, K, scale=None, p0=0.4):
     w = synth.ternary(seed, N, K, p0)
     if scale is None:

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from binary_bit_weight_amd import lowbit as L
 from binary_bit_weight_amd import synth
-from gpu_util import announce, f32_tol_ok, make_i2s, make_tq2, torch
+from gpu_util import announce, f32_tol_ok, make_i2s, make_tq2, relu2_mul_tol_ok, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -260,6 +260,54 @@ def test_gemv_plan_matches_oracle(fmt, M, big):
             y_ref, tsum = fn(packed, N, K, xs_np[slot][0], rows)
             ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
             assert ok, "N=%d K=%d round %d: worst error / bound %.3f" % (N, K, rnd, worst)
+
+
+@pytest.mark.parametrize("fmt", ["i2s", "tq2"])
+def test_gemv_plan_relu2_mul_and_residual(fmt):
+    """Fused epilogues of a one-token prepared batch against the oracle: gated
+    pairs y = relu(gate)^2 * up [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"] (the
+    FFN shape 6912 x 2560 and a ragged 100-row pair with another x), mixed
+    with a plain product whose bias is the residual stream [BL "Fused
+    BitLinear + Residual Add Kernel"]; run twice with new x contents."""
+    t = torch()
+    K, Kr = 2560, 384 if fmt == "i2s" else 512
+    mk = (lambda s, N, K: make_i2s(s, N, K)) if fmt == "i2s" else (lambda s, N, K: make_tq2(s, N, K))
+    up = (lambda p, N, K: L.upload_i2s(p, N, K)) if fmt == "i2s" else (lambda p, N, K: L.upload_tq2(p, N, K))
+    fn = oracle.i2s_gemv_f32 if fmt == "i2s" else oracle.tq2_gemv_f32
+    xs = {0: _x(830, 1, K), 1: _x(831, 1, Kr)}
+    xd = {k: t.from_numpy(v).cuda() for k, v in xs.items()}
+    pairs, items = [], []
+    for i, (N, KK, slot) in enumerate([(6912, K, 0), (100, Kr, 1)]):
+        pg, pu = mk(840 + 2 * i, N, KK)[2], mk(841 + 2 * i, N, KK)[2]
+        y = t.empty((1, N), dtype=t.float32, device="cuda")
+        items.append(L.Relu2Mul(up(pg, N, KK), up(pu, N, KK), xd[slot], y))
+        pairs.append((pg, pu, N, KK, slot, y))
+    pp = mk(850, 2560, K)[2]
+    res = synth.normal_f32(851, 1, 2560)[0]
+    yp = t.empty((1, 2560), dtype=t.float32, device="cuda")
+    items.append((up(pp, 2560, K), xd[0], t.from_numpy(res).cuda(), yp))
+    announce("gemv plan relu2 mul", fmt)
+    plan = L.GemvPlan(items, 1)
+    for rnd in range(2):
+        if rnd == 1:
+            for slot in xs:
+                xs[slot] = _x(860 + slot, 1, xs[slot].shape[1])
+                xd[slot].copy_(t.from_numpy(xs[slot]))
+        plan.run()
+        t.cuda.synchronize()
+        for pg, pu, N, KK, slot, y in pairs:
+            rows = synth.sample_rows(N + rnd, N, 48) if N > 100 else np.arange(N)
+            g_ref, tg = fn(pg, N, KK, xs[slot], rows)
+            u_ref, tu = fn(pu, N, KK, xs[slot], rows)
+            ok, worst = relu2_mul_tol_ok(y.cpu().numpy()[:, rows], g_ref, tg, u_ref, tu)
+            assert ok, "pair N=%d K=%d round %d: worst error / bound %.3f" % (N, KK, rnd, worst)
+            assert (g_ref > 0).any() and (g_ref < 0).any()
+        rows = synth.sample_rows(7 + rnd, 2560, 48)
+        y_ref, tsum = fn(pp, 2560, K, xs[0], rows)
+        want = y_ref + res[rows].astype(np.float64)[None, :]
+        got = yp.cpu().numpy()[:, rows].astype(np.float64)
+        bound = 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)
+        assert (np.abs(got - want) <= bound).all(), "residual round %d" % rnd
 
 
 @pytest.mark.parametrize("fmt", ["i2s", "tq2"])

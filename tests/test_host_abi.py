@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES), "binding and header disagree"
-    assert L.ll_abi_version() == 1
+    assert L.ll_abi_version() == 2
     assert L.ll_strerror(-5) == "workspace missing or too small"
 
 
@@ -190,6 +190,34 @@ def test_plan_bytes_hold_every_activation_layout():
     b_shared = lib.ll_gemv_plan_bytes(shared, 3, L.LL_ACT_F32, 1)
     assert 5 * (2560 + 8448) <= b_shared < 5 * (2 * 2560 + 8448)
     assert lib.ll_gemv_plan_bytes(fused, 2, L.LL_ACT_I8, 1) == 2 ** 64 - 1
+
+
+def _pair(N, K, x, y, N2=None, K2=None, bias=None, epi=1):
+    return L.ll_gemv_item_ex(_w(N=N, K=K), _w(N=N2 or N, K=K2 or K), C.c_void_p(x),
+                             None if bias is None else C.c_void_p(bias), C.c_void_p(y), epi)
+
+
+def test_plan_ex_gated_pair_validation():
+    """Host-only: a gated pair (LL_EPI_RELU2_MUL) shares its activation layout
+    with a plain item of the same x and K, and is rejected with M != 1, a
+    bias, gate and up of different N or K, or an unknown epilogue code."""
+    lib = L.lib()
+    plain = L.ll_gemv_item_ex(_w(N=2560, K=2560), L.ll_weights(), C.c_void_p(FAKE), None, C.c_void_p(FAKE), 0)
+    ok = (L.ll_gemv_item_ex * 2)(plain, _pair(6912, 2560, FAKE, FAKE))
+    b_ok = lib.ll_gemv_plan_bytes_ex(ok, 2, L.LL_ACT_F32, 1)
+    assert b_ok != 2 ** 64 - 1 and b_ok >= 5 * 2560
+    one = (L.ll_gemv_item * 1)(_item(2560, 2560, FAKE, FAKE))
+    assert b_ok < lib.ll_gemv_plan_bytes(one, 1, L.LL_ACT_F32, 1) + 5 * 2560   # one layout for the shared x
+    assert lib.ll_gemv_plan_bytes_ex(ok, 2, L.LL_ACT_F32, 2) == 2 ** 64 - 1     # M != 1
+    plan = L.ll_gemv_plan()
+    cases = [(_pair(64, 2560, FAKE, FAKE, K2=5120), -2),
+             (_pair(64, 2560, FAKE, FAKE, N2=65), -2),
+             (_pair(64, 2560, FAKE, FAKE, bias=FAKE), -1),
+             (_pair(64, 2560, FAKE, FAKE, epi=7), -1)]
+    for item, want in cases:
+        arr = (L.ll_gemv_item_ex * 1)(item)
+        assert lib.ll_gemv_plan_bytes_ex(arr, 1, L.LL_ACT_F32, 1) == 2 ** 64 - 1
+        assert lib.ll_gemv_plan_init_ex(arr, 1, L.LL_ACT_F32, 1, None, 0, C.byref(plan)) == want
 
 
 def test_w1_device_argument_errors_and_workspace():

@@ -442,3 +442,35 @@ def test_quantize_bf16_matches_f32(orc):
     q1, s1 = orc.quantize_bf16(xb)
     q2, s2 = orc.quantize_f32(xf)
     assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
+# ------------------------------------------------------------------ fused epilogues
+def test_relu2_mul_closed_forms(orc):
+    """[BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"]: max(0, gate)^2 * up, values
+    worked by hand: negative and zero gates give 0 whatever up is (a dropped
+    ReLU would give 63 and -7 for the first two), 0.5^2 * 4 = 1, 2^2 * 3 = 12,
+    3^2 * -1 = -9 (a missing square would give 1.5*... and -3)."""
+    g = [-3.0, -0.0, 0.0, 0.5, 2.0, 3.0, -1e30]
+    u = [7.0, -7.0, 7.0, 4.0, 3.0, -1.0, 5.0]
+    assert orc.relu2_mul(g, u).tolist() == [0.0, 0.0, 0.0, 1.0, 12.0, -9.0, 0.0]
+
+
+def test_relu2_mul_scaling_and_products(orc):
+    """Homogeneity (degree 2 in a positive gate scale, 1 in the up scale) and
+    the product of the oracle's own exact gemv results for a one-hot gate row:
+    gate = s_g x_k, up = s_u x_j, so out = s_g^2 x_k^2 s_u x_j when x_k > 0."""
+    rng = np.random.default_rng(5)
+    g, u = rng.normal(size=64), rng.normal(size=64)
+    base = orc.relu2_mul(g, u)
+    assert np.array_equal(orc.relu2_mul(4.0 * g, 0.5 * u), 8.0 * base)   # powers of two: exact
+    K = 128
+    x = np.zeros((1, K), np.float32)
+    x[0, 5], x[0, 9] = 3.0, -2.0
+    wg = np.zeros((1, K), np.int8); wg[0, 5] = 1
+    wu = np.zeros((1, K), np.int8); wu[0, 9] = -1
+    pg = orc.i2s_encode(wg, 0.5)
+    pu = orc.i2s_encode(wu, 0.25)
+    gate, _ = orc.i2s_gemv_f32(pg, 1, K, x)
+    up, _ = orc.i2s_gemv_f32(pu, 1, K, x)
+    assert gate[0, 0] == 1.5 and up[0, 0] == 0.5
+    assert orc.relu2_mul(gate, up)[0, 0] == 1.5 * 1.5 * 0.5
