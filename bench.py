@@ -237,6 +237,33 @@ def gemm_roofline(L, synth, torch, dev, stream, steps, M=512):
     return res
 
 
+def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
+    """The same 30-layer decode step with the pages' fused epilogues: O and
+    down add the residual stream (as their bias), gate and up run as one
+    gated pair (y = relu(gate)^2 * up).  Same weights and bytes as the
+    headline step; prepare + product per step, timed with HIP events."""
+    fused = []
+    for layer in range(LAYERS):
+        by = {name: items[len(ROLES) * layer + r] for r, (name, _, _, _) in enumerate(ROLES)}
+        res_h = [torch.from_numpy(synth.normal_f32(5000 + 2 * layer + j, 1, HIDDEN)).to(dev).reshape(HIDDEN)
+                 for j in range(2)]
+        for name in ("q", "k", "v"):
+            fused.append(by[name])
+        W, x, _, y = by["o"]
+        fused.append((W, x, res_h[0], y))
+        (Wu, xu, _, yu), (Wg, _, _, _) = by["up"], by["gate"]
+        fused.append(L.Relu2Mul(Wg, Wu, xu, yu))
+        W, x, _, y = by["down"]
+        fused.append((W, x, res_h[1], y))
+    plan = L.GemvPlan(fused, 1)
+    for _ in range(5):
+        plan.run(stream)
+    ms = time_events(torch, lambda: plan.run(stream), steps, stream)
+    return {"ms_per_step": round(ms, 4), "GB_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+            "products": len(fused), "tiles": int(plan.plan.tiles),
+            "note": "gate+up as 30 gated pairs (relu^2 * up), residual added to O and down"}
+
+
 def extras_single(L, synth, torch, dev, stream):
     out = {}
     for name, N, K in [("2560x2560", 2560, 2560), ("6912x2560", 6912, 2560), ("2560x6912", 2560, 6912)]:
@@ -427,7 +454,9 @@ def main():
         res["cpu_baseline"] = cpu_baseline(oracle, synth, packed)
     if not args.no_extras:
         log("extras")
-        res["extras"] = extras_single(L, synth, torch, dev, stream)
+        res["extras"] = {"i2s_decode_step_fused_epilogues":
+                         fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, args.steps)}
+        res["extras"].update(extras_single(L, synth, torch, dev, stream))
     print(json.dumps(res), flush=True)
 
 
