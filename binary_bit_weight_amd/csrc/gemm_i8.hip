@@ -123,6 +123,24 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
         *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
     };
 
+    // epilogue operands, requested before the main loop so their latency is
+    // hidden: token scales of this lane's rows (row half kh after the
+    // exchange), the weight scale, the biases of its columns
+    float xsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + kh * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        xsv[r] = xs[m < M ? m : M - 1];
+    }
+    const float sw = *reinterpret_cast<const float*>(codes + N * rowbytes);
+    const float* bsrc = bias ? bias : xs;                 // always a valid address
+    float bnv[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t n = n0 + wn * 64 + nb * 32 + li;
+        bnv[nb] = bsrc[bias ? (n < N ? n : N - 1) : 0];
+    }
+
     i32x16 acc[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -200,14 +218,6 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
 
     // The two k halves of each wave tile meet: the wave of half kh keeps row
     // block mb = kh and hands the other to its partner through LDS.
-    // token scales of this lane's rows (row half kh after the exchange),
-    // requested before the exchange so their latency overlaps it
-    float xsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + kh * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        xsv[r] = xs[m < M ? m : M - 1];
-    }
     __syncthreads();                                       // every wave is done with the operand buffers
     int32_t* xb = reinterpret_cast<int32_t*>(lds);
     i32x16 fin[2];
@@ -265,14 +275,6 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     // 4 h + r % 4; its output pointer is formed once, each store adds a
     // uniform row offset.  The stores of a full tile run as one straight block
     // (a branch between stores would make each wait for the one before).
-    const float sw = *reinterpret_cast<const float*>(codes + N * rowbytes);
-    const float* bsrc = bias ? bias : xs;                 // always a valid address
-    float bnv[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t n = n0 + wn * 64 + nb * 32 + li;
-        bnv[nb] = bsrc[bias ? (n < N ? n : N - 1) : 0];
-    }
     float out[2][16];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
