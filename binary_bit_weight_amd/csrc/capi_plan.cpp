@@ -24,8 +24,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Layout {
     size_t prob_off = 0, prep_off = 0, map_off = 0, frag_off = 0, total = 0;
     std::vector<int> prep_of;          // item -> distinct activation index
-    std::vector<const void*> xs;       // distinct activations
+    std::vector<const void*> xs;       // distinct activations (with their norm)
     std::vector<int64_t> xk;           // their K
+    std::vector<const float*> xnw;     // their RMSNorm weights (or NULL)
+    std::vector<float> xeps;           // and epsilon
     std::vector<size_t> frag_at;       // byte offset of each activation's operands
     int64_t tiles = 0, kmax = 0;       // workgroups of the product launch
     bool f4 = false;                   // fp4 engine (one token)
@@ -59,6 +61,13 @@ ll_status check_item(const ll_gemv_item_ex& it, int i, int32_t act, int64_t M, i
     if (!aligned(it.x, 16)) return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: x must be 16-byte aligned", i);
     if (!aligned(it.y, 4) || (it.bias && !aligned(it.bias, 4)))
         return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: y / bias must be 4-byte aligned", i);
+    if (it.norm_w) {
+        if (M != 1) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: the RMSNorm prologue needs M == 1", i);
+        if (!aligned(it.norm_w, 16))
+            return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: norm_w must be 16-byte aligned", i);
+        if (!(it.norm_eps >= 0.0f) || it.norm_eps > 3.4e38f)
+            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: norm_eps must be finite and >= 0", i);
+    }
     if (it.epilogue == LL_EPI_NONE) return LL_OK;
     if (it.epilogue != LL_EPI_RELU2_MUL)
         return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: unknown epilogue %d", i, int(it.epilogue));
@@ -83,17 +92,23 @@ ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, 
     for (int i = 0; i < count; ++i) L.kmax = std::max(L.kmax, items[i].w.K);
     L.f4 = llk::f4_engine(M, L.kmax);
     for (int i = 0; i < count; ++i)
-        if (is_pair(items[i]) && !L.f4)
-            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: the gated pair needs every K <= 2^20", i);
+        if ((is_pair(items[i]) || items[i].norm_w) && !L.f4)
+            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: gated pairs and norms need every K <= 2^20", i);
     for (int i = 0; i < count; ++i) {
         const int64_t rows = L.f4 ? llk::f4_batch_rows(is_pair(items[i])) : llk::planes_batch_rows();
         int found = -1;
+        const float eps = items[i].norm_w ? items[i].norm_eps : 0.0f;
         for (size_t j = 0; j < L.xs.size(); ++j)
-            if (L.xs[j] == items[i].x && L.xk[j] == items[i].w.K) { found = int(j); break; }
+            if (L.xs[j] == items[i].x && L.xk[j] == items[i].w.K && L.xnw[j] == items[i].norm_w && L.xeps[j] == eps) {
+                found = int(j);
+                break;
+            }
         if (found < 0) {
             found = int(L.xs.size());
             L.xs.push_back(items[i].x);
             L.xk.push_back(items[i].w.K);
+            L.xnw.push_back(items[i].norm_w);
+            L.xeps.push_back(eps);
         }
         L.prep_of[size_t(i)] = found;
         L.tiles += (items[i].w.N + rows - 1) / rows;              // (logical) workgroups
@@ -184,7 +199,8 @@ ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int3
     for (size_t j = 0; j < L.xs.size(); ++j) {
         const float* x = static_cast<const float*>(L.xs[j]);
         if (L.f4)
-            llk::fill_f4_prep(host.data() + L.prep_off + j * llk::f4_prep_bytes(), x, base + L.frag_at[j], L.xk[j]);
+            llk::fill_f4_prep(host.data() + L.prep_off + j * llk::f4_prep_bytes(), x, base + L.frag_at[j], L.xk[j],
+                              L.xnw[j], L.xeps[j]);
         else
             llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
                                   L.xk[j]);

@@ -92,6 +92,11 @@ struct F4Prep {
     const float* x;
     void* ops;
     int64_t K;
+    // RMSNorm prologue [BL "Fused RMSNorm + BitLinear + Residual Add M=1
+    // Kernel"], or NULL: the operand is xn = (x * rinv) * norm_w with
+    // rinv = 1 / sqrt(sum x^2 / K + eps) (0 for a zero row with eps = 0).
+    const float* norm_w;
+    float eps;
 };
 
 struct F4Prob {
@@ -116,11 +121,35 @@ struct TokScale {
     float f1, f2;                 // x * f1 * f2 = x * 2^(34 - E), both factors exact powers of two
 };
 
-// max |x| over a token row, by the 256 threads of a workgroup (barrier inside).
-__device__ __forceinline__ TokScale token_scale(const float* x, int64_t K, int tid, float* smax) {
-    float mx = 0.0f;
+// 1 / sqrt(sum x^2 / K + eps) of a token row, rounded once to fp32 (sum and
+// root in fp64), by the 256 threads of a workgroup (barrier inside).
+__device__ __forceinline__ float rms_inv(const float* x, int64_t K, float eps, int tid, double* sacc) {
+    double ss = 0.0;
     for (int64_t i = tid; i < K / 4; i += 256) {
         const f32x4 u = ld16f(x + 4 * i);
+        ss += (double(u[0]) * u[0] + double(u[1]) * u[1]) + (double(u[2]) * u[2] + double(u[3]) * u[3]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    if ((tid & 63) == 0) sacc[tid >> 6] = ss;
+    __syncthreads();
+    const double d = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+    const double den = d / double(K) + double(eps);
+    return den > 0.0 ? float(1.0 / sqrt(den)) : 0.0f;
+}
+
+// max |x| (or |xn| with a norm: xn = (x * rinv) * w) over a token row, by the
+// 256 threads of a workgroup (barrier inside).
+__device__ __forceinline__ TokScale token_scale(const float* x, const float* w, float rinv, int64_t K, int tid,
+                                                float* smax) {
+    float mx = 0.0f;
+    for (int64_t i = tid; i < K / 4; i += 256) {
+        f32x4 u = ld16f(x + 4 * i);
+        if (w) {
+            const f32x4 g = ld16f(w + 4 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = __fmul_rn(__fmul_rn(u[e], rinv), g[e]);
+        }
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
     }
     mx = wave_max(mx);
@@ -176,15 +205,17 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
     const int slice = int(blockIdx.y);
     if (slice >= nslices(K)) return;                       // whole workgroup
     const float* x = P.x;
+    const float* nw = P.norm_w;
     uint8_t* ops = static_cast<uint8_t*>(P.ops);
     __shared__ float smax[4];                              // four waves
     __shared__ long long ssum[4];
+    __shared__ double sacc[4];
     const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
 
     const int lc = tid >> 5, s = (tid >> 4) & 1, q = (tid >> 2) & 3, j = tid & 3;
     const int64_t c = int64_t(slice) * kSliceChunks + lc;
     const bool live = c < nchunks(K);
-    float v[8];
+    float v[8], nv[8];
     if (FMT == 1) {
         // i2_s: byte 16 (q%2) + 4 j + b of group 2c + q/2 holds the elements
         // 128 g + 32 t + 16 (q%2) + 4 j + b at shifts 6 - 2t; nibble h of the
@@ -195,7 +226,13 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int t = (s == 0 ? 3 : 2) - 2 * h;
-            const f32x4 w4 = ld16f(x + 128 * gc + 32 * t + 16 * (q & 1) + 4 * j);
+            const int64_t k0 = 128 * gc + 32 * t + 16 * (q & 1) + 4 * j;
+            const f32x4 w4 = ld16f(x + k0);
+            if (nw) {
+                const f32x4 g4 = ld16f(nw + k0);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) nv[2 * b + h] = g4[b];
+            }
 #pragma unroll
             for (int b = 0; b < 4; ++b) v[2 * b + h] = ok ? w4[b] : 0.0f;
         }
@@ -203,18 +240,30 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
         // TQ2_0: byte 16 q + 4 j + b of block c holds elements 4 (16 q + 4 j + b) + i
         // at bits 2 i; nibble h of step s takes i = 2h + s.
         const int64_t cc = live ? c : 0;
-        const float* xb = x + 256 * cc + 64 * q + 16 * j;
+        const int64_t k0 = 256 * cc + 64 * q + 16 * j;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const f32x4 w4 = ld16f(xb + 4 * b);
+            const f32x4 w4 = ld16f(x + k0 + 4 * b);
+            if (nw) {
+                const f32x4 g4 = ld16f(nw + k0 + 4 * b);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) nv[2 * b + h] = g4[2 * h + s];
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) v[2 * b + h] = live ? w4[2 * h + s] : 0.0f;
         }
     }
+    // RMSNorm prologue: the same two fp32 multiplies as in token_scale
+    float rinv = 0.0f;
+    if (nw) {
+        rinv = rms_inv(x, K, P.eps, tid, sacc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(__fmul_rn(v[e], rinv), nv[e]);
+    }
 
     // max |x| over the token (this thread's elements were requested above, so
     // both loads are in flight together)
-    const TokScale ts = token_scale(x, K, tid, smax);
+    const TokScale ts = token_scale(x, nw, rinv, K, tid, smax);
     const int E = ts.E;
     uint32_t out[kPl];
     long long xsum = 0;
@@ -499,11 +548,13 @@ void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* 
     *static_cast<F4Prob*>(dst) = p;
 }
 
-void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K) {
+void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K, const float* norm_w, float eps) {
     F4Prep p;
     p.x = x;
     p.ops = ops;
     p.K = K;
+    p.norm_w = norm_w;
+    p.eps = eps;
     *static_cast<F4Prep*>(dst) = p;
 }
 

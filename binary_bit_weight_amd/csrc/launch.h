@@ -75,7 +75,8 @@ int64_t f4_grid(int64_t T);                         // workgroups launched for T
 // codes2 / scales2: the up weights of a gated pair (codes / scales the gate), or NULL
 void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
                   int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2);
-void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K);
+// norm_w: the RMSNorm weights of an activation normalised in the preparation, or NULL
+void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K, const float* norm_w, float eps);
 hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int64_t kmax, hipStream_t stream);
 // map: int32 [T], the product of each logical workgroup
 // pairs: the table holds gated pairs (a kernel variant with their epilogue)

@@ -324,7 +324,7 @@ LL_EPI_NONE, LL_EPI_RELU2_MUL = 0, 1
 
 class ll_gemv_item_ex(C.Structure):
     _fields_ = [("w", ll_weights), ("w2", ll_weights), ("x", C.c_void_p), ("bias", C.c_void_p), ("y", C.c_void_p),
-                ("epilogue", C.c_int32)]
+                ("epilogue", C.c_int32), ("norm_eps", C.c_float), ("norm_w", C.c_void_p)]
 
 
 class ll_gemv_plan(C.Structure):
@@ -347,10 +347,20 @@ SIGNATURES.update({
 
 class Relu2Mul:
     """A gated pair for GemvPlan (M = 1): y = relu(W_gate x)^2 * (W_up x)
-    [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"], both products from one x."""
+    [BL "Fused Gate+Up+ReLU²×Mul M=1 Kernel"], both products from one x
+    (optionally RMS-normalised: norm = (weights [K], eps))."""
 
-    def __init__(self, w_gate, w_up, x, y):
-        self.w_gate, self.w_up, self.x, self.y = w_gate, w_up, x, y
+    def __init__(self, w_gate, w_up, x, y, norm=None):
+        self.w_gate, self.w_up, self.x, self.y, self.norm = w_gate, w_up, x, y, norm
+
+
+class Normed:
+    """A product of an RMS-normalised activation for GemvPlan (M = 1) [BL
+    "Fused RMSNorm + BitLinear + Residual Add M=1 Kernel"]: y = W xn (+ bias,
+    the residual) with xn = x / sqrt(mean(x^2) + eps) * norm_w."""
+
+    def __init__(self, w, x, norm_w, eps, bias, y):
+        self.w, self.x, self.norm_w, self.eps, self.bias, self.y = w, x, norm_w, eps, bias, y
 
 
 class GemvPlan:
@@ -366,16 +376,21 @@ class GemvPlan:
         arr = (ll_gemv_item_ex * len(self.items))()
         for i, it in enumerate(self.items):
             if isinstance(it, Relu2Mul):
-                arr[i] = ll_gemv_item_ex(it.w_gate.desc, it.w_up.desc, _dev(it.x), None, _dev(it.y), LL_EPI_RELU2_MUL)
+                nw, eps = it.norm if it.norm is not None else (None, 0.0)
+                arr[i] = ll_gemv_item_ex(it.w_gate.desc, it.w_up.desc, _dev(it.x), None, _dev(it.y), LL_EPI_RELU2_MUL,
+                                         float(eps), _dev(nw))
+            elif isinstance(it, Normed):
+                arr[i] = ll_gemv_item_ex(it.w.desc, ll_weights(), _dev(it.x), _dev(it.bias), _dev(it.y), LL_EPI_NONE,
+                                         float(it.eps), _dev(it.norm_w))
             else:
                 w, x, b, y = it
-                arr[i] = ll_gemv_item_ex(w.desc, ll_weights(), _dev(x), _dev(b), _dev(y), LL_EPI_NONE)
+                arr[i] = ll_gemv_item_ex(w.desc, ll_weights(), _dev(x), _dev(b), _dev(y), LL_EPI_NONE, 0.0, None)
         self._arr = arr
         self.plan = ll_gemv_plan()
         n = lib().ll_gemv_plan_bytes_ex(arr, len(self.items), LL_ACT_F32, M)
         if n == 2 ** 64 - 1:   # invalid items: let init report which one
             _check(lib().ll_gemv_plan_init_ex(arr, len(self.items), LL_ACT_F32, M, None, 0, C.byref(self.plan)))
-        dev = self.items[0].x.device if isinstance(self.items[0], Relu2Mul) else self.items[0][1].device
+        dev = self.items[0].x.device if isinstance(self.items[0], (Relu2Mul, Normed)) else self.items[0][1].device
         self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=dev)
         _check(lib().ll_gemv_plan_init_ex(arr, len(self.items), LL_ACT_F32, M, _dev(self.mem), int(n),
                                           C.byref(self.plan)))

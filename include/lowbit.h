@@ -246,6 +246,12 @@ typedef struct {
     const float* bias;   /* device fp32 [N] or NULL (LL_EPI_NONE only) */
     float* y;            /* device fp32 [M, N] */
     int32_t epilogue;    /* ll_epilogue */
+    float norm_eps;      /* RMSNorm epsilon (>= 0), with norm_w */
+    const float* norm_w; /* RMSNorm prologue [BL "Fused RMSNorm + BitLinear + Residual Add M=1
+                            Kernel"]: device fp32 [K] (16-byte aligned), or NULL.  The product
+                            then multiplies xn = (x * rinv) * norm_w, rinv = 1 / sqrt(sum_k x^2 / K
+                            + norm_eps) (sum and root in fp64, rinv rounded to fp32, two fp32
+                            multiplies; a zero row with norm_eps = 0 gives xn = 0).  M == 1 only. */
 } ll_gemv_item_ex;
 
 /* Device bytes ll_gemv_plan_init needs for these items ((size_t)-1 for
@@ -262,7 +268,9 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
 /* The same for items with a fused epilogue (ll_gemv_item_ex); plain items
    are LL_EPI_NONE with w2 unused.  An invalid epilogue code, a gated pair
    whose matrices differ in format, N or K, a gated pair with M != 1 or a
-   bias is LL_EINVAL (LL_ESHAPE for the shape mismatch). */
+   bias is LL_EINVAL (LL_ESHAPE for the shape mismatch); so is a norm with
+   M != 1 or a negative or non-finite epsilon.  Items sharing x, K, norm_w
+   and norm_eps share one prepared operand. */
 size_t ll_gemv_plan_bytes_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M);
 ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M,
                                void* mem, size_t bytes, ll_gemv_plan* plan);

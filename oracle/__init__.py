@@ -257,3 +257,14 @@ def relu2_mul(gate, up):
     u = np.asarray(up, np.float64)
     r = np.where(g > 0.0, g, 0.0)
     return (r * r) * u
+
+
+def rmsnorm(x, w, eps):
+    """[BL "Fused RMSNorm + BitLinear + Residual Add M=1 Kernel"] the
+    normalised activation x * rinv * w with rinv = 1 / sqrt(mean(x^2) + eps),
+    in fp64 (a zero row with eps = 0 gives 0: the reading for 0 / 0)."""
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    w = np.asarray(w, np.float64)
+    den = np.mean(x * x, axis=1, keepdims=True) + float(eps)
+    rinv = np.where(den > 0.0, 1.0 / np.sqrt(np.where(den > 0.0, den, 1.0)), 0.0)
+    return x * rinv * w[None, :]

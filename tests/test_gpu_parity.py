@@ -311,6 +311,60 @@ def test_gemv_plan_relu2_mul_and_residual(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["i2s", "tq2"])
+def test_gemv_plan_rmsnorm_prologue(fmt):
+    """RMSNorm prologue of a one-token prepared batch [BL "Fused RMSNorm +
+    BitLinear + Residual Add M=1 Kernel"] against the oracle (xn from
+    oracle.rmsnorm in fp64): two normed products sharing x and the norm (one
+    prepared operand), a plain product of the same x (its own), a normed
+    gated pair, and a zero row with eps = 0 whose output is the residual bit
+    for bit.  Outputs carry the residual add where the page's kernel has it."""
+    t = torch()
+    K, N = 2560, 2560
+    mk = (lambda s, N, K: make_i2s(s, N, K)[2]) if fmt == "i2s" else (lambda s, N, K: make_tq2(s, N, K)[2])
+    up = (lambda p, N, K: L.upload_i2s(p, N, K)) if fmt == "i2s" else (lambda p, N, K: L.upload_tq2(p, N, K))
+    fn = oracle.i2s_gemv_f32 if fmt == "i2s" else oracle.tq2_gemv_f32
+    eps = 1e-5
+    x0 = _x(870, 1, K)
+    x2 = _x(871, 1, K)
+    x3 = np.zeros((1, K), np.float32)
+    g0 = synth.uniform_f32(872, K, 0.5, 1.5)
+    g2 = synth.uniform_f32(873, K, 0.5, 1.5)
+    d = {k: t.from_numpy(v).cuda() for k, v in dict(x0=x0, x2=x2, x3=x3, g0=g0, g2=g2).items()}
+    res = synth.normal_f32(874, 1, N)[0]
+    resd = t.from_numpy(res).cuda()
+    P = {name: mk(880 + i, N if name not in ("gate", "up") else 6912, K)
+         for i, name in enumerate(["q", "k", "v", "o", "gate", "up"])}
+    Wd = {name: up(p, N if name not in ("gate", "up") else 6912, K) for name, p in P.items()}
+    Y = {name: t.empty((1, N if name != "ffn" else 6912), dtype=t.float32, device="cuda")
+         for name in ["q", "k", "v", "o", "ffn"]}
+    items = [L.Normed(Wd["q"], d["x0"], d["g0"], eps, resd, Y["q"]),
+             L.Normed(Wd["k"], d["x0"], d["g0"], eps, None, Y["k"]),
+             (Wd["v"], d["x0"], None, Y["v"]),
+             L.Relu2Mul(Wd["gate"], Wd["up"], d["x2"], Y["ffn"], norm=(d["g2"], eps)),
+             L.Normed(Wd["o"], d["x3"], d["g0"], 0.0, resd, Y["o"])]
+    announce("gemv plan rmsnorm", fmt)
+    plan = L.GemvPlan(items, 1)
+    assert plan.plan.nprep == 4                      # (x0, g0), x0 plain, (x2, g2), (x3, g0, eps 0)
+    plan.run()
+    t.cuda.synchronize()
+    xn0 = oracle.rmsnorm(x0, g0, eps).astype(np.float32)
+    xn2 = oracle.rmsnorm(x2, g2, eps).astype(np.float32)
+    rows = synth.sample_rows(875, N, 48)
+    for name, xin, add in [("q", xn0, res), ("k", xn0, None), ("v", x0, None)]:
+        y_ref, tsum = fn(P[name], N, K, xin, rows)
+        want = y_ref + (0.0 if add is None else add[rows].astype(np.float64)[None, :])
+        got = Y[name].cpu().numpy()[:, rows].astype(np.float64)
+        bound = 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)
+        assert (np.abs(got - want) <= bound).all(), name
+    frows = synth.sample_rows(876, 6912, 48)
+    g_ref, tg = fn(P["gate"], 6912, K, xn2, frows)
+    u_ref, tu = fn(P["up"], 6912, K, xn2, frows)
+    ok, worst = relu2_mul_tol_ok(Y["ffn"].cpu().numpy()[:, frows], g_ref, tg, u_ref, tu)
+    assert ok, "normed gated pair: worst error / bound %.3f" % worst
+    assert np.array_equal(Y["o"].cpu().numpy()[0].view(np.uint32), res.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["i2s", "tq2"])
 def test_gemv_plan_one_token_edges(fmt):
     """One-token prepared batch (the fp4 digit-plane engine) on the cases its
     activation split has to survive: an all-zero token (y = bias exactly),

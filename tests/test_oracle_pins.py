@@ -474,3 +474,22 @@ def test_relu2_mul_scaling_and_products(orc):
     up, _ = orc.i2s_gemv_f32(pu, 1, K, x)
     assert gate[0, 0] == 1.5 and up[0, 0] == 0.5
     assert orc.relu2_mul(gate, up)[0, 0] == 1.5 * 1.5 * 0.5
+
+
+def test_rmsnorm_closed_forms(orc):
+    """[BL "Fused RMSNorm + BitLinear + Residual Add M=1 Kernel"]: with unit
+    weights and eps = 0 the output has mean square 1 exactly in exact
+    arithmetic; (3, 4) has mean square 12.5, so xn = (3, 4) / sqrt(12.5);
+    a positive rescaling of x changes nothing when eps = 0; eps enters under
+    the root (x = (1, 1), eps = 3 gives 1/2); the weights scale elementwise;
+    a zero row gives 0 (the 0/0 reading)."""
+    xn = orc.rmsnorm([[3.0, 4.0]], [1.0, 1.0], 0.0)[0]
+    assert abs(xn[0] - 3.0 / 12.5 ** 0.5) < 1e-15 and abs(xn[1] - 4.0 / 12.5 ** 0.5) < 1e-15
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(3, 256))
+    one = orc.rmsnorm(x, np.ones(256), 0.0)
+    assert np.allclose(np.mean(one * one, axis=1), 1.0, rtol=1e-14, atol=0)
+    assert np.allclose(orc.rmsnorm(7.5 * x, np.ones(256), 0.0), one, rtol=1e-14, atol=0)
+    assert orc.rmsnorm([[1.0, 1.0]], [1.0, 1.0], 3.0).tolist() == [[0.5, 0.5]]
+    assert orc.rmsnorm([[1.0, 1.0]], [2.0, -4.0], 3.0).tolist() == [[1.0, -2.0]]
+    assert orc.rmsnorm([[0.0, 0.0]], [1.0, 1.0], 0.0).tolist() == [[0.0, 0.0]]
