@@ -238,30 +238,38 @@ def gemm_roofline(L, synth, torch, dev, stream, steps, M=512):
 
 
 def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
-    """The same 30-layer decode step with the pages' fused epilogues: O and
-    down add the residual stream (as their bias), gate and up run as one
-    gated pair (y = relu(gate)^2 * up).  Same weights and bytes as the
-    headline step; prepare + product per step, timed with HIP events."""
-    fused = []
+    """The same 30-layer decode step with the pages' fused kernels, as one
+    BitNet layer runs them: Q, K, V from the RMS-normalised input; O and down
+    from their sub-norms plus the residual stream (as the bias); gate and up
+    as one gated pair (y = relu(gate)^2 * up) of the normalised FFN input.
+    Same weights and bytes as the headline step; prepare + product per step,
+    timed with HIP events."""
+    fused, keep = [], []
+    eps = 1e-5
     for layer in range(LAYERS):
         by = {name: items[len(ROLES) * layer + r] for r, (name, _, _, _) in enumerate(ROLES)}
         res_h = [torch.from_numpy(synth.normal_f32(5000 + 2 * layer + j, 1, HIDDEN)).to(dev).reshape(HIDDEN)
                  for j in range(2)]
+        norms = [torch.from_numpy(synth.uniform_f32(6000 + 4 * layer + j, HIDDEN if j != 3 else FFN, 0.5, 1.5)).to(dev)
+                 for j in range(4)]                       # attention input, attention sub, FFN input, FFN sub
+        keep += res_h + norms
         for name in ("q", "k", "v"):
-            fused.append(by[name])
+            W, x, _, y = by[name]
+            fused.append(L.Normed(W, x, norms[0], eps, None, y))
         W, x, _, y = by["o"]
-        fused.append((W, x, res_h[0], y))
+        fused.append(L.Normed(W, x, norms[1], eps, res_h[0], y))
         (Wu, xu, _, yu), (Wg, _, _, _) = by["up"], by["gate"]
-        fused.append(L.Relu2Mul(Wg, Wu, xu, yu))
+        fused.append(L.Relu2Mul(Wg, Wu, xu, yu, norm=(norms[2], eps)))
         W, x, _, y = by["down"]
-        fused.append((W, x, res_h[1], y))
+        fused.append(L.Normed(W, x, norms[3], eps, res_h[1], y))
     plan = L.GemvPlan(fused, 1)
     for _ in range(5):
         plan.run(stream)
     ms = time_events(torch, lambda: plan.run(stream), steps, stream)
     return {"ms_per_step": round(ms, 4), "GB_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
             "products": len(fused), "tiles": int(plan.plan.tiles),
-            "note": "gate+up as 30 gated pairs (relu^2 * up), residual added to O and down"}
+            "note": "RMSNorm prologues on Q/K/V, O, gate/up, down; gate+up as 30 gated pairs (relu^2 * up); "
+                    "residual added to O and down"}
 
 
 def extras_single(L, synth, torch, dev, stream):
