@@ -46,7 +46,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores, published (POP/
 LAYERS = 30
 HIDDEN, FFN = 2560, 6912
 # dominant kernel of a step: i2_s, M = 1, fp4 digit planes on the fp4 matrix cores
-KERNEL = "f4_batch_kernel<1, false>"
+KERNEL = "f4_batch_kernel<1, false, 1>"
 KERNEL_SOURCES = ["binary_bit_weight_amd/csrc/gemv_fp4.hip", "binary_bit_weight_amd/csrc/common.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "f4_batch_i2s_m1_decode30_counters.md")
 # the other half of the metric: the i2_s int8 prefill GEMM at M = 512

@@ -2,9 +2,10 @@
 // host validates every item once and lays out device tables inside the
 // plan memory; every later run costs two launches: one preparing the
 // operands of every distinct activation (into the plan memory), one walking
-// the table of products.  One token (M == 1): fp4 digit planes on the fp4
-// matrix cores (gemv_fp4.hip); 2 <= M <= 16: int8 planes on the int8 matrix
-// cores, up to three tokens per pass (gemv_planes.hip).  An item may carry a
+// the table of products.  Every K <= 2^20: fp4 digit planes on the fp4 matrix
+// cores, all M <= 16 tokens in one pass over the weights (gemv_fp4.hip);
+// larger K: int8 planes on the int8 matrix cores, up to three tokens per
+// pass (gemv_planes.hip).  An item may carry a
 // fused epilogue: a gated pair (gate and up of one activation, y = relu(g)^2
 // * u, one token) runs as workgroups of 64 rows of both matrices.
 #include <hip/hip_runtime_api.h>
@@ -114,7 +115,8 @@ ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, 
         L.tiles += (items[i].w.N + rows - 1) / rows;              // (logical) workgroups
     }
     const size_t prob_sz = L.f4 ? llk::f4_prob_bytes() : llk::planes_prob_bytes();
-    const size_t prep_sz = L.f4 ? llk::f4_prep_bytes() : llk::planes_prep_bytes();
+    // fp4 engine: one preparation entry per token of each distinct activation
+    const size_t prep_sz = L.f4 ? llk::f4_prep_bytes() * size_t(M) : llk::planes_prep_bytes();
     L.prob_off = 0;
     L.prep_off = round_up(size_t(count) * prob_sz, 256);
     L.map_off = round_up(L.prep_off + L.xs.size() * prep_sz, 256);
@@ -122,7 +124,7 @@ ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, 
     size_t at = L.frag_off;
     for (size_t j = 0; j < L.xs.size(); ++j) {
         L.frag_at.push_back(at);
-        const size_t bytes = L.f4 ? llk::f4_operand_bytes(L.xk[j]) : llk::planes_operand_bytes(M, L.xk[j]);
+        const size_t bytes = L.f4 ? llk::f4_operand_bytes(M, L.xk[j]) : llk::planes_operand_bytes(M, L.xk[j]);
         at = round_up(at + bytes, 256);
     }
     L.total = at;
@@ -187,7 +189,7 @@ ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int3
         if (L.f4)
             llk::fill_f4_prob(host.data() + L.prob_off + size_t(i) * llk::f4_prob_bytes(), it.w.codes, it.w.scales,
                               ops, it.bias, it.y, it.w.N, it.w.K, first, pair ? it.w2.codes : nullptr,
-                              pair ? it.w2.scales : nullptr);
+                              pair ? it.w2.scales : nullptr, M);
         else
             llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
                                   it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
@@ -199,8 +201,10 @@ ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int3
     for (size_t j = 0; j < L.xs.size(); ++j) {
         const float* x = static_cast<const float*>(L.xs[j]);
         if (L.f4)
-            llk::fill_f4_prep(host.data() + L.prep_off + j * llk::f4_prep_bytes(), x, base + L.frag_at[j], L.xk[j],
-                              L.xnw[j], L.xeps[j]);
+            for (int64_t m = 0; m < M; ++m)
+                llk::fill_f4_prep(host.data() + L.prep_off + (j * size_t(M) + size_t(m)) * llk::f4_prep_bytes(),
+                                  x + m * L.xk[j], base + L.frag_at[j] + m * llk::f4_op_stride(L.xk[j]), L.xk[j],
+                                  L.xnw[j], L.xeps[j]);
         else
             llk::fill_planes_prep(host.data() + L.prep_off + j * llk::planes_prep_bytes(), x, base + L.frag_at[j],
                                   L.xk[j]);
@@ -246,7 +250,8 @@ ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (llk::f4_engine(plan->M, plan->kmax))
-        return hip_status(llk::launch_f4_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->kmax, s),
+        return hip_status(llk::launch_f4_batch_prep(plan->prep_table, int(plan->prep_entries), plan->fmt, plan->kmax,
+                                                    s),
                           "ll_gemv_plan_prepare");
     return hip_status(llk::launch_planes_batch_prep(plan->prep_table, plan->nprep, plan->fmt, plan->M, s),
                       "ll_gemv_plan_prepare");
@@ -258,7 +263,7 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (llk::f4_engine(plan->M, plan->kmax))
         return hip_status(llk::launch_f4_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->tiles,
-                                                       plan->kmax, plan->epilogues != 0, s),
+                                                       plan->kmax, plan->epilogues != 0, plan->M, s),
                           "ll_gemv_plan_product");
     return hip_status(llk::launch_planes_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->M,
                                                        plan->tiles, s),

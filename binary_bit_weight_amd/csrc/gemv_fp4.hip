@@ -113,6 +113,8 @@ struct F4Prob {
     const uint8_t* codes2;
     const uint16_t* scales2;
     int32_t pair;
+    int32_t M;                    // tokens (1 .. 16): token m's digits at ops + m opstride, y row m
+    int64_t opstride;
 };
 
 // ---------------------------------------------------------------- digits
@@ -292,32 +294,55 @@ __device__ __forceinline__ f32x4 mfma_f4(i32x4 a, i32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, 127, 0, 127);
 }
 
-// LDS: two activation windows (digits of 1024 k), then one weight tile per wave.
-__host__ __device__ constexpr int64_t prod_lds_bytes() { return 2 * kAWin + kWaves * kWTile; }
+// Shapes per token count MT (1, 2, 4, 8): every token is its own 16-row
+// MFMA block (twelve digit planes, four rows of weight 0), so one decoded
+// weight tile feeds MT blocks.  KG chunks of 256 k per pipeline group: 4
+// (weight loads of 4 rows x 256 bytes) while the activation windows of all
+// tokens fit beside the tiles, else 2 (8 rows x 128 bytes).
+template <int MT>
+struct F4Cfg {
+    static constexpr int KG = MT <= 2 ? 4 : 2;
+    static constexpr int WStride = KG * 64 + 16;                 // padded LDS tile row
+    static constexpr int WTile = 16 * kCB * WStride;             // one wave's tile
+    static constexpr int AWin = MT * KG * kChunkBytes;           // one group's digits, all tokens
+    static constexpr int APer = (AWin / 16 + kThreads - 1) / kThreads;   // 16-byte window pieces per thread
+    static constexpr int LPR = KG * 4;                           // lanes per row in a weight load
+    static constexpr int RPI = 64 / LPR;                         // rows per weight load
+    static constexpr int NLD = kWaveRows / RPI;                  // weight loads per wave and group
+    static constexpr int64_t Lds = 2 * int64_t(AWin) + int64_t(kWaves) * WTile;
+};
+static_assert(F4Cfg<1>::AWin == kAWin && F4Cfg<1>::WTile == kWTile, "one-token shapes");
 
-template <int FMT>
+// LDS: two activation windows, then one weight tile per wave.
+__host__ __device__ constexpr int64_t prod_lds_bytes() { return F4Cfg<1>::Lds; }
+
+template <int FMT, int MT>
 struct Regs {
-    i32x4 w[4 * kCB];             // load i of column block cb: rows 16 cb + 4 i + q, 16 bytes at 16 nl
-    i32x4 a[kAPer];               // pieces tid + kThreads p of the activation window
-    uint16_t sc[kGroup * kCB];    // TQ2_0: scale of this lane's row per chunk and column block
+    i32x4 w[F4Cfg<MT>::NLD];                 // load i: row RPI i + lane / LPR, 16 bytes at 16 (lane % LPR)
+    i32x4 a[F4Cfg<MT>::APer];                // pieces tid + kThreads p of the activation window
+    uint16_t sc[F4Cfg<MT>::KG * kCB];        // TQ2_0: scale of this lane's row per chunk and column block
 };
 
-// Returns this lane's result: lane l holds row row0 + l (column block l / 16,
-// meaningful for l < 16 kCB and rows < N), bias not added.
-template <int FMT>
-__device__ __forceinline__ float f4_rows(const F4Prob& P, const uint8_t* __restrict__ codes,
-                                         const uint16_t* __restrict__ scales, int64_t row0, int tid, char* abuf,
-                                         char* wtile) {
+// out[m] = this lane's result for token m0 + m: lane l holds row row0 + l
+// (column block l / 16, meaningful for l < 16 kCB, rows < N and m0 + m <
+// P.M), bias not added.  Token t's digits are at P.ops + t P.opstride.
+template <int FMT, int MT>
+__device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restrict__ codes,
+                                        const uint16_t* __restrict__ scales, int64_t row0, int m0, int tid, char* abuf,
+                                        char* wtile, float (&out)[MT]) {
+    using C = F4Cfg<MT>;
+    constexpr int KG = C::KG;
     const int lane = tid & 63, nl = lane & 15, q = lane >> 4;
     const int64_t N = P.N, K = P.K, nch = nchunks(K);
     const uint32_t rowbytes = uint32_t(K / 4);
-    const int ngr = int((nch + kGroup - 1) / kGroup);
+    const int ngr = int((nch + KG - 1) / KG);
     const int64_t abytes = nch * kChunkBytes;
-    // loads: lane (q, nl) takes row 16 cb + 4 i + q, bytes 256 g + 16 nl of group g
-    const uint8_t* lrow[4 * kCB];
+    const int lr = lane / C::LPR, lp = lane % C::LPR;
+    // loads: lane takes row RPI i + lr, bytes KG 64 g + 16 lp of group g
+    const uint8_t* lrow[C::NLD];
 #pragma unroll
-    for (int j = 0; j < 4 * kCB; ++j) {
-        int64_t r = row0 + 4 * j + q;
+    for (int j = 0; j < C::NLD; ++j) {
+        int64_t r = row0 + C::RPI * j + lr;
         r = r < N ? r : N - 1;                             // clamped rows are not stored
         lrow[j] = codes + r * int64_t(rowbytes);
     }
@@ -330,82 +355,128 @@ __device__ __forceinline__ float f4_rows(const F4Prob& P, const uint8_t* __restr
     }
     // Every load is issued by every lane from an in-bounds (clamped) address;
     // bytes past the end of a row are zeroed when stored to LDS.
-    auto load = [&](int g, Regs<FMT>& r) {
+    auto load = [&](int g, Regs<FMT, MT>& r) {
         const int gc = g < ngr ? g : ngr - 1;
-        const uint32_t off = uint32_t(gc) * (kGroup * 64) + 16 * nl;
+        const uint32_t off = uint32_t(gc) * (KG * 64) + 16 * lp;
         const uint32_t offc = off < rowbytes ? off : rowbytes - 16;
 #pragma unroll
-        for (int j = 0; j < 4 * kCB; ++j) r.w[j] = LL_F4_NT ? ld16_stream(lrow[j] + offc) : ld16(lrow[j] + offc);
+        for (int j = 0; j < C::NLD; ++j) r.w[j] = LL_F4_NT ? ld16_stream(lrow[j] + offc) : ld16(lrow[j] + offc);
 #pragma unroll
-        for (int p = 0; p < kAPer; ++p) {
-            int64_t o = int64_t(gc) * kAWin + 16 * (tid + kThreads * p);
-            o = o < abytes ? o : abytes - 16;
-            r.a[p] = ld16(P.ops + o);
+        for (int p = 0; p < C::APer; ++p) {
+            const int pc = tid + kThreads * p;             // piece of the window: token pc / (KG 96)
+            if constexpr (MT == 1) {
+                int64_t o = int64_t(gc) * C::AWin + 16 * pc;
+                o = o < abytes ? o : abytes - 16;
+                r.a[p] = ld16(P.ops + o);
+            } else {
+                int m = m0 + pc / (KG * (kChunkBytes / 16));
+                const int within = pc % (KG * (kChunkBytes / 16));
+                m = m < P.M ? m : P.M - 1;                 // tokens past M: any in-bounds bytes (unused)
+                int64_t o = int64_t(gc) * (KG * kChunkBytes) + 16 * within;
+                o = o < abytes ? o : abytes - 16;
+                r.a[p] = ld16(P.ops + int64_t(m) * P.opstride + o);
+            }
         }
         if (FMT == 2) {
 #pragma unroll
-            for (int c = 0; c < kGroup; ++c) {
-                int64_t b = int64_t(gc) * kGroup + c;
+            for (int c = 0; c < KG; ++c) {
+                int64_t b = int64_t(gc) * KG + c;
                 b = b < nch ? b : nch - 1;
 #pragma unroll
                 for (int cb = 0; cb < kCB; ++cb) r.sc[c * kCB + cb] = ld2(srow[cb] + b);
             }
         }
     };
-    uint16_t csc[kGroup * kCB];
-    auto store = [&](int g, const Regs<FMT>& r) {
-        const bool ok = uint32_t(g) * (kGroup * 64) + 16 * nl < rowbytes;
+    // scales of the group being multiplied: chunk c of column block cb in bits
+    // 16 c of cscp[cb] (a runtime shift, not a runtime index into an array)
+    uint64_t cscp[kCB];
+    auto store = [&](int g, const Regs<FMT, MT>& r) {
+        const bool ok = uint32_t(g) * (KG * 64) + 16 * lp < rowbytes;
 #pragma unroll
-        for (int j = 0; j < 4 * kCB; ++j)
-            *reinterpret_cast<i32x4*>(wtile + (4 * j + q) * kWStride + 16 * nl) = ok ? r.w[j] : i32x4{0, 0, 0, 0};
+        for (int j = 0; j < C::NLD; ++j)
+            *reinterpret_cast<i32x4*>(wtile + (C::RPI * j + lr) * C::WStride + 16 * lp) = ok ? r.w[j] : i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int p = 0; p < kAPer; ++p) {
-            const int o = 16 * (tid + kThreads * p);
-            const bool aok = int64_t(g) * kAWin + o < abytes;      // digits past the row end are zero
-            if (kAPer * kThreads * 16 == kAWin || o < kAWin)
-                *reinterpret_cast<i32x4*>(abuf + (g & 1) * kAWin + o) = aok ? r.a[p] : i32x4{0, 0, 0, 0};
+        for (int p = 0; p < C::APer; ++p) {
+            const int pc = tid + kThreads * p;
+            const int within = pc % (KG * (kChunkBytes / 16));
+            const bool aok = int64_t(g) * (KG * kChunkBytes) + 16 * (MT == 1 ? pc : within) < abytes;   // digits past the row end are zero
+            if (C::APer * kThreads * 16 == C::AWin || pc < C::AWin / 16)
+                *reinterpret_cast<i32x4*>(abuf + (g & 1) * C::AWin + 16 * pc) = aok ? r.a[p] : i32x4{0, 0, 0, 0};
         }
         if (FMT == 2)
 #pragma unroll
-            for (int i = 0; i < kGroup * kCB; ++i) csc[i] = r.sc[i];
-    };
-
-    f32x4 acc[kCB];
+            for (int cb = 0; cb < kCB; ++cb) {
+                uint64_t v = 0;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int c = 0; c < KG; ++c) v |= uint64_t(r.sc[c * kCB + cb]) << (16 * c);
+                cscp[cb] = v;
+            }
+    };
+    auto scale_of = [&](int c, int cb) { return half_bits_to_float(uint16_t(cscp[cb] >> (16 * c))); };
+
+    f32x4 acc[MT][kCB];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) acc[m][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int arow = q * kQuarterBytes + (nl < kPl ? nl : kPl - 1) * kPlRowBytes;
 
+    auto decode = [&](const i32x4& u4, i32x4& b0, i32x4& b1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t u = uint32_t(u4[i]);
+            if (FMT == 1) {
+                b0[i] = int(u & 0x33333333u);
+                b1[i] = int((u >> 2) & 0x33333333u);
+            } else {
+                b0[i] = int((u & 0x11111111u) | ((u & 0x22222222u) << 2));
+                b1[i] = int(((u >> 2) & 0x11111111u) | (u & 0x88888888u));
+            }
+        }
+    };
+    auto mma = [&](f32x4& a, const i32x4& a0, const i32x4& a1, const i32x4& b0, const i32x4& b1, float sb) {
+        if (FMT == 1) {
+            a = mfma_f4(a0, b0, a);
+            a = mfma_f4(a1, b1, a);
+        } else {
+            f32x4 blk = mfma_f4(a0, b0, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            blk = mfma_f4(a1, b1, blk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = fmaf(sb, blk[i], a[i]);
+        }
+    };
     auto compute = [&](int g) {
-        const int cn = nch - int64_t(g) * kGroup < kGroup ? int(nch - int64_t(g) * kGroup) : kGroup;
+        const int cn = nch - int64_t(g) * KG < KG ? int(nch - int64_t(g) * KG) : KG;
 #pragma unroll LL_F4_CUNROLL
         for (int c = 0; c < cn; ++c) {                  // the last group may hold fewer chunks
-            const char* ap = abuf + (g & 1) * kAWin + arow + c * kChunkBytes;
-            const i32x4 a0 = *reinterpret_cast<const i32x4*>(ap);
-            const i32x4 a1 = *reinterpret_cast<const i32x4*>(ap + kStepBytes);
+            const char* ap = abuf + (g & 1) * C::AWin + arow + c * kChunkBytes;
+            if constexpr (MT == 1) {
+                const i32x4 a0 = *reinterpret_cast<const i32x4*>(ap);
+                const i32x4 a1 = *reinterpret_cast<const i32x4*>(ap + kStepBytes);
 #pragma unroll
-            for (int cb = 0; cb < kCB; ++cb) {
-                const i32x4 u4 = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * kWStride + 64 * c + 16 * q);
-                i32x4 b0, b1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t u = uint32_t(u4[i]);
-                    if (FMT == 1) {
-                        b0[i] = int(u & 0x33333333u);
-                        b1[i] = int((u >> 2) & 0x33333333u);
-                    } else {
-                        b0[i] = int((u & 0x11111111u) | ((u & 0x22222222u) << 2));
-                        b1[i] = int(((u >> 2) & 0x11111111u) | (u & 0x88888888u));
-                    }
+                for (int cb = 0; cb < kCB; ++cb) {
+                    const i32x4 u4 = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * C::WStride + 64 * c + 16 * q);
+                    i32x4 b0, b1;
+                    decode(u4, b0, b1);
+                    mma(acc[0][cb], a0, a1, b0, b1, FMT == 2 ? scale_of(c, cb) : 0.0f);
                 }
-                if (FMT == 1) {
-                    acc[cb] = mfma_f4(a0, b0, acc[cb]);
-                    acc[cb] = mfma_f4(a1, b1, acc[cb]);
-                } else {
-                    f32x4 blk = mfma_f4(a0, b0, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-                    blk = mfma_f4(a1, b1, blk);
-                    const float sb = half_bits_to_float(csc[c * kCB + cb]);
+            } else {
+                // the weight tile is decoded once and multiplied by every token's block
+                i32x4 b0[kCB], b1[kCB];
+                float sb[kCB];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[cb][i] = fmaf(sb, blk[i], acc[cb][i]);
+                for (int cb = 0; cb < kCB; ++cb) {
+                    const i32x4 u4 = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * C::WStride + 64 * c + 16 * q);
+                    decode(u4, b0[cb], b1[cb]);
+                    sb[cb] = FMT == 2 ? scale_of(c, cb) : 0.0f;
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const char* am = ap + m * (KG * kChunkBytes);
+                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(am);
+                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(am + kStepBytes);
+#pragma unroll
+                    for (int cb = 0; cb < kCB; ++cb) mma(acc[m][cb], a0, a1, b0[cb], b1[cb], sb[cb]);
                 }
             }
         }
@@ -416,7 +487,7 @@ __device__ __forceinline__ float f4_rows(const F4Prob& P, const uint8_t* __restr
     // g + 2 is being fetched.  The weight tile is private to the wave and its
     // LDS accesses execute in program order, so it is rewritten after the
     // multiply without a barrier; the barrier orders the shared windows.
-    Regs<FMT> r0, r1;
+    Regs<FMT, MT> r0, r1;
     load(0, r0);
     load(1, r1);
     store(0, r0);
@@ -438,59 +509,83 @@ __device__ __forceinline__ float f4_rows(const F4Prob& P, const uint8_t* __restr
     }
     if (g < ngr) compute(g);                           // odd group count: the last one is in the tile
 
-    // Epilogue: plane 4q + i of this lane's column weighted by 2 * 8^(11 - r)
-    // (the 2 undoes the half-valued weights), summed over the quarters.
-    const uint8_t* meta = P.ops + meta_off(K);
-    const int E = ld32(meta);
-    double tot[kCB];
+    // Epilogue per token: plane 4q + i of this lane's column weighted by
+    // 2 * 8^(11 - r) (the 2 undoes the half-valued weights), summed over the
+    // quarters.
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-        double t = 0.0;
+    for (int m = 0; m < MT; ++m) {
+        const int mc = m0 + m < P.M ? m0 + m : P.M - 1;
+        const uint8_t* meta = P.ops + int64_t(mc) * P.opstride + meta_off(K);
+        const int E = ld32(meta);
+        double tot[kCB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * q + i;
-            const double wgt = r < kPl ? ldexp(1.0, 1 + 3 * (kPl - 1 - r)) : 0.0;
-            t = fma(double(acc[cb][i]), wgt, t);
+        for (int cb = 0; cb < kCB; ++cb) {
+            double t = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q + i;
+                const double wgt = r < kPl ? ldexp(1.0, 1 + 3 * (kPl - 1 - r)) : 0.0;
+                t = fma(double(acc[m][cb][i]), wgt, t);
+            }
+            t += __shfl_xor(t, 16, kWave);
+            t += __shfl_xor(t, 32, kWave);
+            tot[cb] = t;
         }
-        t += __shfl_xor(t, 16, kWave);
-        t += __shfl_xor(t, 32, kWave);
-        tot[cb] = t;
-    }
-    // lane l stores row row0 + l of column block l / 16
-    double t = tot[0];
+        // lane l holds row row0 + l of column block l / 16
+        double t = tot[0];
 #pragma unroll
-    for (int cb = 1; cb < kCB; ++cb)
-        if (q == cb) t = tot[cb];
-    const double unit = ldexp(1.0, E - 34);
-    double yv;
-    if (FMT == 1) {
-        long long xs = 0;
-        for (int64_t sl = 0; sl < nslices(K); ++sl)
-            xs += *(__attribute__((address_space(1))) const long long*)(meta + 8 + 8 * sl);
-        const float scale = *(const __attribute__((address_space(1))) float*)(codes + N * int64_t(rowbytes));
-        yv = double(scale) * ((t - double(xs)) * unit);
-    } else {
-        yv = t * unit;                                      // block scales are inside t
+        for (int cb = 1; cb < kCB; ++cb)
+            if (q == cb) t = tot[cb];
+        const double unit = ldexp(1.0, E - 34);
+        double yv;
+        if (FMT == 1) {
+            long long xs = 0;
+            for (int64_t sl = 0; sl < nslices(K); ++sl)
+                xs += *(__attribute__((address_space(1))) const long long*)(meta + 8 + 8 * sl);
+            const float scale = *(const __attribute__((address_space(1))) float*)(codes + N * int64_t(rowbytes));
+            yv = double(scale) * ((t - double(xs)) * unit);
+        } else {
+            yv = t * unit;                                  // block scales are inside t
+        }
+        out[m] = float(yv);
     }
-    return float(yv);
+}
+
+// Waves per SIMD the register allocation aims at, per format and token count
+// (the LDS of F4Cfg<MT> allows 3, 2, 3, 2 workgroups per CU).  One-token
+// TQ2_0 needs more registers for its block scales: at three waves it would
+// spill inside the main loop (measured 14% slower); with four tokens three
+// waves still measured faster despite a small spill.
+#ifndef LL_F4_OCC
+#define LL_F4_OCC 3
+#endif
+#ifndef LL_F4_OCC_TQ2
+#define LL_F4_OCC_TQ2 2
+#endif
+__host__ __device__ constexpr int f4_occ(int FMT, int MT) {
+    return MT == 8 || MT == 2 ? 2 : MT == 4 ? 3 : FMT == 2 ? LL_F4_OCC_TQ2 : LL_F4_OCC;
 }
 
 // grid: 8 * ceil(T / 8) workgroups for T logical ones; hardware workgroup w
 // runs on XCD w % 8, and takes logical index (w % 8) * T8 + w / 8.
-#ifndef LL_F4_OCC
-#define LL_F4_OCC 3                                    // waves per SIMD the register allocation aims at
-#endif
-template <int FMT, bool PAIRS>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LL_F4_OCC))) f4_batch_kernel(const F4Prob* __restrict__ tab,
-                                                            const int32_t* __restrict__ map, int64_t T) {
+// passes > 1 (M > MT): logical workgroup L multiplies tile L / passes for the
+// tokens [MT (L % passes), MT (L % passes + 1)); the passes of one tile are
+// consecutive logical workgroups, so they run on one XCD and the later ones
+// find the weights in its L2.
+template <int FMT, bool PAIRS, int MT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(f4_occ(FMT, MT)))) f4_batch_kernel(
+    const F4Prob* __restrict__ tab, const int32_t* __restrict__ map, int64_t T, int passes) {
+    static_assert(!PAIRS || MT == 1, "gated pairs are one-token items");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t w = blockIdx.x, T8 = (T + 7) / 8;
-    const int64_t L = (w % 8) * T8 + w / 8;
-    if (L >= T) return;                                    // whole workgroup
+    const int64_t LP = (w % 8) * T8 + w / 8;
+    if (LP >= T) return;                                   // whole workgroup
+    const int64_t L = MT == 1 ? LP : LP / passes;          // one token: one pass
+    const int m0 = MT == 1 ? 0 : MT * int(LP % passes);
     const F4Prob& P = tab[ld32(map + L)];
     const int tid = int(threadIdx.x), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: selects stay scalar
-    char* wtile = lds + 2 * kAWin + wave * kWTile;
+    char* wtile = lds + 2 * F4Cfg<MT>::AWin + wave * F4Cfg<MT>::WTile;
     // Gated pair (only in launches whose table holds one): waves 0, 1
     // multiply 64 gate rows, waves 2, 3 the same rows of the up matrix, all
     // from one activation window.  Waves past the last row still take part
@@ -499,23 +594,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(L
     const int half = pair ? wave >> 1 : 0;
     const int64_t row0 = pair ? (L - P.wg0) * (kWgRows / 2) + (wave & 1) * kWaveRows
                               : (L - P.wg0) * kWgRows + wave * kWaveRows;
-    const float v = f4_rows<FMT>(P, half ? P.codes2 : P.codes, half ? P.scales2 : P.scales, row0, tid, lds, wtile);
+    float v[MT];
+    f4_rows<FMT, MT>(P, half ? P.codes2 : P.codes, half ? P.scales2 : P.scales, row0, m0, tid, lds, wtile, v);
     const int64_t row = row0 + lane;                       // = row0 + 16 cb + nl for cb = q
     if (!pair) {
         // [BL "Fused BitLinear + Residual Add Kernel"]: a residual passed as the bias is added last
-        float out = v;
-        if (P.bias) out = __fadd_rn(out, P.bias[row < P.N ? row : P.N - 1]);
-        if (lane < kWaveRows && row < P.N) P.y[row] = out;
+        const float bv = P.bias ? P.bias[row < P.N ? row : P.N - 1] : 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float out = v[m];
+            if (P.bias) out = __fadd_rn(out, bv);
+            if (m0 + m < P.M && lane < kWaveRows && row < P.N) P.y[int64_t(m0 + m) * P.N + row] = out;
+        }
         return;
     }
     // the up results reach the gate waves through LDS
     __syncthreads();                                       // every wave is done with the operand buffers
     float* xch = reinterpret_cast<float*>(lds);
-    if (half == 1 && lane < kWaveRows) xch[(wave & 1) * kWaveRows + lane] = v;
+    if (half == 1 && lane < kWaveRows) xch[(wave & 1) * kWaveRows + lane] = v[0];
     __syncthreads();
     if (half == 0 && lane < kWaveRows && row < P.N) {
         const float u = xch[(wave & 1) * kWaveRows + lane];
-        const float r = v > 0.0f ? v : 0.0f;
+        const float r = v[0] > 0.0f ? v[0] : 0.0f;
         P.y[row] = __fmul_rn(__fmul_rn(r, r), u);
     }
 }
@@ -524,15 +624,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(L
 
 namespace llk {
 
-bool f4_engine(int64_t M, int64_t kmax) { return M == 1 && kmax <= kMaxK; }
-size_t f4_operand_bytes(int64_t K) { return size_t(op_bytes(K)); }
+bool f4_engine(int64_t M, int64_t kmax) { return M >= 1 && M <= 16 && kmax <= kMaxK; }
+int64_t f4_op_stride(int64_t K) { return (op_bytes(K) + 255) / 256 * 256; }
+size_t f4_operand_bytes(int64_t M, int64_t K) { return size_t(M * f4_op_stride(K)); }
 int64_t f4_batch_rows(bool pair) { return pair ? kWgRows / 2 : kWgRows; }
 size_t f4_prob_bytes() { return sizeof(F4Prob); }
 size_t f4_prep_bytes() { return sizeof(F4Prep); }
 int64_t f4_grid(int64_t T) { return 8 * ((T + 7) / 8); }
 
 void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
-                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2) {
+                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2, int64_t M) {
     F4Prob p;
     p.codes2 = static_cast<const uint8_t*>(codes2);
     p.scales2 = static_cast<const uint16_t*>(scales2);
@@ -545,6 +646,8 @@ void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* 
     p.N = N;
     p.K = K;
     p.wg0 = wg0;
+    p.M = int32_t(M);
+    p.opstride = f4_op_stride(K);
     *static_cast<F4Prob*>(dst) = p;
 }
 
@@ -568,23 +671,33 @@ hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int6
     return hipGetLastError();
 }
 
-template <int FMT, bool PAIRS>
-hipError_t launch_f4_product(const F4Prob* t, const int32_t* m, int64_t T, hipStream_t stream) {
-    const dim3 grid{unsigned(f4_grid(T))}, block{unsigned(kThreads)};
-    const size_t lds = size_t(prod_lds_bytes());
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(f4_batch_kernel<FMT, PAIRS>), lds);
+template <int FMT, bool PAIRS, int MT>
+hipError_t launch_f4_product(const F4Prob* t, const int32_t* m, int64_t T, int passes, hipStream_t stream) {
+    const dim3 grid{unsigned(f4_grid(T * passes))}, block{unsigned(kThreads)};
+    const size_t lds = size_t(F4Cfg<MT>::Lds);
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(f4_batch_kernel<FMT, PAIRS, MT>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((f4_batch_kernel<FMT, PAIRS>), grid, block, lds, stream, t, m, T);
+    hipLaunchKernelGGL((f4_batch_kernel<FMT, PAIRS, MT>), grid, block, lds, stream, t, m, T * passes, passes);
     return hipGetLastError();
 }
 
+// M = 9 .. 16 runs as two passes of eight tokens (measured faster than one
+// pass of sixteen, which leaves one wave per SIMD).
+template <int FMT>
+hipError_t launch_f4_fmt(const F4Prob* t, const int32_t* m, int64_t T, bool pairs, int64_t M, hipStream_t stream) {
+    if (M == 1)
+        return pairs ? launch_f4_product<FMT, true, 1>(t, m, T, 1, stream) : launch_f4_product<FMT, false, 1>(t, m, T, 1, stream);
+    if (M == 2) return launch_f4_product<FMT, false, 2>(t, m, T, 1, stream);
+    if (M <= 4) return launch_f4_product<FMT, false, 4>(t, m, T, 1, stream);
+    return launch_f4_product<FMT, false, 8>(t, m, T, M <= 8 ? 1 : 2, stream);
+}
+
 hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
-                                   bool pairs, hipStream_t stream) {
+                                   bool pairs, int64_t M, hipStream_t stream) {
     (void)kmax;
     const F4Prob* t = static_cast<const F4Prob*>(prob_table);
     const int32_t* m = static_cast<const int32_t*>(map);
-    if (fmt == 1) return pairs ? launch_f4_product<1, true>(t, m, T, stream) : launch_f4_product<1, false>(t, m, T, stream);
-    return pairs ? launch_f4_product<2, true>(t, m, T, stream) : launch_f4_product<2, false>(t, m, T, stream);
+    return fmt == 1 ? launch_f4_fmt<1>(t, m, T, pairs, M, stream) : launch_f4_fmt<2>(t, m, T, pairs, M, stream);
 }
 
 }  // namespace llk

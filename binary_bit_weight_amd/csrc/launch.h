@@ -62,24 +62,26 @@ hipError_t launch_planes_batch_product(const void* prob_table, const void* map, 
 }  // namespace llk
 
 namespace llk {
-// fp32-activation single-token product on the fp4 matrix cores (gemv_fp4.hip),
+// fp32-activation decode product on the fp4 matrix cores (gemv_fp4.hip),
 // formats i2_s (fmt 1) and TQ2_0 (fmt 2): activations as twelve base-8 digit
-// planes (one preparation launch), weights fed to the MFMAs straight from
-// registers.  Used by prepared batches with M == 1 and every K <= 2^20.
-bool f4_engine(int64_t M, int64_t kmax);
-size_t f4_operand_bytes(int64_t K);                  // prepared digits of one activation
+// planes per token (one preparation launch), weights fed to the MFMAs straight
+// from registers, one 16-row MFMA block per token.  Used by prepared batches
+// with M <= 16 and every K <= 2^20.
+bool f4_engine(int64_t M, int64_t kmax);             // 1 <= M <= 16, every K <= 2^20
+int64_t f4_op_stride(int64_t K);                     // bytes between two tokens' prepared digits
+size_t f4_operand_bytes(int64_t M, int64_t K);       // prepared digits of one activation (M tokens)
 int64_t f4_batch_rows(bool pair);                   // output rows per workgroup (a gated pair: rows of both)
 size_t f4_prob_bytes();
 size_t f4_prep_bytes();
 int64_t f4_grid(int64_t T);                         // workgroups launched for T logical ones
-// codes2 / scales2: the up weights of a gated pair (codes / scales the gate), or NULL
+// codes2 / scales2: the up weights of a gated pair (codes / scales the gate), or NULL;
+// ops: token 0's digits, token m's at ops + m f4_op_stride(K)
 void fill_f4_prob(void* dst, const void* codes, const void* scales, const void* ops, const float* bias, float* y,
-                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2);
-// norm_w: the RMSNorm weights of an activation normalised in the preparation, or NULL
+                  int64_t N, int64_t K, int64_t wg0, const void* codes2, const void* scales2, int64_t M);
+// one entry per token; norm_w: the RMSNorm weights of an activation normalised in the preparation, or NULL
 void fill_f4_prep(void* dst, const float* x, void* ops, int64_t K, const float* norm_w, float eps);
-hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int64_t kmax, hipStream_t stream);
-// map: int32 [T], the product of each logical workgroup
-// pairs: the table holds gated pairs (a kernel variant with their epilogue)
+hipError_t launch_f4_batch_prep(const void* prep_table, int nentries, int fmt, int64_t kmax, hipStream_t stream);
+// map: int32 [T], the product of each logical workgroup; pairs: the table holds gated pairs
 hipError_t launch_f4_batch_product(const void* prob_table, const void* map, int fmt, int64_t T, int64_t kmax,
-                                   bool pairs, hipStream_t stream);
+                                   bool pairs, int64_t M, hipStream_t stream);
 }  // namespace llk

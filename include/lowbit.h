@@ -204,10 +204,11 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
    walks a device-resident table of all products.  All items share act,
    format and M (1 <= M <= 16); N and K may differ.  Only act == LL_ACT_F32
    with i2_s or TQ2_0 is supported.  Items with the same x pointer and K
-   share one activation layout: for M == 1 (and every K <= 2^20) twelve
-   balanced base-8 fp4 digit planes per token, multiplied on the fp4 matrix
-   cores (y within the same tolerance as ll_bitlinear_gemv); otherwise the
-   int8 planes of ll_bitlinear_gemv. */
+   share one activation layout: with every K <= 2^20, twelve balanced base-8
+   fp4 digit planes per token, multiplied on the fp4 matrix cores with all M
+   tokens in one pass over the weights (two passes for M > 8; y within the
+   same tolerance as ll_bitlinear_gemv); otherwise the int8 planes of
+   ll_bitlinear_gemv. */
 typedef struct {
     ll_weights w;        /* packed weights (device pointers, as for ll_bitlinear_gemv) */
     const void* x;       /* device fp32 [M, K] */

@@ -219,7 +219,8 @@ def test_i2s_gemv_i8_matches_gemm():
 
 # ------------------------------------------------------------------ prepared batch
 @pytest.mark.parametrize("fmt,M,big", [("i2s", 1, False), ("i2s", 1, True), ("i2s", 2, False), ("i2s", 4, False),
-                                      ("tq2", 1, False), ("tq2", 1, True), ("tq2", 3, False), ("tq2", 16, False)])
+                                      ("i2s", 5, False), ("i2s", 16, True), ("tq2", 1, False), ("tq2", 1, True),
+                                      ("tq2", 3, False), ("tq2", 8, False), ("tq2", 16, False)])
 def test_gemv_plan_matches_oracle(fmt, M, big):
     """A prepared batch of products with mixed N and K (some sharing x) against
     the oracle, row by row, run twice (second run with new x contents).  With
