@@ -24,8 +24,12 @@ launches between HIP events), int8 TOPS against the dense int8 peak, with its
 HBM traffic and matrix-core busy fraction from its own committed counter
 summary when that matches the current source.
 
+"roofline_w1a8" reports the W1A8 LM head (248320 x 5120, G = 128, M = 1) the
+same way, whole calls over rotating weight copies.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
        python bench.py --gemm-only      (the GEMM roofline alone)
+       python bench.py --w1-only        (the W1A8 LM-head line alone)
        python bench.py --copy-probe     (a plain 256 MiB device copy, to
                                          calibrate rocprofv3 byte counters)
 """
@@ -54,6 +58,11 @@ GEMM_KERNEL = "gemm_i8_i2s_kernel"
 GEMM_SOURCES = ["binary_bit_weight_amd/csrc/gemm_i8.hip", "binary_bit_weight_amd/csrc/common.h"]
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_i8_i2s_m512_counters.md")
 GEMM_SHAPES = [(6912, 2560), (2560, 6912)]    # (N, K) at M = 512; the first is the roofline line
+# W1A8 (binary weights, int8 activations): the LM head at hidden 5120, G = 128
+W1_KERNEL = "w1_gemv_kernel"
+W1_SOURCES = ["binary_bit_weight_amd/csrc/gemv_w1.hip", "binary_bit_weight_amd/csrc/common.h"]
+W1_SUMMARY = os.path.join(ROOT, "profiles", "w1_gemv_lm_head_m1_counters.md")
+W1_HEAD = (248320, 5120, 128)
 COPY_PROBE_BYTES = 256 << 20
 ROLES = [("q", HIDDEN, HIDDEN, 0), ("k", HIDDEN, HIDDEN, 0), ("v", HIDDEN, HIDDEN, 0), ("o", HIDDEN, HIDDEN, 1),
          ("up", FFN, HIDDEN, 2), ("gate", FFN, HIDDEN, 2), ("down", HIDDEN, FFN, 3)]   # (name, N, K, x slot)
@@ -272,6 +281,49 @@ def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
                     "residual added to O and down"}
 
 
+def w1_roofline(L, synth, torch, dev, stream, steps):
+    """The W1A8 LM head (248320 x 5120, G = 128) at M = 1 and 8: whole calls
+    (preparation + product) back to back between HIP events, rotating over 4
+    device copies of the weights (past twice the Infinity Cache); effective
+    weight bandwidth against the HBM peak."""
+    N, K, G = W1_HEAD
+    bits, sc = w1_weights(L, synth, 503, N, K, G)
+    wbytes = bits.nbytes + sc.nbytes
+    reps = max(1, int(np.ceil(2 ** 29 / wbytes)))
+    Ws = [L.upload_w1(bits, sc, K, G, dev) for _ in range(reps)]
+    lines = []
+    for M in (1, 8):
+        x = torch.from_numpy(synth.normal_f32(510 + M, M, K)).to(dev)
+        xq, xsc = L.quantize(x, stream)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.zeros((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
+        for i in range(2 * reps):
+            L.ll_bitlinear_gemv(Ws[i % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(steps, 4 * reps)
+        e0.record(stream)
+        for i in range(n):
+            L.ll_bitlinear_gemv(Ws[i % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        gbs = wbytes / (ms * 1e-3) / 1e9
+        lines.append({"workload": "W1A8 LM head %d x %d, G = %d, M = %d (int8 x from N(0,1)), %d weight copies rotated"
+                                  % (N, K, G, M, reps),
+                      "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "call_ms": round(ms, 5),
+                      "algorithmic_bytes_per_call": int(wbytes)})
+    del Ws
+    torch.cuda.empty_cache()
+    kv = summary_values(W1_SUMMARY, W1_SOURCES)
+    head = lines[0]
+    return {"bound": "hbm", "achieved": head["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["frac"],
+            "workload": head["workload"], "kernel": W1_KERNEL + " (with w1_prep_kernel: one call)",
+            "call_ms": head["call_ms"], "algorithmic_bytes_per_call": head["algorithmic_bytes_per_call"],
+            "traffic": int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None,
+            "traffic_unit": "HBM bytes per product launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel_source_sha256_16": kernel_source_sha(W1_SOURCES), "other_shapes": lines[1:]}
+
+
 def extras_single(L, synth, torch, dev, stream):
     out = {}
     for name, N, K in [("2560x2560", 2560, 2560), ("6912x2560", 6912, 2560), ("2560x6912", 2560, 6912)]:
@@ -359,6 +411,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--gemm-only", action="store_true")
+    ap.add_argument("--w1-only", action="store_true")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -379,6 +432,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.gemm_only:                                   # the GEMM roofline alone (for the profiler)
         print(json.dumps({"roofline_gemm": gemm_roofline(L, synth, torch, dev, stream, args.steps)}), flush=True)
+        return
+    if args.w1_only:                                     # the W1A8 LM-head line alone (for the profiler)
+        print(json.dumps({"roofline_w1a8": w1_roofline(L, synth, torch, dev, stream, args.steps)}), flush=True)
         return
     log("building the decode step")
     packed, items, weight_bytes = build_decode_step(L, synth, torch, dev)
@@ -461,6 +517,9 @@ def main():
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(oracle, synth, packed)
     if not args.no_extras:
+        # the W1A8 LM head needs its 179 MB of weights built on the host: with the extras
+        log("W1A8 LM head")
+        res["roofline_w1a8"] = w1_roofline(L, synth, torch, dev, stream, args.steps)
         log("extras")
         res["extras"] = {"i2s_decode_step_fused_epilogues":
                          fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, args.steps)}
