@@ -246,22 +246,20 @@ def gemm_roofline(L, synth, torch, dev, stream, steps, M=512):
     return res
 
 
-def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
-    """The same 30-layer decode step with the pages' fused kernels, as one
+def fused_decode_items(L, synth, torch, dev, items, eps=1e-5):
+    """The decode step's products with the pages' fused kernels, as one
     BitNet layer runs them: Q, K, V from the RMS-normalised input; O and down
     from their sub-norms plus the residual stream (as the bias); gate and up
     as one gated pair (y = relu(gate)^2 * up) of the normalised FFN input.
-    Same weights and bytes as the headline step; prepare + product per step,
-    timed with HIP events."""
-    fused, keep = [], []
-    eps = 1e-5
+    Returns (plan items, per-layer (norms, residuals)); the same weights."""
+    fused, extra = [], []
     for layer in range(LAYERS):
         by = {name: items[len(ROLES) * layer + r] for r, (name, _, _, _) in enumerate(ROLES)}
         res_h = [torch.from_numpy(synth.normal_f32(5000 + 2 * layer + j, 1, HIDDEN)).to(dev).reshape(HIDDEN)
                  for j in range(2)]
         norms = [torch.from_numpy(synth.uniform_f32(6000 + 4 * layer + j, HIDDEN if j != 3 else FFN, 0.5, 1.5)).to(dev)
                  for j in range(4)]                       # attention input, attention sub, FFN input, FFN sub
-        keep += res_h + norms
+        extra.append((norms, res_h))
         for name in ("q", "k", "v"):
             W, x, _, y = by[name]
             fused.append(L.Normed(W, x, norms[0], eps, None, y))
@@ -271,6 +269,14 @@ def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
         fused.append(L.Relu2Mul(Wg, Wu, xu, yu, norm=(norms[2], eps)))
         W, x, _, y = by["down"]
         fused.append(L.Normed(W, x, norms[3], eps, res_h[1], y))
+    return fused, extra
+
+
+def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
+    """The same 30-layer decode step with the fused kernels (fused_decode_items);
+    same weights and bytes as the headline step; prepare + product per step,
+    timed with HIP events."""
+    fused, extra = fused_decode_items(L, synth, torch, dev, items)
     plan = L.GemvPlan(fused, 1)
     for _ in range(5):
         plan.run(stream)

@@ -419,7 +419,10 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) acc[m][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int arow = q * kQuarterBytes + (nl < kPl ? nl : kPl - 1) * kPlRowBytes;
+    // rows kPl..15 of the operand are weighted 0 in the epilogue: they read
+    // rows 0..3 of the quarter, so no two lanes of an 8-lane LDS phase share
+    // an address
+    const int arow = q * kQuarterBytes + (nl < kPl ? nl : nl - kPl) * kPlRowBytes;
 
     auto decode = [&](const i32x4& u4, i32x4& b0, i32x4& b1) {
 #pragma unroll

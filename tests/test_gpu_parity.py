@@ -487,3 +487,67 @@ def test_gemv_f32_zero_token(fmt, M):
     y_ref, tsum = fn(packed, N, K, x)
     ok, worst = f32_tol_ok(y, y_ref + bias.astype(np.float64)[None, :], tsum)
     assert ok, "worst error / bound = %.3f" % worst
+
+
+# ------------------------------------------------------------------ the benchmarked configurations
+def _bench():
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    return bench
+
+
+def test_decode_step_as_benched():
+    """The headline workload exactly as bench.py builds and launches it: the
+    30-layer i2_s decode step (210 products, 594.7 MB, one prepared batch),
+    sampled rows of three layers' seven products against the oracle."""
+    t = torch()
+    bench = _bench()
+    packed, items, wbytes = bench.build_decode_step(L, synth, t, "cuda")
+    assert wbytes == 594740040 and len(items) == 210
+    plan = L.GemvPlan(items, 1)
+    announce("decode step as benched", plan.plan.tiles)
+    plan.run()
+    t.cuda.synchronize()
+    for layer in (0, 17, 29):
+        for r, (name, N, K, _) in enumerate(bench.ROLES):
+            W, x, _, y = items[7 * layer + r]
+            rows = synth.sample_rows(layer * 7 + r, N, 12)
+            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, x.cpu().numpy(), rows)
+            ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
+            assert ok, "layer %d %s: worst error / bound %.3f" % (layer, name, worst)
+
+
+def test_fused_decode_step_as_benched():
+    """The fused decode step of bench.py's extras (RMSNorm prologues, gated
+    ReLU² pairs, residual adds on O and down), sampled rows of two layers
+    against the oracle's rmsnorm, products and relu2_mul."""
+    t = torch()
+    bench = _bench()
+    packed, items, wbytes = bench.build_decode_step(L, synth, t, "cuda")
+    fused, extra = bench.fused_decode_items(L, synth, t, "cuda", items)
+    plan = L.GemvPlan(fused, 1)
+    announce("fused decode step as benched", plan.plan.tiles)
+    plan.run()
+    t.cuda.synchronize()
+    eps = 1e-5
+    for layer in (3, 26):
+        by = {name: items[7 * layer + r] for r, (name, _, _, _) in enumerate(bench.ROLES)}
+        norms, res = [n.cpu().numpy() for n in extra[layer][0]], [v.cpu().numpy() for v in extra[layer][1]]
+        xs = {name: by[name][1].cpu().numpy() for name in by}
+        for name, nidx, radd in [("q", 0, None), ("o", 1, 0), ("down", 3, 1)]:
+            _, N, K, _ = [rr for rr in bench.ROLES if rr[0] == name][0]
+            rows = synth.sample_rows(layer + nidx, N, 12)
+            xn = oracle.rmsnorm(xs[name], norms[nidx], eps).astype(np.float32)
+            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, xn, rows)
+            want = y_ref + (0.0 if radd is None else res[radd][rows].astype(np.float64)[None, :])
+            got = by[name][3].cpu().numpy()[:, rows].astype(np.float64)
+            assert (np.abs(got - want) <= 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)).all(), (layer, name)
+        N, K = bench.FFN, bench.HIDDEN
+        rows = synth.sample_rows(layer + 9, N, 12)
+        xn = oracle.rmsnorm(xs["up"], norms[2], eps).astype(np.float32)
+        g_ref, tg = oracle.i2s_gemv_f32(packed["gate"][0], N, K, xn, rows)
+        u_ref, tu = oracle.i2s_gemv_f32(packed["up"][0], N, K, xn, rows)
+        ok, worst = relu2_mul_tol_ok(by["up"][3].cpu().numpy()[:, rows], g_ref, tg, u_ref, tu)
+        assert ok, "layer %d gated pair: worst error / bound %.3f" % (layer, worst)
