@@ -46,6 +46,9 @@ constexpr int kWinK1 = 1024;                          // k per window
 constexpr int kWinB1 = kWinK1 / 8;                    // 128 code bytes per row per window
 constexpr int kChunks = kWinK1 / 128;                 // 8 MFMA chunks per window
 constexpr int kW1MaxSplits = 8;                       // K splits of a narrow matrix
+#ifndef LL_W1_FUSE_WORK
+#define LL_W1_FUSE_WORK 256                                // row blocks x A rows up to which the preparation is fused
+#endif
 
 // LDS row of a wave's tile: 128 code bytes | the window's scales (1024/G fp16) | pad to 16 mod 128.
 __host__ __device__ inline int w1_stride(int G) {
@@ -96,6 +99,35 @@ __device__ __forceinline__ uint8_t fp8_small_int(int v) {
     return uint8_t(code | (v < 0 ? 0x80 : 0));
 }
 
+// One 16-byte piece u of an A row of digit h (0: hi, 1: lo) from the 32
+// source bytes (lo4, hi4) at 32 qp of its 128-k chunk, qp = 2 (u % 2) + u / 4.
+// Piece u holds A bytes 16u + i of lane quarter q = u / 2; byte i pairs with B
+// quarter qp, nibble 16 (q % 2) + i, i.e. the chunk-local weight
+// 32 qp + 2 (q % 2) + i / 8 + 4 (i % 8): all sixteen lie in those 32 bytes.
+// sum: the sixteen source values (0 outside the slot).
+__device__ __forceinline__ i32x4 w1_piece(const i32x4& lo4, const i32x4& hi4, int u, int h, bool in_slot, int& sum) {
+    const uint32_t dw[8] = {uint32_t(lo4[0]), uint32_t(lo4[1]), uint32_t(lo4[2]), uint32_t(lo4[3]),
+                            uint32_t(hi4[0]), uint32_t(hi4[1]), uint32_t(hi4[2]), uint32_t(hi4[3])};
+    const int b0 = 2 * ((u >> 1) & 1);
+    uint32_t out[4];
+    sum = 0;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int i = 4 * w4 + bb;
+            const int v = in_slot ? int(int8_t(dw[i & 7] >> (8 * (b0 + (i >> 3))))) : 0;
+            sum += v;
+            const int hi = (v + 8) >> 4;                // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
+            const int d = h == 0 ? hi : v - 16 * hi;
+            word |= uint32_t(fp8_small_int(d)) << (8 * bb);
+        }
+        out[w4] = word;
+    }
+    return i32x4{int(out[0]), int(out[1]), int(out[2]), int(out[3])};
+}
+
 // ---------------------------------------------------------------- preparation
 // One thread per 16-byte piece of an A row (chunk c, row r, piece u), plus the
 // group sums.  Grid: (ceil(chunks * R * 8 / 256), 1) and a second pass over
@@ -120,31 +152,11 @@ __global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__
         const int h = r & 1, pm = r >> 1;
         const int m = pm / S, j = pm % S;
         const int8_t* xr = xq + int64_t(m) * K + 128 * c;
-        // Piece u holds A bytes 16u + i of lane quarter q = u / 2; byte i pairs
-        // with B quarter qp = 2 (u % 2) + u / 4, nibble 16 (q % 2) + i, i.e. the
-        // chunk-local weight 32 qp + 2 (q % 2) + i / 8 + 4 (i % 8): all sixteen
-        // lie in the 32 bytes at 32 qp, read with two vector loads.
-        const int q = u >> 1, qp = 2 * (u & 1) + (u >> 2);
+        const int qp = 2 * (u & 1) + (u >> 2);
         const bool in_slot = G >= 128 || (32 * qp) / G == j;   // the whole piece is in slot j or not
         const i32x4 lo4 = ld16(xr + 32 * qp), hi4 = ld16(xr + 32 * qp + 16);
-        const uint32_t dw[8] = {uint32_t(lo4[0]), uint32_t(lo4[1]), uint32_t(lo4[2]), uint32_t(lo4[3]),
-                                uint32_t(hi4[0]), uint32_t(hi4[1]), uint32_t(hi4[2]), uint32_t(hi4[3])};
-        const int b0 = 2 * (q & 1);
-        uint32_t out[4];
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const int i = 4 * w4 + bb;
-                const int v = in_slot ? int(int8_t(dw[i & 7] >> (8 * (b0 + (i >> 3))))) : 0;
-                const int hi = (v + 8) >> 4;                // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
-                const int d = h == 0 ? hi : v - 16 * hi;
-                word |= uint32_t(fp8_small_int(d)) << (8 * bb);
-            }
-            out[w4] = word;
-        }
-        st16(A + (c * R + r) * 128 + 16 * u, i32x4{int(out[0]), int(out[1]), int(out[2]), int(out[3])});
+        int sum;
+        st16(A + (c * R + r) * 128 + 16 * u, w1_piece(lo4, hi4, u, h, in_slot, sum));
     }
 }
 
@@ -173,8 +185,11 @@ __device__ void w1_qsum(const int8_t* __restrict__ xq, int64_t M, int64_t K, int
 // in fp64, so their sum is too, in any order) to part and counts itself in;
 // the last to arrive adds the partials and writes y, then resets the counter
 // (counters start zero and every call leaves them zero).
-template <int G, int MT, int NP, int PK>
-__global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per_eu(G >= 128 && PK * (G / 128) == 8 ? 3 : 1))) w1_gemv_kernel(const uint32_t* __restrict__ bits,
+// FUSED (G == 128, one row block of A rows): ws is the int8 activations
+// xq [M][K] themselves; every workgroup forms its windows' digit rows and
+// group sums while staging them (no preparation launch).
+template <int G, int MT, int NP, int PK, bool FUSED>
+__global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per_eu(G >= 128 && PK * (G / 128) == 8 && !FUSED ? 3 : 1))) w1_gemv_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
                                                                  const float* __restrict__ xs,
@@ -219,12 +234,14 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     // A window loads: R rows x 8 chunks x 128 B = 64 R pieces of 16 B; qs: M x ngw ints
     const int apieces = 64 * R;
     constexpr int kAMax = NP == 1 ? 1 : (16 * MT * 64 / PK + 255) / 256;   // R <= 16 MT / PK
+    static_assert(!FUSED || (G == 128 && MT == 1), "fused preparation: G = 128, one row block");
     struct Regs {
         i32x4 w[4];
         uint16_t sc[kScMax];
-        i32x4 a[kAMax];
+        i32x4 a[kAMax * (FUSED ? 2 : 1)];                  // fused: the 32 source bytes of each piece
         int32_t qs[2];
     };
+    const int8_t* xq = static_cast<const int8_t*>(ws);
     auto load = [&](int w, Regs& r) {
         const uint32_t off = uint32_t(w) * kWinB1 + 16 * lc;
         const uint32_t offc = off < rowbytes ? off : rowbytes - 16;
@@ -251,16 +268,26 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
                 int64_t cg = int64_t(w) * kChunks + c;
                 const int64_t nchunk = K / 128;
                 cg = cg < nchunk ? cg : nchunk - 1;
-                r.a[i] = ld16(Ag + (cg * R) * 128 + 16 * rem);
+                if constexpr (FUSED) {
+                    // piece u of row (token m, digit h): the 32 source bytes at 32 qp
+                    const int u = rem & 7, m = rem >> 4, qp = 2 * (u & 1) + (u >> 2);
+                    const int8_t* src = xq + int64_t(m) * K + 128 * cg + 32 * qp;
+                    r.a[2 * i] = ld16(src);
+                    r.a[2 * i + 1] = ld16(src + 16);
+                } else {
+                    r.a[i] = ld16(Ag + (cg * R) * 128 + 16 * rem);
+                }
             }
         }
+        if constexpr (!FUSED) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + 256 * i;
-            const int m = e / ngw, gi = e % ngw;
-            int64_t g = int64_t(w) * ngw + gi;
-            g = g < ng ? g : ng - 1;
-            r.qs[i] = ld32(qsg + int64_t(m < M ? m : M - 1) * ng + g);
+            for (int i = 0; i < 2; ++i) {
+                const int e = tid + 256 * i;
+                const int m = e / ngw, gi = e % ngw;
+                int64_t g = int64_t(w) * ngw + gi;
+                g = g < ng ? g : ng - 1;
+                r.qs[i] = ld32(qsg + int64_t(m < M ? m : M - 1) * ng + g);
+            }
         }
     };
     auto store_w = [&](int w, const Regs& r) {
@@ -280,16 +307,39 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     };
     auto store_a = [&](int w, const Regs& r) {
         char* ab = abase + (w & 1) * abytes;
-#pragma unroll
-        for (int i = 0; i < kAMax; ++i) {
-            const int p = tid + 256 * i;
-            if (i * 256 < apieces && p < apieces) *reinterpret_cast<i32x4*>(ab + 16 * p) = r.a[i];
-        }
         int32_t* qsl = reinterpret_cast<int32_t*>(ab + kChunks * R * 128 + 128);
+        if constexpr (FUSED) {
+            // digit rows converted here; the hi-digit pieces of a (chunk, token)
+            // are 8 aligned lanes, whose source sums add up to the group sum
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + 256 * i;
-            if (e < M * ngw) qsl[e] = r.qs[i];
+            for (int i = 0; i < kAMax; ++i) {
+                if (i * 256 < apieces) {
+                    const int p = tid + 256 * i;
+                    const int pc = p < apieces ? p : apieces - 1;
+                    const int c = pc / (8 * R), rem = pc % (8 * R);
+                    const int u = rem & 7, h = (rem >> 3) & 1, m = rem >> 4;
+                    int sum;
+                    const i32x4 d = w1_piece(r.a[2 * i], r.a[2 * i + 1], u, h, true, sum);
+                    sum += __shfl_xor(sum, 1, 64);
+                    sum += __shfl_xor(sum, 2, 64);
+                    sum += __shfl_xor(sum, 4, 64);
+                    if (p < apieces) {
+                        *reinterpret_cast<i32x4*>(ab + 16 * p) = d;
+                        if (u == 0 && h == 0) qsl[m * ngw + c] = sum;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kAMax; ++i) {
+                const int p = tid + 256 * i;
+                if (i * 256 < apieces && p < apieces) *reinterpret_cast<i32x4*>(ab + 16 * p) = r.a[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = tid + 256 * i;
+                if (e < M * ngw) qsl[e] = r.qs[i];
+            }
         }
     };
 
@@ -470,7 +520,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     if (tid == 0) st_coherent(counters + rb, 0);          // ready for the next call
 }
 
-template <int G, int MT, int NP, int PK>
+template <int G, int MT, int NP, int PK, bool FUSED = false>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                      const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
                      hipStream_t stream) {
@@ -478,20 +528,40 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     size_t lds = size_t(w1_lds_bytes(M, G));
     const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
     lds = lds > red ? lds : red;
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP, PK>), lds);
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP, PK, FUSED>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP, PK>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias, y,
-                       nsplit, part, counters);
+    hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP, PK, FUSED>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias,
+                       y, nsplit, part, counters);
     return hipGetLastError();
+}
+
+// The preparation is fused into the product for G = 128 when every
+// workgroup forming its own windows' digits costs less than the separate
+// launch: that work grows with row blocks x A rows, and the measured break
+// even lies between 224 (7168 rows, two tokens: 12.9 -> 11.4 us) and 272
+// (17408 rows, one token: 17.1 -> 18.4 us).
+bool w1_fused(int64_t N, int G, int64_t Mb) {
+    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
+    return G == 128 && w1_arows(int(Mb), G) <= 16 && rbs * w1_arows(int(Mb), G) <= LL_W1_FUSE_WORK;
 }
 
 template <int G>
 hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                        const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
-                       hipStream_t stream) {
+                       bool fused, hipStream_t stream) {
     constexpr int kUnits = G >= 128 ? kChunks / (G / 128) : kChunks;   // units per window
     constexpr int kMaxPk = G >= 128 ? kUnits : 8 / w1_slots(G);          // R >= 2 S
     constexpr int P8 = kMaxPk < 8 ? kMaxPk : 8, P4 = kMaxPk < 4 ? kMaxPk : 4;
+    if constexpr (G == 128) {
+        if (fused) {
+            switch (w1_pack(M, G)) {
+            case 8: return launch_w1<G, 1, 2, 8, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+            case 4: return launch_w1<G, 1, 2, 4, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+            case 2: return launch_w1<G, 1, 2, 2, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+            default: return launch_w1<G, 1, 2, 1, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+            }
+        }
+    }
     switch (w1_pack(M, G)) {
     case 8: return launch_w1<G, 1, 2, P8>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
     case 4: return launch_w1<G, 1, 2, P4>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
@@ -508,6 +578,7 @@ int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
 #ifndef LL_W1_TARGET_WGS
 #define LL_W1_TARGET_WGS 256
 #endif
+
 // K splits: enough workgroups to spread a narrow matrix over the chip, at
 // most one split per 1024-k window.
 int w1_splits(int64_t N, int64_t K) {
@@ -549,22 +620,27 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
         const int64_t pieces = (K / 128) * R * 8;
         const int64_t pblocks = (pieces + 255) / 256;
         const int64_t items = Mb * (K / G);
-        hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned(pblocks + (items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb, K,
-                           G, ws, pblocks);
+        const bool fused = w1_fused(N, G, Mb);
+        if (!fused)
+            hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned(pblocks + (items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb,
+                               K, G, ws, pblocks);
+        const void* aop = fused ? static_cast<const void*>(xb) : static_cast<const void*>(ws);
         hipError_t e = hipSuccess;
         switch (G) {
         case 32:
-            e = launch_w1_g<32>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters, stream);
+            e = launch_w1_g<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
+                                stream);
             break;
         case 64:
-            e = launch_w1_g<64>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters, stream);
+            e = launch_w1_g<64>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
+                                stream);
             break;
         case 128:
-            e = launch_w1_g<128>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters,
+            e = launch_w1_g<128>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
                                  stream);
             break;
         default:
-            e = launch_w1_g<256>(bits, scales, N, K, int(Mb), ws, xs + m0, bias, y + m0 * N, ns, part, counters,
+            e = launch_w1_g<256>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
                                  stream);
             break;
         }
