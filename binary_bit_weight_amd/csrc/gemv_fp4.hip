@@ -489,38 +489,47 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
     // activation window g % 2) while group g + 1 waits in registers and group
     // g + 2 is being fetched.  The weight tile is private to the wave and its
     // LDS accesses execute in program order, so it is rewritten after the
-    // multiply without a barrier; the barrier orders the shared windows.
-    // multiply group gg from the tile, fetch group gg + 2 into rl (which held
-    // gg, already in the tile), then move group gg + 1 from rs into the tile
-    auto step = [&](int gg, Regs<FMT, MT>& rl, const Regs<FMT, MT>& rs, bool fetch) {
-        if (fetch) load(gg + 2, rl);
-        compute(gg);
-        __builtin_amdgcn_sched_barrier(0);             // a group's multiplies stay before its successor's
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        store(gg + 1, rs);
-        __syncthreads();
-    };
+    // multiply without a barrier; the barrier orders the shared windows.  The
+    // loop runs while both of its fetches are groups of the row; a tail
+    // multiplies the last one to three.
     Regs<FMT, MT> r0, r1;
     load(0, r0);
-    load(1, r1);
+    load(1, r1);                                       // past the row for a one-group row: in-bounds bytes, unused
     store(0, r0);
     __syncthreads();
     int g = 0;
-    for (; g + 4 <= ngr; g += 2) {                     // every fetch is a group of the row; no exit between a load and its use
-        step(g, r0, r1, true);
-        step(g + 1, r1, r0, true);
+    for (; g + 4 <= ngr; g += 2) {                     // no exit between a load and its use
+        load(g + 2, r0);
+        compute(g);
+        __builtin_amdgcn_sched_barrier(0);             // a group's multiplies stay before its successor's
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 1, r1);
+        __syncthreads();
+        load(g + 3, r1);
+        compute(g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 2, r0);
+        __syncthreads();
     }
     // 1 .. 3 groups left (the same count in the whole workgroup): group g is
     // in the tile, group g + 1 in r1; only group g + 2 is still to be fetched
-    if (g + 3 == ngr) {
-        step(g, r0, r1, true);
-        step(g + 1, r1, r0, false);
-        compute(g + 2);
-    } else if (g + 2 == ngr) {
-        step(g, r0, r1, false);
+    const int left = ngr - g;
+    if (left == 3) load(g + 2, r0);
+    compute(g);
+    if (left >= 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 1, r1);
+        __syncthreads();
         compute(g + 1);
-    } else {
-        compute(g);
+    }
+    if (left == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        store(g + 2, r0);
+        __syncthreads();
+        compute(g + 2);
     }
 
     // Epilogue per token: plane 4q + i of this lane's column weighted by
