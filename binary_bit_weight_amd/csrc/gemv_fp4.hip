@@ -37,7 +37,8 @@
 // activation operand read) and fetches them per 1024 k with loads of 4 rows x
 // 256 contiguous bytes (the shape the memory system streams fastest; a load
 // in operand order touches 16 rows per 16 lanes), which go through a padded
-// LDS tile private to the wave.  The workgroup's four waves share a
+// LDS tile private to the wave (a TQ2_0 row's block scales for the tile sit
+// in its padding, one 2-byte load per lane and column block).  The workgroup's four waves share a
 // double-buffered LDS window of activation digits, the only thing they
 // synchronise on.  Loads run two tiles ahead of the multiply.  Workgroup ids
 // are mapped so that the workgroups of one product run on one XCD and share
@@ -320,7 +321,7 @@ template <int FMT, int MT>
 struct Regs {
     i32x4 w[F4Cfg<MT>::NLD];                 // load i: row RPI i + lane / LPR, 16 bytes at 16 (lane % LPR)
     i32x4 a[F4Cfg<MT>::APer];                // pieces tid + kThreads p of the activation window
-    uint16_t sc[F4Cfg<MT>::KG * kCB];        // TQ2_0: scale of this lane's row per chunk and column block
+    uint16_t sc[kCB];                        // TQ2_0: scale of row nl, chunk q % KG of the group, per column block
 };
 
 // out[m] = this lane's result for token m0 + m: lane l holds row row0 + l
@@ -378,18 +379,12 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
             }
         }
         if (FMT == 2) {
+            int64_t b = int64_t(gc) * KG + q % KG;
+            b = b < nch ? b : nch - 1;
 #pragma unroll
-            for (int c = 0; c < KG; ++c) {
-                int64_t b = int64_t(gc) * KG + c;
-                b = b < nch ? b : nch - 1;
-#pragma unroll
-                for (int cb = 0; cb < kCB; ++cb) r.sc[c * kCB + cb] = ld2(srow[cb] + b);
-            }
+            for (int cb = 0; cb < kCB; ++cb) r.sc[cb] = ld2(srow[cb] + b);
         }
     };
-    // scales of the group being multiplied: chunk c of column block cb in bits
-    // 16 c of cscp[cb] (a runtime shift, not a runtime index into an array)
-    uint64_t cscp[kCB];
     auto store = [&](int g, const Regs<FMT, MT>& r) {
         const bool ok = uint32_t(g) * (KG * 64) + 16 * lp < rowbytes;
 #pragma unroll
@@ -403,15 +398,14 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
             if (C::APer * kThreads * 16 == C::AWin || pc < C::AWin / 16)
                 *reinterpret_cast<i32x4*>(abuf + (g & 1) * C::AWin + 16 * pc) = aok ? r.a[p] : i32x4{0, 0, 0, 0};
         }
-        if (FMT == 2)
+        if (FMT == 2 && q < KG)                        // the group's block scales in the row padding
 #pragma unroll
-            for (int cb = 0; cb < kCB; ++cb) {
-                uint64_t v = 0;
-#pragma unroll
-                for (int c = 0; c < KG; ++c) v |= uint64_t(r.sc[c * kCB + cb]) << (16 * c);
-                cscp[cb] = v;
-            }
+            for (int cb = 0; cb < kCB; ++cb)
+                *reinterpret_cast<uint16_t*>(wtile + (16 * cb + nl) * C::WStride + KG * 64 + 2 * q) = r.sc[cb];
     };
+    // block scales of the group being multiplied: chunk c of column block cb
+    // in bits 16 c of cscp[cb] (a runtime shift, not a runtime index)
+    uint64_t cscp[kCB];
     auto scale_of = [&](int c, int cb) { return half_bits_to_float(uint16_t(cscp[cb] >> (16 * c))); };
 
     f32x4 acc[MT][kCB];
@@ -450,6 +444,12 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
     };
     auto compute = [&](int g) {
         const int cn = nch - int64_t(g) * KG < KG ? int(nch - int64_t(g) * KG) : KG;
+        if (FMT == 2)
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) {
+                const char* sp = wtile + (16 * cb + nl) * C::WStride + KG * 64;
+                cscp[cb] = KG == 4 ? *reinterpret_cast<const uint64_t*>(sp) : uint64_t(*reinterpret_cast<const uint32_t*>(sp));
+            }
 #pragma unroll LL_F4_CUNROLL
         for (int c = 0; c < cn; ++c) {                  // the last group may hold fewer chunks
             const char* ap = abuf + (g & 1) * C::AWin + arow + c * kChunkBytes;
@@ -575,18 +575,21 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
 }
 
 // Waves per SIMD the register allocation aims at, per format and token count
-// (the LDS of F4Cfg<MT> allows 3, 2, 3, 2 workgroups per CU).  One-token
-// TQ2_0 needs more registers for its block scales: at three waves it would
-// spill inside the main loop (measured 14% slower); with four tokens three
-// waves still measured faster despite a small spill.
+// (the LDS of F4Cfg<MT> allows 3, 2, 3, 2 workgroups per CU).  TQ2_0 keeps
+// each group's block scales in the LDS row padding, so one token fits three
+// waves without spilling; with four tokens it would spill inside the main
+// loop at three waves (measured 17% slower than two).
 #ifndef LL_F4_OCC
 #define LL_F4_OCC 3
 #endif
 #ifndef LL_F4_OCC_TQ2
-#define LL_F4_OCC_TQ2 2
+#define LL_F4_OCC_TQ2 3
+#endif
+#ifndef LL_F4_OCC_TQ2_MT4
+#define LL_F4_OCC_TQ2_MT4 2
 #endif
 __host__ __device__ constexpr int f4_occ(int FMT, int MT) {
-    return MT == 8 || MT == 2 ? 2 : MT == 4 ? 3 : FMT == 2 ? LL_F4_OCC_TQ2 : LL_F4_OCC;
+    return MT == 8 || MT == 2 ? 2 : MT == 4 ? (FMT == 2 ? LL_F4_OCC_TQ2_MT4 : 3) : FMT == 2 ? LL_F4_OCC_TQ2 : LL_F4_OCC;
 }
 
 // grid: 8 * ceil(T / 8) workgroups for T logical ones; hardware workgroup w
