@@ -27,6 +27,14 @@ summary when that matches the current source.
 "roofline_w1a8" reports the W1A8 LM head (248320 x 5120, G = 128, M = 1) the
 same way, whole calls over rotating weight copies.
 
+The defaults (500 warm-up steps, about 60 ms, then 200 timed steps) let the
+GPU clocks settle first: after an idle period (the host builds 595 MB of
+synthetic weights before the timing) the step takes about 20 ms of
+continuous work to reach its steady time, and a timed window inside that
+ramp reads up to 10% slow.  The other lines (GEMM, W1A8, extras) run their
+own calls for at least 60 ms before timing (settle()), since some follow
+the CPU oracle leg.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
        python bench.py --gemm-only      (the GEMM roofline alone)
        python bench.py --w1-only        (the W1A8 LM-head line alone)
@@ -152,6 +160,20 @@ def w1_weights(L, synth, seed, N, K, G):
     return bits, scales
 
 
+def settle(torch, fn, seconds=0.06):
+    """Runs fn(i) in batches of 20 calls until `seconds` of wall time have
+    passed: after an idle period the GPU clocks need about 20 ms of
+    continuous work to reach their steady state."""
+    t0, i = time.perf_counter(), 0
+    while True:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_graph(torch, call, copies, calls, stream):
     """GPU time of one call: `calls` calls (call(i, stream) with i cycling
     over `copies` weight copies) captured in one HIP graph and replayed, so
@@ -163,7 +185,7 @@ def time_graph(torch, call, copies, calls, stream):
     with torch.cuda.graph(g):
         for i in range(calls):
             call(i % copies, None)
-    g.replay()
+    settle(torch, lambda i: g.replay())
     ms = time_events(torch, g.replay, 3, stream)
     del g
     return ms / calls
@@ -218,8 +240,7 @@ def gemm_roofline(L, synth, torch, dev, stream, steps, M=512):
     lines = []
     for N, K in GEMM_SHAPES:
         W, _, xq, xsc, y, gws = gemm_operands(L, synth, torch, dev, stream, N, K, M)
-        for _ in range(5):
-            L.ll_bitlinear_gemm(W, xq, xsc, M, None, y, None, gws, stream)
+        settle(torch, lambda i: L.ll_bitlinear_gemm(W, xq, xsc, M, None, y, None, gws, stream))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
@@ -278,8 +299,7 @@ def fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, steps):
     timed with HIP events."""
     fused, extra = fused_decode_items(L, synth, torch, dev, items)
     plan = L.GemvPlan(fused, 1)
-    for _ in range(5):
-        plan.run(stream)
+    settle(torch, lambda i: plan.run(stream))
     ms = time_events(torch, lambda: plan.run(stream), steps, stream)
     return {"ms_per_step": round(ms, 4), "GB_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
             "products": len(fused), "tiles": int(plan.plan.tiles),
@@ -303,8 +323,7 @@ def w1_roofline(L, synth, torch, dev, stream, steps):
         xq, xsc = L.quantize(x, stream)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ws = torch.zeros((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M),), dtype=torch.uint8, device=dev)
-        for i in range(2 * reps):
-            L.ll_bitlinear_gemv(Ws[i % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream)
+        settle(torch, lambda i: L.ll_bitlinear_gemv(Ws[i % reps], L.LL_ACT_I8, xq, xsc, M, None, y, ws, stream))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n = max(steps, 4 * reps)
         e0.record(stream)
@@ -411,8 +430,8 @@ def extras_single(L, synth, torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
