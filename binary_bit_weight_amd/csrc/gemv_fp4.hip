@@ -126,12 +126,30 @@ struct TokScale {
 
 // 1 / sqrt(sum x^2 / K + eps) of a token row, rounded once to fp32 (sum and
 // root in fp64), by the 256 threads of a workgroup (barrier inside).
+// The row is read in batches of kRowBatch 16-byte loads per thread, all
+// requested before any is used (clamped to the row; the copies past it are
+// not counted).  The first batch, the whole row up to 8192 elements, is
+// straight-line code, so its loads overlap every load issued before it.
+constexpr int kRowBatch = 8;
+
 __device__ __forceinline__ float rms_inv(const float* x, int64_t K, float eps, int tid, double* sacc) {
     double ss = 0.0;
-    for (int64_t i = tid; i < K / 4; i += 256) {
-        const f32x4 u = ld16f(x + 4 * i);
-        ss += (double(u[0]) * u[0] + double(u[1]) * u[1]) + (double(u[2]) * u[2] + double(u[3]) * u[3]);
-    }
+    const int64_t n4 = K / 4;
+    auto batch = [&](int64_t i0) {
+        f32x4 u[kRowBatch];
+#pragma unroll
+        for (int b = 0; b < kRowBatch; ++b) {
+            const int64_t i = i0 + 256 * b;
+            u[b] = ld16f(x + 4 * (i < n4 ? i : n4 - 1));
+        }
+#pragma unroll
+        for (int b = 0; b < kRowBatch; ++b)
+            if (i0 + 256 * b < n4)
+                ss += (double(u[b][0]) * u[b][0] + double(u[b][1]) * u[b][1]) +
+                      (double(u[b][2]) * u[b][2] + double(u[b][3]) * u[b][3]);
+    };
+    batch(tid);
+    for (int64_t i0 = tid + 256 * kRowBatch; i0 < n4; i0 += 256 * kRowBatch) batch(i0);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
     if ((tid & 63) == 0) sacc[tid >> 6] = ss;
@@ -146,15 +164,26 @@ __device__ __forceinline__ float rms_inv(const float* x, int64_t K, float eps, i
 __device__ __forceinline__ TokScale token_scale(const float* x, const float* w, float rinv, int64_t K, int tid,
                                                 float* smax) {
     float mx = 0.0f;
-    for (int64_t i = tid; i < K / 4; i += 256) {
-        f32x4 u = ld16f(x + 4 * i);
-        if (w) {
-            const f32x4 g = ld16f(w + 4 * i);
+    const int64_t n4 = K / 4;
+    auto batch = [&](int64_t i0) {
+        f32x4 u[kRowBatch], g[kRowBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) u[e] = __fmul_rn(__fmul_rn(u[e], rinv), g[e]);
+        for (int b = 0; b < kRowBatch; ++b) {
+            const int64_t i = i0 + 256 * b, ic = i < n4 ? i : n4 - 1;
+            u[b] = ld16f(x + 4 * ic);
+            if (w) g[b] = ld16f(w + 4 * ic);
         }
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
-    }
+#pragma unroll
+        for (int b = 0; b < kRowBatch; ++b) {
+            if (i0 + 256 * b >= n4) continue;              // a clamped copy
+            if (w)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[b][e] = __fmul_rn(__fmul_rn(u[b][e], rinv), g[b][e]);
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(u[b][0]), fabsf(u[b][1])), fmaxf(fabsf(u[b][2]), fabsf(u[b][3]))));
+        }
+    };
+    batch(tid);
+    for (int64_t i0 = tid + 256 * kRowBatch; i0 < n4; i0 += 256 * kRowBatch) batch(i0);
     mx = wave_max(mx);
     if ((tid & 63) == 0) smax[tid >> 6] = mx;
     __syncthreads();
@@ -218,26 +247,24 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
     const int lc = tid >> 5, s = (tid >> 4) & 1, q = (tid >> 2) & 3, j = tid & 3;
     const int64_t c = int64_t(slice) * kSliceChunks + lc;
     const bool live = c < nchunks(K);
-    float v[8], nv[8];
+    // This thread's elements are requested first and used only after the
+    // row's max |x|, so the two sets of loads are in flight together.
+    constexpr int NR = FMT == 1 ? 2 : 4;
+    f32x4 raw[NR], rawn[NR];
+    bool ok = live;
     if (FMT == 1) {
         // i2_s: byte 16 (q%2) + 4 j + b of group 2c + q/2 holds the elements
         // 128 g + 32 t + 16 (q%2) + 4 j + b at shifts 6 - 2t; nibble h of the
         // masked word takes t = 3 - 2h (step 0) or t = 2 - 2h (step 1).
         const int64_t g = 2 * c + (q >> 1);
-        const bool ok = live && g < K / 128;
+        ok = live && g < K / 128;
         const int64_t gc = ok ? g : 0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int t = (s == 0 ? 3 : 2) - 2 * h;
             const int64_t k0 = 128 * gc + 32 * t + 16 * (q & 1) + 4 * j;
-            const f32x4 w4 = ld16f(x + k0);
-            if (nw) {
-                const f32x4 g4 = ld16f(nw + k0);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) nv[2 * b + h] = g4[b];
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b) v[2 * b + h] = ok ? w4[b] : 0.0f;
+            raw[h] = ld16f(x + k0);
+            if (nw) rawn[h] = ld16f(nw + k0);
         }
     } else {
         // TQ2_0: byte 16 q + 4 j + b of block c holds elements 4 (16 q + 4 j + b) + i
@@ -246,28 +273,24 @@ __global__ void __launch_bounds__(256) f4_prep_kernel(const F4Prep* __restrict__
         const int64_t k0 = 256 * cc + 64 * q + 16 * j;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const f32x4 w4 = ld16f(x + k0 + 4 * b);
-            if (nw) {
-                const f32x4 g4 = ld16f(nw + k0 + 4 * b);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) nv[2 * b + h] = g4[2 * h + s];
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) v[2 * b + h] = live ? w4[2 * h + s] : 0.0f;
+            raw[b] = ld16f(x + k0 + 4 * b);
+            if (nw) rawn[b] = ld16f(nw + k0 + 4 * b);
         }
     }
     // RMSNorm prologue: the same two fp32 multiplies as in token_scale
-    float rinv = 0.0f;
-    if (nw) {
-        rinv = rms_inv(x, K, P.eps, tid, sacc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(__fmul_rn(v[e], rinv), nv[e]);
-    }
-
-    // max |x| over the token (this thread's elements were requested above, so
-    // both loads are in flight together)
+    const float rinv = nw ? rms_inv(x, K, P.eps, tid, sacc) : 0.0f;
+    // max |x| over the token
     const TokScale ts = token_scale(x, nw, rinv, K, tid, smax);
     const int E = ts.E;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // element e = 2b + h: i2_s word h, lane b; TQ2_0 word b, lane 2h + s
+        const int b = e >> 1, h = e & 1;
+        float xv = FMT == 1 ? raw[h][b] : raw[b][2 * h + s];
+        if (nw) xv = __fmul_rn(__fmul_rn(xv, rinv), FMT == 1 ? rawn[h][b] : rawn[b][2 * h + s]);
+        v[e] = ok ? xv : 0.0f;
+    }
     uint32_t out[kPl];
     long long xsum = 0;
     make_digits<8>(v, ts, out, xsum);
