@@ -389,8 +389,7 @@ def extras_single(L, synth, torch, dev, stream):
         x = torch.from_numpy(synth.normal_f32(304 + M, M, K)).to(dev)
         ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in copies]
         plan = L.GemvPlan([(Wc, x, None, yc) for Wc, yc in zip(copies, ys)], M)
-        for _ in range(3):
-            plan.run(stream)
+        settle(torch, lambda i: plan.run(stream))
         ms = time_events(torch, lambda: plan.run(stream), 20, stream)
         nbytes = ncopy * blocks.size
         out["tq2_plan_%dx6912x2560_M%d" % (ncopy, M)] = {"us": round(ms * 1e3, 2), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
