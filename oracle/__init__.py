@@ -59,6 +59,7 @@ def lib():
             "orc_tq2_encode": (C.c_int, [P, P, I64, I64, P]),
             "orc_tq2_decode": (I64, [P, I64, I64, P, P]),
             "orc_tq2_gemv_f32": (None, [P, I64, I64, P, I64, P, I64, P, P]),
+            "orc_tq2_gemm_i8": (None, [P, I64, I64, P, P, I64, P, I64, P, P]),
             "orc_w1_encode": (C.c_int, [P, I64, I64, P]),
             "orc_w1_decode": (None, [P, I64, I64, P]),
             "orc_w1_from_dense": (C.c_int, [P, I64, I64, C.c_int32, P, P]),
@@ -178,6 +179,22 @@ def tq2_gemv_f32(blocks, N, K, x, rows=None):
     y = np.empty((M, nr), np.float64)
     t = np.empty((M, nr), np.float64)
     lib().orc_tq2_gemv_f32(_p(blocks), N, K, _p(x), M, _p(r), nr, _p(y), _p(t))
+    return y, t
+
+
+def tq2_gemm_i8(blocks, N, K, q, s_tok, rows=None):
+    """int8 activations q [M, K] with scales s_tok [M] against TQ2_0 blocks:
+    y = s_tok * sum_b s_b * sum_{k in b} w q in fp64 (exact integer block
+    sums), and T = s_tok * sum_b |s_b| * sum_{k in b} |q|, both [M, len(rows)]."""
+    blocks = _c(blocks, np.uint8)
+    q = _c(np.atleast_2d(q), np.int8)
+    s_tok = _c(s_tok, np.float32)
+    M = q.shape[0]
+    assert q.shape[1] == K and s_tok.size == M
+    r, nr = _rows(rows, N)
+    y = np.empty((M, nr), np.float64)
+    t = np.empty((M, nr), np.float64)
+    lib().orc_tq2_gemm_i8(_p(blocks), N, K, _p(q), _p(s_tok), M, _p(r), nr, _p(y), _p(t))
     return y, t
 
 

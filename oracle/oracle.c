@@ -305,6 +305,40 @@ void orc_tq2_gemv_f32(const uint8_t* blocks, int64_t N, int64_t K, const float* 
     }
 }
 
+/* int8 activations with TQ2_0 weights (the int8 reading of the block   */
+/* product above, with x replaced by its quantization q, s_tok):        */
+/* y = s_tok * sum_b s_b * d_b, d_b = sum_{k in b} w*q exactly (int64), */
+/* every product and the sum in fp64.  tsum = s_tok * sum_b |s_b| *     */
+/* sum_{k in b} |q|.  y, tsum: fp64 [M, nr]; same row conventions as    */
+/* orc_i2s_gemv_f32.                                                    */
+void orc_tq2_gemm_i8(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* q, const float* s_tok,
+                     int64_t M, const int64_t* rows, int64_t nr, double* y, double* tsum)
+{
+    int64_t nb = K / 256;
+    if (!rows) nr = N;
+    for (int64_t i = 0; i < nr; ++i) {
+        int64_t n = rows ? rows[i] : i;
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, ab = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t* blk = blocks + 66 * (n * nb + b);
+                double s = orc_f16_to_f64((uint16_t)(blk[64] | (blk[65] << 8)));
+                int64_t d = 0, da = 0;
+                for (int e = 0; e < 256; ++e) {
+                    int w = tq2_value_of((blk[e / 4] >> (2 * (e % 4))) & 3);
+                    int64_t qv = q[m * K + b * 256 + e];
+                    d += (int64_t)w * qv;
+                    da += qv < 0 ? -qv : qv;
+                }
+                acc += s * (double)d;
+                ab += fabs(s) * (double)da;
+            }
+            y[m * nr + i] = (double)s_tok[m] * acc;
+            if (tsum) tsum[m * nr + i] = (double)s_tok[m] * ab;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* W1 sign bits  [BG "API", "Method", "Correctness"]                   */
 /*                                                                     */

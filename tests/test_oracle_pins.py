@@ -289,6 +289,47 @@ def test_tq2_exact_bruteforce(orc):
         assert abs(y[0, i] - float(exact[i])) <= t[0, i] * K * 2.0 ** -51
 
 
+def test_tq2_gemm_i8_exact_bruteforce(orc):
+    """int8 activations against TQ2_0 blocks: the oracle's fp64 value against
+    the exact rational s_tok * sum_b s_b * sum_{k in b} w q, with the weights
+    decoded by the independent pure-Python unpacker."""
+    N, K, M = 3, 512, 2
+    w = synth.ternary(85, N, K)
+    sc = synth.uniform_f16_bits(86, N * K // 256, 0.005, 0.05)
+    q, s = orc.quantize_f32(synth.normal_f32(87, M, K))
+    b = orc.tq2_encode(w, sc)
+    y, t = orc.tq2_gemm_i8(b, N, K, q, s)
+    wb, scb = brute.tq2_unpack(b.tolist(), N, K)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for bi in range(K // 256):
+                d = sum(wb[n][k] * int(q[m, k]) for k in range(bi * 256, bi * 256 + 256))
+                tot += brute.f16(scb[n * (K // 256) + bi]) * d
+            exact = Fraction(float(s[m])) * tot
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(t[m, n]) * 2 ** -48
+
+
+@pytest.mark.parametrize("N,K,M", [(29, 512, 1), (8, 768, 5), (4, 2560, 17)])
+def test_tq2_gemm_i8_vs_numpy_and_gemv(orc, N, K, M):
+    """The same product three ways: numpy over the decoded weights, and the
+    fp32-activation oracle on q (exact integers) times s_tok."""
+    w = synth.ternary(95 + N, N, K)
+    sc = synth.uniform_f16_bits(96 + N, N * K // 256, 0.005, 0.05)
+    q, s = orc.quantize_f32(synth.normal_f32(97 + N, M, K))
+    b = orc.tq2_encode(w, sc)
+    y, t = orc.tq2_gemm_i8(b, N, K, q, s)
+    sb = sc.view(np.float16).astype(np.float64).reshape(N, K // 256)
+    q64 = q.astype(np.float64).reshape(M, K // 256, 256)
+    w64 = w.astype(np.float64).reshape(N, K // 256, 256)
+    ref = s.astype(np.float64)[:, None] * np.einsum("mbk,nbk,nb->mn", q64, w64, sb)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+    tref = s.astype(np.float64)[:, None] * np.einsum("mbk,nb->mn", np.abs(q64), np.abs(sb))
+    np.testing.assert_allclose(t, tref, rtol=1e-12)
+    yg, _ = orc.tq2_gemv_f32(b, N, K, q.astype(np.float32))
+    np.testing.assert_allclose(y, s.astype(np.float64)[:, None] * yg, rtol=1e-12, atol=1e-13)
+
+
 def test_tq2_invalid_code_and_roundtrip(orc):
     w = synth.ternary(91, 4, 256)
     sc = synth.uniform_f16_bits(92, 4, 0.005, 0.05)
