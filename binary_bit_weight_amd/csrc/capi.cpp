@@ -126,6 +126,11 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
                                                       static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
                                                       s),
                               fn);
+        if (w->fmt == LL_FMT_TQ2_0)
+            return hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
+                                                      static_cast<const uint16_t*>(w->scales), w->N, w->K,
+                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, s),
+                              fn);
         if (w->fmt == LL_FMT_W1) {
             st = check_w1_device(w, fn);
             if (st) return st;
@@ -146,7 +151,8 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     if (!w || M < 1) return size_t(-1);
     if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->N, w->K, w->group);
-    if (w->fmt == LL_FMT_I2S && w->K > 0 && w->N > 0) return llk::gemm_i8_workspace(M, w->N, w->K);
+    if ((w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) && w->K > 0 && w->N > 0)
+        return llk::gemm_i8_workspace(M, w->N, w->K);
     return 0;
 }
 
@@ -173,12 +179,20 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                                               bias, y, workspace, static_cast<hipStream_t>(stream)),
                           fn);
     }
-    if (w->fmt != LL_FMT_I2S) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s and W1 only");
+    if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0)
+        return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s, TQ2_0 and W1 only");
+    if (w->fmt == LL_FMT_TQ2_0 && acc_out)
+        return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for TQ2_0 (per-block scales)");
     const size_t need = llk::gemm_i8_workspace(M, w->N, w->K);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
     if (need > 0 && !aligned(workspace, 16))
         return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
+    if (w->fmt == LL_FMT_TQ2_0)
+        return hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
+                                                  static_cast<const uint16_t*>(w->scales), w->N, w->K, xq, xs, M, bias,
+                                                  y, need > 0 ? workspace : nullptr, static_cast<hipStream_t>(stream)),
+                          fn);
     return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y,
                                               acc_out, need > 0 ? workspace : nullptr,
                                               static_cast<hipStream_t>(stream)),

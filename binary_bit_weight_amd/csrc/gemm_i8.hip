@@ -27,12 +27,28 @@
 // stages, every load from a clamped in-bounds address so the compiler can
 // count its waits; one barrier per group.
 //
+// TQ2_0 weights (llama.cpp TQ2_0 as described by the Hesper API doc: 2-bit
+// two's-complement codes, four consecutive elements per byte, an fp16 scale
+// per 256-element block; codes and scales in separate device arrays) use the
+// same kernel.  Element k of a row is again in code byte k/4, so the code
+// loads are the same; field t of byte j holds element 4j + t, so a step
+// takes field t of its lane's 16 code bytes (elements 4 (16 h + j) + t) and
+// the activation tile is stored as four planes of 32 bytes per 128-k group,
+// plane t holding elements 4i + t (a 4 x 4 byte transpose of every 16-byte
+// piece).  Each 256-k block's exact int32 sum is scaled by the block scale
+// into fp32 accumulators (the block's first multiply starts from zero), and
+// y = acc * s_tok (+ bias).  Split K keeps whole blocks and the last split
+// adds the fp32 partials in split order, so the result does not depend on
+// which split finishes last.
+//
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its exact
 // int32 partial tile to the workspace and increments the tile's counter; the
 // split that arrives last adds the others' partials to its own and runs the
 // epilogue, then resets the counter (so the counters stay zero between
 // calls).  Integer addition makes the result independent of the order.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -54,15 +70,18 @@ constexpr size_t kGemmLds = size_t(2) * kBuf > size_t(kXchg) ? size_t(2) * kBuf 
 #ifndef LL_GEMM_DEPTH
 #define LL_GEMM_DEPTH 4                                  // register stages of global loads
 #endif
+#ifndef LL_GEMM_DEPTH_TQ2
+#define LL_GEMM_DEPTH_TQ2 2                              // TQ2_0: its fp32 block sums take the registers of two stages
+#endif
 
 
-__global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N,
-                                                                int64_t K, const int8_t* __restrict__ xq,
-                                                                const float* __restrict__ xs, int64_t M,
-                                                                const float* __restrict__ bias, float* __restrict__ y,
-                                                                int32_t* __restrict__ acc_out, int S,
-                                                                int32_t* __restrict__ part,
-                                                                int32_t* __restrict__ counters) {
+// FMT 1: i2_s, FMT 2: TQ2_0 (scales: fp16 [N][K/256]).
+template <int FMT>
+__device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                                             int64_t N, int64_t K, const int8_t* __restrict__ xq,
+                                             const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
+                                             float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
+                                             int32_t* __restrict__ part, int32_t* __restrict__ counters) {
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -83,7 +102,9 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     const int64_t m0 = (tile % TM) * BM, n0 = (tile / TM) * BN;
     const int64_t rowbytes = K / 4;
     const int64_t ng = K / 128;
-    const int64_t g0 = ng * split / S, g1 = ng * (split + 1) / S;
+    // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
+    const int64_t nsplit_units = FMT == 1 ? ng : K / 256, per_unit = FMT == 1 ? 1 : 2;
+    const int64_t g0 = per_unit * (nsplit_units * split / S), g1 = per_unit * (nsplit_units * (split + 1) / S);
 
     // Loads of one group: two 16-byte activation chunks (row idx / 8, chunk
     // idx % 8 for idx = tid + 512 c) and 8 code bytes (column tid / 4,
@@ -101,26 +122,62 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     int64_t ncl = n0 + bcol;
     ncl = ncl < N ? ncl : N - 1;
     const uint8_t* bptr = codes + ncl * rowbytes + 8 * bqt;
+    // TQ2_0: block scales of this lane's two columns
+    const uint16_t* sptr[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        int64_t n = n0 + wn * 64 + nb * 32 + li;
+        n = n < N ? n : N - 1;
+        sptr[nb] = FMT == 2 ? scales + n * (K / 256) : nullptr;
+    }
 
     struct Stage {
         i32x4 a[2];
         u32x2 b;
+        uint16_t sc[FMT == 2 ? 2 : 1];                      // TQ2_0: the group's block scales
     };
     auto load = [&](int64_t g, Stage& s) {
         const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
         for (int c = 0; c < 2; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
         s.b = *(const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc);
+        if constexpr (FMT == 2)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) s.sc[nb] = ld2(sptr[nb] + gc / 2);
     };
-    auto store = [&](int buf, const Stage& s) {
+    // TQ2_0: scales of the block being multiplied, taken when its second
+    // (odd) group is stored
+    float curs[2] = {0.0f, 0.0f};
+    auto store = [&](int buf, const Stage& s, bool odd) {
         int8_t* A = lds + buf * kBuf;
         int8_t* B = A + BM * LDA;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int idx = tid + kThreads * c;
-            *reinterpret_cast<i32x4*>(&A[(idx >> 3) * LDA + 16 * (idx & 7)]) = s.a[c];
+            int8_t* arow_l = &A[(idx >> 3) * LDA];
+            if constexpr (FMT == 1) {
+                *reinterpret_cast<i32x4*>(arow_l + 16 * (idx & 7)) = s.a[c];
+            } else {
+                // piece p (elements 16 p + 4 i + t in byte t of dword i) ->
+                // dword t = elements 16 p + 4 i + t, i = 0..3: bytes 4p..4p+3 of plane t
+                const uint32_t d0 = uint32_t(s.a[c][0]), d1 = uint32_t(s.a[c][1]);
+                const uint32_t d2 = uint32_t(s.a[c][2]), d3 = uint32_t(s.a[c][3]);
+                const uint32_t x01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);   // d0.b0 d1.b0 d0.b1 d1.b1
+                const uint32_t y01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);   // d0.b2 d1.b2 d0.b3 d1.b3
+                const uint32_t x23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+                const uint32_t y23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+                const int p = idx & 7;
+                *reinterpret_cast<uint32_t*>(arow_l + 0 + 4 * p) = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+                *reinterpret_cast<uint32_t*>(arow_l + 32 + 4 * p) = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+                *reinterpret_cast<uint32_t*>(arow_l + 64 + 4 * p) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
+                *reinterpret_cast<uint32_t*>(arow_l + 96 + 4 * p) = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
+            }
         }
         *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
+        if constexpr (FMT == 2)
+            if (odd)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) curs[nb] = half_bits_to_float(s.sc[nb]);
     };
 
     // epilogue operands, requested before the main loop so their latency is
@@ -132,7 +189,7 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
         const int64_t m = m0 + wm * 64 + kh * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         xsv[r] = xs[m < M ? m : M - 1];
     }
-    const float sw = *reinterpret_cast<const float*>(codes + N * rowbytes);
+    const float sw = FMT == 1 ? *reinterpret_cast<const float*>(codes + N * rowbytes) : 1.0f;
     const float* bsrc = bias ? bias : xs;                 // always a valid address
     float bnv[2];
 #pragma unroll
@@ -142,18 +199,26 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     }
 
     i32x16 acc[2][2];
+    f32x16 facc[FMT == 2 ? 2 : 1][2];                      // TQ2_0: scaled block sums
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0;
+            for (int r = 0; r < 16; ++r) {
+                acc[mb][nb][r] = 0;
+                if constexpr (FMT == 2) facc[mb][nb][r] = 0.0f;
+            }
 
-    auto compute = [&](int buf) {
+    // odd (TQ2_0): the group ends a 256-k block, whose sums are then scaled
+    // into facc; the block's first multiply (even group, first step) starts
+    // from zero
+    auto compute = [&](int buf, bool odd) {
         const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 16 * h + 64 * kh;
         const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + 16 * h;
-        // code byte j of this lane's 16 holds, in field t (bits 6 - 2t), the
-        // weight of k = 32 t + 16 h + j: the B operand of step t
+        // i2_s: code byte j of this lane's 16 holds, in field t (bits 6 - 2t),
+        // the weight of k = 32 t + 16 h + j: the B operand of step t.  TQ2_0:
+        // field t (bits 2t) holds element 4 (16 h + j) + t, matching plane t.
         i32x4 bq[2], ao[2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) bq[nb] = *reinterpret_cast<const i32x4*>(B + nb * 32 * LDB);
@@ -164,31 +229,45 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
                 ao[tt][mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA + 32 * tt);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int sh = 6 - 4 * kh - 2 * tt;
+            const int sh = FMT == 1 ? 6 - 4 * kh - 2 * tt : 4 * kh + 2 * tt;
+            // code -> int8 by byte permute: i2_s {-1, 0, +1}, TQ2_0 {0, +1, -2, -1}
+            constexpr uint32_t table = FMT == 1 ? 0x000100FFu : 0xFFFE0100u;
             i32x4 bo[2];
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    bo[nb][i] = int(__builtin_amdgcn_perm(0u, 0x000100FFu, (uint32_t(bq[nb][i]) >> sh) & 0x03030303u));
+                    bo[nb][i] = int(__builtin_amdgcn_perm(0u, table, (uint32_t(bq[nb][i]) >> sh) & 0x03030303u));
+            const bool first = FMT == 2 && !odd && tt == 0;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[tt][mb], bo[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[tt][mb], bo[nb], first ? i32x16{} : acc[mb][nb],
+                                                                        0, 0, 0);
         }
+        if constexpr (FMT == 2)
+            if (odd)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), curs[nb], facc[mb][nb][r]);
     };
 
     // Group g + i is multiplied from LDS buffer i % 2; register stage i % D
     // holds group g + i from its load (D - 1 groups earlier) to its store
     // (one group earlier).  The main loop runs whole runs of D groups with no
     // early exit; the last 1 .. D - 1 groups follow it.
-    constexpr int D = LL_GEMM_DEPTH;
+    constexpr int D = FMT == 1 ? LL_GEMM_DEPTH : LL_GEMM_DEPTH_TQ2;
     static_assert(D % 2 == 0 && D >= 2, "even register depth");
+    // (g0 and D are even, so group g + i is odd exactly when i is)
     Stage st[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) load(g0 + i, st[i]);
-    store(0, st[0]);
+    store(0, st[0], false);
     __syncthreads();
     const int64_t nsteps = g1 - g0;
     int64_t g = g0;
@@ -199,8 +278,8 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
             // the next group and the multiplies of this one may interleave
             load(g + D + i, st[i]);
             __builtin_amdgcn_sched_barrier(0);
-            store((i + 1) & 1, st[(i + 1) % D]);
-            compute(i & 1);
+            store((i + 1) & 1, st[(i + 1) % D], (i + 1) & 1);
+            compute(i & 1, i & 1);
             __syncthreads();
         }
     }
@@ -209,36 +288,57 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     for (int j = 0; j < D - 1; ++j) {
         if (j < rem) {
             if (j > 0) {
-                store(j & 1, st[j]);
+                store(j & 1, st[j], j & 1);
                 __syncthreads();
             }
-            compute(j & 1);
+            compute(j & 1, j & 1);
         }
     }
 
     // The two k halves of each wave tile meet: the wave of half kh keeps row
     // block mb = kh and hands the other to its partner through LDS.
+    // (TQ2_0: the same with the fp32 block-scaled sums)
+    using E = std::conditional_t<FMT == 1, int32_t, float>;
+    using V = std::conditional_t<FMT == 1, i32x16, f32x16>;
     __syncthreads();                                       // every wave is done with the operand buffers
-    int32_t* xb = reinterpret_cast<int32_t*>(lds);
-    i32x16 fin[2];
-    if (kh == 0) {
+    E* xb = reinterpret_cast<E*>(lds);
+    V fin[2];
+    if constexpr (FMT == 1) {
+        if (kh == 0) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            fin[nb] = acc[0][nb];
+            for (int nb = 0; nb < 2; ++nb) {
+                fin[nb] = acc[0][nb];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[1][nb][r];
+                for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[1][nb][r];
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                fin[nb] = acc[1][nb];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[0][nb][r];
+            }
         }
     } else {
+        if (kh == 0) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            fin[nb] = acc[1][nb];
+            for (int nb = 0; nb < 2; ++nb) {
+                fin[nb] = facc[0][nb];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[0][nb][r];
+                for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = facc[1][nb][r];
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                fin[nb] = facc[1][nb];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = facc[0][nb][r];
+            }
         }
     }
     __syncthreads();
     {
-        const int32_t* pb = xb + ((1 - kh) * 4 + wq) * 32 * 64;
+        const E* pb = xb + ((1 - kh) * 4 + wq) * 32 * 64;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -253,24 +353,45 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st_coherent(mine + (nb * 16 + r) * kThreads + tid, fin[nb][r]);
+            for (int r = 0; r < 16; ++r)
+                st_coherent(mine + (nb * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[nb][r])));
         wait_vmem();
         __syncthreads();
         if (tid == 0) last_flag = atomicAdd(counters + tile, 1) == S - 1;
         __syncthreads();
         if (!last_flag) return;
-        for (int s = 0; s < S; ++s) {
-            if (s == split) continue;
-            const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+        if constexpr (FMT == 1) {
+            for (int s = 0; s < S; ++s) {
+                if (s == split) continue;
+                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) fin[nb][r] += ld_coherent(other + (nb * 16 + r) * kThreads + tid);
+            }
+        } else {
+            // fp32 partials added in split order (this split's own from registers)
+            V tot[2];
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) fin[nb][r] += ld_coherent(other + (nb * 16 + r) * kThreads + tid);
+                for (int r = 0; r < 16; ++r) tot[nb][r] = 0.0f;
+            for (int s = 0; s < S; ++s) {
+                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        tot[nb][r] += s == split ? fin[nb][r]
+                                                 : __builtin_bit_cast(float, ld_coherent(other + (nb * 16 + r) * kThreads + tid));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) fin[nb] = tot[nb];
         }
         if (tid == 0) st_coherent(counters + tile, 0);    // ready for the next call
     }
 
-    // Epilogue: y = ((float)acc * s_tok) * s_w (+ bias).  Lane (li, h) of half
+    // Epilogue: y = ((float)acc * s_tok) * s_w (+ bias); TQ2_0 y = acc * s_tok (+ bias).  Lane (li, h) of half
     // kh holds column wn 64 + nb 32 + li and rows wm 64 + kh 32 + 8 (r / 4) +
     // 4 h + r % 4; its output pointer is formed once, each store adds a
     // uniform row offset.  The stores of a full tile run as one straight block
@@ -280,7 +401,7 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float v = __fmul_rn(__fmul_rn(float(fin[nb][r]), xsv[r]), sw);
+            float v = FMT == 1 ? __fmul_rn(__fmul_rn(float(fin[nb][r]), xsv[r]), sw) : __fmul_rn(float(fin[nb][r]), xsv[r]);
             out[nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
         }
     const int64_t lrow = m0 + wm * 64 + kh * 32 + 4 * h, lcol = n0 + wn * 64 + li;
@@ -299,23 +420,44 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
                 if (lrow + ml < M && lcol + nb * 32 < N) yl[int64_t(ml) * N + nb * 32] = out[nb][r];
             }
     }
-    if (acc_out) {
+    if (FMT == 1 && acc_out) {
         int32_t* al = acc_out + lrow * N + lcol;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ml = 8 * (r >> 2) + (r & 3);
-                if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = fin[nb][r];
+                if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = int32_t(fin[nb][r]);
             }
     }
+}
+
+__global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N,
+                                                                int64_t K, const int8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs, int64_t M,
+                                                                const float* __restrict__ bias, float* __restrict__ y,
+                                                                int32_t* __restrict__ acc_out, int S,
+                                                                int32_t* __restrict__ part,
+                                                                int32_t* __restrict__ counters) {
+    gemm_i8_body<1>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters);
+}
+
+__global__ void __launch_bounds__(kThreads) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint16_t* __restrict__ scales, int64_t N,
+                                                                int64_t K, const int8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs, int64_t M,
+                                                                const float* __restrict__ bias, float* __restrict__ y,
+                                                                int S, int32_t* __restrict__ part,
+                                                                int32_t* __restrict__ counters) {
+    gemm_i8_body<2>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
 }
 
 #ifndef LL_GEMM_SLOTS
 #define LL_GEMM_SLOTS 256
 #endif
 // Split count: enough workgroups to cover the chip (LL_GEMM_SLOTS resident
-// workgroups) without leaving a split fewer than four groups.
+// workgroups) without leaving a split fewer than four groups (two TQ2_0
+// blocks: splits keep whole blocks).
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool allow = true) {
     if (!allow) return 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -347,6 +489,21 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_i2s_kernel), kGemmLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_i8_i2s_kernel, grid, block, kGemmLds, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
+                       part, counters);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
+                              const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
+    const int S = gemm_splits(M, N, K, ws != nullptr);
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int32_t* part = static_cast<int32_t*>(ws);
+    int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
+    const int64_t T = tiles * S;
+    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_tq2_kernel), kGemmLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_i8_tq2_kernel, grid, block, kGemmLds, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
                        part, counters);
     return hipGetLastError();
 }

@@ -32,6 +32,12 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,
                               int32_t* acc_out, void* ws, hipStream_t stream);
+// The same product with TQ2_0 weights (codes N*K/4 bytes, scales fp16
+// [N][K/256]); y = s_tok * sum_b s_b * d_b in fp32 (no acc_out); the same
+// workspace size and rules.
+hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                              const int8_t* xq, const float* xs, int64_t M, const float* bias, float* y,
+                              void* ws, hipStream_t stream);
 
 }  // namespace llk
 

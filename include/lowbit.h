@@ -178,9 +178,9 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    exact value (x split into five int8 planes per token, exact integer sums,
    fp64 epilogue; up to three tokens per pass over the weights).
    act == LL_ACT_I8: x int8 [M,K], xs fp32 [M] from ll_quantize_act; formats
-   i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32) and W1
-   (y = (float)((double)xs[m] * sum_g s_g * d_g), d_g the exact per-group
-   integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
+   i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32), TQ2_0 (as
+   ll_bitlinear_gemm) and W1 (y = (float)((double)xs[m] * sum_g s_g * d_g),
+   d_g the exact per-group integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
    [M,N].  workspace: device buffer of at least
    ll_gemv_workspace_size(w, act, M) bytes (may be NULL when that is 0);
    it is overwritten.  With W1 weights a narrow matrix splits K over
@@ -288,11 +288,15 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
    Format i2_s: y = ((float)acc * xs[m]) * scale.  xq: device int8 [M,K];
    xs: device fp32 [M]; bias: device fp32 [N] or NULL; y: device fp32 [M,N];
    acc_out: device int32 [M,N] receiving the raw integer dot (or NULL; i2_s
-   only).  Format W1 [BG "Method"]: as ll_bitlinear_gemv, in passes of up to
-   16 tokens that each read the weights once.
+   only).  Format TQ2_0 [TQ "TQ2_0 Format"; with int8 activations]: each
+   256-k block's exact int32 dot d_b is scaled by its fp16 scale into fp32,
+   y = (sum_b s_b * d_b) * xs[m] (+ bias), within 1e-5 * xs[m] * sum_b |s_b|
+   * sum_{k in b} |q_k| (+1e-6) of the exact value; the same result for
+   every split of K.  Format W1 [BG "Method"]: as ll_bitlinear_gemv, in
+   passes of up to 16 tokens that each read the weights once.
    workspace: device buffer of at least ll_gemm_workspace_size(w, M) bytes,
-   16-byte aligned (NULL allowed when that is 0).  For i2_s it holds the
-   split-K partial tiles and per-tile counters: it must be zero-filled
+   16-byte aligned (NULL allowed when that is 0).  For i2_s and TQ2_0 it
+   holds the split-K partial tiles and per-tile counters: it must be zero-filled
    before its first use, every call leaves the counters zero again, and two
    calls sharing one workspace must not run concurrently. */
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M);

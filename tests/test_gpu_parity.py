@@ -185,6 +185,60 @@ def test_i2s_gemm_i8_prefill_full(N, K):
     _i2s_i8_case(N, K, 512, 401 if N == 6912 else 402, rows=synth.sample_rows(7, N, 48))
 
 
+# ------------------------------------------------------------------ TQ2_0, int8 activations (GEMM)
+def _tq2_i8_case(N, K, M, seed, rows=None, bias=False, repeat=1):
+    """fp32 bound against the oracle's fp64 value: the kernel scales each
+    256-k block's exact int32 sum into fp32 (the same bound as the
+    fp32-activation paths, with T = s_tok * sum_b |s_b| sum_{k in b} |q|)."""
+    t = torch()
+    w, sc, blocks = make_tq2(seed, N, K)
+    q, s = oracle.quantize_bf16(synth.normal_bf16_bits(seed + 3, M, K))
+    W = L.upload_tq2(blocks, N, K)
+    b = synth.uniform_f32(seed + 4, N, -1, 1) if bias else None
+    outs = []
+    for _ in range(repeat):
+        y, _ = L.gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), bias=None if b is None else t.from_numpy(b).cuda())
+        outs.append(y.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "repeated calls differ"
+    y = outs[0] if rows is None else outs[0][:, rows]
+    y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s, rows)
+    if b is not None:
+        y_ref = y_ref + (b if rows is None else b[rows])[None, :].astype(np.float64)
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
+    assert ok, "N=%d K=%d M=%d: worst error / bound %.3f" % (N, K, M, worst)
+
+
+# split K (whole 256-k blocks): (5, 2560, 300) 5 ways, (300, 2048, 200) 4, (64, 4096, 40) 8,
+# (257, 1792, 130) 3 uneven ways (2, 2, 3 blocks)
+@pytest.mark.parametrize("N,K,M", [(77, 512, 65), (128, 256, 128), (200, 768, 17), (33, 256, 1), (130, 1280, 129),
+                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1792, 130)])
+def test_tq2_gemm_i8_small(N, K, M):
+    announce("tq2 gemm i8", N, K, M)
+    _tq2_i8_case(N, K, M, 620 + N + M, bias=(M == 65), repeat=2 if K >= 1792 else 1)
+
+
+@pytest.mark.parametrize("N,K", [(6912, 2560), (2560, 6912)])
+def test_tq2_gemm_i8_prefill_full(N, K):
+    announce("tq2 gemm i8 full", N, K)
+    _tq2_i8_case(N, K, 512, 411 if N == 6912 else 412, rows=synth.sample_rows(8, N, 48))
+
+
+def test_tq2_gemv_i8_matches_oracle():
+    """int8 activations with TQ2_0 at decode sizes (ll_bitlinear_gemv, M <= 16)
+    take the same kernel without split K."""
+    t = torch()
+    N, K, M = 300, 1024, 5
+    w, sc, blocks = make_tq2(13, N, K)
+    q, s = oracle.quantize_f32(_x(14, M, K))
+    W = L.upload_tq2(blocks, N, K)
+    announce("tq2 gemv i8")
+    y = L.gemv(W, t.from_numpy(q).cuda(), xs=t.from_numpy(s).cuda()).cpu().numpy()
+    y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s)
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
+    assert ok, worst
+
+
 def test_i2s_gemm_i8_workspace_reuse():
     """Two calls sharing one (zero-filled once) workspace: the split-K tile
     counters are left zero by the first call, so the second is exact too."""
