@@ -15,8 +15,8 @@ product, timed live with HIP events on its stream; its HBM traffic is taken
 from the committed rocprofv3 counter summary when that summary was made from
 the current kernel source), the CPU oracle timed on a bounded sample (one
 layer's seven products, repeated), and extras: single-call per-matrix GEMV
-times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM (TOPS against the
-int8 matrix-core peak).
+times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM with i2_s and
+TQ2_0 weights (TOPS against the int8 matrix-core peak).
 
 The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
 reported as "roofline_gemm": the GEMM kernel timed the same way (back-to-back
@@ -423,6 +423,16 @@ def extras_single(L, synth, torch, dev, stream):
         out["i2s_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
                                                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
                                                    "quantize_us": round(msq * 1e3, 2)}
+    # the same product with TQ2_0 weights (fp16 scale per 256-k block, U(0.005, 0.05))
+    for N, K in GEMM_SHAPES:
+        _, xb, xq, xsc, y, _ = gemm_operands(L, synth, torch, dev, stream, N, K)
+        sc = synth.uniform_f16_bits(424, N * K // 256, 0.005, 0.05)
+        Wt = L.upload_tq2(L.ll_pack_tq2(synth.ternary(423, N, K), sc), N, K, dev)
+        gws = torch.zeros((max(L.ll_gemm_workspace_size(Wt, 512), 16),), dtype=torch.uint8, device=dev)
+        ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemm(Wt, xq, xsc, 512, None, y, None, gws, st), 1, 20, stream)
+        tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
+        out["tq2_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
+                                                   "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
     return out
 
 

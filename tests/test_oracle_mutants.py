@@ -23,6 +23,9 @@ MUTANTS = [
      "int w = tq2_value_of((blk[e / 4] >> (6 - 2 * (e % 4))) & 3);"),
     ("tq2 scale byte order", "double s = orc_f16_to_f64((uint16_t)(blk[64] | (blk[65] << 8)));",
      "double s = orc_f16_to_f64((uint16_t)(blk[65] | (blk[64] << 8)));"),
+    ("tq2 i8 token scale dropped", "y[m * nr + i] = (double)s_tok[m] * acc;", "y[m * nr + i] = acc;"),
+    ("tq2 i8 block scale dropped", "acc += s * (double)d;", "acc += (double)d;"),
+    ("tq2 i8 activation index", "int64_t qv = q[m * K + b * 256 + e];", "int64_t qv = q[m * K + b * 256 + (e ^ 1)];"),
     ("w1 sign", "d += (int64_t)(2 * b - 1) * qv;", "d += (int64_t)(1 - 2 * b) * qv;"),
     ("w1 scale index", "S += orc_f16_to_f64(sc[n * (K / G) + g]) * (double)d;",
      "S += orc_f16_to_f64(sc[n * (K / G)]) * (double)d;"),
