@@ -52,6 +52,7 @@ def lib():
             "orc_f16_to_f64": (C.c_double, [C.c_uint16]),
             "orc_f64_to_f16": (C.c_uint16, [C.c_double]),
             "orc_bf16_to_f32": (C.c_float, [C.c_uint16]),
+            "orc_f32_to_bf16": (C.c_uint16, [C.c_float]),
             "orc_i2s_encode": (C.c_int, [P, I64, I64, C.c_float, P]),
             "orc_i2s_decode": (I64, [P, I64, I64, P, P]),
             "orc_i2s_gemv_f32": (None, [P, I64, I64, P, I64, P, I64, P, P]),
@@ -101,6 +102,13 @@ def f64_to_f16(v: float) -> int:
 
 def bf16_to_f32(b: int) -> float:
     return lib().orc_bf16_to_f32(int(b))
+
+
+def f32_to_bf16(y):
+    """bf16 bits (round to nearest, ties to even) of every fp32 value of y."""
+    y = np.asarray(y, np.float32)
+    f = lib().orc_f32_to_bf16
+    return np.array([f(float(v)) for v in y.reshape(-1)], np.uint16).reshape(y.shape)
 
 
 # ---------------------------------------------------------------- i2_s

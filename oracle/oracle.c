@@ -85,6 +85,29 @@ float orc_bf16_to_f32(uint16_t b)
     return f;
 }
 
+/* fp32 -> bf16, round to nearest, ties to the even bf16 [BG "API":
+   binary_linear returns bf16]: of the two bf16 values around f (f's bits
+   cut to 16, and the next one away from zero) the nearer one, the one with
+   an even last bit on a tie.  The next value past the largest finite bf16
+   counts as 2^128 (so overflow rounds to infinity as in IEEE); NaN gives the
+   quiet NaN 0x7FC0 with f's sign. */
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f)) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+    uint16_t lo = (uint16_t)(u >> 16);
+    if ((u & 0xFFFFu) == 0) return lo;                 /* exactly representable (also +-inf) */
+    uint16_t hi = (uint16_t)(lo + 1);
+    double fv = fabs((double)f);
+    double lv = fabs((double)orc_bf16_to_f32(lo));
+    double hv = (hi & 0x7FFFu) == 0x7F80u ? ldexp(1.0, 128) : fabs((double)orc_bf16_to_f32(hi));
+    double dl = fv - lv, dh = hv - fv;
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
 static void put_f32_le(uint8_t* p, float f)
 {
     uint32_t u;

@@ -31,6 +31,8 @@ MUTANTS = [
      "S += orc_f16_to_f64(sc[n * (K / G)]) * (double)d;"),
     ("w1 bit order", "int b = (bits[n * (K / 32) + k / 32] >> (k % 32)) & 1;",
      "int b = (bits[n * (K / 32) + k / 32] >> (31 - k % 32)) & 1;"),
+    ("bf16 tie rule", "return (lo & 1u) ? hi : lo;", "return (lo & 1u) ? lo : hi;"),
+    ("bf16 nearest", "if (dl < dh) return lo;", "if (dl > dh) return lo;"),
     ("quantize rounding", "float r = rintf(v);", "float r = truncf(v);"),
     ("quantize scale", "volatile float sv = a / 127.0f;", "volatile float sv = a / 128.0f;"),
     ("i8 epilogue operand", "volatile float t = (float)acc * s_tok[m];", "volatile float t = (float)acc * s_w;"),

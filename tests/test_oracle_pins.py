@@ -54,6 +54,43 @@ def test_f16_encode_matches_numpy(orc):
     assert np.array_equal(got, ref)
 
 
+def test_f32_to_bf16_round_trip(orc):
+    """Every bf16 value converts back to itself; NaNs stay NaN."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = np.array([orc.bf16_to_f32(int(b)) for b in bits], np.float32)
+    got = orc.f32_to_bf16(vals)
+    nan = np.isnan(vals)
+    assert np.array_equal(got[~nan], bits[~nan])
+    assert np.isnan(np.array([orc.bf16_to_f32(int(b)) for b in got[nan]], np.float32)).all()
+
+
+def test_f32_to_bf16_matches_integer_rounding(orc):
+    """Against the integer form of round-to-nearest-even on the bit pattern
+    (add 0x7FFF plus the lowest kept bit, cut 16 bits), a different
+    formulation from the oracle's comparison of the two neighbours, on
+    random finite floats of every magnitude."""
+    rng = np.random.default_rng(1234)
+    u = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    u = u[np.isfinite(f)]
+    ref = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16(u.view(np.float32)), ref)
+
+
+def test_f32_to_bf16_worked_cases(orc):
+    one = np.float32(1.0)
+    cases = [(one, 0x3F80),
+             (np.float32(1 + 2.0 ** -8), 0x3F80),                   # tie, even below
+             (np.float32(1 + 3 * 2.0 ** -8), 0x3F82),               # tie, even above
+             (np.float32(1 + 2.0 ** -8 + 2.0 ** -20), 0x3F81),      # past the tie
+             (np.float32(-(1 + 2.0 ** -8 + 2.0 ** -20)), 0xBF81),
+             (np.float32(np.finfo(np.float32).max), 0x7F80),        # past max bf16 + half ulp: infinity
+             (np.float32(2.0 ** -133), 0x0001),                     # the least bf16 subnormal, exact
+             (np.float32(2.0 ** -134), 0x0000)]                     # half of it: tie, even (zero)
+    for v, b in cases:
+        assert int(orc.f32_to_bf16(np.array([v]))[0]) == b, (v, b)
+
+
 def test_bf16_decode(orc):
     g = np.random.default_rng(6)
     bits = g.integers(0, 65536, 5000).astype(np.uint16)
