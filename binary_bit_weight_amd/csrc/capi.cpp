@@ -199,4 +199,78 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                       fn);
 }
 
+// One-shot bf16 layer: workspace = int8 x [M K] | token scales [M] | fp32 y
+// [M N] | the product's own workspace, each part on a 256-byte boundary.
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+struct LinearLayout {
+    size_t q, s, y, p, total;
+};
+static bool linear_layout(const ll_weights* w, int64_t M, LinearLayout& L) {
+    size_t prod;
+    if (w->fmt == LL_FMT_W1) {
+        if (w->group <= 0) return false;
+        prod = llk::w1_workspace(M, w->N, w->K, w->group);
+    } else if (w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) {
+        prod = llk::gemm_i8_workspace(M, w->N, w->K);
+    } else {
+        return false;
+    }
+    L.q = 0;
+    L.s = round256(size_t(M) * size_t(w->K));
+    L.y = L.s + round256(size_t(M) * 4);
+    L.p = L.y + round256(size_t(M) * size_t(w->N) * 4);
+    L.total = L.p + prod;
+    return true;
+}
+
+size_t ll_binary_linear_workspace_size(const ll_weights* w, int64_t M) {
+    if (!w || M < 1 || w->N <= 0 || w->K <= 0) return size_t(-1);
+    LinearLayout L;
+    return linear_layout(w, M, L) ? L.total : size_t(-1);
+}
+
+ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, const float* bias, uint16_t* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ll_binary_linear";
+    ll_status st = check_weights(w, fn);
+    if (st) return st;
+    if (M < 1 || M > 65535 * 128) return ll::fail(LL_ESHAPE, "ll_binary_linear: M must be in [1, 65535*128]");
+    if (w->K > (int64_t(1) << 20)) return ll::fail(LL_ERANGE, "ll_binary_linear: K <= 2^20");
+    if (!x || !y) return ll::fail(LL_EINVAL, "ll_binary_linear: x or y is NULL");
+    if (!aligned(x, 2) || !aligned(y, 2) || (bias && !aligned(bias, 4)))
+        return ll::fail(LL_EALIGN, "ll_binary_linear: x / y must be 2-byte and bias 4-byte aligned");
+    if (w->fmt == LL_FMT_W1) {
+        st = check_w1_device(w, fn);
+        if (st) return st;
+    }
+    LinearLayout L;
+    if (!linear_layout(w, M, L)) return ll::fail(LL_EINVAL, "ll_binary_linear: unsupported format");
+    if (!workspace || workspace_bytes < L.total)
+        return ll::failf(LL_EWORKSPACE, "ll_binary_linear: workspace of %zu bytes required", L.total);
+    if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_binary_linear: workspace must be 16-byte aligned");
+    char* base = static_cast<char*>(workspace);
+    int8_t* q = reinterpret_cast<int8_t*>(base + L.q);
+    float* s = reinterpret_cast<float*>(base + L.s);
+    float* y32 = reinterpret_cast<float*>(base + L.y);
+    void* pw = L.total > L.p ? base + L.p : nullptr;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = hip_status(llk::launch_quantize(x, true, M, w->K, q, s, hs), fn);
+    if (st) return st;
+    if (w->fmt == LL_FMT_W1)
+        st = hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
+                                            w->N, w->K, w->group, q, s, M, bias, y32, pw, hs),
+                        fn);
+    else if (w->fmt == LL_FMT_TQ2_0)
+        st = hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
+                                                static_cast<const uint16_t*>(w->scales), w->N, w->K, q, s, M, bias, y32,
+                                                pw, hs),
+                        fn);
+    else
+        st = hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, q, s, M, bias, y32,
+                                                nullptr, pw, hs),
+                        fn);
+    if (st) return st;
+    return hip_status(llk::launch_f32_to_bf16(y32, y, M * w->N, hs), fn);
+}
+
 }  // extern "C"

@@ -15,6 +15,8 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs,
                            hipStream_t stream);
+// bf16 bits (round to nearest, ties to even) of n fp32 values.
+hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStream_t stream);
 
 // W1A8 product (binary weights, int8 activations), any M (passes of up to 16
 // tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.

@@ -46,6 +46,8 @@ SIGNATURES = {
     "ll_bitlinear_gemv": (C.c_int, [_P, _I32, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "ll_gemm_workspace_size": (_SZ, [_P, _I64]),
     "ll_bitlinear_gemm": (C.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "ll_binary_linear_workspace_size": (_SZ, [_P, _I64]),
+    "ll_binary_linear": (C.c_int, [_P, _P, _I64, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -253,6 +255,19 @@ def ll_bitlinear_gemm(w: Weights, xq, xs, M, bias, y, acc_out=None, workspace=No
                                    _dev(workspace), ws_bytes, _stream(stream)))
 
 
+def ll_binary_linear_workspace_size(w: Weights, M) -> int:
+    n = lib().ll_binary_linear_workspace_size(w.ref, M)
+    if n == C.c_size_t(-1).value:
+        raise RuntimeError("ll_binary_linear_workspace_size: unsupported weights or M")
+    return int(n)
+
+
+def ll_binary_linear(w: Weights, x, M, bias, y, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ll_binary_linear(w.ref, _dev(x), M, _dev(bias), _dev(y), _dev(workspace), ws_bytes,
+                                  _stream(stream)))
+
+
 # ------------------------------------------------------------------ conveniences
 # Allocation and upload helpers around the entry points above (torch provides
 # the memory); each call still ends in exactly one library entry point.
@@ -298,6 +313,18 @@ def gemv(w: Weights, x, xs=None, bias=None, stream=None):
     # zero-filled: split-K counters (W1) must start at zero (each call leaves them zero)
     ws = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=x.device) if nws else None
     ll_bitlinear_gemv(w, act, x, xs, M, bias, y, ws, stream)
+    return y
+
+
+def binary_linear(w: Weights, x, bias=None, stream=None, workspace=None):
+    """y bf16 [M,N] = ll_binary_linear(x bf16 [M,K]); a zero-filled workspace
+    is allocated unless one is given."""
+    import torch
+    M = x.shape[0]
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.zeros((ll_binary_linear_workspace_size(w, M),), dtype=torch.uint8, device=x.device)
+    ll_binary_linear(w, x, M, bias, y, workspace, stream)
     return y
 
 

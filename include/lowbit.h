@@ -304,6 +304,24 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                             const float* bias, float* y, int32_t* acc_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* [BG "API": binary_linear(x, wq, wscale, bias, group_size), bf16 in and out]
+   One call from bf16 activations to bf16 outputs: per-token int8
+   quantization of x (as ll_quantize_act), the int8 product of
+   ll_bitlinear_gemm for the format (i2_s, TQ2_0 or W1, any M >= 1), the
+   bias added in fp32, and y rounded to bf16 (to nearest, ties to even;
+   NaN -> 0x7FC0 with its sign).  x: device bf16 bits [M,K]; bias: device
+   fp32 [N] or NULL; y: device bf16 bits [M,N].  The result is the bf16
+   rounding of what ll_quantize_act followed by ll_bitlinear_gemm gives.
+   workspace: device buffer of at least ll_binary_linear_workspace_size(w, M)
+   bytes, 16-byte aligned, zero-filled before its first use (it holds the
+   quantized x, the fp32 y and the product's split counters, which every
+   call leaves zero); two calls sharing one workspace must not run
+   concurrently.  Three launches on `stream`; returns (size_t)-1 from the
+   size function for an unsupported format or invalid arguments. */
+size_t ll_binary_linear_workspace_size(const ll_weights* w, int64_t M);
+ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, const float* bias, uint16_t* y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -157,6 +157,37 @@ def test_gemm_and_quantize_argument_errors():
     assert lib.ll_quantize_act(None, L.LL_DT_F32, 2, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == -1
 
 
+def test_binary_linear_arguments_and_workspace():
+    """ll_binary_linear: errors found before any launch, and the workspace
+    layout (int8 x | token scales | fp32 y | the product's workspace, each on
+    a 256-byte boundary); TQ2_0 products refuse acc_out."""
+    lib = L.lib()
+    w = _w(N=64, K=256)
+    M = 3
+    n = lib.ll_binary_linear_workspace_size(C.byref(w), M)
+    # 768 -> 768, 12 -> 256, 64*3*4 = 768 -> 768, no split workspace for one 128-row tile
+    assert n == 768 + 256 + 768 + lib.ll_gemm_workspace_size(C.byref(w), M)
+    wt = _w(fmt=L.LL_FMT_TQ2_0, N=64, K=256)
+    assert lib.ll_binary_linear_workspace_size(C.byref(wt), M) == n
+    w1 = _w(fmt=L.LL_FMT_W1, N=64, K=256, group=128)
+    assert lib.ll_binary_linear_workspace_size(C.byref(w1), M) > 768 + 256 + 768
+    assert lib.ll_binary_linear_workspace_size(C.byref(w), 0) == C.c_size_t(-1).value
+
+    def call(w, x=FAKE, M=M, y=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.ll_binary_linear(C.byref(w), C.c_void_p(x) if x else None, M, None, C.c_void_p(y) if y else None,
+                                    C.c_void_p(ws) if ws else None, wsb, None)
+    assert call(w, M=0) == -2
+    assert call(w, x=0) == -1
+    assert call(w, x=FAKE + 1) == -3
+    assert call(w, ws=0) == -5
+    assert call(w, wsb=n - 1) == -5
+    assert call(w, ws=FAKE + 8) == -3
+    assert call(_w(K=200)) == -2                       # i2_s needs K % 128 == 0
+    assert call(_w(fmt=L.LL_FMT_TQ2_0, scales=0)) == -1
+    assert lib.ll_bitlinear_gemm(C.byref(wt), C.c_void_p(FAKE), C.c_void_p(FAKE), 32, None, C.c_void_p(FAKE),
+                                 C.c_void_p(FAKE), C.c_void_p(FAKE), 1 << 30, None) == -1
+
+
 def test_workspace_sizes():
     w = _w(N=6912, K=2560)
     # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + block sums (16 ints per 256-k block, blocks
