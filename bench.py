@@ -15,8 +15,9 @@ product, timed live with HIP events on its stream; its HBM traffic is taken
 from the committed rocprofv3 counter summary when that summary was made from
 the current kernel source), the CPU oracle timed on a bounded sample (one
 layer's seven products, repeated), and extras: single-call per-matrix GEMV
-times, the TQ2_0 small-batch GEMV and the int8 prefill GEMM with i2_s and
-TQ2_0 weights (TOPS against the int8 matrix-core peak).
+times, the TQ2_0 small-batch GEMV, the int8 prefill GEMM with i2_s and
+TQ2_0 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
+layer.
 
 The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
 reported as "roofline_gemm": the GEMM kernel timed the same way (back-to-back
@@ -433,6 +434,28 @@ def extras_single(L, synth, torch, dev, stream):
         tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
         out["tq2_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
                                                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    # the one-shot bf16 layer (quantize + product + bf16 rounding, three launches)
+    N, K = GEMM_SHAPES[0]
+    W, xb, _, _, _, _ = gemm_operands(L, synth, torch, dev, stream, N, K)
+    yb = torch.empty((512, N), dtype=torch.bfloat16, device=dev)
+    lws = torch.zeros((L.ll_binary_linear_workspace_size(W, 512),), dtype=torch.uint8, device=dev)
+    ms = time_graph(torch, lambda i, st: L.ll_binary_linear(W, xb, 512, None, yb, lws, st), 1, 20, stream)
+    out["i2s_binary_linear_bf16_M512_%dx%d" % (N, K)] = {
+        "us": round(ms * 1e3, 2), "TOPS": round(2 * 512 * N * K / (ms * 1e-3) / 1e12, 1)}
+    N, K, G = W1_HEAD
+    bits, sc = w1_weights(L, synth, 503, N, K, G)
+    wbytes = bits.nbytes + sc.nbytes
+    reps = max(1, int(np.ceil(2 ** 29 / wbytes)))
+    Ws = [L.upload_w1(bits, sc, K, G, dev) for _ in range(reps)]
+    xb1 = torch.from_numpy(synth.normal_bf16_bits(512, 1, K).view(np.int16)).to(dev).view(torch.bfloat16)
+    yb1 = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    lws = torch.zeros((L.ll_binary_linear_workspace_size(Ws[0], 1),), dtype=torch.uint8, device=dev)
+    ms = time_graph(torch, lambda i, st: L.ll_binary_linear(Ws[i], xb1, 1, None, yb1, lws, st), reps, 2 * reps, stream)
+    out["w1a8_binary_linear_bf16_lm_head_%dx%d_M1" % (N, K)] = {
+        "us": round(ms * 1e3, 2), "GB_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del Ws
+    torch.cuda.empty_cache()
     return out
 
 
