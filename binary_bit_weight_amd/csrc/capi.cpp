@@ -148,8 +148,14 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
     return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: unknown activation type");
 }
 
+// W1 with group size 128 above 16 tokens runs on the int8 matrix cores
+// (fp32 group scaling); other W1 products run as passes of up to 16 tokens
+// with exact fp64 group scaling.
+static bool w1_mfma(const ll_weights* w, int64_t M) { return w->fmt == LL_FMT_W1 && w->group == 128 && M > 16; }
+
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     if (!w || M < 1) return size_t(-1);
+    if (w1_mfma(w, M) && w->K > 0 && w->N > 0) return llk::gemm_i8_workspace(M, w->N, w->K);
     if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->N, w->K, w->group);
     if ((w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) && w->K > 0 && w->N > 0)
         return llk::gemm_i8_workspace(M, w->N, w->K);
@@ -170,6 +176,18 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
         st = check_w1_device(w, fn);
         if (st) return st;
         if (acc_out) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for W1 (per-group scales)");
+        if (w1_mfma(w, M)) {
+            const size_t need = llk::gemm_i8_workspace(M, w->N, w->K);
+            if (need > 0 && (!workspace || workspace_bytes < need))
+                return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
+            if (need > 0 && !aligned(workspace, 16))
+                return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
+            return hip_status(llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes),
+                                                     static_cast<const uint16_t*>(w->scales), w->N, w->K, xq, xs, M,
+                                                     bias, y, need > 0 ? workspace : nullptr,
+                                                     static_cast<hipStream_t>(stream)),
+                              fn);
+        }
         const size_t need = llk::w1_workspace(M, w->N, w->K, w->group);
         if (!workspace || workspace_bytes < need)
             return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
@@ -207,7 +225,9 @@ struct LinearLayout {
 };
 static bool linear_layout(const ll_weights* w, int64_t M, LinearLayout& L) {
     size_t prod;
-    if (w->fmt == LL_FMT_W1) {
+    if (w1_mfma(w, M)) {
+        prod = llk::gemm_i8_workspace(M, w->N, w->K);
+    } else if (w->fmt == LL_FMT_W1) {
         if (w->group <= 0) return false;
         prod = llk::w1_workspace(M, w->N, w->K, w->group);
     } else if (w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) {
@@ -253,10 +273,16 @@ ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, co
     float* s = reinterpret_cast<float*>(base + L.s);
     float* y32 = reinterpret_cast<float*>(base + L.y);
     void* pw = L.total > L.p ? base + L.p : nullptr;
+    const bool w1m = w1_mfma(w, M);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     st = hip_status(llk::launch_quantize(x, true, M, w->K, q, s, hs), fn);
     if (st) return st;
-    if (w->fmt == LL_FMT_W1)
+    if (w1m)
+        st = hip_status(llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes),
+                                               static_cast<const uint16_t*>(w->scales), w->N, w->K, q, s, M, bias, y32,
+                                               pw, hs),
+                        fn);
+    else if (w->fmt == LL_FMT_W1)
         st = hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
                                             w->N, w->K, w->group, q, s, M, bias, y32, pw, hs),
                         fn);

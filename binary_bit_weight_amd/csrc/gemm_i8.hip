@@ -41,6 +41,15 @@
 // adds the fp32 partials in split order, so the result does not depend on
 // which split finishes last.
 //
+// W1 sign bits with fp16 scales per 128-weight group (binary-gemm card,
+// "Method"; group size 128 only) use it too: bit k of a row is bit k % 8 of
+// byte k / 8, so a 128-k group is 16 code bytes in natural k order and the
+// activation tile is stored as for i2_s.  A lane's 16 weights of a step are
+// 16 bits of its code dword; each nibble is spread to four bytes by one
+// multiply and a mask and mapped to -1 / +1 (b * 0xFE ^ 0xFF).  Every group
+// is a scale block; its scale is kept per LDS buffer, since the next group
+// is stored before this one is multiplied.
+//
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its exact
 // int32 partial tile to the workspace and increments the tile's counter; the
@@ -75,7 +84,8 @@ constexpr size_t kGemmLds = size_t(2) * kBuf > size_t(kXchg) ? size_t(2) * kBuf 
 #endif
 
 
-// FMT 1: i2_s, FMT 2: TQ2_0 (scales: fp16 [N][K/256]).
+// FMT 1: i2_s, FMT 2: TQ2_0 (scales: fp16 [N][K/256]), FMT 3: W1 with
+// G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).
 template <int FMT>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
@@ -100,10 +110,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t tile = L / S;
     const int split = int(L % S);
     const int64_t m0 = (tile % TM) * BM, n0 = (tile / TM) * BN;
-    const int64_t rowbytes = K / 4;
+    const int64_t rowbytes = FMT == 3 ? K / 8 : K / 4;
     const int64_t ng = K / 128;
     // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
-    const int64_t nsplit_units = FMT == 1 ? ng : K / 256, per_unit = FMT == 1 ? 1 : 2;
+    const int64_t nsplit_units = FMT != 2 ? ng : K / 256, per_unit = FMT != 2 ? 1 : 2;
     const int64_t g0 = per_unit * (nsplit_units * split / S), g1 = per_unit * (nsplit_units * (split + 1) / S);
 
     // Loads of one group: two 16-byte activation chunks (row idx / 8, chunk
@@ -121,33 +131,37 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int bcol = tid >> 2, bqt = tid & 3;
     int64_t ncl = n0 + bcol;
     ncl = ncl < N ? ncl : N - 1;
-    const uint8_t* bptr = codes + ncl * rowbytes + 8 * bqt;
-    // TQ2_0: block scales of this lane's two columns
+    const uint8_t* bptr = codes + ncl * rowbytes + (FMT == 3 ? 4 : 8) * bqt;
+    // TQ2_0 / W1: block scales of this lane's two columns
     const uint16_t* sptr[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         int64_t n = n0 + wn * 64 + nb * 32 + li;
         n = n < N ? n : N - 1;
-        sptr[nb] = FMT == 2 ? scales + n * (K / 256) : nullptr;
+        sptr[nb] = FMT == 2 ? scales + n * (K / 256) : FMT == 3 ? scales + n * (K / 128) : nullptr;
     }
 
     struct Stage {
         i32x4 a[2];
         u32x2 b;
-        uint16_t sc[FMT == 2 ? 2 : 1];                      // TQ2_0: the group's block scales
+        uint16_t sc[FMT == 1 ? 1 : 2];                      // TQ2_0 / W1: the group's block scales
     };
     auto load = [&](int64_t g, Stage& s) {
         const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
         for (int c = 0; c < 2; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
-        s.b = *(const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc);
-        if constexpr (FMT == 2)
+        if constexpr (FMT == 3)
+            s.b = u32x2{*(const __attribute__((address_space(1))) uint32_t*)(bptr + 16 * gc), 0u};
+        else
+            s.b = *(const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc);
+        if constexpr (FMT != 1)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) s.sc[nb] = ld2(sptr[nb] + gc / 2);
+            for (int nb = 0; nb < 2; ++nb) s.sc[nb] = ld2(sptr[nb] + (FMT == 2 ? gc / 2 : gc));
     };
-    // TQ2_0: scales of the block being multiplied, taken when its second
-    // (odd) group is stored
-    float curs[2] = {0.0f, 0.0f};
+    // scales of the block being multiplied: TQ2_0 in curs[0], taken when the
+    // block's second (odd) group is stored; W1 in curs[buf], the group in LDS
+    // buffer buf
+    float curs[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
     auto store = [&](int buf, const Stage& s, bool odd) {
         int8_t* A = lds + buf * kBuf;
         int8_t* B = A + BM * LDA;
@@ -155,7 +169,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         for (int c = 0; c < 2; ++c) {
             const int idx = tid + kThreads * c;
             int8_t* arow_l = &A[(idx >> 3) * LDA];
-            if constexpr (FMT == 1) {
+            if constexpr (FMT != 2) {
                 *reinterpret_cast<i32x4*>(arow_l + 16 * (idx & 7)) = s.a[c];
             } else {
                 // piece p (elements 16 p + 4 i + t in byte t of dword i) ->
@@ -173,11 +187,18 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                 *reinterpret_cast<uint32_t*>(arow_l + 96 + 4 * p) = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
             }
         }
-        *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
-        if constexpr (FMT == 2)
+        if constexpr (FMT == 3)
+            *reinterpret_cast<uint32_t*>(&B[bcol * LDB + 4 * bqt]) = s.b[0];
+        else
+            *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
+        if constexpr (FMT == 2) {
             if (odd)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) curs[nb] = half_bits_to_float(s.sc[nb]);
+                for (int nb = 0; nb < 2; ++nb) curs[0][nb] = half_bits_to_float(s.sc[nb]);
+        } else if constexpr (FMT == 3) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) curs[buf][nb] = half_bits_to_float(s.sc[nb]);
+        }
     };
 
     // epilogue operands, requested before the main loop so their latency is
@@ -199,7 +220,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     }
 
     i32x16 acc[2][2];
-    f32x16 facc[FMT == 2 ? 2 : 1][2];                      // TQ2_0: scaled block sums
+    f32x16 facc[FMT == 1 ? 1 : 2][2];                      // TQ2_0 / W1: scaled block sums
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -207,7 +228,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 acc[mb][nb][r] = 0;
-                if constexpr (FMT == 2) facc[mb][nb][r] = 0.0f;
+                if constexpr (FMT != 1) facc[mb][nb][r] = 0.0f;
             }
 
     // odd (TQ2_0): the group ends a 256-k block, whose sums are then scaled
@@ -215,7 +236,8 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // from zero
     auto compute = [&](int buf, bool odd) {
         const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 16 * h + 64 * kh;
-        const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + 16 * h;
+        // (W1: all 16 code bytes of the column's group; the lane takes its half of each dword)
+        const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + (FMT == 3 ? 0 : 16 * h);
         // i2_s: code byte j of this lane's 16 holds, in field t (bits 6 - 2t),
         // the weight of k = 32 t + 16 h + j: the B operand of step t.  TQ2_0:
         // field t (bits 2t) holds element 4 (16 h + j) + t, matching plane t.
@@ -234,11 +256,22 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             constexpr uint32_t table = FMT == 1 ? 0x000100FFu : 0xFFFE0100u;
             i32x4 bo[2];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb) {
+                if constexpr (FMT == 3) {
+                    // bits 16 h .. 16 h + 15 of code dword t = 2 kh + tt: k = 32 t + 16 h + j
+                    const uint32_t v = (uint32_t(bq[nb][2 * kh + tt]) >> (16 * h)) & 0xFFFFu;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    bo[nb][i] = int(__builtin_amdgcn_perm(0u, table, (uint32_t(bq[nb][i]) >> sh) & 0x03030303u));
-            const bool first = FMT == 2 && !odd && tt == 0;
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t sp = (((v >> (4 * i)) & 0xFu) * 0x00204081u) & 0x01010101u;   // bit e -> byte e
+                        bo[nb][i] = int((sp * 0xFEu) ^ 0xFFFFFFFFu);                                // 1 -> +1, 0 -> -1
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        bo[nb][i] = int(__builtin_amdgcn_perm(0u, table, (uint32_t(bq[nb][i]) >> sh) & 0x03030303u));
+                }
+            }
+            const bool first = (FMT == 2 && !odd && tt == 0) || (FMT == 3 && tt == 0);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -246,22 +279,24 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                     acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[tt][mb], bo[nb], first ? i32x16{} : acc[mb][nb],
                                                                         0, 0, 0);
         }
-        if constexpr (FMT == 2)
-            if (odd)
+        if constexpr (FMT != 1)
+            if (FMT == 3 || odd)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const float sc = FMT == 3 ? curs[buf][nb] : curs[0][nb];
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), curs[nb], facc[mb][nb][r]);
+                            facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), sc, facc[mb][nb][r]);
+                    }
     };
 
     // Group g + i is multiplied from LDS buffer i % 2; register stage i % D
     // holds group g + i from its load (D - 1 groups earlier) to its store
     // (one group earlier).  The main loop runs whole runs of D groups with no
     // early exit; the last 1 .. D - 1 groups follow it.
-    constexpr int D = FMT == 1 ? LL_GEMM_DEPTH : LL_GEMM_DEPTH_TQ2;
+    constexpr int D = FMT == 1 ? LL_GEMM_DEPTH : LL_GEMM_DEPTH_TQ2;   // (W1 as TQ2_0)
     static_assert(D % 2 == 0 && D >= 2, "even register depth");
     // (g0 and D are even, so group g + i is odd exactly when i is)
     Stage st[D];
@@ -442,6 +477,16 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __
     gemm_i8_body<1>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters);
 }
 
+__global__ void __launch_bounds__(kThreads) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits,
+                                                               const uint16_t* __restrict__ scales, int64_t N,
+                                                               int64_t K, const int8_t* __restrict__ xq,
+                                                               const float* __restrict__ xs, int64_t M,
+                                                               const float* __restrict__ bias, float* __restrict__ y,
+                                                               int S, int32_t* __restrict__ part,
+                                                               int32_t* __restrict__ counters) {
+    gemm_i8_body<3>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
+}
+
 __global__ void __launch_bounds__(kThreads) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes,
                                                                 const uint16_t* __restrict__ scales, int64_t N,
                                                                 int64_t K, const int8_t* __restrict__ xq,
@@ -490,6 +535,21 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_i8_i2s_kernel, grid, block, kGemmLds, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
                        part, counters);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
+                             const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
+    const int S = gemm_splits(M, N, K, ws != nullptr);
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int32_t* part = static_cast<int32_t*>(ws);
+    int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
+    const int64_t T = tiles * S;
+    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_w1_kernel), kGemmLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_i8_w1_kernel, grid, block, kGemmLds, stream, reinterpret_cast<const uint8_t*>(bits), scales,
+                       N, K, xq, xs, M, bias, y, S, part, counters);
     return hipGetLastError();
 }
 

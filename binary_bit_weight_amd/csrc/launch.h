@@ -34,6 +34,10 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,
                               int32_t* acc_out, void* ws, hipStream_t stream);
+// The same product with W1 weights of group size 128 (bits uint32 [N][K/32],
+// scales fp16 [N][K/128]); y = s_tok * sum_g s_g * d_g in fp32 (no acc_out).
+hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
+                             const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
 // The same product with TQ2_0 weights (codes N*K/4 bytes, scales fp16
 // [N][K/256]); y = s_tok * sum_b s_b * d_b in fp32 (no acc_out); the same
 // workspace size and rules.

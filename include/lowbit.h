@@ -292,8 +292,13 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
    256-k block's exact int32 dot d_b is scaled by its fp16 scale into fp32,
    y = (sum_b s_b * d_b) * xs[m] (+ bias), within 1e-5 * xs[m] * sum_b |s_b|
    * sum_{k in b} |q_k| (+1e-6) of the exact value; the same result for
-   every split of K.  Format W1 [BG "Method"]: as ll_bitlinear_gemv, in
-   passes of up to 16 tokens that each read the weights once.
+   every split of K.  Format W1 [BG "Method"]: with group size 128 and
+   M > 16 on the int8 matrix cores, each group's exact int32 dot scaled by
+   its fp16 scale into fp32, y = (sum_g s_g * d_g) * xs[m] (+ bias), within
+   1e-5 * xs[m] * sum_g |s_g| * sum_{k in g} |q_k| (+1e-6) of the exact
+   value and the same for every split of K; other group sizes, and M <= 16,
+   as ll_bitlinear_gemv (bit-exact), in passes of up to 16 tokens that each
+   read the weights once.
    workspace: device buffer of at least ll_gemm_workspace_size(w, M) bytes,
    16-byte aligned (NULL allowed when that is 0).  For i2_s and TQ2_0 it
    holds the split-K partial tiles and per-tile counters: it must be zero-filled

@@ -56,14 +56,66 @@ def test_w1a8_small_bitexact(N, K, G, M):
         "mismatches: %d" % int((y.view(np.uint32) != y_ref.view(np.uint32)).sum())
 
 
-@pytest.mark.parametrize("N,K,G,M", [(70, 1024, 128, 40), (20, 512, 32, 9), (129, 2560, 256, 33)])
+@pytest.mark.parametrize("N,K,G,M", [(70, 1024, 64, 40), (20, 512, 32, 9), (129, 2560, 256, 33)])
 def test_w1a8_gemm_passes_bitexact(N, K, G, M):
-    """ll_bitlinear_gemm with W1: M above one pass of tokens."""
+    """ll_bitlinear_gemm with W1 and a group size other than 128: M above one
+    pass of tokens, exact fp64 group scaling."""
     bits, scales = make_w1(5300 + N, N, K, G)
     q, s = _acts(5400 + M, M, K)
     announce("w1a8 gemm", N, K, G, M)
     y, y_ref = _run(bits, scales, K, G, q, s, use_gemm=True)
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+def _w1_bound(scales, K, G, q, s, rows=None):
+    """T = s_tok * sum_g |s_g| * sum_{k in g} |q_k| for the fp32 bound of the
+    matrix-core path (group scaling in fp32)."""
+    sg = np.abs(scales.view(np.float16).astype(np.float64))
+    if rows is not None:
+        sg = sg[rows]
+    qa = np.abs(q.astype(np.float64)).reshape(q.shape[0], K // G, G).sum(axis=2)
+    return s.astype(np.float64)[:, None] * (qa @ sg.T)
+
+
+# G = 128 above 16 tokens: the int8 matrix cores.  Ragged tiles, five groups
+# (K = 640), a bias, and split K: (5, 2560, 300) five ways, (64, 4096, 40)
+# eight, (300, 2048, 200) four, (257, 1664, 130) three uneven ways.
+@pytest.mark.parametrize("N,K,M", [(70, 1024, 40), (200, 640, 17), (130, 1280, 129), (5, 2560, 300), (64, 4096, 40),
+                                   (300, 2048, 200), (257, 1664, 130)])
+def test_w1a8_gemm_mfma_within_bound(N, K, M):
+    G = 128
+    bits, scales = make_w1(5600 + N, N, K, G)
+    q, s = _acts(5700 + M, M, K)
+    bias = synth.uniform_f32(5800 + N, N, -1, 1) if M == 129 else None
+    announce("w1a8 gemm mfma", N, K, M)
+    t = torch()
+    W = L.upload_w1(bits, scales, K, G)
+    outs = []
+    for _ in range(2 if K >= 1664 else 1):
+        y, _ = L.gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), bias=None if bias is None else t.from_numpy(bias).cuda())
+        outs.append(y.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "repeated calls differ"
+    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, bias=bias)
+    bound = 1e-5 * _w1_bound(scales, K, G, q, s) + 1e-6
+    err = np.abs(outs[0].astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= bound).all(), "worst error / bound %.3f" % float((err / bound).max())
+
+
+def test_w1a8_gemm_mfma_gate_full_sampled():
+    """The gate shape (17408 x 5120, G = 128) at M = 512 on the matrix cores."""
+    N, K, G, M = 17408, 5120, 128, 512
+    bits, scales = make_w1(5900, N, K, G)
+    q, s = _acts(5901, M, K)
+    rows = synth.sample_rows(5902, N, 32)
+    announce("w1a8 gemm mfma gate")
+    t = torch()
+    W = L.upload_w1(bits, scales, K, G)
+    y, _ = L.gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda())
+    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, rows=rows)
+    bound = 1e-5 * _w1_bound(scales, K, G, q, s, rows) + 1e-6
+    err = np.abs(y.cpu().numpy()[:, rows].astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= bound).all(), "worst error / bound %.3f" % float((err / bound).max())
 
 
 @pytest.mark.parametrize("N,M", [(7168, 1), (7168, 8), (17408, 1), (17408, 8), (248320, 1), (248320, 8)])
