@@ -15,8 +15,8 @@ product, timed live with HIP events on its stream; its HBM traffic is taken
 from the committed rocprofv3 counter summary when that summary was made from
 the current kernel source), the CPU oracle timed on a bounded sample (one
 layer's seven products, repeated), and extras: single-call per-matrix GEMV
-times, the TQ2_0 small-batch GEMV, the int8 prefill GEMM with i2_s and
-TQ2_0 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
+times, the TQ2_0 small-batch GEMV, the int8 prefill GEMM with i2_s, TQ2_0
+and W1 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
 layer.
 
 The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
@@ -434,6 +434,21 @@ def extras_single(L, synth, torch, dev, stream):
         tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
         out["tq2_gemm_i8_M512_%dx%d" % (N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
                                                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    # W1A8 (G = 128) at M = 512 on the int8 matrix cores: the gate and the LM head
+    for name, N, seed in [("gate", 17408, 502), ("lm_head", 248320, 503)]:
+        K, G = 5120, 128
+        bits, sc = w1_weights(L, synth, seed, N, K, G)
+        Ww = L.upload_w1(bits, sc, K, G, dev)
+        x = torch.from_numpy(synth.normal_f32(520, 512, K)).to(dev)
+        xq, xsc = L.quantize(x, stream)
+        y = torch.empty((512, N), dtype=torch.float32, device=dev)
+        gws = torch.zeros((max(L.ll_gemm_workspace_size(Ww, 512), 16),), dtype=torch.uint8, device=dev)
+        ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemm(Ww, xq, xsc, 512, None, y, None, gws, st), 1, 20, stream)
+        tops = 2 * 512 * N * K / (ms * 1e-3) / 1e12
+        out["w1a8_gemm_i8_M512_%s_%dx%d" % (name, N, K)] = {"us": round(ms * 1e3, 2), "TOPS": round(tops, 1),
+                                                             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+        del Ww, y
+        torch.cuda.empty_cache()
     # the one-shot bf16 layer (quantize + product + bf16 rounding, three launches)
     N, K = GEMM_SHAPES[0]
     W, xb, _, _, _, _ = gemm_operands(L, synth, torch, dev, stream, N, K)
