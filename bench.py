@@ -149,15 +149,23 @@ def build_decode_step(L, synth, torch, dev):
     return packed, items, weight_bytes
 
 
+_W1_HOST = {}
+
+
 def w1_weights(L, synth, seed, N, K, G):
     """Sign bits and fp16 group mean-abs scales of dense N(0, 0.02) rows
-    (generated in 4096-row chunks, converted by ll_w1_from_dense)."""
+    (generated in 4096-row chunks, converted by ll_w1_from_dense); built once
+    per (seed, N, K, G) and process."""
+    key = (seed, N, K, G)
+    if key in _W1_HOST:
+        return _W1_HOST[key]
     bits = np.empty((N, K // 32), np.uint32)
     scales = np.empty((N, K // G), np.uint16)
     for c in range((N + synth.CHUNK_ROWS - 1) // synth.CHUNK_ROWS):
         r0 = c * synth.CHUNK_ROWS
         rows = min(synth.CHUNK_ROWS, N - r0)
         bits[r0:r0 + rows], scales[r0:r0 + rows] = L.ll_w1_from_dense(synth.dense_chunk(seed, K, c, rows), G)
+    _W1_HOST[key] = (bits, scales)
     return bits, scales
 
 
