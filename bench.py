@@ -368,7 +368,7 @@ def extras_single(L, synth, torch, dev, stream):
         Ws = [L.upload_i2s(p, N, K, dev) for _ in range(reps)]
         x = torch.from_numpy(synth.normal_f32(6, 1, K)).to(dev)
         y = torch.empty((1, N), dtype=torch.float32, device=dev)
-        ws = torch.empty((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, 1),), dtype=torch.uint8, device=dev)
+        ws = torch.zeros((L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, 1),), dtype=torch.uint8, device=dev)
         ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_F32, x, None, 1, None, y, ws, st),
                         reps, 2 * reps, stream)
         out["i2s_gemv_f32_single_call_" + name] = {"us": round(ms * 1e3, 2),
@@ -383,7 +383,7 @@ def extras_single(L, synth, torch, dev, stream):
     for M in (1, 8, 16):
         x = torch.from_numpy(synth.normal_f32(303, M, K)).to(dev)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ws = torch.empty((max(L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, M), 16),), dtype=torch.uint8, device=dev)
+        ws = torch.zeros((max(L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_F32, M), 16),), dtype=torch.uint8, device=dev)
         ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_F32, x, None, M, None, y, ws, st),
                         reps, 2 * reps, stream)
         out["tq2_gemv_f32_single_call_6912x2560_M%d" % M] = {

@@ -54,6 +54,28 @@ ll_status check_weights(const ll_weights* w, const char* fn) {
     }
 }
 
+static_assert(llk::kCounterBytes == LL_WORKSPACE_COUNTER_BYTES, "counter region size of lowbit.h");
+
+// A device workspace: split-K counters in its first llk::kCounterBytes, then
+// the data region a product's launcher lays out.
+struct Workspace {
+    int32_t* counters;
+    void* data;
+};
+Workspace split_ws(void* ws) {
+    char* b = static_cast<char*>(ws);
+    return {reinterpret_cast<int32_t*>(b), b ? b + llk::kCounterBytes : nullptr};
+}
+// Bytes of a workspace whose data region needs `data` bytes (0: no workspace).
+size_t with_counters(size_t data) { return data ? llk::kCounterBytes + data : 0; }
+
+ll_status check_workspace(void* ws, size_t bytes, size_t need, const char* fn) {
+    if (need == 0) return LL_OK;
+    if (!ws || bytes < need) return ll::failf(LL_EWORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+    if (!aligned(ws, 16)) return ll::failf(LL_EALIGN, "%s: workspace must be 16-byte aligned", fn);
+    return LL_OK;
+}
+
 }  // namespace
 
 namespace llk {
@@ -90,9 +112,9 @@ ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, 
 
 size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M) {
     if (!w || M < 1 || M > 16 || w->K <= 0) return size_t(-1);
-    if (act == LL_ACT_F32)
-        return llk::planes_workspace(M, w->K);
-    if (act == LL_ACT_I8) return w->fmt == LL_FMT_W1 && w->group > 0 ? llk::w1_workspace(M, w->N, w->K, w->group) : 0;
+    if (act == LL_ACT_F32) return with_counters(llk::planes_workspace(M, w->K));
+    if (act == LL_ACT_I8)
+        return w->fmt == LL_FMT_W1 && w->group > 0 ? with_counters(llk::w1_workspace(M, w->N, w->K, w->group)) : 0;
     return size_t(-1);
 }
 
@@ -109,13 +131,11 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
     if (act == LL_ACT_F32) {
         if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0)
             return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: fp32 activations need format i2_s or TQ2_0");
-        const size_t need = llk::planes_workspace(M, w->K);
-        if (need > 0 && (!workspace || workspace_bytes < need))
-            return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
-        if (need > 0 && !aligned(workspace, 16))
-            return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
+        const size_t need = with_counters(llk::planes_workspace(M, w->K));
+        st = check_workspace(workspace, workspace_bytes, need, fn);
+        if (st) return st;
         return hip_status(llk::launch_gemv_planes(w->fmt, w->codes, w->scales, w->N, w->K, static_cast<const float*>(x),
-                                                  M, bias, y, workspace, s),
+                                                  M, bias, y, need ? split_ws(workspace).data : nullptr, s),
                           fn);
     }
     if (act == LL_ACT_I8) {
@@ -124,23 +144,25 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
         if (w->fmt == LL_FMT_I2S)
             return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K,
                                                       static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
-                                                      s),
+                                                      nullptr, s),
                               fn);
         if (w->fmt == LL_FMT_TQ2_0)
             return hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
                                                       static_cast<const uint16_t*>(w->scales), w->N, w->K,
-                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, s),
+                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
+                                                      s),
                               fn);
         if (w->fmt == LL_FMT_W1) {
             st = check_w1_device(w, fn);
             if (st) return st;
-            const size_t need = llk::w1_workspace(M, w->N, w->K, w->group);
-            if (!workspace || workspace_bytes < need)
-                return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemv: workspace of %zu bytes required", need);
-            if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: workspace must be 16-byte aligned");
+            const size_t need = with_counters(llk::w1_workspace(M, w->N, w->K, w->group));
+            st = check_workspace(workspace, workspace_bytes, need, fn);
+            if (st) return st;
+            const Workspace ws = split_ws(workspace);
             return hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes),
                                                   static_cast<const uint16_t*>(w->scales), w->N, w->K, w->group,
-                                                  static_cast<const int8_t*>(x), xs, M, bias, y, workspace, s),
+                                                  static_cast<const int8_t*>(x), xs, M, bias, y, ws.counters, ws.data,
+                                                  s),
                               fn);
         }
         return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: int8 activations with this format are not supported");
@@ -153,13 +175,36 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
 // with exact fp64 group scaling.
 static bool w1_mfma(const ll_weights* w, int64_t M) { return w->fmt == LL_FMT_W1 && w->group == 128 && M > 16; }
 
+// The product of ll_bitlinear_gemm on validated arguments; ws: a workspace
+// of ll_gemm_workspace_size bytes, or NULL when that is 0.
+static hipError_t run_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
+                           float* y, int32_t* acc_out, void* ws, hipStream_t s) {
+    const Workspace W = split_ws(ws);
+    if (w1_mfma(w, M))
+        return llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
+                                      w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s);
+    if (w->fmt == LL_FMT_W1)
+        return llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales), w->N,
+                                   w->K, w->group, xq, xs, M, bias, y, W.counters, W.data, s);
+    if (w->fmt == LL_FMT_TQ2_0)
+        return llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
+                                       w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s);
+    return llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y, acc_out,
+                                   W.counters, W.data, s);
+}
+
+// Data-region bytes of the product ll_bitlinear_gemm runs (0: no workspace).
+static size_t gemm_data_bytes(const ll_weights* w, int64_t M) {
+    if (w1_mfma(w, M)) return llk::gemm_i8_workspace(M, w->N, w->K);
+    if (w->fmt == LL_FMT_W1) return llk::w1_workspace(M, w->N, w->K, w->group);
+    return llk::gemm_i8_workspace(M, w->N, w->K);
+}
+
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
-    if (!w || M < 1) return size_t(-1);
-    if (w1_mfma(w, M) && w->K > 0 && w->N > 0) return llk::gemm_i8_workspace(M, w->N, w->K);
-    if (w->fmt == LL_FMT_W1 && w->group > 0) return llk::w1_workspace(M, w->N, w->K, w->group);
-    if ((w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) && w->K > 0 && w->N > 0)
-        return llk::gemm_i8_workspace(M, w->N, w->K);
-    return 0;
+    if (!w || M < 1 || w->K <= 0 || w->N <= 0) return size_t(-1);
+    if (w->fmt == LL_FMT_W1 && w->group <= 0) return size_t(-1);
+    if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0 && w->fmt != LL_FMT_W1) return size_t(-1);
+    return with_counters(gemm_data_bytes(w, M));
 }
 
 ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
@@ -176,70 +221,32 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
         st = check_w1_device(w, fn);
         if (st) return st;
         if (acc_out) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for W1 (per-group scales)");
-        if (w1_mfma(w, M)) {
-            const size_t need = llk::gemm_i8_workspace(M, w->N, w->K);
-            if (need > 0 && (!workspace || workspace_bytes < need))
-                return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
-            if (need > 0 && !aligned(workspace, 16))
-                return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
-            return hip_status(llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes),
-                                                     static_cast<const uint16_t*>(w->scales), w->N, w->K, xq, xs, M,
-                                                     bias, y, need > 0 ? workspace : nullptr,
-                                                     static_cast<hipStream_t>(stream)),
-                              fn);
-        }
-        const size_t need = llk::w1_workspace(M, w->N, w->K, w->group);
-        if (!workspace || workspace_bytes < need)
-            return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
-        if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
-        return hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes),
-                                              static_cast<const uint16_t*>(w->scales), w->N, w->K, w->group, xq, xs, M,
-                                              bias, y, workspace, static_cast<hipStream_t>(stream)),
-                          fn);
     }
-    if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0)
+    if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0 && w->fmt != LL_FMT_W1)
         return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s, TQ2_0 and W1 only");
     if (w->fmt == LL_FMT_TQ2_0 && acc_out)
         return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for TQ2_0 (per-block scales)");
-    const size_t need = llk::gemm_i8_workspace(M, w->N, w->K);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return ll::failf(LL_EWORKSPACE, "ll_bitlinear_gemm: workspace of %zu bytes required", need);
-    if (need > 0 && !aligned(workspace, 16))
-        return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: workspace must be 16-byte aligned");
-    if (w->fmt == LL_FMT_TQ2_0)
-        return hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
-                                                  static_cast<const uint16_t*>(w->scales), w->N, w->K, xq, xs, M, bias,
-                                                  y, need > 0 ? workspace : nullptr, static_cast<hipStream_t>(stream)),
-                          fn);
-    return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y,
-                                              acc_out, need > 0 ? workspace : nullptr,
-                                              static_cast<hipStream_t>(stream)),
+    const size_t need = with_counters(gemm_data_bytes(w, M));
+    st = check_workspace(workspace, workspace_bytes, need, fn);
+    if (st) return st;
+    return hip_status(run_gemm(w, xq, xs, M, bias, y, acc_out, need ? workspace : nullptr, static_cast<hipStream_t>(stream)),
                       fn);
 }
 
-// One-shot bf16 layer: workspace = int8 x [M K] | token scales [M] | fp32 y
-// [M N] | the product's own workspace, each part on a 256-byte boundary.
+// One-shot bf16 layer: workspace = split-K counters | the product's data
+// region | int8 x [M K] | token scales [M] | fp32 y [M N], each part on a
+// 256-byte boundary.
 static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct LinearLayout {
-    size_t q, s, y, p, total;
+    size_t q, s, y, total;
 };
 static bool linear_layout(const ll_weights* w, int64_t M, LinearLayout& L) {
-    size_t prod;
-    if (w1_mfma(w, M)) {
-        prod = llk::gemm_i8_workspace(M, w->N, w->K);
-    } else if (w->fmt == LL_FMT_W1) {
-        if (w->group <= 0) return false;
-        prod = llk::w1_workspace(M, w->N, w->K, w->group);
-    } else if (w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0) {
-        prod = llk::gemm_i8_workspace(M, w->N, w->K);
-    } else {
-        return false;
-    }
-    L.q = 0;
-    L.s = round256(size_t(M) * size_t(w->K));
+    if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0 && w->fmt != LL_FMT_W1) return false;
+    if (w->fmt == LL_FMT_W1 && w->group <= 0) return false;
+    L.q = round256(llk::kCounterBytes + gemm_data_bytes(w, M));
+    L.s = L.q + round256(size_t(M) * size_t(w->K));
     L.y = L.s + round256(size_t(M) * 4);
-    L.p = L.y + round256(size_t(M) * size_t(w->N) * 4);
-    L.total = L.p + prod;
+    L.total = L.y + size_t(M) * size_t(w->N) * 4;
     return true;
 }
 
@@ -265,36 +272,16 @@ ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, co
     }
     LinearLayout L;
     if (!linear_layout(w, M, L)) return ll::fail(LL_EINVAL, "ll_binary_linear: unsupported format");
-    if (!workspace || workspace_bytes < L.total)
-        return ll::failf(LL_EWORKSPACE, "ll_binary_linear: workspace of %zu bytes required", L.total);
-    if (!aligned(workspace, 16)) return ll::fail(LL_EALIGN, "ll_binary_linear: workspace must be 16-byte aligned");
+    st = check_workspace(workspace, workspace_bytes, L.total, fn);
+    if (st) return st;
     char* base = static_cast<char*>(workspace);
     int8_t* q = reinterpret_cast<int8_t*>(base + L.q);
     float* s = reinterpret_cast<float*>(base + L.s);
     float* y32 = reinterpret_cast<float*>(base + L.y);
-    void* pw = L.total > L.p ? base + L.p : nullptr;
-    const bool w1m = w1_mfma(w, M);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     st = hip_status(llk::launch_quantize(x, true, M, w->K, q, s, hs), fn);
     if (st) return st;
-    if (w1m)
-        st = hip_status(llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes),
-                                               static_cast<const uint16_t*>(w->scales), w->N, w->K, q, s, M, bias, y32,
-                                               pw, hs),
-                        fn);
-    else if (w->fmt == LL_FMT_W1)
-        st = hip_status(llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
-                                            w->N, w->K, w->group, q, s, M, bias, y32, pw, hs),
-                        fn);
-    else if (w->fmt == LL_FMT_TQ2_0)
-        st = hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
-                                                static_cast<const uint16_t*>(w->scales), w->N, w->K, q, s, M, bias, y32,
-                                                pw, hs),
-                        fn);
-    else
-        st = hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, q, s, M, bias, y32,
-                                                nullptr, pw, hs),
-                        fn);
+    st = hip_status(run_gemm(w, q, s, M, bias, y32, nullptr, base, hs), fn);
     if (st) return st;
     return hip_status(llk::launch_f32_to_bf16(y32, y, M * w->N, hs), fn);
 }

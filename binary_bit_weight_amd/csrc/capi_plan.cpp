@@ -2,7 +2,7 @@
 // host validates every item once and lays out device tables inside the
 // plan memory; every later run costs two launches: one preparing the
 // operands of every distinct activation (into the plan memory), one walking
-// the table of products.  Every K <= 2^20: fp4 digit planes on the fp4 matrix
+// the table of products.  Every K <= 2^17: fp4 digit planes on the fp4 matrix
 // cores, all M <= 16 tokens in one pass over the weights (gemv_fp4.hip);
 // larger K: int8 planes on the int8 matrix cores, up to three tokens per
 // pass (gemv_planes.hip).  An item may carry a
@@ -94,7 +94,7 @@ ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, 
     L.f4 = llk::f4_engine(M, L.kmax);
     for (int i = 0; i < count; ++i)
         if ((is_pair(items[i]) || items[i].norm_w) && !L.f4)
-            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: gated pairs and norms need every K <= 2^20", i);
+            return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: gated pairs and norms need every K <= 2^17", i);
     for (int i = 0; i < count; ++i) {
         const int64_t rows = L.f4 ? llk::f4_batch_rows(is_pair(items[i])) : llk::planes_batch_rows();
         int found = -1;

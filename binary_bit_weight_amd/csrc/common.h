@@ -78,6 +78,15 @@ __device__ __forceinline__ double ld_coherent64(const double* p) {
     return __longlong_as_double(__hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+// One split's arrival at its tile's counter: an agent-scope acquire-release
+// read-modify-write.  Its release half orders the partial sums that the
+// workgroup published before the barrier that precedes it (each wave waits
+// for its stores first); its acquire half orders the partial-sum loads that
+// the last arrival makes after the barrier that follows it.  Returns the
+// count before this arrival.
+__device__ __forceinline__ int32_t arrive_acq_rel(int32_t* c) {
+    return __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until every vector memory operation of this wave has completed
 // (gfx9 s_waitcnt: vmcnt = 0, expcnt and lgkmcnt not waited on).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -392,7 +392,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                 st_coherent(mine + (nb * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[nb][r])));
         wait_vmem();
         __syncthreads();
-        if (tid == 0) last_flag = atomicAdd(counters + tile, 1) == S - 1;
+        if (tid == 0) last_flag = arrive_acq_rel(counters + tile) == S - 1;
         __syncthreads();
         if (!last_flag) return;
         if constexpr (FMT == 1) {
@@ -520,15 +520,14 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K) {
     const int S = gemm_splits(M, N, K);
     if (S == 1) return 0;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    return size_t(tiles) * S * kTileInts * 4 + size_t(tiles) * 4;
+    return size_t(tiles) * S * kTileInts * 4;
 }
 
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq, const float* xs,
-                              int64_t M, const float* bias, float* y, int32_t* acc_out, void* ws, hipStream_t stream) {
-    const int S = gemm_splits(M, N, K, ws != nullptr);
+                              int64_t M, const float* bias, float* y, int32_t* acc_out, int32_t* counters, void* ws, hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
     int32_t* part = static_cast<int32_t*>(ws);
-    int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
     const int64_t T = tiles * S;
     const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_i2s_kernel), kGemmLds);
@@ -539,11 +538,11 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
 }
 
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
-                             const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
-    const int S = gemm_splits(M, N, K, ws != nullptr);
+                             const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
+                             hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
     int32_t* part = static_cast<int32_t*>(ws);
-    int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
     const int64_t T = tiles * S;
     const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_w1_kernel), kGemmLds);
@@ -554,11 +553,11 @@ hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64
 }
 
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
-                              const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
-    const int S = gemm_splits(M, N, K, ws != nullptr);
+                              const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
+                             hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
     int32_t* part = static_cast<int32_t*>(ws);
-    int32_t* counters = S > 1 ? part + tiles * S * int64_t(kTileInts) : nullptr;
     const int64_t T = tiles * S;
     const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_tq2_kernel), kGemmLds);

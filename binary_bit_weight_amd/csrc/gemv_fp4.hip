@@ -14,8 +14,10 @@
 // (the digits of X + 4*(8^12-1)/7, each minus 4).  Every digit is an e2m1
 // value, so the twelve digit planes are the rows of the fp4 operand A.  The
 // rounding to X is the only approximation: |x - X 2^(E-34)| <= 2^(E-35) <=
-// 2^-34 max|x|, so |y - y_exact| <= scale * K * 2^-34 * max|x|, far inside
-// 1e-5 * scale * sum|x| for any K the engine accepts (K <= 2^20).
+// 2^-34 max|x|, so |y - y_exact| <= scale * K * 2^-34 * max|x|.  The bound
+// the product promises is at least 1e-5 * scale * max|x| (sum|x| >= max|x|),
+// so the engine takes K <= 2^17 (2^17 * 2^-34 = 7.6e-6); longer rows go to
+// the int8-plane engine, whose truncation error is 2^-41 relative.
 //
 // Weights as fp4.  i2_s codes c = w + 1 in {0, 1, 2} are used as the e2m1
 // bit patterns 0000 / 0001 / 0010, i.e. the values c/2; masking a code word
@@ -78,7 +80,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kAWin = kGroup * kChunkBytes;            // activation digits of one tile's k range
 constexpr int kAPer = (kAWin / 16 + kThreads - 1) / kThreads;   // 16-byte window pieces per thread
 constexpr int kWgRows = kWaves * kWaveRows;
-constexpr int64_t kMaxK = int64_t(1) << 20;            // exact fp32 MFMA sums: 4 K < 2^23
+constexpr int64_t kMaxK = int64_t(1) << 17;            // the rounding of x stays inside the tolerance (exact fp32 MFMA sums up to 2^20)
 
 constexpr uint32_t kDigitNibbles = 0x5420ACDEu;        // nibble v: e2m1 code of the digit v - 4
 constexpr uint32_t kBiasLo = 0x24924u, kBiasHi = 0x24924u;   // 4*(8^12-1)/7 split at bit 18

@@ -494,7 +494,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     if (nsplit == 1) return;
     wait_vmem();
     __syncthreads();
-    if (tid == 0) last_flag = atomicAdd(counters + rb, 1) == nsplit - 1;
+    if (tid == 0) last_flag = arrive_acq_rel(counters + rb) == nsplit - 1;
     __syncthreads();
     if (!last_flag) return;
     for (int e = tid; e < kW1Waves * 2 * 16 * M; e += 64 * kW1Waves) {
@@ -583,13 +583,14 @@ int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
 // most one split per 1024-k window.
 int w1_splits(int64_t N, int64_t K) {
     const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
+    if (rbs > kMaxCounters) return 1;                  // one counter per row block
     const int64_t nwin = (K + kWinK1 - 1) / kWinK1;
     int64_t s = (LL_W1_TARGET_WGS + rbs - 1) / rbs;
     s = s < nwin ? s : nwin;
     s = s < kW1MaxSplits ? s : kW1MaxSplits;
     return int(s < 1 ? 1 : s);
 }
-// Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64, counters [rbs].
+// Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64.
 size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G) + 255) / 256 * 256; }
 
 }  // namespace
@@ -602,17 +603,17 @@ size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G) {
     const int ns = w1_splits(N, K);
     if (ns == 1) return w1_ws_bytes(Mp, K, G);
     const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
-    return w1_split_off(Mp, K, G) + size_t(rbs) * ns * kW1Rows * Mp * 8 + size_t(rbs) * 4;
+    return w1_split_off(Mp, K, G) + size_t(rbs) * ns * kW1Rows * Mp * 8;
 }
 
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
-                          const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream) {
+                          const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
+                          hipStream_t stream) {
     const int64_t tb = w1_tokens_per_pass(G);
+    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
     const int ns = w1_splits(N, K);
     const int64_t Mp = M < tb ? M : tb;
-    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
     double* part = ns > 1 ? reinterpret_cast<double*>(static_cast<char*>(ws) + w1_split_off(Mp, K, G)) : nullptr;
-    int32_t* counters = ns > 1 ? reinterpret_cast<int32_t*>(part + rbs * ns * kW1Rows * Mp) : nullptr;
     for (int64_t m0 = 0; m0 < M; m0 += tb) {               // every pass reads the weights once
         const int64_t Mb = M - m0 < tb ? M - m0 : tb;
         const int8_t* xb = xq + m0 * K;

@@ -8,6 +8,16 @@
 
 namespace llk {
 
+// Every device workspace the library is given starts with a region of
+// kCounterBytes that holds only split-K arrival counters (int32, one per
+// output tile or row block, at most kMaxCounters).  Each call that uses
+// counters leaves them zero again, and no call writes anything else there,
+// so one workspace zero-filled once serves calls of any shape and format in
+// turn.  The launchers take the counter base and the data region (the
+// workspace past the counters) as separate pointers.
+constexpr size_t kCounterBytes = 4096;
+constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
+
 // Raises a kernel's dynamic LDS limit to at least `bytes` on the current
 // device.  hipFuncSetAttribute is a host-side call that costs microseconds,
 // so each (kernel, device) pair is set once and remembered.
@@ -20,30 +30,32 @@ hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStrea
 
 // W1A8 product (binary weights, int8 activations), any M (passes of up to 16
 // tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.
-// Narrow matrices split K over workgroups: the workspace then also holds
-// partial sums and per-row-block counters (zero-filled before its first use;
-// every call leaves the counters zero).
+// ws (w1_workspace bytes) holds the prepared activation operands and, for a
+// narrow matrix whose K is split over workgroups, their fp64 partial sums;
+// counters: one per row block (zero on entry, left zero).
 size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G);
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
-                          const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
+                          const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
+                          hipStream_t stream);
 
 // int8-activation prefill product, format i2_s.  ws: gemm_i8_workspace bytes
-// (split-K partial tiles and per-tile counters; zero-filled before its first
-// use, the counters are left zero by every call), or NULL to forbid splits.
+// of split-K partial tiles and counters one per output tile (zero on entry,
+// left zero), or NULL (either) to forbid splits.
 size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,
-                              int32_t* acc_out, void* ws, hipStream_t stream);
+                              int32_t* acc_out, int32_t* counters, void* ws, hipStream_t stream);
 // The same product with W1 weights of group size 128 (bits uint32 [N][K/32],
 // scales fp16 [N][K/128]); y = s_tok * sum_g s_g * d_g in fp32 (no acc_out).
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
-                             const float* xs, int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
+                             const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
+                             hipStream_t stream);
 // The same product with TQ2_0 weights (codes N*K/4 bytes, scales fp16
 // [N][K/256]); y = s_tok * sum_b s_b * d_b in fp32 (no acc_out); the same
 // workspace size and rules.
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                               const int8_t* xq, const float* xs, int64_t M, const float* bias, float* y,
-                              void* ws, hipStream_t stream);
+                              int32_t* counters, void* ws, hipStream_t stream);
 
 }  // namespace llk
 
@@ -78,8 +90,8 @@ namespace llk {
 // formats i2_s (fmt 1) and TQ2_0 (fmt 2): activations as twelve base-8 digit
 // planes per token (one preparation launch), weights fed to the MFMAs straight
 // from registers, one 16-row MFMA block per token.  Used by prepared batches
-// with M <= 16 and every K <= 2^20.
-bool f4_engine(int64_t M, int64_t kmax);             // 1 <= M <= 16, every K <= 2^20
+// with M <= 16 and every K <= 2^17.
+bool f4_engine(int64_t M, int64_t kmax);             // 1 <= M <= 16, every K <= 2^17
 int64_t f4_op_stride(int64_t K);                     // bytes between two tokens' prepared digits
 size_t f4_operand_bytes(int64_t M, int64_t K);       // prepared digits of one activation (M tokens)
 int64_t f4_batch_rows(bool pair);                   // output rows per workgroup (a gated pair: rows of both)

@@ -34,6 +34,17 @@
  *     launched.  On error the function returns a negative ll_status, leaves
  *     every output untouched, and ll_last_error() describes the problem.
  *   - Device pointers must be 16-byte aligned (LL_EALIGN otherwise).
+ *   - Workspaces.  A device entry point that needs scratch memory takes a
+ *     caller-owned device buffer, 16-byte aligned, of at least the size its
+ *     ll_*_workspace_size function returns (LL_EWORKSPACE otherwise).  The
+ *     first LL_WORKSPACE_COUNTER_BYTES bytes of every workspace hold only
+ *     split-K arrival counters: zero-fill the buffer (at least those bytes)
+ *     once before its first use.  Every call leaves the counters zero and
+ *     writes nothing else there, so one buffer serves calls of any entry
+ *     point, format and shape in turn (an M = 8 call followed by an M = 1
+ *     call, say).  The rest of the buffer is overwritten by each call.
+ *     Calls that can overlap in time (different streams, or a graph replayed
+ *     concurrently) must not share a workspace.
  */
 #ifndef LOWBIT_H
 #define LOWBIT_H
@@ -45,7 +56,10 @@
 extern "C" {
 #endif
 
-#define LL_ABI_VERSION 2
+#define LL_ABI_VERSION 3
+
+/* Bytes at the start of every workspace reserved for split-K counters. */
+#define LL_WORKSPACE_COUNTER_BYTES 4096
 
 typedef enum {
     LL_OK = 0,
@@ -181,13 +195,10 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32), TQ2_0 (as
    ll_bitlinear_gemm) and W1 (y = (float)((double)xs[m] * sum_g s_g * d_g),
    d_g the exact per-group integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
-   [M,N].  workspace: device buffer of at least
-   ll_gemv_workspace_size(w, act, M) bytes (may be NULL when that is 0);
-   it is overwritten.  With W1 weights a narrow matrix splits K over
-   workgroups and the workspace also holds their per-row-block counters: it
-   must be zero-filled before its first use (every call leaves the counters
-   zero again), and two calls sharing one workspace must not run
-   concurrently. */
+   [M,N].  workspace: at least ll_gemv_workspace_size(w, act, M) bytes (may
+   be NULL when that is 0), under the workspace rules above; with W1 weights
+   a narrow matrix splits K over workgroups, which count their arrivals in
+   the workspace's counter region. */
 ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs,
                             int64_t M, const float* bias, float* y,
                             void* workspace, size_t workspace_bytes, void* stream);
@@ -204,7 +215,7 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
    walks a device-resident table of all products.  All items share act,
    format and M (1 <= M <= 16); N and K may differ.  Only act == LL_ACT_F32
    with i2_s or TQ2_0 is supported.  Items with the same x pointer and K
-   share one activation layout: with every K <= 2^20, twelve balanced base-8
+   share one activation layout: with every K <= 2^17, twelve balanced base-8
    fp4 digit planes per token, multiplied on the fp4 matrix cores with all M
    tokens in one pass over the weights (two passes for M > 8; y within the
    same tolerance as ll_bitlinear_gemv); otherwise the int8 planes of
@@ -299,11 +310,11 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
    value and the same for every split of K; other group sizes, and M <= 16,
    as ll_bitlinear_gemv (bit-exact), in passes of up to 16 tokens that each
    read the weights once.
-   workspace: device buffer of at least ll_gemm_workspace_size(w, M) bytes,
-   16-byte aligned (NULL allowed when that is 0).  For i2_s and TQ2_0 it
-   holds the split-K partial tiles and per-tile counters: it must be zero-filled
-   before its first use, every call leaves the counters zero again, and two
-   calls sharing one workspace must not run concurrently. */
+   workspace: at least ll_gemm_workspace_size(w, M) bytes (NULL allowed
+   when that is 0; (size_t)-1 for invalid arguments), under the workspace
+   rules above.  It holds the split-K partial tiles of narrow products (all
+   formats on the matrix cores) or the prepared operands of the W1 passes,
+   and the counters of both. */
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M);
 ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,
                             const float* bias, float* y, int32_t* acc_out,
@@ -317,11 +328,9 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
    NaN -> 0x7FC0 with its sign).  x: device bf16 bits [M,K]; bias: device
    fp32 [N] or NULL; y: device bf16 bits [M,N].  The result is the bf16
    rounding of what ll_quantize_act followed by ll_bitlinear_gemm gives.
-   workspace: device buffer of at least ll_binary_linear_workspace_size(w, M)
-   bytes, 16-byte aligned, zero-filled before its first use (it holds the
-   quantized x, the fp32 y and the product's split counters, which every
-   call leaves zero); two calls sharing one workspace must not run
-   concurrently.  Three launches on `stream`; returns (size_t)-1 from the
+   workspace: at least ll_binary_linear_workspace_size(w, M) bytes, under
+   the workspace rules above (it holds the quantized x, the product's
+   scratch and the fp32 y).  Three launches on `stream`; returns (size_t)-1 from the
    size function for an unsupported format or invalid arguments. */
 size_t ll_binary_linear_workspace_size(const ll_weights* w, int64_t M);
 ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, const float* bias, uint16_t* y,

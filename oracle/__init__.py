@@ -14,6 +14,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -83,6 +84,29 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+def cores() -> int:
+    """Host threads of the all-core runs: the CPUs this process may use, at
+    most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _by_rows(call, rows, N, threads):
+    """All-core form of a product: call(sub) evaluates the output rows `sub`
+    (int64 indices; None = all N rows) and returns arrays of shape
+    [M, len(sub)].  With threads > 1 the rows are cut into that many
+    contiguous slices, each evaluated by the same C function on its own
+    thread (ctypes releases the GIL for the call), and the results are
+    joined along the row axis.  Only the partition differs from a single
+    call: every output comes from the same scalar loop."""
+    if threads is None or threads <= 1:
+        return call(None if rows is None else _c(rows, np.int64))
+    r = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    parts = [p for p in np.array_split(r, min(threads, max(1, r.size))) if p.size]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(call, parts))
+    return tuple(np.concatenate([part[i] for part in res], axis=1) for i in range(len(res[0])))
+
+
 def _rows(rows, N):
     if rows is None:
         return None, N
@@ -131,29 +155,36 @@ def i2s_decode(packed: np.ndarray, N: int, K: int):
     return w, float(s[0]), int(bad)
 
 
-def i2s_gemv_f32(packed, N, K, x, rows=None):
-    """y[m, i] = scale * sum_k w[rows[i], k] * x[m, k] in fp64; also T."""
+def i2s_gemv_f32(packed, N, K, x, rows=None, threads=None):
+    """y[m, i] = scale * sum_k w[rows[i], k] * x[m, k] in fp64; also T.
+    threads: rows split over that many host threads (_by_rows)."""
     packed = _c(packed, np.uint8)
     x = _c(np.atleast_2d(x), np.float32)
     M = x.shape[0]
     assert x.shape[1] == K
-    r, nr = _rows(rows, N)
-    y = np.empty((M, nr), np.float64)
-    t = np.empty((M, nr), np.float64)
-    lib().orc_i2s_gemv_f32(_p(packed), N, K, _p(x), M, _p(r), nr, _p(y), _p(t))
-    return y, t
+
+    def one(sub):
+        r, nr = _rows(sub, N)
+        y = np.empty((M, nr), np.float64)
+        t = np.empty((M, nr), np.float64)
+        lib().orc_i2s_gemv_f32(_p(packed), N, K, _p(x), M, _p(r), nr, _p(y), _p(t))
+        return y, t
+    return _by_rows(one, rows, N, threads)
 
 
-def i2s_gemm_i8(packed, N, K, q, s_tok, rows=None):
+def i2s_gemm_i8(packed, N, K, q, s_tok, rows=None, threads=None):
     packed = _c(packed, np.uint8)
     q = _c(np.atleast_2d(q), np.int8)
     s_tok = _c(s_tok, np.float32)
     M = q.shape[0]
-    r, nr = _rows(rows, N)
-    y = np.empty((M, nr), np.float32)
-    acc = np.empty((M, nr), np.int64)
-    lib().orc_i2s_gemm_i8(_p(packed), N, K, _p(q), _p(s_tok), M, _p(r), nr, _p(y), _p(acc))
-    return y, acc
+
+    def one(sub):
+        r, nr = _rows(sub, N)
+        y = np.empty((M, nr), np.float32)
+        acc = np.empty((M, nr), np.int64)
+        lib().orc_i2s_gemm_i8(_p(packed), N, K, _p(q), _p(s_tok), M, _p(r), nr, _p(y), _p(acc))
+        return y, acc
+    return _by_rows(one, rows, N, threads)
 
 
 # ---------------------------------------------------------------- TQ2_0
@@ -179,18 +210,21 @@ def tq2_decode(blocks, N, K):
     return w, sc, int(bad)
 
 
-def tq2_gemv_f32(blocks, N, K, x, rows=None):
+def tq2_gemv_f32(blocks, N, K, x, rows=None, threads=None):
     blocks = _c(blocks, np.uint8)
     x = _c(np.atleast_2d(x), np.float32)
     M = x.shape[0]
-    r, nr = _rows(rows, N)
-    y = np.empty((M, nr), np.float64)
-    t = np.empty((M, nr), np.float64)
-    lib().orc_tq2_gemv_f32(_p(blocks), N, K, _p(x), M, _p(r), nr, _p(y), _p(t))
-    return y, t
+
+    def one(sub):
+        r, nr = _rows(sub, N)
+        y = np.empty((M, nr), np.float64)
+        t = np.empty((M, nr), np.float64)
+        lib().orc_tq2_gemv_f32(_p(blocks), N, K, _p(x), M, _p(r), nr, _p(y), _p(t))
+        return y, t
+    return _by_rows(one, rows, N, threads)
 
 
-def tq2_gemm_i8(blocks, N, K, q, s_tok, rows=None):
+def tq2_gemm_i8(blocks, N, K, q, s_tok, rows=None, threads=None):
     """int8 activations q [M, K] with scales s_tok [M] against TQ2_0 blocks:
     y = s_tok * sum_b s_b * sum_{k in b} w q in fp64 (exact integer block
     sums), and T = s_tok * sum_b |s_b| * sum_{k in b} |q|, both [M, len(rows)]."""
@@ -199,11 +233,14 @@ def tq2_gemm_i8(blocks, N, K, q, s_tok, rows=None):
     s_tok = _c(s_tok, np.float32)
     M = q.shape[0]
     assert q.shape[1] == K and s_tok.size == M
-    r, nr = _rows(rows, N)
-    y = np.empty((M, nr), np.float64)
-    t = np.empty((M, nr), np.float64)
-    lib().orc_tq2_gemm_i8(_p(blocks), N, K, _p(q), _p(s_tok), M, _p(r), nr, _p(y), _p(t))
-    return y, t
+
+    def one(sub):
+        r, nr = _rows(sub, N)
+        y = np.empty((M, nr), np.float64)
+        t = np.empty((M, nr), np.float64)
+        lib().orc_tq2_gemm_i8(_p(blocks), N, K, _p(q), _p(s_tok), M, _p(r), nr, _p(y), _p(t))
+        return y, t
+    return _by_rows(one, rows, N, threads)
 
 
 # ---------------------------------------------------------------- W1
@@ -236,7 +273,7 @@ def w1_from_dense(W, G):
     return bits, sc
 
 
-def w1a8_gemm(bits, scales, K, G, q, s_tok, bias=None, rows=None):
+def w1a8_gemm(bits, scales, K, G, q, s_tok, bias=None, rows=None, threads=None):
     bits = _c(bits, np.uint32)
     scales = _c(scales, np.uint16)
     N = bits.shape[0]
@@ -244,14 +281,17 @@ def w1a8_gemm(bits, scales, K, G, q, s_tok, bias=None, rows=None):
     s_tok = _c(s_tok, np.float32)
     M = q.shape[0]
     b = None if bias is None else _c(bias, np.float32)
-    r, nr = _rows(rows, N)
-    y = np.empty((M, nr), np.float32)
-    S = np.empty((M, nr), np.float64)
-    mism = lib().orc_w1a8_gemm(_p(bits), _p(scales), N, K, int(G), _p(q), _p(s_tok), M, _p(b),
-                               _p(r), nr, _p(y), _p(S))
-    if mism:
-        raise AssertionError("W1 identity disagreed %d times" % mism)
-    return y, S
+
+    def one(sub):
+        r, nr = _rows(sub, N)
+        y = np.empty((M, nr), np.float32)
+        S = np.empty((M, nr), np.float64)
+        mism = lib().orc_w1a8_gemm(_p(bits), _p(scales), N, K, int(G), _p(q), _p(s_tok), M, _p(b),
+                                   _p(r), nr, _p(y), _p(S))
+        if mism:
+            raise AssertionError("W1 identity disagreed %d times" % mism)
+        return y, S
+    return _by_rows(one, rows, N, threads)
 
 
 # ---------------------------------------------------------------- activations

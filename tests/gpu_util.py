@@ -10,6 +10,9 @@ from binary_bit_weight_amd import lowbit as L
 from binary_bit_weight_amd import synth
 
 
+TH = oracle.cores()        # host threads of the oracle on full-size comparisons
+
+
 def torch():
     import torch as t
     return t

@@ -2,17 +2,17 @@
 same seeded inputs.  Integer-activation paths must be bit-exact; fp32
 activation paths must satisfy |y_gpu - y_ref| <= 1e-5 * T + 1e-6.
 
-Small shapes are compared element by element (they still span several
-tiles and a ragged tail); the full configuration sizes are compared on
-sampled output rows (always including the first and the last row), in the
-launch configuration the benchmark times."""
+Every output is compared: small shapes (they still span several tiles and
+a ragged tail) and the full configuration sizes, the latter in the launch
+configuration the benchmark times, with the oracle's rows split over every
+host core (oracle.cores())."""
 import numpy as np
 import pytest
 
 import oracle
 from binary_bit_weight_amd import lowbit as L
 from binary_bit_weight_amd import synth
-from gpu_util import announce, f32_tol_ok, make_i2s, make_tq2, relu2_mul_tol_ok, torch
+from gpu_util import TH, announce, f32_tol_ok, make_i2s, make_tq2, relu2_mul_tol_ok, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +83,8 @@ def test_i2s_gemv_f32_decode_full(N, K, seed):
     announce("i2s gemv f32 full", N, K)
     W = L.upload_i2s(packed, N, K)
     y = L.gemv(W, t.from_numpy(x).cuda()).cpu().numpy()
-    rows = synth.sample_rows(seed, N, 96)
-    y_ref, tsum = oracle.i2s_gemv_f32(packed, N, K, x, rows)
-    ok, worst = f32_tol_ok(y[:, rows], y_ref, tsum)
+    y_ref, tsum = oracle.i2s_gemv_f32(packed, N, K, x, threads=TH)
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
     assert ok, "worst error / bound = %.3f" % worst
 
 
@@ -143,9 +142,8 @@ def test_tq2_gemv_f32_full(M):
     announce("tq2 gemv f32 full", M)
     W = L.upload_tq2(blocks, N, K)
     y = L.gemv(W, t.from_numpy(x).cuda()).cpu().numpy()
-    rows = synth.sample_rows(301, N, 64)
-    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x, rows)
-    ok, worst = f32_tol_ok(y[:, rows], y_ref, tsum)
+    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x, threads=TH)
+    ok, worst = f32_tol_ok(y, y_ref, tsum)
     assert ok, "worst error / bound = %.3f" % worst
 
 
@@ -161,7 +159,7 @@ def _i2s_i8_case(N, K, M, seed, rows=None, bias=False):
                     bias=None if b is None else t.from_numpy(b).cuda(), want_acc=True)
     y = y.cpu().numpy()
     acc = acc.cpu().numpy()
-    y_ref, acc_ref = oracle.i2s_gemm_i8(packed, N, K, q, s, rows)
+    y_ref, acc_ref = oracle.i2s_gemm_i8(packed, N, K, q, s, rows, threads=TH)
     if rows is not None:
         y, acc = y[:, rows], acc[:, rows]
     if b is not None:
@@ -182,7 +180,7 @@ def test_i2s_gemm_i8_small(N, K, M):
 @pytest.mark.parametrize("N,K", [(6912, 2560), (2560, 6912)])
 def test_i2s_gemm_i8_prefill_full(N, K):
     announce("i2s gemm i8 full", N, K)
-    _i2s_i8_case(N, K, 512, 401 if N == 6912 else 402, rows=synth.sample_rows(7, N, 48))
+    _i2s_i8_case(N, K, 512, 401 if N == 6912 else 402)
 
 
 # ------------------------------------------------------------------ TQ2_0, int8 activations (GEMM)
@@ -202,7 +200,7 @@ def _tq2_i8_case(N, K, M, seed, rows=None, bias=False, repeat=1):
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "repeated calls differ"
     y = outs[0] if rows is None else outs[0][:, rows]
-    y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s, rows)
+    y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s, rows, threads=TH)
     if b is not None:
         y_ref = y_ref + (b if rows is None else b[rows])[None, :].astype(np.float64)
     ok, worst = f32_tol_ok(y, y_ref, tsum)
@@ -221,7 +219,7 @@ def test_tq2_gemm_i8_small(N, K, M):
 @pytest.mark.parametrize("N,K", [(6912, 2560), (2560, 6912)])
 def test_tq2_gemm_i8_prefill_full(N, K):
     announce("tq2 gemm i8 full", N, K)
-    _tq2_i8_case(N, K, 512, 411 if N == 6912 else 412, rows=synth.sample_rows(8, N, 48))
+    _tq2_i8_case(N, K, 512, 411 if N == 6912 else 412)
 
 
 def test_tq2_gemv_i8_matches_oracle():
@@ -248,14 +246,13 @@ def test_i2s_gemm_i8_workspace_reuse():
     W = L.upload_i2s(packed, N, K)
     ws = t.zeros((max(L.ll_gemm_workspace_size(W, M), 16),), dtype=t.uint8, device="cuda")
     assert L.ll_gemm_workspace_size(W, M) > 0
-    rows = synth.sample_rows(651, N, 40)
     for rnd in range(2):
         q, s = oracle.quantize_bf16(synth.normal_bf16_bits(652 + rnd, M, K))
         y = t.empty((M, N), dtype=t.float32, device="cuda")
         announce("gemm workspace reuse", rnd)
         L.ll_bitlinear_gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, None, ws)
-        y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s, rows)
-        assert np.array_equal(y.cpu().numpy()[:, rows].view(np.uint32), y_ref.view(np.uint32)), rnd
+        y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s, threads=TH)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rnd
 
 
 def test_i2s_gemv_i8_matches_gemm():
@@ -277,7 +274,7 @@ def test_i2s_gemv_i8_matches_gemm():
                                       ("tq2", 3, False), ("tq2", 8, False), ("tq2", 16, False)])
 def test_gemv_plan_matches_oracle(fmt, M, big):
     """A prepared batch of products with mixed N and K (some sharing x) against
-    the oracle, row by row, run twice (second run with new x contents).  With
+    the oracle, every row, run twice (second run with new x contents).  With
     big, one product has K = 8448 (33 plane blocks, a ragged last window)."""
     t = torch()
     shapes = [(2560, 2560, 0), (6912, 2560, 0), (2560, 6912, 1), (37, 384 if fmt == "i2s" else 512, 2),
@@ -310,10 +307,9 @@ def test_gemv_plan_matches_oracle(fmt, M, big):
         plan.run()
         t.cuda.synchronize()
         for (W, xd, _, y), (packed, N, K, slot) in zip(items, refs):
-            rows = synth.sample_rows(N + rnd, N, 40)
             fn = oracle.i2s_gemv_f32 if fmt == "i2s" else oracle.tq2_gemv_f32
-            y_ref, tsum = fn(packed, N, K, xs_np[slot][0], rows)
-            ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
+            y_ref, tsum = fn(packed, N, K, xs_np[slot][0], threads=TH)
+            ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
             assert ok, "N=%d K=%d round %d: worst error / bound %.3f" % (N, K, rnd, worst)
 
 
@@ -351,16 +347,14 @@ def test_gemv_plan_relu2_mul_and_residual(fmt):
         plan.run()
         t.cuda.synchronize()
         for pg, pu, N, KK, slot, y in pairs:
-            rows = synth.sample_rows(N + rnd, N, 48) if N > 100 else np.arange(N)
-            g_ref, tg = fn(pg, N, KK, xs[slot], rows)
-            u_ref, tu = fn(pu, N, KK, xs[slot], rows)
-            ok, worst = relu2_mul_tol_ok(y.cpu().numpy()[:, rows], g_ref, tg, u_ref, tu)
+            g_ref, tg = fn(pg, N, KK, xs[slot], threads=TH)
+            u_ref, tu = fn(pu, N, KK, xs[slot], threads=TH)
+            ok, worst = relu2_mul_tol_ok(y.cpu().numpy(), g_ref, tg, u_ref, tu)
             assert ok, "pair N=%d K=%d round %d: worst error / bound %.3f" % (N, KK, rnd, worst)
             assert (g_ref > 0).any() and (g_ref < 0).any()
-        rows = synth.sample_rows(7 + rnd, 2560, 48)
-        y_ref, tsum = fn(pp, 2560, K, xs[0], rows)
-        want = y_ref + res[rows].astype(np.float64)[None, :]
-        got = yp.cpu().numpy()[:, rows].astype(np.float64)
+        y_ref, tsum = fn(pp, 2560, K, xs[0], threads=TH)
+        want = y_ref + res.astype(np.float64)[None, :]
+        got = yp.cpu().numpy().astype(np.float64)
         bound = 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)
         assert (np.abs(got - want) <= bound).all(), "residual round %d" % rnd
 
@@ -404,17 +398,15 @@ def test_gemv_plan_rmsnorm_prologue(fmt):
     t.cuda.synchronize()
     xn0 = oracle.rmsnorm(x0, g0, eps).astype(np.float32)
     xn2 = oracle.rmsnorm(x2, g2, eps).astype(np.float32)
-    rows = synth.sample_rows(875, N, 48)
     for name, xin, add in [("q", xn0, res), ("k", xn0, None), ("v", x0, None)]:
-        y_ref, tsum = fn(P[name], N, K, xin, rows)
-        want = y_ref + (0.0 if add is None else add[rows].astype(np.float64)[None, :])
-        got = Y[name].cpu().numpy()[:, rows].astype(np.float64)
+        y_ref, tsum = fn(P[name], N, K, xin, threads=TH)
+        want = y_ref + (0.0 if add is None else add.astype(np.float64)[None, :])
+        got = Y[name].cpu().numpy().astype(np.float64)
         bound = 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)
         assert (np.abs(got - want) <= bound).all(), name
-    frows = synth.sample_rows(876, 6912, 48)
-    g_ref, tg = fn(P["gate"], 6912, K, xn2, frows)
-    u_ref, tu = fn(P["up"], 6912, K, xn2, frows)
-    ok, worst = relu2_mul_tol_ok(Y["ffn"].cpu().numpy()[:, frows], g_ref, tg, u_ref, tu)
+    g_ref, tg = fn(P["gate"], 6912, K, xn2, threads=TH)
+    u_ref, tu = fn(P["up"], 6912, K, xn2, threads=TH)
+    ok, worst = relu2_mul_tol_ok(Y["ffn"].cpu().numpy(), g_ref, tg, u_ref, tu)
     assert ok, "normed gated pair: worst error / bound %.3f" % worst
     assert np.array_equal(Y["o"].cpu().numpy()[0].view(np.uint32), res.view(np.uint32))
 
@@ -555,7 +547,7 @@ def _bench():
 def test_decode_step_as_benched():
     """The headline workload exactly as bench.py builds and launches it: the
     30-layer i2_s decode step (210 products, 594.7 MB, one prepared batch),
-    sampled rows of three layers' seven products against the oracle."""
+    every output of every product against the oracle."""
     t = torch()
     bench = _bench()
     packed, items, wbytes = bench.build_decode_step(L, synth, t, "cuda")
@@ -564,18 +556,17 @@ def test_decode_step_as_benched():
     announce("decode step as benched", plan.plan.tiles)
     plan.run()
     t.cuda.synchronize()
-    for layer in (0, 17, 29):
+    for layer in range(bench.LAYERS):
         for r, (name, N, K, _) in enumerate(bench.ROLES):
             W, x, _, y = items[7 * layer + r]
-            rows = synth.sample_rows(layer * 7 + r, N, 12)
-            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, x.cpu().numpy(), rows)
-            ok, worst = f32_tol_ok(y.cpu().numpy()[:, rows], y_ref, tsum)
+            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, x.cpu().numpy(), threads=TH)
+            ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
             assert ok, "layer %d %s: worst error / bound %.3f" % (layer, name, worst)
 
 
 def test_fused_decode_step_as_benched():
     """The fused decode step of bench.py's extras (RMSNorm prologues, gated
-    ReLU² pairs, residual adds on O and down), sampled rows of two layers
+    ReLU² pairs, residual adds on O and down), every output of every layer
     against the oracle's rmsnorm, products and relu2_mul."""
     t = torch()
     bench = _bench()
@@ -586,22 +577,160 @@ def test_fused_decode_step_as_benched():
     plan.run()
     t.cuda.synchronize()
     eps = 1e-5
-    for layer in (3, 26):
+    for layer in range(bench.LAYERS):
         by = {name: items[7 * layer + r] for r, (name, _, _, _) in enumerate(bench.ROLES)}
         norms, res = [n.cpu().numpy() for n in extra[layer][0]], [v.cpu().numpy() for v in extra[layer][1]]
         xs = {name: by[name][1].cpu().numpy() for name in by}
-        for name, nidx, radd in [("q", 0, None), ("o", 1, 0), ("down", 3, 1)]:
+        for name, nidx, radd in [("q", 0, None), ("k", 0, None), ("v", 0, None), ("o", 1, 0), ("down", 3, 1)]:
             _, N, K, _ = [rr for rr in bench.ROLES if rr[0] == name][0]
-            rows = synth.sample_rows(layer + nidx, N, 12)
             xn = oracle.rmsnorm(xs[name], norms[nidx], eps).astype(np.float32)
-            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, xn, rows)
-            want = y_ref + (0.0 if radd is None else res[radd][rows].astype(np.float64)[None, :])
-            got = by[name][3].cpu().numpy()[:, rows].astype(np.float64)
+            y_ref, tsum = oracle.i2s_gemv_f32(packed[name][0], N, K, xn, threads=TH)
+            want = y_ref + (0.0 if radd is None else res[radd].astype(np.float64)[None, :])
+            got = by[name][3].cpu().numpy().astype(np.float64)
             assert (np.abs(got - want) <= 1e-5 * tsum + 1e-6 + 2.0 ** -23 * np.abs(want)).all(), (layer, name)
         N, K = bench.FFN, bench.HIDDEN
-        rows = synth.sample_rows(layer + 9, N, 12)
         xn = oracle.rmsnorm(xs["up"], norms[2], eps).astype(np.float32)
-        g_ref, tg = oracle.i2s_gemv_f32(packed["gate"][0], N, K, xn, rows)
-        u_ref, tu = oracle.i2s_gemv_f32(packed["up"][0], N, K, xn, rows)
-        ok, worst = relu2_mul_tol_ok(by["up"][3].cpu().numpy()[:, rows], g_ref, tg, u_ref, tu)
+        g_ref, tg = oracle.i2s_gemv_f32(packed["gate"][0], N, K, xn, threads=TH)
+        u_ref, tu = oracle.i2s_gemv_f32(packed["up"][0], N, K, xn, threads=TH)
+        ok, worst = relu2_mul_tol_ok(by["up"][3].cpu().numpy(), g_ref, tg, u_ref, tu)
         assert ok, "layer %d gated pair: worst error / bound %.3f" % (layer, worst)
+
+
+# ------------------------------------------------------------------ one workspace, many shapes and entry points
+def test_workspace_shared_across_shapes_and_entry_points():
+    """One zero-filled workspace serves, in turn: a W1 product of a narrow
+    matrix at M = 8 and M = 1 (split K, counters), an fp32 single call whose
+    int8 planes fill the data region, an i2_s GEMM split three ways at M = 512
+    and again at M = 640 (other tile counts), and the W1 product again.  The
+    split counters sit at the start of every workspace, which no call writes
+    with data, so each call is exact whatever ran before it."""
+    import gpu_util
+    t = torch()
+    K, G = 5120, 128
+    bits, scales = gpu_util.make_w1(501, 7168, K, G)
+    W1 = L.upload_w1(bits, scales, K, G)
+    _, _, p_i2s = make_i2s(402, 2560, 6912)
+    Wi = L.upload_i2s(p_i2s, 2560, 6912)
+    _, _, p_f = make_i2s(403, 3000, 2560)
+    Wf = L.upload_i2s(p_f, 3000, 2560)
+    need = max(L.ll_gemv_workspace_size(W1, L.LL_ACT_I8, 8), L.ll_gemv_workspace_size(Wf, L.LL_ACT_F32, 5),
+               L.ll_gemm_workspace_size(Wi, 512), L.ll_gemm_workspace_size(Wi, 640))
+    ws = t.zeros((need,), dtype=t.uint8, device="cuda")
+
+    def w1(M, seed):
+        q, s = oracle.quantize_f32(_x(seed, M, K))
+        y = t.empty((M, 7168), dtype=t.float32, device="cuda")
+        announce("shared workspace w1", M)
+        L.ll_bitlinear_gemv(W1, L.LL_ACT_I8, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, ws)
+        y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, threads=TH)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), ("w1", M)
+
+    def f32(M, seed):
+        x = _x(seed, M, 2560)
+        y = t.empty((M, 3000), dtype=t.float32, device="cuda")
+        announce("shared workspace f32", M)
+        L.ll_bitlinear_gemv(Wf, L.LL_ACT_F32, t.from_numpy(x).cuda(), None, M, None, y, ws)
+        y_ref, tsum = oracle.i2s_gemv_f32(p_f, 3000, 2560, x, threads=TH)
+        ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
+        assert ok, ("f32", M, worst)
+
+    def gemm(M, seed):
+        q, s = oracle.quantize_bf16(synth.normal_bf16_bits(seed, M, 6912))
+        y = t.empty((M, 2560), dtype=t.float32, device="cuda")
+        announce("shared workspace gemm", M)
+        L.ll_bitlinear_gemm(Wi, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, None, ws)
+        y_ref, _ = oracle.i2s_gemm_i8(p_i2s, 2560, 6912, q, s, threads=TH)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), ("gemm", M)
+
+    w1(8, 9100)
+    w1(1, 9101)
+    f32(5, 9102)
+    w1(1, 9103)
+    gemm(512, 9104)
+    gemm(640, 9105)
+    w1(8, 9106)
+    assert not ws[:4096].any().item()          # counters left zero
+
+
+# ------------------------------------------------------------------ TQ2_0 prepared batch at the full shape
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_tq2_plan_full(M):
+    """TQ2_0 6912 x 2560 as a prepared batch (the fp4 engine, all M tokens in
+    one pass over the weights; two passes at M = 16), every output."""
+    t = torch()
+    N, K = 6912, 2560
+    _, _, blocks = make_tq2(301, N, K)
+    x = _x(304 + M, M, K)
+    W = L.upload_tq2(blocks, N, K)
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    plan = L.GemvPlan([(W, t.from_numpy(x).cuda(), None, y)], M)
+    announce("tq2 plan full", M)
+    plan.run()
+    t.cuda.synchronize()
+    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x, threads=TH)
+    ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
+    assert ok, "worst error / bound %.3f" % worst
+
+
+# ------------------------------------------------------------------ the fp4 engine's K limit
+def test_plan_k_limit_of_the_fp4_engine():
+    """Rows of K = 2^17 still run on the fp4 digit engine; a batch holding a
+    row of K = 2^17 + 128 runs on the int8-plane engine instead (its rounding
+    error stays inside the bound for any K).  One large element among small
+    ones keeps sum|x| close to max|x|, where the bound is tightest."""
+    t = torch()
+    for K in (1 << 17, (1 << 17) + 128):
+        N = 40
+        _, _, packed = make_i2s(9200 + K % 7, N, K)
+        x = _x(9201, 1, K) * np.float32(1e-3)
+        x[0, 5] = np.float32(9.0)
+        W = L.upload_i2s(packed, N, K)
+        y = t.empty((1, N), dtype=t.float32, device="cuda")
+        plan = L.GemvPlan([(W, t.from_numpy(x).cuda(), None, y)], 1)
+        announce("plan K limit", K)
+        plan.run()
+        t.cuda.synchronize()
+        y_ref, tsum = oracle.i2s_gemv_f32(packed, N, K, x, threads=TH)
+        ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
+        assert ok, "K=%d: worst error / bound %.3f" % (K, worst)
+
+
+# ------------------------------------------------------------------ single calls: extreme activations
+@pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 2), ("i2s", 5), ("tq2", 1), ("tq2", 3)])
+def test_gemv_f32_single_call_extreme_x(fmt, M):
+    """The single-call fp32 engine (int8 planes; fused at M = 1) on
+    activations at the ends of the fp32 range: every token subnormal
+    (|x| < 2^-126), subnormals beside one normal element, elements near the
+    largest finite fp32 (K and the scale keep y finite), and +-max|x|
+    everywhere.  Every token of a call gets the same case."""
+    t = torch()
+    N, K = 70, 256 if fmt == "tq2" else 128
+    rng = synth.rng(9300 + M)
+    sign = np.where(rng.random((M, K)) < 0.5, -1.0, 1.0).astype(np.float32)
+    cases = {
+        "subnormal": (synth.normal_f32(9301, M, K) * np.float32(1e-41)).astype(np.float32),
+        "subnormal_and_one_normal": None,
+        "near_max": sign * np.float32(3.0e38) * rng.random((M, K)).astype(np.float32),
+        "max_everywhere": sign * np.float32(2.5e37),
+    }
+    mixed = (synth.normal_f32(9302, M, K) * np.float32(1e-40)).astype(np.float32)
+    mixed[:, 3] = np.float32(1.5e-30)
+    cases["subnormal_and_one_normal"] = mixed
+    if fmt == "i2s":
+        _, _, packed = make_i2s(9310, N, K, scale=1e-3)
+        W = L.upload_i2s(packed, N, K)
+        fn = oracle.i2s_gemv_f32
+    else:
+        w = synth.ternary(9311, N, K)
+        sc = np.full(N * K // 256, 0x1400, np.uint16)            # fp16 2^-10
+        packed = L.ll_pack_tq2(w, sc)
+        W = L.upload_tq2(packed, N, K)
+        fn = oracle.tq2_gemv_f32
+    for name, x in cases.items():
+        assert np.isfinite(x).all()
+        announce("single call extreme x", fmt, M, name)
+        y = L.gemv(W, t.from_numpy(np.ascontiguousarray(x)).cuda()).cpu().numpy()
+        y_ref, tsum = fn(packed, N, K, x)
+        assert np.isfinite(y_ref).all() and (np.abs(y_ref) < 3.4e38).all()
+        ok, worst = f32_tol_ok(y, y_ref, tsum)
+        assert ok, "%s: worst error / bound %.3f" % (name, worst)

@@ -1,14 +1,15 @@
 """GPU parity of the W1A8 path (binary sign-bit weights, fp16 group scales,
 int8 per-token activations) against the CPU oracle: bit-exact, every element
-for the small shapes, sampled rows for the full workload shapes (hidden
-5120, G = 128, N = 7168 / 17408 / 248320, M = 1 and 8)."""
+of the small shapes and of the full workload shapes (hidden 5120, G = 128,
+N = 7168 / 17408 / 248320, M = 1 and 8), the oracle's rows split over every
+host core for the latter."""
 import numpy as np
 import pytest
 
 import oracle
 from binary_bit_weight_amd import lowbit as L
 from binary_bit_weight_amd import synth
-from gpu_util import announce, make_w1, torch
+from gpu_util import TH, announce, make_w1, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +30,7 @@ def _run(bits, scales, K, G, q, s, bias=None, rows=None, use_gemm=False):
     else:
         y = L.gemv(W, xq, xs, bias=b)
     y = y.cpu().numpy()
-    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, bias=bias, rows=rows)
+    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, bias=bias, rows=rows, threads=TH)
     if rows is not None:
         y = y[:, rows]
     return y, y_ref
@@ -102,30 +103,29 @@ def test_w1a8_gemm_mfma_within_bound(N, K, M):
     assert (err <= bound).all(), "worst error / bound %.3f" % float((err / bound).max())
 
 
-def test_w1a8_gemm_mfma_gate_full_sampled():
-    """The gate shape (17408 x 5120, G = 128) at M = 512 on the matrix cores."""
+def test_w1a8_gemm_mfma_gate_full():
+    """The gate shape (17408 x 5120, G = 128) at M = 512 on the matrix cores,
+    every output."""
     N, K, G, M = 17408, 5120, 128, 512
     bits, scales = make_w1(5900, N, K, G)
     q, s = _acts(5901, M, K)
-    rows = synth.sample_rows(5902, N, 32)
     announce("w1a8 gemm mfma gate")
     t = torch()
     W = L.upload_w1(bits, scales, K, G)
     y, _ = L.gemm(W, t.from_numpy(q).cuda(), t.from_numpy(s).cuda())
-    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, rows=rows)
-    bound = 1e-5 * _w1_bound(scales, K, G, q, s, rows) + 1e-6
-    err = np.abs(y.cpu().numpy()[:, rows].astype(np.float64) - y_ref.astype(np.float64))
+    y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s, threads=TH)
+    bound = 1e-5 * _w1_bound(scales, K, G, q, s) + 1e-6
+    err = np.abs(y.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
     assert (err <= bound).all(), "worst error / bound %.3f" % float((err / bound).max())
 
 
 @pytest.mark.parametrize("N,M", [(7168, 1), (7168, 8), (17408, 1), (17408, 8), (248320, 1), (248320, 8)])
-def test_w1a8_full_shapes_sampled(N, M):
+def test_w1a8_full_shapes(N, M):
     K, G = 5120, 128
     bits, scales = make_w1(501 if N == 7168 else 502 if N == 17408 else 503, N, K, G)
     q, s = _acts(510 + M, M, K)
-    rows = synth.sample_rows(N + M, N, 64)
     announce("w1a8 full", N, M)
-    y, y_ref = _run(bits, scales, K, G, q, s, rows=rows)
+    y, y_ref = _run(bits, scales, K, G, q, s)
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
 
 

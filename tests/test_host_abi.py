@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES), "binding and header disagree"
-    assert L.ll_abi_version() == 2
+    assert L.ll_abi_version() == 3
     assert L.ll_strerror(-5) == "workspace missing or too small"
 
 
@@ -114,6 +114,7 @@ def test_validate_finds_first_bad_code():
 
 
 # ------------------------------------------------------------- device-entry validation (no GPU needed)
+CB = 4096                                          # LL_WORKSPACE_COUNTER_BYTES
 FAKE = 0x10000            # aligned, never dereferenced: validation fails first
 
 
@@ -159,18 +160,19 @@ def test_gemm_and_quantize_argument_errors():
 
 def test_binary_linear_arguments_and_workspace():
     """ll_binary_linear: errors found before any launch, and the workspace
-    layout (int8 x | token scales | fp32 y | the product's workspace, each on
-    a 256-byte boundary); TQ2_0 products refuse acc_out."""
+    layout (split-K counters | the product's data | int8 x | token scales |
+    fp32 y, each on a 256-byte boundary); TQ2_0 products refuse acc_out."""
     lib = L.lib()
     w = _w(N=64, K=256)
     M = 3
     n = lib.ll_binary_linear_workspace_size(C.byref(w), M)
-    # 768 -> 768, 12 -> 256, 64*3*4 = 768 -> 768, no split workspace for one 128-row tile
-    assert n == 768 + 256 + 768 + lib.ll_gemm_workspace_size(C.byref(w), M)
+    # counters 4096, no split data for one 128-row tile, x 768 -> 768, scales 12 -> 256, y 64*3*4 = 768
+    assert lib.ll_gemm_workspace_size(C.byref(w), M) == 0
+    assert n == CB + 768 + 256 + 768
     wt = _w(fmt=L.LL_FMT_TQ2_0, N=64, K=256)
     assert lib.ll_binary_linear_workspace_size(C.byref(wt), M) == n
     w1 = _w(fmt=L.LL_FMT_W1, N=64, K=256, group=128)
-    assert lib.ll_binary_linear_workspace_size(C.byref(w1), M) > 768 + 256 + 768
+    assert lib.ll_binary_linear_workspace_size(C.byref(w1), M) > CB + 768 + 256 + 768
     assert lib.ll_binary_linear_workspace_size(C.byref(w), 0) == C.c_size_t(-1).value
 
     def call(w, x=FAKE, M=M, y=FAKE, ws=FAKE, wsb=1 << 30):
@@ -192,11 +194,11 @@ def test_workspace_sizes():
     w = _w(N=6912, K=2560)
     # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + block sums (16 ints per 256-k block, blocks
     # padded to a multiple of 4) + exponents + row sums
-    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 2) == (10 * 2560 + 12 * 64 + 8 + 10 * 4 + 15) // 16 * 16
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 2) == CB + (10 * 2560 + 12 * 64 + 8 + 10 * 4 + 15) // 16 * 16
     # M = 1 with K <= 8192 builds the planes inside the product kernel
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == 0
     w2 = _w(N=64, K=8320)
-    assert L.lib().ll_gemv_workspace_size(C.byref(w2), L.LL_ACT_F32, 1) == (5 * 8320 + 36 * 64 + 4 + 5 * 4 + 15) // 16 * 16
+    assert L.lib().ll_gemv_workspace_size(C.byref(w2), L.LL_ACT_F32, 1) == CB + (5 * 8320 + 36 * 64 + 4 + 5 * 4 + 15) // 16 * 16
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 8) > 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 17) == 2 ** 64 - 1
@@ -256,16 +258,16 @@ def test_w1_device_argument_errors_and_workspace():
     w = _w(fmt=L.LL_FMT_W1, N=64, K=5120, group=128)
     # A rows: 40 chunks x (2 digits x 8 tokens) x 128 B, then int32 group sums [8][40]; one row block
     # of 128 splits K five ways (one per 1024-k window): fp64 partial sums [5][128][tokens] at the
-    # next 256-byte boundary, then one int32 counter
-    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 8) == 40 * 16 * 128 + 8 * 40 * 4 + 5 * 128 * 8 * 8 + 4
+    # next 256-byte boundary; all of it after the 4096-byte counter region (one counter in use)
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 8) == CB + 40 * 16 * 128 + 8 * 40 * 4 + 5 * 128 * 8 * 8
     base1 = 40 * 2 * 128 + 40 * 4
-    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == (base1 + 255) // 256 * 256 + 5 * 128 * 8 + 4
+    assert lib.ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == CB + (base1 + 255) // 256 * 256 + 5 * 128 * 8
     # a wide matrix (1940 row blocks) is not split
     wide = _w(fmt=L.LL_FMT_W1, N=248320, K=5120, group=128)
-    assert lib.ll_gemv_workspace_size(C.byref(wide), L.LL_ACT_I8, 1) == base1
+    assert lib.ll_gemv_workspace_size(C.byref(wide), L.LL_ACT_I8, 1) == CB + base1
     # G = 32: four group slots per 128-k chunk, passes of 4 tokens
     w32 = _w(fmt=L.LL_FMT_W1, N=64, K=512, group=32)
-    assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == 4 * 32 * 128 + 4 * 16 * 4
+    assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == CB + 4 * 32 * 128 + 4 * 16 * 4
     assert _gemv(w, act=L.LL_ACT_I8, M=8, ws=0) == -5
     assert _gemv(w, act=L.LL_ACT_I8, M=8, wsb=16) == -5
     assert _gemv(_w(fmt=L.LL_FMT_W1, K=160, group=32), act=L.LL_ACT_I8) == -2      # K % 128 on the device

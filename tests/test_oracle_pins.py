@@ -4,12 +4,17 @@ and printed footprint table (fixtures under tests/golden/), hand-derived
 worked examples, closed forms, identities, numpy library routines on the
 unpacked weights, and exact brute force on tiny shapes (tests/brute.py).
 
+The W1 bit order inside a 32-bit word (least significant bit first) is
+pinned to the only bit-order statements on the pages, those of the WHT
+sign-table pull request (tests/golden/w1_bit_order.txt).  The TQ2_0 element
+order inside a block (least significant pair first) is pinned to the TQ2_0
+page's own helper shift (the value index in a byte times two, tests/brute.py);
+no real TQ2_0 file is available to check it against.
+
 Parity unpinned (internally consistent, not checkable against an outside
-artefact because none is available): the TQ2_0 element order inside a block
-(least significant pair first), the W1 bit order inside a 32-bit word
-(least significant bit first), and the activation-quantization constants
-(/127, ties-to-even, multiply by 127/absmax).  Each is one reading, stated
-in oracle.c where it is used.
+artefact because none is available): the activation-quantization constants
+(/127, ties-to-even, multiply by 127/absmax).  It is one reading, stated in
+oracle.c where it is used.
 """
 import struct
 from fractions import Fraction
@@ -390,6 +395,34 @@ def test_w1_stored_bit(orc):
     bits = orc.w1_encode(w)
     for i, (_, b) in enumerate(rows):
         assert (int(bits[0, 0]) >> i) & 1 == b
+
+
+def test_w1_bit_order_pages(orc):
+    """Element k of a row sits at bit k & 31 of word k >> 5 (the WHT
+    sign-table page, tests/golden/w1_bit_order.txt), and the four elements
+    4t .. 4t+3 form nibble t & 7 of word t >> 3: a lone +1 among -1 encodes to
+    exactly that one bit, a +1 nibble to exactly that nibble, and decoding the
+    single-bit word gives the lone +1 back at k."""
+    K = 128
+    rows = [tuple(int(v) for v in r) for r in read_golden("w1_bit_order.txt")]
+    assert len(rows) >= 10
+    for e, word, bit in rows:
+        assert (word, bit) == (e >> 5, e & 31)
+        w = -np.ones((1, K), np.int8)
+        w[0, e] = 1
+        packed = orc.w1_encode(w)
+        want = np.zeros((1, K // 32), np.uint32)
+        want[0, word] = np.uint32(1) << np.uint32(bit)
+        assert np.array_equal(packed, want), e
+        back = orc.w1_decode(want, K)
+        assert back[0, e] == 1 and (np.delete(back[0], e) == -1).all()
+    for t in range(K // 4):
+        w = -np.ones((1, K), np.int8)
+        w[0, 4 * t:4 * t + 4] = 1
+        packed = orc.w1_encode(w)
+        want = np.zeros((1, K // 32), np.uint32)
+        want[0, t >> 3] = np.uint32(0xF) << np.uint32(4 * (t & 7))
+        assert np.array_equal(packed, want), t
 
 
 def test_w1_worked_example(orc):
