@@ -1,31 +1,34 @@
-// Prefill-size BitLinear product with int8 activations and i2_s weights on
-// the int8 matrix cores (Hesper "BitLinear": "Subgroup-Matrix Multi-row
-// BitLinear Kernel" computes Y = X W^T per output tile; binary-gemm card,
-// "Requirements and limits": prefill needs a different kernel than the
-// decode GEMV).  acc[m,n] = sum_k w[n,k] q[m,k] exactly in int32, and
+// Prefill-size BitLinear product with int8 activations on the int8 matrix
+// cores (Hesper "BitLinear": "Subgroup-Matrix Multi-row BitLinear Kernel"
+// computes Y = X W^T per output tile; binary-gemm card, "Requirements and
+// limits": prefill needs a different kernel than the decode GEMV).  For i2_s
+// weights acc[m,n] = sum_k w[n,k] q[m,k] exactly in int32, and
 // y = ((float)acc * s_tok[m]) * s_w.
 //
 // MI355X design: v_mfma_i32_32x32x32_i8; lane l holds 16 consecutive k of
 // row (or column) l % 32 at k offset 16 (l / 32) of a 32-k step.  The 32
 // bytes of one 128-k group of an i2_s row hold, in their four 2-bit fields,
 // the k runs 32t + [0, 32) for t = 0..3 (byte j of the group, field t:
-// element 32t + j), so the weights decode in natural k order and the
+// element 32t + j), so a lane's 16 code bytes (bytes 16 (l / 32) .. + 15 of
+// its column's group) are its B operand for all four 32-k steps, and the
 // activations need no reordering.
 //
-// Workgroup tile 128 x 128 as four 64 x 64 wave tiles, each owned by two
-// waves (eight waves, two per SIMD): one multiplies the 32-k steps 0 and 1
-// of every 128-k group, the other steps 2 and 3, and the pair adds its
-// halves through LDS at the end.  A wave keeps four 32 x 32 accumulators,
-// so every operand read from LDS feeds two multiplies, and while one wave of
-// a SIMD waits (LDS, barrier) the other multiplies.  Per group the workgroup
-// stores the int8 activation tile (rows padded to 144 bytes) and the weight
-// codes still packed (32 bytes per column, padded to 48) into one of two LDS
-// buffers.  A lane reads its column's 16 code bytes once per group and
-// decodes its two steps in registers (shift, mask, byte permute through
-// {0xFF, 0x00, 0x01}).  Both paddings put the 8 lanes of one LDS access on
-// distinct banks.  Global loads run D - 1 groups ahead in D register
-// stages, every load from a clamped in-bounds address so the compiler can
-// count its waits; one barrier per group.
+// Workgroup tile 128 x 128, four waves (one per SIMD), each owning a 64 x 64
+// wave tile (four 32 x 32 accumulators) over the whole of K.
+//   - Activations: a 128-row x 128-k int8 tile per group, loaded from global
+//     memory into registers D - 1 groups ahead, stored into one of two LDS
+//     buffers (rows padded to 144 bytes, so the eight lanes of an LDS access
+//     fall on distinct banks) and read back as MFMA operands.
+//   - Weight codes never touch LDS: each lane loads its own 16 code bytes
+//     per column block and group straight into registers (the two waves of a
+//     column share them through the L1), decoded in registers per step
+//     (shift, mask, byte permute).
+//   - The loop is software-pipelined: while the four MFMAs of a 32-k step
+//     run, the lane reads the next step's activation operands from LDS and
+//     decodes the next step's weights; the next group's tile is stored into
+//     the other LDS buffer during the first step; one barrier per group,
+//     placed before the last step's MFMAs so that they overlap the wait, and
+//     waiting on LDS traffic only (global prefetches stay in flight).
 //
 // TQ2_0 weights (llama.cpp TQ2_0 as described by the Hesper API doc: 2-bit
 // two's-complement codes, four consecutive elements per byte, an fp16 scale
@@ -45,17 +48,17 @@
 // "Method"; group size 128 only) use it too: bit k of a row is bit k % 8 of
 // byte k / 8, so a 128-k group is 16 code bytes in natural k order and the
 // activation tile is stored as for i2_s.  A lane's 16 weights of a step are
-// 16 bits of its code dword; each nibble is spread to four bytes by one
-// multiply and a mask and mapped to -1 / +1 (b * 0xFE ^ 0xFF).  Every group
-// is a scale block; its scale is kept per LDS buffer, since the next group
-// is stored before this one is multiplied.
+// 16 bits of code dword t; each nibble is spread to four bytes by one
+// multiply and a mask and mapped to -1 / +1 by a byte permute.  Every group
+// is a scale block.
 //
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
-// workgroups of a tile split its groups S ways.  Each split writes its exact
-// int32 partial tile to the workspace and increments the tile's counter; the
-// split that arrives last adds the others' partials to its own and runs the
-// epilogue, then resets the counter (so the counters stay zero between
-// calls).  Integer addition makes the result independent of the order.
+// workgroups of a tile split its groups S ways.  Each split writes its
+// partial tile to the workspace and counts itself in at the tile's counter
+// (agent-scope acquire-release); the split that arrives last adds the
+// others' partials to its own and runs the epilogue, then resets the
+// counter (so the counters stay zero between calls).  Integer addition
+// makes the i2_s result independent of the order.
 #include <type_traits>
 
 #include "common.h"
@@ -65,24 +68,26 @@ namespace {
 
 using namespace llk;
 
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-
-constexpr int BM = 128, BN = 128, LDA = 144, LDB = 48;
-constexpr int kThreads = 512;                            // eight waves
+constexpr int BM = 128, BN = 128, LDA = 144;
+constexpr int kThreads = 256;                            // four waves, one per SIMD
 constexpr int kTileInts = BM * BN;                       // one partial tile
-constexpr int kBuf = BM * LDA + BN * LDB;                // one LDS buffer: activation tile, then packed codes
-constexpr int kXchg = kTileInts * 4;                     // final exchange of half accumulators (bytes)
-constexpr size_t kGemmLds = size_t(2) * kBuf > size_t(kXchg) ? size_t(2) * kBuf : size_t(kXchg);
+constexpr int kBuf = BM * LDA;                           // one LDS buffer: the activation tile of a group
+constexpr size_t kGemmLds = size_t(2) * kBuf;
 #ifndef LL_GEMM_XCD
 #define LL_GEMM_XCD 1                                    // XCD-grouped workgroup order
 #endif
-#ifndef LL_GEMM_DEPTH
-#define LL_GEMM_DEPTH 4                                  // register stages of global loads
+#ifndef LL_GEMM_I2S_SETS
+#define LL_GEMM_I2S_SETS 1                               // i2_s accumulator sets: 1, or 3 (codes masked in place)
 #endif
-#ifndef LL_GEMM_DEPTH_TQ2
-#define LL_GEMM_DEPTH_TQ2 2                              // TQ2_0: its fp32 block sums take the registers of two stages
+#ifndef LL_GEMM_DEPTH
+#define LL_GEMM_DEPTH 3                                  // register stages (groups) of global loads
 #endif
 
+// Waits for this wave's LDS operations, then meets the other waves of the
+// workgroup.  Outstanding global loads (prefetches of later groups) stay in
+// flight; the memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // FMT 1: i2_s, FMT 2: TQ2_0 (scales: fp16 [N][K/256]), FMT 3: W1 with
 // G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).
@@ -94,14 +99,15 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                                              int32_t* __restrict__ part, int32_t* __restrict__ counters) {
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
+    __shared__ __attribute__((aligned(16))) float xs_tile[BM];   // token scales of the tile's rows
+    __shared__ __attribute__((aligned(16))) int32_t qsum_tile[BM];  // i2_s: sum_k q of the tile's rows
     const int tid = threadIdx.x, lane = tid & 63;
-    const int kh = __builtin_amdgcn_readfirstlane(tid >> 8);   // k half: steps 2 kh, 2 kh + 1
-    const int wq = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
-    const int wm = wq >> 1, wn = wq & 1;                   // rows 64 wm, columns 64 wn of the tile
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;                     // rows 64 wm, columns 64 wn of the tile
     const int li = lane & 31, h = lane >> 5;
     const int64_t TM = (M + BM - 1) / BM;
-    // Hardware workgroup w runs on XCD w % 8; it takes logical index
-    // (w % 8) T8 + w / 8, so consecutive logical workgroups (the splits and
+    // Hardware workgroup b runs on XCD b % 8; it takes logical index
+    // (b % 8) T8 + b / 8, so consecutive logical workgroups (the splits and
     // row tiles of one column tile, which read the same weight codes) share
     // one XCD's L2.
     const int64_t T = ((N + BN - 1) / BN) * TM * S, T8 = (T + 7) / 8;
@@ -116,59 +122,57 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t nsplit_units = FMT != 2 ? ng : K / 256, per_unit = FMT != 2 ? 1 : 2;
     const int64_t g0 = per_unit * (nsplit_units * split / S), g1 = per_unit * (nsplit_units * (split + 1) / S);
 
-    // Loads of one group: two 16-byte activation chunks (row idx / 8, chunk
-    // idx % 8 for idx = tid + 512 c) and 8 code bytes (column tid / 4,
-    // quarter tid % 4 of the 32-byte group); rows and columns are clamped
-    // (results of clamped ones are not stored).
-    const int8_t* arow[2];
+    // Activation loads of one group: four 16-byte chunks per thread, chunk
+    // idx = tid + 256 c is row idx / 8, bytes 16 (idx % 8) of the group;
+    // rows past M are clamped (their results are not stored).
+    const int8_t* arow[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const int idx = tid + kThreads * c;
         int64_t m = m0 + (idx >> 3);
         m = m < M ? m : M - 1;
         arow[c] = xq + m * K + 16 * (idx & 7);
     }
-    const int bcol = tid >> 2, bqt = tid & 3;
-    int64_t ncl = n0 + bcol;
-    ncl = ncl < N ? ncl : N - 1;
-    const uint8_t* bptr = codes + ncl * rowbytes + (FMT == 3 ? 4 : 8) * bqt;
-    // TQ2_0 / W1: block scales of this lane's two columns
+    // Weight codes of this lane's two columns (wn 64 + nb 32 + li), clamped;
+    // i2_s / TQ2_0: bytes 16 h .. 16 h + 15 of the 32-byte group; W1: the
+    // group's 16 bytes (both halves of the wave load the same).
+    const uint8_t* bptr[2];
     const uint16_t* sptr[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         int64_t n = n0 + wn * 64 + nb * 32 + li;
         n = n < N ? n : N - 1;
+        bptr[nb] = codes + n * rowbytes + (FMT == 3 ? 0 : 16 * h);
         sptr[nb] = FMT == 2 ? scales + n * (K / 256) : FMT == 3 ? scales + n * (K / 128) : nullptr;
     }
 
     struct Stage {
-        i32x4 a[2];
-        u32x2 b;
+        i32x4 a[4];
+        i32x4 b[2];
         uint16_t sc[FMT == 1 ? 1 : 2];                      // TQ2_0 / W1: the group's block scales
     };
     auto load = [&](int64_t g, Stage& s) {
         const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
-        if constexpr (FMT == 3)
-            s.b = u32x2{*(const __attribute__((address_space(1))) uint32_t*)(bptr + 16 * gc), 0u};
-        else
-            s.b = *(const __attribute__((address_space(1))) u32x2*)(bptr + 32 * gc);
+        for (int c = 0; c < 4; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) s.b[nb] = ld16(bptr[nb] + (FMT == 3 ? 16 : 32) * gc);
         if constexpr (FMT != 1)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) s.sc[nb] = ld2(sptr[nb] + (FMT == 2 ? gc / 2 : gc));
     };
-    // scales of the block being multiplied: TQ2_0 in curs[0], taken when the
-    // block's second (odd) group is stored; W1 in curs[buf], the group in LDS
-    // buffer buf
-    float curs[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    auto store = [&](int buf, const Stage& s, bool odd) {
+    // i2_s: this thread's share of sum_k q of its four rows (idx / 8), summed
+    // from the chunks it stores (v_dot4 against 1)
+    int32_t qs[4] = {0, 0, 0, 0};
+    auto store_a = [&](int buf, const Stage& s) {
         int8_t* A = lds + buf * kBuf;
-        int8_t* B = A + BM * LDA;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 4; ++c) {
             const int idx = tid + kThreads * c;
             int8_t* arow_l = &A[(idx >> 3) * LDA];
+            if constexpr (FMT == 1)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qs[c] = __builtin_amdgcn_sdot4(s.a[c][e], 0x01010101, qs[c], false);
             if constexpr (FMT != 2) {
                 *reinterpret_cast<i32x4*>(arow_l + 16 * (idx & 7)) = s.a[c];
             } else {
@@ -187,28 +191,54 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                 *reinterpret_cast<uint32_t*>(arow_l + 96 + 4 * p) = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
             }
         }
-        if constexpr (FMT == 3)
-            *reinterpret_cast<uint32_t*>(&B[bcol * LDB + 4 * bqt]) = s.b[0];
-        else
-            *reinterpret_cast<u32x2*>(&B[bcol * LDB + 8 * bqt]) = s.b;
-        if constexpr (FMT == 2) {
-            if (odd)
+    };
+    // activation operands of step t (rows wm 64 + mb 32 + li, k 32 t + 16 h)
+    auto read_a = [&](int buf, int t, i32x4 (&ao)[2]) {
+        const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 32 * t + 16 * h;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) curs[0][nb] = half_bits_to_float(s.sc[nb]);
-        } else if constexpr (FMT == 3) {
+        for (int mb = 0; mb < 2; ++mb) ao[mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA);
+    };
+    // weight operands of step t from the lane's code registers
+    auto decode = [&](const i32x4 (&bq)[2], int t, i32x4 (&bo)[2]) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) curs[buf][nb] = half_bits_to_float(s.sc[nb]);
+        for (int nb = 0; nb < 2; ++nb) {
+            if constexpr (FMT == 3) {
+                // bits 16 h .. 16 h + 15 of code dword t: k = 32 t + 16 h + j
+                const uint32_t v = uint32_t(bq[nb][t]) >> (16 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sp = (((v >> (4 * i)) & 0xFu) * 0x00204081u) & 0x01010101u;   // bit e -> byte e
+                    bo[nb][i] = int(__builtin_amdgcn_perm(0u, 0x000001FFu, sp));                // 0 -> -1, 1 -> +1
+                }
+            } else if constexpr (FMT == 1 && LL_GEMM_I2S_SETS == 3) {
+                // i2_s: the code c = w + 1 of field t (bits 6 - 2t) masked where
+                // it sits: step 0 (shifted down two bits) and step 1 give 16 c,
+                // step 2 gives 4 c, step 3 gives c; each step's accumulator set
+                // carries that factor
+                const uint32_t mask = t <= 1 ? 0x30303030u : t == 2 ? 0x0C0C0C0Cu : 0x03030303u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    bo[nb][i] = int((t == 0 ? uint32_t(bq[nb][i]) >> 2 : uint32_t(bq[nb][i])) & mask);
+            } else if constexpr (FMT == 1) {
+                // i2_s, one accumulator set: the code c = w + 1 of field t
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bo[nb][i] = int((uint32_t(bq[nb][i]) >> (6 - 2 * t)) & 0x03030303u);
+            } else {
+                // TQ2_0: field t at bits 2t, two's complement {0, +1, -2, -1}
+                constexpr uint32_t table = 0xFFFE0100u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    bo[nb][i] = int(__builtin_amdgcn_perm(0u, table, (uint32_t(bq[nb][i]) >> (2 * t)) & 0x03030303u));
+            }
         }
     };
 
     // epilogue operands, requested before the main loop so their latency is
-    // hidden: token scales of this lane's rows (row half kh after the
-    // exchange), the weight scale, the biases of its columns
-    float xsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + kh * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        xsv[r] = xs[m < M ? m : M - 1];
+    // hidden: the token scales of the tile's rows (into LDS, read back after
+    // the loop), the weight scale, the biases of this lane's columns
+    if (tid < BM) {
+        const int64_t m = m0 + tid;
+        xs_tile[tid] = xs[m < M ? m : M - 1];
     }
     const float sw = FMT == 1 ? *reinterpret_cast<const float*>(codes + N * rowbytes) : 1.0f;
     const float* bsrc = bias ? bias : xs;                 // always a valid address
@@ -219,7 +249,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         bnv[nb] = bsrc[bias ? (n < N ? n : N - 1) : 0];
     }
 
-    i32x16 acc[2][2];
+    // acc: the exact integer sums (i2_s: of steps 0 and 1, times 16);
+    // i2_s also acc4 (step 2, times 4) and acc1 (step 3)
+    constexpr int NS = FMT == 1 && LL_GEMM_I2S_SETS == 3 ? 2 : 1;
+    i32x16 acc[2][2], acc4[NS][2], acc1[NS][2];
     f32x16 facc[FMT == 1 ? 1 : 2][2];                      // TQ2_0 / W1: scaled block sums
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -228,168 +261,218 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 acc[mb][nb][r] = 0;
-                if constexpr (FMT != 1) facc[mb][nb][r] = 0.0f;
-            }
-
-    // odd (TQ2_0): the group ends a 256-k block, whose sums are then scaled
-    // into facc; the block's first multiply (even group, first step) starts
-    // from zero
-    auto compute = [&](int buf, bool odd) {
-        const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 16 * h + 64 * kh;
-        // (W1: all 16 code bytes of the column's group; the lane takes its half of each dword)
-        const int8_t* B = lds + buf * kBuf + BM * LDA + (wn * 64 + li) * LDB + (FMT == 3 ? 0 : 16 * h);
-        // i2_s: code byte j of this lane's 16 holds, in field t (bits 6 - 2t),
-        // the weight of k = 32 t + 16 h + j: the B operand of step t.  TQ2_0:
-        // field t (bits 2t) holds element 4 (16 h + j) + t, matching plane t.
-        i32x4 bq[2], ao[2][2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bq[nb] = *reinterpret_cast<const i32x4*>(B + nb * 32 * LDB);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                ao[tt][mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA + 32 * tt);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int sh = FMT == 1 ? 6 - 4 * kh - 2 * tt : 4 * kh + 2 * tt;
-            // code -> int8 by byte permute: i2_s {-1, 0, +1}, TQ2_0 {0, +1, -2, -1}
-            constexpr uint32_t table = FMT == 1 ? 0x000100FFu : 0xFFFE0100u;
-            i32x4 bo[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                if constexpr (FMT == 3) {
-                    // bits 16 h .. 16 h + 15 of code dword t = 2 kh + tt: k = 32 t + 16 h + j
-                    const uint32_t v = (uint32_t(bq[nb][2 * kh + tt]) >> (16 * h)) & 0xFFFFu;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t sp = (((v >> (4 * i)) & 0xFu) * 0x00204081u) & 0x01010101u;   // bit e -> byte e
-                        bo[nb][i] = int((sp * 0xFEu) ^ 0xFFFFFFFFu);                                // 1 -> +1, 0 -> -1
-                    }
+                if constexpr (FMT == 1) {
+                    acc4[mb % NS][nb][r] = 0;
+                    acc1[mb % NS][nb][r] = 0;
                 } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        bo[nb][i] = int(__builtin_amdgcn_perm(0u, table, (uint32_t(bq[nb][i]) >> sh) & 0x03030303u));
+                    facc[mb][nb][r] = 0.0f;
                 }
             }
-            const bool first = (FMT == 2 && !odd && tt == 0) || (FMT == 3 && tt == 0);
+
+    // the four MFMAs of step t; `fresh`: the step starts a new scale block
+    // (TQ2_0: first step of an even group; W1: first step of every group)
+    auto mfma = [&](const i32x4 (&ao)[2], const i32x4 (&bo)[2], int t, bool fresh) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[tt][mb], bo[nb], first ? i32x16{} : acc[mb][nb],
-                                                                        0, 0, 0);
-        }
-        if constexpr (FMT != 1)
-            if (FMT == 3 || odd)
+            for (int nb = 0; nb < 2; ++nb) {
+                if constexpr (FMT == 1 && LL_GEMM_I2S_SETS == 3) {
+                    if (t <= 1)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[mb], bo[nb], acc[mb][nb], 0, 0, 0);
+                    else if (t == 2)
+                        acc4[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[mb], bo[nb], acc4[mb][nb], 0, 0, 0);
+                    else
+                        acc1[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[mb], bo[nb], acc1[mb][nb], 0, 0, 0);
+                } else {
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[mb], bo[nb], fresh ? i32x16{} : acc[mb][nb], 0, 0, 0);
+                }
+            }
+    };
+    // TQ2_0 / W1: a finished scale block's exact sums into the fp32 accumulators
+    auto scale_in = [&](const float (&sc)[2]) {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        const float sc = FMT == 3 ? curs[buf][nb] : curs[0][nb];
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), sc, facc[mb][nb][r]);
-                    }
+                for (int r = 0; r < 16; ++r) facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), sc[nb], facc[mb][nb][r]);
     };
 
-    // Group g + i is multiplied from LDS buffer i % 2; register stage i % D
-    // holds group g + i from its load (D - 1 groups earlier) to its store
-    // (one group earlier).  The main loop runs whole runs of D groups with no
-    // early exit; the last 1 .. D - 1 groups follow it.
-    constexpr int D = FMT == 1 ? LL_GEMM_DEPTH : LL_GEMM_DEPTH_TQ2;   // (W1 as TQ2_0)
-    static_assert(D % 2 == 0 && D >= 2, "even register depth");
-    // (g0 and D are even, so group g + i is odd exactly when i is)
+    // Pipeline (one wave per SIMD, so any wait of the wave idles its matrix
+    // core: every wait below targets operations issued at least a step
+    // earlier).  Per group gi, multiplied from LDS buffer buf with its four
+    // steps' activation operands already in registers (ac):
+    //   step 0: MFMAs; decode step 1; store the next group's tile into the
+    //           other buffer; load group gi + D into the freed register stage
+    //   step 1: MFMAs; decode step 2
+    //   barrier (the stores of step 0 are done by now)
+    //   step 2: MFMAs; decode step 3; read all four steps' operands of the
+    //           next group (an), used two steps later
+    //   step 3: MFMAs; decode the next group's step 0
+    // Register stage i % D holds group g0 + i from its load (D - 1 groups
+    // ahead) until the step 0 that stores its tile and copies its codes.
+    constexpr int D = LL_GEMM_DEPTH;
+    constexpr int U = D % 2 ? 2 * D : D;                // unroll: a multiple of D and of the buffer count
+    static_assert(D >= 2, "register depth");
     Stage st[D];
+    i32x4 bq[2], bqn[2], bo[2][2], ac[4][2], an[4][2];
+    float sc[2] = {0.0f, 0.0f}, scn[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < D; ++i) load(g0 + i, st[i]);
-    store(0, st[0], false);
-    __syncthreads();
-    const int64_t nsteps = g1 - g0;
-    int64_t g = g0;
-    for (; g + D <= g1; g += D) {
+    store_a(0, st[0]);
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            // loads first (kept there by the scheduling barrier); the store of
-            // the next group and the multiplies of this one may interleave
-            load(g + D + i, st[i]);
-            __builtin_amdgcn_sched_barrier(0);
-            store((i + 1) & 1, st[(i + 1) % D], (i + 1) & 1);
-            compute(i & 1, i & 1);
-            __syncthreads();
-        }
+    for (int nb = 0; nb < 2; ++nb) {
+        bq[nb] = st[0].b[nb];
+        bqn[nb] = bq[nb];
+        if constexpr (FMT != 1) sc[nb] = half_bits_to_float(st[0].sc[nb]);
     }
-    const int rem = int(nsteps % D);
+    lds_barrier();
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) {
-        if (j < rem) {
-            if (j > 0) {
-                store(j & 1, st[j], j & 1);
-                __syncthreads();
-            }
-            compute(j & 1, j & 1);
-        }
-    }
+    for (int t = 0; t < 4; ++t) read_a(0, t, ac[t]);
+    decode(bq, 0, bo[0]);
 
-    // The two k halves of each wave tile meet: the wave of half kh keeps row
-    // block mb = kh and hands the other to its partner through LDS.
-    // (TQ2_0: the same with the fp32 block-scaled sums)
+    // One group gi (register stage si, LDS buffer buf); `next`: a following
+    // group exists.  `odd` (TQ2_0): gi ends a 256-k block.
+    auto group = [&](int64_t gi, int si, int buf, bool next, bool odd) {
+        const bool fresh0 = (FMT == 2 && !odd) || FMT == 3;
+        __builtin_amdgcn_sched_barrier(0);
+        // step 0
+        mfma(ac[0], bo[0], 0, fresh0);
+        decode(bq, 1, bo[1]);
+        if (next) {
+            const Stage& ns = st[(si + 1) % D];
+            store_a(buf ^ 1, ns);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                bqn[nb] = ns.b[nb];
+                if constexpr (FMT != 1) scn[nb] = half_bits_to_float(ns.sc[nb]);
+            }
+        }
+        load(gi + D, st[si]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // two global loads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // step 1
+        mfma(ac[1], bo[1], 1, false);
+        decode(bq, 2, bo[0]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 2
+        mfma(ac[2], bo[0], 2, false);
+        decode(bq, 3, bo[1]);
+        if (next)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) read_a(buf ^ 1, t, an[t]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // step 3
+        mfma(ac[3], bo[1], 3, false);
+        if (next) decode(bqn, 0, bo[0]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FMT == 3) scale_in(sc);
+        if constexpr (FMT == 2)
+            if (odd) scale_in(sc);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ac[t][0] = an[t][0];
+            ac[t][1] = an[t][1];
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            bq[nb] = bqn[nb];
+            if constexpr (FMT == 2) {
+                if (odd) sc[nb] = scn[nb];
+            } else if constexpr (FMT == 3) {
+                sc[nb] = scn[nb];
+            }
+        }
+    };
+
+    // (g0 is even (TQ2_0) and U is even, so group g0 + i is odd exactly when i is)
+    int64_t g = g0;
+    for (; g + U < g1; g += U) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) group(g + i, i % D, i & 1, true, i & 1);
+    }
+    // the last 1 .. U groups
+    const int rem = int(g1 - g);
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+        if (j < rem) group(g + j, j % D, j & 1, j + 1 < rem, j & 1);
+
     using E = std::conditional_t<FMT == 1, int32_t, float>;
     using V = std::conditional_t<FMT == 1, i32x16, f32x16>;
-    __syncthreads();                                       // every wave is done with the operand buffers
-    E* xb = reinterpret_cast<E*>(lds);
-    V fin[2];
     if constexpr (FMT == 1) {
-        if (kh == 0) {
+        // i2_s: sum_k w q = sum_k c q - sum_k q (w = c - 1); the row sums of q
+        // over this split's groups, from the eight threads that stored each row
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                fin[nb] = acc[0][nb];
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[1][nb][r];
-            }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                fin[nb] = acc[1][nb];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = acc[0][nb][r];
-            }
+            for (int o = 1; o < 8; o <<= 1) qs[c] += __shfl_xor(qs[c], o, kWave);
+            if ((tid & 7) == 0) qsum_tile[(tid >> 3) + 32 * c] = qs[c];
         }
-    } else {
-        if (kh == 0) {
+        __syncthreads();
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                fin[nb] = facc[0][nb];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xb[((0 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = facc[1][nb][r];
+            for (int rq = 0; rq < 4; ++rq) {
+                const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rq + e;
+                        if constexpr (LL_GEMM_I2S_SETS == 3)
+                            acc[mb][nb][r] = (acc[mb][nb][r] >> 4) + (acc4[mb % NS][nb][r] >> 2) + acc1[mb % NS][nb][r] - q4[e];
+                        else
+                            acc[mb][nb][r] = acc[mb][nb][r] - q4[e];
+                    }
             }
-        } else {
+    }
+    V fin[2][2];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                fin[nb] = facc[1][nb];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xb[((1 * 4 + wq) * 32 + nb * 16 + r) * 64 + lane] = facc[0][nb][r];
-            }
+        for (int nb = 0; nb < 2; ++nb) {
+            if constexpr (FMT == 1)
+                fin[mb][nb] = acc[mb][nb];
+            else
+                fin[mb][nb] = facc[mb][nb];
         }
-    }
-    __syncthreads();
-    {
-        const E* pb = xb + ((1 - kh) * 4 + wq) * 32 * 64;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) fin[nb][r] += pb[(nb * 16 + r) * 64 + lane];
-    }
 
     if (S > 1) {
-        // Publish this split's partial tile with device-coherent stores, wait for
-        // them to complete, then count the split in; the split that arrives last
-        // reads the others' partials (device-coherent loads) and finishes the tile.
+        // Publish this split's partial tile (device-coherent stores), wait for
+        // them, count the split in; the split that arrives last reads the
+        // others' partials (device-coherent loads) and finishes the tile.
         int32_t* mine = part + (tile * S + split) * int64_t(kTileInts);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                st_coherent(mine + (nb * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[nb][r])));
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    st_coherent(mine + ((mb * 2 + nb) * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[mb][nb][r])));
         wait_vmem();
         __syncthreads();
         if (tid == 0) last_flag = arrive_acq_rel(counters + tile) == S - 1;
@@ -400,100 +483,125 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                 if (s == split) continue;
                 const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) fin[nb][r] += ld_coherent(other + (nb * 16 + r) * kThreads + tid);
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            fin[mb][nb][r] += ld_coherent(other + ((mb * 2 + nb) * 16 + r) * kThreads + tid);
             }
         } else {
             // fp32 partials added in split order (this split's own from registers)
-            V tot[2];
+            V tot[2][2];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tot[nb][r] = 0.0f;
-            for (int s = 0; s < S; ++s) {
-                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        tot[nb][r] += s == split ? fin[nb][r]
-                                                 : __builtin_bit_cast(float, ld_coherent(other + (nb * 16 + r) * kThreads + tid));
+                    for (int r = 0; r < 16; ++r) tot[mb][nb][r] = 0.0f;
+            for (int s = 0; s < S; ++s) {
+                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            tot[mb][nb][r] += s == split ? fin[mb][nb][r]
+                                                         : __builtin_bit_cast(float, ld_coherent(other + ((mb * 2 + nb) * 16 + r) * kThreads + tid));
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) fin[nb] = tot[nb];
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) fin[mb][nb] = tot[mb][nb];
         }
         if (tid == 0) st_coherent(counters + tile, 0);    // ready for the next call
     }
 
-    // Epilogue: y = ((float)acc * s_tok) * s_w (+ bias); TQ2_0 y = acc * s_tok (+ bias).  Lane (li, h) of half
-    // kh holds column wn 64 + nb 32 + li and rows wm 64 + kh 32 + 8 (r / 4) +
-    // 4 h + r % 4; its output pointer is formed once, each store adds a
-    // uniform row offset.  The stores of a full tile run as one straight block
-    // (a branch between stores would make each wait for the one before).
-    float out[2][16];
+    // Epilogue: i2_s y = ((float)acc * s_tok) * s_w (+ bias); TQ2_0 / W1
+    // y = acc * s_tok (+ bias).  Lane (li, h) holds column wn 64 + nb 32 + li
+    // and rows wm 64 + mb 32 + 8 (r / 4) + 4 h + r % 4; its output pointer is
+    // formed once, each store adds a uniform offset.  The stores of a full
+    // tile run as one straight block (a branch between stores would make each
+    // wait for the one before).
+    float xsv[2][16];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float v = FMT == 1 ? __fmul_rn(__fmul_rn(float(fin[nb][r]), xsv[r]), sw) : __fmul_rn(float(fin[nb][r]), xsv[r]);
-            out[nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
+        for (int rq = 0; rq < 4; ++rq) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&xs_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xsv[mb][4 * rq + e] = v[e];
         }
-    const int64_t lrow = m0 + wm * 64 + kh * 32 + 4 * h, lcol = n0 + wn * 64 + li;
-    float* yl = y + lrow * N + lcol;
-    if (m0 + BM <= M && n0 + BN <= N) {
+    float out[2][2][16];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) yl[int64_t(8 * (r >> 2) + (r & 3)) * N + nb * 32] = out[nb][r];
-    } else {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int ml = 8 * (r >> 2) + (r & 3);
-                if (lrow + ml < M && lcol + nb * 32 < N) yl[int64_t(ml) * N + nb * 32] = out[nb][r];
+                float v = FMT == 1 ? __fmul_rn(__fmul_rn(float(fin[mb][nb][r]), xsv[mb][r]), sw)
+                                   : __fmul_rn(float(fin[mb][nb][r]), xsv[mb][r]);
+                out[mb][nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
             }
+    const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * 64 + li;
+    float* yl = y + lrow * N + lcol;
+    if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    yl[int64_t(mb * 32 + 8 * (r >> 2) + (r & 3)) * N + nb * 32] = out[mb][nb][r];
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
+                    if (lrow + ml < M && lcol + nb * 32 < N) yl[int64_t(ml) * N + nb * 32] = out[mb][nb][r];
+                }
     }
     if (FMT == 1 && acc_out) {
         int32_t* al = acc_out + lrow * N + lcol;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ml = 8 * (r >> 2) + (r & 3);
-                if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = int32_t(fin[nb][r]);
-            }
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
+                    if (lrow + ml < M && lcol + nb * 32 < N) al[int64_t(ml) * N + nb * 32] = int32_t(fin[mb][nb][r]);
+                }
     }
 }
 
-__global__ void __launch_bounds__(kThreads) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N,
-                                                                int64_t K, const int8_t* __restrict__ xq,
-                                                                const float* __restrict__ xs, int64_t M,
-                                                                const float* __restrict__ bias, float* __restrict__ y,
-                                                                int32_t* __restrict__ acc_out, int S,
-                                                                int32_t* __restrict__ part,
-                                                                int32_t* __restrict__ counters) {
+// Register budgets: the i2_s kernel fits two waves per SIMD (two workgroups
+// share a CU once there are more tiles than CUs); the TQ2_0 and W1 kernels
+// keep their fp32 block sums as well and are sized for one.
+#define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
+
+LL_GEMM_ATTRS(2) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
+                                 const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
+                                 float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
+                                 int32_t* __restrict__ part, int32_t* __restrict__ counters) {
     gemm_i8_body<1>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters);
 }
 
-__global__ void __launch_bounds__(kThreads) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits,
-                                                               const uint16_t* __restrict__ scales, int64_t N,
-                                                               int64_t K, const int8_t* __restrict__ xq,
-                                                               const float* __restrict__ xs, int64_t M,
-                                                               const float* __restrict__ bias, float* __restrict__ y,
-                                                               int S, int32_t* __restrict__ part,
-                                                               int32_t* __restrict__ counters) {
+LL_GEMM_ATTRS(1) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N,
+                                int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
+                                const float* __restrict__ bias, float* __restrict__ y, int S,
+                                int32_t* __restrict__ part, int32_t* __restrict__ counters) {
     gemm_i8_body<3>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
 }
 
-__global__ void __launch_bounds__(kThreads) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes,
-                                                                const uint16_t* __restrict__ scales, int64_t N,
-                                                                int64_t K, const int8_t* __restrict__ xq,
-                                                                const float* __restrict__ xs, int64_t M,
-                                                                const float* __restrict__ bias, float* __restrict__ y,
-                                                                int S, int32_t* __restrict__ part,
-                                                                int32_t* __restrict__ counters) {
+LL_GEMM_ATTRS(1) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N,
+                                 int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
+                                 const float* __restrict__ bias, float* __restrict__ y, int S,
+                                 int32_t* __restrict__ part, int32_t* __restrict__ counters) {
     gemm_i8_body<2>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
 }
 
@@ -502,14 +610,25 @@ __global__ void __launch_bounds__(kThreads) gemm_i8_tq2_kernel(const uint8_t* __
 #endif
 // Split count: enough workgroups to cover the chip (LL_GEMM_SLOTS resident
 // workgroups) without leaving a split fewer than four groups (two TQ2_0
-// blocks: splits keep whole blocks).
+// blocks: splits keep whole blocks), and at most one counter per tile in
+// the counter region.
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool allow = true) {
-    if (!allow) return 1;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (!allow || tiles > kMaxCounters) return 1;
     const int64_t ng = K / 128;
     int64_t s = 1;
     while (tiles * (s + 1) <= LL_GEMM_SLOTS && ng / (s + 1) >= 4) ++s;
     return int(s);
+}
+
+template <typename Kern, typename... Args>
+hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, hipStream_t stream, Args... args) {
+    const int64_t T = tiles * S;
+    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kernel), kGemmLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, block, kGemmLds, stream, args...);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -524,47 +643,30 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq, const float* xs,
-                              int64_t M, const float* bias, float* y, int32_t* acc_out, int32_t* counters, void* ws, hipStream_t stream) {
+                              int64_t M, const float* bias, float* y, int32_t* acc_out, int32_t* counters, void* ws,
+                              hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
-    int32_t* part = static_cast<int32_t*>(ws);
-    const int64_t T = tiles * S;
-    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_i2s_kernel), kGemmLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_i8_i2s_kernel, grid, block, kGemmLds, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
-                       part, counters);
-    return hipGetLastError();
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    return launch_tiles(gemm_i8_i2s_kernel, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
+                        static_cast<int32_t*>(ws), counters);
 }
 
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                              const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                              hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
-    int32_t* part = static_cast<int32_t*>(ws);
-    const int64_t T = tiles * S;
-    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_w1_kernel), kGemmLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_i8_w1_kernel, grid, block, kGemmLds, stream, reinterpret_cast<const uint8_t*>(bits), scales,
-                       N, K, xq, xs, M, bias, y, S, part, counters);
-    return hipGetLastError();
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    return launch_tiles(gemm_i8_w1_kernel, tiles, S, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
+                        xs, M, bias, y, S, static_cast<int32_t*>(ws), counters);
 }
 
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                             hipStream_t stream) {
+                              hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr && tiles <= kMaxCounters);
-    int32_t* part = static_cast<int32_t*>(ws);
-    const int64_t T = tiles * S;
-    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(gemm_i8_tq2_kernel), kGemmLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_i8_tq2_kernel, grid, block, kGemmLds, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
-                       part, counters);
-    return hipGetLastError();
+    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    return launch_tiles(gemm_i8_tq2_kernel, tiles, S, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
+                        static_cast<int32_t*>(ws), counters);
 }
 
 }  // namespace llk
