@@ -207,30 +207,58 @@ size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {
     return with_counters(gemm_data_bytes(w, M));
 }
 
-ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
-                            float* y, int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "ll_bitlinear_gemm";
+// Argument checks of ll_bitlinear_gemm and its allocation-free variant.
+static ll_status check_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
+                            const float* y, const int32_t* acc_out, const char* fn) {
     ll_status st = check_weights(w, fn);
     if (st) return st;
-    if (M < 1 || M > 65535 * 128) return ll::fail(LL_ESHAPE, "ll_bitlinear_gemm: M must be in [1, 65535*128]");
-    if (!xq || !xs || !y) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: xq, xs or y is NULL");
-    if (!aligned(xq, 16)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xq must be 16-byte aligned");
+    if (M < 1 || M > 65535 * 128) return ll::failf(LL_ESHAPE, "%s: M must be in [1, 65535*128]", fn);
+    if (!xq || !xs || !y) return ll::failf(LL_EINVAL, "%s: xq, xs or y is NULL", fn);
+    if (!aligned(xq, 16)) return ll::failf(LL_EALIGN, "%s: xq must be 16-byte aligned", fn);
     if (!aligned(xs, 4) || !aligned(y, 4) || (bias && !aligned(bias, 4)) || (acc_out && !aligned(acc_out, 4)))
-        return ll::fail(LL_EALIGN, "ll_bitlinear_gemm: xs / y / bias / acc_out must be 4-byte aligned");
+        return ll::failf(LL_EALIGN, "%s: xs / y / bias / acc_out must be 4-byte aligned", fn);
     if (w->fmt == LL_FMT_W1) {
         st = check_w1_device(w, fn);
         if (st) return st;
-        if (acc_out) return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for W1 (per-group scales)");
+        if (acc_out) return ll::failf(LL_EINVAL, "%s: acc_out is not available for W1 (per-group scales)", fn);
     }
     if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0 && w->fmt != LL_FMT_W1)
-        return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: formats i2_s, TQ2_0 and W1 only");
+        return ll::failf(LL_EINVAL, "%s: formats i2_s, TQ2_0 and W1 only", fn);
     if (w->fmt == LL_FMT_TQ2_0 && acc_out)
-        return ll::fail(LL_EINVAL, "ll_bitlinear_gemm: acc_out is not available for TQ2_0 (per-block scales)");
+        return ll::failf(LL_EINVAL, "%s: acc_out is not available for TQ2_0 (per-block scales)", fn);
+    return LL_OK;
+}
+
+ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
+                            float* y, int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ll_bitlinear_gemm";
+    ll_status st = check_gemm(w, xq, xs, M, bias, y, acc_out, fn);
+    if (st) return st;
     const size_t need = with_counters(gemm_data_bytes(w, M));
     st = check_workspace(workspace, workspace_bytes, need, fn);
     if (st) return st;
     return hip_status(run_gemm(w, xq, xs, M, bias, y, acc_out, need ? workspace : nullptr, static_cast<hipStream_t>(stream)),
                       fn);
+}
+
+size_t ll_gemm_noalloc_scratch_bytes(void) { return llk::static_scratch_bytes(); }
+
+ll_status ll_bitlinear_gemm_noalloc(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,
+                                    const float* bias, float* y, int32_t* acc_out, void* stream) {
+    const char* fn = "ll_bitlinear_gemm_noalloc";
+    ll_status st = check_gemm(w, xq, xs, M, bias, y, acc_out, fn);
+    if (st) return st;
+    const size_t need = with_counters(gemm_data_bytes(w, M));
+    if (need > llk::static_scratch_bytes())
+        return ll::failf(LL_EWORKSPACE, "%s: this product needs %zu bytes of scratch, more than the %zu-byte static scratch",
+                         fn, need, llk::static_scratch_bytes());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (need) {
+        st = hip_status(llk::static_scratch(&ws, s), fn);
+        if (st) return st;
+    }
+    return hip_status(run_gemm(w, xq, xs, M, bias, y, acc_out, ws, s), fn);
 }
 
 // One-shot bf16 layer: workspace = split-K counters | the product's data

@@ -18,6 +18,12 @@ namespace llk {
 constexpr size_t kCounterBytes = 4096;
 constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
 
+// The static device scratch of the allocation-free entry point: its size,
+// and the address of the current device's copy (its counter region cleared
+// on `stream` the first time a device asks).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out, hipStream_t stream);
+
 // Raises a kernel's dynamic LDS limit to at least `bytes` on the current
 // device.  hipFuncSetAttribute is a host-side call that costs microseconds,
 // so each (kernel, device) pair is set once and remembered.

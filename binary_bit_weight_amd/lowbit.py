@@ -46,6 +46,8 @@ SIGNATURES = {
     "ll_bitlinear_gemv": (C.c_int, [_P, _I32, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "ll_gemm_workspace_size": (_SZ, [_P, _I64]),
     "ll_bitlinear_gemm": (C.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "ll_gemm_noalloc_scratch_bytes": (_SZ, []),
+    "ll_bitlinear_gemm_noalloc": (C.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P]),
     "ll_binary_linear_workspace_size": (_SZ, [_P, _I64]),
     "ll_binary_linear": (C.c_int, [_P, _P, _I64, _P, _P, _P, _SZ, _P]),
 }
@@ -253,6 +255,15 @@ def ll_bitlinear_gemm(w: Weights, xq, xs, M, bias, y, acc_out=None, workspace=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ll_bitlinear_gemm(w.ref, _dev(xq), _dev(xs), M, _dev(bias), _dev(y), _dev(acc_out),
                                    _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def ll_gemm_noalloc_scratch_bytes() -> int:
+    return int(lib().ll_gemm_noalloc_scratch_bytes())
+
+
+def ll_bitlinear_gemm_noalloc(w: Weights, xq, xs, M, bias, y, acc_out=None, stream=None):
+    _check(lib().ll_bitlinear_gemm_noalloc(w.ref, _dev(xq), _dev(xs), M, _dev(bias), _dev(y), _dev(acc_out),
+                                           _stream(stream)))
 
 
 def ll_binary_linear_workspace_size(w: Weights, M) -> int:

@@ -320,6 +320,22 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                             const float* bias, float* y, int32_t* acc_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): the
+   product of ll_bitlinear_gemm, with the same arguments, rules and results,
+   but no workspace argument.  Its scratch (split-K counters and partial
+   tiles, the operands of W1 passes) is a static device array of
+   ll_gemm_noalloc_scratch_bytes() bytes (32 MiB), one copy per GPU, held by
+   the library from its load until the process ends; the call allocates and
+   frees nothing.  A product needing more scratch than that (ll_gemm_
+   workspace_size above the limit: W1 passes with very long K) is refused
+   with LL_EWORKSPACE before anything is launched.  Every call on a GPU
+   shares that GPU's array: calls that overlap in time on one GPU (other
+   streams, concurrent graph replays) race and must not be made. */
+size_t ll_gemm_noalloc_scratch_bytes(void);
+ll_status ll_bitlinear_gemm_noalloc(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,
+                                    const float* bias, float* y, int32_t* acc_out, void* stream);
+
 /* [BG "API": binary_linear(x, wq, wscale, bias, group_size), bf16 in and out]
    One call from bf16 activations to bf16 outputs: per-token int8
    quantization of x (as ll_quantize_act), the int8 product of
