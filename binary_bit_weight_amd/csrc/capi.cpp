@@ -99,14 +99,15 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
 
 extern "C" {
 
-ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* xq, float* xs, void* stream) {
+ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* xq, float* xs, int32_t* xsum,
+                          void* stream) {
     if (!x || !xq || !xs) return ll::fail(LL_EINVAL, "ll_quantize_act: NULL pointer");
     if (x_dtype != LL_DT_F32 && x_dtype != LL_DT_BF16) return ll::fail(LL_EINVAL, "ll_quantize_act: unknown dtype");
     if (M <= 0 || K <= 0) return ll::fail(LL_EINVAL, "ll_quantize_act: M and K must be positive");
     if (M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 20)) return ll::fail(LL_ERANGE, "ll_quantize_act: M < 2^31, K <= 2^20");
-    if (!aligned(x, x_dtype == LL_DT_F32 ? 4 : 2) || !aligned(xs, 4))
-        return ll::fail(LL_EALIGN, "ll_quantize_act: x / xs not aligned to their element size");
-    return hip_status(llk::launch_quantize(x, x_dtype == LL_DT_BF16, M, K, xq, xs, static_cast<hipStream_t>(stream)),
+    if (!aligned(x, x_dtype == LL_DT_F32 ? 4 : 2) || !aligned(xs, 4) || (xsum && !aligned(xsum, 4)))
+        return ll::fail(LL_EALIGN, "ll_quantize_act: x / xs / xsum not aligned to their element size");
+    return hip_status(llk::launch_quantize(x, x_dtype == LL_DT_BF16, M, K, xq, xs, xsum, static_cast<hipStream_t>(stream)),
                       "ll_quantize_act");
 }
 
@@ -177,20 +178,23 @@ static bool w1_mfma(const ll_weights* w, int64_t M) { return w->fmt == LL_FMT_W1
 
 // The product of ll_bitlinear_gemm on validated arguments; ws: a workspace
 // of ll_gemm_workspace_size bytes, or NULL when that is 0.
+// xsum (i2_s): per-token sums of xq from the quantization, or NULL; y16:
+// bf16 output written instead of y, or NULL.
 static hipError_t run_gemm(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M, const float* bias,
-                           float* y, int32_t* acc_out, void* ws, hipStream_t s) {
+                           float* y, int32_t* acc_out, void* ws, hipStream_t s, const int32_t* xsum = nullptr,
+                           uint16_t* y16 = nullptr) {
     const Workspace W = split_ws(ws);
     if (w1_mfma(w, M))
         return llk::launch_gemm_i8_w1(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
-                                      w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s);
+                                      w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s, y16);
     if (w->fmt == LL_FMT_W1)
         return llk::launch_w1_gemv(static_cast<const uint32_t*>(w->codes), static_cast<const uint16_t*>(w->scales), w->N,
-                                   w->K, w->group, xq, xs, M, bias, y, W.counters, W.data, s);
+                                   w->K, w->group, xq, xs, M, bias, y, W.counters, W.data, s, y16);
     if (w->fmt == LL_FMT_TQ2_0)
         return llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
-                                       w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s);
+                                       w->N, w->K, xq, xs, M, bias, y, W.counters, W.data, s, y16);
     return llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K, xq, xs, M, bias, y, acc_out,
-                                   W.counters, W.data, s);
+                                   W.counters, W.data, s, xsum, y16);
 }
 
 // Data-region bytes of the product ll_bitlinear_gemm runs (0: no workspace).
@@ -262,19 +266,21 @@ ll_status ll_bitlinear_gemm_noalloc(const ll_weights* w, const int8_t* xq, const
 }
 
 // One-shot bf16 layer: workspace = split-K counters | the product's data
-// region | int8 x [M K] | token scales [M] | fp32 y [M N], each part on a
-// 256-byte boundary.
+// region | int8 x [M K] | token scales [M] | token sums of q [M], each part
+// on a 256-byte boundary.  Two launches: the quantization (which also sums
+// each token's codes, the offset term of the i2_s product), then the product
+// with the bias and the bf16 rounding in its epilogue.
 static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct LinearLayout {
-    size_t q, s, y, total;
+    size_t q, s, qs, total;
 };
 static bool linear_layout(const ll_weights* w, int64_t M, LinearLayout& L) {
     if (w->fmt != LL_FMT_I2S && w->fmt != LL_FMT_TQ2_0 && w->fmt != LL_FMT_W1) return false;
     if (w->fmt == LL_FMT_W1 && w->group <= 0) return false;
     L.q = round256(llk::kCounterBytes + gemm_data_bytes(w, M));
     L.s = L.q + round256(size_t(M) * size_t(w->K));
-    L.y = L.s + round256(size_t(M) * 4);
-    L.total = L.y + size_t(M) * size_t(w->N) * 4;
+    L.qs = L.s + round256(size_t(M) * 4);
+    L.total = L.qs + size_t(M) * 4;
     return true;
 }
 
@@ -305,13 +311,11 @@ ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, co
     char* base = static_cast<char*>(workspace);
     int8_t* q = reinterpret_cast<int8_t*>(base + L.q);
     float* s = reinterpret_cast<float*>(base + L.s);
-    float* y32 = reinterpret_cast<float*>(base + L.y);
+    int32_t* qs = w->fmt == LL_FMT_I2S ? reinterpret_cast<int32_t*>(base + L.qs) : nullptr;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = hip_status(llk::launch_quantize(x, true, M, w->K, q, s, hs), fn);
+    st = hip_status(llk::launch_quantize(x, true, M, w->K, q, s, qs, hs), fn);
     if (st) return st;
-    st = hip_status(run_gemm(w, q, s, M, bias, y32, nullptr, base, hs), fn);
-    if (st) return st;
-    return hip_status(llk::launch_f32_to_bf16(y32, y, M * w->N, hs), fn);
+    return hip_status(run_gemm(w, q, s, M, bias, nullptr, nullptr, base, hs, qs, y), fn);
 }
 
 }  // extern "C"

@@ -91,6 +91,15 @@ __device__ __forceinline__ int32_t arrive_acq_rel(int32_t* c) {
 // (gfx9 s_waitcnt: vmcnt = 0, expcnt and lgkmcnt not waited on).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// fp32 -> bf16 bits, round to nearest with ties to even on the bit pattern
+// (add 0x7FFF plus the lowest kept bit, keep the high half; overflow goes to
+// infinity); NaN becomes the quiet NaN 0x7FC0 with its sign.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t(((u >> 16) & 0x8000u) | 0x7FC0u);
+    return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 // fp16 bits -> fp32 (exact).
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return float(__builtin_bit_cast(_Float16, h));

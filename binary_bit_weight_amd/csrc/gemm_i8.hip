@@ -90,13 +90,16 @@ constexpr size_t kGemmLds = size_t(2) * kBuf;
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // FMT 1: i2_s, FMT 2: TQ2_0 (scales: fp16 [N][K/256]), FMT 3: W1 with
-// G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).
-template <int FMT>
+// G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).  XSUM (i2_s):
+// the per-token sums of q come in xsum (from the quantization) instead of
+// being summed here.  y16: bf16 output written instead of y, or NULL.
+template <int FMT, bool XSUM = false>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                              const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                              float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
-                                             int32_t* __restrict__ part, int32_t* __restrict__ counters) {
+                                             int32_t* __restrict__ part, int32_t* __restrict__ counters,
+                                             const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
     __shared__ __attribute__((aligned(16))) float xs_tile[BM];   // token scales of the tile's rows
@@ -170,7 +173,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         for (int c = 0; c < 4; ++c) {
             const int idx = tid + kThreads * c;
             int8_t* arow_l = &A[(idx >> 3) * LDA];
-            if constexpr (FMT == 1)
+            if constexpr (FMT == 1 && !XSUM)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qs[c] = __builtin_amdgcn_sdot4(s.a[c][e], 0x01010101, qs[c], false);
             if constexpr (FMT != 2) {
@@ -239,6 +242,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     if (tid < BM) {
         const int64_t m = m0 + tid;
         xs_tile[tid] = xs[m < M ? m : M - 1];
+        if constexpr (XSUM) qsum_tile[tid] = xsum[m < M ? m : M - 1];
     }
     const float sw = FMT == 1 ? *reinterpret_cast<const float*>(codes + N * rowbytes) : 1.0f;
     const float* bsrc = bias ? bias : xs;                 // always a valid address
@@ -425,12 +429,15 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     using V = std::conditional_t<FMT == 1, i32x16, f32x16>;
     if constexpr (FMT == 1) {
         // i2_s: sum_k w q = sum_k c q - sum_k q (w = c - 1); the row sums of q
-        // over this split's groups, from the eight threads that stored each row
+        // over this split's groups, from the eight threads that stored each
+        // row (with XSUM the whole rows' sums, subtracted once in the epilogue)
+        if constexpr (!XSUM) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < 4; ++c) {
 #pragma unroll
-            for (int o = 1; o < 8; o <<= 1) qs[c] += __shfl_xor(qs[c], o, kWave);
-            if ((tid & 7) == 0) qsum_tile[(tid >> 3) + 32 * c] = qs[c];
+                for (int o = 1; o < 8; o <<= 1) qs[c] += __shfl_xor(qs[c], o, kWave);
+                if ((tid & 7) == 0) qsum_tile[(tid >> 3) + 32 * c] = qs[c];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -443,10 +450,11 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * rq + e;
+                        const int32_t qsub = XSUM ? 0 : q4[e];
                         if constexpr (LL_GEMM_I2S_SETS == 3)
-                            acc[mb][nb][r] = (acc[mb][nb][r] >> 4) + (acc4[mb % NS][nb][r] >> 2) + acc1[mb % NS][nb][r] - q4[e];
+                            acc[mb][nb][r] = (acc[mb][nb][r] >> 4) + (acc4[mb % NS][nb][r] >> 2) + acc1[mb % NS][nb][r] - qsub;
                         else
-                            acc[mb][nb][r] = acc[mb][nb][r] - q4[e];
+                            acc[mb][nb][r] = acc[mb][nb][r] - qsub;
                     }
             }
     }
@@ -532,6 +540,13 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             const f32x4 v = *reinterpret_cast<const f32x4*>(&xs_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) xsv[mb][4 * rq + e] = v[e];
+            if constexpr (FMT == 1 && XSUM) {
+                const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fin[mb][nb][4 * rq + e] -= q4[e];
+            }
         }
     float out[2][2][16];
 #pragma unroll
@@ -545,6 +560,30 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                 out[mb][nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
             }
     const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * 64 + li;
+    if (y16) {
+        uint16_t* yl16 = y16 + lrow * N + lcol;
+        if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        yl16[int64_t(mb * 32 + 8 * (r >> 2) + (r & 3)) * N + nb * 32] = f32_to_bf16_rne(out[mb][nb][r]);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
+                        if (lrow + ml < M && lcol + nb * 32 < N)
+                            yl16[int64_t(ml) * N + nb * 32] = f32_to_bf16_rne(out[mb][nb][r]);
+                    }
+        }
+        return;
+    }
     float* yl = y + lrow * N + lcol;
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
@@ -584,25 +623,27 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 // keep their fp32 block sums as well and are sized for one.
 #define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
 
+template <bool XSUM>
 LL_GEMM_ATTRS(2) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                  const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                  float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
-                                 int32_t* __restrict__ part, int32_t* __restrict__ counters) {
-    gemm_i8_body<1>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters);
+                                 int32_t* __restrict__ part, int32_t* __restrict__ counters,
+                                 const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
+    gemm_i8_body<1, XSUM>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
 LL_GEMM_ATTRS(1) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N,
                                 int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
                                 const float* __restrict__ bias, float* __restrict__ y, int S,
-                                int32_t* __restrict__ part, int32_t* __restrict__ counters) {
-    gemm_i8_body<3>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
+                                int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
+    gemm_i8_body<3>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
 LL_GEMM_ATTRS(1) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N,
                                  int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
                                  const float* __restrict__ bias, float* __restrict__ y, int S,
-                                 int32_t* __restrict__ part, int32_t* __restrict__ counters) {
-    gemm_i8_body<2>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters);
+                                 int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
+    gemm_i8_body<2>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
 #ifndef LL_GEMM_SLOTS
@@ -644,29 +685,32 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq, const float* xs,
                               int64_t M, const float* bias, float* y, int32_t* acc_out, int32_t* counters, void* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* xsum, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
-    return launch_tiles(gemm_i8_i2s_kernel, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
-                        static_cast<int32_t*>(ws), counters);
+    if (xsum)
+        return launch_tiles(gemm_i8_i2s_kernel<true>, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
+                            static_cast<int32_t*>(ws), counters, xsum, y16);
+    return launch_tiles(gemm_i8_i2s_kernel<false>, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
+                        static_cast<int32_t*>(ws), counters, xsum, y16);
 }
 
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                              const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                             hipStream_t stream) {
+                             hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
     return launch_tiles(gemm_i8_w1_kernel, tiles, S, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
-                        xs, M, bias, y, S, static_cast<int32_t*>(ws), counters);
+                        xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
 }
 
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
     return launch_tiles(gemm_i8_tq2_kernel, tiles, S, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
-                        static_cast<int32_t*>(ws), counters);
+                        static_cast<int32_t*>(ws), counters, y16);
 }
 
 }  // namespace llk

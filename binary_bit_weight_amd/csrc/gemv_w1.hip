@@ -196,7 +196,8 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
                                                                  const float* __restrict__ bias,
                                                                  float* __restrict__ y, int nsplit,
                                                                  double* __restrict__ part,
-                                                                 int32_t* __restrict__ counters) {
+                                                                 int32_t* __restrict__ counters,
+                                                                 uint16_t* __restrict__ y16) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ int last_flag;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -488,7 +489,10 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
         } else if (n < N) {
             float out = float(double(xs[m]) * s);
             if (bias) out = __fadd_rn(out, bias[n]);
-            y[int64_t(m) * N + n] = out;
+            if (y16)
+                y16[int64_t(m) * N + n] = f32_to_bf16_rne(out);
+            else
+                y[int64_t(m) * N + n] = out;
         }
     }
     if (nsplit == 1) return;
@@ -515,7 +519,10 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
             if (sp < nsplit) s += pv[sp];
         float out = float(double(xs[m]) * s);
         if (bias) out = __fadd_rn(out, bias[n]);
-        y[int64_t(m) * N + n] = out;
+        if (y16)
+            y16[int64_t(m) * N + n] = f32_to_bf16_rne(out);
+        else
+            y[int64_t(m) * N + n] = out;
     }
     if (tid == 0) st_coherent(counters + rb, 0);          // ready for the next call
 }
@@ -523,7 +530,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
 template <int G, int MT, int NP, int PK, bool FUSED = false>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                      const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
-                     hipStream_t stream) {
+                     uint16_t* y16, hipStream_t stream) {
     const dim3 grid{unsigned((N + kW1Rows - 1) / kW1Rows * nsplit)}, block{64 * kW1Waves};
     size_t lds = size_t(w1_lds_bytes(M, G));
     const size_t red = size_t(kW1Waves) * 2 * 16 * 8 * MT * sizeof(double);
@@ -531,7 +538,7 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_gemv_kernel<G, MT, NP, PK, FUSED>), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP, PK, FUSED>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias,
-                       y, nsplit, part, counters);
+                       y, nsplit, part, counters, y16);
     return hipGetLastError();
 }
 
@@ -548,28 +555,28 @@ bool w1_fused(int64_t N, int G, int64_t Mb) {
 template <int G>
 hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                        const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
-                       bool fused, hipStream_t stream) {
+                       bool fused, uint16_t* y16, hipStream_t stream) {
     constexpr int kUnits = G >= 128 ? kChunks / (G / 128) : kChunks;   // units per window
     constexpr int kMaxPk = G >= 128 ? kUnits : 8 / w1_slots(G);          // R >= 2 S
     constexpr int P8 = kMaxPk < 8 ? kMaxPk : 8, P4 = kMaxPk < 4 ? kMaxPk : 4;
     if constexpr (G == 128) {
         if (fused) {
             switch (w1_pack(M, G)) {
-            case 8: return launch_w1<G, 1, 2, 8, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-            case 4: return launch_w1<G, 1, 2, 4, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-            case 2: return launch_w1<G, 1, 2, 2, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-            default: return launch_w1<G, 1, 2, 1, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+            case 8: return launch_w1<G, 1, 2, 8, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+            case 4: return launch_w1<G, 1, 2, 4, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+            case 2: return launch_w1<G, 1, 2, 2, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+            default: return launch_w1<G, 1, 2, 1, true>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
             }
         }
     }
     switch (w1_pack(M, G)) {
-    case 8: return launch_w1<G, 1, 2, P8>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-    case 4: return launch_w1<G, 1, 2, P4>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-    case 2: return launch_w1<G, 1, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    case 8: return launch_w1<G, 1, 2, P8>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+    case 4: return launch_w1<G, 1, 2, P4>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+    case 2: return launch_w1<G, 1, 2, 2>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
     default: break;
     }
-    if (w1_arows(M, G) <= 16) return launch_w1<G, 1, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
-    return launch_w1<G, 2, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, stream);
+    if (w1_arows(M, G) <= 16) return launch_w1<G, 1, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
+    return launch_w1<G, 2, 2, 1>(bits, sc, N, K, M, ws, xs, bias, y, nsplit, part, counters, y16, stream);
 }
 
 // Tokens per pass: the A rows of a pass (2 x tokens x slots) fit two row blocks.
@@ -608,7 +615,7 @@ size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G) {
 
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, uint16_t* y16) {
     const int64_t tb = w1_tokens_per_pass(G);
     const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
     const int ns = w1_splits(N, K);
@@ -630,19 +637,19 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
         switch (G) {
         case 32:
             e = launch_w1_g<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
-                                stream);
+                                y16 ? y16 + m0 * N : nullptr, stream);
             break;
         case 64:
             e = launch_w1_g<64>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
-                                stream);
+                                y16 ? y16 + m0 * N : nullptr, stream);
             break;
         case 128:
             e = launch_w1_g<128>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
-                                 stream);
+                                 y16 ? y16 + m0 * N : nullptr, stream);
             break;
         default:
             e = launch_w1_g<256>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
-                                 stream);
+                                 y16 ? y16 + m0 * N : nullptr, stream);
             break;
         }
         if (e != hipSuccess) return e;

@@ -29,7 +29,8 @@ hipError_t static_scratch(void** out, hipStream_t stream);
 // so each (kernel, device) pair is set once and remembered.
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
 
-hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs,
+// xsum: int32 [M] receiving sum_k q[m,k], or NULL
+hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs, int32_t* xsum,
                            hipStream_t stream);
 // bf16 bits (round to nearest, ties to even) of n fp32 values.
 hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStream_t stream);
@@ -42,26 +43,29 @@ hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStrea
 size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G);
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, uint16_t* y16 = nullptr);
 
 // int8-activation prefill product, format i2_s.  ws: gemm_i8_workspace bytes
 // of split-K partial tiles and counters one per output tile (zero on entry,
 // left zero), or NULL (either) to forbid splits.
 size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
+// xsum: sum_k q per token from the quantization (then the kernel skips its
+// own row sums), or NULL; y16: bf16 output [M,N] written instead of y, or NULL.
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y,
-                              int32_t* acc_out, int32_t* counters, void* ws, hipStream_t stream);
+                              int32_t* acc_out, int32_t* counters, void* ws, hipStream_t stream,
+                              const int32_t* xsum = nullptr, uint16_t* y16 = nullptr);
 // The same product with W1 weights of group size 128 (bits uint32 [N][K/32],
 // scales fp16 [N][K/128]); y = s_tok * sum_g s_g * d_g in fp32 (no acc_out).
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                              const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
-                             hipStream_t stream);
+                             hipStream_t stream, uint16_t* y16 = nullptr);
 // The same product with TQ2_0 weights (codes N*K/4 bytes, scales fp16
 // [N][K/256]); y = s_tok * sum_b s_b * d_b in fp32 (no acc_out); the same
 // workspace size and rules.
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                               const int8_t* xq, const float* xs, int64_t M, const float* bias, float* y,
-                              int32_t* counters, void* ws, hipStream_t stream);
+                              int32_t* counters, void* ws, hipStream_t stream, uint16_t* y16 = nullptr);
 
 }  // namespace llk
 

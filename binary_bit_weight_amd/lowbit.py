@@ -41,7 +41,7 @@ SIGNATURES = {
     "ll_unpack_w1": (C.c_int, [_P, _I64, _I64, _P]),
     "ll_w1_from_dense": (C.c_int, [_P, _I64, _I64, _I32, _P, _P]),
     "ll_validate": (C.c_int, [_I32, _P, _I64, _I64, _P]),
-    "ll_quantize_act": (C.c_int, [_P, _I32, _I64, _I64, _P, _P, _P]),
+    "ll_quantize_act": (C.c_int, [_P, _I32, _I64, _I64, _P, _P, _P, _P]),
     "ll_gemv_workspace_size": (_SZ, [_P, _I32, _I64]),
     "ll_bitlinear_gemv": (C.c_int, [_P, _I32, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "ll_gemm_workspace_size": (_SZ, [_P, _I64]),
@@ -230,11 +230,11 @@ class Weights:
         return C.byref(self.desc)
 
 
-def ll_quantize_act(x, xq, xs, stream=None):
+def ll_quantize_act(x, xq, xs, stream=None, xsum=None):
     import torch
     M, K = x.shape
     dt = LL_DT_BF16 if x.dtype == torch.bfloat16 else LL_DT_F32
-    _check(lib().ll_quantize_act(_dev(x), dt, M, K, _dev(xq), _dev(xs), _stream(stream)))
+    _check(lib().ll_quantize_act(_dev(x), dt, M, K, _dev(xq), _dev(xs), _dev(xsum), _stream(stream)))
 
 
 def ll_gemv_workspace_size(w: Weights, act, M):
@@ -304,14 +304,16 @@ def upload_w1(bits, scales, K, group, device="cuda") -> Weights:
                    _to_gpu(np.asarray(scales, np.uint16).view(np.int16), device), group)
 
 
-def quantize(x, stream=None):
-    """(xq int8 [M,K], xs fp32 [M]) = ll_quantize_act(x)."""
+def quantize(x, stream=None, with_sum=False):
+    """(xq int8 [M,K], xs fp32 [M]) = ll_quantize_act(x); with_sum also
+    returns xsum int32 [M] = sum_k xq[m,k]."""
     import torch
     M, K = x.shape
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     xs = torch.empty((M,), dtype=torch.float32, device=x.device)
-    ll_quantize_act(x, xq, xs, stream)
-    return xq, xs
+    xsum = torch.empty((M,), dtype=torch.int32, device=x.device) if with_sum else None
+    ll_quantize_act(x, xq, xs, stream, xsum)
+    return (xq, xs, xsum) if with_sum else (xq, xs)
 
 
 def gemv(w: Weights, x, xs=None, bias=None, stream=None):

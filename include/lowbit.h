@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LL_ABI_VERSION 3
+#define LL_ABI_VERSION 4
 
 /* Bytes at the start of every workspace reserved for split-K counters. */
 #define LL_WORKSPACE_COUNTER_BYTES 4096
@@ -176,9 +176,11 @@ ll_status ll_validate(int32_t fmt, const void* codes, int64_t N, int64_t K, int6
    x: device [M,K] fp32 or bf16 (x_dtype); xq: device int8 [M,K];
    xs: device fp32 [M].  For each token: a = max|x|; a == 0 gives s = 0 and
    q = 0; else inv = 127/a (IEEE fp32 division), q = round-half-even(x*inv)
-   clamped to [-127,127], s = a/127.  1 <= M, 1 <= K <= 2^20. */
+   clamped to [-127,127], s = a/127.  xsum: device int32 [M] receiving
+   sum_k q[m,k] (the per-token term of the offset form sum_k w q =
+   sum_k (w+1) q - sum_k q), or NULL.  1 <= M, 1 <= K <= 2^20. */
 ll_status ll_quantize_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
-                          int8_t* xq, float* xs, void* stream);
+                          int8_t* xq, float* xs, int32_t* xsum, void* stream);
 
 /* Bytes of device workspace ll_bitlinear_gemv needs for these arguments
    (0 when none is needed).  Returns (size_t)-1 for invalid arguments. */
@@ -345,9 +347,11 @@ ll_status ll_bitlinear_gemm_noalloc(const ll_weights* w, const int8_t* xq, const
    fp32 [N] or NULL; y: device bf16 bits [M,N].  The result is the bf16
    rounding of what ll_quantize_act followed by ll_bitlinear_gemm gives.
    workspace: at least ll_binary_linear_workspace_size(w, M) bytes, under
-   the workspace rules above (it holds the quantized x, the product's
-   scratch and the fp32 y).  Three launches on `stream`; returns (size_t)-1 from the
-   size function for an unsupported format or invalid arguments. */
+   the workspace rules above (it holds the quantized x with its token scales
+   and sums, and the product's scratch).  Two launches on `stream`: the
+   quantization, then the product with the bias and the bf16 rounding in its
+   epilogue.  The size function returns (size_t)-1 for an unsupported
+   format or invalid arguments. */
 size_t ll_binary_linear_workspace_size(const ll_weights* w, int64_t M);
 ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, const float* bias, uint16_t* y,
                            void* workspace, size_t workspace_bytes, void* stream);

@@ -76,6 +76,31 @@ def test_binary_linear_w1_bitexact(N, K, G, M, with_bias):
     assert np.array_equal(y, oracle.f32_to_bf16(y32))
 
 
+# W1 with G = 128 above 16 tokens: the int8 matrix cores with fp32 group
+# scaling and the bf16 rounding in their epilogue; (300, 2048, 200) splits K
+# four ways, (130, 1280, 129) has ragged tiles and a bias
+@pytest.mark.parametrize("N,K,M,with_bias", [(300, 2048, 200, False), (130, 1280, 129, True)])
+def test_binary_linear_w1_mfma_within_bound(N, K, M, with_bias):
+    G = 128
+    bits, scales = make_w1(7450 + N, N, K, G)
+    xb = synth.normal_bf16_bits(7550 + M, M, K)
+    b, bd = _bias(7650 + N, N, with_bias)
+    W = L.upload_w1(bits, scales, K, G)
+    announce("binary_linear w1 mfma", N, K, M)
+    y = _bits(L.binary_linear(W, _bf16_dev(xb), bias=bd))
+    yv = np.array([oracle.bf16_to_f32(int(v)) for v in y.reshape(-1)], np.float64).reshape(y.shape)
+    q, s = oracle.quantize_bf16(xb)
+    y_ref, S = oracle.w1a8_gemm(bits, scales, K, G, q, s, bias=b, threads=TH)
+    # fp32 bound of the matrix-core path (T = s_tok sum_g |s_g| sum_{k in g} |q|), then half a bf16 ulp
+    sg = np.abs(scales.view(np.float16).astype(np.float64))
+    qa = np.abs(q.astype(np.float64)).reshape(M, K // G, G).sum(axis=2)
+    tsum = s.astype(np.float64)[:, None] * (qa @ sg.T)
+    exact = s.astype(np.float64)[:, None] * S + (0.0 if b is None else b.astype(np.float64)[None, :])
+    bound = 1e-5 * tsum + 1e-6 + np.abs(exact) * 2.0 ** -8 + 2.0 ** -24 * np.abs(exact)
+    assert (np.abs(yv - exact) <= bound).all(), "worst %.3f" % float((np.abs(yv - exact) / bound).max())
+    assert y_ref.shape == y.shape
+
+
 @pytest.mark.parametrize("N,K,M", [(150, 768, 33), (64, 2048, 5)])
 def test_binary_linear_tq2_within_bound(N, K, M):
     w, sc, blocks = make_tq2(7700 + N, N, K)

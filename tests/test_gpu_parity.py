@@ -40,10 +40,14 @@ def test_quantize_bitexact(M, K, dtype):
             xf[0, 4:] = np.clip(xf[0, 4:], -100, 100)
         x = t.from_numpy(xf).cuda()
         q_ref, s_ref = oracle.quantize_f32(xf)
-    xq, xs = L.quantize(x)
+    xq, xs, xsum = L.quantize(x, with_sum=True)
     t.cuda.synchronize()
     assert np.array_equal(xq.cpu().numpy(), q_ref)
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(xsum.cpu().numpy().astype(np.int64), q_ref.astype(np.int64).sum(axis=1))
+    xq2, xs2 = L.quantize(x)                           # without the sums: the same codes
+    t.cuda.synchronize()
+    assert np.array_equal(xq2.cpu().numpy(), q_ref)
 
 
 # ------------------------------------------------------------------ i2_s, fp32 activations

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES), "binding and header disagree"
-    assert L.ll_abi_version() == 3
+    assert L.ll_abi_version() == 4
     assert L.ll_strerror(-5) == "workspace missing or too small"
 
 
@@ -153,26 +153,28 @@ def test_gemm_and_quantize_argument_errors():
                                  None, 0, None) == -2
     assert lib.ll_bitlinear_gemm(C.byref(w), C.c_void_p(FAKE + 1), C.c_void_p(FAKE), 32, None, C.c_void_p(FAKE),
                                  None, None, 0, None) == -3
-    assert lib.ll_quantize_act(C.c_void_p(FAKE), 5, 4, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == -1
-    assert lib.ll_quantize_act(C.c_void_p(FAKE), L.LL_DT_F32, 0, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == -1
-    assert lib.ll_quantize_act(None, L.LL_DT_F32, 2, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None) == -1
+    assert lib.ll_quantize_act(C.c_void_p(FAKE), 5, 4, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -1
+    assert lib.ll_quantize_act(C.c_void_p(FAKE), L.LL_DT_F32, 0, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -1
+    assert lib.ll_quantize_act(None, L.LL_DT_F32, 2, 4, C.c_void_p(FAKE), C.c_void_p(FAKE), None, None) == -1
+    assert lib.ll_quantize_act(C.c_void_p(FAKE), L.LL_DT_F32, 2, 4, C.c_void_p(FAKE), C.c_void_p(FAKE),
+                               C.c_void_p(FAKE + 2), None) == -3
 
 
 def test_binary_linear_arguments_and_workspace():
     """ll_binary_linear: errors found before any launch, and the workspace
     layout (split-K counters | the product's data | int8 x | token scales |
-    fp32 y, each on a 256-byte boundary); TQ2_0 products refuse acc_out."""
+    token sums, each on a 256-byte boundary); TQ2_0 products refuse acc_out."""
     lib = L.lib()
     w = _w(N=64, K=256)
     M = 3
     n = lib.ll_binary_linear_workspace_size(C.byref(w), M)
-    # counters 4096, no split data for one 128-row tile, x 768 -> 768, scales 12 -> 256, y 64*3*4 = 768
+    # counters 4096, no split data for one 128-row tile, x 768 -> 768, scales 12 -> 256, sums 12
     assert lib.ll_gemm_workspace_size(C.byref(w), M) == 0
-    assert n == CB + 768 + 256 + 768
+    assert n == CB + 768 + 256 + 12
     wt = _w(fmt=L.LL_FMT_TQ2_0, N=64, K=256)
     assert lib.ll_binary_linear_workspace_size(C.byref(wt), M) == n
     w1 = _w(fmt=L.LL_FMT_W1, N=64, K=256, group=128)
-    assert lib.ll_binary_linear_workspace_size(C.byref(w1), M) > CB + 768 + 256 + 768
+    assert lib.ll_binary_linear_workspace_size(C.byref(w1), M) > CB + 768 + 256 + 12
     assert lib.ll_binary_linear_workspace_size(C.byref(w), 0) == C.c_size_t(-1).value
 
     def call(w, x=FAKE, M=M, y=FAKE, ws=FAKE, wsb=1 << 30):
