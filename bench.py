@@ -210,23 +210,71 @@ def time_events(torch, fn, reps, stream):
     return s.elapsed_time(e) / reps
 
 
-def cpu_baseline(oracle, synth, packed, budget_s=12.0):
-    """The oracle (single thread, fp64, decoding every weight from the packed
-    bytes) on one layer's seven products, repeated until budget_s elapses."""
-    xs = [synth.normal_f32(9000 + s, 1, HIDDEN if s != 3 else FFN) for s in range(4)]
-    done_bytes, t0, layers = 0, time.perf_counter(), 0
-    while True:
-        for name, N, K, slot in ROLES:
-            p, _, _ = packed[name]
-            oracle.i2s_gemv_f32(p, N, K, xs[slot])
-            done_bytes += p.size
-        layers += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full layer(s) of the decode step (7 i2_s GEMVs, %.1f MB) on one host core, %.1f s"
-                      % (layers, done_bytes / 1e6, dt)}
+def cpu_baseline(oracle, packed, items):
+    """The oracle (fp64, decoding every weight from the packed bytes) on the
+    whole decode step the GPU leg runs -- its 210 products on their own
+    activations -- single-threaded and with its rows split over every host
+    core (oracle.cores()); the median of three runs of each."""
+    xs = [x.cpu().numpy() for (_, x, _, _) in items]
+    nbytes = sum(packed[name][0].size for _ in range(LAYERS) for (name, _, _, _) in ROLES)
+
+    def run(threads):
+        t0 = time.perf_counter()
+        for layer in range(LAYERS):
+            for r, (name, N, K, _) in enumerate(ROLES):
+                oracle.i2s_gemv_f32(packed[name][0], N, K, xs[len(ROLES) * layer + r], threads=threads)
+        return time.perf_counter() - t0
+
+    cores = oracle.cores()
+    one = sorted(run(1) for _ in range(3))[1]
+    allc = sorted(run(cores) for _ in range(3))[1]
+    return {"value": round(nbytes / allc / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "the whole 30-layer decode step (210 i2_s GEMVs, %.1f MB, the GPU leg's activations), "
+                      "median of 3 runs: %.2f s on %d host threads" % (nbytes / 1e6, allc, cores),
+            "single_thread": {"value": round(nbytes / one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(one, 3)}}
+
+
+def stream_probe(L, torch, dev, stream, nbytes=1 << 30):
+    """Plain streaming read of a 1 GiB device buffer (ll_probe_stream_read),
+    timed with HIP events: the read rate the weight-streaming kernels are
+    compared with."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    blocks = 256 * 8
+    sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+    settle(torch, lambda i: L.ll_probe_stream_read(buf, sink, blocks, stream))
+    ms = time_events(torch, lambda: L.ll_probe_stream_read(buf, sink, blocks, stream), 20, stream)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "ms": round(ms, 4)}
+
+
+def dependent_decode_step(L, torch, items, weight_bytes, steps, stream):
+    """The same 30 layers with the products of a layer grouped as a real
+    decode orders them: Q/K/V (one activation), O, up/gate (one activation),
+    down -- 120 prepared batches run one after another (2 launches each),
+    captured in one HIP graph.  Each batch waits for the one before, as a
+    layer's input waits for the previous layer's output."""
+    plans = []
+    for layer in range(LAYERS):
+        it = items[len(ROLES) * layer: len(ROLES) * (layer + 1)]
+        for group in ([0, 1, 2], [3], [4, 5], [6]):
+            plans.append(L.GemvPlan([it[r] for r in group], 1))
+
+    def run(st):
+        for pl in plans:
+            pl.prepare(st)
+            pl.product(st)
+    run(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(None)
+    settle(torch, lambda i: g.replay())
+    ms = time_events(torch, g.replay, steps, stream)
+    del g
+    return {"ms_per_step": round(ms, 4), "GB_s": round(weight_bytes / (ms * 1e-3) / 1e9, 1), "batches": len(plans),
+            "note": "per layer: Q/K/V, O, up/gate, down as four prepared batches in order (graph replay)"}
 
 
 def gemm_operands(L, synth, torch, dev, stream, N, K, M=512):
@@ -360,6 +408,18 @@ def w1_roofline(L, synth, torch, dev, stream, steps):
 
 def extras_single(L, synth, torch, dev, stream):
     out = {}
+    # the 256 x 512 i2_s GEMV of the smallest configuration (scale 1/16, seed 101)
+    w = synth.ternary(101, 256, 512)
+    p = L.ll_pack_i2s(w, 0.0625)
+    reps = max(1, int(np.ceil(2 ** 29 / p.size / 64)))
+    Ws = [L.upload_i2s(p, 256, 512, dev) for _ in range(reps)]
+    x = torch.from_numpy(synth.normal_f32(102, 1, 512)).to(dev)
+    y = torch.empty((1, 256), dtype=torch.float32, device=dev)
+    ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_F32, x, None, 1, None, y, None, st),
+                    reps, max(2 * reps, 64), stream)
+    out["i2s_gemv_f32_single_call_256x512"] = {"us": round(ms * 1e3, 2), "GB_s": round(p.size / (ms * 1e-3) / 1e9, 1),
+                                               "weight_bytes": int(p.size)}
+    del Ws
     for name, N, K in [("2560x2560", 2560, 2560), ("6912x2560", 6912, 2560), ("2560x6912", 2560, 6912)]:
         w = synth.ternary(5, N, K)
         p = L.ll_pack_i2s(w, 0.05)
@@ -406,7 +466,7 @@ def extras_single(L, synth, torch, dev, stream):
         del copies, plan
     # W1A8 decode, hidden 5120, G = 128: QKV, MLP gate, LM head at M = 1 and 8
     K, G = 5120, 128
-    for name, N, seed in [("qkv", 7168, 501), ("gate", 17408, 502), ("lm_head", 248320, 503)]:
+    for name, N, seed in [("qkv", 7168, 501), ("qkv_card", 8192, 504), ("gate", 17408, 502), ("lm_head", 248320, 503)]:
         bits, sc = w1_weights(L, synth, seed, N, K, G)
         wbytes = bits.nbytes + sc.nbytes
         reps = max(1, int(np.ceil(2 ** 29 / wbytes)))
@@ -528,6 +588,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # whatever --warmup says, at least 80 ms of continuous steps before the
+    # timing: after an idle period the clocks need about 20 ms to settle
+    t_settle = time.perf_counter()
+    settle(torch, lambda i: step(), 0.08)
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     # the step's two launches captured once in a HIP graph and replayed
     # (reported beside the headline: same kernels, no host launch cost)
     graph = torch.cuda.CUDAGraph()
@@ -589,7 +654,11 @@ def main():
                                "~U(0.01,0.1); 210 products as one prepared batch (2 launches)",
                    "M": 1, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN,
                    "weight_bytes_per_step": int(weight_bytes),
-                   "ms_per_step_graph_replay": round(ms_per_step_graph, 4)},
+                   "ms_per_step_graph_replay": round(ms_per_step_graph, 4),
+                   "independent_products": "the 210 products run as one batch, each on its own activation: a "
+                                           "throughput figure for the layer stack's weights; extras."
+                                           "i2s_decode_step_dependent runs the layers in order",
+                   "warmup_settle_ms": round(settle_ms, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -601,14 +670,20 @@ def main():
     res["roofline_gemm"] = gemm_roofline(L, synth, torch, dev, stream, args.steps)
     if not args.no_cpu:
         log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(oracle, synth, packed)
+        res["cpu_baseline"] = cpu_baseline(oracle, packed, items)
+    log("stream probe")
+    sp = stream_probe(L, torch, dev, stream)
+    res["roofline"]["stream_probe_GB_s"] = sp["GB_s"]
+    res["roofline"]["frac_of_stream_probe"] = round(achieved / sp["GB_s"], 4)
     if not args.no_extras:
         # the W1A8 LM head needs its 179 MB of weights built on the host: with the extras
         log("W1A8 LM head")
         res["roofline_w1a8"] = w1_roofline(L, synth, torch, dev, stream, args.steps)
         log("extras")
         res["extras"] = {"i2s_decode_step_fused_epilogues":
-                         fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, args.steps)}
+                         fused_decode_step(L, synth, torch, dev, stream, items, weight_bytes, args.steps),
+                         "i2s_decode_step_dependent": dependent_decode_step(L, torch, items, weight_bytes, args.steps,
+                                                                            stream)}
         res["extras"].update(extras_single(L, synth, torch, dev, stream))
     print(json.dumps(res), flush=True)
 

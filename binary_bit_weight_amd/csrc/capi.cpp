@@ -245,6 +245,15 @@ ll_status ll_bitlinear_gemm(const ll_weights* w, const int8_t* xq, const float* 
                       fn);
 }
 
+ll_status ll_probe_stream_read(const void* p, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+    if (!p || !sink) return ll::fail(LL_EINVAL, "ll_probe_stream_read: NULL pointer");
+    if (bytes == 0 || bytes % 16) return ll::fail(LL_ESHAPE, "ll_probe_stream_read: bytes must be a positive multiple of 16");
+    if (blocks < 1 || blocks > 65535) return ll::fail(LL_EINVAL, "ll_probe_stream_read: blocks must be in [1, 65535]");
+    if (!aligned(p, 16) || !aligned(sink, 4)) return ll::fail(LL_EALIGN, "ll_probe_stream_read: p 16-byte, sink 4-byte aligned");
+    return hip_status(llk::launch_stream_read(p, bytes, sink, blocks, static_cast<hipStream_t>(stream)),
+                      "ll_probe_stream_read");
+}
+
 size_t ll_gemm_noalloc_scratch_bytes(void) { return llk::static_scratch_bytes(); }
 
 ll_status ll_bitlinear_gemm_noalloc(const ll_weights* w, const int8_t* xq, const float* xs, int64_t M,

@@ -78,15 +78,20 @@ __device__ __forceinline__ double ld_coherent64(const double* p) {
     return __longlong_as_double(__hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)),
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-// One split's arrival at its tile's counter: an agent-scope acquire-release
-// read-modify-write.  Its release half orders the partial sums that the
-// workgroup published before the barrier that precedes it (each wave waits
-// for its stores first); its acquire half orders the partial-sum loads that
-// the last arrival makes after the barrier that follows it.  Returns the
-// count before this arrival.
-__device__ __forceinline__ int32_t arrive_acq_rel(int32_t* c) {
-    return __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Split-K handoff.  A split publishes its partial sums, every wave waits for
+// its stores, the workgroup meets at a barrier, and one thread counts the
+// split in with arrive_release: an agent-scope release read-modify-write,
+// which orders the published partials before the count.  The split that
+// reads count + 1 == splits is the last; its threads then take
+// acquire_agent (an agent-scope acquire fence, which pairs with every other
+// split's release through the counter) before loading the others'
+// partials.  Only the last split pays for the acquire (a cache invalidate),
+// so the arrivals do not throw away the L2 contents other workgroups are
+// still reading.
+__device__ __forceinline__ int32_t arrive_release(int32_t* c) {
+    return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 // Wait until every vector memory operation of this wave has completed
 // (gfx9 s_waitcnt: vmcnt = 0, expcnt and lgkmcnt not waited on).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -55,10 +55,10 @@
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its
 // partial tile to the workspace and counts itself in at the tile's counter
-// (agent-scope acquire-release); the split that arrives last adds the
-// others' partials to its own and runs the epilogue, then resets the
-// counter (so the counters stay zero between calls).  Integer addition
-// makes the i2_s result independent of the order.
+// (an agent-scope release); the split that arrives last takes an acquire
+// fence, adds the others' partials to its own and runs the epilogue, then
+// resets the counter (so the counters stay zero between calls).  Integer
+// addition makes the i2_s result independent of the order.
 #include <type_traits>
 
 #include "common.h"
@@ -483,9 +483,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                     st_coherent(mine + ((mb * 2 + nb) * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[mb][nb][r])));
         wait_vmem();
         __syncthreads();
-        if (tid == 0) last_flag = arrive_acq_rel(counters + tile) == S - 1;
+        if (tid == 0) last_flag = arrive_release(counters + tile) == S - 1;
         __syncthreads();
         if (!last_flag) return;
+        acquire_agent();
         if constexpr (FMT == 1) {
             for (int s = 0; s < S; ++s) {
                 if (s == split) continue;

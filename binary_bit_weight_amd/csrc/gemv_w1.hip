@@ -498,9 +498,10 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     if (nsplit == 1) return;
     wait_vmem();
     __syncthreads();
-    if (tid == 0) last_flag = arrive_acq_rel(counters + rb) == nsplit - 1;
+    if (tid == 0) last_flag = arrive_release(counters + rb) == nsplit - 1;
     __syncthreads();
     if (!last_flag) return;
+    acquire_agent();
     for (int e = tid; e < kW1Waves * 2 * 16 * M; e += 64 * kW1Waves) {
         const int m = e % M;
         const int col = e / M;

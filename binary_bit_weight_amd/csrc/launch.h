@@ -24,6 +24,10 @@ constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
 size_t static_scratch_bytes();
 hipError_t static_scratch(void** out, hipStream_t stream);
 
+// Diagnostic streaming read of `bytes` (a multiple of 16) by `blocks`
+// workgroups; one word per workgroup into sink.
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+
 // Raises a kernel's dynamic LDS limit to at least `bytes` on the current
 // device.  hipFuncSetAttribute is a host-side call that costs microseconds,
 // so each (kernel, device) pair is set once and remembered.
@@ -32,8 +36,6 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
 // xsum: int32 [M] receiving sum_k q[m,k], or NULL
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs, int32_t* xsum,
                            hipStream_t stream);
-// bf16 bits (round to nearest, ties to even) of n fp32 values.
-hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStream_t stream);
 
 // W1A8 product (binary weights, int8 activations), any M (passes of up to 16
 // tokens, each reading the weights once); K % 128 == 0, G in {32,64,128,256}.

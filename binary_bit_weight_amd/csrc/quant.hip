@@ -115,38 +115,9 @@ __global__ void __launch_bounds__(256) quant_kernel(const void* __restrict__ x, 
     }
 }
 
-// fp32 -> bf16 bits, round to nearest with ties to even (on the bit
-// pattern: add 0x7FFF plus the lowest kept bit, keep the high half); NaN
-// becomes the quiet NaN 0x7FC0 with its sign.  Four elements per thread and
-// step, grid-stride.
-__global__ void __launch_bounds__(256) f32_to_bf16_kernel(const float* __restrict__ y, uint16_t* __restrict__ out,
-                                                          int64_t n) {
-    const int64_t stride = int64_t(gridDim.x) * 256 * 4;
-    for (int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; i0 < n; i0 += stride) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t i = i0 + e;
-            if (i >= n) break;
-            const uint32_t u = __float_as_uint(y[i]);
-            uint16_t b;
-            if ((u & 0x7FFFFFFFu) > 0x7F800000u) b = uint16_t(((u >> 16) & 0x8000u) | 0x7FC0u);
-            else b = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-            out[i] = b;
-        }
-    }
-}
-
 }  // namespace
 
 namespace llk {
-
-hipError_t launch_f32_to_bf16(const float* y, uint16_t* out, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    const int64_t blocks = (n + 1023) / 1024;
-    const dim3 grid{unsigned(blocks < 8192 ? blocks : 8192)}, block{256};
-    hipLaunchKernelGGL(f32_to_bf16_kernel, grid, block, 0, stream, y, out, n);
-    return hipGetLastError();
-}
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, int8_t* xq, float* xs, int32_t* xsum,
                            hipStream_t stream) {

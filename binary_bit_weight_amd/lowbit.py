@@ -46,6 +46,7 @@ SIGNATURES = {
     "ll_bitlinear_gemv": (C.c_int, [_P, _I32, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "ll_gemm_workspace_size": (_SZ, [_P, _I64]),
     "ll_bitlinear_gemm": (C.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "ll_probe_stream_read": (C.c_int, [_P, _SZ, _P, _I32, _P]),
     "ll_gemm_noalloc_scratch_bytes": (_SZ, []),
     "ll_bitlinear_gemm_noalloc": (C.c_int, [_P, _P, _P, _I64, _P, _P, _P, _P]),
     "ll_binary_linear_workspace_size": (_SZ, [_P, _I64]),
@@ -255,6 +256,12 @@ def ll_bitlinear_gemm(w: Weights, xq, xs, M, bias, y, acc_out=None, workspace=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ll_bitlinear_gemm(w.ref, _dev(xq), _dev(xs), M, _dev(bias), _dev(y), _dev(acc_out),
                                    _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def ll_probe_stream_read(buf, sink, blocks, stream=None):
+    """Streams every byte of the device tensor buf once (diagnostic)."""
+    _check(lib().ll_probe_stream_read(_dev(buf), buf.numel() * buf.element_size(), _dev(sink), blocks,
+                                      _stream(stream)))
 
 
 def ll_gemm_noalloc_scratch_bytes() -> int:

@@ -356,6 +356,17 @@ size_t ll_binary_linear_workspace_size(const ll_weights* w, int64_t M);
 ll_status ll_binary_linear(const ll_weights* w, const uint16_t* x, int64_t M, const float* bias, uint16_t* y,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ */
+/* Diagnostics                                                          */
+/* ------------------------------------------------------------------ */
+
+/* A plain streaming read of `bytes` (a positive multiple of 16) at device
+   pointer p (16-byte aligned) by `blocks` workgroups of 256 threads, each
+   16-byte word once: the reference read rate the weight-streaming products
+   are compared with.  sink: device uint32 [blocks], overwritten with a fold
+   of what each workgroup read. */
+ll_status ll_probe_stream_read(const void* p, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
