@@ -65,7 +65,7 @@ constexpr int kSliceChunks = 8;                        // chunks per preparation
 #define LL_F4_CUNROLL 1                                // chunk loop of the multiply not unrolled (register use)
 #endif
 #ifndef LL_F4_NT
-#define LL_F4_NT 0                                     // weights read with non-temporal loads
+#define LL_F4_NT 1                                     // weights read with non-temporal loads
 #endif
 constexpr int kCB = LL_F4_CB;
 constexpr int kGroup = 4;                              // chunks per weight tile: 256 bytes of each row
