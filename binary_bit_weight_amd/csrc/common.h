@@ -34,6 +34,25 @@ __device__ __forceinline__ int32_t ld32(const void* p) { return *(gint32*)p; }
 __device__ __forceinline__ f32x4 ld16f(const void* p) { return *(gf32x4*)p; }
 __device__ __forceinline__ uint16_t ld2(const void* p) { return *(__attribute__((address_space(1))) const uint16_t*)p; }
 
+// Buffer loads: a resource (base address, size in bytes) in scalar registers
+// plus a per-lane byte offset.  The hardware returns zeros for an offset at or
+// past the size, so a resource ending with its array makes every read past the
+// array's end a read of zeros.  bytes <= 0 gives an empty resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : bytes >= int64_t(0xFFFFFFFF) ? 0xFFFFFFFFu : uint32_t(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(n), 0x00020000);
+}
+// 16 bytes, streaming (non-temporal: read once).
+__device__ __forceinline__ i32x4 buffer_ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ uint16_t buffer_ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buffer_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // Butterfly sum / max over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

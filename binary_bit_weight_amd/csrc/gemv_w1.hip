@@ -5,13 +5,18 @@
 //     d = sum w*q = 2 * sum_{b=1} q - sum q,
 // so only sum_{b=1} q has to be formed from the bits.  It runs on the fp8 x fp4
 // matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales):
-//   B (weights): a 32-bit word of bits masked in place, (word >> j) & 0x11111111,
-//       is eight fp4 (e2m1) values b * 0.5 -- no unpacking beyond one shift
-//       and one AND per 8 weights;
-//   A (activations): q = 16 * hi + lo with hi, lo in [-8, 8], both exact in
-//       fp8 e4m3, one MFMA row each; rows are (token, group slot, digit).
-// Every product is a multiple of 1/4 below 2^10 and every sum stays below
-// 2^22, so the fp32 accumulation is exact: sum_{b=1} q = 2 * (16 D_hi + D_lo).
+//   B (weights): a 32-bit word of bits masked in place is eight fp4 (e2m1)
+//       values: word & (0x11111111 << j) for j = 0, 1, 2 leaves bit 4i + j at
+//       bit j of nibble i (value b * 2^(j-1)), and (word >> 1) & 0x44444444
+//       moves bit 4i + 3 (the nibble's sign position) to bit 2 (value b * 2):
+//       five operations per 32 weights;
+//   A (activations): q = 16 * hi + lo with hi, lo in [-8, 8], one MFMA row
+//       each; rows are (token, group slot, digit).  The digit meeting nibble
+//       position j is stored times 2^(2 - min(j, 2)), so every product is
+//       2 b d whatever j is (integers of at most 3 significant bits below 2^6,
+//       exact in fp8 e4m3).
+// Every product is an integer below 2^5 in magnitude and every sum stays below
+// 2^13, so the fp32 accumulation is exact: sum_{b=1} q = (16 D_hi + D_lo) / 2.
 // The epilogue forms S = sum_g s_g * d_g with fp64 fmas of exact products in
 // group order and y = (float)((double)xs * S) (+ bias), bit for bit the
 // oracle's result.
@@ -32,6 +37,11 @@
 // window.  Loads run two windows ahead of the multiply.
 #include "common.h"
 #include "launch.h"
+
+#include <mutex>
+#include <type_traits>
+#include <tuple>
+#include <vector>
 
 namespace {
 
@@ -87,23 +97,13 @@ __host__ __device__ inline int w1_lds_bytes(int M, int G) {
     return kW1Waves * kW1RowsPerWave * w1_stride(G) + 2 * ((w1_abuf_bytes(M, G) + 15) / 16 * 16);
 }
 
-__device__ __forceinline__ uint8_t fp8_small_int(int v) {
-    // exact e4m3 encoding of an integer in [-8, 8]
-    const int a = v < 0 ? -v : v;
-    int code;
-    if (a == 0) code = 0;
-    else if (a == 1) code = 0x38;
-    else if (a < 4) code = 0x40 | ((a - 2) << 2);          // 2 -> 0x40, 3 -> 0x44
-    else if (a < 8) code = 0x48 | ((a - 4) << 1);          // 4..7 -> 0x48, 0x4A, 0x4C, 0x4E
-    else code = 0x50;                                      // 8
-    return uint8_t(code | (v < 0 ? 0x80 : 0));
-}
-
 // One 16-byte piece u of an A row of digit h (0: hi, 1: lo) from the 32
 // source bytes (lo4, hi4) at 32 qp of its 128-k chunk, qp = 2 (u % 2) + u / 4.
 // Piece u holds A bytes 16u + i of lane quarter q = u / 2; byte i pairs with B
-// quarter qp, nibble 16 (q % 2) + i, i.e. the chunk-local weight
-// 32 qp + 2 (q % 2) + i / 8 + 4 (i % 8): all sixteen lie in those 32 bytes.
+// quarter qp, nibble e = 16 (q % 2) + i, i.e. B word j = e / 8 and the
+// chunk-local weight 32 qp + 4 (i % 8) + j: source byte j of source dword
+// i % 8.  The digit is stored times 2^(2 - min(j, 2)) through the hardware's
+// fp32 -> fp8 (OCP e4m3) conversion, exact for these values.
 // sum: the sixteen source values (0 outside the slot).
 __device__ __forceinline__ i32x4 w1_piece(const i32x4& lo4, const i32x4& hi4, int u, int h, bool in_slot, int& sum) {
     const uint32_t dw[8] = {uint32_t(lo4[0]), uint32_t(lo4[1]), uint32_t(lo4[2]), uint32_t(lo4[3]),
@@ -113,19 +113,28 @@ __device__ __forceinline__ i32x4 w1_piece(const i32x4& lo4, const i32x4& hi4, in
     sum = 0;
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
-        uint32_t word = 0;
+        const int j = b0 + (w4 >> 1);                      // B word of output bytes 4 w4 .. 4 w4 + 3
+        const float scale = float(1 << (2 - (j < 2 ? j : 2)));
+        float f[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-            const int i = 4 * w4 + bb;
-            const int v = in_slot ? int(int8_t(dw[i & 7] >> (8 * (b0 + (i >> 3))))) : 0;
+            const int v = in_slot ? int(int8_t(dw[4 * (w4 & 1) + bb] >> (8 * j))) : 0;
             sum += v;
-            const int hi = (v + 8) >> 4;                // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
+            const int hi = (v + 8) >> 4;                    // floor((v + 8) / 16): v = 16 hi + lo, lo in [-8, 7]
             const int d = h == 0 ? hi : v - 16 * hi;
-            word |= uint32_t(fp8_small_int(d)) << (8 * bb);
+            f[bb] = float(d) * scale;
         }
-        out[w4] = word;
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], word, true);
+        out[w4] = uint32_t(word);
     }
     return i32x4{int(out[0]), int(out[1]), int(out[2]), int(out[3])};
+}
+
+// The B operand of one 128-k chunk of a row from its 32-bit word of bits.
+__device__ __forceinline__ i32x8 w1_bv(uint32_t word) {
+    return i32x8{int(word & 0x11111111u), int(word & 0x22222222u), int(word & 0x44444444u),
+                 int((word >> 1) & 0x44444444u), 0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------- preparation
@@ -394,8 +403,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const uint32_t word = *reinterpret_cast<const uint32_t*>(wtile + (16 * cb + nl) * stride + 16 * c + 4 * q);
-                const i32x8 bv{int(word & 0x11111111u), int((word >> 1) & 0x11111111u), int((word >> 2) & 0x11111111u),
-                               int((word >> 3) & 0x11111111u), 0, 0, 0, 0};
+                const i32x8 bv = w1_bv(word);
 #pragma unroll
                 for (int b = 0; b < MT; ++b)
                     acc[cb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -420,7 +428,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
                             const float v = __builtin_fmaf(16.0f, acc[cb][b][2 * t], acc[cb][b][2 * t + 1]);
                             const int gic = ok ? gi : 0;
                             const int qsv = qsl[(m < M ? m : 0) * ngw + gic];
-                            const int d = int(4.0f * v) - qsv;
+                            const int d = int(v) - qsv;
                             const double sc = double(half_bits_to_float(*reinterpret_cast<const uint16_t*>(srow + 2 * gic)));
                             const double nv = __builtin_fma(sc, double(d), sacc[cb][b][t]);
                             sacc[cb][b][t] = ok ? nv : sacc[cb][b][t];
@@ -528,6 +536,357 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     if (tid == 0) st_coherent(counters + rb, 0);          // ready for the next call
 }
 
+// ---------------------------------------------------------------- streaming product
+// Tall matrices (no K split, few tokens).  Every workgroup first stages the A
+// operand of the whole K range (digit rows, group sums) and the token scales
+// in LDS, once.  Its waves then work alone: wave i of W streams the 32-row
+// blocks i, i + W, i + 2W, ... window after window, its loads running two
+// windows ahead straight across block boundaries, so no wave drains its
+// pipeline or waits for another.  A block's epilogue adds its pack and group
+// slots through the wave's own weight tile, which is free between the
+// block's last window and the next block's first.
+// LDS: [4 waves][32 rows][stride] tiles | [4 waves][32] fp32 biases |
+// A [K/128][R][128 B] | zeros [8 chunks][R][128 B] | qs [M][K/G] int32 |
+// one zero int32, padding | xs [M] fp32.
+// A tile row: 128 code bytes | the window's scales, padded to 16 mod 128
+// bytes (rows of one 8-row store then start 4 banks apart).
+__host__ __device__ constexpr int w1_stream_stride(int G) {
+    return (kWinB1 + 2 * (kWinK1 / G) - 16 + 127) / 128 * 128 + 16;
+}
+__host__ __device__ inline int w1_stream_a_bytes(int M, int64_t K, int G) {
+    return int((K / 128 + kChunks) * w1_arows(M, G) * 128 + (M * (K / G) + 4) * 4 + 16 * 4);
+}
+__host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G) {
+    return kW1Waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
+}
+
+#ifndef LL_W1_STREAM_WPE
+#define LL_W1_STREAM_WPE 2                                 // waves per SIMD the register budget is cut for
+#endif
+#ifndef LL_W1_STREAM_FUSE
+#define LL_W1_STREAM_FUSE 1                                // G = 128: every workgroup forms the A digits itself
+#endif
+#ifndef LL_W1_STREAM_DEPTH
+#define LL_W1_STREAM_DEPTH 3                               // windows of weights in flight per wave
+#endif
+template <int G, int PK, bool FUSED>
+__global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
+                                                                 const uint16_t* __restrict__ scales, int64_t N,
+                                                                 int64_t K, int M, const void* __restrict__ ws,
+                                                                 const float* __restrict__ xs,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ y, uint16_t* __restrict__ y16) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nl = lane & 15, q = lane >> 4;
+    constexpr int S = G >= 128 ? 1 : 128 / G;
+    const int R = w1_arows(M, G);
+    constexpr int stride = w1_stream_stride(G);
+    constexpr int ngw = kWinK1 / G;
+    const int64_t ng = K / G, nchunk = K / 128;
+    const uint32_t rowbytes = uint32_t(K / 8);
+    const int nwin = int((K + kWinK1 - 1) / kWinK1);
+    char* wtile = lds + wave * kW1RowsPerWave * stride;
+    float* wbias = reinterpret_cast<float*>(lds + kW1Waves * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
+    char* abase = lds + kW1Waves * kW1RowsPerWave * (stride + 4);
+    char* zbase = abase + nchunk * R * 128;                 // a window's worth of zero A rows
+    int32_t* qs_all = reinterpret_cast<int32_t*>(zbase + kChunks * R * 128);
+    float* xs_l = reinterpret_cast<float*>(qs_all + M * ng + 4);
+
+    // The wave's share: 32-row blocks wid, wid + W, ...; T windows in all.
+    // Its first windows are requested before the A operand is staged, so the
+    // two latencies overlap.
+    const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
+    const int64_t W = int64_t(gridDim.x) * kW1Waves;
+    const int64_t wid = int64_t(blockIdx.x) * kW1Waves + __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
+    const int64_t T = (wid < nwb ? (nwb - wid + W - 1) / W : 0) * nwin;
+
+    // Loads are buffer loads whose resource starts at the window's first byte
+    // (row n0, window w) and ends with the array: a lane offset past the end
+    // (rows beyond N, the last row's bytes beyond K) reads zeros, and every
+    // per-window address is scalar.  The lanes' offsets are fixed.
+    const int lr = lane >> 3, lc = lane & 7;               // weight loads: 8 rows x 128 B, lane -> row 8i + lr, bytes 16 lc
+    constexpr int kSc = kW1RowsPerWave * ngw / 64;          // scale loads per lane and window (one fp16 each)
+    static_assert(kW1RowsPerWave * ngw % 64 == 0 && 64 % ngw == 0, "a window's scales fill whole loads");
+    uint32_t woff[4], soff[kSc];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) woff[i] = uint32_t(8 * i + lr) * rowbytes + 16 * lc;
+#pragma unroll
+    for (int u = 0; u < kSc; ++u) {
+        const int e = lane + 64 * u;
+        soff[u] = uint32_t((int64_t(e / ngw) * ng + e % ngw) * 2);
+    }
+    const uint32_t boff = 4 * uint32_t(lane & 31);
+    const uint8_t* bits8 = reinterpret_cast<const uint8_t*>(bits);
+    const uint8_t* sc8 = reinterpret_cast<const uint8_t*>(scales);
+    const int64_t wbytes = N * int64_t(rowbytes), sbytes = N * ng * 2;
+    struct Regs {
+        i32x4 w[4];
+        uint16_t sc[kSc];
+        float b;
+    };
+    // The wave's windows in order: window w of the block starting at row n0.
+    // Loads, stores to the tile and multiplies each walk them with a cursor
+    // of their own; loads past the last window repeat it (never multiplied).
+    int64_t ln0 = wid * kW1RowsPerWave, lt = 0;
+    int lw = 0, sw = 0, cw = 0;
+    int64_t cn0 = wid * kW1RowsPerWave;
+    auto load = [&](Regs& r) {
+        const int64_t n0 = ln0;
+        const int w = lw;
+        if (++lt < T && ++lw == nwin) {
+            lw = 0;
+            ln0 += W * kW1RowsPerWave;
+        }
+        const int64_t w0 = n0 * int64_t(rowbytes) + int64_t(w) * kWinB1;
+        const auto wr = buffer_rsrc(bits8 + w0, wbytes - w0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.w[i] = buffer_ld16_stream(wr, woff[i]);
+        const int64_t s0 = (n0 * ng + int64_t(w) * ngw) * 2;
+        const auto sr = buffer_rsrc(sc8 + s0, sbytes - s0);
+#pragma unroll
+        for (int u = 0; u < kSc; ++u) r.sc[u] = buffer_ld2(sr, soff[u]);
+        const auto br = buffer_rsrc(bias ? bias + n0 : xs, bias ? (N - n0) * 4 : 0);
+        r.b = __builtin_bit_cast(float, buffer_ld4(br, boff));
+    };
+    constexpr int D = G >= 128 ? LL_W1_STREAM_DEPTH : 2;  // (small groups: many scale registers per window)
+    Regs r[D];
+    if (T > 0) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) load(r[i]);
+    }
+
+    // A of the whole K range, once per workgroup
+    const int64_t apieces = nchunk * R * 8;
+    if constexpr (FUSED) {
+        // digit rows formed here from xq [M][K]; the hi-digit pieces of a
+        // (chunk, token) are 8 aligned lanes whose source sums add up to the
+        // group sum (G = 128: chunk = group)
+        const int8_t* xq = static_cast<const int8_t*>(ws);
+        for (int64_t p0 = 0; p0 < apieces; p0 += 64 * kW1Waves) {
+            const int64_t p = p0 + tid;
+            const int64_t pc = p < apieces ? p : apieces - 1;
+            const int64_t c = pc / (8 * R);
+            const int rem = int(pc % (8 * R));
+            const int u = rem & 7, h = (rem >> 3) & 1, m = rem >> 4, qp = 2 * (u & 1) + (u >> 2);
+            const int8_t* src = xq + int64_t(m) * K + 128 * c + 32 * qp;
+            int sum;
+            const i32x4 d = w1_piece(ld16(src), ld16(src + 16), u, h, true, sum);
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            if (p < apieces) {
+                *reinterpret_cast<i32x4*>(abase + 16 * p) = d;
+                if (u == 0 && h == 0) qs_all[int64_t(m) * ng + c] = sum;
+            }
+        }
+    } else {
+        const int8_t* Ag = static_cast<const int8_t*>(ws);
+        const int32_t* qsg = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
+        for (int64_t p = tid; p < apieces; p += 64 * kW1Waves)
+            *reinterpret_cast<i32x4*>(abase + 16 * p) = ld16(Ag + 16 * p);
+        for (int64_t e = tid; e < M * ng; e += 64 * kW1Waves) qs_all[e] = ld32(qsg + e);
+    }
+    for (int e = tid; e < kChunks * R * 8; e += 64 * kW1Waves) *reinterpret_cast<i32x4*>(zbase + 16 * e) = i32x4{0, 0, 0, 0};
+    if (tid == 0) qs_all[M * ng] = 0;                      // the group sum of pairs outside the packed slots
+    if (tid < M) xs_l[tid] = xs[tid];
+    __syncthreads();
+    if (T == 0) return;
+
+    static_assert(kW1RowsPerWave * stride >= 2 * 16 * 8 * 8, "a block's epilogue sums fit the tile");
+    char* wt_lane = wtile + lr * stride + 16 * lc;          // + 8 i stride: this lane's 16 weight bytes of row 8i + lr
+    char* st_lane = wtile + (lane / ngw) * stride + kWinB1 + 2 * (lane % ngw);   // + (64 u / ngw) stride: scale u
+    auto store_w = [&](const Regs& r) {
+        const int w = sw;
+        sw = sw + 1 == nwin ? 0 : sw + 1;
+        if (uint32_t(w + 1) * kWinB1 <= rowbytes) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(wt_lane + 8 * i * stride) = r.w[i];
+        } else {
+            const bool ok = uint32_t(w) * kWinB1 + 16 * lc < rowbytes;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<i32x4*>(wt_lane + 8 * i * stride) = ok ? r.w[i] : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kSc; ++u) *reinterpret_cast<uint16_t*>(st_lane + (64 * u / ngw) * stride) = r.sc[u];
+        if (lane < kW1RowsPerWave) wbias[lane] = r.b;
+    };
+
+    f32x4 acc[2];
+    double sacc[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[cb][0] = sacc[cb][1] = 0.0;
+    }
+    constexpr int cpg = G >= 128 ? G / 128 : 1;             // chunks per unit (a group, or one chunk of S groups)
+    constexpr int kSet = cpg * PK;                          // chunks per packed set
+    constexpr int kSets = (kChunks + kSet - 1) / kSet;
+    constexpr int kGStep = G >= 128 ? PK : PK * S;          // groups per set
+    // Lane row nl of the A operand: PK == 1 row nl; else slot sl = nl / R,
+    // row rl = nl % R (no slot: nl >= PK R).  Lanes without a row of the
+    // chunk read the zero row.
+    const int sl = PK == 1 ? 0 : (nl < PK * R ? nl / R : PK), rl = PK == 1 ? nl : nl % R;
+    const bool has_row = PK == 1 ? nl < R : sl < PK;
+    const char* zrow_q = zbase + rl * 128 + 32 * q;          // + c R 128: zeros for chunk c
+    const char* b_lane = wtile + nl * stride + 4 * q;       // + 16 cb stride + 16 c: word of chunk c
+    // epilogue pairs: lane slot tt holds pair pp = 2 q + tt = (k M + m) S + j
+    int g0[2], qb[2];
+    bool sok[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int pp = 2 * q + tt;
+        const int sp = PK == 1 ? 0 : pp / (M * S);
+        const int p = PK == 1 ? pp : pp % (M * S);
+        const int m = p / S, j = p % S;
+        sok[tt] = PK == 1 || sp < PK;
+        g0[tt] = sok[tt] ? (G >= 128 ? sp : sp * S + j) : 0;   // group within the set
+        qb[tt] = sok[tt] ? (m < M ? m : 0) * int(ng) + g0[tt] : M * int(ng);   // outside: the zero sum
+    }
+    // One window's multiply.  FULL (every chunk of the window inside K): no
+    // exit between chunks, so every LDS read of the window (A rows, weight
+    // words, the epilogues' scales and group sums) is issued ahead of the
+    // chain of matrix products.
+    auto compute = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int w = cw;
+        const char* a_w = abase + (int64_t(w) * kChunks * R + rl) * 128 + 32 * q;   // + c R 128: chunk c
+        const char* a_own = PK == 1 && has_row ? a_w : zrow_q;    // PK = 1: one choice for the window
+        uint32_t wd[kChunks][2];
+        float scv[kSets][2][2];
+        int qsv[kSets][2];
+        bool okv[kSets][2];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) wd[c][cb] = *reinterpret_cast<const uint32_t*>(b_lane + 16 * cb * stride + 16 * c);
+        }
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                int gi = g0[tt] + st * kGStep;                      // group within the window
+                bool ok = sok[tt];
+                if (!FULL) {
+                    ok = ok && int64_t(w) * ngw + gi < ng;
+                    gi = ok ? gi : 0;
+                }
+                okv[st][tt] = ok;
+                qsv[st][tt] = sok[tt] ? qs_all[qb[tt] + int64_t(w) * ngw + (gi - g0[tt])] : 0;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    scv[st][cb][tt] = half_bits_to_float(
+                        *reinterpret_cast<const uint16_t*>(wtile + (16 * cb + nl) * stride + kWinB1 + 2 * gi));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int64_t cg = int64_t(w) * kChunks + c;
+            if (!FULL && cg >= nchunk) break;
+            const bool first = (c % kSet) == 0;
+            // the lane's A row of chunk c, or zeros (the chunk belongs to another slot)
+            const char* ap = (PK == 1 ? a_own : (has_row && sl == (c / cpg) % PK ? a_w : zrow_q)) + c * R * 128;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
+            const i32x8 av{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    av, w1_bv(wd[c][cb]), first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[cb], 0, 4, 0, 127, 0, 127);
+            if ((c % kSet) == kSet - 1 || (!FULL && cg + 1 == nchunk)) {
+                const int st = c / kSet;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const float v = __builtin_fmaf(16.0f, acc[cb][2 * tt], acc[cb][2 * tt + 1]);
+                        const int d = int(v) - qsv[st][tt];
+                        // a pair outside the packed slots has v = 0 and a zero group sum:
+                        // it adds 0; in a cut window a group past K adds 0 * d
+                        const double sc = FULL || okv[st][tt] ? double(scv[st][cb][tt]) : 0.0;
+                        sacc[cb][tt] = __builtin_fma(sc, double(d), sacc[cb][tt]);
+                    }
+                }
+            }
+        }
+    };
+    // y[m][n] = (float)((double)xs[m] * S[m][n]) (+ bias) for the block whose
+    // last window was just multiplied: pair p = (k M + m) S + j (pack slot k)
+    // of lane quarter p / 2, slot p % 2; lane (row col, token parity) adds its
+    // token's pairs
+    auto finish = [&]() {
+        const int64_t n0 = cn0;
+        double* red = reinterpret_cast<double*>(wtile);    // [2 cb][16 nl][8 pairs]
+        const int col = lane & 31;
+        const float bias_v = wbias[col];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                red[(cb * 16 + nl) * 8 + 2 * q + tt] = sacc[cb][tt];
+                sacc[cb][tt] = 0.0;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const int64_t n = n0 + col;
+        for (int m = lane >> 5; m < M; m += 2) {
+            double sum = 0.0;
+            for (int k = 0; k < PK; ++k)
+                for (int j = 0; j < S; ++j) sum += red[col * 8 + (k * M + m) * S + j];
+            if (n < N) {
+                float out = float(double(xs_l[m]) * sum);
+                if (bias) out = __fadd_rn(out, bias_v);
+                if (y16)
+                    y16[int64_t(m) * N + n] = f32_to_bf16_rne(out);
+                else
+                    y[int64_t(m) * N + n] = out;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    // multiply the window in the tile; after a block's last window, its epilogue
+    auto step = [&]() {
+        if (int64_t(cw + 1) * kChunks <= nchunk)
+            compute(std::true_type{});
+        else
+            compute(std::false_type{});
+        if (cw + 1 == nwin) {
+            finish();
+            cw = 0;
+            cn0 += W * kW1RowsPerWave;
+        } else {
+            ++cw;
+        }
+    };
+
+    // Window t is multiplied from the tile while windows t + 1 ... t + D - 1
+    // wait in registers and window t + D is being fetched into the
+    // registers window t came in.
+    store_w(r[0]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    int64_t t = 0;
+    for (; t + D <= T; t += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            load(r[i]);                                    // window t + i + D
+            step();                                        // window t + i
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            store_w(r[(i + 1) % D]);                       // window t + i + 1
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) {                      // the last T - t < D windows, all loaded
+        if (t + i < T) {
+            step();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            store_w(r[(i + 1) % D]);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
+    }
+}
+
 template <int G, int MT, int NP, int PK, bool FUSED = false>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                      const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
@@ -541,6 +900,64 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     hipLaunchKernelGGL((w1_gemv_kernel<G, MT, NP, PK, FUSED>), grid, block, lds, stream, bits, sc, N, K, M, ws, xs, bias,
                        y, nsplit, part, counters, y16);
     return hipGetLastError();
+}
+
+#ifndef LL_W1_STREAM_A_MAX
+#define LL_W1_STREAM_A_MAX (48 * 1024)                     // A bytes up to which the streaming product runs
+#endif
+
+// Workgroups of a kernel resident on the whole device at once (cached per
+// kernel, LDS size and device).
+int resident_wgs(const void* kernel, size_t lds) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static std::mutex mu;
+    static std::vector<std::tuple<const void*, size_t, int, int>> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : seen)
+        if (std::get<0>(e) == kernel && std::get<1>(e) == lds && std::get<2>(e) == dev) return std::get<3>(e);
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 64 * kW1Waves, lds) != hipSuccess) return 0;
+    const int n = cus * per;
+    seen.emplace_back(kernel, lds, dev, n);
+    return n;
+}
+
+bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb);
+
+template <int G, int PK, bool FUSED>
+hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                              const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
+    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED>);
+    const size_t lds = size_t(w1_stream_lds_bytes(M, K, G));
+    hipError_t e = allow_dynamic_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    const int slots = resident_wgs(kern, lds);
+    if (slots <= 0) return hipErrorInvalidConfiguration;
+    // as many blocks for every wave as the fullest one needs: the grid is the
+    // fewest workgroups that still give each wave at most that many
+    const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
+    const int64_t per_wave = (nwb + int64_t(slots) * kW1Waves - 1) / (int64_t(slots) * kW1Waves);
+    const int64_t grid = (nwb + kW1Waves * per_wave - 1) / (kW1Waves * per_wave);
+    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED>), dim3{unsigned(grid)}, dim3{64 * kW1Waves}, lds, stream, bits, sc,
+                       N, K, M, ws, xs, bias, y, y16);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_w1_stream(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                            const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
+    constexpr bool F = G == 128 && LL_W1_STREAM_FUSE;
+    constexpr int kUnits = G >= 128 ? kChunks / (G / 128) : kChunks;
+    constexpr int kMaxPk = G >= 128 ? kUnits : 8 / w1_slots(G);
+    constexpr int P8 = kMaxPk < 8 ? kMaxPk : 8, P4 = kMaxPk < 4 ? kMaxPk : 4;
+    switch (w1_pack(M, G)) {
+    case 8: return launch_w1_stream_k<G, P8, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    case 4: return launch_w1_stream_k<G, P4, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    case 2: return launch_w1_stream_k<G, 2, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    default: return launch_w1_stream_k<G, 1, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    }
 }
 
 // The preparation is fused into the product for G = 128 when every
@@ -598,6 +1015,11 @@ int w1_splits(int64_t N, int64_t K) {
     s = s < kW1MaxSplits ? s : kW1MaxSplits;
     return int(s < 1 ? 1 : s);
 }
+// The streaming product: a matrix tall enough to run unsplit, A rows in one
+// row block, the A operand of the whole K range small enough for LDS.
+bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb) {
+    return w1_splits(N, K) == 1 && w1_arows(int(Mb), G) <= 16 && w1_stream_a_bytes(int(Mb), K, G) <= LL_W1_STREAM_A_MAX;
+}
 // Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64.
 size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G) + 255) / 256 * 256; }
 
@@ -629,12 +1051,25 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
         const int64_t pieces = (K / 128) * R * 8;
         const int64_t pblocks = (pieces + 255) / 256;
         const int64_t items = Mb * (K / G);
-        const bool fused = w1_fused(N, G, Mb);
+        const bool streamed = w1_streamed(N, K, G, Mb);
+        const bool fused = streamed ? G == 128 && LL_W1_STREAM_FUSE : w1_fused(N, G, Mb);
         if (!fused)
             hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned(pblocks + (items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb,
                                K, G, ws, pblocks);
         const void* aop = fused ? static_cast<const void*>(xb) : static_cast<const void*>(ws);
         hipError_t e = hipSuccess;
+        if (streamed) {
+            float* yb = y16 ? nullptr : y + m0 * N;
+            uint16_t* yb16 = y16 ? y16 + m0 * N : nullptr;
+            switch (G) {
+            case 32: e = launch_w1_stream<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
+            case 64: e = launch_w1_stream<64>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
+            case 128: e = launch_w1_stream<128>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
+            default: e = launch_w1_stream<256>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
+            }
+            if (e != hipSuccess) return e;
+            continue;
+        }
         switch (G) {
         case 32:
             e = launch_w1_g<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, y + m0 * N, ns, part, counters, fused,
