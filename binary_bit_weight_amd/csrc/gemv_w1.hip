@@ -137,6 +137,21 @@ __device__ __forceinline__ i32x8 w1_bv(uint32_t word) {
                  int((word >> 1) & 0x44444444u), 0, 0, 0, 0};
 }
 
+// fp8 (A) x fp4 (B) product with the A block scales taken from byte `byte`
+// (a constant after unrolling) of sa; B block scales 1.
+template <int BYTE>
+__device__ __forceinline__ f32x4 w1_mfma_b(const i32x8& a, const i32x8& b, const f32x4& c, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, BYTE, sa, 0, 127);
+}
+__device__ __forceinline__ f32x4 w1_mfma_unit(int byte, const i32x8& a, const i32x8& b, const f32x4& c, int sa) {
+    switch (byte) {
+    case 0: return w1_mfma_b<0>(a, b, c, sa);
+    case 1: return w1_mfma_b<1>(a, b, c, sa);
+    case 2: return w1_mfma_b<2>(a, b, c, sa);
+    default: return w1_mfma_b<3>(a, b, c, sa);
+    }
+}
+
 // ---------------------------------------------------------------- preparation
 // One thread per 16-byte piece of an A row (chunk c, row r, piece u), plus the
 // group sums.  Grid: (ceil(chunks * R * 8 / 256), 1) and a second pass over
@@ -546,15 +561,14 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
 // slots through the wave's own weight tile, which is free between the
 // block's last window and the next block's first.
 // LDS: [4 waves][32 rows][stride] tiles | [4 waves][32] fp32 biases |
-// A [K/128][R][128 B] | zeros [8 chunks][R][128 B] | qs [M][K/G] int32 |
-// one zero int32, padding | xs [M] fp32.
+// A [K/128][R][128 B] | qs [M][K/G] int32 | padding | xs [M] fp32.
 // A tile row: 128 code bytes | the window's scales, padded to 16 mod 128
 // bytes (rows of one 8-row store then start 4 banks apart).
 __host__ __device__ constexpr int w1_stream_stride(int G) {
     return (kWinB1 + 2 * (kWinK1 / G) - 16 + 127) / 128 * 128 + 16;
 }
 __host__ __device__ inline int w1_stream_a_bytes(int M, int64_t K, int G) {
-    return int((K / 128 + kChunks) * w1_arows(M, G) * 128 + (M * (K / G) + 4) * 4 + 16 * 4);
+    return int((K / 128) * w1_arows(M, G) * 128 + (M * (K / G) + 4) * 4 + 16 * 4);
 }
 __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G) {
     return kW1Waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
@@ -589,8 +603,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     char* wtile = lds + wave * kW1RowsPerWave * stride;
     float* wbias = reinterpret_cast<float*>(lds + kW1Waves * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
     char* abase = lds + kW1Waves * kW1RowsPerWave * (stride + 4);
-    char* zbase = abase + nchunk * R * 128;                 // a window's worth of zero A rows
-    int32_t* qs_all = reinterpret_cast<int32_t*>(zbase + kChunks * R * 128);
+    int32_t* qs_all = reinterpret_cast<int32_t*>(abase + nchunk * R * 128);
     float* xs_l = reinterpret_cast<float*>(qs_all + M * ng + 4);
 
     // The wave's share: 32-row blocks wid, wid + W, ...; T windows in all.
@@ -651,34 +664,55 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     };
     constexpr int D = G >= 128 ? LL_W1_STREAM_DEPTH : 2;  // (small groups: many scale registers per window)
     Regs r[D];
+
+    // A of the whole K range, once per workgroup.  FUSED: digit rows formed
+    // here from xq [M][K]; the hi-digit pieces of a (chunk, token) are 8
+    // aligned lanes whose source sums add up to the group sum (G = 128:
+    // chunk = group).  The sources of the first pieces are requested before
+    // the weights, so converting them waits on them alone.
+    const int64_t apieces = nchunk * R * 8;
+    const int8_t* xq = static_cast<const int8_t*>(ws);
+    auto piece_src = [&](int64_t pc) {
+        const int64_t c = pc / (8 * R);
+        const int rem = int(pc % (8 * R));
+        const int u = rem & 7, m = rem >> 4, qp = 2 * (u & 1) + (u >> 2);
+        return xq + int64_t(m) * K + 128 * c + 32 * qp;
+    };
+    auto put_piece = [&](int64_t p, const i32x4& lo4, const i32x4& hi4) {
+        const int64_t pc = p < apieces ? p : apieces - 1;
+        const int64_t c = pc / (8 * R);
+        const int rem = int(pc % (8 * R));
+        const int u = rem & 7, h = (rem >> 3) & 1, m = rem >> 4;
+        int sum;
+        const i32x4 d = w1_piece(lo4, hi4, u, h, true, sum);
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        sum += __shfl_xor(sum, 4, 64);
+        if (p < apieces) {
+            *reinterpret_cast<i32x4*>(abase + 16 * p) = d;
+            if (u == 0 && h == 0) qs_all[int64_t(m) * ng + c] = sum;
+        }
+    };
+    constexpr int kPre = FUSED ? 3 : 0;                    // pieces per thread requested ahead of the weights
+    i32x4 pre[kPre > 0 ? kPre : 1][2];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int64_t p = tid + 64 * kW1Waves * i;
+        const int8_t* src = piece_src(p < apieces ? p : apieces - 1);
+        pre[i][0] = ld16(src);
+        pre[i][1] = ld16(src + 16);
+    }
     if (T > 0) {
 #pragma unroll
         for (int i = 0; i < D; ++i) load(r[i]);
     }
-
-    // A of the whole K range, once per workgroup
-    const int64_t apieces = nchunk * R * 8;
     if constexpr (FUSED) {
-        // digit rows formed here from xq [M][K]; the hi-digit pieces of a
-        // (chunk, token) are 8 aligned lanes whose source sums add up to the
-        // group sum (G = 128: chunk = group)
-        const int8_t* xq = static_cast<const int8_t*>(ws);
-        for (int64_t p0 = 0; p0 < apieces; p0 += 64 * kW1Waves) {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) put_piece(tid + 64 * kW1Waves * i, pre[i][0], pre[i][1]);
+        for (int64_t p0 = 64 * kW1Waves * kPre; p0 < apieces; p0 += 64 * kW1Waves) {
             const int64_t p = p0 + tid;
-            const int64_t pc = p < apieces ? p : apieces - 1;
-            const int64_t c = pc / (8 * R);
-            const int rem = int(pc % (8 * R));
-            const int u = rem & 7, h = (rem >> 3) & 1, m = rem >> 4, qp = 2 * (u & 1) + (u >> 2);
-            const int8_t* src = xq + int64_t(m) * K + 128 * c + 32 * qp;
-            int sum;
-            const i32x4 d = w1_piece(ld16(src), ld16(src + 16), u, h, true, sum);
-            sum += __shfl_xor(sum, 1, 64);
-            sum += __shfl_xor(sum, 2, 64);
-            sum += __shfl_xor(sum, 4, 64);
-            if (p < apieces) {
-                *reinterpret_cast<i32x4*>(abase + 16 * p) = d;
-                if (u == 0 && h == 0) qs_all[int64_t(m) * ng + c] = sum;
-            }
+            const int8_t* src = piece_src(p < apieces ? p : apieces - 1);
+            put_piece(p, ld16(src), ld16(src + 16));
         }
     } else {
         const int8_t* Ag = static_cast<const int8_t*>(ws);
@@ -687,8 +721,6 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
             *reinterpret_cast<i32x4*>(abase + 16 * p) = ld16(Ag + 16 * p);
         for (int64_t e = tid; e < M * ng; e += 64 * kW1Waves) qs_all[e] = ld32(qsg + e);
     }
-    for (int e = tid; e < kChunks * R * 8; e += 64 * kW1Waves) *reinterpret_cast<i32x4*>(zbase + 16 * e) = i32x4{0, 0, 0, 0};
-    if (tid == 0) qs_all[M * ng] = 0;                      // the group sum of pairs outside the packed slots
     if (tid < M) xs_l[tid] = xs[tid];
     __syncthreads();
     if (T == 0) return;
@@ -725,11 +757,22 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     constexpr int kSets = (kChunks + kSet - 1) / kSet;
     constexpr int kGStep = G >= 128 ? PK : PK * S;          // groups per set
     // Lane row nl of the A operand: PK == 1 row nl; else slot sl = nl / R,
-    // row rl = nl % R (no slot: nl >= PK R).  Lanes without a row of the
-    // chunk read the zero row.
+    // row rl = nl % R (no slot: nl >= PK R).  A lane always holds its own
+    // unit's A row.  Unit u of a packed set is multiplied with the A block
+    // scale 1 (E8M0 127) on the rows of slot u and 2^-127 (E8M0 0) on all
+    // others: a row of another slot then adds terms below 2^-121 (|digit| <=
+    // 32, b <= 2) to sums that are integers, below 2^-110 in all, which the
+    // fp32 sums round away (a row summing to 0 stays below 1 and int() gives
+    // 0).  So one A read serves all PK units of a set and no zero rows are
+    // read.
     const int sl = PK == 1 ? 0 : (nl < PK * R ? nl / R : PK), rl = PK == 1 ? nl : nl % R;
     const bool has_row = PK == 1 ? nl < R : sl < PK;
-    const char* zrow_q = zbase + rl * 128 + 32 * q;          // + c R 128: zeros for chunk c
+    const int own_sl = has_row ? sl : 0, own_rl = has_row ? rl : 0;    // rowless lanes read any A row
+    const char* a_lane = abase + (own_sl * cpg * R + own_rl) * 128 + 32 * q;   // + (window chunk of unit 0) R 128
+    uint32_t sa[2] = {0u, 0u};                              // E8M0 block scale of unit u: byte u % 4 of sa[u / 4]
+#pragma unroll
+    for (int u = 0; u < PK; ++u)
+        if (has_row && sl == u) sa[u / 4] |= 127u << (8 * (u % 4));
     const char* b_lane = wtile + nl * stride + 4 * q;       // + 16 cb stride + 16 c: word of chunk c
     // epilogue pairs: lane slot tt holds pair pp = 2 q + tt = (k M + m) S + j
     int g0[2], qb[2];
@@ -751,8 +794,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     auto compute = [&](auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int w = cw;
-        const char* a_w = abase + (int64_t(w) * kChunks * R + rl) * 128 + 32 * q;   // + c R 128: chunk c
-        const char* a_own = PK == 1 && has_row ? a_w : zrow_q;    // PK = 1: one choice for the window
+        const char* a_w = a_lane + int64_t(w) * kChunks * R * 128;
         uint32_t wd[kChunks][2];
         float scv[kSets][2][2];
         int qsv[kSets][2];
@@ -781,31 +823,43 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
             }
         }
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int64_t cg = int64_t(w) * kChunks + c;
-            if (!FULL && cg >= nchunk) break;
-            const bool first = (c % kSet) == 0;
-            // the lane's A row of chunk c, or zeros (the chunk belongs to another slot)
-            const char* ap = (PK == 1 ? a_own : (has_row && sl == (c / cpg) % PK ? a_w : zrow_q)) + c * R * 128;
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
-            const i32x8 av{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int st = 0; st < kSets; ++st) {
+            // the lane's own A rows for this set: chunk st kSet + sl cpg + i
+            i32x8 av[cpg];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av, w1_bv(wd[c][cb]), first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[cb], 0, 4, 0, 127, 0, 127);
-            if ((c % kSet) == kSet - 1 || (!FULL && cg + 1 == nchunk)) {
-                const int st = c / kSet;
+            for (int i = 0; i < cpg; ++i) {
+                const char* ap = a_w + (st * kSet + i) * R * 128;
+                if (!FULL && int64_t(w) * kChunks + st * kSet + own_sl * cpg + i >= nchunk) ap = a_lane;   // past K: any row
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
+                av[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
+            for (int u = 0; u < PK; ++u) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const float v = __builtin_fmaf(16.0f, acc[cb][2 * tt], acc[cb][2 * tt + 1]);
-                        const int d = int(v) - qsv[st][tt];
-                        // a pair outside the packed slots has v = 0 and a zero group sum:
-                        // it adds 0; in a cut window a group past K adds 0 * d
-                        const double sc = FULL || okv[st][tt] ? double(scv[st][cb][tt]) : 0.0;
-                        sacc[cb][tt] = __builtin_fma(sc, double(d), sacc[cb][tt]);
+                for (int i = 0; i < cpg; ++i) {
+                    const int c = st * kSet + u * cpg + i;
+                    if (c >= kChunks) continue;
+                    const int64_t cg = int64_t(w) * kChunks + c;
+                    if (!FULL && cg >= nchunk) continue;
+                    const bool first = u == 0 && i == 0;
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[cb] = w1_mfma_unit(u % 4, av[i], w1_bv(wd[c][cb]), first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[cb],
+                                               int(sa[u / 4]));
+                    if ((c % kSet) == kSet - 1 || (!FULL && cg + 1 == nchunk)) {
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                            for (int tt = 0; tt < 2; ++tt) {
+                                const float v = __builtin_fmaf(16.0f, acc[cb][2 * tt], acc[cb][2 * tt + 1]);
+                                const int d = int(v) - qsv[st][tt];
+                                // a pair outside the packed slots has v below 1 and a zero group
+                                // sum: it adds 0; in a cut window a group past K adds 0 * d
+                                const double sc = FULL || okv[st][tt] ? double(scv[st][cb][tt]) : 0.0;
+                                sacc[cb][tt] = __builtin_fma(sc, double(d), sacc[cb][tt]);
+                            }
+                        }
                     }
                 }
             }
