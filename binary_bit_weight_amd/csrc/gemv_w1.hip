@@ -570,8 +570,8 @@ __host__ __device__ constexpr int w1_stream_stride(int G) {
 __host__ __device__ inline int w1_stream_a_bytes(int M, int64_t K, int G) {
     return int((K / 128) * w1_arows(M, G) * 128 + (M * (K / G) + 4) * 4 + 16 * 4);
 }
-__host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G) {
-    return kW1Waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
+__host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int waves) {
+    return waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
 }
 
 #ifndef LL_W1_STREAM_WPE
@@ -583,8 +583,8 @@ __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G) {
 #ifndef LL_W1_STREAM_DEPTH
 #define LL_W1_STREAM_DEPTH 3                               // windows of weights in flight per wave
 #endif
-template <int G, int PK, bool FUSED>
-__global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
+template <int G, int PK, bool FUSED, int WV>
+__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
                                                                  const float* __restrict__ xs,
@@ -601,8 +601,8 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     const uint32_t rowbytes = uint32_t(K / 8);
     const int nwin = int((K + kWinK1 - 1) / kWinK1);
     char* wtile = lds + wave * kW1RowsPerWave * stride;
-    float* wbias = reinterpret_cast<float*>(lds + kW1Waves * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
-    char* abase = lds + kW1Waves * kW1RowsPerWave * (stride + 4);
+    float* wbias = reinterpret_cast<float*>(lds + WV * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
+    char* abase = lds + WV * kW1RowsPerWave * (stride + 4);
     int32_t* qs_all = reinterpret_cast<int32_t*>(abase + nchunk * R * 128);
     float* xs_l = reinterpret_cast<float*>(qs_all + M * ng + 4);
 
@@ -610,8 +610,8 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     // Its first windows are requested before the A operand is staged, so the
     // two latencies overlap.
     const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
-    const int64_t W = int64_t(gridDim.x) * kW1Waves;
-    const int64_t wid = int64_t(blockIdx.x) * kW1Waves + __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
+    const int64_t W = int64_t(gridDim.x) * WV;
+    const int64_t wid = int64_t(blockIdx.x) * WV + __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
     const int64_t T = (wid < nwb ? (nwb - wid + W - 1) / W : 0) * nwin;
 
     // Loads are buffer loads whose resource starts at the window's first byte
@@ -697,7 +697,7 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     i32x4 pre[kPre > 0 ? kPre : 1][2];
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-        const int64_t p = tid + 64 * kW1Waves * i;
+        const int64_t p = tid + 64 * WV * i;
         const int8_t* src = piece_src(p < apieces ? p : apieces - 1);
         pre[i][0] = ld16(src);
         pre[i][1] = ld16(src + 16);
@@ -708,8 +708,8 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     }
     if constexpr (FUSED) {
 #pragma unroll
-        for (int i = 0; i < kPre; ++i) put_piece(tid + 64 * kW1Waves * i, pre[i][0], pre[i][1]);
-        for (int64_t p0 = 64 * kW1Waves * kPre; p0 < apieces; p0 += 64 * kW1Waves) {
+        for (int i = 0; i < kPre; ++i) put_piece(tid + 64 * WV * i, pre[i][0], pre[i][1]);
+        for (int64_t p0 = 64 * WV * kPre; p0 < apieces; p0 += 64 * WV) {
             const int64_t p = p0 + tid;
             const int8_t* src = piece_src(p < apieces ? p : apieces - 1);
             put_piece(p, ld16(src), ld16(src + 16));
@@ -717,9 +717,9 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
     } else {
         const int8_t* Ag = static_cast<const int8_t*>(ws);
         const int32_t* qsg = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
-        for (int64_t p = tid; p < apieces; p += 64 * kW1Waves)
+        for (int64_t p = tid; p < apieces; p += 64 * WV)
             *reinterpret_cast<i32x4*>(abase + 16 * p) = ld16(Ag + 16 * p);
-        for (int64_t e = tid; e < M * ng; e += 64 * kW1Waves) qs_all[e] = ld32(qsg + e);
+        for (int64_t e = tid; e < M * ng; e += 64 * WV) qs_all[e] = ld32(qsg + e);
     }
     if (tid < M) xs_l[tid] = xs[tid];
     __syncthreads();
@@ -957,12 +957,15 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
 }
 
 #ifndef LL_W1_STREAM_A_MAX
-#define LL_W1_STREAM_A_MAX (48 * 1024)                     // A bytes up to which the streaming product runs
+#define LL_W1_STREAM_A_MAX (48 * 1024)                     // A bytes up to which 4-wave workgroups stream (several per CU)
+#endif
+#ifndef LL_W1_STREAM_A_MAX8
+#define LL_W1_STREAM_A_MAX8 (112 * 1024)                   // ... and 8-wave workgroups (one per CU, sharing the A)
 #endif
 
 // Workgroups of a kernel resident on the whole device at once (cached per
 // kernel, LDS size and device).
-int resident_wgs(const void* kernel, size_t lds) {
+int resident_wgs(const void* kernel, int threads, size_t lds) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     static std::mutex mu;
@@ -972,7 +975,7 @@ int resident_wgs(const void* kernel, size_t lds) {
         if (std::get<0>(e) == kernel && std::get<1>(e) == lds && std::get<2>(e) == dev) return std::get<3>(e);
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 64 * kW1Waves, lds) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, lds) != hipSuccess) return 0;
     const int n = cus * per;
     seen.emplace_back(kernel, lds, dev, n);
     return n;
@@ -980,23 +983,32 @@ int resident_wgs(const void* kernel, size_t lds) {
 
 bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb);
 
-template <int G, int PK, bool FUSED>
-hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
-                              const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED>);
-    const size_t lds = size_t(w1_stream_lds_bytes(M, K, G));
+template <int G, int PK, bool FUSED, int WV>
+hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                               const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
+    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV>);
+    const size_t lds = size_t(w1_stream_lds_bytes(M, K, G, WV));
     hipError_t e = allow_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
-    const int slots = resident_wgs(kern, lds);
+    const int slots = resident_wgs(kern, 64 * WV, lds);
     if (slots <= 0) return hipErrorInvalidConfiguration;
     // as many blocks for every wave as the fullest one needs: the grid is the
     // fewest workgroups that still give each wave at most that many
     const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
-    const int64_t per_wave = (nwb + int64_t(slots) * kW1Waves - 1) / (int64_t(slots) * kW1Waves);
-    const int64_t grid = (nwb + kW1Waves * per_wave - 1) / (kW1Waves * per_wave);
-    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED>), dim3{unsigned(grid)}, dim3{64 * kW1Waves}, lds, stream, bits, sc,
+    const int64_t per_wave = (nwb + int64_t(slots) * WV - 1) / (int64_t(slots) * WV);
+    const int64_t grid = (nwb + WV * per_wave - 1) / (WV * per_wave);
+    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV>), dim3{unsigned(grid)}, dim3{64 * WV}, lds, stream, bits, sc,
                        N, K, M, ws, xs, bias, y, y16);
     return hipGetLastError();
+}
+// Four waves per workgroup (several workgroups per CU) while the A operand
+// is small; eight (one workgroup per CU sharing one copy of A) above that.
+template <int G, int PK, bool FUSED>
+hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                              const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
+    if (w1_stream_a_bytes(M, K, G) <= LL_W1_STREAM_A_MAX)
+        return launch_w1_stream_wv<G, PK, FUSED, 4>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    return launch_w1_stream_wv<G, PK, FUSED, 8>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
 }
 
 template <int G>
@@ -1052,7 +1064,7 @@ hipError_t launch_w1_g(const uint32_t* bits, const uint16_t* sc, int64_t N, int6
 }
 
 // Tokens per pass: the A rows of a pass (2 x tokens x slots) fit two row blocks.
-int64_t w1_tokens_per_pass(int G) { return 16 / w1_slots(G); }
+int64_t w1_tokens_per_pass_max(int G) { return 16 / w1_slots(G); }
 
 #ifndef LL_W1_TARGET_WGS
 #define LL_W1_TARGET_WGS 256
@@ -1072,7 +1084,15 @@ int w1_splits(int64_t N, int64_t K) {
 // The streaming product: a matrix tall enough to run unsplit, A rows in one
 // row block, the A operand of the whole K range small enough for LDS.
 bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb) {
-    return w1_splits(N, K) == 1 && w1_arows(int(Mb), G) <= 16 && w1_stream_a_bytes(int(Mb), K, G) <= LL_W1_STREAM_A_MAX;
+    return w1_splits(N, K) == 1 && w1_arows(int(Mb), G) <= 16 && w1_stream_a_bytes(int(Mb), K, G) <= LL_W1_STREAM_A_MAX8;
+}
+// Tokens per pass: up to two row blocks of A rows; half that when only the
+// half pass can stream (two streamed passes read the weights twice and still
+// beat one pass of the windowed product).
+int64_t w1_tokens_per_pass(int64_t N, int64_t K, int G, int64_t M) {
+    const int64_t tb = w1_tokens_per_pass_max(G);
+    if (M > tb / 2 && !w1_streamed(N, K, G, M < tb ? M : tb) && w1_streamed(N, K, G, tb / 2)) return tb / 2;
+    return tb;
 }
 // Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64.
 size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G) + 255) / 256 * 256; }
@@ -1082,7 +1102,7 @@ size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G
 namespace llk {
 
 size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G) {
-    const int64_t tb = w1_tokens_per_pass(G);
+    const int64_t tb = w1_tokens_per_pass(N, K, G, M);
     const int64_t Mp = M < tb ? M : tb;
     const int ns = w1_splits(N, K);
     if (ns == 1) return w1_ws_bytes(Mp, K, G);
@@ -1093,7 +1113,7 @@ size_t w1_workspace(int64_t M, int64_t N, int64_t K, int G) {
 hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, int G, const int8_t* xq,
                           const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                           hipStream_t stream, uint16_t* y16) {
-    const int64_t tb = w1_tokens_per_pass(G);
+    const int64_t tb = w1_tokens_per_pass(N, K, G, M);
     const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
     const int ns = w1_splits(N, K);
     const int64_t Mp = M < tb ? M : tb;

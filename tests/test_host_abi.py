@@ -267,9 +267,10 @@ def test_w1_device_argument_errors_and_workspace():
     # a wide matrix (1940 row blocks) is not split
     wide = _w(fmt=L.LL_FMT_W1, N=248320, K=5120, group=128)
     assert lib.ll_gemv_workspace_size(C.byref(wide), L.LL_ACT_I8, 1) == CB + base1
-    # G = 32: four group slots per 128-k chunk, passes of 4 tokens
+    # G = 32: four group slots per 128-k chunk; passes of 2 tokens (a 4-token pass has 32 A rows,
+    # more than the streamed product takes, and two streamed passes beat one windowed pass)
     w32 = _w(fmt=L.LL_FMT_W1, N=64, K=512, group=32)
-    assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == CB + 4 * 32 * 128 + 4 * 16 * 4
+    assert lib.ll_gemm_workspace_size(C.byref(w32), 100) == CB + 4 * 16 * 128 + 2 * 16 * 4
     assert _gemv(w, act=L.LL_ACT_I8, M=8, ws=0) == -5
     assert _gemv(w, act=L.LL_ACT_I8, M=8, wsb=16) == -5
     assert _gemv(_w(fmt=L.LL_FMT_W1, K=160, group=32), act=L.LL_ACT_I8) == -2      # K % 128 on the device
