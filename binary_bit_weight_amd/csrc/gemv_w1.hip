@@ -561,14 +561,17 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
 // slots through the wave's own weight tile, which is free between the
 // block's last window and the next block's first.
 // LDS: [4 waves][32 rows][stride] tiles | [4 waves][32] fp32 biases |
-// A [K/128][R][128 B] | qs [M][K/G] int32 | padding | xs [M] fp32.
+// A [K/128][R][kARow] | qs [M][K/G] int32 | padding | xs [M] fp32.  An A row
+// holds 128 bytes padded to 144, so the 16 rows one MFMA operand read
+// touches start 36 banks apart instead of all on the same bank.
+constexpr int kARow = 144;
 // A tile row: 128 code bytes | the window's scales, padded to 16 mod 128
 // bytes (rows of one 8-row store then start 4 banks apart).
 __host__ __device__ constexpr int w1_stream_stride(int G) {
     return (kWinB1 + 2 * (kWinK1 / G) - 16 + 127) / 128 * 128 + 16;
 }
 __host__ __device__ inline int w1_stream_a_bytes(int M, int64_t K, int G) {
-    return int((K / 128) * w1_arows(M, G) * 128 + (M * (K / G) + 4) * 4 + 16 * 4);
+    return int((K / 128) * w1_arows(M, G) * kARow + (M * (K / G) + 4) * 4 + 16 * 4);
 }
 __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int waves) {
     return waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
@@ -603,7 +606,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     char* wtile = lds + wave * kW1RowsPerWave * stride;
     float* wbias = reinterpret_cast<float*>(lds + WV * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
     char* abase = lds + WV * kW1RowsPerWave * (stride + 4);
-    int32_t* qs_all = reinterpret_cast<int32_t*>(abase + nchunk * R * 128);
+    int32_t* qs_all = reinterpret_cast<int32_t*>(abase + nchunk * R * kARow);
     float* xs_l = reinterpret_cast<float*>(qs_all + M * ng + 4);
 
     // The wave's share: 32-row blocks wid, wid + W, ...; T windows in all.
@@ -689,7 +692,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
         sum += __shfl_xor(sum, 2, 64);
         sum += __shfl_xor(sum, 4, 64);
         if (p < apieces) {
-            *reinterpret_cast<i32x4*>(abase + 16 * p) = d;
+            *reinterpret_cast<i32x4*>(abase + (p >> 3) * kARow + 16 * (p & 7)) = d;
             if (u == 0 && h == 0) qs_all[int64_t(m) * ng + c] = sum;
         }
     };
@@ -718,7 +721,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
         const int8_t* Ag = static_cast<const int8_t*>(ws);
         const int32_t* qsg = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
         for (int64_t p = tid; p < apieces; p += 64 * WV)
-            *reinterpret_cast<i32x4*>(abase + 16 * p) = ld16(Ag + 16 * p);
+            *reinterpret_cast<i32x4*>(abase + (p >> 3) * kARow + 16 * (p & 7)) = ld16(Ag + 16 * p);
         for (int64_t e = tid; e < M * ng; e += 64 * WV) qs_all[e] = ld32(qsg + e);
     }
     if (tid < M) xs_l[tid] = xs[tid];
@@ -768,7 +771,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     const int sl = PK == 1 ? 0 : (nl < PK * R ? nl / R : PK), rl = PK == 1 ? nl : nl % R;
     const bool has_row = PK == 1 ? nl < R : sl < PK;
     const int own_sl = has_row ? sl : 0, own_rl = has_row ? rl : 0;    // rowless lanes read any A row
-    const char* a_lane = abase + (own_sl * cpg * R + own_rl) * 128 + 32 * q;   // + (window chunk of unit 0) R 128
+    const char* a_lane = abase + (own_sl * cpg * R + own_rl) * kARow + 32 * q;   // + (window chunk of unit 0) R kARow
     uint32_t sa[2] = {0u, 0u};                              // E8M0 block scale of unit u: byte u % 4 of sa[u / 4]
 #pragma unroll
     for (int u = 0; u < PK; ++u)
@@ -794,7 +797,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     auto compute = [&](auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int w = cw;
-        const char* a_w = a_lane + int64_t(w) * kChunks * R * 128;
+        const char* a_w = a_lane + int64_t(w) * kChunks * R * kARow;
         uint32_t wd[kChunks][2];
         float scv[kSets][2][2];
         int qsv[kSets][2];
@@ -828,7 +831,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
             i32x8 av[cpg];
 #pragma unroll
             for (int i = 0; i < cpg; ++i) {
-                const char* ap = a_w + (st * kSet + i) * R * 128;
+                const char* ap = a_w + (st * kSet + i) * R * kARow;
                 if (!FULL && int64_t(w) * kChunks + st * kSet + own_sl * cpg + i >= nchunk) ap = a_lane;   // past K: any row
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(ap);
                 const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + 16);
