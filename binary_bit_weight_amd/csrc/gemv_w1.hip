@@ -959,11 +959,8 @@ hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_
     return hipGetLastError();
 }
 
-#ifndef LL_W1_STREAM_A_MAX
-#define LL_W1_STREAM_A_MAX (48 * 1024)                     // A bytes up to which 4-wave workgroups stream (several per CU)
-#endif
 #ifndef LL_W1_STREAM_A_MAX8
-#define LL_W1_STREAM_A_MAX8 (112 * 1024)                   // ... and 8-wave workgroups (one per CU, sharing the A)
+#define LL_W1_STREAM_A_MAX8 (112 * 1024)                   // A bytes up to which the streaming product runs
 #endif
 
 // Workgroups of a kernel resident on the whole device at once (cached per
@@ -1004,13 +1001,13 @@ hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t
                        N, K, M, ws, xs, bias, y, y16);
     return hipGetLastError();
 }
-// Four waves per workgroup (several workgroups per CU) while the A operand
-// is small; eight (one workgroup per CU sharing one copy of A) above that.
+// Eight waves per workgroup: one workgroup per CU (the register budget
+// allows two waves per SIMD) sharing one staged copy of A.  Measured against
+// four-wave workgroups (two per CU, each staging its own A) on the LM head
+// 248320 x 5120: M = 1 36.6 -> 36.1 us, M = 2 41.3 -> 38.9, M = 4 53.8 -> 49.2.
 template <int G, int PK, bool FUSED>
 hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                               const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    if (w1_stream_a_bytes(M, K, G) <= LL_W1_STREAM_A_MAX)
-        return launch_w1_stream_wv<G, PK, FUSED, 4>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
     return launch_w1_stream_wv<G, PK, FUSED, 8>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
 }
 
