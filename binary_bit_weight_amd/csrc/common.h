@@ -46,6 +46,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ i32x4 buffer_ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
+__device__ __forceinline__ i32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// 8 bytes into the low half of a 16-byte vector.
+__device__ __forceinline__ i32x4 buffer_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return i32x4{int(v[0]), int(v[1]), 0, 0};
+}
 __device__ __forceinline__ uint16_t buffer_ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }

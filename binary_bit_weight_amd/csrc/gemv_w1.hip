@@ -48,6 +48,7 @@ namespace {
 using namespace llk;
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 constexpr int kW1Waves = 4;
 constexpr int kW1RowsPerWave = 32;
@@ -586,7 +587,10 @@ __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int 
 #ifndef LL_W1_STREAM_DEPTH
 #define LL_W1_STREAM_DEPTH 3                               // windows of weights in flight per wave
 #endif
-template <int G, int PK, bool FUSED, int WV>
+// SCV (G >= 128, K a multiple of 1024): a window's scales of one row are one
+// aligned 16- or 8-byte vector, loaded by lanes 0..31 in one instruction
+// (else one fp16 per lane and load).
+template <int G, int PK, bool FUSED, int WV, bool SCV>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
@@ -632,14 +636,17 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
         const int e = lane + 64 * u;
         soff[u] = uint32_t((int64_t(e / ngw) * ng + e % ngw) * 2);
     }
+    static_assert(!SCV || G >= 128, "row-vector scale loads: at most 8 scales per row and window");
+    const uint32_t svoff = uint32_t(lane) * uint32_t(ng) * 2;   // SCV: row lane's scales of the window
     const uint32_t boff = 4 * uint32_t(lane & 31);
     const uint8_t* bits8 = reinterpret_cast<const uint8_t*>(bits);
     const uint8_t* sc8 = reinterpret_cast<const uint8_t*>(scales);
     const int64_t wbytes = N * int64_t(rowbytes), sbytes = N * ng * 2;
     struct Regs {
         i32x4 w[4];
-        uint16_t sc[kSc];
-        float b;
+        uint16_t sc[SCV ? 1 : kSc];
+        i32x4 s4;                                          // SCV
+        float b;                                           // the block's bias (its first window only)
     };
     // The wave's windows in order: window w of the block starting at row n0.
     // Loads, stores to the tile and multiplies each walk them with a cursor
@@ -660,10 +667,21 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
         for (int i = 0; i < 4; ++i) r.w[i] = buffer_ld16_stream(wr, woff[i]);
         const int64_t s0 = (n0 * ng + int64_t(w) * ngw) * 2;
         const auto sr = buffer_rsrc(sc8 + s0, sbytes - s0);
+        if constexpr (SCV) {
+            if (lane < kW1RowsPerWave) {
+                if constexpr (ngw == 8)
+                    r.s4 = buffer_ld16(sr, svoff);
+                else
+                    r.s4 = buffer_ld8(sr, svoff);
+            }
+        } else {
 #pragma unroll
-        for (int u = 0; u < kSc; ++u) r.sc[u] = buffer_ld2(sr, soff[u]);
-        const auto br = buffer_rsrc(bias ? bias + n0 : xs, bias ? (N - n0) * 4 : 0);
-        r.b = __builtin_bit_cast(float, buffer_ld4(br, boff));
+            for (int u = 0; u < kSc; ++u) r.sc[u] = buffer_ld2(sr, soff[u]);
+        }
+        if (w == 0 && lane < kW1RowsPerWave) {                 // the bias rides with a block's first window
+            const auto br = buffer_rsrc(bias ? bias + n0 : xs, bias ? (N - n0) * 4 : 0);
+            r.b = __builtin_bit_cast(float, buffer_ld4(br, boff));
+        }
     };
     constexpr int D = G >= 128 ? LL_W1_STREAM_DEPTH : 2;  // (small groups: many scale registers per window)
     Regs r[D];
@@ -743,9 +761,18 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<i32x4*>(wt_lane + 8 * i * stride) = ok ? r.w[i] : i32x4{0, 0, 0, 0};
         }
+        if constexpr (SCV) {
+            if (lane < kW1RowsPerWave) {
+                if constexpr (ngw == 8)
+                    *reinterpret_cast<i32x4*>(wtile + lane * stride + kWinB1) = r.s4;
+                else
+                    *reinterpret_cast<i32x2*>(wtile + lane * stride + kWinB1) = i32x2{r.s4[0], r.s4[1]};
+            }
+        } else {
 #pragma unroll
-        for (int u = 0; u < kSc; ++u) *reinterpret_cast<uint16_t*>(st_lane + (64 * u / ngw) * stride) = r.sc[u];
-        if (lane < kW1RowsPerWave) wbias[lane] = r.b;
+            for (int u = 0; u < kSc; ++u) *reinterpret_cast<uint16_t*>(st_lane + (64 * u / ngw) * stride) = r.sc[u];
+        }
+        if (w == 0 && lane < kW1RowsPerWave) wbias[lane] = r.b;
     };
 
     f32x4 acc[2];
@@ -983,10 +1010,10 @@ int resident_wgs(const void* kernel, int threads, size_t lds) {
 
 bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb);
 
-template <int G, int PK, bool FUSED, int WV>
+template <int G, int PK, bool FUSED, int WV, bool SCV>
 hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                                const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV>);
+    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV, SCV>);
     const size_t lds = size_t(w1_stream_lds_bytes(M, K, G, WV));
     hipError_t e = allow_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -997,7 +1024,7 @@ hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t
     const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
     const int64_t per_wave = (nwb + int64_t(slots) * WV - 1) / (int64_t(slots) * WV);
     const int64_t grid = (nwb + WV * per_wave - 1) / (WV * per_wave);
-    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV>), dim3{unsigned(grid)}, dim3{64 * WV}, lds, stream, bits, sc,
+    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV, SCV>), dim3{unsigned(grid)}, dim3{64 * WV}, lds, stream, bits, sc,
                        N, K, M, ws, xs, bias, y, y16);
     return hipGetLastError();
 }
@@ -1008,7 +1035,10 @@ hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t
 template <int G, int PK, bool FUSED>
 hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                               const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    return launch_w1_stream_wv<G, PK, FUSED, 8>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    if constexpr (G >= 128) {
+        if (K % kWinK1 == 0) return launch_w1_stream_wv<G, PK, FUSED, 8, true>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    }
+    return launch_w1_stream_wv<G, PK, FUSED, 8, false>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
 }
 
 template <int G>
