@@ -69,7 +69,10 @@ namespace {
 using namespace llk;
 
 constexpr int BM = 128, BN = 128, LDA = 144;
-constexpr int kThreads = 256;                            // four waves, one per SIMD
+constexpr int kThreads = 256;                            // four waves, one per SIMD (TQ2_0, W1)
+#ifndef LL_GEMM_I2S_WAVES
+#define LL_GEMM_I2S_WAVES 8                              // i2_s: eight waves, two per SIMD
+#endif
 constexpr int kTileInts = BM * BN;                       // one partial tile
 constexpr int kBuf = BM * LDA;                           // one LDS buffer: the activation tile of a group
 constexpr size_t kGemmLds = size_t(2) * kBuf;
@@ -93,7 +96,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).  XSUM (i2_s):
 // the per-token sums of q come in xsum (from the quantization) instead of
 // being summed here.  y16: bf16 output written instead of y, or NULL.
-template <int FMT, bool XSUM = false>
+template <int FMT, bool XSUM = false, int WV = 4>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                              const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
@@ -104,9 +107,17 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     __shared__ int last_flag;
     __shared__ __attribute__((aligned(16))) float xs_tile[BM];   // token scales of the tile's rows
     __shared__ __attribute__((aligned(16))) int32_t qsum_tile[BM];  // i2_s: sum_k q of the tile's rows
+    // WV = 4: one wave per SIMD, wave tiles 64 x 64; WV = 8: two waves per
+    // SIMD (one's vector work runs while the other's matrix products do),
+    // wave tiles 64 x 32
+    constexpr int TH = 64 * WV;                            // threads
+    constexpr int WNW = WV / 2;                            // waves along N
+    constexpr int NB = BN / (32 * WNW);                    // 32-column blocks per wave
+    constexpr int CA = BM * 8 / TH;                        // 16-byte activation chunks per thread and group
+    constexpr int WC = 32 * NB;                            // columns per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;                     // rows 64 wm, columns 64 wn of the tile
+    const int wm = w / WNW, wn = w % WNW;                  // rows 64 wm, columns WC wn of the tile
     const int li = lane & 31, h = lane >> 5;
     const int64_t TM = (M + BM - 1) / BM;
     // Hardware workgroup b runs on XCD b % 8; it takes logical index
@@ -125,53 +136,53 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t nsplit_units = FMT != 2 ? ng : K / 256, per_unit = FMT != 2 ? 1 : 2;
     const int64_t g0 = per_unit * (nsplit_units * split / S), g1 = per_unit * (nsplit_units * (split + 1) / S);
 
-    // Activation loads of one group: four 16-byte chunks per thread, chunk
-    // idx = tid + 256 c is row idx / 8, bytes 16 (idx % 8) of the group;
+    // Activation loads of one group: CA 16-byte chunks per thread, chunk
+    // idx = tid + TH c is row idx / 8, bytes 16 (idx % 8) of the group;
     // rows past M are clamped (their results are not stored).
-    const int8_t* arow[4];
+    const int8_t* arow[CA];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int idx = tid + kThreads * c;
+    for (int c = 0; c < CA; ++c) {
+        const int idx = tid + TH * c;
         int64_t m = m0 + (idx >> 3);
         m = m < M ? m : M - 1;
         arow[c] = xq + m * K + 16 * (idx & 7);
     }
-    // Weight codes of this lane's two columns (wn 64 + nb 32 + li), clamped;
+    // Weight codes of this lane's NB columns (wn WC + nb 32 + li), clamped;
     // i2_s / TQ2_0: bytes 16 h .. 16 h + 15 of the 32-byte group; W1: the
     // group's 16 bytes (both halves of the wave load the same).
-    const uint8_t* bptr[2];
-    const uint16_t* sptr[2];
+    const uint8_t* bptr[NB];
+    const uint16_t* sptr[NB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        int64_t n = n0 + wn * 64 + nb * 32 + li;
+    for (int nb = 0; nb < NB; ++nb) {
+        int64_t n = n0 + wn * WC + nb * 32 + li;
         n = n < N ? n : N - 1;
         bptr[nb] = codes + n * rowbytes + (FMT == 3 ? 0 : 16 * h);
         sptr[nb] = FMT == 2 ? scales + n * (K / 256) : FMT == 3 ? scales + n * (K / 128) : nullptr;
     }
 
     struct Stage {
-        i32x4 a[4];
-        i32x4 b[2];
-        uint16_t sc[FMT == 1 ? 1 : 2];                      // TQ2_0 / W1: the group's block scales
+        i32x4 a[CA];
+        i32x4 b[NB];
+        uint16_t sc[FMT == 1 ? 1 : NB];                     // TQ2_0 / W1: the group's block scales
     };
     auto load = [&](int64_t g, Stage& s) {
         const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
+        for (int c = 0; c < CA; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s.b[nb] = ld16(bptr[nb] + (FMT == 3 ? 16 : 32) * gc);
+        for (int nb = 0; nb < NB; ++nb) s.b[nb] = ld16(bptr[nb] + (FMT == 3 ? 16 : 32) * gc);
         if constexpr (FMT != 1)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) s.sc[nb] = ld2(sptr[nb] + (FMT == 2 ? gc / 2 : gc));
+            for (int nb = 0; nb < NB; ++nb) s.sc[nb] = ld2(sptr[nb] + (FMT == 2 ? gc / 2 : gc));
     };
-    // i2_s: this thread's share of sum_k q of its four rows (idx / 8), summed
+    // i2_s: this thread's share of sum_k q of its CA rows (idx / 8), summed
     // from the chunks it stores (v_dot4 against 1)
-    int32_t qs[4] = {0, 0, 0, 0};
+    int32_t qs[CA] = {};
     auto store_a = [&](int buf, const Stage& s) {
         int8_t* A = lds + buf * kBuf;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int idx = tid + kThreads * c;
+        for (int c = 0; c < CA; ++c) {
+            const int idx = tid + TH * c;
             int8_t* arow_l = &A[(idx >> 3) * LDA];
             if constexpr (FMT == 1 && !XSUM)
 #pragma unroll
@@ -202,9 +213,9 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         for (int mb = 0; mb < 2; ++mb) ao[mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA);
     };
     // weight operands of step t from the lane's code registers
-    auto decode = [&](const i32x4 (&bq)[2], int t, i32x4 (&bo)[2]) {
+    auto decode = [&](const i32x4 (&bq)[NB], int t, i32x4 (&bo)[NB]) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
             if constexpr (FMT == 3) {
                 // bits 16 h .. 16 h + 15 of code dword t: k = 32 t + 16 h + j
                 const uint32_t v = uint32_t(bq[nb][t]) >> (16 * h);
@@ -246,22 +257,22 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     }
     const float sw = FMT == 1 ? *reinterpret_cast<const float*>(codes + N * rowbytes) : 1.0f;
     const float* bsrc = bias ? bias : xs;                 // always a valid address
-    float bnv[2];
+    float bnv[NB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t n = n0 + wn * 64 + nb * 32 + li;
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t n = n0 + wn * WC + nb * 32 + li;
         bnv[nb] = bsrc[bias ? (n < N ? n : N - 1) : 0];
     }
 
     // acc: the exact integer sums (i2_s: of steps 0 and 1, times 16);
     // i2_s also acc4 (step 2, times 4) and acc1 (step 3)
     constexpr int NS = FMT == 1 && LL_GEMM_I2S_SETS == 3 ? 2 : 1;
-    i32x16 acc[2][2], acc4[NS][2], acc1[NS][2];
-    f32x16 facc[FMT == 1 ? 1 : 2][2];                      // TQ2_0 / W1: scaled block sums
+    i32x16 acc[2][NB], acc4[NS][NB], acc1[NS][NB];
+    f32x16 facc[FMT == 1 ? 1 : 2][NB];                     // TQ2_0 / W1: scaled block sums
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 acc[mb][nb][r] = 0;
@@ -275,11 +286,11 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 
     // the four MFMAs of step t; `fresh`: the step starts a new scale block
     // (TQ2_0: first step of an even group; W1: first step of every group)
-    auto mfma = [&](const i32x4 (&ao)[2], const i32x4 (&bo)[2], int t, bool fresh) {
+    auto mfma = [&](const i32x4 (&ao)[2], const i32x4 (&bo)[NB], int t, bool fresh) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 if constexpr (FMT == 1 && LL_GEMM_I2S_SETS == 3) {
                     if (t <= 1)
                         acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[mb], bo[nb], acc[mb][nb], 0, 0, 0);
@@ -293,11 +304,11 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             }
     };
     // TQ2_0 / W1: a finished scale block's exact sums into the fp32 accumulators
-    auto scale_in = [&](const float (&sc)[2]) {
+    auto scale_in = [&](const float (&sc)[NB]) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) facc[mb][nb][r] = __builtin_fmaf(float(acc[mb][nb][r]), sc[nb], facc[mb][nb][r]);
     };
@@ -319,13 +330,13 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     constexpr int U = D % 2 ? 2 * D : D;                // unroll: a multiple of D and of the buffer count
     static_assert(D >= 2, "register depth");
     Stage st[D];
-    i32x4 bq[2], bqn[2], bo[2][2], ac[4][2], an[4][2];
-    float sc[2] = {0.0f, 0.0f}, scn[2] = {0.0f, 0.0f};
+    i32x4 bq[NB], bqn[NB], bo[2][NB], ac[4][2], an[4][2];
+    float sc[NB] = {}, scn[NB] = {};
 #pragma unroll
     for (int i = 0; i < D; ++i) load(g0 + i, st[i]);
     store_a(0, st[0]);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
         bq[nb] = st[0].b[nb];
         bqn[nb] = bq[nb];
         if constexpr (FMT != 1) sc[nb] = half_bits_to_float(st[0].sc[nb]);
@@ -347,14 +358,14 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             const Stage& ns = st[(si + 1) % D];
             store_a(buf ^ 1, ns);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 bqn[nb] = ns.b[nb];
                 if constexpr (FMT != 1) scn[nb] = half_bits_to_float(ns.sc[nb]);
             }
         }
         load(gi + D, st[si]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2 * NB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
@@ -365,7 +376,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         mfma(ac[1], bo[1], 1, false);
         decode(bq, 2, bo[0]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2 * NB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
@@ -379,7 +390,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
             for (int t = 0; t < 4; ++t) read_a(buf ^ 1, t, an[t]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2 * NB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
@@ -389,7 +400,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         mfma(ac[3], bo[1], 3, false);
         if (next) decode(bqn, 0, bo[0]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2 * NB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
@@ -403,7 +414,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             ac[t][1] = an[t][1];
         }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
             bq[nb] = bqn[nb];
             if constexpr (FMT == 2) {
                 if (odd) sc[nb] = scn[nb];
@@ -433,10 +444,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         // row (with XSUM the whole rows' sums, subtracted once in the epilogue)
         if constexpr (!XSUM) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < CA; ++c) {
 #pragma unroll
                 for (int o = 1; o < 8; o <<= 1) qs[c] += __shfl_xor(qs[c], o, kWave);
-                if ((tid & 7) == 0) qsum_tile[(tid >> 3) + 32 * c] = qs[c];
+                if ((tid & 7) == 0) qsum_tile[(tid >> 3) + (TH / 8) * c] = qs[c];
             }
         }
         __syncthreads();
@@ -446,7 +457,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             for (int rq = 0; rq < 4; ++rq) {
                 const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * rq + e;
@@ -458,11 +469,11 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                     }
             }
     }
-    V fin[2][2];
+    V fin[2][NB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
             if constexpr (FMT == 1)
                 fin[mb][nb] = acc[mb][nb];
             else
@@ -477,10 +488,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    st_coherent(mine + ((mb * 2 + nb) * 16 + r) * kThreads + tid, __builtin_bit_cast(int32_t, E(fin[mb][nb][r])));
+                    st_coherent(mine + ((mb * NB + nb) * 16 + r) * TH + tid, __builtin_bit_cast(int32_t, E(fin[mb][nb][r])));
         wait_vmem();
         __syncthreads();
         if (tid == 0) last_flag = arrive_release(counters + tile) == S - 1;
@@ -494,18 +505,18 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            fin[mb][nb][r] += ld_coherent(other + ((mb * 2 + nb) * 16 + r) * kThreads + tid);
+                            fin[mb][nb][r] += ld_coherent(other + ((mb * NB + nb) * 16 + r) * TH + tid);
             }
         } else {
             // fp32 partials added in split order (this split's own from registers)
-            V tot[2][2];
+            V tot[2][NB];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) tot[mb][nb][r] = 0.0f;
             for (int s = 0; s < S; ++s) {
@@ -513,16 +524,16 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             tot[mb][nb][r] += s == split ? fin[mb][nb][r]
-                                                         : __builtin_bit_cast(float, ld_coherent(other + ((mb * 2 + nb) * 16 + r) * kThreads + tid));
+                                                         : __builtin_bit_cast(float, ld_coherent(other + ((mb * NB + nb) * 16 + r) * TH + tid));
             }
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) fin[mb][nb] = tot[mb][nb];
+                for (int nb = 0; nb < NB; ++nb) fin[mb][nb] = tot[mb][nb];
         }
         if (tid == 0) st_coherent(counters + tile, 0);    // ready for the next call
     }
@@ -544,30 +555,30 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             if constexpr (FMT == 1 && XSUM) {
                 const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) fin[mb][nb][4 * rq + e] -= q4[e];
             }
         }
-    float out[2][2][16];
+    float out[2][NB][16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float v = FMT == 1 ? __fmul_rn(__fmul_rn(float(fin[mb][nb][r]), xsv[mb][r]), sw)
                                    : __fmul_rn(float(fin[mb][nb][r]), xsv[mb][r]);
                 out[mb][nb][r] = bias ? __fadd_rn(v, bnv[nb]) : v;
             }
-    const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * 64 + li;
+    const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * WC + li;
     if (y16) {
         uint16_t* yl16 = y16 + lrow * N + lcol;
         if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         yl16[int64_t(mb * 32 + 8 * (r >> 2) + (r & 3)) * N + nb * 32] = f32_to_bf16_rne(out[mb][nb][r]);
@@ -575,7 +586,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
@@ -590,7 +601,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     yl[int64_t(mb * 32 + 8 * (r >> 2) + (r & 3)) * N + nb * 32] = out[mb][nb][r];
@@ -598,7 +609,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
@@ -610,7 +621,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int ml = mb * 32 + 8 * (r >> 2) + (r & 3);
@@ -624,13 +635,13 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 // keep their fp32 block sums as well and are sized for one.
 #define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
 
-template <bool XSUM>
-LL_GEMM_ATTRS(2) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
+template <bool XSUM, int WV>
+__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                  const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                  float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
                                  int32_t* __restrict__ part, int32_t* __restrict__ counters,
                                  const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
-    gemm_i8_body<1, XSUM>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+    gemm_i8_body<1, XSUM, WV>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
 LL_GEMM_ATTRS(1) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N,
@@ -664,9 +675,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K, bool allow = true) {
 }
 
 template <typename Kern, typename... Args>
-hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, hipStream_t stream, Args... args) {
+hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, int threads, hipStream_t stream, Args... args) {
     const int64_t T = tiles * S;
-    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(kThreads)};
+    const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(threads)};
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kernel), kGemmLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kernel, grid, block, kGemmLds, stream, args...);
@@ -689,11 +700,12 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
                               hipStream_t stream, const int32_t* xsum, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    constexpr int WV = LL_GEMM_I2S_WAVES;
     if (xsum)
-        return launch_tiles(gemm_i8_i2s_kernel<true>, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
-                            static_cast<int32_t*>(ws), counters, xsum, y16);
-    return launch_tiles(gemm_i8_i2s_kernel<false>, tiles, S, stream, codes, N, K, xq, xs, M, bias, y, acc_out, S,
-                        static_cast<int32_t*>(ws), counters, xsum, y16);
+        return launch_tiles(gemm_i8_i2s_kernel<true, WV>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
+                            acc_out, S, static_cast<int32_t*>(ws), counters, xsum, y16);
+    return launch_tiles(gemm_i8_i2s_kernel<false, WV>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
+                        acc_out, S, static_cast<int32_t*>(ws), counters, xsum, y16);
 }
 
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
@@ -701,7 +713,7 @@ hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64
                              hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
-    return launch_tiles(gemm_i8_w1_kernel, tiles, S, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
+    return launch_tiles(gemm_i8_w1_kernel, tiles, S, kThreads, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
                         xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
 }
 
@@ -710,7 +722,7 @@ hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int6
                               hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
-    return launch_tiles(gemm_i8_tq2_kernel, tiles, S, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
+    return launch_tiles(gemm_i8_tq2_kernel, tiles, S, kThreads, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
                         static_cast<int32_t*>(ws), counters, y16);
 }
 
