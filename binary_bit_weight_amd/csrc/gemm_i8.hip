@@ -73,6 +73,9 @@ constexpr int kThreads = 256;                            // four waves, one per 
 #ifndef LL_GEMM_I2S_WAVES
 #define LL_GEMM_I2S_WAVES 8                              // i2_s: eight waves, two per SIMD
 #endif
+#ifndef LL_GEMM_BLOCK_WAVES
+#define LL_GEMM_BLOCK_WAVES 8                            // TQ2_0 and W1 (block-scaled sums)
+#endif
 constexpr int kTileInts = BM * BN;                       // one partial tile
 constexpr int kBuf = BM * LDA;                           // one LDS buffer: the activation tile of a group
 constexpr size_t kGemmLds = size_t(2) * kBuf;
@@ -644,18 +647,20 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2,
     gemm_i8_body<1, XSUM, WV>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
-LL_GEMM_ATTRS(1) gemm_i8_w1_kernel(const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N,
-                                int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
-                                const float* __restrict__ bias, float* __restrict__ y, int S,
-                                int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
-    gemm_i8_body<3>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
+template <int WV>
+__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4))) gemm_i8_w1_kernel(
+    const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
+    float* __restrict__ y, int S, int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
+    gemm_i8_body<3, false, WV>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
-LL_GEMM_ATTRS(1) gemm_i8_tq2_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N,
-                                 int64_t K, const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M,
-                                 const float* __restrict__ bias, float* __restrict__ y, int S,
-                                 int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
-    gemm_i8_body<2>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
+template <int WV>
+__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4))) gemm_i8_tq2_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
+    float* __restrict__ y, int S, int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
+    gemm_i8_body<2, false, WV>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
 #ifndef LL_GEMM_SLOTS
@@ -713,7 +718,8 @@ hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64
                              hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
-    return launch_tiles(gemm_i8_w1_kernel, tiles, S, kThreads, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
+    constexpr int WV = LL_GEMM_BLOCK_WAVES;
+    return launch_tiles(gemm_i8_w1_kernel<WV>, tiles, S, 64 * WV, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
                         xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
 }
 
@@ -722,7 +728,8 @@ hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int6
                               hipStream_t stream, uint16_t* y16) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
-    return launch_tiles(gemm_i8_tq2_kernel, tiles, S, kThreads, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
+    constexpr int WV = LL_GEMM_BLOCK_WAVES;
+    return launch_tiles(gemm_i8_tq2_kernel<WV>, tiles, S, 64 * WV, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
                         static_cast<int32_t*>(ws), counters, y16);
 }
 
