@@ -13,10 +13,13 @@ divided by the step time.
 The JSON line also carries the roofline of the dominant kernel (the batched
 product, timed live with HIP events on its stream; its HBM traffic is taken
 from the committed rocprofv3 counter summary when that summary was made from
-the current kernel source), the CPU oracle timed on a bounded sample (one
-layer's seven products, repeated), and extras: single-call per-matrix GEMV
-times, the TQ2_0 small-batch GEMV, the int8 prefill GEMM with i2_s, TQ2_0
-and W1 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
+the current kernel source, and the rate of a read-only streaming kernel as
+the practical bound), the CPU oracle on the whole step (its rows split over
+every host core, and on one core; the median of three runs each), and
+extras: single-call per-matrix GEMV times, the same step with the fused
+epilogues and as dependent per-layer batches, the TQ2_0 small-batch GEMV,
+the W1A8 products of hidden 5120, the int8 prefill GEMM with i2_s, TQ2_0 and
+W1 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
 layer.
 
 The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
@@ -28,13 +31,14 @@ summary when that matches the current source.
 "roofline_w1a8" reports the W1A8 LM head (248320 x 5120, G = 128, M = 1) the
 same way, whole calls over rotating weight copies.
 
-The defaults (500 warm-up steps, about 60 ms, then 200 timed steps) let the
-GPU clocks settle first: after an idle period (the host builds 595 MB of
-synthetic weights before the timing) the step takes about 20 ms of
-continuous work to reach its steady time, and a timed window inside that
-ramp reads up to 10% slow.  The other lines (GEMM, W1A8, extras) run their
-own calls for at least 60 ms before timing (settle()), since some follow
-the CPU oracle leg.
+Warm-up is by time as well as by count: after the W warm-up steps the step
+keeps running until at least 80 ms of continuous work have passed
+(reported as "warmup_settle_ms"), because after an idle period (the host
+builds 595 MB of synthetic weights before the timing) the step takes about
+20 ms to reach its steady time, and a timed window inside that ramp reads up
+to 10% slow.  The other lines (GEMM, W1A8, extras) run their own calls for
+at least 60 ms before timing (settle()), since some follow the CPU oracle
+leg.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
        python bench.py --gemm-only      (the GEMM roofline alone)
@@ -68,7 +72,7 @@ GEMM_SOURCES = ["binary_bit_weight_amd/csrc/gemm_i8.hip", "binary_bit_weight_amd
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_i8_i2s_m512_counters.md")
 GEMM_SHAPES = [(6912, 2560), (2560, 6912)]    # (N, K) at M = 512; the first is the roofline line
 # W1A8 (binary weights, int8 activations): the LM head at hidden 5120, G = 128
-W1_KERNEL = "w1_gemv_kernel"
+W1_KERNEL = "w1_stream_kernel"
 W1_SOURCES = ["binary_bit_weight_amd/csrc/gemv_w1.hip", "binary_bit_weight_amd/csrc/common.h"]
 W1_SUMMARY = os.path.join(ROOT, "profiles", "w1_gemv_lm_head_m1_counters.md")
 W1_HEAD = (248320, 5120, 128)
@@ -399,7 +403,7 @@ def w1_roofline(L, synth, torch, dev, stream, steps):
     kv = summary_values(W1_SUMMARY, W1_SOURCES)
     head = lines[0]
     return {"bound": "hbm", "achieved": head["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["frac"],
-            "workload": head["workload"], "kernel": W1_KERNEL + " (with w1_prep_kernel: one call)",
+            "workload": head["workload"], "kernel": W1_KERNEL + " (the whole call is this one launch)",
             "call_ms": head["call_ms"], "algorithmic_bytes_per_call": head["algorithmic_bytes_per_call"],
             "traffic": int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None,
             "traffic_unit": "HBM bytes per product launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

@@ -199,8 +199,9 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    d_g the exact per-group integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
    [M,N].  workspace: at least ll_gemv_workspace_size(w, act, M) bytes (may
    be NULL when that is 0), under the workspace rules above; with W1 weights
-   a narrow matrix splits K over workgroups, which count their arrivals in
-   the workspace's counter region. */
+   it holds the prepared activation digits of group sizes other than 128,
+   and a narrow matrix splits K over workgroups, which publish partial sums
+   there and count their arrivals in the workspace's counter region. */
 ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs,
                             int64_t M, const float* bias, float* y,
                             void* workspace, size_t workspace_bytes, void* stream);
@@ -310,8 +311,9 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream);
    its fp16 scale into fp32, y = (sum_g s_g * d_g) * xs[m] (+ bias), within
    1e-5 * xs[m] * sum_g |s_g| * sum_{k in g} |q_k| (+1e-6) of the exact
    value and the same for every split of K; other group sizes, and M <= 16,
-   as ll_bitlinear_gemv (bit-exact), in passes of up to 16 tokens that each
-   read the weights once.
+   as ll_bitlinear_gemv (bit-exact), in passes of up to 16 tokens (8 where
+   only a pass of 8 fits the streaming product) that each read the weights
+   once.
    workspace: at least ll_gemm_workspace_size(w, M) bytes (NULL allowed
    when that is 0; (size_t)-1 for invalid arguments), under the workspace
    rules above.  It holds the split-K partial tiles of narrow products (all
