@@ -437,6 +437,17 @@ def extras_single(L, synth, torch, dev, stream):
                         reps, 2 * reps, stream)
         out["i2s_gemv_f32_single_call_" + name] = {"us": round(ms * 1e3, 2),
                                                    "GB_s": round(p.size / (ms * 1e-3) / 1e9, 1)}
+        # the same matrix with int8 activations (ll_bitlinear_gemv, act = LL_ACT_I8): one plane per
+        # token, all tokens in one pass over the weights
+        for M in (1, 8, 16):
+            q = torch.from_numpy(np.clip(np.rint(synth.normal_f32(7 + M, M, K) * 40), -127, 127).astype(np.int8)).to(dev)
+            xs8 = torch.full((M,), 0.025, dtype=torch.float32, device=dev)
+            y8 = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ws8 = torch.zeros((max(L.ll_gemv_workspace_size(Ws[0], L.LL_ACT_I8, M), 16),), dtype=torch.uint8, device=dev)
+            ms = time_graph(torch, lambda i, st: L.ll_bitlinear_gemv(Ws[i], L.LL_ACT_I8, q, xs8, M, None, y8, ws8, st),
+                            reps, 2 * reps, stream)
+            out["i2s_gemv_i8_single_call_%s_M%d" % (name, M)] = {"us": round(ms * 1e3, 2),
+                                                                 "GB_s": round(p.size / (ms * 1e-3) / 1e9, 1)}
     # TQ2_0 small batch, N=6912, K=2560
     N, K = 6912, 2560
     w = synth.ternary(301, N, K)

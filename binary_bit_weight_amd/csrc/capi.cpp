@@ -142,16 +142,9 @@ ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, con
     if (act == LL_ACT_I8) {
         if (!xs) return ll::fail(LL_EINVAL, "ll_bitlinear_gemv: int8 activations need their scales xs");
         if (!aligned(xs, 4)) return ll::fail(LL_EALIGN, "ll_bitlinear_gemv: xs must be 4-byte aligned");
-        if (w->fmt == LL_FMT_I2S)
-            return hip_status(llk::launch_gemm_i8_i2s(static_cast<const uint8_t*>(w->codes), w->N, w->K,
-                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
-                                                      nullptr, s),
-                              fn);
-        if (w->fmt == LL_FMT_TQ2_0)
-            return hip_status(llk::launch_gemm_i8_tq2(static_cast<const uint8_t*>(w->codes),
-                                                      static_cast<const uint16_t*>(w->scales), w->N, w->K,
-                                                      static_cast<const int8_t*>(x), xs, M, bias, y, nullptr, nullptr,
-                                                      s),
+        if (w->fmt == LL_FMT_I2S || w->fmt == LL_FMT_TQ2_0)
+            return hip_status(llk::launch_gemv_i8_planes(w->fmt, w->codes, w->scales, w->N, w->K,
+                                                         static_cast<const int8_t*>(x), xs, M, bias, y, s),
                               fn);
         if (w->fmt == LL_FMT_W1) {
             st = check_w1_device(w, fn);

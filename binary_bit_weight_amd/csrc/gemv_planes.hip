@@ -1,7 +1,9 @@
 // Decode product with fp32 activations, 1 <= M <= 16 (passes of up to three
 // tokens), i2_s or TQ2_0, on the int8 matrix cores with exact integer
 // accumulation.  Single calls and M >= 2; a prepared batch of one token runs
-// on the fp4 digit-plane engine instead.
+// on the fp4 digit-plane engine instead.  The same product serves int8
+// activations (one plane per token, all M <= 16 tokens in one pass, see
+// kInt8 below).
 //
 // Activation split.  Each token row x is written as
 //     x = 2^(E-6) * sum_{p=0..4} q_p * 128^-p  +  r,
@@ -363,22 +365,33 @@ __host__ __device__ constexpr int field_mul(int t) {
 //              double-buffered LDS window (one workgroup barrier per window);
 //   kFused:    the fp32 row x (M == 1), split into planes by the workgroup,
 //              whole row in LDS, no barrier in the main loop.
+//   kInt8:     int8 activations q with per-token scales (1 <= M <= 16): one
+//              plane per token, read straight from the caller's [M][K] rows
+//              and staged per window like kWindowed (TQ2_0 rows reordered
+//              into the plane layout while being stored to LDS); the
+//              per-token sums sum q come from extra MFMAs against an all-ones
+//              operand, so nothing is prepared and there is one launch.
 // (Copying a prepared row whole into LDS instead of windowing it was
 // measured slower in batches: the larger LDS lowers occupancy more than
 // the barriers cost.)
-enum { kWindowed = 0, kFused = 1 };
+enum { kWindowed = 0, kFused = 1, kInt8 = 2 };
 
 // ws: the fp32 token row (kFused); pvw: the prepared operands of these M <= 3
-// tokens (kWindowed).
+// tokens (kWindowed), or pvw.planes = the int8 rows [mrun][K] (kInt8, M the
+// row capacity >= mrun, xs_tok the per-token scales).
 template <int FMT, int M, int MODE>
 __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int64_t N, int64_t K, const void* __restrict__ ws, const PlaneView& pvw,
                                             const float* __restrict__ bias, float* __restrict__ y, int64_t n0,
-                                            char* __restrict__ lds) {
+                                            char* __restrict__ lds, const float* __restrict__ xs_tok = nullptr,
+                                            int mrun = 0) {
     constexpr bool FUSED = MODE == kFused;
+    constexpr bool INT8 = MODE == kInt8;
     constexpr bool WHOLE = FUSED;                      // whole plane row in LDS
     static_assert(!WHOLE || M == 1, "whole-row forms handle one token");
-    constexpr int RR = kP * M;                          // plane rows in use (<= 15)
+    constexpr int RR = (INT8 ? 1 : kP) * M;             // plane rows in use (<= 16)
+    static_assert(RR <= 16, "one 16-row operand");
+    const int rlast = (INT8 ? mrun : RR) - 1;           // last row present in memory
     constexpr int kAChunks = WHOLE ? 1 : (RR * (kWinK / 16) + 64 * kWaves - 1) / (64 * kWaves);   // plane chunks per thread
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
@@ -426,7 +439,9 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     // anyway on a few hot bytes (LL_PLANES_DUMMY=1) gives the compiler exact
     // wait counts, i.e. a full two-window prefetch, but measured slower on
     // the decode step (more requests in flight, no gain in bandwidth).
-    const uint8_t* dummy = (FUSED ? static_cast<const uint8_t*>(ws) : reinterpret_cast<const uint8_t*>(pv.planes)) + 16 * nl;
+    // (kInt8: the first 16 bytes of the int8 rows, the only bytes every shape has)
+    const uint8_t* dummy = INT8 ? reinterpret_cast<const uint8_t*>(pv.planes)
+                                : (FUSED ? static_cast<const uint8_t*>(ws) : reinterpret_cast<const uint8_t*>(pv.planes)) + 16 * nl;
     auto load = [&](int w, Regs& r) {
         const bool live = w < nwin;
 #pragma unroll
@@ -445,9 +460,9 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 const int c = tid + 64 * kWaves * i;
                 const int row = c / kAPerRow, col = c % kAPerRow;
                 const int64_t k = int64_t(w) * kWinK + 16 * col;
-                r.a[i] = ld16(pv.planes + int64_t(row < RR ? row : RR - 1) * K + (k < K ? k : K - 16));
+                r.a[i] = ld16(pv.planes + int64_t(row < rlast ? row : rlast) * K + (k < K ? k : K - 16));
             }
-            if (FMT == 2) r.xs = ld16(pv.xsum + 64 * (live ? w : nwin - 1) + 4 * (tid & 15));
+            if (FMT == 2 && !INT8) r.xs = ld16(pv.xsum + 64 * (live ? w : nwin - 1) + 4 * (tid & 15));
         }
         if (FMT == 2) {
 #pragma unroll
@@ -476,16 +491,33 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
             const int c = tid + 64 * kWaves * i;
             const int row = c / kAPerRow, col = c % kAPerRow;
             const bool ok = int64_t(w) * kWinK + 16 * col < K;
-            if (row < RR)
-                *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + row * kAStride + 16 * col) =
-                    ok ? r.a[i] : i32x4{0, 0, 0, 0};
+            if (row >= RR) continue;
+            const i32x4 v = ok ? r.a[i] : i32x4{0, 0, 0, 0};
+            int8_t* dst = abuf + (w & 1) * abytes + row * kAStride;
+            if (INT8 && FMT == 2) {
+                // elements 16c + 4b + f of 256-k block (c = col % 16) go to the plane
+                // layout's 64f + 4c + b: dword f gathers byte f of the chunk's four dwords
+                const int base = 256 * (col >> 4) + 4 * (col & 15);
+                const uint32_t d0 = uint32_t(v[0]), d1 = uint32_t(v[1]), d2 = uint32_t(v[2]), d3 = uint32_t(v[3]);
+                const uint32_t x01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);   // d0.b0 d1.b0 d0.b1 d1.b1
+                const uint32_t y01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);   // d0.b2 d1.b2 d0.b3 d1.b3
+                const uint32_t x23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+                const uint32_t y23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+                *reinterpret_cast<uint32_t*>(dst + base) = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+                *reinterpret_cast<uint32_t*>(dst + base + 64) = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+                *reinterpret_cast<uint32_t*>(dst + base + 128) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
+                *reinterpret_cast<uint32_t*>(dst + base + 192) = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
+            } else {
+                *reinterpret_cast<i32x4*>(dst + 16 * col) = v;
+            }
         }
-        if (FMT == 2 && tid < 16) *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + RR * kAStride + 16 * tid) = r.xs;
+        if (FMT == 2 && !INT8 && tid < 16) *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + RR * kAStride + 16 * tid) = r.xs;
     };
 
     i32x4 acc[4];                                        // i2_s: one accumulator per field
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = i32x4{0, 0, 0, 0};
+    i32x4 qsum = i32x4{0, 0, 0, 0};                      // kInt8, i2_s: sum q per row so far
     double dacc[4] = {0.0, 0.0, 0.0, 0.0};               // TQ2_0: block-scaled sums per plane row
 
     auto compute = [&](int w) {
@@ -519,6 +551,14 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 for (int j = 0; j < 4; ++j) b[j] = int(field<FMT>(uint32_t(u[j]), t));
                 bacc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, FMT == 2 ? i32x4{0, 0, 0, 0} : acc[t], 0, 0, 0);
             }
+            i32x4 bsum = i32x4{0, 0, 0, 0};               // kInt8: sum q of this segment (TQ2_0) or so far (i2_s)
+            if constexpr (INT8) {
+                const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+                bsum = FMT == 2 ? bsum : qsum;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) bsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], ones, bsum, 0, 0, 0);
+                if (FMT == 1) qsum = bsum;
+            }
             if (FMT == 2) {
                 // C lane (column nl, quarter q) holds plane rows 4q..4q+3
                 const double sc = double(half_bits_to_float(csc[seg]));
@@ -526,6 +566,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q + r;
                     const int xs = row >= RR ? 0
+                                   : INT8  ? bsum[r]
                                    : WHOLE ? fsums[row * nblk + s]
                                            : *reinterpret_cast<const int*>(abuf + (w & 1) * abytes + RR * kAStride +
                                                                            4 * (16 * seg + row));
@@ -574,6 +615,32 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
         if constexpr (!WHOLE) __syncthreads();
     }
 
+    if constexpr (INT8) {
+        // lane (nl, q) holds tokens 4q .. 4q + 3 of column n: i2_s
+        // y = ((float)(sum_t acc_t / mul_t - sum q) * s_tok) * s_w, TQ2_0
+        // y = s_tok * (block-scaled sum), then + bias
+        const int64_t n = n0 + 16 * wave + nl;
+        if (n >= N) return;
+        const float sw = FMT == 1 ? *(const __attribute__((address_space(1))) float*)(codes + N * int64_t(rowbytes)) : 1.0f;
+        const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * q + r;
+            if (m >= mrun) break;
+            const float st = xs_tok[m];
+            float out;
+            if (FMT == 1) {
+                int dot = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dot += acc[t][r] / field_mul<FMT>(t);
+                out = __fmul_rn(__fmul_rn(float(dot - qsum[r]), st), sw);
+            } else {
+                out = float(double(st) * dacc[r]);
+            }
+            y[int64_t(m) * N + n] = bias ? __fadd_rn(out, bn) : out;
+        }
+        return;
+    }
     // per plane row: D_row = (i2_s) sum_t acc_t / mul_t - total plane sum, or
     // (TQ2_0) the block-scaled sum; then y = f * 2^(E-6) * sum_p 128^-p D_(5m+p)
     double d[4];
@@ -676,6 +743,18 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_fused_kernel(const ui
     planes_rows<FMT, 1, kFused>(codes, scales, N, K, x, PlaneView{}, bias, y, int64_t(blockIdx.x) * kRows, lds);
 }
 
+template <int FMT, int MT>
+__global__ void __launch_bounds__(64 * kWaves) gemv_planes_i8_kernel(const uint8_t* __restrict__ codes,
+                                                                      const uint16_t* __restrict__ scales, int64_t N,
+                                                                      int64_t K, const int8_t* __restrict__ xq,
+                                                                      const float* __restrict__ xs, int M,
+                                                                      const float* __restrict__ bias,
+                                                                      float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const PlaneView pv{const_cast<int8_t*>(xq), nullptr, nullptr, nullptr};
+    planes_rows<FMT, MT, kInt8>(codes, scales, N, K, xq, pv, bias, y, int64_t(blockIdx.x) * kRows, lds, xs, M);
+}
+
 struct PlanesProb {          // product of a prepared batch
     const uint8_t* codes;
     const uint16_t* scales;
@@ -749,6 +828,17 @@ hipError_t launch_fused_single(const uint8_t* c, const uint16_t* s, int64_t N, i
     hipError_t e = allow_lds(gemv_planes_fused_kernel<FMT>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_planes_fused_kernel<FMT>), grid, block, lds, stream, c, s, N, K, x, bias, y);
+    return hipGetLastError();
+}
+
+template <int FMT, int MT>
+hipError_t launch_i8(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, const int8_t* xq, const float* xs,
+                     int M, const float* bias, float* y, hipStream_t stream) {
+    const dim3 grid{unsigned((N + kRows - 1) / kRows)}, block{64 * kWaves};
+    const size_t lds = size_t(kWaves * kWTile + 2 * (MT * kAStride + 256));
+    hipError_t e = allow_lds(gemv_planes_i8_kernel<FMT, MT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_planes_i8_kernel<FMT, MT>), grid, block, lds, stream, c, s, N, K, xq, xs, M, bias, y);
     return hipGetLastError();
 }
 
@@ -838,6 +928,26 @@ hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, in
     case 9: return launch_single<2, 1>(c, s, N, K, ws, bias, y, stream);
     case 10: return launch_single<2, 2>(c, s, N, K, ws, bias, y, stream);
     default: return launch_single<2, 3>(c, s, N, K, ws, bias, y, stream);
+    }
+}
+
+hipError_t launch_gemv_i8_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K,
+                                 const int8_t* xq, const float* xs, int64_t M, const float* bias, float* y,
+                                 hipStream_t stream) {
+    const uint8_t* c = static_cast<const uint8_t*>(codes);
+    const uint16_t* s = static_cast<const uint16_t*>(scales);
+    const int m = int(M), mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+    switch (fmt * 32 + mt) {
+    case 33: return launch_i8<1, 1>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 34: return launch_i8<1, 2>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 36: return launch_i8<1, 4>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 40: return launch_i8<1, 8>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 48: return launch_i8<1, 16>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 65: return launch_i8<2, 1>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 66: return launch_i8<2, 2>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 68: return launch_i8<2, 4>(c, s, N, K, xq, xs, m, bias, y, stream);
+    case 72: return launch_i8<2, 8>(c, s, N, K, xq, xs, m, bias, y, stream);
+    default: return launch_i8<2, 16>(c, s, N, K, xq, xs, m, bias, y, stream);
     }
 }
 

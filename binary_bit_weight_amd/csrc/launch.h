@@ -91,6 +91,10 @@ void fill_planes_prob(void* dst, const void* codes, const void* scales, const vo
 void fill_planes_prep(void* dst, const float* x, void* ws, int64_t K);
 hipError_t launch_gemv_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K, const float* x,
                               int64_t M, const float* bias, float* y, void* ws, hipStream_t stream);
+// int8 activations xq [M][K] with per-token scales xs, 1 <= M <= 16, one launch, no workspace
+hipError_t launch_gemv_i8_planes(int fmt, const void* codes, const void* scales, int64_t N, int64_t K,
+                                 const int8_t* xq, const float* xs, int64_t M, const float* bias, float* y,
+                                 hipStream_t stream);
 hipError_t launch_planes_batch_prep(const void* prep_table, int nprep, int fmt, int64_t M, hipStream_t stream);
 // map: int32 [wgs], the product each workgroup runs
 hipError_t launch_planes_batch_product(const void* prob_table, const void* map, int fmt, int64_t M, int64_t wgs,

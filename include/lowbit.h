@@ -194,9 +194,12 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    exact value (x split into five int8 planes per token, exact integer sums,
    fp64 epilogue; up to three tokens per pass over the weights).
    act == LL_ACT_I8: x int8 [M,K], xs fp32 [M] from ll_quantize_act; formats
-   i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32), TQ2_0 (as
-   ll_bitlinear_gemm) and W1 (y = (float)((double)xs[m] * sum_g s_g * d_g),
-   d_g the exact per-group integer dot).  bias: device fp32 [N] added last, or NULL.  y: device fp32
+   i2_s (y = ((float)acc * xs[m]) * scale, acc exact int32, the same bits as
+   ll_bitlinear_gemm), TQ2_0 (y = (float)((double)xs[m] * sum_b s_b * acc_b),
+   acc_b the exact block sums) and W1 (y = (float)((double)xs[m] *
+   sum_g s_g * d_g), d_g the exact per-group integer dot); i2_s and TQ2_0
+   take all M tokens in one pass over the weights and need no workspace.
+   bias: device fp32 [N] added last, or NULL.  y: device fp32
    [M,N].  workspace: at least ll_gemv_workspace_size(w, act, M) bytes (may
    be NULL when that is 0), under the workspace rules above; with W1 weights
    it holds the prepared activation digits of group sizes other than 128,

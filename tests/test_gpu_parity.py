@@ -226,21 +226,6 @@ def test_tq2_gemm_i8_prefill_full(N, K):
     _tq2_i8_case(N, K, 512, 411 if N == 6912 else 412)
 
 
-def test_tq2_gemv_i8_matches_oracle():
-    """int8 activations with TQ2_0 at decode sizes (ll_bitlinear_gemv, M <= 16)
-    take the same kernel without split K."""
-    t = torch()
-    N, K, M = 300, 1024, 5
-    w, sc, blocks = make_tq2(13, N, K)
-    q, s = oracle.quantize_f32(_x(14, M, K))
-    W = L.upload_tq2(blocks, N, K)
-    announce("tq2 gemv i8")
-    y = L.gemv(W, t.from_numpy(q).cuda(), xs=t.from_numpy(s).cuda()).cpu().numpy()
-    y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s)
-    ok, worst = f32_tol_ok(y, y_ref, tsum)
-    assert ok, worst
-
-
 def test_i2s_gemm_i8_workspace_reuse():
     """Two calls sharing one (zero-filled once) workspace: the split-K tile
     counters are left zero by the first call, so the second is exact too."""
@@ -259,17 +244,70 @@ def test_i2s_gemm_i8_workspace_reuse():
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rnd
 
 
-def test_i2s_gemv_i8_matches_gemm():
-    """The int8 decode entry point (M <= 16) gives the same bits as the oracle."""
+# ------------------------------------------------------------------ int8 activations at decode sizes (M <= 16)
+def _gemv_i8_case(fmt, N, K, M, seed, bias=False, sample=None):
+    """ll_bitlinear_gemv with int8 activations: i2_s bit for bit against the
+    oracle (y = ((float)acc * s_tok) * s_w, then + bias), TQ2_0 inside the
+    fp32 bound; every output written (y starts as NaN).  sample: check that
+    many random rows (plus the first and last) instead of all."""
     t = torch()
-    N, K, M = 300, 1024, 4
-    w, scale, packed = make_i2s(9, N, K)
-    q, s = oracle.quantize_f32(_x(10, M, K))
-    W = L.upload_i2s(packed, N, K)
-    announce("i2s gemv i8")
-    y = L.gemv(W, t.from_numpy(q).cuda(), xs=t.from_numpy(s).cuda()).cpu().numpy()
-    y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s)
-    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+    if fmt == "i2s":
+        w, scale, packed = make_i2s(seed, N, K)
+        W = L.upload_i2s(packed, N, K)
+    else:
+        w, sc, blocks = make_tq2(seed, N, K)
+        W = L.upload_tq2(blocks, N, K)
+    q, s = oracle.quantize_bf16(synth.normal_bf16_bits(seed + 3, M, K))
+    b = synth.uniform_f32(seed + 4, N, -1, 1) if bias else None
+    assert L.ll_gemv_workspace_size(W, L.LL_ACT_I8, M) == 0
+    y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+    L.ll_bitlinear_gemv(W, L.LL_ACT_I8, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M,
+                        None if b is None else t.from_numpy(b).cuda(), y, None)
+    y = y.cpu().numpy()
+    rows = None
+    if sample:
+        rng = np.random.default_rng(seed + 5)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, sample, replace=False)])).astype(np.int64)
+        y = y[:, rows]
+    bb = None if b is None else (b if rows is None else b[rows])
+    if fmt == "i2s":
+        y_ref, _ = oracle.i2s_gemm_i8(packed, N, K, q, s, rows, threads=TH)
+        if bb is not None:
+            y_ref = (y_ref + bb[None, :]).astype(np.float32)
+        bad = np.argwhere(y.view(np.uint32) != y_ref.view(np.uint32))
+        assert bad.size == 0, "N=%d K=%d M=%d: %d outputs differ, first %s" % (N, K, M, len(bad), bad[:4].tolist())
+    else:
+        y_ref, tsum = oracle.tq2_gemm_i8(blocks, N, K, q, s, rows, threads=TH)
+        if bb is not None:
+            y_ref = y_ref + bb[None, :].astype(np.float64)
+        ok, worst = f32_tol_ok(y, y_ref, tsum)
+        assert ok, "N=%d K=%d M=%d: worst error / bound %.3f" % (N, K, M, worst)
+
+
+# ragged N (33, 37, 77, 130, 300), ragged last window (K = 384, 1152, 1280, 8448), every row capacity
+# (M = 1, 2, 3..4, 5..8, 9..16), bias
+@pytest.mark.parametrize("N,K,M,bias", [(300, 1024, 4, False), (33, 128, 1, True), (37, 384, 2, False),
+                                        (130, 1152, 3, True), (300, 2560, 7, False), (64, 8448, 16, True),
+                                        (100, 4096, 13, False), (77, 768, 16, False), (16, 256, 9, True)])
+def test_i2s_gemv_i8_small(N, K, M, bias):
+    announce("i2s gemv i8", N, K, M)
+    _gemv_i8_case("i2s", N, K, M, 700 + N + M, bias)
+
+
+@pytest.mark.parametrize("N,K,M,bias", [(300, 1024, 5, False), (33, 256, 1, True), (37, 512, 2, False),
+                                        (130, 1280, 3, True), (300, 2560, 7, False), (64, 8448, 16, True),
+                                        (100, 4096, 11, False), (77, 768, 16, False), (16, 256, 9, True)])
+def test_tq2_gemv_i8_small(N, K, M, bias):
+    announce("tq2 gemv i8", N, K, M)
+    _gemv_i8_case("tq2", N, K, M, 720 + N + M, bias)
+
+
+# the decode shapes at full size, sampled rows
+@pytest.mark.parametrize("fmt", ["i2s", "tq2"])
+@pytest.mark.parametrize("N,K,M", [(2560, 2560, 1), (6912, 2560, 8), (2560, 6912, 16)])
+def test_gemv_i8_decode_shapes(fmt, N, K, M):
+    announce("gemv i8 decode", fmt, N, K, M)
+    _gemv_i8_case(fmt, N, K, M, 740 + N + M, bias=(M == 8), sample=None if N * M <= 2560 else 384)
 
 
 # ------------------------------------------------------------------ prepared batch
