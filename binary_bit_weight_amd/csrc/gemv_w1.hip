@@ -590,13 +590,22 @@ __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int 
 // SCV (G >= 128, K a multiple of 1024): a window's scales of one row are one
 // aligned 16- or 8-byte vector, loaded by lanes 0..31 in one instruction
 // (else one fp16 per lane and load).
-template <int G, int PK, bool FUSED, int WV, bool SCV>
+// KSPLIT (a matrix with fewer 32-row blocks than half the resident waves):
+// each block is one wave's only work, and ks consecutive waves of a
+// workgroup (ks a power of two dividing WV) split its windows, so a wave
+// waits on fewer windows in a row.  Each wave leaves its per-row sums in its
+// own tile; after a workgroup barrier the block's first wave adds the ks
+// shares in order and writes y.  The fp64 sums of s_g d_g terms are exact
+// (see the windowed product), so the split does not change a bit.
+constexpr int kRedBytes = 2 * 16 * 8 * 8;                 // [2 cb][16 rows][8 pairs] fp64 epilogue sums
+template <int G, int PK, bool FUSED, int WV, bool SCV, bool KSPLIT>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
                                                                  const uint16_t* __restrict__ scales, int64_t N,
                                                                  int64_t K, int M, const void* __restrict__ ws,
                                                                  const float* __restrict__ xs,
                                                                  const float* __restrict__ bias,
-                                                                 float* __restrict__ y, uint16_t* __restrict__ y16) {
+                                                                 float* __restrict__ y, uint16_t* __restrict__ y16,
+                                                                 int ks) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
@@ -618,8 +627,13 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     // two latencies overlap.
     const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
     const int64_t W = int64_t(gridDim.x) * WV;
-    const int64_t wid = int64_t(blockIdx.x) * WV + __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
-    const int64_t T = (wid < nwb ? (nwb - wid + W - 1) / W : 0) * nwin;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
+    // KSPLIT: wave wv works on block wv / ks of the workgroup, windows [wlo, whi)
+    const int kss = KSPLIT ? wv % ks : 0;
+    const int64_t wid = KSPLIT ? int64_t(blockIdx.x) * (WV / ks) + wv / ks : int64_t(blockIdx.x) * WV + wv;
+    const int wlo = KSPLIT ? int(int64_t(nwin) * kss / ks) : 0;
+    const int whi = KSPLIT ? int(int64_t(nwin) * (kss + 1) / ks) : nwin;
+    const int64_t T = KSPLIT ? (wid < nwb ? whi - wlo : 0) : (wid < nwb ? (nwb - wid + W - 1) / W : 0) * nwin;
 
     // Loads are buffer loads whose resource starts at the window's first byte
     // (row n0, window w) and ends with the array: a lane offset past the end
@@ -652,7 +666,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     // Loads, stores to the tile and multiplies each walk them with a cursor
     // of their own; loads past the last window repeat it (never multiplied).
     int64_t ln0 = wid * kW1RowsPerWave, lt = 0;
-    int lw = 0, sw = 0, cw = 0;
+    int lw = wlo, sw = wlo, cw = wlo;
     int64_t cn0 = wid * kW1RowsPerWave;
     auto load = [&](Regs& r) {
         const int64_t n0 = ln0;
@@ -744,9 +758,10 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     }
     if (tid < M) xs_l[tid] = xs[tid];
     __syncthreads();
-    if (T == 0) return;
+    if (!KSPLIT && T == 0) return;
 
-    static_assert(kW1RowsPerWave * stride >= 2 * 16 * 8 * 8, "a block's epilogue sums fit the tile");
+    static_assert(kW1RowsPerWave * stride >= kRedBytes + 8 * kW1RowsPerWave * 8,
+                  "a block's epilogue sums and (KSPLIT) its share for up to 8 tokens fit the tile");
     char* wt_lane = wtile + lr * stride + 16 * lc;          // + 8 i stride: this lane's 16 weight bytes of row 8i + lr
     char* st_lane = wtile + (lane / ngw) * stride + kWinB1 + 2 * (lane % ngw);   // + (64 u / ngw) stride: scale u
     auto store_w = [&](const Regs& r) {
@@ -901,7 +916,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     // token's pairs
     auto finish = [&]() {
         const int64_t n0 = cn0;
-        double* red = reinterpret_cast<double*>(wtile);    // [2 cb][16 nl][8 pairs]
+        double* red = reinterpret_cast<double*>(wtile);    // [2 cb][16 nl][8 pairs] (kRedBytes)
         const int col = lane & 31;
         const float bias_v = wbias[col];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -935,7 +950,7 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
             compute(std::true_type{});
         else
             compute(std::false_type{});
-        if (cw + 1 == nwin) {
+        if (!KSPLIT && cw + 1 == nwin) {
             finish();
             cw = 0;
             cn0 += W * kW1RowsPerWave;
@@ -947,26 +962,66 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     // Window t is multiplied from the tile while windows t + 1 ... t + D - 1
     // wait in registers and window t + D is being fetched into the
     // registers window t came in.
-    store_w(r[0]);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    int64_t t = 0;
-    for (; t + D <= T; t += D) {
+    if (T > 0) {
+        store_w(r[0]);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        int64_t t = 0;
+        for (; t + D <= T; t += D) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            load(r[i]);                                    // window t + i + D
-            step();                                        // window t + i
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            store_w(r[(i + 1) % D]);                       // window t + i + 1
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            for (int i = 0; i < D; ++i) {
+                load(r[i]);                                // window t + i + D
+                step();                                    // window t + i
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                store_w(r[(i + 1) % D]);                   // window t + i + 1
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i) {                  // the last T - t < D windows, all loaded
+            if (t + i < T) {
+                step();
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                store_w(r[(i + 1) % D]);
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
         }
     }
+    if constexpr (KSPLIT) {
+        // this wave's share of its block (zero without windows): per row col
+        // and token m, share[m][col] at kRedBytes in its own tile, which no
+        // store of a window touches any more
+        double* red = reinterpret_cast<double*>(wtile);
+        double* share = reinterpret_cast<double*>(wtile + kRedBytes);
+        const int col = lane & 31;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i) {                      // the last T - t < D windows, all loaded
-        if (t + i < T) {
-            step();
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            store_w(r[(i + 1) % D]);
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) red[(cb * 16 + nl) * 8 + 2 * q + tt] = sacc[cb][tt];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (int m = lane >> 5; m < M; m += 2) {
+            double sum = 0.0;
+            for (int k = 0; k < PK; ++k)
+                for (int j = 0; j < S; ++j) sum += red[col * 8 + (k * M + m) * S + j];
+            share[m * kW1RowsPerWave + col] = sum;
+        }
+        __syncthreads();
+        if (kss == 0 && wid < nwb) {
+            const int64_t n = wid * kW1RowsPerWave + col;
+            for (int m = lane >> 5; m < M; m += 2) {
+                double sum = 0.0;
+                for (int k2 = 0; k2 < ks; ++k2)
+                    sum += reinterpret_cast<const double*>(lds + (wv + k2) * kW1RowsPerWave * stride +
+                                                           kRedBytes)[m * kW1RowsPerWave + col];
+                if (n < N) {
+                    float out = float(double(xs_l[m]) * sum);
+                    if (bias) out = __fadd_rn(out, bias[n]);
+                    if (y16)
+                        y16[int64_t(m) * N + n] = f32_to_bf16_rne(out);
+                    else
+                        y[int64_t(m) * N + n] = out;
+                }
+            }
         }
     }
 }
@@ -1010,22 +1065,41 @@ int resident_wgs(const void* kernel, int threads, size_t lds) {
 
 bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb);
 
+#ifndef LL_W1_STREAM_KSPLIT
+#define LL_W1_STREAM_KSPLIT 1                              // split the windows of short matrices over waves
+#endif
 template <int G, int PK, bool FUSED, int WV, bool SCV>
 hipError_t launch_w1_stream_wv(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                                const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV, SCV>);
+    const void* kern = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV, SCV, false>);
     const size_t lds = size_t(w1_stream_lds_bytes(M, K, G, WV));
     hipError_t e = allow_dynamic_lds(kern, lds);
     if (e != hipSuccess) return e;
     const int slots = resident_wgs(kern, 64 * WV, lds);
     if (slots <= 0) return hipErrorInvalidConfiguration;
+    const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
+    const int64_t nwin = (K + kWinK1 - 1) / kWinK1;
+    // KSPLIT: the split with the fewest windows per wave whose workgroups are
+    // all resident at once (the smaller split on a tie)
+    int ks = 1;
+    if (LL_W1_STREAM_KSPLIT && nwb * 2 <= int64_t(slots) * WV)
+        for (int k = 2; k <= WV; k *= 2)
+            if ((nwb + WV / k - 1) / (WV / k) <= slots && (nwin + k - 1) / k < (nwin + ks - 1) / ks) ks = k;
+    if (ks > 1) {
+        const void* kk = reinterpret_cast<const void*>(w1_stream_kernel<G, PK, FUSED, WV, SCV, true>);
+        e = allow_dynamic_lds(kk, lds);
+        if (e != hipSuccess) return e;
+        const int64_t grid = (nwb + WV / ks - 1) / (WV / ks);
+        hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV, SCV, true>), dim3{unsigned(grid)}, dim3{64 * WV}, lds,
+                           stream, bits, sc, N, K, M, ws, xs, bias, y, y16, ks);
+        return hipGetLastError();
+    }
     // as many blocks for every wave as the fullest one needs: the grid is the
     // fewest workgroups that still give each wave at most that many
-    const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
     const int64_t per_wave = (nwb + int64_t(slots) * WV - 1) / (int64_t(slots) * WV);
     const int64_t grid = (nwb + WV * per_wave - 1) / (WV * per_wave);
-    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV, SCV>), dim3{unsigned(grid)}, dim3{64 * WV}, lds, stream, bits, sc,
-                       N, K, M, ws, xs, bias, y, y16);
+    hipLaunchKernelGGL((w1_stream_kernel<G, PK, FUSED, WV, SCV, false>), dim3{unsigned(grid)}, dim3{64 * WV}, lds, stream,
+                       bits, sc, N, K, M, ws, xs, bias, y, y16, 1);
     return hipGetLastError();
 }
 // Eight waves per workgroup: one workgroup per CU (the register budget
@@ -1113,8 +1187,12 @@ int w1_splits(int64_t N, int64_t K) {
 }
 // The streaming product: a matrix tall enough to run unsplit, A rows in one
 // row block, the A operand of the whole K range small enough for LDS.
+#ifndef LL_W1_STREAM_NARROW
+#define LL_W1_STREAM_NARROW 1                              // short matrices stream too (their windows split over waves)
+#endif
 bool w1_streamed(int64_t N, int64_t K, int G, int64_t Mb) {
-    return w1_splits(N, K) == 1 && w1_arows(int(Mb), G) <= 16 && w1_stream_a_bytes(int(Mb), K, G) <= LL_W1_STREAM_A_MAX8;
+    return (LL_W1_STREAM_NARROW || w1_splits(N, K) == 1) && w1_arows(int(Mb), G) <= 16 &&
+           w1_stream_a_bytes(int(Mb), K, G) <= LL_W1_STREAM_A_MAX8;
 }
 // Tokens per pass: up to two row blocks of A rows; half that when only the
 // half pass can stream (two streamed passes read the weights twice and still

@@ -179,14 +179,16 @@ def test_w1a8_unit_scales_integer_result():
     assert np.array_equal(y, exact) and np.array_equal(y_ref, exact)
 
 
-@pytest.mark.parametrize("M", [1, 8])
-def test_w1a8_split_workspace_reuse(M):
-    """A narrow matrix splits K over workgroups (partial sums and per-row-block
-    counters in the workspace): three calls in a row on one zero-filled
-    workspace, with new activations each time, stay bit-exact (the counters
-    are left zero by every call)."""
+@pytest.mark.parametrize("M,K", [(1, 5120), (8, 5120), (8, 8192)])
+def test_w1a8_split_workspace_reuse(M, K):
+    """A narrow matrix splits K: K = 5120 streams, its windows split over the
+    waves of a workgroup; K = 8192 at M = 8 (an A operand too large for the
+    streaming product) splits K over workgroups, with partial sums and
+    per-row-block counters in the workspace.  Three calls in a row on one
+    zero-filled workspace, with new activations each time, stay bit-exact
+    (the counters are left zero by every call)."""
     t = torch()
-    N, K, G = 300, 5120, 128
+    N, G = 300, 128
     bits, scales = make_w1(5800 + M, N, K, G)
     W = L.upload_w1(bits, scales, K, G)
     nws = L.ll_gemv_workspace_size(W, L.LL_ACT_I8, M)
