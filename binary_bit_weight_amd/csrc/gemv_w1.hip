@@ -584,6 +584,14 @@ __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int 
 #ifndef LL_W1_STREAM_FUSE
 #define LL_W1_STREAM_FUSE 1                                // G = 128: every workgroup forms the A digits itself
 #endif
+// ... up to this many tokens.  Every workgroup converts the whole A operand,
+// work that grows with the tokens; above two tokens the preparation launch
+// (A formed once, copied into each workgroup's LDS) costs less.  Measured
+// (us, fused / prepared): 7168 x 5120 at M = 1 7.3 / 8.6, M = 4 11.1 / 10.3,
+// M = 8 15.6 / 11.7; 248320 x 5120 at M = 8 54.1 / 51.0.
+#ifndef LL_W1_STREAM_FUSE_MAXM
+#define LL_W1_STREAM_FUSE_MAXM 2
+#endif
 #ifndef LL_W1_STREAM_DEPTH
 #define LL_W1_STREAM_DEPTH 3                               // windows of weights in flight per wave
 #endif
@@ -1115,10 +1123,9 @@ hipError_t launch_w1_stream_k(const uint32_t* bits, const uint16_t* sc, int64_t 
     return launch_w1_stream_wv<G, PK, FUSED, 8, false>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
 }
 
-template <int G>
-hipError_t launch_w1_stream(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
-                            const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
-    constexpr bool F = G == 128 && LL_W1_STREAM_FUSE;
+template <int G, bool F>
+hipError_t launch_w1_stream_f(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                              const float* xs, const float* bias, float* y, uint16_t* y16, hipStream_t stream) {
     constexpr int kUnits = G >= 128 ? kChunks / (G / 128) : kChunks;
     constexpr int kMaxPk = G >= 128 ? kUnits : 8 / w1_slots(G);
     constexpr int P8 = kMaxPk < 8 ? kMaxPk : 8, P4 = kMaxPk < 4 ? kMaxPk : 4;
@@ -1128,6 +1135,17 @@ hipError_t launch_w1_stream(const uint32_t* bits, const uint16_t* sc, int64_t N,
     case 2: return launch_w1_stream_k<G, 2, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
     default: return launch_w1_stream_k<G, 1, F>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
     }
+}
+// fused: ws is xq [M][K] and each workgroup forms the A digits itself (G =
+// 128 only); else ws holds the prepared operands of w1_prep_kernel.
+template <int G>
+hipError_t launch_w1_stream(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
+                            const float* xs, const float* bias, float* y, uint16_t* y16, bool fused,
+                            hipStream_t stream) {
+    if constexpr (G == 128) {
+        if (fused) return launch_w1_stream_f<G, true>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
+    }
+    return launch_w1_stream_f<G, false>(bits, sc, N, K, M, ws, xs, bias, y, y16, stream);
 }
 
 // The preparation is fused into the product for G = 128 when every
@@ -1234,7 +1252,7 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
         const int64_t pblocks = (pieces + 255) / 256;
         const int64_t items = Mb * (K / G);
         const bool streamed = w1_streamed(N, K, G, Mb);
-        const bool fused = streamed ? G == 128 && LL_W1_STREAM_FUSE : w1_fused(N, G, Mb);
+        const bool fused = streamed ? G == 128 && LL_W1_STREAM_FUSE && Mb <= LL_W1_STREAM_FUSE_MAXM : w1_fused(N, G, Mb);
         if (!fused)
             hipLaunchKernelGGL(w1_prep_kernel, dim3{unsigned(pblocks + (items + 3) / 4)}, dim3{256}, 0, stream, xb, Mb,
                                K, G, ws, pblocks);
@@ -1244,10 +1262,10 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
             float* yb = y16 ? nullptr : y + m0 * N;
             uint16_t* yb16 = y16 ? y16 + m0 * N : nullptr;
             switch (G) {
-            case 32: e = launch_w1_stream<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
-            case 64: e = launch_w1_stream<64>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
-            case 128: e = launch_w1_stream<128>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
-            default: e = launch_w1_stream<256>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, stream); break;
+            case 32: e = launch_w1_stream<32>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, fused, stream); break;
+            case 64: e = launch_w1_stream<64>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, fused, stream); break;
+            case 128: e = launch_w1_stream<128>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, fused, stream); break;
+            default: e = launch_w1_stream<256>(bits, scales, N, K, int(Mb), aop, xs + m0, bias, yb, yb16, fused, stream); break;
             }
             if (e != hipSuccess) return e;
             continue;
