@@ -8,10 +8,15 @@
 // pass (gemv_planes.hip).  An item may carry a
 // fused epilogue: a gated pair (gate and up of one activation, y = relu(g)^2
 // * u, one token) runs as workgroups of 64 rows of both matrices.
+// Batches of W1A8 products (int8 activations, group 128) run on the W1
+// streaming product (gemv_w1.hip): the preparation forms each distinct
+// activation's fp8 digit operand, the product launch runs every matrix.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstring>
+#include <queue>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -149,6 +154,109 @@ std::vector<ll_gemv_item_ex> widen(const ll_gemv_item* items, int32_t count) {
     return ex;
 }
 
+// ---------------------------------------------------------------- W1A8 batches
+struct LayoutI8 {
+    size_t prob_off = 0, prep_off = 0, map_off = 0, frag_off = 0, total = 0;
+    std::vector<int> prep_of;
+    std::vector<const int8_t*> xq;
+    std::vector<int64_t> xk, blk0;
+    std::vector<size_t> frag_at;
+    int64_t tiles = 0, kmax = 0, prep_blocks = 0;    // tiles: the most workgroups any assignment uses
+    bool scv = true;                   // every K a multiple of 1024
+};
+
+// Workgroups per product: start from one each and give the next one to the
+// product whose waves have the longest stream of windows (a wave's blocks x
+// windows per block), while the total stays within the resident workgroups
+// and each product has at most one block per wave.  slots <= 0 (unknown):
+// one block per wave everywhere.
+std::vector<int64_t> assign_w1_wgs(const ll_gemv_item_i8* items, int32_t count, int64_t slots) {
+    std::vector<int64_t> wgs(size_t(count), 1);
+    if (slots <= 0) {
+        for (int i = 0; i < count; ++i) wgs[size_t(i)] = llk::w1_batch_wgs(items[i].w.N);
+        return wgs;
+    }
+    auto windows = [&](int i) {
+        const int64_t per_wave = (llk::w1_batch_blocks(items[i].w.N) + 8 * wgs[size_t(i)] - 1) / (8 * wgs[size_t(i)]);
+        return per_wave * ((items[i].w.K + 1023) / 1024);
+    };
+    std::priority_queue<std::pair<int64_t, int>> heap;
+    for (int i = 0; i < count; ++i) heap.push({windows(i), i});
+    int64_t total = count;
+    while (total < slots && !heap.empty()) {
+        const int i = heap.top().second;
+        heap.pop();
+        if (wgs[size_t(i)] >= llk::w1_batch_wgs(items[i].w.N)) continue;    // one block per wave already
+        ++wgs[size_t(i)];
+        ++total;
+        heap.push({windows(i), i});
+    }
+    return wgs;
+}
+
+ll_status check_item_i8(const ll_gemv_item_i8& it, int i, int64_t M) {
+    const ll_weights& w = it.w;
+    if (w.fmt != LL_FMT_W1) return ll::failf(LL_EINVAL, "ll_gemv_plan_i8: item %d: int8 activations need format W1", i);
+    if (w.N <= 0 || w.K <= 0) return ll::failf(LL_EINVAL, "ll_gemv_plan_i8: item %d: N and K must be positive", i);
+    if (w.N > (int64_t(1) << 31) - 1 || w.K > (int64_t(1) << 24))
+        return ll::failf(LL_ERANGE, "ll_gemv_plan_i8: item %d: N must be < 2^31 and K <= 2^24", i);
+    if (w.group != 128 || w.K % 128)
+        return ll::failf(LL_ESHAPE, "ll_gemv_plan_i8: item %d: group 128 and K %% 128 == 0 required", i);
+    if (!w.codes || !w.scales || !it.xq || !it.xs || !it.y)
+        return ll::failf(LL_EINVAL, "ll_gemv_plan_i8: item %d: NULL codes, scales, xq, xs or y", i);
+    if (!aligned(w.codes, 16) || !aligned(w.scales, 2))
+        return ll::failf(LL_EALIGN, "ll_gemv_plan_i8: item %d: codes must be 16-byte, scales 2-byte aligned", i);
+    if (!aligned(it.xq, 16) || !aligned(it.xs, 4) || !aligned(it.y, 4) || (it.bias && !aligned(it.bias, 4)))
+        return ll::failf(LL_EALIGN, "ll_gemv_plan_i8: item %d: xq must be 16-byte, xs / y / bias 4-byte aligned", i);
+    if (!llk::w1_batch_fits(M, w.K))
+        return ll::failf(LL_ERANGE, "ll_gemv_plan_i8: item %d: the operand of %lld tokens x K = %lld is too large", i,
+                         static_cast<long long>(M), static_cast<long long>(w.K));
+    return LL_OK;
+}
+
+ll_status plan_layout_i8(const ll_gemv_item_i8* items, int32_t count, int64_t M, LayoutI8& L) {
+    if (!items || count <= 0) return ll::fail(LL_EINVAL, "ll_gemv_plan_i8: no items");
+    if (M < 1 || M > 8) return ll::fail(LL_ESHAPE, "ll_gemv_plan_i8: M must be in [1, 8]");
+    for (int i = 0; i < count; ++i) {
+        ll_status st = check_item_i8(items[i], i, M);
+        if (st) return st;
+    }
+    L.prep_of.assign(size_t(count), -1);
+    for (int i = 0; i < count; ++i) {
+        const int64_t K = items[i].w.K;
+        L.kmax = std::max(L.kmax, K);
+        L.scv = L.scv && K % 1024 == 0;
+        int found = -1;
+        for (size_t j = 0; j < L.xq.size(); ++j)
+            if (L.xq[j] == items[i].xq && L.xk[j] == K) {
+                found = int(j);
+                break;
+            }
+        if (found < 0) {
+            found = int(L.xq.size());
+            L.xq.push_back(items[i].xq);
+            L.xk.push_back(K);
+            L.blk0.push_back(L.prep_blocks);
+            L.prep_blocks += llk::w1_batch_prep_blocks(M, K);
+        }
+        L.prep_of[size_t(i)] = found;
+        L.tiles += llk::w1_batch_wgs(items[i].w.N);
+    }
+    L.prob_off = 0;
+    L.prep_off = round_up(size_t(count) * llk::w1_batch_prob_bytes(), 256);
+    L.map_off = round_up(L.prep_off + L.xq.size() * llk::w1_batch_prep_bytes(), 256);
+    L.frag_off = round_up(L.map_off + size_t(L.tiles) * 4, 256);
+    size_t at = L.frag_off;
+    for (size_t j = 0; j < L.xq.size(); ++j) {
+        L.frag_at.push_back(at);
+        at = round_up(at + llk::w1_batch_operand_bytes(M, L.xk[j]), 256);
+    }
+    L.total = at;
+    if (L.tiles > (int64_t(1) << 31) - 1 || L.prep_blocks > (int64_t(1) << 31) - 1 || L.xq.size() > 65535)
+        return ll::fail(LL_ERANGE, "ll_gemv_plan_i8: batch too large");
+    return LL_OK;
+}
+
 ll_status check_plan(const ll_gemv_plan* p) {
     if (!p || !p->mem || !p->prob_table || !p->prep_table || !p->map_table || p->count <= 0 || p->nprep <= 0)
         return ll::fail(LL_EINVAL, "ll_gemv_plan: plan not initialised");
@@ -245,10 +353,66 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
     return ll_gemv_plan_init_ex(ex.data(), count, act, M, mem, bytes, plan);
 }
 
+size_t ll_gemv_plan_bytes_i8(const ll_gemv_item_i8* items, int32_t count, int64_t M) {
+    LayoutI8 L;
+    if (plan_layout_i8(items, count, M, L)) return size_t(-1);
+    return L.total;
+}
+
+ll_status ll_gemv_plan_init_i8(const ll_gemv_item_i8* items, int32_t count, int64_t M, void* mem, size_t bytes,
+                               ll_gemv_plan* plan) {
+    if (!plan) return ll::fail(LL_EINVAL, "ll_gemv_plan_init_i8: plan is NULL");
+    LayoutI8 L;
+    ll_status st = plan_layout_i8(items, count, M, L);
+    if (st) return st;
+    if (!mem || bytes < L.total)
+        return ll::failf(LL_EWORKSPACE, "ll_gemv_plan_init_i8: %zu device bytes required", L.total);
+    if (!aligned(mem, 16)) return ll::fail(LL_EALIGN, "ll_gemv_plan_init_i8: mem must be 16-byte aligned");
+    char* base = static_cast<char*>(mem);
+    std::vector<char> host(L.frag_off, 0);
+    int32_t* map = reinterpret_cast<int32_t*>(host.data() + L.map_off);
+    const std::vector<int64_t> wgs = assign_w1_wgs(items, count, llk::w1_batch_slots(M, L.kmax, L.scv));
+    int64_t first = 0;
+    for (int i = 0; i < count; ++i) {
+        const ll_gemv_item_i8& it = items[i];
+        const char* ops = base + L.frag_at[size_t(L.prep_of[size_t(i)])];
+        llk::fill_w1_prob(host.data() + L.prob_off + size_t(i) * llk::w1_batch_prob_bytes(), it.w.codes, it.w.scales,
+                          ops, it.xs, it.bias, it.y, it.w.N, it.w.K, first, wgs[size_t(i)]);
+        for (int64_t g = 0; g < wgs[size_t(i)]; ++g) map[first + g] = i;
+        first += wgs[size_t(i)];
+    }
+    for (size_t j = 0; j < L.xq.size(); ++j)
+        llk::fill_w1_prep(host.data() + L.prep_off + j * llk::w1_batch_prep_bytes(), L.xq[j], base + L.frag_at[j], M,
+                          L.xk[j], L.blk0[j]);
+    st = hip_status(hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice), "ll_gemv_plan_init_i8");
+    if (st) return st;
+    ll_gemv_plan p;
+    std::memset(&p, 0, sizeof p);
+    p.mem = mem;
+    p.bytes = L.total;
+    p.count = count;
+    p.nprep = int32_t(L.xq.size());
+    p.act = LL_ACT_I8;
+    p.fmt = LL_FMT_W1;
+    p.M = M;
+    p.tiles = first;                                    // workgroups of the product launch
+    p.prep_entries = L.prep_blocks;                     // preparation blocks
+    p.kmax = L.kmax;
+    p.prob_table = base + L.prob_off;
+    p.prep_table = base + L.prep_off;
+    p.map_table = base + L.map_off;
+    p.flags = L.scv ? 1 : 0;
+    *plan = p;
+    return LL_OK;
+}
+
 ll_status ll_gemv_plan_prepare(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->act == LL_ACT_I8)
+        return hip_status(llk::launch_w1_batch_prep(plan->prep_table, plan->nprep, plan->prep_entries, plan->M, s),
+                          "ll_gemv_plan_prepare");
     if (llk::f4_engine(plan->M, plan->kmax))
         return hip_status(llk::launch_f4_batch_prep(plan->prep_table, int(plan->prep_entries), plan->fmt, plan->kmax,
                                                     s),
@@ -261,6 +425,10 @@ ll_status ll_gemv_plan_product(const ll_gemv_plan* plan, void* stream) {
     ll_status st = check_plan(plan);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (plan->act == LL_ACT_I8)
+        return hip_status(llk::launch_w1_batch_product(plan->prob_table, plan->map_table, plan->tiles, plan->M,
+                                                       plan->kmax, (plan->flags & 1) != 0, s),
+                          "ll_gemv_plan_product");
     if (llk::f4_engine(plan->M, plan->kmax))
         return hip_status(llk::launch_f4_batch_product(plan->prob_table, plan->map_table, plan->fmt, plan->tiles,
                                                        plan->kmax, plan->epilogues != 0, plan->M, s),

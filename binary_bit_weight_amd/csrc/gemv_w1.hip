@@ -160,15 +160,17 @@ __device__ __forceinline__ f32x4 w1_mfma_unit(int byte, const i32x8& a, const i3
 __device__ void w1_qsum(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G, void* __restrict__ ws,
                         int64_t block);
 
-__global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
-                                                      void* __restrict__ ws, int64_t prep_blocks) {
-    if (int64_t(blockIdx.x) >= prep_blocks) {              // the group sums, in the same launch
-        w1_qsum(xq, M, K, G, ws, int64_t(blockIdx.x) - prep_blocks);
+// Block `block` of the preparation of one activation (prep_blocks piece
+// blocks, then the group-sum blocks).
+__device__ __forceinline__ void w1_prep_body(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
+                                             void* __restrict__ ws, int64_t prep_blocks, int64_t block) {
+    if (block >= prep_blocks) {                            // the group sums, in the same launch
+        w1_qsum(xq, M, K, G, ws, block - prep_blocks);
         return;
     }
     const int S = w1_slots(G), R = w1_arows(int(M), G);
     const int64_t pieces = (K / 128) * R * 8;
-    const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t id = block * 256 + threadIdx.x;
     int8_t* A = static_cast<int8_t*>(ws);
     if (id < pieces) {
         const int u = int(id % 8);
@@ -183,6 +185,11 @@ __global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__
         int sum;
         st16(A + (c * R + r) * 128 + 16 * u, w1_piece(lo4, hi4, u, h, in_slot, sum));
     }
+}
+
+__global__ void __launch_bounds__(256) w1_prep_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K, int G,
+                                                      void* __restrict__ ws, int64_t prep_blocks) {
+    w1_prep_body(xq, M, K, G, ws, prep_blocks, blockIdx.x);
 }
 
 // Group sums qs[m][g] = sum_{k in g} q: one wave per (token, group).
@@ -606,15 +613,14 @@ __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int 
 // shares in order and writes y.  The fp64 sums of s_g d_g terms are exact
 // (see the windowed product), so the split does not change a bit.
 constexpr int kRedBytes = 2 * 16 * 8 * 8;                 // [2 cb][16 rows][8 pairs] fp64 epilogue sums
+// The product of workgroup wg of nwg working on one matrix (lds: the
+// workgroup's dynamic LDS).
 template <int G, int PK, bool FUSED, int WV, bool SCV, bool KSPLIT>
-__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
-                                                                 const uint16_t* __restrict__ scales, int64_t N,
-                                                                 int64_t K, int M, const void* __restrict__ ws,
-                                                                 const float* __restrict__ xs,
-                                                                 const float* __restrict__ bias,
-                                                                 float* __restrict__ y, uint16_t* __restrict__ y16,
-                                                                 int ks) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits, const uint16_t* __restrict__ scales,
+                                               int64_t N, int64_t K, int M, const void* __restrict__ ws,
+                                               const float* __restrict__ xs, const float* __restrict__ bias,
+                                               float* __restrict__ y, uint16_t* __restrict__ y16, int ks, int64_t wg,
+                                               int64_t nwg, char* __restrict__ lds) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nl = lane & 15, q = lane >> 4;
     constexpr int S = G >= 128 ? 1 : 128 / G;
@@ -634,11 +640,11 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     // Its first windows are requested before the A operand is staged, so the
     // two latencies overlap.
     const int64_t nwb = (N + kW1RowsPerWave - 1) / kW1RowsPerWave;
-    const int64_t W = int64_t(gridDim.x) * WV;
+    const int64_t W = nwg * WV;
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar cursors
     // KSPLIT: wave wv works on block wv / ks of the workgroup, windows [wlo, whi)
     const int kss = KSPLIT ? wv % ks : 0;
-    const int64_t wid = KSPLIT ? int64_t(blockIdx.x) * (WV / ks) + wv / ks : int64_t(blockIdx.x) * WV + wv;
+    const int64_t wid = KSPLIT ? wg * (WV / ks) + wv / ks : wg * WV + wv;
     const int wlo = KSPLIT ? int(int64_t(nwin) * kss / ks) : 0;
     const int whi = KSPLIT ? int(int64_t(nwin) * (kss + 1) / ks) : nwin;
     const int64_t T = KSPLIT ? (wid < nwb ? whi - wlo : 0) : (wid < nwb ? (nwb - wid + W - 1) / W : 0) * nwin;
@@ -1034,6 +1040,19 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL
     }
 }
 
+template <int G, int PK, bool FUSED, int WV, bool SCV, bool KSPLIT>
+__global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE))) w1_stream_kernel(const uint32_t* __restrict__ bits,
+                                                                 const uint16_t* __restrict__ scales, int64_t N,
+                                                                 int64_t K, int M, const void* __restrict__ ws,
+                                                                 const float* __restrict__ xs,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ y, uint16_t* __restrict__ y16,
+                                                                 int ks) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    w1_stream_body<G, PK, FUSED, WV, SCV, KSPLIT>(bits, scales, N, K, M, ws, xs, bias, y, y16, ks, blockIdx.x, gridDim.x,
+                                                  lds);
+}
+
 template <int G, int MT, int NP, int PK, bool FUSED = false>
 hipError_t launch_w1(const uint32_t* bits, const uint16_t* sc, int64_t N, int64_t K, int M, const void* ws,
                      const float* xs, const float* bias, float* y, int nsplit, double* part, int32_t* counters,
@@ -1223,6 +1242,74 @@ int64_t w1_tokens_per_pass(int64_t N, int64_t K, int G, int64_t M) {
 // Split-K scratch after the pass operands: partial sums [rbs x nsplit x 128 rows x tokens] fp64.
 size_t w1_split_off(int64_t Mp, int64_t K, int G) { return (w1_ws_bytes(Mp, K, G) + 255) / 256 * 256; }
 
+// ---------------------------------------------------------------- prepared batches
+// Many W1 products (G = 128, 1 <= M <= 8, the A operand of each within the
+// streaming product's LDS) in two launches.  The first forms the operands of
+// every distinct activation into the plan memory (the layout of
+// w1_prep_kernel); the second runs every product's streaming product from
+// them, the workgroups of all products in one grid (a table maps each
+// workgroup to its product).  The host gives each product a number of
+// workgroups so that all of them are resident at once and the longest
+// stream of windows any wave has is as short as it can be; each wave then
+// streams its blocks back to back, as in a single product.
+struct W1Prob {              // one product
+    const uint32_t* bits;
+    const uint16_t* scales;
+    const void* ops;         // prepared operands of its activation
+    const float* xs;         // token scales [M]
+    const float* bias;
+    float* y;
+    int64_t N, K;
+    int64_t wg0, wgs;        // its first workgroup and workgroup count
+};
+struct W1Prep {              // one distinct activation
+    const int8_t* xq;        // [M][K]
+    void* ops;
+    int64_t K;
+    int64_t blk0, pblocks;   // its first block of the preparation launch; its piece blocks
+};
+constexpr int kW1BatchWaves = 8;
+
+__global__ void __launch_bounds__(256) w1_batch_prep_kernel(const W1Prep* __restrict__ tab, int nprep, int M) {
+    // this block's activation: the last entry whose first block is <= blockIdx.x
+    const int64_t b = blockIdx.x;
+    int lo = 0, hi = nprep - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (tab[mid].blk0 <= b) lo = mid;
+        else hi = mid - 1;
+    }
+    const W1Prep& P = tab[lo];
+    w1_prep_body(P.xq, M, P.K, 128, P.ops, P.pblocks, b - P.blk0);
+}
+
+template <int PK, bool SCV>
+__global__ void __launch_bounds__(64 * kW1BatchWaves) __attribute__((amdgpu_waves_per_eu(LL_W1_STREAM_WPE)))
+w1_batch_kernel(const W1Prob* __restrict__ tab, const int32_t* __restrict__ map, int M) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int64_t wg = blockIdx.x;
+    const W1Prob& P = tab[ld32(map + wg)];
+    w1_stream_body<128, PK, false, kW1BatchWaves, SCV, false>(P.bits, P.scales, P.N, P.K, M, P.ops, P.xs, P.bias, P.y,
+                                                              nullptr, 1, wg - P.wg0, P.wgs, lds);
+}
+
+template <int PK, bool SCV>
+int w1_batch_resident(int M, int64_t kmax) {
+    const size_t lds = size_t(w1_stream_lds_bytes(M, kmax, 128, kW1BatchWaves));
+    const void* k = reinterpret_cast<const void*>(w1_batch_kernel<PK, SCV>);
+    if (allow_dynamic_lds(k, lds) != hipSuccess) return 0;
+    return resident_wgs(k, 64 * kW1BatchWaves, lds);
+}
+
+template <int PK, bool SCV>
+hipError_t launch_w1_batch(const W1Prob* tab, const int32_t* map, int64_t wgs, int M, int64_t kmax, hipStream_t stream) {
+    const size_t lds = size_t(w1_stream_lds_bytes(M, kmax, 128, kW1BatchWaves));
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(w1_batch_kernel<PK, SCV>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((w1_batch_kernel<PK, SCV>), dim3{unsigned(wgs)}, dim3{64 * kW1BatchWaves}, lds, stream, tab, map, M);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace llk {
@@ -1291,6 +1378,82 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool w1_batch_fits(int64_t M, int64_t K) {
+    return M >= 1 && M <= 8 && K % 128 == 0 && w1_stream_a_bytes(int(M), K, 128) <= LL_W1_STREAM_A_MAX8;
+}
+int64_t w1_batch_wgs(int64_t N) { return ((N + kW1RowsPerWave - 1) / kW1RowsPerWave + kW1BatchWaves - 1) / kW1BatchWaves; }
+int64_t w1_batch_blocks(int64_t N) { return (N + kW1RowsPerWave - 1) / kW1RowsPerWave; }
+int64_t w1_batch_prep_blocks(int64_t M, int64_t K) {
+    const int64_t pieces = (K / 128) * w1_arows(int(M), 128) * 8;
+    return (pieces + 255) / 256 + (M * (K / 128) + 3) / 4;
+}
+size_t w1_batch_operand_bytes(int64_t M, int64_t K) { return w1_ws_bytes(M, K, 128); }
+size_t w1_batch_prob_bytes() { return sizeof(W1Prob); }
+size_t w1_batch_prep_bytes() { return sizeof(W1Prep); }
+
+int w1_batch_slots(int64_t M, int64_t kmax, bool scv) {
+    const int m = int(M);
+    switch (w1_pack(m, 128) * 2 + (scv ? 1 : 0)) {
+    case 17: return w1_batch_resident<8, true>(m, kmax);
+    case 16: return w1_batch_resident<8, false>(m, kmax);
+    case 9: return w1_batch_resident<4, true>(m, kmax);
+    case 8: return w1_batch_resident<4, false>(m, kmax);
+    case 5: return w1_batch_resident<2, true>(m, kmax);
+    case 4: return w1_batch_resident<2, false>(m, kmax);
+    case 3: return w1_batch_resident<1, true>(m, kmax);
+    default: return w1_batch_resident<1, false>(m, kmax);
+    }
+}
+
+void fill_w1_prob(void* dst, const void* bits, const void* scales, const void* ops, const float* xs, const float* bias,
+                  float* y, int64_t N, int64_t K, int64_t wg0, int64_t wgs) {
+    W1Prob p;
+    p.bits = static_cast<const uint32_t*>(bits);
+    p.scales = static_cast<const uint16_t*>(scales);
+    p.ops = ops;
+    p.xs = xs;
+    p.bias = bias;
+    p.y = y;
+    p.N = N;
+    p.K = K;
+    p.wg0 = wg0;
+    p.wgs = wgs;
+    *static_cast<W1Prob*>(dst) = p;
+}
+
+void fill_w1_prep(void* dst, const int8_t* xq, void* ops, int64_t M, int64_t K, int64_t blk0) {
+    W1Prep p;
+    p.xq = xq;
+    p.ops = ops;
+    p.K = K;
+    p.blk0 = blk0;
+    p.pblocks = ((K / 128) * w1_arows(int(M), 128) * 8 + 255) / 256;
+    *static_cast<W1Prep*>(dst) = p;
+}
+
+hipError_t launch_w1_batch_prep(const void* prep_table, int nprep, int64_t blocks, int64_t M, hipStream_t stream) {
+    hipLaunchKernelGGL(w1_batch_prep_kernel, dim3{unsigned(blocks)}, dim3{256}, 0, stream,
+                       static_cast<const W1Prep*>(prep_table), nprep, int(M));
+    return hipGetLastError();
+}
+
+hipError_t launch_w1_batch_product(const void* prob_table, const void* map, int64_t wgs, int64_t M, int64_t kmax,
+                                   bool scv, hipStream_t stream) {
+    const W1Prob* tab = static_cast<const W1Prob*>(prob_table);
+    const int32_t* mp = static_cast<const int32_t*>(map);
+    const int m = int(M);
+    switch (w1_pack(m, 128) * 2 + (scv ? 1 : 0)) {
+    case 17: return launch_w1_batch<8, true>(tab, mp, wgs, m, kmax, stream);
+    case 16: return launch_w1_batch<8, false>(tab, mp, wgs, m, kmax, stream);
+    case 9: return launch_w1_batch<4, true>(tab, mp, wgs, m, kmax, stream);
+    case 8: return launch_w1_batch<4, false>(tab, mp, wgs, m, kmax, stream);
+    case 5: return launch_w1_batch<2, true>(tab, mp, wgs, m, kmax, stream);
+    case 4: return launch_w1_batch<2, false>(tab, mp, wgs, m, kmax, stream);
+    case 3: return launch_w1_batch<1, true>(tab, mp, wgs, m, kmax, stream);
+    default: return launch_w1_batch<1, false>(tab, mp, wgs, m, kmax, stream);
+    }
 }
 
 }  // namespace llk

@@ -47,6 +47,29 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
                           const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                           hipStream_t stream, uint16_t* y16 = nullptr);
 
+// Prepared batches of W1 products (G = 128): w1_batch_fits(M, K) for every
+// product; one table entry per product (fill_w1_prob, wg0 its first
+// workgroup, wgs its workgroups: 1 .. w1_batch_wgs(N), a wave's blocks
+// ceil(w1_batch_blocks(N) / (8 wgs))) and per distinct activation
+// (fill_w1_prep, blk0 its first of w1_batch_prep_blocks(M, K) blocks,
+// operands of w1_batch_operand_bytes(M, K) bytes); scv: every K % 1024 == 0.
+// w1_batch_slots: workgroups of the product launch resident at once on the
+// current device (0 when it cannot be queried).
+bool w1_batch_fits(int64_t M, int64_t K);
+int64_t w1_batch_wgs(int64_t N);
+int64_t w1_batch_blocks(int64_t N);
+int w1_batch_slots(int64_t M, int64_t kmax, bool scv);
+int64_t w1_batch_prep_blocks(int64_t M, int64_t K);
+size_t w1_batch_operand_bytes(int64_t M, int64_t K);
+size_t w1_batch_prob_bytes();
+size_t w1_batch_prep_bytes();
+void fill_w1_prob(void* dst, const void* bits, const void* scales, const void* ops, const float* xs, const float* bias,
+                  float* y, int64_t N, int64_t K, int64_t wg0, int64_t wgs);
+void fill_w1_prep(void* dst, const int8_t* xq, void* ops, int64_t M, int64_t K, int64_t blk0);
+hipError_t launch_w1_batch_prep(const void* prep_table, int nprep, int64_t blocks, int64_t M, hipStream_t stream);
+hipError_t launch_w1_batch_product(const void* prob_table, const void* map, int64_t wgs, int64_t M, int64_t kmax,
+                                   bool scv, hipStream_t stream);
+
 // int8-activation prefill product, format i2_s.  ws: gemm_i8_workspace bytes
 // of split-K partial tiles and counters one per output tile (zero on entry,
 // left zero), or NULL (either) to forbid splits.

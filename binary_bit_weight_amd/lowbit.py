@@ -378,7 +378,12 @@ class ll_gemv_plan(C.Structure):
     _fields_ = [("mem", C.c_void_p), ("bytes", C.c_size_t), ("count", C.c_int32), ("nprep", C.c_int32),
                 ("act", C.c_int32), ("fmt", C.c_int32), ("M", C.c_int64), ("tiles", C.c_int64),
                 ("prep_entries", C.c_int64), ("kmax", C.c_int64), ("prob_table", C.c_void_p),
-                ("prep_table", C.c_void_p), ("map_table", C.c_void_p), ("epilogues", C.c_int32)]
+                ("prep_table", C.c_void_p), ("map_table", C.c_void_p), ("epilogues", C.c_int32),
+                ("flags", C.c_int32)]
+
+
+class ll_gemv_item_i8(C.Structure):
+    _fields_ = [("w", ll_weights), ("xq", C.c_void_p), ("xs", C.c_void_p), ("bias", C.c_void_p), ("y", C.c_void_p)]
 
 
 SIGNATURES.update({
@@ -386,6 +391,8 @@ SIGNATURES.update({
     "ll_gemv_plan_init": (C.c_int, [_P, _I32, _I32, _I64, _P, _SZ, _P]),
     "ll_gemv_plan_bytes_ex": (_SZ, [_P, _I32, _I32, _I64]),
     "ll_gemv_plan_init_ex": (C.c_int, [_P, _I32, _I32, _I64, _P, _SZ, _P]),
+    "ll_gemv_plan_bytes_i8": (_SZ, [_P, _I32, _I64]),
+    "ll_gemv_plan_init_i8": (C.c_int, [_P, _I32, _I64, _P, _SZ, _P]),
     "ll_gemv_plan_run": (C.c_int, [_P, _P]),
     "ll_gemv_plan_prepare": (C.c_int, [_P, _P]),
     "ll_gemv_plan_product": (C.c_int, [_P, _P]),
@@ -441,6 +448,36 @@ class GemvPlan:
         self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=dev)
         _check(lib().ll_gemv_plan_init_ex(arr, len(self.items), LL_ACT_F32, M, _dev(self.mem), int(n),
                                           C.byref(self.plan)))
+
+    def prepare(self, stream=None):
+        _check(lib().ll_gemv_plan_prepare(C.byref(self.plan), _stream(stream)))
+
+    def product(self, stream=None):
+        _check(lib().ll_gemv_plan_product(C.byref(self.plan), _stream(stream)))
+
+    def run(self, stream=None):
+        _check(lib().ll_gemv_plan_run(C.byref(self.plan), _stream(stream)))
+
+
+class GemvPlanI8:
+    """A prepared batch of W1A8 decode products (ll_gemv_plan_init_i8): items
+    (Weights with group 128, xq int8 [M,K], xs fp32 [M], bias_or_None, y fp32
+    [M,N]) as GPU tensors; the plan keeps them alive.  run() = prepare() +
+    product()."""
+
+    def __init__(self, items, M):
+        import torch
+        self.items = list(items)
+        arr = (ll_gemv_item_i8 * len(self.items))()
+        for i, (w, xq, xs, b, y) in enumerate(self.items):
+            arr[i] = ll_gemv_item_i8(w.desc, _dev(xq), _dev(xs), _dev(b), _dev(y))
+        self._arr = arr
+        self.plan = ll_gemv_plan()
+        n = lib().ll_gemv_plan_bytes_i8(arr, len(self.items), M)
+        if n == 2 ** 64 - 1:   # invalid items: let init report which one
+            _check(lib().ll_gemv_plan_init_i8(arr, len(self.items), M, None, 0, C.byref(self.plan)))
+        self.mem = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=self.items[0][1].device)
+        _check(lib().ll_gemv_plan_init_i8(arr, len(self.items), M, _dev(self.mem), int(n), C.byref(self.plan)))
 
     def prepare(self, stream=None):
         _check(lib().ll_gemv_plan_prepare(C.byref(self.plan), _stream(stream)))

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LL_ABI_VERSION 4
+#define LL_ABI_VERSION 5
 
 /* Bytes at the start of every workspace reserved for split-K counters. */
 #define LL_WORKSPACE_COUNTER_BYTES 4096
@@ -242,6 +242,7 @@ typedef struct {
     void* prep_table;    /* inside mem */
     void* map_table;     /* inside mem: product index of every workgroup */
     int32_t epilogues;   /* nonzero when some item has a fused epilogue */
+    int32_t flags;       /* launch variant chosen by the init call */
 } ll_gemv_plan;
 
 /* Fused epilogues of a prepared product.
@@ -292,6 +293,29 @@ ll_status ll_gemv_plan_init(const ll_gemv_item* items, int32_t count, int32_t ac
 size_t ll_gemv_plan_bytes_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M);
 ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int32_t act, int64_t M,
                                void* mem, size_t bytes, ll_gemv_plan* plan);
+/* [BG "Method", "API": binary_gemm; BL "High-Level API": PreparedDispatch]
+   A prepared batch of W1A8 products: binary weights with group size 128
+   and int8 activations, 1 <= M <= 8, every product as ll_bitlinear_gemv
+   computes it (bit-exact: y = (float)((double)xs[m] * sum_g s_g * d_g),
+   then + bias).  Items with the same xq pointer and K share one prepared
+   operand.  Each item's K must leave the operand of M tokens within the
+   streaming product's workgroup memory: (K / 128) * 2M * 144 + 4 (M K / 128
+   + 4) + 64 <= 114688 bytes (M = 1: K <= 50,176; M = 8: K <= 6,272), else
+   LL_ERANGE.  Validation otherwise as
+   ll_bitlinear_gemv (LL_EINVAL for another format or a missing pointer,
+   LL_ESHAPE for a group other than 128 or K % 128 != 0, LL_EALIGN for xq
+   not 16-byte aligned or xs, y, bias not 4-byte aligned).  Run with
+   ll_gemv_plan_run / _prepare / _product like the plans above. */
+typedef struct {
+    ll_weights w;        /* W1 weights, group 128 (device pointers) */
+    const int8_t* xq;    /* device int8 [M, K] */
+    const float* xs;     /* device fp32 [M] per-token scales */
+    const float* bias;   /* device fp32 [N] or NULL */
+    float* y;            /* device fp32 [M, N] */
+} ll_gemv_item_i8;
+size_t ll_gemv_plan_bytes_i8(const ll_gemv_item_i8* items, int32_t count, int64_t M);
+ll_status ll_gemv_plan_init_i8(const ll_gemv_item_i8* items, int32_t count, int64_t M, void* mem, size_t bytes,
+                               ll_gemv_plan* plan);
 /* Both launches: ll_gemv_plan_prepare, then ll_gemv_plan_product. */
 ll_status ll_gemv_plan_run(const ll_gemv_plan* plan, void* stream);
 /* Lays out the current contents of every x as operands (inside mem). */

@@ -200,3 +200,91 @@ def test_w1a8_split_workspace_reuse(M, K):
         L.ll_bitlinear_gemv(W, L.LL_ACT_I8, t.from_numpy(q).cuda(), t.from_numpy(s).cuda(), M, None, y, ws)
         y_ref, _ = oracle.w1a8_gemm(bits, scales, K, G, q, s)
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), rnd
+
+
+def _plan_case(shapes, M, seed, bias_at=()):
+    """Runs a W1A8 prepared batch twice (the second time with new activation
+    contents and scales in the same buffers) and compares every output with
+    the oracle bit for bit.  shapes: (N, K, activation slot)."""
+    t = torch()
+    acts, items, refs = {}, [], []
+    for i, (N, K, slot) in enumerate(shapes):
+        bits, scales = make_w1(seed + i, N, K, 128)
+        W = L.upload_w1(bits, scales, K, 128)
+        if slot not in acts:
+            q, s = _acts(seed + 100 + slot, M, K)
+            acts[slot] = [q, s, t.from_numpy(q).cuda(), t.from_numpy(s).cuda()]
+        b = synth.uniform_f32(seed + 200 + i, N, -1, 1) if i in bias_at else None
+        y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+        a = acts[slot]
+        items.append((W, a[2], a[3], None if b is None else t.from_numpy(b).cuda(), y))
+        refs.append((bits, scales, K, slot, b))
+    plan = L.GemvPlanI8(items, M)
+    for rnd in range(2):
+        if rnd == 1:
+            for slot, a in acts.items():
+                q, s = _acts(seed + 300 + slot, M, a[0].shape[1])
+                a[2].copy_(t.from_numpy(q))
+                a[3].copy_(t.from_numpy(s))
+                a[0], a[1] = q, s
+        announce("w1a8 plan", M, len(shapes), rnd)
+        plan.run()
+        t.cuda.synchronize()
+        for (W, _, _, _, y), (bits, scales, K, slot, b) in zip(items, refs):
+            y_ref, _ = oracle.w1a8_gemm(bits, scales, K, 128, acts[slot][0], acts[slot][1], bias=b, threads=TH)
+            got = y.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), y_ref.view(np.uint32)), \
+                "N=%d K=%d round %d: %d mismatches" % (W.N, K, rnd, int((got.view(np.uint32) != y_ref.view(np.uint32)).sum()))
+
+
+# every token count (packed units 8 / 4 / 2 / 1); with scv every K is a multiple of 1024 (row-vector scale
+# loads), else one K = 1152 ends in a cut window; ragged N (37, 130, 300, 1000) and a 16-row matrix
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("scv", [True, False])
+def test_w1a8_plan_matches_oracle(M, scv):
+    shapes = [(300, 5120, 0), (37, 5120, 0), (1000, 2048, 1), (16, 1024, 2)]
+    shapes += [] if scv else [(130, 1152, 3), (20, 128, 4)]
+    shapes += [(50, 17408, 5)] if M <= 2 else []
+    _plan_case(shapes, M, 6000 + 10 * M + int(scv), bias_at=(1, 3))
+
+
+def test_w1a8_plan_decode_layer():
+    """One decoder layer of the hidden-5120 shapes as one batch at M = 1: QKV
+    7168, O 5120, gate and up 17408 (one activation), down 5120 x 17408."""
+    shapes = [(7168, 5120, 0), (5120, 5120, 1), (17408, 5120, 2), (17408, 5120, 2), (5120, 17408, 3)]
+    _plan_case(shapes, 1, 6500)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_w1a8_plan_decode_layers_streamed(M):
+    """Four decoder layers in one batch: more workgroups than the device holds
+    at once, so most products get fewer workgroups than blocks and each wave
+    streams several blocks back to back.  The layers share weights and
+    activations (separate device copies), so every layer's outputs equal the
+    oracle's of the first; every output is compared bit for bit."""
+    t = torch()
+    shapes = [(7168, 5120, 0), (5120, 5120, 1), (17408, 5120, 2), (17408, 5120, 2), (5120, 17408, 3)]
+    acts, host, items = {}, [], []
+    for i, (N, K, slot) in enumerate(shapes):
+        bits, scales = make_w1(6600 + i, N, K, 128)
+        if slot not in acts:
+            q, s = _acts(6700 + slot, M, K)
+            acts[slot] = (q, s, t.from_numpy(q).cuda(), t.from_numpy(s).cuda())
+        host.append((bits, scales, K, slot))
+    outs = []
+    for layer in range(4):
+        for i, (N, K, slot) in enumerate(shapes):
+            bits, scales, _, _ = host[i]
+            y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+            items.append((L.upload_w1(bits, scales, K, 128), acts[slot][2], acts[slot][3], None, y))
+            outs.append((i, y))
+    plan = L.GemvPlanI8(items, M)
+    assert plan.plan.tiles < sum((N + 255) // 256 for N, _, _ in shapes) * 4    # fewer workgroups than blocks / 8
+    announce("w1a8 plan 4 layers", M)
+    plan.run()
+    t.cuda.synchronize()
+    refs = [oracle.w1a8_gemm(b, sc, K, 128, acts[slot][0], acts[slot][1], threads=TH)[0] for b, sc, K, slot in host]
+    for i, y in outs:
+        got = y.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), refs[i].view(np.uint32)), \
+            "product %d: %d mismatches" % (i, int((got.view(np.uint32) != refs[i].view(np.uint32)).sum()))

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES), "binding and header disagree"
-    assert L.ll_abi_version() == 4
+    assert L.ll_abi_version() == 5
     assert L.ll_strerror(-5) == "workspace missing or too small"
 
 
@@ -253,6 +253,48 @@ def test_plan_ex_gated_pair_validation():
         arr = (L.ll_gemv_item_ex * 1)(item)
         assert lib.ll_gemv_plan_bytes_ex(arr, 1, L.LL_ACT_F32, 1) == 2 ** 64 - 1
         assert lib.ll_gemv_plan_init_ex(arr, 1, L.LL_ACT_F32, 1, None, 0, C.byref(plan)) == want
+
+
+def _item_i8(N, K, xq, y, group=128, fmt=None, xs=None, bias=None):
+    return L.ll_gemv_item_i8(_w(fmt=L.LL_FMT_W1 if fmt is None else fmt, N=N, K=K, group=group), C.c_void_p(xq),
+                             C.c_void_p(FAKE if xs is None else xs), None if bias is None else C.c_void_p(bias),
+                             C.c_void_p(y))
+
+
+def test_plan_i8_layout_and_validation():
+    """Host-only: a W1A8 plan holds one prepared operand per distinct (xq, K)
+    (A digit rows of K / 128 chunks x 2M rows x 128 B, then M x K / 128
+    int32 group sums) and rejects other formats, group sizes, M outside
+    [1, 8], operands too large for the streaming product, NULL and
+    misaligned pointers, before anything is launched."""
+    lib = L.lib()
+    one = (L.ll_gemv_item_i8 * 1)(_item_i8(7168, 5120, FAKE, FAKE))
+    b1 = lib.ll_gemv_plan_bytes_i8(one, 1, 1)
+    ops = 40 * 2 * 128 + 40 * 4
+    assert ops <= b1 < ops + 4096
+    shared = (L.ll_gemv_item_i8 * 3)(_item_i8(7168, 5120, FAKE, FAKE), _item_i8(17408, 5120, FAKE, FAKE),
+                                     _item_i8(5120, 17408, FAKE * 3, FAKE))
+    b3 = lib.ll_gemv_plan_bytes_i8(shared, 3, 1)
+    ops3 = ops + 136 * 2 * 128 + 136 * 4
+    assert ops3 <= b3 < ops3 + 8192
+    assert lib.ll_gemv_plan_bytes_i8(one, 1, 8) > lib.ll_gemv_plan_bytes_i8(one, 1, 1)
+    plan = L.ll_gemv_plan()
+    cases = [(_item_i8(64, 5120, FAKE, FAKE, fmt=L.LL_FMT_I2S), 1, -1),      # another format
+             (_item_i8(64, 5120, FAKE, FAKE, group=64), 1, -2),              # group 64
+             (_item_i8(64, 5120, FAKE, FAKE), 9, -2),                        # M = 9
+             (_item_i8(64, 5120, FAKE, FAKE), 0, -2),                        # M = 0
+             (_item_i8(64, 6400, FAKE, FAKE), 8, -7),                        # operand of 8 x 6400 too large
+             (_item_i8(64, 50304, FAKE, FAKE), 1, -7),                       # 1 x 50304 too large
+             (_item_i8(64, 5120, FAKE + 8, FAKE), 1, -3),                    # xq not 16-byte aligned
+             (_item_i8(64, 5120, FAKE, FAKE + 2), 1, -3),                    # y not 4-byte aligned
+             (_item_i8(64, 5120, 0, FAKE), 1, -1)]                           # NULL xq
+    for item, M, want in cases:
+        arr = (L.ll_gemv_item_i8 * 1)(item)
+        assert lib.ll_gemv_plan_bytes_i8(arr, 1, M) == 2 ** 64 - 1, (M, want)
+        assert lib.ll_gemv_plan_init_i8(arr, 1, M, None, 0, C.byref(plan)) == want, (M, want)
+    assert lib.ll_gemv_plan_bytes_i8((L.ll_gemv_item_i8 * 1)(_item_i8(64, 6272, FAKE, FAKE)), 1, 8) != 2 ** 64 - 1
+    assert lib.ll_gemv_plan_bytes_i8((L.ll_gemv_item_i8 * 1)(_item_i8(64, 50176, FAKE, FAKE)), 1, 1) != 2 ** 64 - 1
+    assert lib.ll_gemv_plan_init_i8(one, 1, 1, None, 0, C.byref(plan)) == -5     # no memory
 
 
 def test_w1_device_argument_errors_and_workspace():
