@@ -498,6 +498,30 @@ def extras_single(L, synth, torch, dev, stream):
                 "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}
         del Ws
         torch.cuda.empty_cache()
+    # W1A8 prepared batches: 12 decoder layers of the same shapes (QKV 7168, O 5120, gate and up 17408 from one
+    # activation, down 5120 x 17408; the down projection only where its operand fits, M <= 2), every matrix its
+    # own device copy, two launches per step (ll_gemv_plan_init_i8)
+    for M in (1, 8):
+        shapes = [(7168, K, 0, 501), (K, K, 1, 505), (17408, K, 2, 502), (17408, K, 2, 506)]
+        shapes += [(K, 17408, 3, 507)] if M <= 2 else []
+        acts, items, wbytes = {}, [], 0
+        for layer in range(12):
+            for N, Kp, slot, seed in shapes:
+                if slot not in acts:
+                    acts[slot] = L.quantize(torch.from_numpy(synth.normal_f32(520 + slot, M, Kp)).to(dev), stream)
+                bits, sc = w1_weights(L, synth, seed, N, Kp, G)
+                items.append((L.upload_w1(bits, sc, Kp, G, dev), acts[slot][0], acts[slot][1], None,
+                              torch.empty((M, N), dtype=torch.float32, device=dev)))
+                wbytes += bits.nbytes + sc.nbytes
+        plan = L.GemvPlanI8(items, M)
+        settle(torch, lambda i: plan.run(stream))
+        ms = time_events(torch, lambda: plan.run(stream), 20, stream)
+        out["w1a8_plan_12_layers_M%d" % M] = {
+            "us": round(ms * 1e3, 2), "GB_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes),
+            "products": len(items)}
+        del plan, items
+        torch.cuda.empty_cache()
     # int8 prefill GEMM, M=512 (bf16 activations quantized per token), as graph replays
     for N, K in GEMM_SHAPES:
         W, xb, xq, xsc, y, gws = gemm_operands(L, synth, torch, dev, stream, N, K)
