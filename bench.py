@@ -74,7 +74,7 @@ GEMM_SHAPES = [(6912, 2560), (2560, 6912)]    # (N, K) at M = 512; the first is 
 # W1A8 (binary weights, int8 activations): the LM head at hidden 5120, G = 128
 W1_KERNEL = "w1_stream_kernel"
 W1_SOURCES = ["binary_bit_weight_amd/csrc/gemv_w1.hip", "binary_bit_weight_amd/csrc/common.h"]
-W1_SUMMARY = os.path.join(ROOT, "profiles", "w1_gemv_lm_head_m1_counters.md")
+W1_SUMMARY = os.path.join(ROOT, "profiles", "w1_stream_lm_head_m1_counters.md")
 W1_HEAD = (248320, 5120, 128)
 COPY_PROBE_BYTES = 256 << 20
 ROLES = [("q", HIDDEN, HIDDEN, 0), ("k", HIDDEN, HIDDEN, 0), ("v", HIDDEN, HIDDEN, 0), ("o", HIDDEN, HIDDEN, 1),
