@@ -101,7 +101,7 @@ ll_status plan_layout(const ll_gemv_item_ex* items, int32_t count, int32_t act, 
         if ((is_pair(items[i]) || items[i].norm_w) && !L.f4)
             return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: gated pairs and norms need every K <= 2^17", i);
     for (int i = 0; i < count; ++i) {
-        const int64_t rows = L.f4 ? llk::f4_batch_rows(is_pair(items[i])) : llk::planes_batch_rows();
+        const int64_t rows = L.f4 ? llk::f4_batch_rows(is_pair(items[i]), items[0].w.fmt, M) : llk::planes_batch_rows();
         int found = -1;
         const float eps = items[i].norm_w ? items[i].norm_eps : 0.0f;
         for (size_t j = 0; j < L.xs.size(); ++j)
@@ -301,7 +301,7 @@ ll_status ll_gemv_plan_init_ex(const ll_gemv_item_ex* items, int32_t count, int3
         else
             llk::fill_planes_prob(host.data() + L.prob_off + size_t(i) * llk::planes_prob_bytes(), it.w.codes,
                                   it.w.scales, ops, it.bias, it.y, it.w.N, it.w.K, first);
-        const int64_t rows = L.f4 ? llk::f4_batch_rows(pair) : llk::planes_batch_rows();
+        const int64_t rows = L.f4 ? llk::f4_batch_rows(pair, items[0].w.fmt, M) : llk::planes_batch_rows();
         const int64_t wgs = (it.w.N + rows - 1) / rows;
         for (int64_t g = 0; g < wgs; ++g) map[first + g] = i;
         first += wgs;

@@ -58,28 +58,32 @@ constexpr int kQuarterBytes = kPl * kPlRowBytes;       // 192
 constexpr int kStepBytes = 4 * kQuarterBytes;          // 768: one 128-k step
 constexpr int kChunkBytes = 2 * kStepBytes;            // 1536: one 256-k chunk
 constexpr int kSliceChunks = 8;                        // chunks per preparation workgroup
+// 16-row column blocks per wave: two (one activation operand read feeds
+// both), except for one token of i2_s, where one block per wave (64-row
+// workgroups, twice as many) measured faster on the 30-layer decode step
+// (5.62 -> 5.80 TB/s; the fused step 5.54 -> 5.66) while TQ2_0 and more
+// tokens lost with it (TQ2_0 batch of 118 copies at M = 1: 6.15 -> 5.85 TB/s;
+// M = 8: 2.32 -> 1.84).
 #ifndef LL_F4_CB
-#define LL_F4_CB 2                                     // 16-row column blocks per wave
+#define LL_F4_CB 2
 #endif
+#ifndef LL_F4_CB_I2S1
+#define LL_F4_CB_I2S1 1
+#endif
+__host__ __device__ constexpr int f4_cb(int FMT, int MT) { return FMT == 1 && MT == 1 ? LL_F4_CB_I2S1 : LL_F4_CB; }
 #ifndef LL_F4_CUNROLL
 #define LL_F4_CUNROLL 1                                // chunk loop of the multiply not unrolled (register use)
 #endif
 #ifndef LL_F4_NT
 #define LL_F4_NT 1                                     // weights read with non-temporal loads
 #endif
-constexpr int kCB = LL_F4_CB;
 constexpr int kGroup = 4;                              // chunks per weight tile: 256 bytes of each row
-constexpr int kWStride = kGroup * 64 + 16;             // padded LDS tile row
-constexpr int kWTile = 16 * kCB * kWStride;            // one wave's tile
-constexpr int kWaveRows = 16 * kCB;
 #ifndef LL_F4_WAVES
 #define LL_F4_WAVES 4
 #endif
 constexpr int kWaves = LL_F4_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kAWin = kGroup * kChunkBytes;            // activation digits of one tile's k range
-constexpr int kAPer = (kAWin / 16 + kThreads - 1) / kThreads;   // 16-byte window pieces per thread
-constexpr int kWgRows = kWaves * kWaveRows;
 constexpr int64_t kMaxK = int64_t(1) << 17;            // the rounding of x stays inside the tolerance (exact fp32 MFMA sums up to 2^20)
 
 constexpr uint32_t kDigitNibbles = 0x5420ACDEu;        // nibble v: e2m1 code of the digit v - 4
@@ -325,38 +329,40 @@ __device__ __forceinline__ f32x4 mfma_f4(i32x4 a, i32x4 b, f32x4 c) {
 // weight tile feeds MT blocks.  KG chunks of 256 k per pipeline group: 4
 // (weight loads of 4 rows x 256 bytes) while the activation windows of all
 // tokens fit beside the tiles, else 2 (8 rows x 128 bytes).
-template <int MT>
+// LDS: two activation windows, then one weight tile per wave.
+template <int FMT, int MT>
 struct F4Cfg {
+    static constexpr int CB = f4_cb(FMT, MT);                    // 16-row column blocks per wave
+    static constexpr int WaveRows = 16 * CB;
+    static constexpr int WgRows = kWaves * WaveRows;
     static constexpr int KG = MT <= 2 ? 4 : 2;
     static constexpr int WStride = KG * 64 + 16;                 // padded LDS tile row
-    static constexpr int WTile = 16 * kCB * WStride;             // one wave's tile
+    static constexpr int WTile = 16 * CB * WStride;              // one wave's tile
     static constexpr int AWin = MT * KG * kChunkBytes;           // one group's digits, all tokens
     static constexpr int APer = (AWin / 16 + kThreads - 1) / kThreads;   // 16-byte window pieces per thread
     static constexpr int LPR = KG * 4;                           // lanes per row in a weight load
     static constexpr int RPI = 64 / LPR;                         // rows per weight load
-    static constexpr int NLD = kWaveRows / RPI;                  // weight loads per wave and group
+    static constexpr int NLD = WaveRows / RPI;                   // weight loads per wave and group
     static constexpr int64_t Lds = 2 * int64_t(AWin) + int64_t(kWaves) * WTile;
 };
-static_assert(F4Cfg<1>::AWin == kAWin && F4Cfg<1>::WTile == kWTile, "one-token shapes");
-
-// LDS: two activation windows, then one weight tile per wave.
-__host__ __device__ constexpr int64_t prod_lds_bytes() { return F4Cfg<1>::Lds; }
+static_assert(F4Cfg<1, 1>::AWin == kAWin && F4Cfg<2, 1>::AWin == kAWin, "one-token shapes");
 
 template <int FMT, int MT>
 struct Regs {
-    i32x4 w[F4Cfg<MT>::NLD];                 // load i: row RPI i + lane / LPR, 16 bytes at 16 (lane % LPR)
-    i32x4 a[F4Cfg<MT>::APer];                // pieces tid + kThreads p of the activation window
-    uint16_t sc[kCB];                        // TQ2_0: scale of row nl, chunk q % KG of the group, per column block
+    i32x4 w[F4Cfg<FMT, MT>::NLD];            // load i: row RPI i + lane / LPR, 16 bytes at 16 (lane % LPR)
+    i32x4 a[F4Cfg<FMT, MT>::APer];           // pieces tid + kThreads p of the activation window
+    uint16_t sc[F4Cfg<FMT, MT>::CB];         // TQ2_0: scale of row nl, chunk q % KG of the group, per column block
 };
 
 // out[m] = this lane's result for token m0 + m: lane l holds row row0 + l
-// (column block l / 16, meaningful for l < 16 kCB, rows < N and m0 + m <
+// (column block l / 16, meaningful for l < 16 CB, rows < N and m0 + m <
 // P.M), bias not added.  Token t's digits are at P.ops + t P.opstride.
 template <int FMT, int MT>
 __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int64_t row0, int m0, int tid, char* abuf,
                                         char* wtile, float (&out)[MT]) {
-    using C = F4Cfg<MT>;
+    using C = F4Cfg<FMT, MT>;
+    constexpr int kCB = C::CB;
     constexpr int KG = C::KG;
     const int lane = tid & 63, nl = lane & 15, q = lane >> 4;
     const int64_t N = P.N, K = P.K, nch = nchunks(K);
@@ -636,15 +642,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(f
     const F4Prob& P = tab[ld32(map + L)];
     const int tid = int(threadIdx.x), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: selects stay scalar
-    char* wtile = lds + 2 * F4Cfg<MT>::AWin + wave * F4Cfg<MT>::WTile;
+    using C = F4Cfg<FMT, MT>;
+    char* wtile = lds + 2 * C::AWin + wave * C::WTile;
     // Gated pair (only in launches whose table holds one): waves 0, 1
     // multiply 64 gate rows, waves 2, 3 the same rows of the up matrix, all
     // from one activation window.  Waves past the last row still take part
     // (clamped rows, nothing stored): the loop has barriers.
     const bool pair = PAIRS && P.pair != 0;
     const int half = pair ? wave >> 1 : 0;
-    const int64_t row0 = pair ? (L - P.wg0) * (kWgRows / 2) + (wave & 1) * kWaveRows
-                              : (L - P.wg0) * kWgRows + wave * kWaveRows;
+    const int64_t row0 = pair ? (L - P.wg0) * (C::WgRows / 2) + (wave & 1) * C::WaveRows
+                              : (L - P.wg0) * C::WgRows + wave * C::WaveRows;
     float v[MT];
     f4_rows<FMT, MT>(P, half ? P.codes2 : P.codes, half ? P.scales2 : P.scales, row0, m0, tid, lds, wtile, v);
     const int64_t row = row0 + lane;                       // = row0 + 16 cb + nl for cb = q
@@ -655,17 +662,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(f
         for (int m = 0; m < MT; ++m) {
             float out = v[m];
             if (P.bias) out = __fadd_rn(out, bv);
-            if (m0 + m < P.M && lane < kWaveRows && row < P.N) P.y[int64_t(m0 + m) * P.N + row] = out;
+            if (m0 + m < P.M && lane < C::WaveRows && row < P.N) P.y[int64_t(m0 + m) * P.N + row] = out;
         }
         return;
     }
     // the up results reach the gate waves through LDS
     __syncthreads();                                       // every wave is done with the operand buffers
     float* xch = reinterpret_cast<float*>(lds);
-    if (half == 1 && lane < kWaveRows) xch[(wave & 1) * kWaveRows + lane] = v[0];
+    if (half == 1 && lane < C::WaveRows) xch[(wave & 1) * C::WaveRows + lane] = v[0];
     __syncthreads();
-    if (half == 0 && lane < kWaveRows && row < P.N) {
-        const float u = xch[(wave & 1) * kWaveRows + lane];
+    if (half == 0 && lane < C::WaveRows && row < P.N) {
+        const float u = xch[(wave & 1) * C::WaveRows + lane];
         const float r = v[0] > 0.0f ? v[0] : 0.0f;
         P.y[row] = __fmul_rn(__fmul_rn(r, r), u);
     }
@@ -678,7 +685,12 @@ namespace llk {
 bool f4_engine(int64_t M, int64_t kmax) { return M >= 1 && M <= 16 && kmax <= kMaxK; }
 int64_t f4_op_stride(int64_t K) { return (op_bytes(K) + 255) / 256 * 256; }
 size_t f4_operand_bytes(int64_t M, int64_t K) { return size_t(M * f4_op_stride(K)); }
-int64_t f4_batch_rows(bool pair) { return pair ? kWgRows / 2 : kWgRows; }
+// the launch variant launch_f4_fmt picks for M tokens: its rows per workgroup
+int64_t f4_batch_rows(bool pair, int fmt, int64_t M) {
+    const int mt = M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8;
+    const int64_t rows = kWaves * 16 * f4_cb(fmt, mt);
+    return pair ? rows / 2 : rows;
+}
 size_t f4_prob_bytes() { return sizeof(F4Prob); }
 size_t f4_prep_bytes() { return sizeof(F4Prep); }
 int64_t f4_grid(int64_t T) { return 8 * ((T + 7) / 8); }
@@ -725,7 +737,7 @@ hipError_t launch_f4_batch_prep(const void* prep_table, int nprep, int fmt, int6
 template <int FMT, bool PAIRS, int MT>
 hipError_t launch_f4_product(const F4Prob* t, const int32_t* m, int64_t T, int passes, hipStream_t stream) {
     const dim3 grid{unsigned(f4_grid(T * passes))}, block{unsigned(kThreads)};
-    const size_t lds = size_t(F4Cfg<MT>::Lds);
+    const size_t lds = size_t(F4Cfg<FMT, MT>::Lds);
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(f4_batch_kernel<FMT, PAIRS, MT>), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((f4_batch_kernel<FMT, PAIRS, MT>), grid, block, lds, stream, t, m, T * passes, passes);

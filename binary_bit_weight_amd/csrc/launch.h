@@ -133,7 +133,7 @@ namespace llk {
 bool f4_engine(int64_t M, int64_t kmax);             // 1 <= M <= 16, every K <= 2^17
 int64_t f4_op_stride(int64_t K);                     // bytes between two tokens' prepared digits
 size_t f4_operand_bytes(int64_t M, int64_t K);       // prepared digits of one activation (M tokens)
-int64_t f4_batch_rows(bool pair);                   // output rows per workgroup (a gated pair: rows of both)
+int64_t f4_batch_rows(bool pair, int fmt, int64_t M);   // output rows per workgroup (a gated pair: rows of both)
 size_t f4_prob_bytes();
 size_t f4_prep_bytes();
 int64_t f4_grid(int64_t T);                         // workgroups launched for T logical ones
