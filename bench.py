@@ -16,11 +16,12 @@ from the committed rocprofv3 counter summary when that summary was made from
 the current kernel source, and the rate of a read-only streaming kernel as
 the practical bound), the CPU oracle on the whole step (its rows split over
 every host core, and on one core; the median of three runs each), and
-extras: single-call per-matrix GEMV times, the same step with the fused
-epilogues and as dependent per-layer batches, the TQ2_0 small-batch GEMV,
-the W1A8 products of hidden 5120, the int8 prefill GEMM with i2_s, TQ2_0 and
-W1 weights (TOPS against the int8 matrix-core peak) and the one-shot bf16
-layer.
+extras: single-call per-matrix GEMV times (fp32 and int8 activations), the
+same step with the fused epilogues and as dependent per-layer batches, the
+TQ2_0 small-batch GEMV, the W1A8 products of hidden 5120 (single calls, a
+plain bf16 matmul of the same shapes as context, and prepared batches of 12
+decoder layers), the int8 prefill GEMM with i2_s, TQ2_0 and W1 weights (TOPS
+against the int8 matrix-core peak) and the one-shot bf16 layer.
 
 The second half of the metric, the i2_s int8 prefill GEMM at M = 512, is
 reported as "roofline_gemm": the GEMM kernel timed the same way (back-to-back
@@ -497,6 +498,29 @@ def extras_single(L, synth, torch, dev, stream):
                 "us": round(ms * 1e3, 2), "GB_s": round(wbytes / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}
         del Ws
+        torch.cuda.empty_cache()
+        # context only (the binary-gemm card compares its kernel with a dequantized bf16 matmul): the same
+        # shape as a plain bf16 [M, K] x [K, N] product of random bf16 weights on this GPU, torch.mm on
+        # contiguous operands, rotated over copies like the W1A8 line
+        bbytes = N * K * 2
+        breps = max(1, int(np.ceil(2 ** 29 / bbytes)))
+        Wb = [torch.randn((K, N), dtype=torch.bfloat16, device=dev) for _ in range(breps)]
+        for M in (1, 8):
+            xb16 = torch.randn((M, K), dtype=torch.bfloat16, device=dev)
+            settle(torch, lambda i: torch.mm(xb16, Wb[i % breps]))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(20, 4 * breps)
+            e0.record(stream)
+            for i in range(n):
+                torch.mm(xb16, Wb[i % breps])
+            e1.record(stream)
+            e1.synchronize()
+            bms = e0.elapsed_time(e1) / n
+            w1 = out["w1a8_gemv_%s_%dx%d_M%d" % (name, N, K, M)]["us"]
+            out["bf16_mm_context_%s_%dx%d_M%d" % (name, N, K, M)] = {
+                "us": round(bms * 1e3, 2), "GB_s": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                "w1a8_speedup": round(bms * 1e3 / w1, 2)}
+        del Wb
         torch.cuda.empty_cache()
     # W1A8 prepared batches: 12 decoder layers of the same shapes (QKV 7168, O 5120, gate and up 17408 from one
     # activation, down 5120 x 17408; the down projection only where its operand fits, M <= 2), every matrix its
