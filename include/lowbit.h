@@ -202,9 +202,11 @@ size_t ll_gemv_workspace_size(const ll_weights* w, int32_t act, int64_t M);
    bias: device fp32 [N] added last, or NULL.  y: device fp32
    [M,N].  workspace: at least ll_gemv_workspace_size(w, act, M) bytes (may
    be NULL when that is 0), under the workspace rules above; with W1 weights
-   it holds the prepared activation digits of group sizes other than 128,
-   and a narrow matrix splits K over workgroups, which publish partial sums
-   there and count their arrivals in the workspace's counter region. */
+   it holds the prepared activation digits (group sizes other than 128, or
+   more than two tokens), and a narrow matrix whose activation operand is
+   too large for one workgroup's memory splits K over workgroups, which
+   publish partial sums there and count their arrivals in the workspace's
+   counter region. */
 ll_status ll_bitlinear_gemv(const ll_weights* w, int32_t act, const void* x, const float* xs,
                             int64_t M, const float* bias, float* y,
                             void* workspace, size_t workspace_bytes, void* stream);
