@@ -37,6 +37,9 @@ ll_status check_weights(const ll_weights* w, const char* fn) {
     switch (w->fmt) {
     case LL_FMT_I2S:
         if (w->K % 128) return ll::failf(LL_ESHAPE, "%s: i2_s needs K %% 128 == 0", fn);
+        // the products sum a code field's terms (up to 2 * 16 * 127 each) over
+        // up to K / 2 elements in one int32 accumulator
+        if (w->K > (int64_t(1) << 20)) return ll::failf(LL_ERANGE, "%s: i2_s needs K <= 2^20 (exact int32 sums)", fn);
         return LL_OK;
     case LL_FMT_TQ2_0:
         if (w->K % 256) return ll::failf(LL_ESHAPE, "%s: TQ2_0 needs K %% 256 == 0", fn);

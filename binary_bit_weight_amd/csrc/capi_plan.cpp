@@ -48,6 +48,8 @@ ll_status check_weights(const ll_weights& w, int i, int32_t fmt0) {
     if (!aligned(w.codes, 16)) return ll::failf(LL_EALIGN, "ll_gemv_plan: item %d: codes must be 16-byte aligned", i);
     if (w.fmt == LL_FMT_I2S) {
         if (w.K % 128) return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: i2_s needs K %% 128 == 0", i);
+        if (w.K > (int64_t(1) << 20))
+            return ll::failf(LL_ERANGE, "ll_gemv_plan: item %d: i2_s needs K <= 2^20 (exact int32 sums)", i);
     } else if (w.fmt == LL_FMT_TQ2_0) {
         if (w.K % 256) return ll::failf(LL_ESHAPE, "ll_gemv_plan: item %d: TQ2_0 needs K %% 256 == 0", i);
         if (!w.scales) return ll::failf(LL_EINVAL, "ll_gemv_plan: item %d: TQ2_0 scales pointer is NULL", i);

@@ -100,6 +100,9 @@ typedef enum {
  *   LL_FMT_W1  : codes  = uint32 [N, K/32] sign bits (ll_pack_w1);
  *                scales = fp16 [N, K/group].  K % 32 == 0, K % group == 0.
  * group: W1 scale group size G (> 0, multiple of 32); ignored otherwise.
+ * Every device entry point takes 1 <= N < 2^31 and 1 <= K <= 2^24, and i2_s
+ * K <= 2^20 (its products keep exact int32 sums of whole rows; larger K is
+ * LL_ERANGE).
  */
 typedef struct {
     int32_t fmt;         /* ll_format */

@@ -261,6 +261,24 @@ def _item_i8(N, K, xq, y, group=128, fmt=None, xs=None, bias=None):
                              C.c_void_p(y))
 
 
+def test_i2s_rows_longer_than_2_20_are_rejected():
+    """i2_s products keep whole-row sums in int32, so every device entry point
+    refuses K > 2^20 on the host (LL_ERANGE) and accepts K = 2^20 as far as
+    validation goes (the byte-size check of a plan)."""
+    lib = L.lib()
+    big = _w(N=64, K=(1 << 20) + 128)
+    assert _gemv(big) == -7
+    assert _gemv(big, act=L.LL_ACT_I8) == -7
+    assert lib.ll_bitlinear_gemm(C.byref(big), C.c_void_p(FAKE), C.c_void_p(FAKE), 32, None, C.c_void_p(FAKE), None,
+                                 C.c_void_p(FAKE), 1 << 30, None) == -7
+    plan = L.ll_gemv_plan()
+    arr = (L.ll_gemv_item * 1)(_item(64, (1 << 20) + 128, FAKE, FAKE))
+    assert lib.ll_gemv_plan_bytes(arr, 1, L.LL_ACT_F32, 1) == 2 ** 64 - 1
+    assert lib.ll_gemv_plan_init(arr, 1, L.LL_ACT_F32, 1, None, 0, C.byref(plan)) == -7
+    ok = (L.ll_gemv_item * 1)(_item(64, 1 << 20, FAKE, FAKE))
+    assert lib.ll_gemv_plan_bytes(ok, 1, L.LL_ACT_F32, 1) != 2 ** 64 - 1
+
+
 def test_plan_i8_layout_and_validation():
     """Host-only: a W1A8 plan holds one prepared operand per distinct (xq, K)
     (A digit rows of K / 128 chunks x 2M rows x 128 B, then M x K / 128
