@@ -195,9 +195,9 @@ static hipError_t run_gemm(const ll_weights* w, const int8_t* xq, const float* x
 
 // Data-region bytes of the product ll_bitlinear_gemm runs (0: no workspace).
 static size_t gemm_data_bytes(const ll_weights* w, int64_t M) {
-    if (w1_mfma(w, M)) return llk::gemm_i8_workspace(M, w->N, w->K);
+    if (w1_mfma(w, M)) return llk::gemm_i8_workspace(M, w->N, w->K, LL_FMT_W1);
     if (w->fmt == LL_FMT_W1) return llk::w1_workspace(M, w->N, w->K, w->group);
-    return llk::gemm_i8_workspace(M, w->N, w->K);
+    return llk::gemm_i8_workspace(M, w->N, w->K, w->fmt);
 }
 
 size_t ll_gemm_workspace_size(const ll_weights* w, int64_t M) {

@@ -99,7 +99,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).  XSUM (i2_s):
 // the per-token sums of q come in xsum (from the quantization) instead of
 // being summed here.  y16: bf16 output written instead of y, or NULL.
-template <int FMT, bool XSUM = false, int WV = 4>
+template <int FMT, bool XSUM = false, int WV = 4, int BNT = BN>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                              const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
@@ -115,7 +115,9 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // wave tiles 64 x 32
     constexpr int TH = 64 * WV;                            // threads
     constexpr int WNW = WV / 2;                            // waves along N
-    constexpr int NB = BN / (32 * WNW);                    // 32-column blocks per wave
+    constexpr int NB = BNT / (32 * WNW);                   // 32-column blocks per wave
+    static_assert(NB >= 1 && NB * 32 * WNW == BNT, "tile width: whole 32-column blocks per wave");
+    constexpr int64_t kPart = int64_t(BM) * BNT;           // ints of one partial tile
     constexpr int CA = BM * 8 / TH;                        // 16-byte activation chunks per thread and group
     constexpr int WC = 32 * NB;                            // columns per wave
     const int tid = threadIdx.x, lane = tid & 63;
@@ -127,12 +129,12 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // (b % 8) T8 + b / 8, so consecutive logical workgroups (the splits and
     // row tiles of one column tile, which read the same weight codes) share
     // one XCD's L2.
-    const int64_t T = ((N + BN - 1) / BN) * TM * S, T8 = (T + 7) / 8;
+    const int64_t T = ((N + BNT - 1) / BNT) * TM * S, T8 = (T + 7) / 8;
     const int64_t L = LL_GEMM_XCD ? (int64_t(blockIdx.x) % 8) * T8 + int64_t(blockIdx.x) / 8 : int64_t(blockIdx.x);
     if (L >= T) return;                                    // whole workgroup, before any barrier
     const int64_t tile = L / S;
     const int split = int(L % S);
-    const int64_t m0 = (tile % TM) * BM, n0 = (tile / TM) * BN;
+    const int64_t m0 = (tile % TM) * BM, n0 = (tile / TM) * BNT;
     const int64_t rowbytes = FMT == 3 ? K / 8 : K / 4;
     const int64_t ng = K / 128;
     // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
@@ -487,7 +489,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         // Publish this split's partial tile (device-coherent stores), wait for
         // them, count the split in; the split that arrives last reads the
         // others' partials (device-coherent loads) and finishes the tile.
-        int32_t* mine = part + (tile * S + split) * int64_t(kTileInts);
+        int32_t* mine = part + (tile * S + split) * kPart;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -504,7 +506,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         if constexpr (FMT == 1) {
             for (int s = 0; s < S; ++s) {
                 if (s == split) continue;
-                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+                const int32_t* other = part + (tile * S + s) * kPart;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -523,7 +525,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
                     for (int r = 0; r < 16; ++r) tot[mb][nb][r] = 0.0f;
             for (int s = 0; s < S; ++s) {
-                const int32_t* other = part + (tile * S + s) * int64_t(kTileInts);
+                const int32_t* other = part + (tile * S + s) * kPart;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -577,7 +579,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * WC + li;
     if (y16) {
         uint16_t* yl16 = y16 + lrow * N + lcol;
-        if (m0 + BM <= M && n0 + BN <= N) {
+        if (m0 + BM <= M && n0 + BNT <= N) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -600,7 +602,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         return;
     }
     float* yl = y + lrow * N + lcol;
-    if (m0 + BM <= M && n0 + BN <= N) {
+    if (m0 + BM <= M && n0 + BNT <= N) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -638,40 +640,61 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 // keep their fp32 block sums as well and are sized for one.
 #define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
 
-template <bool XSUM, int WV>
+template <bool XSUM, int WV, int BNT>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                  const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                  float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
                                  int32_t* __restrict__ part, int32_t* __restrict__ counters,
                                  const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
-    gemm_i8_body<1, XSUM, WV>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+    gemm_i8_body<1, XSUM, WV, BNT>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
-template <int WV>
+template <int WV, int BNT>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4))) gemm_i8_w1_kernel(
     const uint8_t* __restrict__ bits, const uint16_t* __restrict__ scales, int64_t N, int64_t K,
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
     float* __restrict__ y, int S, int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
-    gemm_i8_body<3, false, WV>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
+    gemm_i8_body<3, false, WV, BNT>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
-template <int WV>
+template <int WV, int BNT>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4))) gemm_i8_tq2_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N, int64_t K,
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
     float* __restrict__ y, int S, int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
-    gemm_i8_body<2, false, WV>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
+    gemm_i8_body<2, false, WV, BNT>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
 #ifndef LL_GEMM_SLOTS
 #define LL_GEMM_SLOTS 256
 #endif
+#ifndef LL_GEMM_NARROW
+#define LL_GEMM_NARROW 1
+#endif
+// Tile width: 128 x 128 tiles of eight waves, or, for an i2_s product whose
+// 128 x 128 tiles would leave half the chip idle (K would be split), 128 x 64
+// tiles of four waves (one per SIMD, the same 64 x 32 wave tiles), split
+// further only where those still leave the chip half idle.  Measured at
+// M = 512: 2560 x 6912 23.7 -> 21.4 us, 2560 x 2560 18.3 -> 10.9 us; at
+// M = 64 .. 256 16-30% faster.  The block-scaled formats keep the wide
+// tiles: their extra vector work per group needs the second wave per SIMD
+// (TQ2_0 2560 x 6912 at M = 512: 26.1 us wide, 30.8 us narrow).
+int gemm_bn(int64_t M, int64_t N, bool narrow_ok) {
+    const int64_t TM = (M + BM - 1) / BM;
+    const bool narrow = LL_GEMM_NARROW && narrow_ok && TM * ((N + BN - 1) / BN) * 2 <= LL_GEMM_SLOTS &&
+                        TM * ((N + BN / 2 - 1) / (BN / 2)) <= LL_GEMM_SLOTS;
+    return narrow ? BN / 2 : BN;
+}
+int64_t gemm_tiles(int64_t M, int64_t N, bool narrow_ok) {
+    const int64_t bn = gemm_bn(M, N, narrow_ok);
+    return ((M + BM - 1) / BM) * ((N + bn - 1) / bn);
+}
 // Split count: enough workgroups to cover the chip (LL_GEMM_SLOTS resident
 // workgroups) without leaving a split fewer than four groups (two TQ2_0
 // blocks: splits keep whole blocks), and at most one counter per tile in
 // the counter region.
-int gemm_splits(int64_t M, int64_t N, int64_t K, bool allow = true) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow = true) {
+    const int64_t tiles = gemm_tiles(M, N, narrow_ok);
     if (!allow || tiles > kMaxCounters) return 1;
     const int64_t ng = K / 128;
     int64_t s = 1;
@@ -693,43 +716,52 @@ hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, int threads, hipStrea
 
 namespace llk {
 
-size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K) {
-    const int S = gemm_splits(M, N, K);
+size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K, int fmt) {
+    const bool narrow_ok = fmt == 1;
+    const int S = gemm_splits(M, N, K, narrow_ok);
     if (S == 1) return 0;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    return size_t(tiles) * S * kTileInts * 4;
+    return size_t(gemm_tiles(M, N, narrow_ok)) * S * size_t(BM) * size_t(gemm_bn(M, N, narrow_ok)) * 4;
 }
 
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq, const float* xs,
                               int64_t M, const float* bias, float* y, int32_t* acc_out, int32_t* counters, void* ws,
                               hipStream_t stream, const int32_t* xsum, uint16_t* y16) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    const int64_t tiles = gemm_tiles(M, N, true);
+    const int S = gemm_splits(M, N, K, true, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_I2S_WAVES;
+    int32_t* part = static_cast<int32_t*>(ws);
+    if (gemm_bn(M, N, true) != BN) {
+        if (xsum)
+            return launch_tiles(gemm_i8_i2s_kernel<true, 4, BN / 2>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias,
+                                y, acc_out, S, part, counters, xsum, y16);
+        return launch_tiles(gemm_i8_i2s_kernel<false, 4, BN / 2>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias, y,
+                            acc_out, S, part, counters, xsum, y16);
+    }
     if (xsum)
-        return launch_tiles(gemm_i8_i2s_kernel<true, WV>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
-                            acc_out, S, static_cast<int32_t*>(ws), counters, xsum, y16);
-    return launch_tiles(gemm_i8_i2s_kernel<false, WV>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
-                        acc_out, S, static_cast<int32_t*>(ws), counters, xsum, y16);
+        return launch_tiles(gemm_i8_i2s_kernel<true, WV, BN>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
+                            acc_out, S, part, counters, xsum, y16);
+    return launch_tiles(gemm_i8_i2s_kernel<false, WV, BN>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
+                        acc_out, S, part, counters, xsum, y16);
 }
 
 hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                              const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                              hipStream_t stream, uint16_t* y16) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    const int64_t tiles = gemm_tiles(M, N, false);
+    const int S = gemm_splits(M, N, K, false, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_BLOCK_WAVES;
-    return launch_tiles(gemm_i8_w1_kernel<WV>, tiles, S, 64 * WV, stream, reinterpret_cast<const uint8_t*>(bits), scales, N, K, xq,
-                        xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
+    const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
+    return launch_tiles(gemm_i8_w1_kernel<WV, BN>, tiles, S, 64 * WV, stream, b8, scales, N, K, xq, xs, M, bias, y, S,
+                        static_cast<int32_t*>(ws), counters, y16);
 }
 
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                               hipStream_t stream, uint16_t* y16) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int S = gemm_splits(M, N, K, ws != nullptr && counters != nullptr);
+    const int64_t tiles = gemm_tiles(M, N, false);
+    const int S = gemm_splits(M, N, K, false, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_BLOCK_WAVES;
-    return launch_tiles(gemm_i8_tq2_kernel<WV>, tiles, S, 64 * WV, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
+    return launch_tiles(gemm_i8_tq2_kernel<WV, BN>, tiles, S, 64 * WV, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
                         static_cast<int32_t*>(ws), counters, y16);
 }
 

@@ -73,7 +73,7 @@ hipError_t launch_w1_batch_product(const void* prob_table, const void* map, int6
 // int8-activation prefill product, format i2_s.  ws: gemm_i8_workspace bytes
 // of split-K partial tiles and counters one per output tile (zero on entry,
 // left zero), or NULL (either) to forbid splits.
-size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K);
+size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K, int fmt);   // fmt: 1 i2_s, 2 TQ2_0, 3 W1
 // xsum: sum_k q per token from the quantization (then the kernel skips its
 // own row sums), or NULL; y16: bf16 output [M,N] written instead of y, or NULL.
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq,

@@ -3,8 +3,8 @@ scratch) against ll_bitlinear_gemm with its own zero-filled workspace, bit
 for bit (the fp32 paths run the same kernels in the same order, so their
 bits agree too), through the C ABI, on calls in a row that leave the
 scratch holding the previous call's contents:
-  1. i2_s 2560 x 6912 at M = 512: split K three ways (partial tiles and
-     counters in the scratch), acc_out too;
+  1. i2_s 2560 x 6912 at M = 256: 128 x 64 tiles split K three ways
+     (partial tiles and counters in the scratch), acc_out too;
   2. i2_s 300 x 2048 at M = 200, smaller: four splits, other tile counts;
   3. W1 with G = 64 at M = 40: passes of 16 tokens whose prepared operands
      live in the scratch;
@@ -45,7 +45,7 @@ def _pair(W, q, s, M, N, want_acc):
 
 def test_noalloc_matches_workspace_product():
     # 1: large split-K i2_s product
-    N, K, M = 2560, 6912, 512
+    N, K, M = 2560, 6912, 256
     _, _, packed = make_i2s(402, N, K)
     W = L.upload_i2s(packed, N, K)
     q, s = oracle.quantize_bf16(synth.normal_bf16_bits(9500, M, K))
