@@ -26,9 +26,11 @@
 // Then sum_k w x = 2 * sum_k (c/2) X - sum_k X, with sum_k X formed by the
 // preparation.  TQ2_0 codes are turned into signed e2m1 halves (+-0.5 as
 // 0001 / 1001) by moving the code's high bit to the nibble's sign bit, and
-// each 256-k block's MFMA sum is multiplied by the block's fp16 scale.
-// Every MFMA sum is exact in fp32 (multiples of 1/2 below 2^23); the
-// epilogue weights the planes by 8^(11-r) in fp64.
+// each 256-k block's MFMA sum is multiplied by the block's fp16 scale (one
+// token: into fp32 plane accumulators; several tokens: a lane first folds
+// its four plane sums exactly, then adds the scaled fold in fp64).  Every
+// MFMA sum is exact in fp32 (multiples of 1/2 below 2^23); the epilogue
+// weights the planes by 8^(11-r) in fp64.
 //
 // Layout and parallelism.  MFMA lane l holds row (or column) l % 16 and the
 // 32 k values 32 (l/16) + e of a 128-k step.  The 16 bytes of a weight row at
@@ -385,6 +387,14 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
         r = r < N ? r : N - 1;
         srow[cb] = scales + r * nch;
     }
+    // Several tokens: thread tid fetches pieces of one token, ttok = tid /
+    // TPT, the pieces tin + TPT p (p < APer) of that token's KG chunks.
+    constexpr int TPT = MT > 1 ? kThreads / MT : kThreads;
+    constexpr int PPT = KG * (kChunkBytes / 16);           // 16-byte pieces per token and group
+    static_assert(MT == 1 || (PPT % TPT == 0 && PPT / TPT == C::APer), "pieces per thread");
+    const int ttok = MT > 1 ? tid / TPT : 0, tin = MT > 1 ? tid % TPT : 0;
+    const uint8_t* tokops = P.ops + int64_t(m0 + ttok < P.M ? m0 + ttok : P.M - 1) * P.opstride;   // tokens past M: unused
+    const uint32_t ab = uint32_t(abytes);
     // Every load is issued by every lane from an in-bounds (clamped) address;
     // bytes past the end of a row are zeroed when stored to LDS.
     auto load = [&](int g, Regs<FMT, MT>& r) {
@@ -401,12 +411,8 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
                 o = o < abytes ? o : abytes - 16;
                 r.a[p] = ld16(P.ops + o);
             } else {
-                int m = m0 + pc / (KG * (kChunkBytes / 16));
-                const int within = pc % (KG * (kChunkBytes / 16));
-                m = m < P.M ? m : P.M - 1;                 // tokens past M: any in-bounds bytes (unused)
-                int64_t o = int64_t(gc) * (KG * kChunkBytes) + 16 * within;
-                o = o < abytes ? o : abytes - 16;
-                r.a[p] = ld16(P.ops + int64_t(m) * P.opstride + o);
+                const uint32_t o = uint32_t(gc) * (KG * kChunkBytes) + 16 * (tin + TPT * p);
+                r.a[p] = ld16(tokops + __builtin_elementwise_min(o, ab - 16));   // both multiples of 16
             }
         }
         if (FMT == 2) {
@@ -417,6 +423,32 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
         }
     };
     auto store = [&](int g, const Regs<FMT, MT>& r) {
+        if constexpr (MT > 1) {
+            // a group inside the row (every group but a partial last one) is stored as loaded
+            char* win = abuf + (g & 1) * C::AWin + 16 * (ttok * PPT + tin);
+            if (uint32_t(g + 1) * (KG * kChunkBytes) <= ab && uint32_t(g + 1) * (KG * 64) <= rowbytes) {
+#pragma unroll
+                for (int j = 0; j < C::NLD; ++j)
+                    *reinterpret_cast<i32x4*>(wtile + (C::RPI * j + lr) * C::WStride + 16 * lp) = r.w[j];
+#pragma unroll
+                for (int p = 0; p < C::APer; ++p) *reinterpret_cast<i32x4*>(win + 16 * TPT * p) = r.a[p];
+            } else {
+                const bool ok = uint32_t(g) * (KG * 64) + 16 * lp < rowbytes;
+#pragma unroll
+                for (int j = 0; j < C::NLD; ++j)
+                    *reinterpret_cast<i32x4*>(wtile + (C::RPI * j + lr) * C::WStride + 16 * lp) = ok ? r.w[j] : i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int p = 0; p < C::APer; ++p) {
+                    const bool aok = uint32_t(g) * (KG * kChunkBytes) + 16 * (tin + TPT * p) < ab;
+                    *reinterpret_cast<i32x4*>(win + 16 * TPT * p) = aok ? r.a[p] : i32x4{0, 0, 0, 0};
+                }
+            }
+            if (FMT == 2 && q < KG)
+#pragma unroll
+                for (int cb = 0; cb < kCB; ++cb)
+                    *reinterpret_cast<uint16_t*>(wtile + (16 * cb + nl) * C::WStride + KG * 64 + 2 * q) = r.sc[cb];
+            return;
+        }
         const bool ok = uint32_t(g) * (KG * 64) + 16 * lp < rowbytes;
 #pragma unroll
         for (int j = 0; j < C::NLD; ++j)
@@ -439,11 +471,21 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
     uint64_t cscp[kCB];
     auto scale_of = [&](int c, int cb) { return half_bits_to_float(uint16_t(cscp[cb] >> (16 * c))); };
 
-    f32x4 acc[MT][kCB];
+    // TQ2_0 with several tokens: per block, a lane folds its four plane sums
+    // (rows 4q + i, weighted 8^(3 - i); exact in fp32: multiples of 1/2
+    // below 2^20) and adds the block-scaled fold into one fp64 accumulator
+    // per token and column block (the product of an fp16 scale and the fold
+    // is exact in fp64), so the result carries no rounding but that of x
+    constexpr bool kFold = FMT == 2 && MT > 1;
+    f32x4 acc[kFold ? 1 : MT][kCB];
+    double facc[kFold ? MT : 1][kCB];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int cb = 0; cb < kCB; ++cb) {
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) acc[m][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int m = 0; m < (kFold ? 1 : MT); ++m) acc[m][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < (kFold ? MT : 1); ++m) facc[m][cb] = 0.0;
+    }
     // rows kPl..15 of the operand are weighted 0 in the epilogue: they read
     // rows 0..3 of the quarter, so no two lanes of an 8-lane LDS phase share
     // an address
@@ -495,23 +537,50 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
                     mma(acc[0][cb], a0, a1, b0, b1, FMT == 2 ? scale_of(c, cb) : 0.0f);
                 }
             } else {
-                // the weight tile is decoded once and multiplied by every token's block
+                // the weight tile is decoded once and multiplied by every
+                // token's block; token m + 1's operands are read while token m
+                // multiplies, and (TQ2_0) token m's block sums are folded
+                // while token m + 1's products run
                 i32x4 b0[kCB], b1[kCB];
-                float sb[kCB];
+                double sb[kCB];
 #pragma unroll
                 for (int cb = 0; cb < kCB; ++cb) {
                     const i32x4 u4 = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * C::WStride + 64 * c + 16 * q);
                     decode(u4, b0[cb], b1[cb]);
-                    sb[cb] = FMT == 2 ? scale_of(c, cb) : 0.0f;
+                    sb[cb] = FMT == 2 ? double(scale_of(c, cb)) : 0.0;
                 }
+                i32x4 a[2][2];
+                f32x4 blk[2][kCB];
+                auto read_tok = [&](int m, i32x4 (&o)[2]) {
+                    const char* am = ap + m * (KG * kChunkBytes);
+                    o[0] = *reinterpret_cast<const i32x4*>(am);
+                    o[1] = *reinterpret_cast<const i32x4*>(am + kStepBytes);
+                };
+                auto fold = [&](int m, const f32x4 (&bk)[kCB]) {
+#pragma unroll
+                    for (int cb = 0; cb < kCB; ++cb) {
+                        const float t = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(bk[cb][0], 8.0f, bk[cb][1]), 8.0f, bk[cb][2]), 8.0f, bk[cb][3]);
+                        facc[m][cb] = __builtin_fma(sb[cb], double(t), facc[m][cb]);
+                    }
+                };
+                read_tok(0, a[0]);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const char* am = ap + m * (KG * kChunkBytes);
-                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(am);
-                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(am + kStepBytes);
+                    if (m + 1 < MT) read_tok(m + 1, a[(m + 1) & 1]);
 #pragma unroll
-                    for (int cb = 0; cb < kCB; ++cb) mma(acc[m][cb], a0, a1, b0[cb], b1[cb], sb[cb]);
+                    for (int cb = 0; cb < kCB; ++cb) {
+                        if constexpr (kFold) {
+                            blk[m & 1][cb] = mfma_f4(a[m & 1][0], b0[cb], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                            blk[m & 1][cb] = mfma_f4(a[m & 1][1], b1[cb], blk[m & 1][cb]);
+                        } else {
+                            acc[m][cb] = mfma_f4(a[m & 1][0], b0[cb], acc[m][cb]);
+                            acc[m][cb] = mfma_f4(a[m & 1][1], b1[cb], acc[m][cb]);
+                        }
+                    }
+                    if constexpr (kFold)
+                        if (m > 0) fold(m - 1, blk[(m - 1) & 1]);
                 }
+                if constexpr (kFold) fold(MT - 1, blk[(MT - 1) & 1]);
             }
         }
     };
@@ -575,11 +644,16 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
             double t = 0.0;
+            if constexpr (kFold) {
+                // the fold of quarter q (planes 4q .. 4q + 3) weighs 2 * 8^(8 - 4q); quarter 3 holds no plane
+                t = q < 3 ? facc[m][cb] * ldexp(1.0, 25 - 12 * q) : 0.0;
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * q + i;
-                const double wgt = r < kPl ? ldexp(1.0, 1 + 3 * (kPl - 1 - r)) : 0.0;
-                t = fma(double(acc[m][cb][i]), wgt, t);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * q + i;
+                    const double wgt = r < kPl ? ldexp(1.0, 1 + 3 * (kPl - 1 - r)) : 0.0;
+                    t = fma(double(acc[m][cb][i]), wgt, t);
+                }
             }
             t += __shfl_xor(t, 16, kWave);
             t += __shfl_xor(t, 32, kWave);

@@ -737,6 +737,27 @@ def test_plan_k_limit_of_the_fp4_engine():
         assert ok, "K=%d: worst error / bound %.3f" % (K, worst)
 
 
+def test_tq2_plan_longest_rows_several_tokens():
+    """TQ2_0 rows of K = 2^17 (the fp4 engine's limit) for three tokens: one
+    large element among small ones keeps sum|x| close to max|x|, and 512
+    block-scaled sums per row are accumulated; the result stays inside the
+    bound (the block sums are folded exactly and added in fp64)."""
+    t = torch()
+    N, K, M = 40, 1 << 17, 3
+    _, _, blocks = make_tq2(9300, N, K)
+    x = _x(9301, M, K) * np.float32(1e-3)
+    x[:, 7] = np.float32(9.0)
+    W = L.upload_tq2(blocks, N, K)
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    plan = L.GemvPlan([(W, t.from_numpy(x).cuda(), None, y)], M)
+    announce("tq2 plan longest rows", N, K, M)
+    plan.run()
+    t.cuda.synchronize()
+    y_ref, tsum = oracle.tq2_gemv_f32(blocks, N, K, x, threads=TH)
+    ok, worst = f32_tol_ok(y.cpu().numpy(), y_ref, tsum)
+    assert ok, "worst error / bound %.3f" % worst
+
+
 # ------------------------------------------------------------------ single calls: extreme activations
 @pytest.mark.parametrize("fmt,M", [("i2s", 1), ("i2s", 2), ("i2s", 5), ("tq2", 1), ("tq2", 3)])
 def test_gemv_f32_single_call_extreme_x(fmt, M):
