@@ -52,6 +52,12 @@
 // multiply and a mask and mapped to -1 / +1 by a byte permute.  Every group
 // is a scale block.
 //
+// Halves along K.  A narrow tile (128 x 64) may run eight waves as two
+// halves of four: half h multiplies the h-th half of the tile's groups from
+// LDS buffers of its own, every barrier is met by both halves (equal group
+// counts), and at the end half 1 hands its exact int32 sums to half 0
+// through LDS, which adds them and writes the tile.
+//
 // Split K.  With few output tiles (N = 2560 at M = 512 gives 80) the
 // workgroups of a tile split its groups S ways.  Each split writes its
 // partial tile to the workspace and counts itself in at the tile's counter
@@ -99,7 +105,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).  XSUM (i2_s):
 // the per-token sums of q come in xsum (from the quantization) instead of
 // being summed here.  y16: bf16 output written instead of y, or NULL.
-template <int FMT, bool XSUM = false, int WV = 4, int BNT = BN>
+template <int FMT, bool XSUM = false, int WV = 4, int BNT = BN, int KH = 1>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                              const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
@@ -109,20 +115,24 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
     __shared__ __attribute__((aligned(16))) float xs_tile[BM];   // token scales of the tile's rows
-    __shared__ __attribute__((aligned(16))) int32_t qsum_tile[BM];  // i2_s: sum_k q of the tile's rows
+    __shared__ __attribute__((aligned(16))) int32_t qsum_tile[KH][BM];  // i2_s: sum_k q of the tile's rows (per half)
     // WV = 4: one wave per SIMD, wave tiles 64 x 64; WV = 8: two waves per
     // SIMD (one's vector work runs while the other's matrix products do),
-    // wave tiles 64 x 32
+    // wave tiles 64 x 32; KH = 2: two halves of WV / 2 waves along K
+    static_assert(KH == 1 || (KH == 2 && FMT == 1 && LL_GEMM_I2S_SETS == 1), "halves along K: i2_s, one accumulator set");
     constexpr int TH = 64 * WV;                            // threads
-    constexpr int WNW = WV / 2;                            // waves along N
+    constexpr int THH = TH / KH;                           // threads of one half
+    constexpr int WNW = WV / KH / 2;                       // waves along N
     constexpr int NB = BNT / (32 * WNW);                   // 32-column blocks per wave
     static_assert(NB >= 1 && NB * 32 * WNW == BNT, "tile width: whole 32-column blocks per wave");
     constexpr int64_t kPart = int64_t(BM) * BNT;           // ints of one partial tile
-    constexpr int CA = BM * 8 / TH;                        // 16-byte activation chunks per thread and group
+    constexpr int CA = BM * 8 / THH;                       // 16-byte activation chunks per thread and group
     constexpr int WC = 32 * NB;                            // columns per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w / WNW, wn = w % WNW;                  // rows 64 wm, columns WC wn of the tile
+    const int kh = KH == 1 ? 0 : w / (WV / KH);            // the half this wave belongs to
+    const int htid = tid % THH;                            // thread index within the half
+    const int wm = (w % (WV / KH)) / WNW, wn = (w % (WV / KH)) % WNW;   // rows 64 wm, columns WC wn of the tile
     const int li = lane & 31, h = lane >> 5;
     const int64_t TM = (M + BM - 1) / BM;
     // Hardware workgroup b runs on XCD b % 8; it takes logical index
@@ -139,7 +149,9 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t ng = K / 128;
     // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
     const int64_t nsplit_units = FMT != 2 ? ng : K / 256, per_unit = FMT != 2 ? 1 : 2;
-    const int64_t g0 = per_unit * (nsplit_units * split / S), g1 = per_unit * (nsplit_units * (split + 1) / S);
+    const int64_t gs0 = per_unit * (nsplit_units * split / S), gs1 = per_unit * (nsplit_units * (split + 1) / S);
+    // this half's groups (the launcher makes the count divisible by KH)
+    const int64_t g0 = gs0 + kh * ((gs1 - gs0) / KH), g1 = g0 + (gs1 - gs0) / KH;
 
     // Activation loads of one group: CA 16-byte chunks per thread, chunk
     // idx = tid + TH c is row idx / 8, bytes 16 (idx % 8) of the group;
@@ -147,7 +159,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int8_t* arow[CA];
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
-        const int idx = tid + TH * c;
+        const int idx = htid + THH * c;
         int64_t m = m0 + (idx >> 3);
         m = m < M ? m : M - 1;
         arow[c] = xq + m * K + 16 * (idx & 7);
@@ -183,11 +195,12 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // i2_s: this thread's share of sum_k q of its CA rows (idx / 8), summed
     // from the chunks it stores (v_dot4 against 1)
     int32_t qs[CA] = {};
+    int8_t* const lds_h = lds + kh * 2 * kBuf;             // this half's two buffers
     auto store_a = [&](int buf, const Stage& s) {
-        int8_t* A = lds + buf * kBuf;
+        int8_t* A = lds_h + buf * kBuf;
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
-            const int idx = tid + TH * c;
+            const int idx = htid + THH * c;
             int8_t* arow_l = &A[(idx >> 3) * LDA];
             if constexpr (FMT == 1 && !XSUM)
 #pragma unroll
@@ -213,7 +226,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     };
     // activation operands of step t (rows wm 64 + mb 32 + li, k 32 t + 16 h)
     auto read_a = [&](int buf, int t, i32x4 (&ao)[2]) {
-        const int8_t* A = lds + buf * kBuf + (wm * 64 + li) * LDA + 32 * t + 16 * h;
+        const int8_t* A = lds_h + buf * kBuf + (wm * 64 + li) * LDA + 32 * t + 16 * h;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) ao[mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA);
     };
@@ -258,7 +271,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     if (tid < BM) {
         const int64_t m = m0 + tid;
         xs_tile[tid] = xs[m < M ? m : M - 1];
-        if constexpr (XSUM) qsum_tile[tid] = xsum[m < M ? m : M - 1];
+        if constexpr (XSUM) qsum_tile[0][tid] = xsum[m < M ? m : M - 1];
     }
     const float sw = FMT == 1 ? *reinterpret_cast<const float*>(codes + N * rowbytes) : 1.0f;
     const float* bsrc = bias ? bias : xs;                 // always a valid address
@@ -452,15 +465,39 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             for (int c = 0; c < CA; ++c) {
 #pragma unroll
                 for (int o = 1; o < 8; o <<= 1) qs[c] += __shfl_xor(qs[c], o, kWave);
-                if ((tid & 7) == 0) qsum_tile[(tid >> 3) + (TH / 8) * c] = qs[c];
+                if ((htid & 7) == 0) qsum_tile[kh][(htid >> 3) + (THH / 8) * c] = qs[c];
             }
         }
-        __syncthreads();
+        if constexpr (KH == 2) {
+            // every wave is past its last LDS operand read; half 1's sums go
+            // through the (now free) activation buffers to half 0, which
+            // finishes the tile alone (no barrier follows: S = 1)
+            __syncthreads();
+            int32_t* xch = reinterpret_cast<int32_t*>(lds) + (w % (WV / KH)) * (2 * NB * 16 * 64) + lane;
+            if (kh == 1)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) xch[((mb * NB + nb) * 16 + r) * 64] = acc[mb][nb][r];
+            __syncthreads();
+            if (kh == 1) return;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mb][nb][r] += xch[((mb * NB + nb) * 16 + r) * 64];
+        } else {
+            __syncthreads();
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+                i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[0][wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+                if constexpr (KH == 2 && !XSUM) q4 += *reinterpret_cast<const i32x4*>(&qsum_tile[1][wm * 64 + mb * 32 + 8 * rq + 4 * h]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -558,7 +595,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) xsv[mb][4 * rq + e] = v[e];
             if constexpr (FMT == 1 && XSUM) {
-                const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[wm * 64 + mb * 32 + 8 * rq + 4 * h]);
+                const i32x4 q4 = *reinterpret_cast<const i32x4*>(&qsum_tile[0][wm * 64 + mb * 32 + 8 * rq + 4 * h]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -640,13 +677,13 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 // keep their fp32 block sums as well and are sized for one.
 #define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
 
-template <bool XSUM, int WV, int BNT>
+template <bool XSUM, int WV, int BNT, int KH = 1>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                  const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                  float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
                                  int32_t* __restrict__ part, int32_t* __restrict__ counters,
                                  const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
-    gemm_i8_body<1, XSUM, WV, BNT>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+    gemm_i8_body<1, XSUM, WV, BNT, KH>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
 template <int WV, int BNT>
@@ -671,6 +708,9 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV
 #ifndef LL_GEMM_NARROW
 #define LL_GEMM_NARROW 1
 #endif
+#ifndef LL_GEMM_HALVES
+#define LL_GEMM_HALVES 1
+#endif
 // Tile width: 128 x 128 tiles of eight waves, or, for an i2_s product whose
 // 128 x 128 tiles would leave half the chip idle (K would be split), 128 x 64
 // tiles of four waves (one per SIMD, the same 64 x 32 wave tiles), split
@@ -678,7 +718,10 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV
 // M = 512: 2560 x 6912 23.7 -> 21.4 us, 2560 x 2560 18.3 -> 10.9 us; at
 // M = 64 .. 256 16-30% faster.  The block-scaled formats keep the wide
 // tiles: their extra vector work per group needs the second wave per SIMD
-// (TQ2_0 2560 x 6912 at M = 512: 26.1 us wide, 30.8 us narrow).
+// (TQ2_0 2560 x 6912 at M = 512: 26.1 us wide, 30.8 us narrow).  A narrow
+// i2_s tile with K unsplit and an even group count runs eight waves as two
+// halves along K (2560 x 6912 at M = 512: 21.4 -> 19.8 us); the tile still
+// reads a 16 KiB activation tile per 128-k group for only 64 columns.
 int gemm_bn(int64_t M, int64_t N, bool narrow_ok) {
     const int64_t TM = (M + BM - 1) / BM;
     const bool narrow = LL_GEMM_NARROW && narrow_ok && TM * ((N + BN - 1) / BN) * 2 <= LL_GEMM_SLOTS &&
@@ -703,13 +746,17 @@ int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow = tr
 }
 
 template <typename Kern, typename... Args>
-hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, int threads, hipStream_t stream, Args... args) {
+hipError_t launch_tiles_lds(Kern kernel, int64_t tiles, int S, int threads, size_t lds, hipStream_t stream, Args... args) {
     const int64_t T = tiles * S;
     const dim3 grid{unsigned(LL_GEMM_XCD ? (T + 7) / 8 * 8 : T)}, block{unsigned(threads)};
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kernel), kGemmLds);
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kernel), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, grid, block, kGemmLds, stream, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
     return hipGetLastError();
+}
+template <typename Kern, typename... Args>
+hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, int threads, hipStream_t stream, Args... args) {
+    return launch_tiles_lds(kernel, tiles, S, threads, kGemmLds, stream, args...);
 }
 
 }  // namespace
@@ -731,6 +778,15 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     constexpr int WV = LL_GEMM_I2S_WAVES;
     int32_t* part = static_cast<int32_t*>(ws);
     if (gemm_bn(M, N, true) != BN) {
+        // narrow tiles: eight waves as two halves along K where the halves
+        // get equal group counts and K is not split over workgroups
+        if (LL_GEMM_HALVES && S == 1 && (K / 128) % 2 == 0) {
+            if (xsum)
+                return launch_tiles_lds(gemm_i8_i2s_kernel<true, 8, BN / 2, 2>, tiles, S, 512, 2 * kGemmLds, stream, codes, N,
+                                        K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+            return launch_tiles_lds(gemm_i8_i2s_kernel<false, 8, BN / 2, 2>, tiles, S, 512, 2 * kGemmLds, stream, codes, N,
+                                    K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+        }
         if (xsum)
             return launch_tiles(gemm_i8_i2s_kernel<true, 4, BN / 2>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias,
                                 y, acc_out, S, part, counters, xsum, y16);
