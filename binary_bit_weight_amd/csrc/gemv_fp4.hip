@@ -337,7 +337,7 @@ struct F4Cfg {
     static constexpr int CB = f4_cb(FMT, MT);                    // 16-row column blocks per wave
     static constexpr int WaveRows = 16 * CB;
     static constexpr int WgRows = kWaves * WaveRows;
-    static constexpr int KG = MT <= 2 ? 4 : 2;
+    static constexpr int KG = MT <= 2 ? 4 : MT <= 8 ? 2 : 1;
     static constexpr int WStride = KG * 64 + 16;                 // padded LDS tile row
     static constexpr int WTile = 16 * CB * WStride;              // one wave's tile
     static constexpr int AWin = MT * KG * kChunkBytes;           // one group's digits, all tokens
@@ -687,6 +687,9 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
 #ifndef LL_F4_OCC
 #define LL_F4_OCC 3
 #endif
+#ifndef LL_F4_TQ2_MT16
+#define LL_F4_TQ2_MT16 1                               // TQ2_0, 9 .. 16 tokens: one pass of sixteen
+#endif
 #ifndef LL_F4_OCC_TQ2
 #define LL_F4_OCC_TQ2 3
 #endif
@@ -694,7 +697,7 @@ __device__ __forceinline__ void f4_rows(const F4Prob& P, const uint8_t* __restri
 #define LL_F4_OCC_TQ2_MT4 2
 #endif
 __host__ __device__ constexpr int f4_occ(int FMT, int MT) {
-    return MT == 8 || MT == 2 ? 2 : MT == 4 ? (FMT == 2 ? LL_F4_OCC_TQ2_MT4 : 3) : FMT == 2 ? LL_F4_OCC_TQ2 : LL_F4_OCC;
+    return MT >= 8 || MT == 2 ? 2 : MT == 4 ? (FMT == 2 ? LL_F4_OCC_TQ2_MT4 : 3) : FMT == 2 ? LL_F4_OCC_TQ2 : LL_F4_OCC;
 }
 
 // grid: 8 * ceil(T / 8) workgroups for T logical ones; hardware workgroup w
@@ -761,7 +764,7 @@ int64_t f4_op_stride(int64_t K) { return (op_bytes(K) + 255) / 256 * 256; }
 size_t f4_operand_bytes(int64_t M, int64_t K) { return size_t(M * f4_op_stride(K)); }
 // the launch variant launch_f4_fmt picks for M tokens: its rows per workgroup
 int64_t f4_batch_rows(bool pair, int fmt, int64_t M) {
-    const int mt = M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8;
+    const int mt = M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : M <= 8 || fmt != 2 || !LL_F4_TQ2_MT16 ? 8 : 16;
     const int64_t rows = kWaves * 16 * f4_cb(fmt, mt);
     return pair ? rows / 2 : rows;
 }
@@ -818,14 +821,17 @@ hipError_t launch_f4_product(const F4Prob* t, const int32_t* m, int64_t T, int p
     return hipGetLastError();
 }
 
-// M = 9 .. 16 runs as two passes of eight tokens (measured faster than one
-// pass of sixteen, which leaves one wave per SIMD).
+// M = 9 .. 16: i2_s runs two passes of eight tokens (sixteen f32x4 plane
+// accumulators per column block would leave one wave per SIMD); TQ2_0, whose
+// folded fp64 accumulators take two registers per token, one pass of sixteen
+// with 256-k groups (6912 x 2560 batch at M = 16: 461 -> 431 us).
 template <int FMT>
 hipError_t launch_f4_fmt(const F4Prob* t, const int32_t* m, int64_t T, bool pairs, int64_t M, hipStream_t stream) {
     if (M == 1)
         return pairs ? launch_f4_product<FMT, true, 1>(t, m, T, 1, stream) : launch_f4_product<FMT, false, 1>(t, m, T, 1, stream);
     if (M == 2) return launch_f4_product<FMT, false, 2>(t, m, T, 1, stream);
     if (M <= 4) return launch_f4_product<FMT, false, 4>(t, m, T, 1, stream);
+    if (FMT == 2 && LL_F4_TQ2_MT16 && M > 8) return launch_f4_product<FMT, false, 16>(t, m, T, 1, stream);
     return launch_f4_product<FMT, false, 8>(t, m, T, M <= 8 ? 1 : 2, stream);
 }
 

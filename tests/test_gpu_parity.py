@@ -698,7 +698,7 @@ def test_workspace_shared_across_shapes_and_entry_points():
 @pytest.mark.parametrize("M", [1, 8, 16])
 def test_tq2_plan_full(M):
     """TQ2_0 6912 x 2560 as a prepared batch (the fp4 engine, all M tokens in
-    one pass over the weights; two passes at M = 16), every output."""
+    one pass over the weights), every output."""
     t = torch()
     N, K = 6912, 2560
     _, _, blocks = make_tq2(301, N, K)
