@@ -12,13 +12,16 @@
 // every step exact in fp32.  The planes are rows of the MFMA operand A.
 // Weights.  Codes are fed as c = w + 1 in {0, 1, 2} (i2_s codes as they are;
 // TQ2_0 codes c' = w mod 4 remapped by c = ((b0 ^ b1) << 1) | !b0 on the
-// packed word), so sum w*q = sum c*q - sum q, with the plane sums sum q
-// computed once per token.  A code is not shifted down to bit 0 of its
-// byte: masked in place it is the int8 value c * 4^j (j < 3), so three of
-// the four fields of a word cost one AND each; the MFMAs of each field
-// accumulate separately and are divided by their exact power of two at the
-// end.  Every product and sum is an exact integer in int32; the epilogue
-// forms
+// packed word), so sum w*q = sum c*q - sum q.  i2_s: the plane sums sum q
+// come once per token from the preparation; a code is not shifted down to
+// bit 0 of its byte: masked in place it is the int8 value c * 4^j (j < 3), so
+// three of the four fields of a word cost one AND each; the MFMAs of each
+// field accumulate separately over the row and are divided by their exact
+// power of two at the end.  TQ2_0: every field is moved to bits 4..5 (the
+// value 16 c), so the four MFMAs of a 256-k block chain into one
+// accumulator, and the block's plane sums come from four more MFMAs against
+// an all-ones operand; the fp64 block scale takes the factor 1/16.  Every
+// product and sum is an exact integer in int32; the epilogue forms
 //     y = scale * 2^(E-6) * sum_p 128^-p (acc_p - xsum_p)
 // in fp64 (exact up to the final roundings), so the only deviation from the
 // exact product is the plane truncation r: |y - y_exact| <=
@@ -65,7 +68,7 @@ constexpr int kWStride = kWinB + 16;      // padded LDS weight row
 constexpr int kWTile = 16 * kWStride;     // one wave's weight tile
 constexpr int kAStride = kWinK + 16;      // padded LDS plane row
 
-__host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * (kP * M * kAStride + 256); }
+__host__ __device__ inline int lds_bytes(int M) { return kWaves * kWTile + 2 * kP * M * kAStride; }
 
 // Fused form of a single product (M = 1, K <= kFusedMaxK): every workgroup
 // builds the planes of the whole row in its LDS (no preparation launch), then
@@ -80,17 +83,18 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int64_t kFusedMaxK = LL_PLANES_FUSED ? 8192 : 0;
 constexpr int kXIt = 8192 / (4 * kThreads);          // float4 of x per thread
 __host__ __device__ inline int fused_astride(int64_t K) { return int((K + 255) / 256 * 256 + 16); }
+// i2_s: each wave's plane sums (TQ2_0 forms its block sums in the product)
 __host__ __device__ inline int fused_sums(int64_t K) {
-    return kP * int((K + 255) / 256) > kWaves * kP ? kP * int((K + 255) / 256) : kWaves * kP;
+    (void)K;
+    return kWaves * kP;
 }
 __host__ __device__ inline int fused_lds_bytes(int64_t K) {
     return kWaves * kWTile + kP * fused_astride(K) + 4 * fused_sums(K) + 4 * kWaves;
 }
 
-// Position of element k inside its 256-element TQ2_0 block in the plane
-// layout: field f = k%4 of byte 16q + 4v + b (k = 64q + 16v + 4b + f) goes to
-// 64f + 16q + 4v + b, so one MFMA (one field) reads 16 consecutive bytes.
-__device__ __forceinline__ int tq2_pos(int e) { return 64 * (e & 3) + 16 * (e >> 6) + 4 * ((e >> 4) & 3) + ((e >> 2) & 3); }
+// TQ2_0 plane layout: element 4m + f of a 256-element block (field f of
+// code byte m) goes to byte 64 f + m of the block, so one MFMA (one field)
+// reads 16 consecutive bytes.
 
 // The product multiplies up to kPassM tokens at a time (5 x 3 = 15 plane
 // rows fill one 16-row MFMA operand); larger M runs several passes.
@@ -98,26 +102,22 @@ constexpr int kPassM = 3;
 __host__ __device__ inline int64_t npass(int64_t M) { return (M + kPassM - 1) / kPassM; }
 
 // Workspace layout of one activation:
-//     planes [5M][K] | xsum [npass][nblk4][16] | E [M] | xtot [5M] (per row),
-// xsum[pass][b][5j + p] the sum of plane row 5m + p (m = 3 pass + j) over
-// 256-k block b, blocks padded to a multiple of 4 (one 1024-k window = one
-// 256-byte piece per pass).
+//     planes [5M][K] | E [M] | xtot [5M] (i2_s: each plane row's sum over
+// the row).  TQ2_0's per-block plane sums are formed by the product itself
+// (MFMAs against an all-ones operand).
 struct PlaneView {
     int8_t* planes;
-    int32_t* xsum;
     int32_t* ex;
     int32_t* xtot;
 };
-__host__ __device__ inline int64_t nblk4(int64_t K) { return (K + 1023) / 1024 * 4; }
 __host__ __device__ inline size_t planes_bytes(int64_t M, int64_t K) {
-    return size_t((kP * M * K + 15) / 16 * 16 + npass(M) * nblk4(K) * 64 + M * 4 + kP * M * 4 + 15) / 16 * 16;
+    return size_t((kP * M * K + 15) / 16 * 16 + M * 4 + kP * M * 4 + 15) / 16 * 16;
 }
 __host__ __device__ inline PlaneView plane_view(const void* base, int64_t M, int64_t K) {
     char* p = static_cast<char*>(const_cast<void*>(base));
     PlaneView v;
     v.planes = reinterpret_cast<int8_t*>(p);
-    v.xsum = reinterpret_cast<int32_t*>(p + (kP * M * K + 15) / 16 * 16);
-    v.ex = v.xsum + npass(M) * nblk4(K) * 16;
+    v.ex = reinterpret_cast<int32_t*>(p + (kP * M * K + 15) / 16 * 16);
     v.xtot = v.ex + M;
     return v;
 }
@@ -125,19 +125,20 @@ __host__ __device__ inline PlaneView plane_view(const void* base, int64_t M, int
 __host__ __device__ inline PlaneView pass_view(const PlaneView& v, int pass, int64_t K) {
     PlaneView u;
     u.planes = v.planes + int64_t(kP * kPassM) * pass * K;
-    u.xsum = v.xsum + int64_t(pass) * nblk4(K) * 16;
     u.ex = v.ex + kPassM * pass;
     u.xtot = v.xtot + kP * kPassM * pass;
     return u;
 }
 
 // ---------------------------------------------------------------- activation preparation
-// One workgroup of 256 threads per token.  Thread t holds elements
-// 4t + 1024i + [0, 4) (float4 loads, all issued before any use), so the
-// 256-k block 4i + wave is held by exactly one wave and its plane sums are
-// wave reductions; the row maximum costs one barrier.  Rows are processed
-// in chunks of kPrepK elements (registers), the maximum over all chunks
-// first.
+// One workgroup of 256 threads per token; float4 loads, all issued before
+// any use.  i2_s: thread t holds elements 4t + 1024i + [0, 4) and sums its
+// digits per plane (one wave reduction per plane at the end).  TQ2_0: each
+// thread holds 16 consecutive elements per four float4s, so its digits of
+// one field are four consecutive bytes of the block's transposed layout (one
+// dword store per plane and field).  The row maximum costs one barrier.
+// Rows are processed in chunks of kPrepK elements (registers), the maximum
+// over all chunks first.
 constexpr int kPrepIt = 8;                           // float4 per thread per chunk
 constexpr int kPrepK = 1024 * kPrepIt;               // elements per chunk
 
@@ -148,15 +149,18 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
     __shared__ int stot[4][kP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const PlaneView v = plane_view(ws, M, K);
-    int tot[kP] = {0, 0, 0, 0, 0};                   // this wave's share of the row's plane sums
-    const int64_t nblk = (K + 255) / 256;
-    // K % 128 == 0 (both formats), so k < K implies k + 3 < K.  (A scalar
-    // fallback here would turn these into FLAT loads, each waiting for the
-    // previous one.)
+    int tot[kP] = {0, 0, 0, 0, 0};                   // i2_s: this thread's share of the row's plane sums
+    // first element of float4 i of a chunk
+    auto kof = [&](int64_t k0, int i) -> int64_t {
+        return FMT == 1 ? k0 + 1024 * i + 4 * tid : k0 + 4096 * (i / 4) + 16 * tid + 4 * (i % 4);
+    };
+    // K % 128 == 0 (both formats; TQ2_0: % 256), so k < K implies k + 3 < K.
+    // (A scalar fallback here would turn these into FLAT loads, each waiting
+    // for the previous one.)
     auto load_chunk = [&](int64_t k0, f32x4 (&x4)[kPrepIt]) {
 #pragma unroll
         for (int i = 0; i < kPrepIt; ++i) {
-            const int64_t k = k0 + 1024 * i + 4 * tid;
+            const int64_t k = kof(k0, i);
             x4[i] = k < K ? ld16f(xr + k) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
@@ -186,12 +190,40 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
         } else {
             load_chunk(k0, x4);                      // L2-resident re-read
         }
-        int s[kPrepIt * kP];                         // per 1024-k slice: this thread's part of the block sums
+        if constexpr (FMT == 2) {
+            // element 4m + f of a 256-k block goes to byte 64 f + m of its plane row
 #pragma unroll
-        for (int e = 0; e < kPrepIt * kP; ++e) s[e] = 0;
+            for (int g = 0; g < kPrepIt / 4; ++g) {
+                const int64_t kg = kof(k0, 4 * g);
+                if (kg >= K) break;
+                uint32_t d[kP][4] = {};              // plane p, field f: four digits
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float xv[4] = {x4[4 * g + i].x, x4[4 * g + i].y, x4[4 * g + i].z, x4[4 * g + i].w};
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        float r = a > 0.0f ? ldexpf(xv[f], 6 - E) : 0.0f;
+#pragma unroll
+                        for (int p = 0; p < kP; ++p) {
+                            const float qp = __builtin_rintf(r);
+                            d[p][f] |= uint32_t(uint8_t(int(qp))) << (8 * i);
+                            r = __fmul_rn(__fsub_rn(r, qp), 128.0f);
+                        }
+                    }
+                }
+                const int64_t base = kg - (kg & 255) + ((kg & 255) >> 2);
+#pragma unroll
+                for (int p = 0; p < kP; ++p) {
+                    int8_t* row = v.planes + int64_t(m * kP + p) * K;
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) *reinterpret_cast<uint32_t*>(row + base + 64 * f) = d[p][f];
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int i = 0; i < kPrepIt; ++i) {
-            const int64_t kb = k0 + 1024 * i;        // this wave's block: kb/256 + wave
+            const int64_t kb = k0 + 1024 * i;
             if (kb >= K) break;
             const int64_t k = kb + 4 * tid;
             const float xv[4] = {x4[i].x, x4[i].y, x4[i].z, x4[i].w};
@@ -210,37 +242,23 @@ __device__ __forceinline__ void prep_token(const float* __restrict__ xr, int64_t
 #pragma unroll
                 for (int p = 0; p < kP; ++p) {
                     int8_t* row = v.planes + int64_t(m * kP + p) * K;
-                    if (FMT == 1) {
-                        const uint32_t packed = uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
-                                                uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
-                        *reinterpret_cast<uint32_t*>(row + k) = packed;
-                    } else {
-                        const int64_t base = k - (k & 255);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) row[base + tq2_pos(int((k + j) & 255))] = int8_t(q[j][p]);
-                    }
+                    const uint32_t packed = uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
+                                            uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
+                    *reinterpret_cast<uint32_t*>(row + k) = packed;
                 }
             }
 #pragma unroll
-            for (int p = 0; p < kP; ++p) s[i * kP + p] = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
-        }
-        wave_sum_n(s);                               // all slices at once: six permute waits
-#pragma unroll
-        for (int i = 0; i < kPrepIt; ++i) {
-            const int64_t b = (k0 + 1024 * i) / 256 + wave;
-#pragma unroll
-            for (int p = 0; p < kP; ++p) {
-                if (lane == 0 && b < nblk)
-                    v.xsum[(m / kPassM) * nblk4(K) * 16 + b * 16 + (m % kPassM) * kP + p] = s[i * kP + p];
-                tot[p] += s[i * kP + p];
-            }
+            for (int p = 0; p < kP; ++p) tot[p] += (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
         }
     }
-    if (lane == 0)
+    if constexpr (FMT == 1) {
+        wave_sum_n(tot);
+        if (lane == 0)
 #pragma unroll
-        for (int p = 0; p < kP; ++p) stot[wave][p] = tot[p];
-    __syncthreads();
-    if (tid < kP) v.xtot[m * kP + tid] = stot[0][tid] + stot[1][tid] + stot[2][tid] + stot[3][tid];
+            for (int p = 0; p < kP; ++p) stot[wave][p] = tot[p];
+        __syncthreads();
+        if (tid < kP) v.xtot[m * kP + tid] = stot[0][tid] + stot[1][tid] + stot[2][tid] + stot[3][tid];
+    }
 }
 
 template <int FMT>
@@ -261,11 +279,17 @@ template <int FMT>
 __device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K, int8_t* __restrict__ A, int astride,
                                           int* __restrict__ sums, float* __restrict__ smax) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nblk = int((K + 255) / 256);
+    // float4 i of this thread: elements k(i) .. k(i) + 3; i2_s: k(i) = 1024 i
+    // + 4 tid; TQ2_0: 16 consecutive elements per thread and four float4s,
+    // k(i) = 4096 (i / 4) + 16 tid + 4 (i % 4), so a thread's digits of one
+    // field are four consecutive bytes of the block's transposed layout
+    auto kof = [&](int i) -> int64_t {
+        return FMT == 1 ? int64_t(4 * kThreads * i + 4 * tid) : int64_t(16 * kThreads * (i / 4) + 16 * tid + 4 * (i % 4));
+    };
     f32x4 xv[kXIt];
 #pragma unroll
     for (int i = 0; i < kXIt; ++i) {
-        const int64_t k = 4 * kThreads * i + 4 * tid;  // K % 128 == 0: k < K implies k + 3 < K
+        const int64_t k = kof(i);                      // K % 128 == 0: k < K implies k + 3 < K
         xv[i] = k < K ? ld16f(x + k) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float a = 0.0f;
@@ -280,10 +304,39 @@ __device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K
     for (int v = 1; v < kWaves; ++v) a = fmaxf(a, smax[v]);
     int E = 0;
     if (a > 0.0f) (void)frexpf(a, &E);                // 2^(E-1) <= a < 2^E
-    int tot[kP] = {0, 0, 0, 0, 0};
-    int bs[kXIt * kP];                                // TQ2_0: this thread's part of each block sum
+    if constexpr (FMT == 2) {
+        // element 4m + f of a 256-k block goes to byte 64 f + m of its plane
+        // row; the block sums of the planes are formed by the product
 #pragma unroll
-    for (int e = 0; e < kXIt * kP; ++e) bs[e] = 0;
+        for (int g = 0; g < kXIt / 4; ++g) {
+            const int64_t k0 = kof(4 * g);
+            if (k0 >= K) break;
+            uint32_t d[kP][4] = {};                    // plane p, field f: four digits
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float xe[4] = {xv[4 * g + i].x, xv[4 * g + i].y, xv[4 * g + i].z, xv[4 * g + i].w};
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    float r = a > 0.0f ? ldexpf(xe[f], 6 - E) : 0.0f;
+#pragma unroll
+                    for (int p = 0; p < kP; ++p) {
+                        const float qp = __builtin_rintf(r);
+                        d[p][f] |= uint32_t(uint8_t(int(qp))) << (8 * i);
+                        r = __fmul_rn(__fsub_rn(r, qp), 128.0f);
+                    }
+                }
+            }
+            const int m0 = int(k0 & 255) >> 2;            // 4-element index of the thread's first element
+#pragma unroll
+            for (int p = 0; p < kP; ++p)
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    *reinterpret_cast<uint32_t*>(A + p * astride + (k0 & ~int64_t(255)) + 64 * f + m0) = d[p][f];
+        }
+        (void)sums;
+        return E;
+    }
+    int tot[kP] = {0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < kXIt; ++i) {
         const int64_t kb = 4 * kThreads * i;
@@ -303,43 +356,18 @@ __device__ __forceinline__ int fused_prep(const float* __restrict__ x, int64_t K
         }
         if (k < K) {
 #pragma unroll
-            for (int p = 0; p < kP; ++p) {
-                int8_t* row = A + p * astride;
-                if (FMT == 1) {
-                    *reinterpret_cast<uint32_t*>(row + k) =
-                        uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
-                        uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) row[(k & ~255) + tq2_pos((k + j) & 255)] = int8_t(q[j][p]);
-                }
-            }
-        }
-        int s4[kP];
-#pragma unroll
-        for (int p = 0; p < kP; ++p) s4[p] = (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
-#pragma unroll
-        for (int p = 0; p < kP; ++p) {
-            if (FMT == 1) tot[p] += s4[p];
-            else bs[i * kP + p] = s4[p];
-        }
-    }
-    if (FMT == 2) {
-        wave_sum_n(bs);
-#pragma unroll
-        for (int i = 0; i < kXIt; ++i) {
-            const int b = kWaves * i + wave;
-#pragma unroll
             for (int p = 0; p < kP; ++p)
-                if (lane == 0 && b < nblk) sums[p * nblk + b] = bs[i * kP + p];
+                *reinterpret_cast<uint32_t*>(A + p * astride + k) =
+                    uint32_t(uint8_t(q[0][p])) | uint32_t(uint8_t(q[1][p])) << 8 |
+                    uint32_t(uint8_t(q[2][p])) << 16 | uint32_t(uint8_t(q[3][p])) << 24;
         }
-    }
-    if (FMT == 1) {
-        wave_sum_n(tot);
 #pragma unroll
-        for (int p = 0; p < kP; ++p)
-            if (lane == 0) sums[wave * kP + p] = tot[p];
+        for (int p = 0; p < kP; ++p) tot[p] += (q[0][p] + q[1][p]) + (q[2][p] + q[3][p]);
     }
+    wave_sum_n(tot);
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+        if (lane == 0) sums[wave * kP + p] = tot[p];
     return E;
 }
 
@@ -354,6 +382,14 @@ __device__ __forceinline__ uint32_t field(uint32_t u, int t) {
     if (bit == 4) return u & 0x30303030u;          // c * 16
     if (bit == 2) return u & 0x0C0C0C0Cu;          // c * 4
     return u & 0x03030303u;                        // c
+}
+// TQ2_0 field t (bits 2t) moved to bits 4..5 of every byte: 16 c for all t,
+// so the four steps of a 256-k block chain into one accumulator
+__device__ __forceinline__ uint32_t field16(uint32_t u, int t) {
+    if (t == 0) return (u << 4) & 0x30303030u;
+    if (t == 1) return (u << 2) & 0x30303030u;
+    if (t == 2) return u & 0x30303030u;
+    return (u >> 2) & 0x30303030u;
 }
 template <int FMT>
 __host__ __device__ constexpr int field_mul(int t) {
@@ -402,7 +438,7 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     const PlaneView pv = pvw;
     char* wtile = lds + wave * kWTile;                  // private to this wave
     int8_t* abuf = reinterpret_cast<int8_t*>(lds + kWaves * kWTile);
-    constexpr int abytes = RR * kAStride + 256;          // planes, then the window's block sums
+    constexpr int abytes = RR * kAStride;                // one window of plane rows
     const int astride = WHOLE ? fused_astride(K) : kAStride;
     int* fsums = reinterpret_cast<int*>(abuf + kP * fused_astride(K));           // fused only
     float* fsmax = reinterpret_cast<float*>(fsums + fused_sums(K));
@@ -427,7 +463,6 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
     struct Regs {
         i32x4 w[4 * kLPR];
         i32x4 a[kAChunks];
-        i32x4 xs;                                          // TQ2_0: block sums of the window (16 B per thread)
         uint16_t sc[kWinK / 256];                          // TQ2_0: scales of this lane's row
     };
     uint16_t csc[kWinK / 256];                             // scales of the window being multiplied
@@ -462,7 +497,6 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 const int64_t k = int64_t(w) * kWinK + 16 * col;
                 r.a[i] = ld16(pv.planes + int64_t(row < rlast ? row : rlast) * K + (k < K ? k : K - 16));
             }
-            if (FMT == 2 && !INT8) r.xs = ld16(pv.xsum + 64 * (live ? w : nwin - 1) + 4 * (tid & 15));
         }
         if (FMT == 2) {
 #pragma unroll
@@ -511,7 +545,6 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                 *reinterpret_cast<i32x4*>(dst + 16 * col) = v;
             }
         }
-        if (FMT == 2 && !INT8 && tid < 16) *reinterpret_cast<i32x4*>(abuf + (w & 1) * abytes + RR * kAStride + 16 * tid) = r.xs;
     };
 
     i32x4 acc[4];                                        // i2_s: one accumulator per field
@@ -543,37 +576,40 @@ __device__ __forceinline__ void planes_rows(const uint8_t* __restrict__ codes, c
                     u[j] = int((v ^ ((v & 0x55555555u) << 1)) ^ 0x55555555u);
                 }
             }
-            i32x4 bacc[4];
+            // i2_s: four accumulators (fields weighted 16, 16, 4, 1) over the
+            // whole row; TQ2_0: one accumulator per block, 16 times the dot
+            i32x4 bacc[FMT == 2 ? 1 : 4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 i32x4 b;
+                if constexpr (FMT == 2) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = int(field<FMT>(uint32_t(u[j]), t));
-                bacc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, FMT == 2 ? i32x4{0, 0, 0, 0} : acc[t], 0, 0, 0);
+                    for (int j = 0; j < 4; ++j) b[j] = int(field16(uint32_t(u[j]), t));
+                    bacc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, t == 0 ? i32x4{0, 0, 0, 0} : bacc[0], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = int(field<FMT>(uint32_t(u[j]), t));
+                    bacc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, acc[t], 0, 0, 0);
+                }
             }
-            i32x4 bsum = i32x4{0, 0, 0, 0};               // kInt8: sum q of this segment (TQ2_0) or so far (i2_s)
-            if constexpr (INT8) {
+            i32x4 bsum = i32x4{0, 0, 0, 0};               // kInt8: sum q of this segment (TQ2_0) or so far (i2_s);
+                                                          // TQ2_0: each plane row's sum over this segment
+            if constexpr (INT8 || FMT == 2) {
                 const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
                 bsum = FMT == 2 ? bsum : qsum;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) bsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], ones, bsum, 0, 0, 0);
                 if (FMT == 1) qsum = bsum;
             }
-            if (FMT == 2) {
-                // C lane (column nl, quarter q) holds plane rows 4q..4q+3
-                const double sc = double(half_bits_to_float(csc[seg]));
+            if constexpr (FMT == 2) {
+                // C lane (column nl, quarter q) holds plane rows 4q..4q+3;
+                // (s / 16) (16 dot - 16 xs) = s (dot - xs) exactly
+                const double sc = double(half_bits_to_float(csc[seg])) * 0.0625;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * q + r;
-                    const int xs = row >= RR ? 0
-                                   : INT8  ? bsum[r]
-                                   : WHOLE ? fsums[row * nblk + s]
-                                           : *reinterpret_cast<const int*>(abuf + (w & 1) * abytes + RR * kAStride +
-                                                                           4 * (16 * seg + row));
-                    int dot = 0;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) dot += bacc[t][r] / field_mul<FMT>(t);
-                    dacc[r] = __builtin_fma(sc, double(dot - xs), dacc[r]);
+                    const int xs = row >= RR ? 0 : bsum[r];
+                    dacc[r] = __builtin_fma(sc, double(bacc[0][r] - 16 * xs), dacc[r]);
                 }
             } else {
 #pragma unroll
@@ -751,7 +787,7 @@ __global__ void __launch_bounds__(64 * kWaves) gemv_planes_i8_kernel(const uint8
                                                                       const float* __restrict__ bias,
                                                                       float* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const PlaneView pv{const_cast<int8_t*>(xq), nullptr, nullptr, nullptr};
+    const PlaneView pv{const_cast<int8_t*>(xq), nullptr, nullptr};
     planes_rows<FMT, MT, kInt8>(codes, scales, N, K, xq, pv, bias, y, int64_t(blockIdx.x) * kRows, lds, xs, M);
 }
 
@@ -835,7 +871,7 @@ template <int FMT, int MT>
 hipError_t launch_i8(const uint8_t* c, const uint16_t* s, int64_t N, int64_t K, const int8_t* xq, const float* xs,
                      int M, const float* bias, float* y, hipStream_t stream) {
     const dim3 grid{unsigned((N + kRows - 1) / kRows)}, block{64 * kWaves};
-    const size_t lds = size_t(kWaves * kWTile + 2 * (MT * kAStride + 256));
+    const size_t lds = size_t(kWaves * kWTile + 2 * MT * kAStride);
     hipError_t e = allow_lds(gemv_planes_i8_kernel<FMT, MT>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_planes_i8_kernel<FMT, MT>), grid, block, lds, stream, c, s, N, K, xq, xs, M, bias, y);

@@ -194,13 +194,12 @@ def test_binary_linear_arguments_and_workspace():
 
 def test_workspace_sizes():
     w = _w(N=6912, K=2560)
-    # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + block sums (16 ints per 256-k block, blocks
-    # padded to a multiple of 4) + exponents + row sums
-    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 2) == CB + (10 * 2560 + 12 * 64 + 8 + 10 * 4 + 15) // 16 * 16
+    # fp32 activations: int8 planes (M <= 3) = 5M*K bytes + exponents + row sums
+    assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 2) == CB + (10 * 2560 + 8 + 10 * 4 + 15) // 16 * 16
     # M = 1 with K <= 8192 builds the planes inside the product kernel
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 1) == 0
     w2 = _w(N=64, K=8320)
-    assert L.lib().ll_gemv_workspace_size(C.byref(w2), L.LL_ACT_F32, 1) == CB + (5 * 8320 + 36 * 64 + 4 + 5 * 4 + 15) // 16 * 16
+    assert L.lib().ll_gemv_workspace_size(C.byref(w2), L.LL_ACT_F32, 1) == CB + (5 * 8320 + 4 + 5 * 4 + 15) // 16 * 16
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 8) > 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_I8, 1) == 0
     assert L.lib().ll_gemv_workspace_size(C.byref(w), L.LL_ACT_F32, 17) == 2 ** 64 - 1
