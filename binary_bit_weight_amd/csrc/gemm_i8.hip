@@ -52,7 +52,9 @@
 // multiply and a mask and mapped to -1 / +1 by a byte permute.  Every group
 // is a scale block.
 //
-// Halves along K.  A narrow tile (128 x 64) may run eight waves as two
+// Narrow tiles.  Where 128 x 128 tiles would leave half the chip idle, an
+// i2_s product runs 64 x 128 tiles (64 tokens, 128 weight rows; one wave
+// along M).  Halves along K.  A narrow tile may run eight waves as two
 // halves of four: half h multiplies the h-th half of the tile's groups from
 // LDS buffers of its own, every barrier is met by both halves (equal group
 // counts), and at the end half 1 hands its exact int32 sums to half 0
@@ -75,14 +77,12 @@ namespace {
 using namespace llk;
 
 constexpr int BM = 128, BN = 128, LDA = 144;
-constexpr int kThreads = 256;                            // four waves, one per SIMD (TQ2_0, W1)
 #ifndef LL_GEMM_I2S_WAVES
 #define LL_GEMM_I2S_WAVES 8                              // i2_s: eight waves, two per SIMD
 #endif
 #ifndef LL_GEMM_BLOCK_WAVES
 #define LL_GEMM_BLOCK_WAVES 8                            // TQ2_0 and W1 (block-scaled sums)
 #endif
-constexpr int kTileInts = BM * BN;                       // one partial tile
 constexpr int kBuf = BM * LDA;                           // one LDS buffer: the activation tile of a group
 constexpr size_t kGemmLds = size_t(2) * kBuf;
 #ifndef LL_GEMM_XCD
@@ -105,7 +105,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // G = 128 (codes: the sign-bit words, scales: fp16 [N][K/128]).  XSUM (i2_s):
 // the per-token sums of q come in xsum (from the quantization) instead of
 // being summed here.  y16: bf16 output written instead of y, or NULL.
-template <int FMT, bool XSUM = false, int WV = 4, int BNT = BN, int KH = 1>
+template <int FMT, bool XSUM = false, int WV = 4, int BNT = BN, int KH = 1, int BMT = BM>
 __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                              int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                              const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
@@ -114,19 +114,21 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
                                              const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ int last_flag;
-    __shared__ __attribute__((aligned(16))) float xs_tile[BM];   // token scales of the tile's rows
-    __shared__ __attribute__((aligned(16))) int32_t qsum_tile[KH][BM];  // i2_s: sum_k q of the tile's rows (per half)
+    __shared__ __attribute__((aligned(16))) float xs_tile[BMT];   // token scales of the tile's rows
+    __shared__ __attribute__((aligned(16))) int32_t qsum_tile[KH][BMT];  // i2_s: sum_k q of the tile's rows (per half)
     // WV = 4: one wave per SIMD, wave tiles 64 x 64; WV = 8: two waves per
     // SIMD (one's vector work runs while the other's matrix products do),
     // wave tiles 64 x 32; KH = 2: two halves of WV / 2 waves along K
     static_assert(KH == 1 || (KH == 2 && FMT == 1 && LL_GEMM_I2S_SETS == 1), "halves along K: i2_s, one accumulator set");
+    static_assert(BMT == 128 || (BMT == 64 && FMT == 1), "tile rows: 128, or 64 (i2_s)");
     constexpr int TH = 64 * WV;                            // threads
     constexpr int THH = TH / KH;                           // threads of one half
-    constexpr int WNW = WV / KH / 2;                       // waves along N
+    constexpr int WNW = WV / KH / (BMT / 64);              // waves along N (BMT / 64 along M)
+    constexpr int kBufT = BMT * LDA;                       // one LDS buffer: the activation tile of a group
     constexpr int NB = BNT / (32 * WNW);                   // 32-column blocks per wave
     static_assert(NB >= 1 && NB * 32 * WNW == BNT, "tile width: whole 32-column blocks per wave");
-    constexpr int64_t kPart = int64_t(BM) * BNT;           // ints of one partial tile
-    constexpr int CA = BM * 8 / THH;                       // 16-byte activation chunks per thread and group
+    constexpr int64_t kPart = int64_t(BMT) * BNT;          // ints of one partial tile
+    constexpr int CA = BMT * 8 / THH;                      // 16-byte activation chunks per thread and group
     constexpr int WC = 32 * NB;                            // columns per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,7 +136,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int htid = tid % THH;                            // thread index within the half
     const int wm = (w % (WV / KH)) / WNW, wn = (w % (WV / KH)) % WNW;   // rows 64 wm, columns WC wn of the tile
     const int li = lane & 31, h = lane >> 5;
-    const int64_t TM = (M + BM - 1) / BM;
+    const int64_t TM = (M + BMT - 1) / BMT;
     // Hardware workgroup b runs on XCD b % 8; it takes logical index
     // (b % 8) T8 + b / 8, so consecutive logical workgroups (the splits and
     // row tiles of one column tile, which read the same weight codes) share
@@ -144,7 +146,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     if (L >= T) return;                                    // whole workgroup, before any barrier
     const int64_t tile = L / S;
     const int split = int(L % S);
-    const int64_t m0 = (tile % TM) * BM, n0 = (tile / TM) * BNT;
+    const int64_t m0 = (tile % TM) * BMT, n0 = (tile / TM) * BNT;
     const int64_t rowbytes = FMT == 3 ? K / 8 : K / 4;
     const int64_t ng = K / 128;
     // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
@@ -195,9 +197,9 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // i2_s: this thread's share of sum_k q of its CA rows (idx / 8), summed
     // from the chunks it stores (v_dot4 against 1)
     int32_t qs[CA] = {};
-    int8_t* const lds_h = lds + kh * 2 * kBuf;             // this half's two buffers
+    int8_t* const lds_h = lds + kh * 2 * kBufT;            // this half's two buffers
     auto store_a = [&](int buf, const Stage& s) {
-        int8_t* A = lds_h + buf * kBuf;
+        int8_t* A = lds_h + buf * kBufT;
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             const int idx = htid + THH * c;
@@ -226,7 +228,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     };
     // activation operands of step t (rows wm 64 + mb 32 + li, k 32 t + 16 h)
     auto read_a = [&](int buf, int t, i32x4 (&ao)[2]) {
-        const int8_t* A = lds_h + buf * kBuf + (wm * 64 + li) * LDA + 32 * t + 16 * h;
+        const int8_t* A = lds_h + buf * kBufT + (wm * 64 + li) * LDA + 32 * t + 16 * h;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) ao[mb] = *reinterpret_cast<const i32x4*>(A + mb * 32 * LDA);
     };
@@ -268,7 +270,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // epilogue operands, requested before the main loop so their latency is
     // hidden: the token scales of the tile's rows (into LDS, read back after
     // the loop), the weight scale, the biases of this lane's columns
-    if (tid < BM) {
+    if (tid < BMT) {
         const int64_t m = m0 + tid;
         xs_tile[tid] = xs[m < M ? m : M - 1];
         if constexpr (XSUM) qsum_tile[0][tid] = xsum[m < M ? m : M - 1];
@@ -616,7 +618,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     const int64_t lrow = m0 + wm * 64 + 4 * h, lcol = n0 + wn * WC + li;
     if (y16) {
         uint16_t* yl16 = y16 + lrow * N + lcol;
-        if (m0 + BM <= M && n0 + BNT <= N) {
+        if (m0 + BMT <= M && n0 + BNT <= N) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -639,7 +641,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         return;
     }
     float* yl = y + lrow * N + lcol;
-    if (m0 + BM <= M && n0 + BNT <= N) {
+    if (m0 + BMT <= M && n0 + BNT <= N) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -672,18 +674,16 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     }
 }
 
-// Register budgets: the i2_s kernel fits two waves per SIMD (two workgroups
-// share a CU once there are more tiles than CUs); the TQ2_0 and W1 kernels
-// keep their fp32 block sums as well and are sized for one.
-#define LL_GEMM_ATTRS(W) __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(W, W)))
+// Register budgets: two waves per SIMD (eight-wave workgroups, or two
+// four-wave workgroups on a CU once there are more tiles than CUs).
 
-template <bool XSUM, int WV, int BNT, int KH = 1>
+template <bool XSUM, int WV, int BNT, int KH = 1, int BMT = BM>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_i8_i2s_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K, const int8_t* __restrict__ xq,
                                  const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
                                  float* __restrict__ y, int32_t* __restrict__ acc_out, int S,
                                  int32_t* __restrict__ part, int32_t* __restrict__ counters,
                                  const int32_t* __restrict__ xsum, uint16_t* __restrict__ y16) {
-    gemm_i8_body<1, XSUM, WV, BNT, KH>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+    gemm_i8_body<1, XSUM, WV, BNT, KH, BMT>(codes, nullptr, N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
 }
 
 template <int WV, int BNT>
@@ -711,37 +711,60 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV
 #ifndef LL_GEMM_HALVES
 #define LL_GEMM_HALVES 1
 #endif
-// Tile width: 128 x 128 tiles of eight waves, or, for an i2_s product whose
-// 128 x 128 tiles would leave half the chip idle (K would be split), 128 x 64
-// tiles of four waves (one per SIMD, the same 64 x 32 wave tiles), split
-// further only where those still leave the chip half idle.  Measured at
-// M = 512: 2560 x 6912 23.7 -> 21.4 us, 2560 x 2560 18.3 -> 10.9 us; at
-// M = 64 .. 256 16-30% faster.  The block-scaled formats keep the wide
-// tiles: their extra vector work per group needs the second wave per SIMD
-// (TQ2_0 2560 x 6912 at M = 512: 26.1 us wide, 30.8 us narrow).  A narrow
-// i2_s tile with K unsplit and an even group count runs eight waves as two
-// halves along K (2560 x 6912 at M = 512: 21.4 -> 19.8 us); the tile still
-// reads a 16 KiB activation tile per 128-k group for only 64 columns.
-int gemm_bn(int64_t M, int64_t N, bool narrow_ok) {
-    const int64_t TM = (M + BM - 1) / BM;
-    const bool narrow = LL_GEMM_NARROW && narrow_ok && TM * ((N + BN - 1) / BN) * 2 <= LL_GEMM_SLOTS &&
-                        TM * ((N + BN / 2 - 1) / (BN / 2)) <= LL_GEMM_SLOTS;
-    return narrow ? BN / 2 : BN;
+#ifndef LL_GEMM_MAX_SPLITS
+#define LL_GEMM_MAX_SPLITS 4                             // the last split adds the others' partial tiles serially
+#endif
+#ifndef LL_GEMM_SPLIT_GROUPS
+#define LL_GEMM_SPLIT_GROUPS 10                          // 128-k groups a split keeps at least
+#endif
+#ifndef LL_GEMM_NARROW_ROWS
+#define LL_GEMM_NARROW_ROWS 64                           // narrow tiles: 64 x 128 (or 128 x 64)
+#endif
+// Tile shape: 128 x 128 tiles of eight waves, or, for an i2_s product
+// whose 128 x 128 tiles would leave half the chip idle (K would be split),
+// tiles of half the area: 64 tokens x 128 weight rows (four waves along N,
+// the same 64 x 32 wave tiles), split further only where those still leave
+// the chip half idle.  Against 128 x 128 split tiles: 2560 x 6912 at M = 512
+// 23.7 -> 21.4 us with 128 x 64 tiles, 2560 x 2560 18.3 -> 10.9 us.  The 64
+// x 128 shape reads half the activation bytes per group of the 128 x 64 one
+// for the same products (and each wave loads its own codes): 2560 x 6912 at
+// M = 512 19.8 -> 16.8 us, 2560 x 2560 11.2 -> 9.4 us.  The block-scaled
+// formats keep the wide tiles: their extra vector work per group needs the
+// second wave per SIMD (TQ2_0 2560 x 6912 at M = 512: 26.1 us wide, 30.8 us
+// with 128 x 64 tiles).  A narrow i2_s tile with K unsplit and an even group
+// count runs eight waves as two halves along K (21.4 -> 19.8 us with the
+// 128 x 64 shape).
+struct TileShape {
+    int bm, bn;
+};
+TileShape gemm_shape(int64_t M, int64_t N, bool narrow_ok) {
+    constexpr int nbm = LL_GEMM_NARROW_ROWS, nbn = BM * BN / 2 / LL_GEMM_NARROW_ROWS;
+    const int64_t wide = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const bool narrow = LL_GEMM_NARROW && narrow_ok && wide * 2 <= LL_GEMM_SLOTS &&
+                        ((M + nbm - 1) / nbm) * ((N + nbn - 1) / nbn) <= LL_GEMM_SLOTS;
+    return narrow ? TileShape{nbm, nbn} : TileShape{BM, BN};
+}
+bool gemm_narrow(int64_t M, int64_t N, bool narrow_ok) {
+    const TileShape t = gemm_shape(M, N, narrow_ok);
+    return t.bm != BM || t.bn != BN;
 }
 int64_t gemm_tiles(int64_t M, int64_t N, bool narrow_ok) {
-    const int64_t bn = gemm_bn(M, N, narrow_ok);
-    return ((M + BM - 1) / BM) * ((N + bn - 1) / bn);
+    const TileShape t = gemm_shape(M, N, narrow_ok);
+    return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
 }
 // Split count: enough workgroups to cover the chip (LL_GEMM_SLOTS resident
-// workgroups) without leaving a split fewer than four groups (two TQ2_0
-// blocks: splits keep whole blocks), and at most one counter per tile in
-// the counter region.
+// workgroups), at most four splits (the last one adds the others' partial
+// tiles one after another) of at least ten 128-k groups each (TQ2_0:
+// splits keep whole blocks), and at most one counter per tile in the
+// counter region.  Measured on 2560 x 6912 at M = 64: twelve splits 17.2
+// us, six 12.6, four 11.2; on 2560 x 2560 at M = 64 two splits beat four
+// (9.2 against 10.1 us).
 int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow = true) {
     const int64_t tiles = gemm_tiles(M, N, narrow_ok);
     if (!allow || tiles > kMaxCounters) return 1;
     const int64_t ng = K / 128;
     int64_t s = 1;
-    while (tiles * (s + 1) <= LL_GEMM_SLOTS && ng / (s + 1) >= 4) ++s;
+    while (s < LL_GEMM_MAX_SPLITS && tiles * (s + 1) <= LL_GEMM_SLOTS && ng / (s + 1) >= LL_GEMM_SPLIT_GROUPS) ++s;
     return int(s);
 }
 
@@ -767,7 +790,8 @@ size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K, int fmt) {
     const bool narrow_ok = fmt == 1;
     const int S = gemm_splits(M, N, K, narrow_ok);
     if (S == 1) return 0;
-    return size_t(gemm_tiles(M, N, narrow_ok)) * S * size_t(BM) * size_t(gemm_bn(M, N, narrow_ok)) * 4;
+    const TileShape t = gemm_shape(M, N, narrow_ok);
+    return size_t(gemm_tiles(M, N, narrow_ok)) * S * size_t(t.bm) * size_t(t.bn) * 4;
 }
 
 hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const int8_t* xq, const float* xs,
@@ -777,21 +801,23 @@ hipError_t launch_gemm_i8_i2s(const uint8_t* codes, int64_t N, int64_t K, const 
     const int S = gemm_splits(M, N, K, true, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_I2S_WAVES;
     int32_t* part = static_cast<int32_t*>(ws);
-    if (gemm_bn(M, N, true) != BN) {
-        // narrow tiles: eight waves as two halves along K where the halves
-        // get equal group counts and K is not split over workgroups
+    if (gemm_narrow(M, N, true)) {
+        // narrow tiles (half the area): eight waves as two halves along K
+        // where the halves get equal group counts and K is not split over
+        // workgroups, else four waves
+        constexpr int NBM = LL_GEMM_NARROW_ROWS, NBN = BM * BN / 2 / LL_GEMM_NARROW_ROWS;
         if (LL_GEMM_HALVES && S == 1 && (K / 128) % 2 == 0) {
             if (xsum)
-                return launch_tiles_lds(gemm_i8_i2s_kernel<true, 8, BN / 2, 2>, tiles, S, 512, 2 * kGemmLds, stream, codes, N,
-                                        K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
-            return launch_tiles_lds(gemm_i8_i2s_kernel<false, 8, BN / 2, 2>, tiles, S, 512, 2 * kGemmLds, stream, codes, N,
-                                    K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+                return launch_tiles_lds(gemm_i8_i2s_kernel<true, 8, NBN, 2, NBM>, tiles, S, 512, 2 * kGemmLds, stream, codes,
+                                        N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
+            return launch_tiles_lds(gemm_i8_i2s_kernel<false, 8, NBN, 2, NBM>, tiles, S, 512, 2 * kGemmLds, stream, codes,
+                                    N, K, xq, xs, M, bias, y, acc_out, S, part, counters, xsum, y16);
         }
         if (xsum)
-            return launch_tiles(gemm_i8_i2s_kernel<true, 4, BN / 2>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias,
-                                y, acc_out, S, part, counters, xsum, y16);
-        return launch_tiles(gemm_i8_i2s_kernel<false, 4, BN / 2>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias, y,
-                            acc_out, S, part, counters, xsum, y16);
+            return launch_tiles(gemm_i8_i2s_kernel<true, 4, NBN, 1, NBM>, tiles, S, 256, stream, codes, N, K, xq, xs, M,
+                                bias, y, acc_out, S, part, counters, xsum, y16);
+        return launch_tiles(gemm_i8_i2s_kernel<false, 4, NBN, 1, NBM>, tiles, S, 256, stream, codes, N, K, xq, xs, M, bias,
+                            y, acc_out, S, part, counters, xsum, y16);
     }
     if (xsum)
         return launch_tiles(gemm_i8_i2s_kernel<true, WV, BN>, tiles, S, 64 * WV, stream, codes, N, K, xq, xs, M, bias, y,
