@@ -173,9 +173,13 @@ def _i2s_i8_case(N, K, M, seed, rows=None, bias=False):
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
 
 
-# split K: (5, 2560, 300) 5 ways, (300, 2048, 200) 4, (64, 4096, 40) 8, (257, 1664, 130) 3 uneven ways
+# Tile paths (narrow 64 x 128 tiles unless noted): K split (5, 2560, 300) two ways, (150, 2688, 33) two
+# uneven ways, (64, 4096, 40) three uneven ways, (100, 5120, 70) four ways; two halves along K
+# (128, 256, 128), (200, 512, 17), (300, 2048, 200); four waves, odd group counts (77, 384, 65),
+# (130, 640, 129), (257, 1664, 130); wide 128 x 128 tiles with ragged rows and columns (1300, 384, 1500)
 @pytest.mark.parametrize("N,K,M", [(77, 384, 65), (128, 256, 128), (200, 512, 17), (33, 128, 1), (130, 640, 129),
-                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1664, 130)])
+                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1664, 130),
+                                   (100, 5120, 70), (150, 2688, 33), (1300, 384, 1500)])
 def test_i2s_gemm_i8_small(N, K, M):
     announce("i2s gemm i8", N, K, M)
     _i2s_i8_case(N, K, M, 600 + N + M, bias=(M == 65))
