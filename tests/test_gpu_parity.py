@@ -215,10 +215,12 @@ def _tq2_i8_case(N, K, M, seed, rows=None, bias=False, repeat=1):
     assert ok, "N=%d K=%d M=%d: worst error / bound %.3f" % (N, K, M, worst)
 
 
-# split K (whole 256-k blocks): (5, 2560, 300) 5 ways, (300, 2048, 200) 4, (64, 4096, 40) 8,
-# (257, 1792, 130) 3 uneven ways (2, 2, 3 blocks)
+# split K (whole 256-k blocks): (5, 2560, 300) two ways (5 + 5 blocks), (150, 2816, 33) two uneven ways
+# (5 + 6), (64, 4096, 40) three uneven ways (5 + 5 + 6), (64, 5376, 40) four uneven ways (5 + 5 + 5 + 6);
+# the others unsplit
 @pytest.mark.parametrize("N,K,M", [(77, 512, 65), (128, 256, 128), (200, 768, 17), (33, 256, 1), (130, 1280, 129),
-                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1792, 130)])
+                                   (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1792, 130),
+                                   (150, 2816, 33), (64, 5376, 40)])
 def test_tq2_gemm_i8_small(N, K, M):
     announce("tq2 gemm i8", N, K, M)
     _tq2_i8_case(N, K, M, 620 + N + M, bias=(M == 65), repeat=2 if K >= 1792 else 1)

@@ -79,10 +79,11 @@ def _w1_bound(scales, K, G, q, s, rows=None):
 
 
 # G = 128 above 16 tokens: the int8 matrix cores.  Ragged tiles, five groups
-# (K = 640), a bias, and split K: (5, 2560, 300) five ways, (64, 4096, 40)
-# eight, (300, 2048, 200) four, (257, 1664, 130) three uneven ways.
+# (K = 640), a bias, and split K: (5, 2560, 300) two ways, (64, 4096, 40)
+# three uneven ways (10 + 11 + 11 groups), (64, 5376, 40) four uneven ways;
+# (300, 2048, 200) and (257, 1664, 130) unsplit.
 @pytest.mark.parametrize("N,K,M", [(70, 1024, 40), (200, 640, 17), (130, 1280, 129), (5, 2560, 300), (64, 4096, 40),
-                                   (300, 2048, 200), (257, 1664, 130)])
+                                   (300, 2048, 200), (257, 1664, 130), (64, 5376, 40)])
 def test_w1a8_gemm_mfma_within_bound(N, K, M):
     G = 128
     bits, scales = make_w1(5600 + N, N, K, G)
