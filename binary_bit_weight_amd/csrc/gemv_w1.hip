@@ -569,7 +569,9 @@ __global__ void __launch_bounds__(64 * kW1Waves) __attribute__((amdgpu_waves_per
 // slots through the wave's own weight tile, which is free between the
 // block's last window and the next block's first.
 // LDS: [4 waves][32 rows][stride] tiles | [4 waves][32] fp32 biases |
-// A [K/128][R][kARow] | qs [M][K/G] int32 | padding | xs [M] fp32.  An A row
+// A [K/128][R][kARow] | qs [M][ngp] fp32 (group sums, exact; rows padded to
+// ngp = K/G rounded up to a multiple of 4, 16-byte aligned) | padding | xs [M]
+// fp32.  An A row
 // holds 128 bytes padded to 144, so the 16 rows one MFMA operand read
 // touches start 36 banks apart instead of all on the same bank.
 constexpr int kARow = 144;
@@ -578,8 +580,9 @@ constexpr int kARow = 144;
 __host__ __device__ constexpr int w1_stream_stride(int G) {
     return (kWinB1 + 2 * (kWinK1 / G) - 16 + 127) / 128 * 128 + 16;
 }
+__host__ __device__ constexpr int64_t w1_qs_stride(int64_t K, int G) { return (K / G + 3) / 4 * 4; }
 __host__ __device__ inline int w1_stream_a_bytes(int M, int64_t K, int G) {
-    return int((K / 128) * w1_arows(M, G) * kARow + (M * (K / G) + 4) * 4 + 16 * 4);
+    return int((K / 128) * w1_arows(M, G) * kARow + (M * w1_qs_stride(K, G) + 4) * 4 + 16 * 4);
 }
 __host__ __device__ inline int w1_stream_lds_bytes(int M, int64_t K, int G, int waves) {
     return waves * kW1RowsPerWave * (w1_stream_stride(G) + 4) + w1_stream_a_bytes(M, K, G);
@@ -633,8 +636,9 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
     char* wtile = lds + wave * kW1RowsPerWave * stride;
     float* wbias = reinterpret_cast<float*>(lds + WV * kW1RowsPerWave * stride) + wave * kW1RowsPerWave;
     char* abase = lds + WV * kW1RowsPerWave * (stride + 4);
-    int32_t* qs_all = reinterpret_cast<int32_t*>(abase + nchunk * R * kARow);
-    float* xs_l = reinterpret_cast<float*>(qs_all + M * ng + 4);
+    const int64_t ngp = w1_qs_stride(K, G);                // group sums per token row (padded)
+    float* qs_all = reinterpret_cast<float*>(abase + nchunk * R * kARow);
+    float* xs_l = qs_all + M * ngp + 4;
 
     // The wave's share: 32-row blocks wid, wid + W, ...; T windows in all.
     // Its first windows are requested before the A operand is staged, so the
@@ -739,7 +743,7 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
         sum += __shfl_xor(sum, 4, 64);
         if (p < apieces) {
             *reinterpret_cast<i32x4*>(abase + (p >> 3) * kARow + 16 * (p & 7)) = d;
-            if (u == 0 && h == 0) qs_all[int64_t(m) * ng + c] = sum;
+            if (u == 0 && h == 0) qs_all[int64_t(m) * ngp + c] = float(sum);
         }
     };
     constexpr int kPre = FUSED ? 3 : 0;                    // pieces per thread requested ahead of the weights
@@ -768,7 +772,7 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
         const int32_t* qsg = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + (w1_a_bytes(M, K, G) + 15) / 16 * 16);
         for (int64_t p = tid; p < apieces; p += 64 * WV)
             *reinterpret_cast<i32x4*>(abase + (p >> 3) * kARow + 16 * (p & 7)) = ld16(Ag + 16 * p);
-        for (int64_t e = tid; e < M * ng; e += 64 * WV) qs_all[e] = ld32(qsg + e);
+        for (int64_t e = tid; e < M * ng; e += 64 * WV) qs_all[(e / ng) * ngp + e % ng] = float(ld32(qsg + e));
     }
     if (tid < M) xs_l[tid] = xs[tid];
     __syncthreads();
@@ -844,7 +848,7 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
         const int m = p / S, j = p % S;
         sok[tt] = PK == 1 || sp < PK;
         g0[tt] = sok[tt] ? (G >= 128 ? sp : sp * S + j) : 0;   // group within the set
-        qb[tt] = sok[tt] ? (m < M ? m : 0) * int(ng) + g0[tt] : M * int(ng);   // outside: the zero sum
+        qb[tt] = sok[tt] ? (m < M ? m : 0) * int(ngp) + g0[tt] : 0;   // outside: not read
     }
     // One window's multiply.  FULL (every chunk of the window inside K): no
     // exit between chunks, so every LDS read of the window (A rows, weight
@@ -856,13 +860,38 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
         const char* a_w = a_lane + int64_t(w) * kChunks * R * kARow;
         uint32_t wd[kChunks][2];
         float scv[kSets][2][2];
-        int qsv[kSets][2];
+        float qsv[kSets][2];
         bool okv[kSets][2];
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) wd[c][cb] = *reinterpret_cast<const uint32_t*>(b_lane + 16 * cb * stride + 16 * c);
         }
+        if constexpr (FULL && PK == 1 && ngw == 8 && kSets == 8) {
+            // one token pair per lane slot, a whole window of eight groups:
+            // a row's eight scales are one 16-byte read of its tile row, a
+            // token's eight group sums two 16-byte reads (rows of ngp floats)
+            i32x4 sv[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) sv[cb] = *reinterpret_cast<const i32x4*>(wtile + (16 * cb + nl) * stride + kWinB1);
+            f32x4 qv[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const float* qp = qs_all + qb[tt] + int64_t(w) * ngw;
+                qv[tt][0] = *reinterpret_cast<const f32x4*>(qp);
+                qv[tt][1] = *reinterpret_cast<const f32x4*>(qp + 4);
+            }
+#pragma unroll
+            for (int st = 0; st < kSets; ++st)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    okv[st][tt] = true;
+                    qsv[st][tt] = qv[tt][st >> 2][st & 3];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        scv[st][cb][tt] = half_bits_to_float(uint16_t(uint32_t(sv[cb][st >> 1]) >> (16 * (st & 1))));
+                }
+        } else
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
 #pragma unroll
@@ -874,7 +903,7 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
                     gi = ok ? gi : 0;
                 }
                 okv[st][tt] = ok;
-                qsv[st][tt] = sok[tt] ? qs_all[qb[tt] + int64_t(w) * ngw + (gi - g0[tt])] : 0;
+                qsv[st][tt] = sok[tt] ? qs_all[qb[tt] + int64_t(w) * ngw + (gi - g0[tt])] : 0.0f;
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
                     scv[st][cb][tt] = half_bits_to_float(
@@ -912,9 +941,10 @@ __device__ __forceinline__ void w1_stream_body(const uint32_t* __restrict__ bits
 #pragma unroll
                             for (int tt = 0; tt < 2; ++tt) {
                                 const float v = __builtin_fmaf(16.0f, acc[cb][2 * tt], acc[cb][2 * tt + 1]);
-                                const int d = int(v) - qsv[st][tt];
-                                // a pair outside the packed slots has v below 1 and a zero group
-                                // sum: it adds 0; in a cut window a group past K adds 0 * d
+                                // the group dot v - sum q, exact in fp32 (integers below 2^17); with
+                                // packed slots a pair outside them has v below 1, truncated to 0, and
+                                // a zero group sum: it adds 0; in a cut window a group past K adds 0 * d
+                                const float d = __fsub_rn(PK == 1 ? v : __builtin_truncf(v), qsv[st][tt]);
                                 const double sc = FULL || okv[st][tt] ? double(scv[st][cb][tt]) : 0.0;
                                 sacc[cb][tt] = __builtin_fma(sc, double(d), sacc[cb][tt]);
                             }
@@ -1327,7 +1357,6 @@ hipError_t launch_w1_gemv(const uint32_t* bits, const uint16_t* scales, int64_t 
                           const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                           hipStream_t stream, uint16_t* y16) {
     const int64_t tb = w1_tokens_per_pass(N, K, G, M);
-    const int64_t rbs = (N + kW1Rows - 1) / kW1Rows;
     const int ns = w1_splits(N, K);
     const int64_t Mp = M < tb ? M : tb;
     double* part = ns > 1 ? reinterpret_cast<double*>(static_cast<char*>(ws) + w1_split_off(Mp, K, G)) : nullptr;
