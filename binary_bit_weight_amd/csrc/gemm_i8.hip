@@ -119,8 +119,8 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // WV = 4: one wave per SIMD, wave tiles 64 x 64; WV = 8: two waves per
     // SIMD (one's vector work runs while the other's matrix products do),
     // wave tiles 64 x 32; KH = 2: two halves of WV / 2 waves along K
-    static_assert(KH == 1 || (KH == 2 && FMT == 1 && LL_GEMM_I2S_SETS == 1), "halves along K: i2_s, one accumulator set");
-    static_assert(BMT == 128 || (BMT == 64 && FMT == 1), "tile rows: 128, or 64 (i2_s)");
+    static_assert(KH == 1 || (KH == 2 && FMT != 3 && LL_GEMM_I2S_SETS == 1), "halves along K: i2_s or TQ2_0");
+    static_assert(BMT == 128 || (BMT == 64 && FMT != 3), "tile rows: 128, or 64 (i2_s, TQ2_0)");
     constexpr int TH = 64 * WV;                            // threads
     constexpr int THH = TH / KH;                           // threads of one half
     constexpr int WNW = WV / KH / (BMT / 64);              // waves along N (BMT / 64 along M)
@@ -152,8 +152,16 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
     // TQ2_0: splits of whole 256-k blocks, so every split starts on an even group
     const int64_t nsplit_units = FMT != 2 ? ng : K / 256, per_unit = FMT != 2 ? 1 : 2;
     const int64_t gs0 = per_unit * (nsplit_units * split / S), gs1 = per_unit * (nsplit_units * (split + 1) / S);
-    // this half's groups (the launcher makes the count divisible by KH)
-    const int64_t g0 = gs0 + kh * ((gs1 - gs0) / KH), g1 = g0 + (gs1 - gs0) / KH;
+    // This half's groups [g0, g1): halves of whole units (TQ2_0: blocks),
+    // half 0 the shorter.  Both halves run the main loop for half 0's count
+    // and the tail up to half 1's (gend), so they meet the same barriers; the
+    // groups of half 0 past g1 load and synchronise but multiply nothing.
+    // (i2_s: the launcher makes the halves equal.)
+    const int64_t nunit = (gs1 - gs0) / per_unit, u0 = KH == 1 ? nunit : nunit / 2;
+    const int64_t g0 = gs0 + kh * u0 * per_unit;
+    const int64_t g1 = KH == 1 || kh == 0 ? g0 + u0 * per_unit : gs1;
+    const int64_t gmain = gs0 + kh * u0 * per_unit + u0 * per_unit;   // end of the common main loop
+    const int64_t gend = g0 + (nunit - u0 * (KH - 1)) * per_unit;       // end of the loop (half 1's count)
 
     // Activation loads of one group: CA 16-byte chunks per thread, chunk
     // idx = tid + TH c is row idx / 8, bytes 16 (idx % 8) of the group;
@@ -185,7 +193,9 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         uint16_t sc[FMT == 1 ? 1 : NB];                     // TQ2_0 / W1: the group's block scales
     };
     auto load = [&](int64_t g, Stage& s) {
-        const int64_t gc = g < g1 ? g : g1 - 1;            // past the range: reload the last group (unused)
+        // past the range: reload the last group (unused); an empty range
+        // (never launched) stays on its first group, inside the rows
+        const int64_t gc = g < g1 ? g : g1 > g0 ? g1 - 1 : g0;
 #pragma unroll
         for (int c = 0; c < CA; ++c) s.a[c] = ld16(arow[c] + 128 * gc);
 #pragma unroll
@@ -368,11 +378,11 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 
     // One group gi (register stage si, LDS buffer buf); `next`: a following
     // group exists.  `odd` (TQ2_0): gi ends a 256-k block.
-    auto group = [&](int64_t gi, int si, int buf, bool next, bool odd) {
+    auto group = [&](int64_t gi, int si, int buf, bool next, bool odd, bool live) {
         const bool fresh0 = (FMT == 2 && !odd) || FMT == 3;
         __builtin_amdgcn_sched_barrier(0);
         // step 0
-        mfma(ac[0], bo[0], 0, fresh0);
+        if (live) mfma(ac[0], bo[0], 0, fresh0);
         decode(bq, 1, bo[1]);
         if (next) {
             const Stage& ns = st[(si + 1) % D];
@@ -393,7 +403,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         }
         __builtin_amdgcn_sched_barrier(0);
         // step 1
-        mfma(ac[1], bo[1], 1, false);
+        if (live) mfma(ac[1], bo[1], 1, false);
         decode(bq, 2, bo[0]);
 #pragma unroll
         for (int k = 0; k < 2 * NB; ++k) {
@@ -404,7 +414,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         if (next) lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // step 2
-        mfma(ac[2], bo[0], 2, false);
+        if (live) mfma(ac[2], bo[0], 2, false);
         decode(bq, 3, bo[1]);
         if (next)
 #pragma unroll
@@ -417,7 +427,7 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
         }
         __builtin_amdgcn_sched_barrier(0);
         // step 3
-        mfma(ac[3], bo[1], 3, false);
+        if (live) mfma(ac[3], bo[1], 3, false);
         if (next) decode(bqn, 0, bo[0]);
 #pragma unroll
         for (int k = 0; k < 2 * NB; ++k) {
@@ -425,9 +435,10 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FMT == 3) scale_in(sc);
+        if constexpr (FMT == 3)
+            if (live) scale_in(sc);
         if constexpr (FMT == 2)
-            if (odd) scale_in(sc);
+            if (odd && live) scale_in(sc);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             ac[t][0] = an[t][0];
@@ -446,15 +457,16 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
 
     // (g0 is even (TQ2_0) and U is even, so group g0 + i is odd exactly when i is)
     int64_t g = g0;
-    for (; g + U < g1; g += U) {
+    for (; g + U < gmain; g += U) {
 #pragma unroll
-        for (int i = 0; i < U; ++i) group(g + i, i % D, i & 1, true, i & 1);
+        for (int i = 0; i < U; ++i) group(g + i, i % D, i & 1, true, i & 1, true);
     }
-    // the last 1 .. U groups
-    const int rem = int(g1 - g);
+    // the last 1 .. U groups (TQ2_0 halves: up to U + 2, half 0's last ones past g1)
+    constexpr int TAIL = U + (KH == 2 && FMT == 2 ? 2 : 0);
+    const int rem = int(gend - g);
 #pragma unroll
-    for (int j = 0; j < U; ++j)
-        if (j < rem) group(g + j, j % D, j & 1, j + 1 < rem, j & 1);
+    for (int j = 0; j < TAIL; ++j)
+        if (j < rem) group(g + j, j % D, j & 1, j + 1 < rem, j & 1, g + j < g1);
 
     using E = std::conditional_t<FMT == 1, int32_t, float>;
     using V = std::conditional_t<FMT == 1, i32x16, f32x16>;
@@ -523,6 +535,32 @@ __device__ __forceinline__ void gemm_i8_body(const uint8_t* __restrict__ codes, 
             else
                 fin[mb][nb] = facc[mb][nb];
         }
+    if constexpr (KH == 2 && FMT != 1) {
+        // TQ2_0 halves: half 1's fp32 block-scaled sums reach half 0 through
+        // the activation buffers; half 0 adds them to its own (one fixed
+        // order) and finishes the tile alone (no barrier follows: S = 1)
+        __syncthreads();
+        int32_t* xch = reinterpret_cast<int32_t*>(lds) + (w % (WV / KH)) * (2 * NB * 16 * 64) + lane;
+        if (kh == 1)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float fv = fin[mb][nb][r];           // (a scalar copy: the element, not the vector, is cast)
+                        xch[((mb * NB + nb) * 16 + r) * 64] = __builtin_bit_cast(int32_t, fv);
+                    }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    fin[mb][nb][r] = __fadd_rn(fin[mb][nb][r], __builtin_bit_cast(float, xch[((mb * NB + nb) * 16 + r) * 64]));
+    }
 
     if (S > 1) {
         // Publish this split's partial tile (device-coherent stores), wait for
@@ -694,12 +732,12 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV
     gemm_i8_body<3, false, WV, BNT>(bits, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
-template <int WV, int BNT>
+template <int WV, int BNT, int KH = 1, int BMT = BM>
 __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4))) gemm_i8_tq2_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t N, int64_t K,
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, const float* __restrict__ bias,
     float* __restrict__ y, int S, int32_t* __restrict__ part, int32_t* __restrict__ counters, uint16_t* __restrict__ y16) {
-    gemm_i8_body<2, false, WV, BNT>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
+    gemm_i8_body<2, false, WV, BNT, KH, BMT>(codes, scales, N, K, xq, xs, M, bias, y, nullptr, S, part, counters, nullptr, y16);
 }
 
 #ifndef LL_GEMM_SLOTS
@@ -716,6 +754,9 @@ __global__ void __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV
 #endif
 #ifndef LL_GEMM_SPLIT_GROUPS
 #define LL_GEMM_SPLIT_GROUPS 10                          // 128-k groups a split keeps at least
+#endif
+#ifndef LL_GEMM_TQ2_HALVES
+#define LL_GEMM_TQ2_HALVES 1                             // TQ2_0: narrow tiles as two halves where unsplit
 #endif
 #ifndef LL_GEMM_NARROW_ROWS
 #define LL_GEMM_NARROW_ROWS 64                           // narrow tiles: 64 x 128 (or 128 x 64)
@@ -752,6 +793,16 @@ int64_t gemm_tiles(int64_t M, int64_t N, bool narrow_ok) {
     const TileShape t = gemm_shape(M, N, narrow_ok);
     return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
 }
+int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow);
+// Narrow tiles: i2_s wherever they apply; TQ2_0 where they need no split and
+// K holds two 256-k blocks or more (it always runs them as two halves along
+// K, one block or more each, its block scaling wanting two waves per SIMD);
+// W1 never.
+bool narrow_for(int fmt, int64_t M, int64_t N, int64_t K) {
+    if (fmt == 1) return true;
+    if (fmt != 2 || !LL_GEMM_TQ2_HALVES || K / 256 < 2) return false;   // each half at least one 256-k block
+    return gemm_narrow(M, N, true) && gemm_splits(M, N, K, true, true) == 1;
+}
 // Split count: enough workgroups to cover the chip (LL_GEMM_SLOTS resident
 // workgroups), at most four splits (the last one adds the others' partial
 // tiles one after another) of at least ten 128-k groups each (TQ2_0:
@@ -759,7 +810,7 @@ int64_t gemm_tiles(int64_t M, int64_t N, bool narrow_ok) {
 // counter region.  Measured on 2560 x 6912 at M = 64: twelve splits 17.2
 // us, six 12.6, four 11.2; on 2560 x 2560 at M = 64 two splits beat four
 // (9.2 against 10.1 us).
-int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow = true) {
+int gemm_splits(int64_t M, int64_t N, int64_t K, bool narrow_ok, bool allow) {
     const int64_t tiles = gemm_tiles(M, N, narrow_ok);
     if (!allow || tiles > kMaxCounters) return 1;
     const int64_t ng = K / 128;
@@ -787,8 +838,8 @@ hipError_t launch_tiles(Kern kernel, int64_t tiles, int S, int threads, hipStrea
 namespace llk {
 
 size_t gemm_i8_workspace(int64_t M, int64_t N, int64_t K, int fmt) {
-    const bool narrow_ok = fmt == 1;
-    const int S = gemm_splits(M, N, K, narrow_ok);
+    const bool narrow_ok = narrow_for(fmt, M, N, K);
+    const int S = gemm_splits(M, N, K, narrow_ok, true);
     if (S == 1) return 0;
     const TileShape t = gemm_shape(M, N, narrow_ok);
     return size_t(gemm_tiles(M, N, narrow_ok)) * S * size_t(t.bm) * size_t(t.bn) * 4;
@@ -840,9 +891,15 @@ hipError_t launch_gemm_i8_w1(const uint32_t* bits, const uint16_t* scales, int64
 hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const int8_t* xq,
                               const float* xs, int64_t M, const float* bias, float* y, int32_t* counters, void* ws,
                               hipStream_t stream, uint16_t* y16) {
-    const int64_t tiles = gemm_tiles(M, N, false);
-    const int S = gemm_splits(M, N, K, false, ws != nullptr && counters != nullptr);
+    const bool narrow = narrow_for(2, M, N, K);
+    const int64_t tiles = gemm_tiles(M, N, narrow);
+    const int S = gemm_splits(M, N, K, narrow, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_BLOCK_WAVES;
+    if (narrow) {                                          // unsplit (S = 1): two halves along K
+        constexpr int NBM = LL_GEMM_NARROW_ROWS, NBN = BM * BN / 2 / LL_GEMM_NARROW_ROWS;
+        return launch_tiles_lds(gemm_i8_tq2_kernel<8, NBN, 2, NBM>, tiles, S, 512, 2 * kGemmLds, stream, codes, scales, N,
+                                K, xq, xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
+    }
     return launch_tiles(gemm_i8_tq2_kernel<WV, BN>, tiles, S, 64 * WV, stream, codes, scales, N, K, xq, xs, M, bias, y, S,
                         static_cast<int32_t*>(ws), counters, y16);
 }
