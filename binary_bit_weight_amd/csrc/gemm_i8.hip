@@ -896,6 +896,7 @@ hipError_t launch_gemm_i8_tq2(const uint8_t* codes, const uint16_t* scales, int6
     const int S = gemm_splits(M, N, K, narrow, ws != nullptr && counters != nullptr);
     constexpr int WV = LL_GEMM_BLOCK_WAVES;
     if (narrow) {                                          // unsplit (S = 1): two halves along K
+        if (S != 1) return hipErrorInvalidValue;           // half 1 leaves before a split's handoff
         constexpr int NBM = LL_GEMM_NARROW_ROWS, NBN = BM * BN / 2 / LL_GEMM_NARROW_ROWS;
         return launch_tiles_lds(gemm_i8_tq2_kernel<8, NBN, 2, NBM>, tiles, S, 512, 2 * kGemmLds, stream, codes, scales, N,
                                 K, xq, xs, M, bias, y, S, static_cast<int32_t*>(ws), counters, y16);
