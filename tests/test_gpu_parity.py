@@ -217,7 +217,8 @@ def _tq2_i8_case(N, K, M, seed, rows=None, bias=False, repeat=1):
 
 # split K (whole 256-k blocks): (5, 2560, 300) two ways (5 + 5 blocks), (150, 2816, 33) two uneven ways
 # (5 + 6), (64, 4096, 40) three uneven ways (5 + 5 + 6), (64, 5376, 40) four uneven ways (5 + 5 + 5 + 6);
-# the others unsplit
+# the others unsplit.  Narrow tiles run as two halves of whole blocks along K: (77, 512, 65) one block
+# each, (200, 768, 17) one and two; (128, 256, 128) has a single block, so it keeps the wide tiles
 @pytest.mark.parametrize("N,K,M", [(77, 512, 65), (128, 256, 128), (200, 768, 17), (33, 256, 1), (130, 1280, 129),
                                    (5, 2560, 300), (300, 2048, 200), (64, 4096, 40), (257, 1792, 130),
                                    (150, 2816, 33), (64, 5376, 40)])
